@@ -1,0 +1,302 @@
+"""Seeded synthetic workloads (inputs only; none of the method's arithmetic).
+
+Every tensor is a pure function of (workload seed, tensor kind, layer,
+sequence, head, step) through a counter-based 32-bit integer hash, so any
+slice can be regenerated alone, on the CPU or on the GPU, with identical
+bits: the hash runs in torch int64 arithmetic (exact on both devices), a
+standard-normal value is read from a fixed inverse-CDF table, and the few
+floating-point operations applied afterwards (x8 outlier scaling, adding the
+mean-query offset, bf16 rounding) are single IEEE operations.
+
+Workload recipe (shapes and structure of the pages' settings: Llama-3.1-8B
+GQA attention, 8k-131k contexts, 5-25% budgets):
+
+* K, V, Q entries ~ N(0, 1) (65536-level inverse-CDF quantiles).
+* Outlier channels: 4 of the 128 channels are scaled x8, drawn
+  independently for K and for Q per (layer, sequence, KV head); the Q set is
+  shared by the KV head's query group.
+* Mean query direction u: a unit vector with +-1/8 on 64 hashed channels.
+  Queries add mu*u with mu = |c|/4, |c| = sqrt(124 + 4*64) the expected row
+  norm.  Heavy keys: 64 positions per (layer, sequence, KV head, epoch) in
+  [4, L0) are replaced by |c| (0.6 u + 0.8 w), w a unit vector with +-1/8 on
+  the other 64 channels (cosine 0.6 with u).  Epoch e of a multi-epoch run
+  uses its own u_e; all epochs' heavy keys are planted at prefill.
+* New keys / values appended at decode steps have no heavy rows.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+_M32 = 0xFFFFFFFF
+_TABLE_CACHE = {}
+
+# tensor-kind ids of the hash streams
+_K, _V, _Q, _KN, _VN = 1, 2, 3, 4, 5
+_META_KOUT, _META_QOUT, _META_U, _META_HEAVY, _META_LEN = 11, 12, 13, 14, 15
+
+
+def _mix32_int(x: int) -> int:
+    x &= _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    return (x >> 16) ^ x
+
+
+def stream_key(*fields: int) -> int:
+    """32-bit key of one stream, chained through the hash field by field."""
+    k = 0x9E3779B9
+    for f in fields:
+        k = _mix32_int(k ^ (int(f) & _M32))
+        k = _mix32_int(k + 0x7F4A7C15)
+    return k
+
+
+def _mix32_np(x):
+    x = x & _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    return (x >> 16) ^ x
+
+
+def _mix32_t(x):
+    x = x & _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
+    return (x >> 16) ^ x
+
+
+def _normal_table(device):
+    import torch
+    key = str(device)
+    if key not in _TABLE_CACHE:
+        from scipy.special import ndtri
+        vals = ndtri((np.arange(65536, dtype=np.float64) + 0.5) / 65536.0).astype(np.float32)
+        _TABLE_CACHE[key] = torch.from_numpy(vals).to(device)
+    return _TABLE_CACHE[key]
+
+
+def normal_stream(key: int, shape, device="cpu"):
+    """float32 tensor of N(0,1) quantiles, element i from hash(hash(i) ^ key)."""
+    import torch
+    n = int(np.prod(shape))
+    idx = torch.arange(n, dtype=torch.int64, device=device)
+    h = _mix32_t(_mix32_t(idx) ^ key)
+    return _normal_table(device)[h >> 16].reshape(shape)
+
+
+def _rank_channels(key: int, n: int) -> np.ndarray:
+    """A key-dependent permutation of range(n) (sorting hashed ids)."""
+    h = _mix32_np(_mix32_np(np.arange(n, dtype=np.int64)) ^ key)
+    return np.lexsort((np.arange(n), h))
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic decode workload and its eviction settings."""
+    name: str
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str                      # "f32" or "bf16"
+    prefill_lens: tuple             # per sequence
+    steps: int
+    seed: int
+    alpha_new: float = 0.05
+    budget: int = 0                 # per selection group (tokens or blocks)
+    n_sink: int = 0
+    n_recent: int = 0
+    policy: str = "ema"             # ema | cumulative | lrfu_block | tiered_int2
+    refresh_interval: int = 1
+    score_free: bool = False
+    structured: bool = True         # outliers, mean query direction, heavy keys
+    n_heavy: int = 64
+    n_epochs: int = 1
+    epoch_steps: int = 0            # 0: one epoch for the whole run
+    beta: float = 0.001
+    page_tokens: int = 16
+    region_fracs: tuple = ()
+    region_half_lives: tuple = ()
+    pinned_regions: tuple = ()
+    window_tokens: int = 32
+    fp_windows: int = 0
+    int2_windows: int = 0
+    extra: dict = field(default_factory=dict, compare=False, hash=False)
+
+    @property
+    def batch(self):
+        return len(self.prefill_lens)
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def scaled(self, **kw):
+        return replace(self, extra={}, **kw)
+
+    # -- per-(layer, sequence, KV head) structure --------------------------
+    def _structure(self, layer, seq, kvh):
+        d = self.head_dim
+        kout = _rank_channels(stream_key(self.seed, _META_KOUT, layer, seq, kvh), d)[:4]
+        qout = _rank_channels(stream_key(self.seed, _META_QOUT, layer, seq, kvh), d)[:4]
+        ck = np.ones(d, np.float32)
+        ck[kout] = 8.0
+        cq = np.ones(d, np.float32)
+        cq[qout] = 8.0
+        return ck, cq
+
+    def _directions(self, layer, seq, kvh, epoch):
+        d = self.head_dim
+        perm = _rank_channels(stream_key(self.seed, _META_U, layer, seq, kvh, epoch), d)
+        signs = np.where(_mix32_np(np.arange(d, dtype=np.int64) ^ stream_key(
+            self.seed, _META_U + 100, layer, seq, kvh, epoch)) & 1, 1.0, -1.0)
+        u = np.zeros(d, np.float32)
+        w = np.zeros(d, np.float32)
+        half = d // 2
+        u[perm[:half]] = (signs[perm[:half]] / math.sqrt(half)).astype(np.float32)
+        w[perm[half:]] = (signs[perm[half:]] / math.sqrt(half)).astype(np.float32)
+        return u, w
+
+    def _norm_c(self):
+        return math.sqrt((self.head_dim - 4) + 4 * 64.0)
+
+    def heavy_positions(self, layer, seq, kvh, epoch):
+        L0 = self.prefill_lens[seq]
+        lo = 4
+        if L0 - lo < self.n_heavy:
+            return np.zeros(0, np.int64)
+        key = stream_key(self.seed, _META_HEAVY, layer, seq, kvh, epoch)
+        # distinct positions: sort hashed candidate ids and take the first n
+        cand = np.arange(lo, L0, dtype=np.int64)
+        h = _mix32_np(_mix32_np(cand) ^ key)
+        return np.sort(cand[np.lexsort((cand, h))[: self.n_heavy]])
+
+    def epoch_of(self, t):
+        if self.epoch_steps <= 0:
+            return 0
+        return min((t - 1) // self.epoch_steps, self.n_epochs - 1)
+
+    # -- tensors -------------------------------------------------------------
+    def _round(self, x):
+        import torch
+        return x if self.dtype == "f32" else x.to(torch.bfloat16)
+
+    def prefill_kv(self, seq, device="cpu", layers=None, heads=None):
+        """(K, V) of one sequence: [len(layers), len(heads), L0, d]."""
+        import torch
+        layers = range(self.n_layers) if layers is None else layers
+        heads = range(self.n_kv_heads) if heads is None else heads
+        L0, d = self.prefill_lens[seq], self.head_dim
+        Ks, Vs = [], []
+        for l in layers:
+            kh, vh = [], []
+            for h in heads:
+                k = normal_stream(stream_key(self.seed, _K, l, seq, h), (L0, d), device)
+                v = normal_stream(stream_key(self.seed, _V, l, seq, h), (L0, d), device)
+                if self.structured:
+                    ck, _ = self._structure(l, seq, h)
+                    k = k * torch.from_numpy(ck).to(device)
+                    nc = self._norm_c()
+                    for e in range(self.n_epochs):
+                        pos = self.heavy_positions(l, seq, h, e)
+                        if len(pos) == 0:
+                            continue
+                        u, w = self._directions(l, seq, h, e)
+                        row = (np.float32(nc * 0.6) * u + np.float32(nc * 0.8) * w).astype(np.float32)
+                        k[torch.from_numpy(pos).to(device)] = torch.from_numpy(row).to(device)
+                kh.append(self._round(k))
+                vh.append(self._round(v))
+            Ks.append(torch.stack(kh))
+            Vs.append(torch.stack(vh))
+        return torch.stack(Ks), torch.stack(Vs)
+
+    def _step_structure(self, seqs, epoch):
+        """Stacked (ck, cq, mu*u) arrays [L, len(seqs), Hkv, d] (cached)."""
+        cache = self.extra.setdefault("_step_structure", {})
+        key = (tuple(seqs), epoch)
+        if key not in cache:
+            L, Hkv, d = self.n_layers, self.n_kv_heads, self.head_dim
+            ck = np.ones((L, len(seqs), Hkv, d), np.float32)
+            cq = np.ones((L, len(seqs), Hkv, d), np.float32)
+            mu_u = np.zeros((L, len(seqs), Hkv, d), np.float32)
+            if self.structured:
+                mu = np.float32(self._norm_c() / 4.0)
+                for l in range(L):
+                    for bi, b in enumerate(seqs):
+                        for h in range(Hkv):
+                            ck[l, bi, h], cq[l, bi, h] = self._structure(l, b, h)
+                            u, _ = self._directions(l, b, h, epoch)
+                            mu_u[l, bi, h] = (mu * u).astype(np.float32)
+            cache[key] = (ck, cq, mu_u)
+        return cache[key]
+
+    def step_inputs(self, t, device="cpu", seqs=None):
+        """(q [L,b,Hq,d], k_new [L,b,Hkv,d], v_new [L,b,Hkv,d]) for step t >= 1."""
+        import torch
+        seqs = list(range(self.batch)) if seqs is None else list(seqs)
+        L, d, Hkv, Hg = self.n_layers, self.head_dim, self.n_kv_heads, self.group_size
+        nb = len(seqs)
+
+        def keys(kind):
+            k = [[[stream_key(self.seed, kind, l, b, h, t) for h in range(Hkv)]
+                  for b in seqs] for l in range(L)]
+            return torch.tensor(k, dtype=torch.int64, device=device)
+
+        table = _normal_table(device)
+        idx_kv = _mix32_t(torch.arange(d, dtype=torch.int64, device=device))
+        idx_q = _mix32_t(torch.arange(Hg * d, dtype=torch.int64, device=device))
+        k = table[_mix32_t(idx_kv ^ keys(_KN)[..., None]) >> 16]            # [L,b,Hkv,d]
+        v = table[_mix32_t(idx_kv ^ keys(_VN)[..., None]) >> 16]
+        z = table[_mix32_t(idx_q ^ keys(_Q)[..., None]) >> 16].reshape(L, nb, Hkv, Hg, d)
+        if self.structured:
+            ck, cq, mu_u = (torch.from_numpy(a).to(device)
+                            for a in self._step_structure(seqs, self.epoch_of(t)))
+            k = k * ck
+            z = z * cq[:, :, :, None, :]
+            z = z + mu_u[:, :, :, None, :]
+        q = z.reshape(L, nb, Hkv * Hg, d)
+        return self._round(q), self._round(k), self._round(v)
+
+
+def _lengths(seed, n, lo, hi):
+    key = stream_key(seed, _META_LEN)
+    h = _mix32_np(_mix32_np(np.arange(n, dtype=np.int64)) ^ key)
+    return tuple(int(lo + (x % (hi - lo + 1))) for x in h)
+
+
+def workload(name: str) -> Workload:
+    """The five configured workloads, by short name."""
+    if name == "tiny":
+        return Workload("tiny_inertiakv_1L_8q2kv_d64_f32", 1, 8, 2, 64, "f32", (512,), 64,
+                        seed=1001, alpha_new=0.05, budget=128, structured=False)
+    if name == "llama8b_32k":
+        return Workload("llama8b_32k_10pct", 32, 32, 8, 128, "bf16", (32768,), 256,
+                        seed=1002, alpha_new=0.05, budget=3277, n_sink=4, n_recent=32)
+    if name == "lazy16x8k":
+        return Workload("batch16_8k_25pct_lazy8", 32, 32, 8, 128, "bf16", (8192,) * 16, 512,
+                        seed=1003, alpha_new=0.05, budget=2048, refresh_interval=8)
+    if name == "scorefree16x8k":
+        return Workload("batch16_8k_25pct_scorefree", 32, 32, 8, 128, "bf16", (8192,) * 16, 512,
+                        seed=1003, alpha_new=0.05, budget=2048, score_free=True, n_recent=32)
+    if name == "lrfu64":
+        return Workload("lrfu_64seq_4k16k_blocks20pct", 32, 32, 8, 128, "bf16",
+                        _lengths(1004, 64, 4096, 16384), 1024, seed=1004, alpha_new=0.05,
+                        policy="lrfu_block", beta=0.001, n_epochs=32, epoch_steps=32,
+                        region_fracs=(0.1, 0.1, 0.2, 0.4, 0.2),
+                        region_half_lives=(170.0, 100.0, 60.0, 30.0, 15.0), pinned_regions=(0,))
+    if name == "qevict131k":
+        return Workload("qevict_131k_fp5_int2_20", 32, 32, 8, 128, "bf16", (131072,), 128,
+                        seed=1005, policy="tiered_int2", n_sink=5, n_recent=32, n_epochs=4,
+                        epoch_steps=32, window_tokens=32, fp_windows=205, int2_windows=819)
+    raise KeyError(name)
+
+
+WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k")

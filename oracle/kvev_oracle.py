@@ -1,0 +1,483 @@
+"""Plain, slow CPU oracle for one decode step of attention-scored KV eviction.
+
+TEST INFRASTRUCTURE.  This module defines what the GPU library must compute.
+Only tests, the smoke check and the CPU-baseline leg of the benchmark may
+import it; the GPU library never does, and this module imports nothing from
+the library.  Floating point is fp64 except the INT2 quantizer, whose integer
+codes are decided in IEEE fp32 exactly as the GPU decides them.
+
+Sources (cited by short tag, with section / equation on that page):
+
+* [InertiaKV]  "What Matters for Aggressive Decoding-Time KV Eviction?
+  Temporal Aggregation and Ranking Preservation" (arXiv 2609.03515).
+* [MemDecay]   "MemDecay: Region-Aware KV Cache Eviction for Efficient LLM
+  Agent Inference" (arXiv 2607.10582).
+* [QEvict]     "QEvict: Recoverable Quantized KV Eviction for
+  Attention-Drift-Robust Long-Context Decoding", technical review.
+* [LRFU-fig]   "Attention-Aware Block Eviction" figure page of the KV-cache
+  docs (chapter 7, EMA eviction).
+
+Conventions.  ``alpha_new`` is the weight on the new observation,
+``score <- alpha_new*new + (1-alpha_new)*score`` ([LRFU-fig], table and
+formula).  [InertiaKV] §3.1 Eq.4 puts its alpha on the old state; the two are
+related by ``alpha_new = 1 - alpha_InertiaKV``.
+
+Where the pages leave a step open, the reading taken is stated at the
+function that implements it (and collected in the design notes).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "ema_update", "cumulative_update", "ema_half_life", "recency_decay",
+    "lrfu_priority", "layer_fold", "layer_fold_weights", "decode_attention",
+    "group_mass", "select_keep", "hole_fill_moves", "apply_moves",
+    "tier_capacities", "route_tiers", "int2_quantize", "int2_dequantize",
+    "TokenModeOracle", "region_decay_rates",
+]
+
+
+# ---------------------------------------------------------------------------
+# Score aggregation primitives
+# ---------------------------------------------------------------------------
+
+def ema_update(score, new, alpha_new):
+    """EMA step ``score <- alpha_new*new + (1-alpha_new)*score``.
+
+    [LRFU-fig] smoothing formula and worked table; [InertiaKV] §3.1 Eq.4
+    (with its alpha equal to ``1 - alpha_new``); [MemDecay] §III-C Eq.2
+    (with rho equal to ``1 - alpha_new``).  Written with plain operators so
+    it also runs on ``decimal.Decimal`` inputs.
+    """
+    return alpha_new * new + (1 - alpha_new) * score
+
+
+def cumulative_update(score, new):
+    """Non-decaying accumulator ``m_t = m_{t-1} + s_t``.
+
+    [InertiaKV] §3.1 Eq.3; [QEvict] §4.2 Eq.1 (per window, per layer).
+    """
+    return score + new
+
+
+def ema_half_life(alpha_new):
+    """Steps for the EMA weight of an observation to halve: ln0.5/ln(1-a).
+
+    [LRFU-fig]: at alpha 0.05 the page gives ln0.5/ln0.95 = 13.5 steps.
+    """
+    return math.log(0.5) / math.log(1.0 - alpha_new)
+
+
+def recency_decay(idle, beta):
+    """``1 - exp(-beta*idle)``: the idle-time factor of [LRFU-fig]."""
+    return 1.0 - np.exp(-beta * np.asarray(idle, dtype=np.float64))
+
+
+def lrfu_priority(score, idle, beta):
+    """Eviction priority ``(1 - score) * (1 - exp(-beta*idle))``.
+
+    [LRFU-fig]: the block with the HIGHER priority is evicted (block B in the
+    page's example).
+    """
+    return (1.0 - np.asarray(score, dtype=np.float64)) * recency_decay(idle, beta)
+
+
+def region_decay_rates(half_lives):
+    """Decay rate per region from its half-life, ``lambda = ln2 / t_half``.
+
+    [MemDecay] §IV-B Eq.7 (``t_half = ln2 / lambda``).
+    """
+    return np.array([math.log(2.0) / h for h in half_lives], dtype=np.float64)
+
+
+def layer_fold(m, G_layers, alpha_new, policy="ema"):
+    """Fold per-layer group mass into the shared state, layer by layer.
+
+    [InertiaKV] App. E "Layer scoring": each eligible layer immediately
+    updates the shared state, ``m_{t,l} = a m_{t,l-1} + (1-a) s_{t,l}`` with
+    ``m_{t,0} = m_{t-1,K}``.  Reading: all layers are eligible, in ascending
+    order.  ``policy="cumulative"`` applies [InertiaKV] Eq.3 per layer.
+    """
+    m = np.array(m, dtype=np.float64, copy=True)
+    for G in G_layers:
+        if policy == "ema":
+            m = ema_update(m, np.asarray(G, dtype=np.float64), alpha_new)
+        elif policy == "cumulative":
+            m = cumulative_update(m, np.asarray(G, dtype=np.float64))
+        else:
+            raise ValueError(policy)
+    return m
+
+
+def layer_fold_weights(alpha_new, n_layers):
+    """Closed-form weights of the layer-sequential EMA.
+
+    [InertiaKV] App. E: the prior state has weight ``alpha^K`` and layer l
+    (1-based) has weight ``(1-alpha) alpha^{K-l}`` (alpha on the old state).
+    Returned as (prior_weight, [w_0 .. w_{L-1}]) with 0-based layers.
+    """
+    keep = 1.0 - alpha_new
+    prior = keep ** n_layers
+    w = [alpha_new * keep ** (n_layers - 1 - l) for l in range(n_layers)]
+    return prior, w
+
+
+# ---------------------------------------------------------------------------
+# Attention with exposed probabilities
+# ---------------------------------------------------------------------------
+
+def decode_attention(q, K, V):
+    """Scaled dot-product decode attention that also returns probabilities.
+
+    [QEvict] §4.1 (Attention): ``a = softmax(q K^T / sqrt(d))``, ``o = a V``.
+    ``q``: [H, d] (the query heads of one KV head's group), ``K``, ``V``:
+    [n, d].  Returns ``(out [H, d], p [H, n], logits [H, n])`` in fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    d = q.shape[-1]
+    s = (q @ K.T) / math.sqrt(d)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mx)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ V, p, s
+
+
+def group_mass(p):
+    """Per-token attention mass summed over a KV head's query group.
+
+    [InertiaKV] §3.1 Eq.1 pools over heads; App. E: for GQA each KV head's
+    attention is shared across its query-head group before pooling.
+    Reading: one score per (sequence, KV head) token, equal to the SUM of the
+    group's probabilities (the mean times the group size; a uniform positive
+    scale, invisible to ranking per [InertiaKV] Corollary 2).
+    """
+    return np.asarray(p, dtype=np.float64).sum(axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Selection and compaction
+# ---------------------------------------------------------------------------
+
+def select_keep(scores, positions, budget, n_sink=0, n_recent=0):
+    """Keep mask: protected tokens plus the top-(budget - |protected|) rest.
+
+    [InertiaKV] §3.1: whenever the cache exceeds B, evict the tokens with the
+    lowest utility.  [MemDecay] §III-A Eq.1: with a forced set F, keeping the
+    highest-scoring tokens after forcing F is optimal.
+
+    Readings: the protected set is the sinks (positions < n_sink) and the
+    n_recent largest positions present (the new token included).  Ranking
+    key is (score, position), larger is kept, so on an exact score tie the
+    more recent token stays.  No eviction when ``len(scores) <= budget``.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    n = scores.shape[0]
+    keep = np.ones(n, dtype=bool)
+    if n <= budget:
+        return keep
+    newest = positions.max()
+    prot = (positions < n_sink) | (positions > newest - n_recent)
+    room = budget - int(prot.sum())
+    if room < 0:
+        raise ValueError("protected tokens exceed the budget")
+    cand = np.flatnonzero(~prot)
+    # ascending by (score, position); the last `room` are kept
+    order = cand[np.lexsort((positions[cand], scores[cand]))]
+    keep[:] = prot
+    if room > 0:
+        keep[order[len(order) - room:]] = True
+    return keep
+
+
+def hole_fill_moves(keep, budget):
+    """Compaction plan that packs the survivors into slots [0, budget).
+
+    Reading (the pages fix no layout): holes are the unkept slots below the
+    budget, ascending; movers are the kept slots at or above it, ascending;
+    mover j fills hole j.  Returns a list of (src_slot, dst_slot).
+    """
+    keep = np.asarray(keep, dtype=bool)
+    n = keep.shape[0]
+    if n <= budget:
+        return []
+    holes = [s for s in range(budget) if not keep[s]]
+    movers = [s for s in range(budget, n) if keep[s]]
+    if len(holes) != len(movers):
+        raise ValueError("keep mask does not hold exactly `budget` slots")
+    return list(zip(movers, holes))
+
+
+def apply_moves(arr, moves, axis=0):
+    """Copy slot ``src`` onto slot ``dst`` for every move, along ``axis``."""
+    arr = np.moveaxis(arr, axis, 0)
+    for src, dst in moves:
+        arr[dst] = arr[src]
+    return np.moveaxis(arr, 0, axis)
+
+
+# ---------------------------------------------------------------------------
+# Tiered (full precision / INT2 / evicted) routing primitives
+# ---------------------------------------------------------------------------
+
+def tier_capacities(b_hist, q, m_f, m_q):
+    """Tier sizes ``K_f = floor((1-q)B_hist/M_f)``, ``K_q = floor(q B_hist/M_q)``.
+
+    [QEvict] §4.3 Eq.3.
+    """
+    return int(math.floor((1.0 - q) * b_hist / m_f)), int(math.floor(q * b_hist / m_q))
+
+
+def route_tiers(scores, candidates, k_f, k_q):
+    """One routing event: F = top K_f, Q = next K_q, E = the rest.
+
+    [QEvict] §4.4 Eq.5 and Algorithm 1 (sort candidates by cumulative score,
+    fill the full-precision tier, then the quantized tier).  Reading: equal
+    scores rank the higher window index first.  Returns three sorted lists.
+    """
+    cand = np.asarray(sorted(candidates), dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64)[cand]
+    order = cand[np.lexsort((cand, s))][::-1]          # descending
+    F = sorted(order[:k_f].tolist())
+    Q = sorted(order[k_f:k_f + k_q].tolist())
+    E = sorted(order[k_f + k_q:].tolist())
+    return F, Q, E
+
+
+def _int2_params(x32):
+    """Asymmetric min-max parameters of one group, stored as fp16.
+
+    Reading of [QEvict] §4.4 line 11 (asymmetric, KIVI-style): zero = min,
+    scale = (max - min) / 3, both rounded to fp16 (round to nearest even);
+    the subtraction and division are single IEEE fp32 operations.
+    """
+    lo = np.float32(x32.min())
+    hi = np.float32(x32.max())
+    span = np.float32(hi - lo)
+    scale = np.float16(np.float32(span / np.float32(3.0)))
+    zero = np.float16(lo)
+    return scale, zero
+
+
+def _int2_codes(x32, scale16, zero16):
+    """Codes ``clamp(rint((x - zero)/scale), 0, 3)`` in IEEE fp32."""
+    s = np.float32(scale16)
+    z = np.float32(zero16)
+    if s == np.float32(0.0):
+        return np.zeros(x32.shape, dtype=np.uint8)
+    t = (x32.astype(np.float32) - z).astype(np.float32)      # fp32 subtract
+    t = (t / s).astype(np.float32)                           # fp32 divide
+    return np.clip(np.rint(t), 0, 3).astype(np.uint8)        # ties to even
+
+
+def int2_quantize(x, axis_groups):
+    """Quantize a [tokens, channels] fp32 tile to 2-bit codes.
+
+    ``axis_groups="channel"``: one (scale, zero) per channel over all tokens
+    of the tile (keys, [QEvict] §4.4 line 11 "per-channel-key").
+    ``axis_groups="token32"``: one (scale, zero) per token per 32-channel
+    group (values, "per-token-value"; the 32-channel grouping is the
+    workload's stated group size).
+    Returns (codes uint8 [T, C], scales fp16, zeros fp16).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    T, C = x.shape
+    codes = np.zeros((T, C), dtype=np.uint8)
+    if axis_groups == "channel":
+        scales = np.zeros(C, dtype=np.float16)
+        zeros = np.zeros(C, dtype=np.float16)
+        for c in range(C):
+            s, z = _int2_params(x[:, c])
+            scales[c], zeros[c] = s, z
+            codes[:, c] = _int2_codes(x[:, c], s, z)
+    elif axis_groups == "token32":
+        ng = C // 32
+        scales = np.zeros((T, ng), dtype=np.float16)
+        zeros = np.zeros((T, ng), dtype=np.float16)
+        for t in range(T):
+            for g in range(ng):
+                seg = x[t, 32 * g:32 * (g + 1)]
+                s, z = _int2_params(seg)
+                scales[t, g], zeros[t, g] = s, z
+                codes[t, 32 * g:32 * (g + 1)] = _int2_codes(seg, s, z)
+    else:
+        raise ValueError(axis_groups)
+    return codes, scales, zeros
+
+
+def int2_dequantize(codes, scales, zeros, axis_groups):
+    """``x_hat = code*scale + zero`` as a separate fp32 multiply and add."""
+    codes = np.asarray(codes).astype(np.float32)
+    T, C = codes.shape
+    if axis_groups == "channel":
+        s = np.asarray(scales, dtype=np.float32)[None, :]
+        z = np.asarray(zeros, dtype=np.float32)[None, :]
+    elif axis_groups == "token32":
+        s = np.repeat(np.asarray(scales, dtype=np.float32), 32, axis=1)
+        z = np.repeat(np.asarray(zeros, dtype=np.float32), 32, axis=1)
+    else:
+        raise ValueError(axis_groups)
+    prod = (codes * s).astype(np.float32)
+    return (prod + z).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Token-granular eviction step (InertiaKV, InertiaKV-Lazy, Score-Free)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class _Group:
+    """State of one (sequence, KV head) selection group, in slot order."""
+    K: np.ndarray          # [L, cap, d] float32 (exact copies of the inputs)
+    V: np.ndarray          # [L, cap, d]
+    pos: np.ndarray        # [cap] int64
+    m: np.ndarray          # [cap] float64 utility
+    n: int = 0
+
+
+@dataclass
+class TokenModeOracle:
+    """Per-(sequence, KV head) utility, selection and compaction.
+
+    One object holds any subset of a batch's sequences (sequences are
+    independent), so large batches can be checked on a sample.
+
+    * ``policy``: "ema" ([InertiaKV] Eq.4, layer-sequential per App. E) or
+      "cumulative" ([InertiaKV] Eq.3).
+    * ``refresh_interval`` r: scores are observed at t in R_r =
+      {t >= 1 : (t-1) mod r == 0} ([InertiaKV] §3.2 Eq.6); r = 1 is full
+      refresh.
+    * ``score_free``: observe only at t = 1, then freeze ([InertiaKV] §3.2
+      "Score-Free decoding").
+    * New tokens: on a non-refresh step the new token starts at the mean of
+      the existing utilities ([InertiaKV] App. E); on a refresh step it
+      starts at 0, like the prefill tokens (m_0 = 0, App. E), and is then
+      folded with its own attention mass (reading: the page states only the
+      non-refresh rule).
+    * Eviction happens once per step after all layers, whenever the group
+      holds more than ``budget`` tokens, including non-refresh steps with
+      the stale utility ([InertiaKV] App. E "Eviction on non-refresh steps").
+    """
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    budget: int
+    alpha_new: float
+    policy: str = "ema"
+    refresh_interval: int = 1
+    score_free: bool = False
+    n_sink: int = 0
+    n_recent: int = 0
+    capacity: int = 0
+    groups: dict = field(default_factory=dict)
+    prefill_len: dict = field(default_factory=dict)
+    last_G: dict = field(default_factory=dict)
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def prefill(self, seq, K, V):
+        """Store a sequence's prefill cache, positions 0..n-1, utility 0.
+
+        ``K``, ``V``: [L, Hkv, n, d].  [InertiaKV] App. E: m_0(i) = 0 for
+        every prefill position; compression acts only during decoding.
+        """
+        K = np.asarray(K, dtype=np.float32)
+        V = np.asarray(V, dtype=np.float32)
+        L, Hkv, n, d = K.shape
+        cap = max(self.capacity, n + 1)
+        for h in range(Hkv):
+            g = _Group(K=np.zeros((L, cap, d), np.float32),
+                       V=np.zeros((L, cap, d), np.float32),
+                       pos=np.zeros(cap, np.int64), m=np.zeros(cap, np.float64))
+            g.K[:, :n] = K[:, h]
+            g.V[:, :n] = V[:, h]
+            g.pos[:n] = np.arange(n)
+            g.n = n
+            self.groups[(seq, h)] = g
+        self.prefill_len[seq] = n
+
+    def is_refresh(self, t):
+        if self.score_free:
+            return t == 1
+        return (t - 1) % self.refresh_interval == 0
+
+    def _grow(self, g):
+        if g.n < g.K.shape[1]:
+            return
+        extra = max(64, g.K.shape[1] // 4)
+        pad = lambda a, fill=0: np.concatenate(
+            [a, np.full((a.shape[0], extra) + a.shape[2:], fill, a.dtype)], axis=1)
+        g.K, g.V = pad(g.K), pad(g.V)
+        g.pos = np.concatenate([g.pos, np.zeros(extra, np.int64)])
+        g.m = np.concatenate([g.m, np.zeros(extra, np.float64)])
+
+    def decode_step(self, t, q, k_new, v_new, seqs):
+        """Append, attend every layer, fold (on refresh steps).
+
+        ``q``: [L, len(seqs), Hq, d]; ``k_new``, ``v_new``: [L, len(seqs),
+        Hkv, d]; ``seqs`` lists the sequence ids in that batch order.
+        Returns ``out`` [L, len(seqs), Hq, d] in fp64.
+        """
+        q = np.asarray(q, dtype=np.float32)
+        k_new = np.asarray(k_new, dtype=np.float32)
+        v_new = np.asarray(v_new, dtype=np.float32)
+        refresh = self.is_refresh(t)
+        Hg = self.group_size
+        for bi, seq in enumerate(seqs):
+            for h in range(self.n_kv_heads):
+                g = self.groups[(seq, h)]
+                init = 0.0 if refresh else float(g.m[:g.n].mean())
+                self._grow(g)
+                g.K[:, g.n] = k_new[:, bi, h]
+                g.V[:, g.n] = v_new[:, bi, h]
+                g.pos[g.n] = self.prefill_len[seq] + t - 1
+                g.m[g.n] = init
+                g.n += 1
+        out = np.zeros((self.n_layers, len(seqs), self.n_q_heads, self.head_dim))
+        self.last_G = {}
+        for l in range(self.n_layers):
+            for bi, seq in enumerate(seqs):
+                for h in range(self.n_kv_heads):
+                    g = self.groups[(seq, h)]
+                    o, p, _ = decode_attention(q[l, bi, h * Hg:(h + 1) * Hg],
+                                               g.K[l, :g.n], g.V[l, :g.n])
+                    out[l, bi, h * Hg:(h + 1) * Hg] = o
+                    if refresh:
+                        G = group_mass(p)
+                        self.last_G[(l, seq, h)] = G
+                        g.m[:g.n] = layer_fold(g.m[:g.n], [G], self.alpha_new,
+                                               self.policy)
+        return out
+
+    def evict(self, budget=None):
+        """Select and compact every group that exceeds the budget."""
+        B = self.budget if budget is None else budget
+        for g in self.groups.values():
+            if g.n <= B:
+                continue
+            keep = select_keep(g.m[:g.n], g.pos[:g.n], B, self.n_sink, self.n_recent)
+            moves = hole_fill_moves(keep, B)
+            for src, dst in moves:
+                g.K[:, dst] = g.K[:, src]
+                g.V[:, dst] = g.V[:, src]
+                g.pos[dst] = g.pos[src]
+                g.m[dst] = g.m[src]
+            g.n = B
+
+    # -- views used by tests ------------------------------------------------
+    def scores(self, seq, h):
+        g = self.groups[(seq, h)]
+        return g.m[:g.n].copy()
+
+    def positions(self, seq, h):
+        g = self.groups[(seq, h)]
+        return g.pos[:g.n].copy()
