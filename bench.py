@@ -1,0 +1,172 @@
+"""Benchmark: steady decode steps of attention-scored KV eviction on one GPU.
+
+Workload: Llama-3.1-8B-shaped attention (32 layers, 32 query heads over 8 KV
+heads, head dim 128, bf16, batch 1), 32,768-token prefill, EMA alpha 0.05
+folded layer by layer, budget 3,277 tokens per KV head with 4 sinks and 32
+recent tokens protected.  One step = kvev_decode_step (append, split
+attention over all layers, probability pass + fold) + kvev_evict
+(radix select + compaction).  W warm-up steps (the first one evicts the
+prefill down to the budget) run untimed, then exactly K steps are timed
+between two device synchronisations; inputs are resident in HBM before the
+timed region.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: the path runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def algorithmic_bytes(w, n_tokens):
+    """Bytes a steady step must move (per the workload's shapes).
+
+    K/V of the retained cache read once in every layer, q read, fp32 output
+    written, appended K/V written, utility read + written, and the K/V of
+    one compaction move read + written in every layer.
+    """
+    L, Hkv, Hq, d = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    kv = L * Hkv * n_tokens * 2 * d * 2
+    q = L * Hq * d * 2
+    out = L * Hq * d * 4
+    app = L * Hkv * 2 * d * 2
+    state = Hkv * n_tokens * 4 * 2
+    move = L * Hkv * 2 * d * 2 * 2
+    return kv, kv + q + out + app + state + move
+
+
+def cpu_baseline(w, steps=3):
+    """Time the CPU oracle on a bounded sample: steady steps of ONE (sequence,
+    KV head) group at the workload's real shape (32 layers, budget+1 tokens,
+    4 query heads, d=128), scaled to the whole step (8 groups)."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    B = w.budget
+    o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=B,
+                            alpha_new=w.alpha_new, n_sink=w.n_sink, n_recent=w.n_recent,
+                            capacity=B + steps + 2)
+    K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0, heads=[0])
+    o.prefill(0, K.float().numpy(), V.float().numpy(), heads=[0])
+    ins = [w.step_inputs(t, seqs=[0]) for t in range(1, steps + 2)]
+    ins = [tuple(x.float().numpy() for x in s) for s in ins]
+    o.decode_step(1, *ins[0], [0])
+    o.evict()
+    t0 = time.perf_counter()
+    for t in range(2, steps + 2):
+        o.decode_step(t, *ins[t - 1], [0])
+        o.evict()
+    dt = time.perf_counter() - t0
+    per_group = dt / steps
+    full_step = per_group * w.n_kv_heads * w.batch
+    return {"value": 1.0 / full_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} steady steps of 1 of {w.n_kv_heads * w.batch} (sequence, KV head) "
+                      f"groups at {w.n_layers} layers x {B + 1} tokens, scaled x{w.n_kv_heads * w.batch}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="llama8b_32k")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_kv_cache_gqa_amd import kvev, synth
+
+    w = synth.workload(args.workload)
+    total = args.warmup + args.steps
+    dev = "cuda"
+    ctx = kvev.context_for(w, max_steps=total)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=dev)
+        ctx.prefill(b, K, V)
+        del K, V
+    inputs = [w.step_inputs(t, device=dev) for t in range(1, total + 1)]
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32,
+                      device=dev)
+    torch.cuda.synchronize()
+
+    for t in range(args.warmup):
+        ctx.decode_step(*inputs[t], out)
+        ctx.evict()
+    ctx.sync()
+    ctx.profile(True)
+    ctx.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        ctx.decode_step(*inputs[t], out)
+        ctx.evict()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ctx.sync()
+    prof = {k: ctx.profile_read(k) for k in ("append", "attn", "combine", "fold", "select", "move")}
+    ctx.close()
+
+    n_tok = w.budget + 1
+    kv_bytes, step_bytes = algorithmic_bytes(w, n_tok)
+    ms_step = dt * 1e3 / args.steps
+    steps_s = args.steps / dt
+    attn_ms, attn_n = prof["attn"]
+    attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
+    attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
+    policy_ms = sum(prof[k][0] for k in ("fold", "select", "move")) / args.steps
+    result = {
+        "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded outlier-channel / heavy-key generator)",
+        "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "batch": w.batch,
+                   "prefill": w.prefill_lens[0], "budget": w.budget, "n_sink": w.n_sink,
+                   "n_recent": w.n_recent, "alpha_new": w.alpha_new},
+        "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
+        "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,
+        "kernel_avg_us": {k: round(v[0] / max(v[1], 1) * 1e3, 3) for k, v in prof.items() if v[1]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 1) if attn_gbps else None,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
+            "traffic": None,
+            "kernel": "attn_split_kernel",
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

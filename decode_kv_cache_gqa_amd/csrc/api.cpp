@@ -1,0 +1,485 @@
+// Host side of the kvev C ABI: validation, allocation, step sequencing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kvev_internal.h"
+
+using namespace kvev;
+
+namespace {
+
+std::string g_create_error;
+
+kvev_status fail(kvev_ctx* c, kvev_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+kvev_status hip_fail(kvev_ctx* c, hipError_t e, const char* where) {
+  c->sticky = true;
+  c->err = std::string(where) + ": " + hipGetErrorString(e);
+  return KVEV_EHIP;
+}
+
+#define KVEV_HIP(c, expr)                                   \
+  do {                                                      \
+    hipError_t e_ = (expr);                                 \
+    if (e_ != hipSuccess) return hip_fail((c), e_, #expr);  \
+  } while (0)
+
+#define KVEV_LIVE(c)                                                          \
+  do {                                                                        \
+    if (!(c)) return KVEV_EINVAL;                                             \
+    if ((c)->sticky) return KVEV_ESTATE;                                      \
+  } while (0)
+
+template <typename T>
+hipError_t dalloc(T** p, size_t count) {
+  *p = nullptr;
+  if (count == 0) return hipSuccess;
+  return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T));
+}
+
+// Profiling: events around named launches on the context's stream.
+struct ProfScope {
+  kvev_ctx* c;
+  const char* name;
+  hipEvent_t a = nullptr;
+  ProfScope(kvev_ctx* c_, const char* n) : c(c_), name(n) {
+    if (!c->prof.enabled) return;
+    a = take_event();
+    hipEventRecord(a, c->stream);
+  }
+  hipEvent_t take_event() {
+    if (!c->prof.pool.empty()) {
+      hipEvent_t e = c->prof.pool.back();
+      c->prof.pool.pop_back();
+      return e;
+    }
+    hipEvent_t e;
+    hipEventCreate(&e);
+    return e;
+  }
+  ~ProfScope() {
+    if (!c->prof.enabled) return;
+    hipEvent_t b = take_event();
+    hipEventRecord(b, c->stream);
+    c->prof.pending.push_back({name, a, b});
+  }
+};
+
+void prof_drain(kvev_ctx* c) {
+  for (auto& r : c->prof.pending) {
+    hipEventSynchronize(r.b);
+    float ms = 0.f;
+    hipEventElapsedTime(&ms, r.a, r.b);
+    bool found = false;
+    for (auto& t : c->prof.totals)
+      if (t.first == r.name) {
+        t.second.first += ms;
+        t.second.second += 1;
+        found = true;
+      }
+    if (!found) c->prof.totals.push_back({r.name, {ms, 1}});
+    c->prof.pool.push_back(r.a);
+    c->prof.pool.push_back(r.b);
+  }
+  c->prof.pending.clear();
+}
+
+void free_all(kvev_ctx* c) {
+  auto& d = c->d;
+  void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
+                  d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag};
+  for (void* p : ptrs)
+    if (p) hipFree(p);
+  d = DevState{};
+  for (auto& r : c->prof.pending) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (auto e : c->prof.pool) hipEventDestroy(e);
+  c->prof.pending.clear();
+  c->prof.pool.clear();
+}
+
+// Allocate pages so that group g can hold `n_slots` slots; collects ptab updates.
+bool ensure_pages(kvev_ctx* c, int g, int64_t n_slots, std::vector<int>& upd) {
+  const int need = static_cast<int>((n_slots + c->PT - 1) / c->PT);
+  auto& pg = c->pages[g];
+  while (static_cast<int>(pg.size()) < need) {
+    if (c->free_pages.empty()) return false;
+    const int p = c->free_pages.back();
+    c->free_pages.pop_back();
+    upd.push_back(g * c->maxpages + static_cast<int>(pg.size()));
+    upd.push_back(p);
+    pg.push_back(p);
+  }
+  return true;
+}
+
+void release_pages(kvev_ctx* c, int g, int64_t n_slots) {
+  const int keep = static_cast<int>((n_slots + c->PT - 1) / c->PT);
+  auto& pg = c->pages[g];
+  while (static_cast<int>(pg.size()) > keep) {
+    c->free_pages.push_back(pg.back());
+    pg.pop_back();
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+void kvev_config_init(kvev_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->page_tokens = kPageTokens;
+  cfg->policy = KVEV_EMA;
+  cfg->alpha_new = 0.05f;
+  cfg->refresh_interval = 1;
+  cfg->dtype = KVEV_BF16;
+}
+
+kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out) {
+  if (!cfg || !out) {
+    g_create_error = "null argument";
+    return KVEV_EINVAL;
+  }
+  *out = nullptr;
+  const kvev_config& f = *cfg;
+  auto bad = [&](const char* m) {
+    g_create_error = m;
+    return KVEV_EINVAL;
+  };
+  if (f.n_layers < 1 || f.n_q_heads < 1 || f.n_kv_heads < 1 || f.batch < 1)
+    return bad("n_layers, n_q_heads, n_kv_heads and batch must be >= 1");
+  if (f.n_q_heads % f.n_kv_heads != 0) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (f.n_q_heads / f.n_kv_heads != 4) return bad("query group size must be 4");
+  if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
+  if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
+  if (f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE) return bad("unsupported policy");
+  if (f.policy == KVEV_EMA && !(f.alpha_new > 0.f && f.alpha_new <= 1.f))
+    return bad("alpha_new must be in (0, 1]");
+  if (f.refresh_interval < 1) return bad("refresh_interval must be >= 1");
+  if (f.n_sink < 0 || f.n_recent < 0) return bad("n_sink and n_recent must be >= 0");
+  if (f.budget < 1) return bad("budget must be >= 1");
+  if (f.n_sink + f.n_recent > f.budget) return bad("n_sink + n_recent exceeds the budget");
+  if (f.max_tokens < 2 || f.max_tokens > (1ll << 30)) return bad("max_tokens out of range");
+  if (f.n_layers > 256) return bad("n_layers must be <= 256");
+
+  kvev_ctx* c = new (std::nothrow) kvev_ctx();
+  if (!c) return bad("out of host memory");
+  c->cfg = f;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  hipGetDevice(&c->device);
+  c->G = f.batch * f.n_kv_heads;
+  c->HG = f.n_q_heads / f.n_kv_heads;
+  c->cap = f.max_tokens;
+  c->maxpages = static_cast<int>((c->cap + c->PT - 1) / c->PT);
+  c->P = static_cast<int64_t>(c->G) * c->maxpages;
+  c->max_splits = static_cast<int>((c->cap + kAttnChunk - 1) / kAttnChunk);
+  c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
+  c->count.assign(c->G, 0);
+  c->prefilled.assign(f.batch, 0);
+  c->pages.assign(c->G, {});
+  c->free_pages.resize(c->P);
+  for (int64_t i = 0; i < c->P; ++i) c->free_pages[i] = static_cast<int>(c->P - 1 - i);
+
+  auto& d = c->d;
+  const int64_t L = f.n_layers, D = f.head_dim, G = c->G, HG = c->HG;
+  const size_t pool_bytes = static_cast<size_t>(L) * c->P * c->PT * D * c->elem;
+  hipError_t e = hipSuccess;
+  auto A = [&](hipError_t r) {
+    if (e == hipSuccess && r != hipSuccess) e = r;
+  };
+  A(hipMalloc(&d.kpool, pool_bytes));
+  A(hipMalloc(&d.vpool, pool_bytes));
+  A(dalloc(&d.ptab, static_cast<size_t>(G) * c->maxpages));
+  A(dalloc(&d.pos, static_cast<size_t>(G) * c->cap));
+  A(dalloc(&d.score, static_cast<size_t>(G) * c->cap));
+  A(dalloc(&d.count, G));
+  A(dalloc(&d.nextpos, G));
+  A(dalloc(&d.logits, static_cast<size_t>(G) * L * c->cap * HG));
+  A(dalloc(&d.part_ml, static_cast<size_t>(L) * G * c->max_splits * HG * 2));
+  A(dalloc(&d.part_o, static_cast<size_t>(L) * G * c->max_splits * HG * D));
+  A(dalloc(&d.ml, static_cast<size_t>(L) * G * HG * 2));
+  A(dalloc(&d.mv_src, static_cast<size_t>(G) * c->cap));
+  A(dalloc(&d.mv_dst, static_cast<size_t>(G) * c->cap));
+  A(dalloc(&d.nmoves, G));
+  A(dalloc(&d.errflag, 1));
+  if (e != hipSuccess) {
+    g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
+    free_all(c);
+    delete c;
+    return e == hipErrorOutOfMemory ? KVEV_ENOMEM : KVEV_EHIP;
+  }
+  // zero everything so unused slots hold finite values
+  A(hipMemsetAsync(d.kpool, 0, pool_bytes, c->stream));
+  A(hipMemsetAsync(d.vpool, 0, pool_bytes, c->stream));
+  A(hipMemsetAsync(d.ptab, 0, sizeof(int) * G * c->maxpages, c->stream));
+  A(hipMemsetAsync(d.score, 0, sizeof(float) * G * c->cap, c->stream));
+  A(hipMemsetAsync(d.pos, 0, sizeof(int) * G * c->cap, c->stream));
+  A(hipMemsetAsync(d.count, 0, sizeof(int) * G, c->stream));
+  A(hipMemsetAsync(d.nextpos, 0, sizeof(int) * G, c->stream));
+  A(hipMemsetAsync(d.nmoves, 0, sizeof(int) * G, c->stream));
+  A(hipMemsetAsync(d.errflag, 0, sizeof(int), c->stream));
+  A(hipMemsetAsync(d.mv_src, 0, sizeof(int) * G * c->cap, c->stream));
+  A(hipMemsetAsync(d.mv_dst, 0, sizeof(int) * G * c->cap, c->stream));
+  A(hipStreamSynchronize(c->stream));
+  if (e != hipSuccess) {
+    g_create_error = std::string("device initialisation failed: ") + hipGetErrorString(e);
+    free_all(c);
+    delete c;
+    return KVEV_EHIP;
+  }
+  *out = c;
+  return KVEV_OK;
+}
+
+kvev_status kvev_destroy(kvev_ctx* c) {
+  if (!c) return KVEV_OK;
+  hipStreamSynchronize(c->stream);
+  free_all(c);
+  delete c;
+  return KVEV_OK;
+}
+
+kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v, int64_t n) {
+  KVEV_LIVE(c);
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (!k || !v) return fail(c, KVEV_EINVAL, "null k or v");
+  if (c->t > 0) return fail(c, KVEV_ESTATE, "prefill after the first decode step");
+  if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
+  const int Hkv = c->cfg.n_kv_heads;
+  std::vector<int> upd;
+  for (int h = 0; h < Hkv; ++h) {
+    const int g = seq * Hkv + h;
+    release_pages(c, g, 0);
+  }
+  for (int h = 0; h < Hkv; ++h) {
+    const int g = seq * Hkv + h;
+    if (!ensure_pages(c, g, n, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
+  }
+  if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
+  KVEV_HIP(c, launch_prefill_scatter(c, seq, k, v, n));
+  // positions 0..n-1, utilities 0, count n, next position n
+  std::vector<int> posv(n);
+  for (int64_t i = 0; i < n; ++i) posv[i] = static_cast<int>(i);
+  for (int h = 0; h < Hkv; ++h) {
+    const int g = seq * Hkv + h;
+    KVEV_HIP(c, hipMemcpyAsync(c->d.pos + static_cast<int64_t>(g) * c->cap, posv.data(),
+                               sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+    KVEV_HIP(c, hipMemsetAsync(c->d.score + static_cast<int64_t>(g) * c->cap, 0,
+                               sizeof(float) * n, c->stream));
+    const int cnt = static_cast<int>(n);
+    KVEV_HIP(c, hipMemcpyAsync(c->d.count + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
+    KVEV_HIP(c, hipMemcpyAsync(c->d.nextpos + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
+    KVEV_HIP(c, hipStreamSynchronize(c->stream));  // host buffers above are stack-local
+    c->count[g] = n;
+  }
+  c->prefilled[seq] = 1;
+  return KVEV_OK;
+}
+
+kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                             float* out) {
+  KVEV_LIVE(c);
+  if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
+  for (int b = 0; b < c->cfg.batch; ++b)
+    if (!c->prefilled[b]) return fail(c, KVEV_ESTATE, "a sequence has no prefill");
+  const int64_t t = c->t + 1;
+  const bool refresh = c->cfg.score_free ? (t == 1) : ((t - 1) % c->cfg.refresh_interval == 0);
+  auto& upd = c->ptab_upd;
+  upd.clear();
+  int64_t n_max = 0;
+  for (int g = 0; g < c->G; ++g) {
+    if (c->count[g] + 1 > c->cap) return fail(c, KVEV_ESTATE, "slot capacity exhausted");
+    if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
+    n_max = std::max(n_max, c->count[g] + 1);
+  }
+  if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
+  {
+    ProfScope p(c, "append");
+    KVEV_HIP(c, launch_append(c, k_new, v_new, refresh ? 1 : 0));
+  }
+  {
+    ProfScope p(c, "attn");
+    KVEV_HIP(c, launch_attention(c, q, static_cast<int>(n_max), refresh ? 1 : 0));
+  }
+  {
+    ProfScope p(c, "combine");
+    KVEV_HIP(c, launch_combine(c, out));
+  }
+  if (refresh) {
+    ProfScope p(c, "fold");
+    KVEV_HIP(c, launch_fold(c, static_cast<int>(n_max)));
+  }
+  for (int g = 0; g < c->G; ++g) c->count[g] += 1;
+  c->t = t;
+  return KVEV_OK;
+}
+
+kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
+  KVEV_LIVE(c);
+  const int64_t B = budget > 0 ? budget : c->cfg.budget;
+  if (B < c->cfg.n_sink + c->cfg.n_recent || B < 1)
+    return fail(c, KVEV_EINVAL, "budget below the protected token count");
+  if (B > (1ll << 30)) return fail(c, KVEV_EINVAL, "budget out of range");
+  int64_t max_moves = 0, n_max = 0;
+  bool any = false;
+  for (int g = 0; g < c->G; ++g) {
+    if (c->count[g] > B) {
+      any = true;
+      max_moves = std::max(max_moves, std::min(B, c->count[g] - B));
+      n_max = std::max(n_max, c->count[g]);
+    }
+  }
+  if (!any) return KVEV_OK;
+  {
+    ProfScope p(c, "select");
+    KVEV_HIP(c, launch_select(c, B, static_cast<int>(n_max)));
+  }
+  if (max_moves > 0) {
+    ProfScope p(c, "move");
+    KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
+  }
+  for (int g = 0; g < c->G; ++g) {
+    if (c->count[g] > B) c->count[g] = B;
+    release_pages(c, g, c->count[g]);
+  }
+  return KVEV_OK;
+}
+
+static kvev_status group_index(kvev_ctx* c, int32_t seq, int32_t h, int* g) {
+  if (seq < 0 || seq >= c->cfg.batch || h < 0 || h >= c->cfg.n_kv_heads)
+    return fail(c, KVEV_ERANGE, "group index out of range");
+  *g = seq * c->cfg.n_kv_heads + h;
+  return KVEV_OK;
+}
+
+kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t cap,
+                        int64_t* n_written) {
+  KVEV_LIVE(c);
+  int g;
+  if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  const int64_t n = c->count[g];
+  if (n_written) *n_written = n;
+  if (!dst || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
+  KVEV_HIP(c, hipMemcpyAsync(dst, c->d.score + static_cast<int64_t>(g) * c->cap, sizeof(float) * n,
+                             hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  return KVEV_OK;
+}
+
+kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* positions, int64_t cap,
+                          int64_t* n_out) {
+  KVEV_LIVE(c);
+  int g;
+  if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  const int64_t n = c->count[g];
+  if (n_out) *n_out = n;
+  if (!positions || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
+  KVEV_HIP(c, hipMemcpyAsync(positions, c->d.pos + static_cast<int64_t>(g) * c->cap,
+                             sizeof(int) * n, hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  return KVEV_OK;
+}
+
+kvev_status kvev_export_kv(kvev_ctx* c, int32_t seq, int32_t h, void* k_out, void* v_out,
+                           int64_t cap, int64_t* n_out) {
+  KVEV_LIVE(c);
+  int g;
+  if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  const int64_t n = c->count[g];
+  if (n_out) *n_out = n;
+  if (!k_out || !v_out || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
+  KVEV_HIP(c, launch_export(c, g, k_out, v_out, n, cap));
+  return KVEV_OK;
+}
+
+kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
+                              const int32_t* positions, const float* scores, const void* k,
+                              const void* v) {
+  KVEV_LIVE(c);
+  int g;
+  if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  if (!positions || !scores || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
+  if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_ERANGE, "n out of range");
+  int maxp = 0;
+  for (int64_t i = 0; i < n; ++i) maxp = std::max(maxp, positions[i]);
+  std::vector<int> upd;
+  if (!ensure_pages(c, g, n, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
+  if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
+  KVEV_HIP(c, launch_import(c, g, k, v, n));
+  KVEV_HIP(c, hipMemcpyAsync(c->d.pos + static_cast<int64_t>(g) * c->cap, positions,
+                             sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(c->d.score + static_cast<int64_t>(g) * c->cap, scores,
+                             sizeof(float) * n, hipMemcpyHostToDevice, c->stream));
+  const int cnt = static_cast<int>(n);
+  KVEV_HIP(c, hipMemcpyAsync(c->d.count + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  release_pages(c, g, n);
+  c->count[g] = n;
+  return KVEV_OK;
+}
+
+kvev_status kvev_sync(kvev_ctx* c) {
+  KVEV_LIVE(c);
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  KVEV_HIP(c, hipGetLastError());
+  int flag = 0;
+  KVEV_HIP(c, hipMemcpy(&flag, c->d.errflag, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag) {
+    c->sticky = true;
+    c->err = "device consistency check failed (flag " + std::to_string(flag) + ")";
+    return KVEV_ESTATE;
+  }
+  return KVEV_OK;
+}
+
+int64_t kvev_step_index(const kvev_ctx* c) { return c ? c->t : -1; }
+
+kvev_status kvev_profile_enable(kvev_ctx* c, int32_t enable) {
+  KVEV_LIVE(c);
+  c->prof.enabled = enable != 0;
+  return KVEV_OK;
+}
+
+kvev_status kvev_profile_reset(kvev_ctx* c) {
+  KVEV_LIVE(c);
+  prof_drain(c);
+  c->prof.totals.clear();
+  return KVEV_OK;
+}
+
+kvev_status kvev_profile_read(kvev_ctx* c, const char* kernel, double* total_ms,
+                              int64_t* launches) {
+  KVEV_LIVE(c);
+  if (!kernel) return fail(c, KVEV_EINVAL, "null kernel name");
+  prof_drain(c);
+  double ms = 0;
+  long long nl = 0;
+  for (auto& t : c->prof.totals)
+    if (t.first == kernel) {
+      ms = t.second.first;
+      nl = t.second.second;
+    }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = nl;
+  return KVEV_OK;
+}
+
+const char* kvev_last_error(const kvev_ctx* c) {
+  if (!c) return g_create_error.c_str();
+  return c->err.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal state of a kvev context and the kernel launchers (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/kvev.h"
+
+namespace kvev {
+
+constexpr int kPageTokens = 16;
+constexpr int kAttnChunk = 512;   // tokens per attention split
+constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
+
+// Device buffers of one context.  Groups are (sequence, KV head) pairs,
+// g = seq * Hkv + kv_head; slots of a group are its cached tokens in order.
+struct DevState {
+  void* kpool = nullptr;   // [L][P][PT][D] cfg.dtype
+  void* vpool = nullptr;
+  int* ptab = nullptr;     // [G][maxpages] physical page of each logical page
+  int* pos = nullptr;      // [G][cap] position of each slot
+  float* score = nullptr;  // [G][cap] utility of each slot
+  int* count = nullptr;    // [G] tokens in the group
+  int* nextpos = nullptr;  // [G] position the next appended token takes
+  float* logits = nullptr; // [G][L][cap][HG] fp32 logits of the last step
+  float* part_ml = nullptr;// [L][G][S][HG][2] per-split (max, sum)
+  float* part_o = nullptr; // [L][G][S][HG][D] per-split unnormalised output
+  float* ml = nullptr;     // [L][G][HG][2] global (max, sum)
+  int* mv_src = nullptr;   // [G][cap] compaction moves
+  int* mv_dst = nullptr;   // [G][cap]
+  int* nmoves = nullptr;   // [G]
+  int* errflag = nullptr;  // [1] device-side consistency failures (bit mask)
+};
+
+struct Launch;  // shape parameters shared by the launchers
+
+struct Profiler {
+  bool enabled = false;
+  struct Rec {
+    std::string name;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<std::pair<std::string, std::pair<double, long long>>> totals;
+  std::vector<hipEvent_t> pool;
+};
+
+}  // namespace kvev
+
+struct kvev_ctx {
+  kvev_config cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int G = 0, HG = 0, PT = kvev::kPageTokens, maxpages = 0;
+  int64_t cap = 0, P = 0;
+  int max_splits = 0;
+  size_t elem = 0;
+  kvev::DevState d;
+  // host mirrors (kept exact: every count change is deterministic)
+  std::vector<int64_t> count;
+  std::vector<int> prefilled;               // per sequence
+  std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
+  std::vector<int> free_pages;
+  int64_t t = 0;
+  bool sticky = false;
+  std::string err;
+  kvev::Profiler prof;
+  std::vector<int> ptab_upd;                // scratch for page-table updates
+};
+
+namespace kvev {
+
+// Launchers (defined in the .hip translation units).  All are stream-ordered.
+hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
+hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
+hipError_t launch_append(kvev_ctx* c, const void* k_new, const void* v_new, int refresh);
+hipError_t launch_attention(kvev_ctx* c, const void* q, int n_max, int write_logits);
+hipError_t launch_combine(kvev_ctx* c, float* out);
+hipError_t launch_fold(kvev_ctx* c, int n_max);
+hipError_t launch_select(kvev_ctx* c, int64_t budget, int n_max);
+hipError_t launch_moves(kvev_ctx* c, int max_moves);
+hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);
+hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n);
+
+}  // namespace kvev

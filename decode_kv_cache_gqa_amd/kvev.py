@@ -1,0 +1,233 @@
+"""ctypes binding of libkvev.so: argument marshalling only.
+
+Every step of the eviction path runs in the library's HIP kernels; this
+module checks tensor shapes, dtypes and devices on the host (so the C side
+never reads out of bounds), passes raw pointers and turns status codes into
+exceptions.  PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvev.so")
+
+OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+EMA, CUMULATIVE = 0, 1
+_STATUS = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EHIP: "EHIP", ESTATE: "ESTATE", ERANGE: "ERANGE"}
+
+
+class KvevError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"kvev {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
+        ("policy", ctypes.c_int32), ("alpha_new", ctypes.c_float),
+        ("refresh_interval", ctypes.c_int32), ("score_free", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+        ("budget", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+_SIGS = {
+    "kvev_config_init": (None, [ctypes.POINTER(Config)]),
+    "kvev_create": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
+    "kvev_destroy": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvev_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
+    "kvev_decode_step": (ctypes.c_int, [ctypes.c_void_p] * 5),
+    "kvev_evict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "kvev_scores": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_retained": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_export_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_import_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
+    "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvev_profile_reset": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvev_profile_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
+}
+
+
+def lib():
+    """Load libkvev.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run decode_kv_cache_gqa_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def config_init():
+    c = Config()
+    lib().kvev_config_init(ctypes.byref(c))
+    return c
+
+
+def make_config(**kw):
+    c = config_init()
+    for k, v in kw.items():
+        if not hasattr(c, k):
+            raise KeyError(k)
+        setattr(c, k, v)
+    return c
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor", device=True):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Context:
+    """One library context (cache, scores, page tables) on the current device."""
+
+    def __init__(self, cfg: Config, stream=None):
+        import torch
+        self.cfg = cfg
+        self._h = ctypes.c_void_p()
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        st = lib().kvev_create(ctypes.byref(cfg), ctypes.c_void_p(self.stream.cuda_stream),
+                               ctypes.byref(self._h))
+        if st != OK:
+            raise KvevError(st, lib().kvev_last_error(None).decode())
+        self.dtype = torch.float32 if cfg.dtype == F32 else torch.bfloat16
+
+    # -- helpers ---------------------------------------------------------------
+    def _check(self, st):
+        if st != OK:
+            raise KvevError(st, lib().kvev_last_error(self._h).decode())
+
+    def close(self):
+        if self._h:
+            lib().kvev_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def step_index(self):
+        return lib().kvev_step_index(self._h)
+
+    # -- C ABI ---------------------------------------------------------------
+    def prefill(self, seq, k, v):
+        c = self.cfg
+        n = k.shape[2]
+        shape = (c.n_layers, c.n_kv_heads, n, c.head_dim)
+        self._check(lib().kvev_prefill(self._h, seq, _ptr(k, self.dtype, shape, "k"),
+                                       _ptr(v, self.dtype, shape, "v"), n))
+
+    def decode_step(self, q, k_new, v_new, out):
+        import torch
+        c = self.cfg
+        qs = (c.n_layers, c.batch, c.n_q_heads, c.head_dim)
+        ks = (c.n_layers, c.batch, c.n_kv_heads, c.head_dim)
+        self._check(lib().kvev_decode_step(
+            self._h, _ptr(q, self.dtype, qs, "q"), _ptr(k_new, self.dtype, ks, "k_new"),
+            _ptr(v_new, self.dtype, ks, "v_new"), _ptr(out, torch.float32, qs, "out")))
+
+    def evict(self, budget=0):
+        self._check(lib().kvev_evict(self._h, int(budget)))
+
+    def scores(self, seq, kv_head):
+        n = ctypes.c_int64()
+        buf = np.zeros(self.cfg.max_tokens, np.float32)
+        self._check(lib().kvev_scores(self._h, seq, kv_head, buf.ctypes.data_as(ctypes.c_void_p),
+                                      buf.size, ctypes.byref(n)))
+        return buf[: n.value].copy()
+
+    def retained(self, seq, kv_head):
+        n = ctypes.c_int64()
+        buf = np.zeros(self.cfg.max_tokens, np.int32)
+        self._check(lib().kvev_retained(self._h, seq, kv_head, buf.ctypes.data_as(ctypes.c_void_p),
+                                        buf.size, ctypes.byref(n)))
+        return buf[: n.value].copy()
+
+    def export_kv(self, seq, kv_head):
+        import torch
+        c = self.cfg
+        cap = c.max_tokens
+        k = torch.empty((c.n_layers, cap, c.head_dim), dtype=self.dtype, device="cuda")
+        v = torch.empty_like(k)
+        n = ctypes.c_int64()
+        self._check(lib().kvev_export_kv(self._h, seq, kv_head, _ptr(k), _ptr(v), cap, ctypes.byref(n)))
+        self.sync()
+        return k[:, : n.value].clone(), v[:, : n.value].clone()
+
+    def import_group(self, seq, kv_head, positions, scores, k, v):
+        c = self.cfg
+        positions = np.ascontiguousarray(positions, dtype=np.int32)
+        scores = np.ascontiguousarray(scores, dtype=np.float32)
+        n = positions.shape[0]
+        if scores.shape[0] != n:
+            raise ValueError("positions and scores differ in length")
+        shape = (c.n_layers, n, c.head_dim)
+        self._check(lib().kvev_import_group(
+            self._h, seq, kv_head, n, positions.ctypes.data_as(ctypes.c_void_p),
+            scores.ctypes.data_as(ctypes.c_void_p), _ptr(k, self.dtype, shape, "k"),
+            _ptr(v, self.dtype, shape, "v")))
+
+    def sync(self):
+        self._check(lib().kvev_sync(self._h))
+
+    def profile(self, enable=True):
+        self._check(lib().kvev_profile_enable(self._h, 1 if enable else 0))
+
+    def profile_reset(self):
+        self._check(lib().kvev_profile_reset(self._h))
+
+    def profile_read(self, kernel):
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        self._check(lib().kvev_profile_read(self._h, kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+
+def context_for(w, max_steps=None, budget=None, stream=None):
+    """A context configured for a synth.Workload (token-granular policies)."""
+    steps = w.steps if max_steps is None else max_steps
+    cfg = make_config(
+        n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+        head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,
+        max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16,
+        policy=CUMULATIVE if w.policy == "cumulative" else EMA, alpha_new=w.alpha_new,
+        refresh_interval=w.refresh_interval, score_free=1 if w.score_free else 0,
+        n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget)
+    return Context(cfg, stream=stream)

@@ -1,0 +1,178 @@
+/*
+ * kvev.h -- C ABI of the attention-scored KV-cache eviction library (gfx950).
+ *
+ * One decode step of the method is kvev_decode_step() followed by
+ * kvev_evict(): at each step, given the query, the cached K/V and a fixed
+ * budget, the library decides which cached entries are retained.  This is the
+ * problem statement of "What Matters for Aggressive Decoding-Time KV
+ * Eviction?" (section 1 and section 3: retain or permanently evict under a
+ * fixed budget B) and of "MemDecay" (section III-A, objective (1)).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are HIP device pointers owned by the caller and
+ *     read or written in stream order on the context's stream; the caller
+ *     keeps them alive until that stream work completes.  Pointers named
+ *     "host" are ordinary host memory, read or written before the call
+ *     returns (such calls synchronise the stream).
+ *   - The library owns all cache memory (allocated by kvev_create); the step
+ *     path itself allocates nothing.
+ *   - Every call returns a kvev_status.  No exception crosses the ABI.  A HIP
+ *     runtime failure returns KVEV_EHIP and makes the context sticky: every
+ *     later call except kvev_last_error / kvev_destroy returns KVEV_ESTATE.
+ *     kvev_last_error() describes the last failure.
+ *   - A context is bound to one HIP stream and is not thread safe.
+ *   - Element dtype of q / k / v inputs is cfg.dtype (fp32 or bf16, dense,
+ *     row-major, head_dim innermost); attention outputs are always fp32.
+ */
+#ifndef KVEV_H
+#define KVEV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvev_ctx kvev_ctx;
+
+typedef enum {
+  KVEV_OK = 0,
+  KVEV_EINVAL = -1, /* bad argument, shape or configuration */
+  KVEV_ENOMEM = -2, /* device allocation failed or page pool exhausted */
+  KVEV_EHIP = -3,   /* HIP runtime error (context becomes sticky) */
+  KVEV_ESTATE = -4, /* call not valid in the current state, or sticky error */
+  KVEV_ERANGE = -5  /* host buffer too small / index out of range */
+} kvev_status;
+
+typedef enum { KVEV_F32 = 0, KVEV_BF16 = 1 } kvev_dtype;
+
+/* Score aggregation rule.
+ *  EMA:        score <- alpha_new*mass + (1-alpha_new)*score, applied once per
+ *              layer in ascending layer order ("What Matters ...", section
+ *              3.1 Eq.4 and appendix E "Layer scoring").
+ *  CUMULATIVE: score <- score + mass per layer (same page, Eq.3).          */
+typedef enum { KVEV_EMA = 0, KVEV_CUMULATIVE = 1 } kvev_policy;
+
+typedef struct {
+  int32_t n_layers;         /* L */
+  int32_t n_q_heads;        /* Hq (multiple of n_kv_heads) */
+  int32_t n_kv_heads;       /* Hkv */
+  int32_t head_dim;         /* d: 64 or 128 */
+  int32_t batch;            /* sequences stepped together */
+  int32_t dtype;            /* kvev_dtype of q, k, v and the cache */
+  int64_t max_tokens;       /* per-sequence slot capacity (>= prefill + steps) */
+  int32_t page_tokens;      /* tokens per cache page; must be 16 */
+  int32_t policy;           /* kvev_policy */
+  float alpha_new;          /* EMA weight on the new observation, (0, 1] */
+  int32_t refresh_interval; /* r >= 1: scores observed at t with (t-1) % r == 0
+                               ("What Matters ...", section 3.2 Eq.6) */
+  int32_t score_free;       /* 1: observe only at t == 1, then freeze
+                               (same page, section 3.2 "Score-Free") */
+  int32_t n_sink;           /* positions < n_sink are never evicted */
+  int32_t n_recent;         /* the n_recent newest positions are never evicted */
+  int64_t budget;           /* retained tokens per (sequence, KV head) */
+} kvev_config;
+
+/* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
+ * refresh_interval 1, no protection; shape fields zero. */
+void kvev_config_init(kvev_config* cfg);
+
+/* Validate *cfg, allocate the page pool and all per-step state on the
+ * current HIP device, bind `hip_stream` (a hipStream_t; NULL = default
+ * stream).  On success *out owns everything until kvev_destroy.
+ * Errors: KVEV_EINVAL (bad config: d not 64/128, Hq % Hkv != 0, budget < 1,
+ * n_sink + n_recent > budget, page_tokens != 16, ...), KVEV_ENOMEM, KVEV_EHIP. */
+kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out);
+
+/* Free everything the context owns (synchronises its stream).  NULL is a no-op. */
+kvev_status kvev_destroy(kvev_ctx* ctx);
+
+/* Load the prefill cache of sequence `seq` (0 <= seq < batch): device k, v
+ * laid out [n_layers][n_kv_heads][n_tokens][head_dim].  Positions are
+ * 0..n_tokens-1 and every utility starts at 0 ("What Matters ...", appendix
+ * E "Momentum initialization").  Must be called for every sequence before
+ * the first decode step, and not after it.  Errors: KVEV_EINVAL (n_tokens < 1
+ * or + decode headroom > max_tokens), KVEV_ESTATE, KVEV_ENOMEM (pool). */
+kvev_status kvev_prefill(kvev_ctx* ctx, int32_t seq, const void* k, const void* v,
+                         int64_t n_tokens);
+
+/* Decode step t (counted by the context from 1): append k_new/v_new at the
+ * next position of every (layer, sequence, KV head); run GQA decode
+ * attention of every layer over the group's cached tokens; write the
+ * attention output; and, on an observation step, fold each KV head's
+ * per-token softmax mass summed over its query group into the utility,
+ * layer by layer.  On a non-observation step the new token's utility starts
+ * at the mean of the group's existing utilities and nothing else changes
+ * ("What Matters ...", appendix E "New token insertion").  On an observation
+ * step the new token starts at 0 and is folded with its own mass.
+ *   q      device [n_layers][batch][n_q_heads][head_dim]   (cfg.dtype)
+ *   k_new  device [n_layers][batch][n_kv_heads][head_dim]  (cfg.dtype)
+ *   v_new  device [n_layers][batch][n_kv_heads][head_dim]  (cfg.dtype)
+ *   out    device [n_layers][batch][n_q_heads][head_dim]   fp32, written
+ * Logits use (q.k)/sqrt(head_dim) in fp32 ("QEvict" review, section 4.1,
+ * (Attention)).  Errors: KVEV_ESTATE (a sequence has no prefill, or the
+ * slot capacity is exhausted), KVEV_EHIP. */
+kvev_status kvev_decode_step(kvev_ctx* ctx, const void* q, const void* k_new,
+                             const void* v_new, float* out);
+
+/* Enforce the budget in every (sequence, KV head) group holding more than
+ * `budget` tokens (budget <= 0: cfg.budget): keep the protected tokens (sinks
+ * and the n_recent newest) and the top (budget - |protected|) of the rest by
+ * (utility, position), larger kept; compact the survivors into slots
+ * [0, budget) of every layer's K and V (holes below the budget, ascending,
+ * take the kept slots at or above it, ascending).  A group within budget is
+ * left untouched.  Eviction is irreversible ("What Matters ...", section 3.1;
+ * "MemDecay", section III-A (1) with the forced set).
+ * Errors: KVEV_EINVAL (budget < n_sink + n_recent), KVEV_EHIP. */
+kvev_status kvev_evict(kvev_ctx* ctx, int64_t budget);
+
+/* Copy the utilities of group (seq, kv_head) in slot order into host `dst`
+ * (capacity `cap` floats); *n_written = the group's token count.
+ * Synchronises.  Errors: KVEV_ERANGE (cap too small / bad indices). */
+kvev_status kvev_scores(kvev_ctx* ctx, int32_t seq, int32_t kv_head, float* dst,
+                        int64_t cap, int64_t* n_written);
+
+/* Copy the positions of group (seq, kv_head) in slot order into host
+ * `positions` (capacity `cap`); *n = count.  Synchronises. */
+kvev_status kvev_retained(kvev_ctx* ctx, int32_t seq, int32_t kv_head,
+                          int32_t* positions, int64_t cap, int64_t* n);
+
+/* Gather the cached K and V of group (seq, kv_head) in slot order into
+ * device buffers k_out / v_out, each [n_layers][n][head_dim] (cfg.dtype),
+ * n = the group's count, which is returned in *n.  cap = rows per layer the
+ * buffers hold.  Stream-ordered (does not synchronise). */
+kvev_status kvev_export_kv(kvev_ctx* ctx, int32_t seq, int32_t kv_head, void* k_out,
+                           void* v_out, int64_t cap, int64_t* n);
+
+/* Replace the state of group (seq, kv_head): n tokens with host `positions`
+ * and host `scores` (slot order), and device k, v [n_layers][n][head_dim].
+ * Used to put both sides of a comparison on the same state.
+ * Errors: KVEV_EINVAL / KVEV_ERANGE (n > capacity), KVEV_ENOMEM. */
+kvev_status kvev_import_group(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int64_t n,
+                              const int32_t* positions, const float* scores,
+                              const void* k, const void* v);
+
+/* Wait for all work queued on the context's stream; report a HIP error. */
+kvev_status kvev_sync(kvev_ctx* ctx);
+
+/* Decode steps taken so far (the t of the last kvev_decode_step). */
+int64_t kvev_step_index(const kvev_ctx* ctx);
+
+/* Kernel timing, measured with HIP events recorded on the context's stream
+ * around every launch of the named kernel while enabled.  `kernel`:
+ * "attn" (split attention), "combine", "fold", "select", "move", "append".
+ * *total_ms / *launches cover the launches since the last reset. */
+kvev_status kvev_profile_enable(kvev_ctx* ctx, int32_t enable);
+kvev_status kvev_profile_reset(kvev_ctx* ctx);
+kvev_status kvev_profile_read(kvev_ctx* ctx, const char* kernel, double* total_ms,
+                              int64_t* launches);
+
+/* Text of the last error on this context ("" if none).  ctx may be NULL
+ * (then: the last kvev_create failure). */
+const char* kvev_last_error(const kvev_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVEV_H */

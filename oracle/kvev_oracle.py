@@ -384,22 +384,25 @@ class TokenModeOracle:
     def group_size(self):
         return self.n_q_heads // self.n_kv_heads
 
-    def prefill(self, seq, K, V):
+    def prefill(self, seq, K, V, heads=None):
         """Store a sequence's prefill cache, positions 0..n-1, utility 0.
 
-        ``K``, ``V``: [L, Hkv, n, d].  [InertiaKV] App. E: m_0(i) = 0 for
-        every prefill position; compression acts only during decoding.
+        ``K``, ``V``: [L, len(heads), n, d] (``heads`` defaults to every KV
+        head; holding a subset checks a sample of independent groups).
+        [InertiaKV] App. E: m_0(i) = 0 for every prefill position;
+        compression acts only during decoding.
         """
         K = np.asarray(K, dtype=np.float32)
         V = np.asarray(V, dtype=np.float32)
-        L, Hkv, n, d = K.shape
+        L, nh, n, d = K.shape
+        heads = list(range(nh)) if heads is None else list(heads)
         cap = max(self.capacity, n + 1)
-        for h in range(Hkv):
+        for j, h in enumerate(heads):
             g = _Group(K=np.zeros((L, cap, d), np.float32),
                        V=np.zeros((L, cap, d), np.float32),
                        pos=np.zeros(cap, np.int64), m=np.zeros(cap, np.float64))
-            g.K[:, :n] = K[:, h]
-            g.V[:, :n] = V[:, h]
+            g.K[:, :n] = K[:, j]
+            g.V[:, :n] = V[:, j]
             g.pos[:n] = np.arange(n)
             g.n = n
             self.groups[(seq, h)] = g
@@ -420,12 +423,16 @@ class TokenModeOracle:
         g.pos = np.concatenate([g.pos, np.zeros(extra, np.int64)])
         g.m = np.concatenate([g.m, np.zeros(extra, np.float64)])
 
+    def held_heads(self, seq):
+        return sorted(h for (s, h) in self.groups if s == seq)
+
     def decode_step(self, t, q, k_new, v_new, seqs):
         """Append, attend every layer, fold (on refresh steps).
 
         ``q``: [L, len(seqs), Hq, d]; ``k_new``, ``v_new``: [L, len(seqs),
         Hkv, d]; ``seqs`` lists the sequence ids in that batch order.
-        Returns ``out`` [L, len(seqs), Hq, d] in fp64.
+        Returns ``out`` [L, len(seqs), Hq, d] in fp64 (zero for the query
+        heads of KV heads this oracle does not hold).
         """
         q = np.asarray(q, dtype=np.float32)
         k_new = np.asarray(k_new, dtype=np.float32)
@@ -433,7 +440,7 @@ class TokenModeOracle:
         refresh = self.is_refresh(t)
         Hg = self.group_size
         for bi, seq in enumerate(seqs):
-            for h in range(self.n_kv_heads):
+            for h in self.held_heads(seq):
                 g = self.groups[(seq, h)]
                 init = 0.0 if refresh else float(g.m[:g.n].mean())
                 self._grow(g)
@@ -446,7 +453,7 @@ class TokenModeOracle:
         self.last_G = {}
         for l in range(self.n_layers):
             for bi, seq in enumerate(seqs):
-                for h in range(self.n_kv_heads):
+                for h in self.held_heads(seq):
                     g = self.groups[(seq, h)]
                     o, p, _ = decode_attention(q[l, bi, h * Hg:(h + 1) * Hg],
                                                g.K[l, :g.n], g.V[l, :g.n])

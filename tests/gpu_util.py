@@ -1,0 +1,164 @@
+"""Lockstep comparison of the HIP library with the CPU oracle (GPU tests)."""
+from __future__ import annotations
+
+import sys
+import time
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle as orc
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Stats:
+    steps: int = 0
+    near_tie_resyncs: int = 0
+    max_out_err: float = 0.0
+    max_score_err: float = 0.0
+    kv_checks: int = 0
+    exact_selection_checks: int = 0
+    notes: list = field(default_factory=list)
+
+
+def rel_err_scores(x, ref):
+    """max over elements of |x - ref| / (|ref| + 1e-30/rtol-floor)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(x - ref), np.abs(ref)
+
+
+def check_scores(gpu, ref, rtol, what):
+    diff = np.abs(np.asarray(gpu, np.float64) - ref)
+    bound = rtol * np.abs(ref) + 1e-30
+    bad = np.flatnonzero(diff > bound)
+    assert bad.size == 0, (f"{what}: {bad.size} scores outside tolerance; first slot {bad[0]}: "
+                           f"gpu={gpu[bad[0]]!r} ref={ref[bad[0]]!r}")
+    nz = np.abs(ref) > 0
+    return float((diff[nz] / np.abs(ref[nz])).max()) if nz.any() else 0.0
+
+
+def check_out(gpu, ref, rtol, what):
+    """Per head: ||o - o_ref||_inf <= rtol ||o_ref||_inf."""
+    worst = 0.0
+    for h in range(ref.shape[0]):
+        den = np.abs(ref[h]).max()
+        err = np.abs(gpu[h] - ref[h]).max()
+        assert err <= rtol * den, f"{what} head {h}: err {err} > {rtol} * {den}"
+        worst = max(worst, err / den if den > 0 else 0.0)
+    return worst
+
+
+def expected_after_evict(scores, pos_pre, B, n_sink, n_recent):
+    """The oracle's selection + hole-fill applied to the GPU's own pre-evict
+    scores and slot layout (fp32 widened to fp64 exactly)."""
+    keep = orc.select_keep(np.asarray(scores, np.float64), pos_pre, B, n_sink, n_recent)
+    moves = orc.hole_fill_moves(keep, B)
+    post = np.array(pos_pre, copy=True)
+    for s, d in moves:
+        post[d] = post[s]
+    return post[: min(B, len(post))]
+
+
+def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=None,
+                       kv_every=1, budget=None, device="cuda", ctx_steps=None):
+    """Run `steps` decode+evict steps of workload `w` on the GPU and the oracle."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    rtol = rtol if rtol is not None else (1e-5 if w.dtype == "f32" else 2e-3)
+    B = w.budget if budget is None else budget
+    sample_seqs = list(range(w.batch)) if sample_seqs is None else list(sample_seqs)
+    sample_heads = list(range(w.n_kv_heads)) if sample_heads is None else list(sample_heads)
+    log(f"[lockstep] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:4]} steps={steps} "
+        f"B={B} seqs={sample_seqs} heads={sample_heads}")
+    t_start = time.time()
+    ctx = kvev.context_for(w, max_steps=ctx_steps or steps, budget=B)
+    o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=B,
+                            alpha_new=w.alpha_new, policy=w.policy if w.policy == "cumulative" else "ema",
+                            refresh_interval=w.refresh_interval, score_free=w.score_free,
+                            n_sink=w.n_sink, n_recent=w.n_recent,
+                            capacity=max(w.prefill_lens) + steps + 1)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=device)
+        ctx.prefill(b, K.contiguous(), V.contiguous())
+        del K, V
+        if b in sample_seqs:
+            Kc, Vc = w.prefill_kv(b, device="cpu", heads=sample_heads)
+            o.prefill(b, Kc.float().numpy(), Vc.float().numpy(), heads=sample_heads)
+    torch.cuda.synchronize()
+    log(f"[lockstep] prefill done in {time.time() - t_start:.1f}s")
+    st = Stats()
+    Hg = w.group_size
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32,
+                      device=device)
+    for t in range(1, steps + 1):
+        q, kn, vn = w.step_inputs(t, device=device)
+        ctx.decode_step(q, kn, vn, out)
+        qc, knc, vnc = w.step_inputs(t, device="cpu", seqs=sample_seqs)
+        ref_out = o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(),
+                                sample_seqs)
+        gout = out.cpu().numpy()
+        for bi, b in enumerate(sample_seqs):
+            for h in sample_heads:
+                for l in range(w.n_layers):
+                    st.max_out_err = max(st.max_out_err, check_out(
+                        gout[l, b, h * Hg:(h + 1) * Hg], ref_out[l, bi, h * Hg:(h + 1) * Hg], rtol,
+                        f"step {t} out l={l} b={b} kvh={h}"))
+        pre = {}
+        for b in sample_seqs:
+            for h in sample_heads:
+                gs = ctx.scores(b, h)
+                gp = ctx.retained(b, h)
+                np.testing.assert_array_equal(gp, o.positions(b, h), err_msg=f"step {t} pre-evict slots")
+                st.max_score_err = max(st.max_score_err, check_scores(
+                    gs, o.scores(b, h), rtol, f"step {t} scores b={b} kvh={h}"))
+                pre[(b, h)] = (gs, gp)
+        ctx.evict(B)
+        ref_pre_scores = {k: o.scores(*k) for k in pre}
+        o.evict(B)
+        for (b, h), (gs, gp) in pre.items():
+            got = ctx.retained(b, h)
+            # selection + compaction on the GPU's own scores: bit-exact
+            exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
+            np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b} kvh={h}")
+            st.exact_selection_checks += 1
+            ref_pos = o.positions(b, h)
+            if not np.array_equal(got, ref_pos):
+                # near-tie exemption: every differing position within 1e-5 of the boundary
+                ms = ref_pre_scores[(b, h)]
+                pos_all = gp
+                keep_ref = np.isin(pos_all, ref_pos)
+                prot = (pos_all < w.n_sink) | (pos_all > pos_all.max() - w.n_recent)
+                kept_scores = ms[keep_ref & ~prot]
+                theta = kept_scores.min() if kept_scores.size else 0.0
+                diff = set(got.tolist()) ^ set(ref_pos.tolist())
+                idx = {p: i for i, p in enumerate(pos_all.tolist())}
+                gaps = [abs(ms[idx[p]] - theta) for p in diff]
+                assert max(gaps) < 1e-5, (f"step {t} b={b} kvh={h}: retained sets differ by {len(diff)} "
+                                          f"positions with oracle score gap {max(gaps):.3e} >= 1e-5")
+                st.near_tie_resyncs += 1
+                g = o.groups[(b, h)]
+                kk = torch.from_numpy(g.K[:, :g.n].copy()).to(w.torch_dtype).to(device).contiguous()
+                vv = torch.from_numpy(g.V[:, :g.n].copy()).to(w.torch_dtype).to(device).contiguous()
+                ctx.import_group(b, h, g.pos[:g.n], g.m[:g.n].astype(np.float32), kk, vv)
+                st.notes.append(f"t={t} b={b} h={h} near-tie resync ({len(diff)} positions)")
+            elif kv_every and t % kv_every == 0:
+                gk, gv = ctx.export_kv(b, h)
+                g = o.groups[(b, h)]
+                rk = torch.from_numpy(g.K[:, :g.n].copy()).to(w.torch_dtype)
+                rv = torch.from_numpy(g.V[:, :g.n].copy()).to(w.torch_dtype)
+                assert torch.equal(gk.cpu(), rk), f"step {t} compacted K differs b={b} kvh={h}"
+                assert torch.equal(gv.cpu(), rv), f"step {t} compacted V differs b={b} kvh={h}"
+                st.kv_checks += 1
+        st.steps = t
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[lockstep] step {t}: out_err {st.max_out_err:.2e} score_err {st.max_score_err:.2e} "
+                f"resyncs {st.near_tie_resyncs} ({time.time() - t_start:.1f}s)")
+    ctx.close()
+    return st

@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side
+validation rejects bad configurations (no GPU calls are made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decode_kv_cache_gqa_amd import kvev
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvev.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvev_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("kvev_create", "kvev_decode_step", "kvev_scores", "kvev_evict",
+                     "kvev_destroy", "kvev_prefill", "kvev_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvev.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kvev.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvev_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_config_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in kvev.Config._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(kvev_config, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "kvev.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(kvev_config));\n'
+                   f'  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(kvev.Config, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(kvev.Config)
+
+
+def _create(**kw):
+    base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, head_dim=64, batch=1, dtype=kvev.F32,
+                max_tokens=100, budget=10)
+    base.update(kw)
+    cfg = kvev.make_config(**base)
+    h = ctypes.c_void_p()
+    st = kvev.lib().kvev_create(ctypes.byref(cfg), None, ctypes.byref(h))
+    return st, kvev.lib().kvev_last_error(None).decode(), h
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(head_dim=96), "head_dim"),
+    (dict(n_q_heads=7), "multiple"),
+    (dict(n_q_heads=16), "group size"),
+    (dict(budget=0), "budget"),
+    (dict(n_sink=8, n_recent=4), "exceeds the budget"),
+    (dict(page_tokens=32), "page_tokens"),
+    (dict(alpha_new=0.0), "alpha_new"),
+    (dict(alpha_new=1.5), "alpha_new"),
+    (dict(refresh_interval=0), "refresh_interval"),
+    (dict(dtype=7), "dtype"),
+    (dict(max_tokens=1), "max_tokens"),
+    (dict(batch=0), ">= 1"),
+    (dict(policy=9), "policy"),
+])
+def test_create_rejects_bad_config(bad, msg):
+    st, err, h = _create(**bad)
+    assert st == kvev.EINVAL
+    assert msg in err
+    assert not h.value
+
+
+def test_null_arguments():
+    L = kvev.lib()
+    assert L.kvev_create(None, None, None) == kvev.EINVAL
+    assert L.kvev_destroy(None) == kvev.OK
+    assert L.kvev_evict(None, 5) == kvev.EINVAL
+    assert L.kvev_decode_step(None, None, None, None, None) == kvev.EINVAL
+    assert L.kvev_step_index(None) == -1
+
+
+def test_config_defaults():
+    c = kvev.config_init()
+    assert c.page_tokens == 16 and c.refresh_interval == 1 and c.policy == kvev.EMA
+    assert abs(c.alpha_new - 0.05) < 1e-7
