@@ -3,9 +3,8 @@
 Workload: Llama-3.1-8B-shaped attention (32 layers, 32 query heads over 8 KV
 heads, head dim 128, bf16, batch 1), 32,768-token prefill, EMA alpha 0.05
 folded layer by layer, budget 3,277 tokens per KV head with 4 sinks and 32
-recent tokens protected.  One step = kvev_decode_step (append, split
-attention over all layers, probability pass + fold) + kvev_evict
-(radix select + compaction).  W warm-up steps (the first one evicts the
+recent tokens protected.  One step = kvev_step: append + split attention over all layers, then
+split merge + probability pass + layer fold + radix select + compaction.  W warm-up steps (the first one evicts the
 prefill down to the budget) run untimed, then exactly K steps are timed
 between two device synchronisations; inputs are resident in HBM before the
 timed region.
@@ -107,20 +106,18 @@ def main():
     torch.cuda.synchronize()
 
     for t in range(args.warmup):
-        ctx.decode_step(*inputs[t], out)
-        ctx.evict()
+        ctx.step(*inputs[t], out)
     ctx.sync()
     ctx.profile(True)
     ctx.profile_reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for t in range(args.warmup, total):
-        ctx.decode_step(*inputs[t], out)
-        ctx.evict()
+        ctx.step(*inputs[t], out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ctx.sync()
-    prof = {k: ctx.profile_read(k) for k in ("append", "attn", "combine", "fold", "select", "move")}
+    prof = {k: ctx.profile_read(k) for k in ("attn", "post", "move")}
     ctx.close()
 
     n_tok = w.budget + 1
@@ -130,7 +127,7 @@ def main():
     attn_ms, attn_n = prof["attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
-    policy_ms = sum(prof[k][0] for k in ("fold", "select", "move")) / args.steps
+    policy_ms = sum(prof[k][0] for k in ("post", "move")) / args.steps
     result = {
         "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
         "value": round(steps_s, 2),
@@ -159,7 +156,7 @@ def main():
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
             "traffic": None,
-            "kernel": "attn_split_kernel",
+            "kernel": "attn_mfma_kernel",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }

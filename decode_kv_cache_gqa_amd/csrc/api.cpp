@@ -96,7 +96,8 @@ void prof_drain(kvev_ctx* c) {
 void free_all(kvev_ctx* c) {
   auto& d = c->d;
   void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
-                  d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag};
+                  d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
+                  d.grpctr};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -173,7 +174,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.budget < 1) return bad("budget must be >= 1");
   if (f.n_sink + f.n_recent > f.budget) return bad("n_sink + n_recent exceeds the budget");
   if (f.max_tokens < 2 || f.max_tokens > (1ll << 30)) return bad("max_tokens out of range");
-  if (f.n_layers > 256) return bad("n_layers must be <= 256");
+  if (f.n_layers > 128) return bad("n_layers must be <= 128");
 
   kvev_ctx* c = new (std::nothrow) kvev_ctx();
   if (!c) return bad("out of host memory");
@@ -215,6 +216,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.mv_dst, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.nmoves, G));
   A(dalloc(&d.errflag, 1));
+  A(dalloc(&d.grpctr, G));
   if (e != hipSuccess) {
     g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
     free_all(c);
@@ -231,6 +233,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(hipMemsetAsync(d.nextpos, 0, sizeof(int) * G, c->stream));
   A(hipMemsetAsync(d.nmoves, 0, sizeof(int) * G, c->stream));
   A(hipMemsetAsync(d.errflag, 0, sizeof(int), c->stream));
+  A(hipMemsetAsync(d.grpctr, 0, sizeof(unsigned) * G, c->stream));
   A(hipMemsetAsync(d.mv_src, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.mv_dst, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipStreamSynchronize(c->stream));
@@ -289,9 +292,10 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
   return KVEV_OK;
 }
 
-kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
-                             float* out) {
-  KVEV_LIVE(c);
+// Shared by kvev_decode_step and kvev_step: pages for the new token, the
+// attention launch and the post launch.
+static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                            float* out, bool do_select, int64_t B) {
   if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
   for (int b = 0; b < c->cfg.batch; ++b)
     if (!c->prefilled[b]) return fail(c, KVEV_ESTATE, "a sequence has no prefill");
@@ -299,55 +303,78 @@ kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, cons
   const bool refresh = c->cfg.score_free ? (t == 1) : ((t - 1) % c->cfg.refresh_interval == 0);
   auto& upd = c->ptab_upd;
   upd.clear();
-  int64_t n_max = 0;
+  int64_t n_max = 0, max_moves = 0;
   for (int g = 0; g < c->G; ++g) {
     if (c->count[g] + 1 > c->cap) return fail(c, KVEV_ESTATE, "slot capacity exhausted");
-    if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
     n_max = std::max(n_max, c->count[g] + 1);
+    if (c->count[g] + 1 > B) max_moves = std::max(max_moves, std::min(B, c->count[g] + 1 - B));
   }
+  for (int g = 0; g < c->G; ++g)
+    if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
   if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
   {
-    ProfScope p(c, "append");
-    KVEV_HIP(c, launch_append(c, k_new, v_new, refresh ? 1 : 0));
-  }
-  {
     ProfScope p(c, "attn");
-    KVEV_HIP(c, launch_attention(c, q, static_cast<int>(n_max), refresh ? 1 : 0));
+    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0));
   }
+  const bool inline_moves = max_moves <= kInlineMoves;
   {
-    ProfScope p(c, "combine");
-    KVEV_HIP(c, launch_combine(c, out));
+    ProfScope p(c, "post");
+    KVEV_HIP(c, launch_post(c, out, static_cast<int>(n_max), refresh ? 1 : 0, do_select ? 1 : 0, B,
+                            inline_moves ? 1 : 0));
   }
-  if (refresh) {
-    ProfScope p(c, "fold");
-    KVEV_HIP(c, launch_fold(c, static_cast<int>(n_max)));
+  if (do_select && !inline_moves) {
+    ProfScope p(c, "move");
+    KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
   }
-  for (int g = 0; g < c->G; ++g) c->count[g] += 1;
+  for (int g = 0; g < c->G; ++g) {
+    c->count[g] += 1;
+    if (do_select && c->count[g] > B) c->count[g] = B;
+    if (do_select) release_pages(c, g, c->count[g]);
+  }
   c->t = t;
   return KVEV_OK;
 }
 
+static kvev_status check_budget(kvev_ctx* c, int64_t budget, int64_t* B) {
+  *B = budget > 0 ? budget : c->cfg.budget;
+  if (*B < c->cfg.n_sink + c->cfg.n_recent || *B < 1)
+    return fail(c, KVEV_EINVAL, "budget below the protected token count");
+  if (*B > (1ll << 30)) return fail(c, KVEV_EINVAL, "budget out of range");
+  return KVEV_OK;
+}
+
+kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                             float* out) {
+  KVEV_LIVE(c);
+  return run_step(c, q, k_new, v_new, out, false, c->cfg.budget);
+}
+
+kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out,
+                      int64_t budget) {
+  KVEV_LIVE(c);
+  int64_t B;
+  if (kvev_status s = check_budget(c, budget, &B)) return s;
+  return run_step(c, q, k_new, v_new, out, true, B);
+}
+
 kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   KVEV_LIVE(c);
-  const int64_t B = budget > 0 ? budget : c->cfg.budget;
-  if (B < c->cfg.n_sink + c->cfg.n_recent || B < 1)
-    return fail(c, KVEV_EINVAL, "budget below the protected token count");
-  if (B > (1ll << 30)) return fail(c, KVEV_EINVAL, "budget out of range");
-  int64_t max_moves = 0, n_max = 0;
+  int64_t B;
+  if (kvev_status s = check_budget(c, budget, &B)) return s;
+  int64_t max_moves = 0;
   bool any = false;
   for (int g = 0; g < c->G; ++g) {
     if (c->count[g] > B) {
       any = true;
       max_moves = std::max(max_moves, std::min(B, c->count[g] - B));
-      n_max = std::max(n_max, c->count[g]);
     }
   }
   if (!any) return KVEV_OK;
   {
     ProfScope p(c, "select");
-    KVEV_HIP(c, launch_select(c, B, static_cast<int>(n_max)));
+    KVEV_HIP(c, launch_select(c, B));
   }
-  if (max_moves > 0) {
+  {
     ProfScope p(c, "move");
     KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
   }

@@ -11,7 +11,8 @@
 namespace kvev {
 
 constexpr int kPageTokens = 16;
-constexpr int kAttnChunk = 512;   // tokens per attention split
+constexpr int kAttnChunk = 256;   // slots per attention split
+constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies itself
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
 
 // Device buffers of one context.  Groups are (sequence, KV head) pairs,
@@ -32,9 +33,8 @@ struct DevState {
   int* mv_dst = nullptr;   // [G][cap]
   int* nmoves = nullptr;   // [G]
   int* errflag = nullptr;  // [1] device-side consistency failures (bit mask)
+  unsigned* grpctr = nullptr;  // [G] arrival counters of the post kernel (0 between launches)
 };
-
-struct Launch;  // shape parameters shared by the launchers
 
 struct Profiler {
   bool enabled = false;
@@ -75,11 +75,11 @@ namespace kvev {
 // Launchers (defined in the .hip translation units).  All are stream-ordered.
 hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
 hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
-hipError_t launch_append(kvev_ctx* c, const void* k_new, const void* v_new, int refresh);
-hipError_t launch_attention(kvev_ctx* c, const void* q, int n_max, int write_logits);
-hipError_t launch_combine(kvev_ctx* c, float* out);
-hipError_t launch_fold(kvev_ctx* c, int n_max);
-hipError_t launch_select(kvev_ctx* c, int64_t budget, int n_max);
+hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                            int n_max, int write_logits);
+hipError_t launch_post(kvev_ctx* c, float* out, int n_max, int refresh, int do_select,
+                       int64_t budget, int inline_moves);
+hipError_t launch_select(kvev_ctx* c, int64_t budget);
 hipError_t launch_moves(kvev_ctx* c, int max_moves);
 hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);
 hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n);

@@ -49,6 +49,7 @@ _SIGS = {
     "kvev_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
     "kvev_decode_step": (ctypes.c_int, [ctypes.c_void_p] * 5),
     "kvev_evict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "kvev_step": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64]),
     "kvev_scores": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "kvev_retained": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -162,6 +163,16 @@ class Context:
         self._check(lib().kvev_decode_step(
             self._h, _ptr(q, self.dtype, qs, "q"), _ptr(k_new, self.dtype, ks, "k_new"),
             _ptr(v_new, self.dtype, ks, "v_new"), _ptr(out, torch.float32, qs, "out")))
+
+    def step(self, q, k_new, v_new, out, budget=0):
+        """decode_step + evict(budget) in one call (fused launches)."""
+        import torch
+        c = self.cfg
+        qs = (c.n_layers, c.batch, c.n_q_heads, c.head_dim)
+        ks = (c.n_layers, c.batch, c.n_kv_heads, c.head_dim)
+        self._check(lib().kvev_step(
+            self._h, _ptr(q, self.dtype, qs, "q"), _ptr(k_new, self.dtype, ks, "k_new"),
+            _ptr(v_new, self.dtype, ks, "v_new"), _ptr(out, torch.float32, qs, "out"), int(budget)))
 
     def evict(self, budget=0):
         self._check(lib().kvev_evict(self._h, int(budget)))

@@ -126,6 +126,15 @@ kvev_status kvev_decode_step(kvev_ctx* ctx, const void* q, const void* k_new,
  * Errors: KVEV_EINVAL (budget < n_sink + n_recent), KVEV_EHIP. */
 kvev_status kvev_evict(kvev_ctx* ctx, int64_t budget);
 
+/* One whole decode step of the method: kvev_decode_step followed by
+ * kvev_evict(budget), fused into two kernel launches (attention with the
+ * append; then probability pass, fold, selection and compaction, with
+ * moves of more than a few slots in a third launch).  Same arguments,
+ * layouts and errors as those two calls; results are identical to calling
+ * them in sequence. */
+kvev_status kvev_step(kvev_ctx* ctx, const void* q, const void* k_new, const void* v_new,
+                      float* out, int64_t budget);
+
 /* Copy the utilities of group (seq, kv_head) in slot order into host `dst`
  * (capacity `cap` floats); *n_written = the group's token count.
  * Synchronises.  Errors: KVEV_ERANGE (cap too small / bad indices). */
@@ -160,7 +169,9 @@ int64_t kvev_step_index(const kvev_ctx* ctx);
 
 /* Kernel timing, measured with HIP events recorded on the context's stream
  * around every launch of the named kernel while enabled.  `kernel`:
- * "attn" (split attention), "combine", "fold", "select", "move", "append".
+ * "attn" (append + split attention), "post" (split merge, probability pass,
+ * fold, and in kvev_step selection + compaction), "select" and "move"
+ * (kvev_evict; "move" also in kvev_step when many slots move).
  * *total_ms / *launches cover the launches since the last reset. */
 kvev_status kvev_profile_enable(kvev_ctx* ctx, int32_t enable);
 kvev_status kvev_profile_reset(kvev_ctx* ctx);

@@ -66,7 +66,7 @@ def expected_after_evict(scores, pos_pre, B, n_sink, n_recent):
 
 
 def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=None,
-                       kv_every=1, budget=None, device="cuda", ctx_steps=None):
+                       kv_every=1, budget=None, device="cuda", ctx_steps=None, fused=False):
     """Run `steps` decode+evict steps of workload `w` on the GPU and the oracle."""
     import torch
     from decode_kv_cache_gqa_amd import kvev
@@ -99,7 +99,10 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                       device=device)
     for t in range(1, steps + 1):
         q, kn, vn = w.step_inputs(t, device=device)
-        ctx.decode_step(q, kn, vn, out)
+        if fused:
+            ctx.step(q, kn, vn, out, B)
+        else:
+            ctx.decode_step(q, kn, vn, out)
         qc, knc, vnc = w.step_inputs(t, device="cpu", seqs=sample_seqs)
         ref_out = o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(),
                                 sample_seqs)
@@ -113,21 +116,30 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
         pre = {}
         for b in sample_seqs:
             for h in sample_heads:
+                if fused:
+                    continue
                 gs = ctx.scores(b, h)
                 gp = ctx.retained(b, h)
                 np.testing.assert_array_equal(gp, o.positions(b, h), err_msg=f"step {t} pre-evict slots")
                 st.max_score_err = max(st.max_score_err, check_scores(
                     gs, o.scores(b, h), rtol, f"step {t} scores b={b} kvh={h}"))
                 pre[(b, h)] = (gs, gp)
-        ctx.evict(B)
-        ref_pre_scores = {k: o.scores(*k) for k in pre}
+        if not fused:
+            ctx.evict(B)
+        keys = [(b, h) for b in sample_seqs for h in sample_heads]
+        ref_pre_scores = {k: o.scores(*k) for k in keys}
+        ref_pre_pos = {k: o.positions(*k) for k in keys}
         o.evict(B)
-        for (b, h), (gs, gp) in pre.items():
+        for (b, h) in keys:
             got = ctx.retained(b, h)
-            # selection + compaction on the GPU's own scores: bit-exact
-            exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
-            np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b} kvh={h}")
-            st.exact_selection_checks += 1
+            if not fused:
+                gs, gp = pre[(b, h)]
+                # selection + compaction on the GPU's own scores: bit-exact
+                exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
+                np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b} kvh={h}")
+                st.exact_selection_checks += 1
+            else:
+                gp = ref_pre_pos[(b, h)]
             ref_pos = o.positions(b, h)
             if not np.array_equal(got, ref_pos):
                 # near-tie exemption: every differing position within 1e-5 of the boundary
@@ -148,7 +160,11 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                 vv = torch.from_numpy(g.V[:, :g.n].copy()).to(w.torch_dtype).to(device).contiguous()
                 ctx.import_group(b, h, g.pos[:g.n], g.m[:g.n].astype(np.float32), kk, vv)
                 st.notes.append(f"t={t} b={b} h={h} near-tie resync ({len(diff)} positions)")
-            elif kv_every and t % kv_every == 0:
+                continue
+            if fused:
+                st.max_score_err = max(st.max_score_err, check_scores(
+                    ctx.scores(b, h), o.scores(b, h), rtol, f"step {t} post-evict scores b={b} kvh={h}"))
+            if kv_every and t % kv_every == 0:
                 gk, gv = ctx.export_kv(b, h)
                 g = o.groups[(b, h)]
                 rk = torch.from_numpy(g.K[:, :g.n].copy()).to(w.torch_dtype)

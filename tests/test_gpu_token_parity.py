@@ -36,6 +36,51 @@ def test_tiny_fp32_full_run():
     assert st.max_out_err <= 1e-5 and st.max_score_err <= 1e-5
 
 
+def test_tiny_fp32_fused_step():
+    st = _gu().run_token_lockstep(synth.workload("tiny"), 64, fused=True)
+    assert st.steps == 64
+
+
+def test_llama_shape_fused_step():
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209)
+    _gu().run_token_lockstep(w, 40, fused=True)
+
+
+def test_lazy_fused_step():
+    w = synth.workload("lazy16x8k").scaled(n_layers=2, prefill_lens=(1000, 1000, 1000), budget=250)
+    _gu().run_token_lockstep(w, 20, fused=True)
+
+
+def test_fused_step_bitwise_equals_separate_calls():
+    """kvev_step == kvev_decode_step + kvev_evict, bit for bit (outputs,
+    utilities, slot layout and cached K/V), including the first step's
+    large compaction and many single-eviction steps."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    w = synth.workload("llama8b_32k").scaled(n_layers=4, prefill_lens=(5000,), budget=500)
+    ctxs = [kvev.context_for(w, max_steps=24) for _ in range(2)]
+    K, V = w.prefill_kv(0, device="cuda")
+    for c in ctxs:
+        c.prefill(0, K, V)
+    outs = [torch.empty((4, 1, 32, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+    for t in range(1, 25):
+        q, kn, vn = w.step_inputs(t, device="cuda")
+        ctxs[0].step(q, kn, vn, outs[0])
+        ctxs[1].decode_step(q, kn, vn, outs[1])
+        ctxs[1].evict()
+        assert torch.equal(outs[0], outs[1]), t
+        for h in range(w.n_kv_heads):
+            np.testing.assert_array_equal(ctxs[0].retained(0, h), ctxs[1].retained(0, h))
+            np.testing.assert_array_equal(ctxs[0].scores(0, h), ctxs[1].scores(0, h))
+    for h in (0, 7):
+        a = ctxs[0].export_kv(0, h)
+        b = ctxs[1].export_kv(0, h)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for c in ctxs:
+        c.sync()
+        c.close()
+
+
 def test_llama_shape_scaled_ragged():
     """Llama-8B head shape, bf16, 3 layers, ragged prefill, 4 sinks + 32 recent."""
     w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209)
@@ -119,4 +164,10 @@ def test_llama8b_32k_full_size_sampled():
     configuration; the oracle follows two sampled KV-head groups."""
     w = synth.workload("llama8b_32k")
     st = _gu().run_token_lockstep(w, 6, sample_heads=[0, 5], kv_every=3, ctx_steps=w.steps)
+    assert st.steps == 6
+
+
+def test_llama8b_32k_full_size_fused_sampled():
+    w = synth.workload("llama8b_32k")
+    st = _gu().run_token_lockstep(w, 6, sample_heads=[3], kv_every=3, ctx_steps=w.steps, fused=True)
     assert st.steps == 6
