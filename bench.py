@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported",
@@ -91,6 +93,16 @@ def main():
 
     import torch
     from decode_kv_cache_gqa_amd import kvev, synth
+
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 4}))
+        return
 
     w = synth.workload(args.workload)
     total = args.warmup + args.steps

@@ -97,7 +97,7 @@ void free_all(kvev_ctx* c) {
   auto& d = c->d;
   void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
-                  d.grpctr};
+                  d.grpctr, d.blk_key, d.blk_slot, d.blk_page, d.blk_sum};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -174,7 +174,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.budget < 1) return bad("budget must be >= 1");
   if (f.n_sink + f.n_recent > f.budget) return bad("n_sink + n_recent exceeds the budget");
   if (f.max_tokens < 2 || f.max_tokens > (1ll << 30)) return bad("max_tokens out of range");
-  if (f.n_layers > 128) return bad("n_layers must be <= 128");
+  if (f.n_layers > 64) return bad("n_layers must be <= 64");
 
   kvev_ctx* c = new (std::nothrow) kvev_ctx();
   if (!c) return bad("out of host memory");
@@ -187,11 +187,12 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->maxpages = static_cast<int>((c->cap + c->PT - 1) / c->PT);
   c->P = static_cast<int64_t>(c->G) * c->maxpages;
   c->max_splits = static_cast<int>((c->cap + kAttnChunk - 1) / kAttnChunk);
+  c->max_post_blocks = std::max(static_cast<int>((c->cap + 63) / 64), f.n_layers);
   c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
   c->count.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
   c->pages.assign(c->G, {});
-  c->free_pages.resize(c->P);
+  c->free_pages.resize(c->P);  // popped from the back: lowest page first
   for (int64_t i = 0; i < c->P; ++i) c->free_pages[i] = static_cast<int>(c->P - 1 - i);
 
   auto& d = c->d;
@@ -217,6 +218,10 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.nmoves, G));
   A(dalloc(&d.errflag, 1));
   A(dalloc(&d.grpctr, G));
+  A(dalloc(&d.blk_key, static_cast<size_t>(G) * c->max_post_blocks));
+  A(dalloc(&d.blk_slot, static_cast<size_t>(G) * c->max_post_blocks));
+  A(dalloc(&d.blk_page, static_cast<size_t>(G) * c->max_post_blocks));
+  A(dalloc(&d.blk_sum, static_cast<size_t>(G) * c->max_post_blocks));
   if (e != hipSuccess) {
     g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
     free_all(c);
@@ -267,10 +272,13 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
     const int g = seq * Hkv + h;
     release_pages(c, g, 0);
   }
-  for (int h = 0; h < Hkv; ++h) {
-    const int g = seq * Hkv + h;
-    if (!ensure_pages(c, g, n, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
-  }
+  // page i of every KV head of the sequence is allocated before page i + 1,
+  // so the pages that survive compaction (the lowest) are adjacent in memory
+  const int64_t npages = (n + c->PT - 1) / c->PT;
+  for (int64_t i = 1; i <= npages; ++i)
+    for (int h = 0; h < Hkv; ++h)
+      if (!ensure_pages(c, seq * Hkv + h, std::min(n, i * c->PT), upd))
+        return fail(c, KVEV_ENOMEM, "page pool exhausted");
   if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
   KVEV_HIP(c, launch_prefill_scatter(c, seq, k, v, n));
   // positions 0..n-1, utilities 0, count n, next position n
@@ -312,6 +320,7 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
   for (int g = 0; g < c->G; ++g)
     if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
   if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
+  c->lstride = (n_max + 15) / 16 * 16;
   {
     ProfScope p(c, "attn");
     KVEV_HIP(c, launch_attention(c, q, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0));
@@ -319,8 +328,8 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
   const bool inline_moves = max_moves <= kInlineMoves;
   {
     ProfScope p(c, "post");
-    KVEV_HIP(c, launch_post(c, out, static_cast<int>(n_max), refresh ? 1 : 0, do_select ? 1 : 0, B,
-                            inline_moves ? 1 : 0));
+    KVEV_HIP(c, launch_post(c, out, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0,
+                            do_select ? 1 : 0, B, inline_moves ? 1 : 0));
   }
   if (do_select && !inline_moves) {
     ProfScope p(c, "move");

@@ -1,7 +1,7 @@
 // Split-K GQA decode attention that exposes per-token logits, with the
 // step's new token appended on the way.
 //
-// Per (layer l, group g = (sequence, KV head), split of tokens) and for the
+// Per (layer l, group g = (sequence, KV head), split of slots) and for the
 // HG query heads that share the KV head:
 //   s[h][t] = (q_h . k_t) / sqrt(d)          ("QEvict" review, section 4.1,
 //                                              (Attention))
@@ -9,8 +9,8 @@
 // The logits are stored (fp32) for the probability pass, which normalises
 // them once every split's (m, l) is merged; the post kernel does the merge.
 // The group's cache holds count[g] tokens in slots [0, count); the new
-// token is slot count[g] and is read from k_new / v_new, then written to its
-// page by the block that owns that slot.
+// token is slot count[g]: it is read from k_new / v_new and written into its
+// page by the lanes that hold it.
 #include "common.h"
 #include "kvev_internal.h"
 
@@ -25,36 +25,49 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& r) {
   return v;
 }
 
+// replace 16-bit element e (0..7) of a 16-byte register
+__device__ __forceinline__ void put16(uint4& r, int e, uint32_t x) {
+  const int sh = (e & 1) * 16;
+  const uint32_t m = ~(0xffffu << sh);
+  const uint32_t v = (x & 0xffffu) << sh;
+  switch (e >> 1) {
+    case 0: r.x = (r.x & m) | v; break;
+    case 1: r.y = (r.y & m) | v; break;
+    case 2: r.z = (r.z & m) | v; break;
+    default: r.w = (r.w & m) | v; break;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// bf16, head_dim 128, group of 4 query heads: q.K^T on MFMA, p.V on VALU.
-//
-// A wave owns NG groups of 16 consecutive slots (one cache page each).  For
-// group j it loads, with all loads of all groups issued before any use:
-//   K (MFMA B operand): lane (r16, q4) reads slot r16, channels
-//     32*s + 8*q4 .. +8 for k-steps s = 0..3 (16-byte loads);
-//   V (p.V layout):      lane (r16, q4) reads slot q4 + 4*u, channels
-//     8*r16 .. +8 for u = 0..3.
-// v_mfma_f32_16x16x32_bf16 with A = the 4 query rows (rows 4..15 zero) gives
-// lane r16 (q4 == 0) the 4 heads' logits of slot r16.
+// bf16, head_dim 128, group of 4 query heads: q.K^T and p.V on the matrix
+// cores (v_mfma_f32_16x16x32_bf16), 64 slots (4 pages) per wave.
+//   q.K^T: A = the 4 query rows (rows 4..15 zero), B = K^T; lane (r16, q4)
+//     loads slot r16 of a page, channels 32*s + 8*q4 .. +8 (k-step s);
+//     lane r16 of row 0 receives the 4 heads' logits of slot r16.
+//   p.V:   A = P (4 rows), B = V; 32 slots (2 pages) per k-step.  Lane
+//     (r16, q4) loads channel 16*ct + r16, slots 8*(q4 & 1) .. +8 of page
+//     2k + (q4 >> 1): 16 contiguous bytes of the channel-major V page.  P is
+//     split into bf16 hi + lo parts (two products), so the rounding of P is
+//     at most 2^-18 relative.
+// Every load of the wave is issued before the first use.
 // ---------------------------------------------------------------------------
-template <int NG, int NW>
+template <int NW>
 __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const int* __restrict__ ptab, const int* __restrict__ count, float* __restrict__ logits,
     float* __restrict__ part_ml, float* __restrict__ part_o, int L, int G, int Hkv, int Hq,
-    int64_t P, int maxpages, int64_t cap, int S, float scale, int write_logits) {
-  constexpr int D = 128, HG = 4;
-  constexpr int WT = NG * 16;   // slots per wave
-  constexpr int CT = NW * WT;   // slots per block
-  __shared__ __align__(16) float p_lds[NW][WT][HG];
+    int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits) {
+  constexpr int D = 128, HG = 4, NG = 4, WT = NG * 16;
+  __shared__ __align__(16) float p_lds[NW][HG][WT];
   __shared__ __align__(16) float wstat[NW][HG][2];
   __shared__ __align__(16) float o_lds[NW][HG][D];
 
   const int split = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int t0 = split * CT;
-  const int wt0 = t0 + wave * WT;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keep it scalar
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int t0 = split * NW * WT, wt0 = t0 + wave * WT;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
   // page indices do not depend on the count: load them alongside it
   int pages[NG];
@@ -63,66 +76,68 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
   const int n = count[g] + 1;  // slots including the new token
   if (t0 >= n) return;
   const int B = G / Hkv, b = g / Hkv, kvh = g % Hkv;
-  const int r16 = lane % 16, q4 = lane / 16;
   const int tnew = n - 1;
   const int64_t new_off = (static_cast<int64_t>(l * B + b) * Hkv + kvh) * D;
 
   bf16x8 qa[4];
   {
-    uint4 z = make_uint4(0, 0, 0, 0);
-    const uint16_t* qp = q + (static_cast<int64_t>(l * B + b) * Hq + kvh * HG + (r16 < HG ? r16 : 0)) * D;
+    const uint16_t* qp = q + (static_cast<int64_t>(l * B + b) * Hq + kvh * HG + (r16 & 3)) * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      uint4 r = r16 < HG ? *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * q4) : z;
+      uint4 r = *reinterpret_cast<const uint4*>(qp + 32 * s);
+      if (r16 >= HG) r = make_uint4(0, 0, 0, 0);
       qa[s] = as_bf16x8(r);
     }
   }
 
-  uint4 kr[NG][4], vr[NG][4];
+  uint4 kr[NG][4];
+  uint4 vr[2][8];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
-    const int gbase = wt0 + 16 * j;
-    const int64_t prow = pool_row(l, pages[j], 0, 0, P, 1, kPageTokens);
-    const int tk = gbase + r16;
+    const bool live = wt0 + 16 * j < n;  // wave-uniform
+    const uint16_t* kb = kpool + kidx(l, pages[j], r16, 8 * q4, P, D);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 r = make_uint4(0, 0, 0, 0);
-      if (tk < n) {
-        const uint16_t* src = (tk == tnew) ? k_new + new_off : kpool + (prow + r16) * D;
-        r = *reinterpret_cast<const uint4*>(src + 32 * s + 8 * q4);
-      }
-      kr[j][s] = r;
-    }
+    for (int s = 0; s < 4; ++s)
+      kr[j][s] = live ? *reinterpret_cast<const uint4*>(kb + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int tv = gbase + q4 + 4 * u;
-      uint4 r = make_uint4(0, 0, 0, 0);
-      if (tv < n) {
-        const uint16_t* src = (tv == tnew) ? v_new + new_off : vpool + (prow + q4 + 4 * u) * D;
-        r = *reinterpret_cast<const uint4*>(src + 8 * r16);
-      }
-      vr[j][u] = r;
-    }
+  for (int k = 0; k < 2; ++k) {
+    const bool second = (q4 >> 1) != 0;
+    const bool live = wt0 + 16 * (2 * k + (second ? 1 : 0)) < n;
+    const uint16_t* vb = vpool + vidx(l, second ? pages[2 * k + 1] : pages[2 * k], 8 * (q4 & 1), r16, P, D);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      vr[k][ct] = live ? *reinterpret_cast<const uint4*>(vb + ct * 16 * kPageTokens) : make_uint4(0, 0, 0, 0);
   }
 
-  // append: the lanes holding the new token write it into its page slot
+  // append: the new token replaces the stale slot contents in registers
+  // and is written into its page
   if (tnew >= wt0 && tnew < wt0 + WT) {
-    const int j = (tnew - wt0) / 16;
-    const int64_t row = pool_row(l, pt[tnew / kPageTokens], 0, tnew % kPageTokens, P, 1, kPageTokens) * D;
+    const int jn = (tnew - wt0) >> 4, rn = (tnew - wt0) & 15;
 #pragma unroll
-    for (int jj = 0; jj < NG; ++jj) {
-      if (jj != j) continue;
-      if (wt0 + 16 * jj + r16 == tnew) {
+    for (int j = 0; j < NG; ++j) {
+      if (j != jn || r16 != rn) continue;
+      uint16_t* kd = kpool + kidx(l, pages[j], rn, 8 * q4, P, D);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(kpool + row + 32 * s + 8 * q4) = kr[jj][s];
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = *reinterpret_cast<const uint4*>(k_new + new_off + 32 * s + 8 * q4);
+        kr[j][s] = v;
+        *reinterpret_cast<uint4*>(kd + 32 * s) = v;
       }
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (wt0 + 16 * jj + q4 + 4 * u == tnew) *reinterpret_cast<uint4*>(vpool + row + 8 * r16) = vr[jj][u];
+    for (int k = 0; k < 2; ++k) {
+      if (k != (jn >> 1) || (q4 >> 1) != (jn & 1) || (q4 & 1) != (rn >> 3)) continue;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const uint16_t x = v_new[new_off + 16 * ct + r16];
+        put16(vr[k][ct], rn & 7, x);
+        vpool[vidx(l, pages[jn], rn, 16 * ct + r16, P, D)] = x;
+      }
     }
   }
 
-  // logits on MFMA
+  // q.K^T
   float sv[NG][HG];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
@@ -133,23 +148,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     const bool valid = q4 == 0 && tk < n;
 #pragma unroll
     for (int h = 0; h < HG; ++h) sv[j][h] = valid ? acc[h] * scale : -INFINITY;
-    if (valid && write_logits) {
-      float4 o4 = make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
-      *reinterpret_cast<float4*>(logits + ((static_cast<int64_t>(g) * L + l) * cap + tk) * HG) = o4;
-    }
+    if (valid && write_logits)
+      *reinterpret_cast<float4*>(logits + ((static_cast<int64_t>(g) * L + l) * lstride + tk) * HG) =
+          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
   }
 
-  // wave max / exp / sum
+  // per-head max and sum over the wave's slots (all live logits sit in lanes 0..15)
   float mh[HG], lh[HG];
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
     float m = sv[0][h];
 #pragma unroll
     for (int j = 1; j < NG; ++j) m = fmaxf(m, sv[j][h]);
-    mh[h] = wave_max(m);
-  }
-#pragma unroll
-  for (int h = 0; h < HG; ++h) {
+    mh[h] = row16_max(m);
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -157,53 +168,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
       sv[j][h] = p;
       sum += p;
     }
-    lh[h] = wave_sum(sum);
+    lh[h] = row16_sum(sum);
   }
   if (q4 == 0) {
 #pragma unroll
     for (int j = 0; j < NG; ++j)
-      *reinterpret_cast<float4*>(&p_lds[wave][16 * j + r16][0]) =
-          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
-  }
-  __syncthreads();
-
-  // p . V
-  float acc[HG][8];
 #pragma unroll
-  for (int h = 0; h < HG; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 pp = *reinterpret_cast<const float4*>(&p_lds[wave][16 * j + q4 + 4 * u][0]);
-      float vf[8];
-      Vec16<bf16_t>::widen(vr[j][u], vf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        acc[0][e] += pp.x * vf[e];
-        acc[1][e] += pp.y * vf[e];
-        acc[2][e] += pp.z * vf[e];
-        acc[3][e] += pp.w * vf[e];
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < HG; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[h][e];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      acc[h][e] = v;
-    }
-  if (q4 == 0) {
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      *reinterpret_cast<float4*>(&o_lds[wave][h][8 * r16]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(&o_lds[wave][h][8 * r16 + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
+      for (int h = 0; h < HG; ++h) p_lds[wave][h][16 * j + r16] = sv[j][h];
   }
   if (lane == 0) {
 #pragma unroll
@@ -211,6 +182,41 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
       wstat[wave][h][0] = mh[h];
       wstat[wave][h][1] = lh[h];
     }
+  }
+  __syncthreads();
+
+  // p.V
+  f32x4 oacc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float4 a = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
+    const float4 c = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
+    const float pv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    uint32_t h16[8], l16[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = r16 < HG ? pv[e] : 0.f;
+      h16[e] = bf16_rne(x);
+      l16[e] = bf16_rne(x - __uint_as_float(h16[e] << 16));
+    }
+    const bf16x8 phi = as_bf16x8(make_uint4(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
+                                            h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16)));
+    const bf16x8 plo = as_bf16x8(make_uint4(l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
+                                            l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16)));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const bf16x8 vb = as_bf16x8(vr[k][ct]);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vb, oacc[ct], 0, 0, 0);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, oacc[ct], 0, 0, 0);
+    }
+  }
+  if (q4 == 0) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int h = 0; h < HG; ++h) o_lds[wave][h][16 * ct + r16] = oacc[ct][h];
   }
   __syncthreads();
 
@@ -238,16 +244,17 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
 
 // ---------------------------------------------------------------------------
 // Generic VALU version (fp32 or bf16, head_dim 64 or 128): lanes split each
-// row into 16-byte pieces; dot products are reduced with cross-lane adds.
-// Used for the fp32 cache and for head_dim 64.
+// K row into 16-byte pieces and reduce the dot products with cross-lane
+// adds; p.V reads the channel-major V pages element-wise.  Used for the
+// fp32 cache and for head_dim 64.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int HG, int NT, int CT>
 __global__ __launch_bounds__(NT) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ ptab,
     const int* __restrict__ count, float* __restrict__ logits, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int L, int G, int Hkv, int Hq, int64_t P, int maxpages, int64_t cap,
-    int S, float scale, int write_logits) {
+    float* __restrict__ part_o, int L, int G, int Hkv, int Hq, int64_t P, int maxpages,
+    int64_t lstride, int S, float scale, int write_logits) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = D / EPL;
   constexpr int TPW = kWave / LPT;
@@ -270,9 +277,6 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   const int tnew = n - 1;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
   const int64_t new_off = (static_cast<int64_t>(l * B + b) * Hkv + kvh) * D + sub * EPL;
-  auto row_of = [&](int t) {
-    return pool_row(l, pt[t / kPageTokens], 0, t % kPageTokens, P, 1, kPageTokens) * D + sub * EPL;
-  };
 
   float qv[HG][EPL];
   {
@@ -289,11 +293,12 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
       raw[u] = make_uint4(0, 0, 0, 0);
       if (i < cnt) {
         const int t = t0 + i;
+        T* row = kpool + kidx(l, pt[t / kPageTokens], t % kPageTokens, sub * EPL, P, D);
         if (t == tnew) {
           raw[u] = *reinterpret_cast<const uint4*>(k_new + new_off);
-          *reinterpret_cast<uint4*>(kpool + row_of(t)) = raw[u];
+          *reinterpret_cast<uint4*>(row) = raw[u];
         } else {
-          raw[u] = *reinterpret_cast<const uint4*>(kpool + row_of(t));
+          raw[u] = *reinterpret_cast<const uint4*>(row);
         }
       }
     }
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
 #pragma unroll
         for (int h = 0; h < HG; ++h) acc[h] += __shfl_xor(acc[h], o, kWave);
       if (i < cnt && sub == 0) {
-        float* dst = logits + ((static_cast<int64_t>(g) * L + l) * cap + t0 + i) * HG;
+        float* dst = logits + ((static_cast<int64_t>(g) * L + l) * lstride + t0 + i) * HG;
 #pragma unroll
         for (int h = 0; h < HG; ++h) {
           const float s = acc[h] * scale;
@@ -374,34 +379,28 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   for (int h = 0; h < HG; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  for (int base = wave * TPW; base < cnt; base += NW * TPW * U) {
-    uint4 raw[U];
+  for (int base = wave * TPW; base < cnt; base += NW * TPW) {
+    const int i = base + tslot;
+    if (i < cnt) {
+      const int t = t0 + i;
+      const int page = pt[t / kPageTokens], r = t % kPageTokens;
+      uint4 raw;
+      T* vv = reinterpret_cast<T*>(&raw);
+      if (t == tnew) {
+        raw = *reinterpret_cast<const uint4*>(v_new + new_off);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * NW * TPW + tslot;
-      raw[u] = make_uint4(0, 0, 0, 0);
-      if (i < cnt) {
-        const int t = t0 + i;
-        if (t == tnew) {
-          raw[u] = *reinterpret_cast<const uint4*>(v_new + new_off);
-          *reinterpret_cast<uint4*>(vpool + row_of(t)) = raw[u];
-        } else {
-          raw[u] = *reinterpret_cast<const uint4*>(vpool + row_of(t));
-        }
+        for (int e = 0; e < EPL; ++e) vpool[vidx(l, page, r, sub * EPL + e, P, D)] = vv[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vv[e] = vpool[vidx(l, page, r, sub * EPL + e, P, D)];
       }
-    }
+      float vf[EPL];
+      Vec16<T>::widen(raw, vf);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + u * NW * TPW + tslot;
-      if (i < cnt) {
-        float vf[EPL];
-        Vec16<T>::widen(raw[u], vf);
+      for (int h = 0; h < HG; ++h) {
+        const float p = s_lds[i][h];
 #pragma unroll
-        for (int h = 0; h < HG; ++h) {
-          const float p = s_lds[i][h];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];
-        }
+        for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];
       }
     }
   }
@@ -430,21 +429,22 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   }
 }
 
-// MFMA kernel shape: 4 waves x 4 groups of 16 slots = 256 slots per split.
-constexpr int kMfmaNG = 4, kMfmaNW = 4;
-static_assert(kMfmaNG * 16 * kMfmaNW == kAttnChunk, "split size");
+// MFMA kernel shape: 4 waves x 64 slots = 256 slots per split.
+constexpr int kMfmaNW = 4;
+static_assert(kMfmaNW * 64 == kAttnChunk, "split size");
 
 template <typename T, int D>
 static hipError_t attention_valu(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                                  int n_max, int write_logits) {
   constexpr int NT = 256;
   const auto& cf = c->cfg;
-  dim3 grid((n_max + kAttnChunk - 1) / kAttnChunk, c->G, cf.n_layers);
+  const int splits = (n_max + kAttnChunk - 1) / kAttnChunk;
+  dim3 grid(splits, c->G, cf.n_layers);
   attn_valu_kernel<T, D, 4, NT, kAttnChunk><<<grid, NT, 0, c->stream>>>(
       static_cast<const T*>(q), static_cast<const T*>(k_new), static_cast<const T*>(v_new),
       static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.count,
       c->d.logits, c->d.part_ml, c->d.part_o, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
-      c->maxpages, c->cap, c->max_splits, 1.0f / sqrtf(static_cast<float>(D)), write_logits);
+      c->maxpages, c->lstride, splits, 1.0f / sqrtf(static_cast<float>(D)), write_logits);
   return hipGetLastError();
 }
 
@@ -454,13 +454,14 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
   const int D = cf.head_dim;
   if (c->HG != 4) return hipErrorInvalidValue;
   if (cf.dtype == KVEV_BF16 && D == 128) {
-    dim3 grid((n_max + kAttnChunk - 1) / kAttnChunk, c->G, cf.n_layers);
-    attn_mfma_kernel<kMfmaNG, kMfmaNW><<<grid, kMfmaNW * kWave, 0, c->stream>>>(
+    const int splits = (n_max + kAttnChunk - 1) / kAttnChunk;
+    dim3 grid(splits, c->G, cf.n_layers);
+    attn_mfma_kernel<kMfmaNW><<<grid, kMfmaNW * kWave, 0, c->stream>>>(
         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
         static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
         static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.logits, c->d.part_ml,
-        c->d.part_o, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P, c->maxpages, c->cap,
-        c->max_splits, 1.0f / sqrtf(128.0f), write_logits);
+        c->d.part_o, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P, c->maxpages, c->lstride,
+        splits, 1.0f / sqrtf(128.0f), write_logits);
     return hipGetLastError();
   }
   if (cf.dtype == KVEV_BF16) return attention_valu<bf16_t, 64>(c, q, k_new, v_new, n_max, write_logits);

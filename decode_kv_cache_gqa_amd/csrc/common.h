@@ -7,6 +7,7 @@
 namespace kvev {
 
 constexpr int kWave = 64;
+constexpr int kPageTokens = 16;  // tokens per cache page
 
 // bf16 is stored as its upper 16 bits of an IEEE binary32.
 struct bf16_t {
@@ -55,11 +56,39 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Row of (layer, page, head-in-page, row-in-page) in a page pool laid out
-// [L][P][HPP][PT][D].
-__device__ __forceinline__ int64_t pool_row(int l, int page, int hs, int r, int64_t P, int HPP,
-                                            int PT) {
-  return ((static_cast<int64_t>(l) * P + page) * HPP + hs) * PT + r;
+// K pages are token-major: element (layer l, page p, row r, channel c) of a
+// pool laid out [L][P][16][D] is at kidx(...).  V pages are channel-major,
+// [L][P][D][16], so that 8 consecutive tokens of one channel are 16
+// contiguous bytes: the operand layout of the p.V matrix-core product.
+__device__ __forceinline__ int64_t kidx(int l, int page, int r, int c, int64_t P, int D) {
+  return ((static_cast<int64_t>(l) * P + page) * kPageTokens + r) * D + c;
+}
+__device__ __forceinline__ int64_t vidx(int l, int page, int r, int c, int64_t P, int D) {
+  return ((static_cast<int64_t>(l) * P + page) * D + c) * kPageTokens + r;
+}
+
+// Butterfly over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0x128>(v));
+  v = fmaxf(v, dpp_f<0x124>(v));
+  v = fmaxf(v, dpp_f<0x122>(v));
+  return fmaxf(v, dpp_f<0x121>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  return v + dpp_f<0x121>(v);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 }  // namespace kvev

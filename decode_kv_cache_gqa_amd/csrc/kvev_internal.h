@@ -7,10 +7,10 @@
 #include <vector>
 
 #include "../../include/kvev.h"
+#include "common.h"
 
 namespace kvev {
 
-constexpr int kPageTokens = 16;
 constexpr int kAttnChunk = 256;   // slots per attention split
 constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies itself
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
@@ -25,8 +25,8 @@ struct DevState {
   float* score = nullptr;  // [G][cap] utility of each slot
   int* count = nullptr;    // [G] tokens in the group
   int* nextpos = nullptr;  // [G] position the next appended token takes
-  float* logits = nullptr; // [G][L][cap][HG] fp32 logits of the last step
-  float* part_ml = nullptr;// [L][G][S][HG][2] per-split (max, sum)
+  float* logits = nullptr; // [G][L][lstride][HG] fp32 logits of the current step
+  float* part_ml = nullptr;// [L][G][S][HG][2] per-split (max, sum), S = splits of the step
   float* part_o = nullptr; // [L][G][S][HG][D] per-split unnormalised output
   float* ml = nullptr;     // [L][G][HG][2] global (max, sum)
   int* mv_src = nullptr;   // [G][cap] compaction moves
@@ -34,6 +34,10 @@ struct DevState {
   int* nmoves = nullptr;   // [G]
   int* errflag = nullptr;  // [1] device-side consistency failures (bit mask)
   unsigned* grpctr = nullptr;  // [G] arrival counters of the post kernel (0 between launches)
+  unsigned long long* blk_key = nullptr;  // [G][max_post_blocks] per-block minimum eviction key
+  int* blk_slot = nullptr;                // [G][max_post_blocks] its slot
+  int* blk_page = nullptr;                // [G][max_post_blocks] that slot's page
+  float* blk_sum = nullptr;               // [G][max_post_blocks] per-block utility sum
 };
 
 struct Profiler {
@@ -55,7 +59,9 @@ struct kvev_ctx {
   int device = 0;
   int G = 0, HG = 0, PT = kvev::kPageTokens, maxpages = 0;
   int64_t cap = 0, P = 0;
+  int64_t lstride = 0;  // slot stride of the logit scratch in the current step
   int max_splits = 0;
+  int max_post_blocks = 0;
   size_t elem = 0;
   kvev::DevState d;
   // host mirrors (kept exact: every count change is deterministic)
@@ -77,8 +83,8 @@ hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const voi
 hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
 hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                             int n_max, int write_logits);
-hipError_t launch_post(kvev_ctx* c, float* out, int n_max, int refresh, int do_select,
-                       int64_t budget, int inline_moves);
+hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
+                       int refresh, int do_select, int64_t budget, int inline_moves);
 hipError_t launch_select(kvev_ctx* c, int64_t budget);
 hipError_t launch_moves(kvev_ctx* c, int max_moves);
 hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);

@@ -233,41 +233,83 @@ __device__ int select_group(int n, int B, int newest, int n_sink, int n_recent,
   return nm;
 }
 
-// Copy `nm` planned moves of one group for every layer (K and V rows).
+// Copy `nm` planned moves of one group for every layer: the K row (16-byte
+// pieces of a token-major page) and the V column (D elements of a
+// channel-major page).  The page table is shared by all layers, so each
+// move's two pages are looked up once; all loads of a batch are issued
+// before its stores.
 template <typename T, int D, int NT>
 __device__ void copy_moves(T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ pt,
                            const int* __restrict__ src, const int* __restrict__ dst, int nm, int L,
                            int64_t P, int64_t cap) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
-  const int total = nm * L * LPR;
-  for (int idx = threadIdx.x; idx < total; idx += NT) {
-    const int sub = idx % LPR, rest = idx / LPR;
-    const int l = rest % L, j = rest / L;
+  constexpr int KB = 4;  // 16-byte K pieces per thread per batch
+  constexpr int VB = 8;  // V elements per thread per batch
+  for (int j = 0; j < nm; ++j) {
     const int s = src[j], d = dst[j];
     if (s < 0 || s >= cap || d < 0 || d >= cap) continue;
-    const int64_t rs = pool_row(l, pt[s / kPageTokens], 0, s % kPageTokens, P, 1, kPageTokens) * D + sub * EPL;
-    const int64_t rd = pool_row(l, pt[d / kPageTokens], 0, d % kPageTokens, P, 1, kPageTokens) * D + sub * EPL;
-    *reinterpret_cast<uint4*>(kpool + rd) = *reinterpret_cast<const uint4*>(kpool + rs);
-    *reinterpret_cast<uint4*>(vpool + rd) = *reinterpret_cast<const uint4*>(vpool + rs);
+    const int ps = pt[s / kPageTokens], pd = pt[d / kPageTokens];
+    const int rs = s % kPageTokens, rd = d % kPageTokens;
+    for (int base = 0; base < L * LPR; base += NT * KB) {
+      uint4 v[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int idx = base + u * NT + threadIdx.x;
+        if (idx < L * LPR)
+          v[u] = *reinterpret_cast<const uint4*>(kpool + kidx(idx / LPR, ps, rs, (idx % LPR) * EPL, P, D));
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int idx = base + u * NT + threadIdx.x;
+        if (idx < L * LPR)
+          *reinterpret_cast<uint4*>(kpool + kidx(idx / LPR, pd, rd, (idx % LPR) * EPL, P, D)) = v[u];
+      }
+    }
+    for (int base = 0; base < L * D; base += NT * VB) {
+      T v[VB];
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int idx = base + u * NT + threadIdx.x;
+        if (idx < L * D) v[u] = vpool[vidx(idx / D, ps, rs, idx % D, P, D)];
+      }
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int idx = base + u * NT + threadIdx.x;
+        if (idx < L * D) vpool[vidx(idx / D, pd, rd, idx % D, P, D)] = v[u];
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Post-attention kernel, grid (blocks per group, groups).  Every block:
+// Post-attention kernel, grid (blocks per group, groups); block c owns slots
+// [64c, 64c + 64) and, when c < L, the output of layer c.  Every block:
 //  * merges the splits' (max, sum) of all layers of its group;
-//  * block c < L writes the attention output of layer c
-//    (out = sum_s e^{m_s - M} o_s / Z);
+//  * block c < L writes the attention output of layer c,
+//    out = sum_s e^{m_s - M} o_s / Z;
 //  * on an observation step, folds its slots' probability mass layer by
 //    layer: mass_l[t] = sum_{h in group} exp(s_l[h][t] - M_l[h]) / Z_l[h],
 //    m <- a*mass + (1-a)*m (EMA) or m <- m + mass (cumulative), l = 0..L-1
 //    ("What Matters ...", section 3.1 Eq.1 pooled per KV head, Eq.3/Eq.4,
-//    appendix E "Layer scoring"); the new token starts at 0.
-// The group's last block to finish (fence + arrival counter, no waiting)
-// records the new token's position, gives it the mean utility on a
-// non-observation step (appendix E "New token insertion"), commits the
-// count and, when asked, selects and compacts the group.
+//    appendix E "Layer scoring"); the new token starts at 0;
+//  * publishes, for its slots other than the new token's, the minimum
+//    eviction key (order-preserving score key, position) over the
+//    unprotected slots and the sum of the utilities.
+// All loads a block needs are issued before the first use.  The group's
+// last block to finish (arrival counter, no waiting) gives the new token the
+// mean utility on a non-observation step (appendix E "New token insertion"),
+// records its position, commits the count and, when asked, selects and
+// compacts: with one token over budget the eviction is the minimum of the
+// published keys and the new token's key, and the only move copies the new
+// token (slot B) into the hole; otherwise a full radix select runs.
+// Data handed between blocks is written through to device scope and read
+// with device-scope loads; no agent-scope fence is used (on this GPU it
+// writes back the whole L2).
 // ---------------------------------------------------------------------------
+constexpr int kPostTok = 64;  // slots per post block (one wave's worth)
+constexpr int kMergeBatch = 16;
+
 struct PostArgs {
   int* count;
   int* pos;
@@ -278,6 +320,10 @@ struct PostArgs {
   const float* part_o;
   float* out;
   unsigned* grpctr;
+  unsigned long long* blk_key;
+  int* blk_slot;
+  int* blk_page;
+  float* blk_sum;
   int* mv_src;
   int* mv_dst;
   int* nmoves;
@@ -285,17 +331,17 @@ struct PostArgs {
   void* kpool;
   void* vpool;
   const int* ptab;
-  int L, G, Hkv, Hq, S, CT, maxpages;
-  int64_t cap, P;
+  const void* k_new;
+  const void* v_new;
+  int L, G, Hkv, Hq, S, CT, maxpages, max_blk;
+  int64_t cap, P, lstride;
   float a;
   int cumulative, refresh, do_select, B, n_sink, n_recent, inline_moves, nblk;
 };
 
-constexpr int kPostTok = 64;  // slots folded per post block
-
 template <typename T, int D, int HG, int NT>
 __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
-  static_assert(NT % kPostTok == 0, "block shape");
+  static_assert(NT % kPostTok == 0 && NT >= 256, "block shape");
   constexpr int LG = NT / kPostTok;  // layer lanes per slot
   extern __shared__ float dyn[];
   const int L = A.L;
@@ -303,28 +349,81 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   float* s_w = dyn + L * HG * 2;            // [HG][S] split weights of this block's layer
   float* s_mass = s_w + HG * A.S;           // [L][kPostTok]
   __shared__ float red[NT / kWave];
+  __shared__ unsigned long long s_key[NT / kWave];
+  __shared__ int s_slot[NT / kWave];
+  __shared__ int s_page[NT / kWave];
   __shared__ int s_last;
-  const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
   const int n = A.count[g] + 1;
+  const int newest = A.nextpos[g];
   const int ns = (n + A.CT - 1) / A.CT;
   const int Bsz = A.G / A.Hkv, b = g / A.Hkv, kvh = g % A.Hkv;
+  const int tbase = c * kPostTok;
+  int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
+  float* gs = A.score + static_cast<int64_t>(g) * A.cap;
+  auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
 
-  // merge every layer's split statistics: (M, Z) per (layer, head)
-  for (int i = tid; i < L * HG; i += NT) {
-    const int l = i / HG, h = i % HG;
-    const float2* pm = reinterpret_cast<const float2*>(A.part_ml) +
-                       (static_cast<int64_t>(l) * A.G + g) * A.S * HG + h;
-    float M = -INFINITY, Z = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float2 v[8];
+  // ---- issue every load of the block ---------------------------------------
+  const int tl = tid % kPostTok, lg = tid / kPostTok;
+  const int t = tbase + tl;
+  const bool fold = A.refresh && tbase < n;
+  float4 s4[8];
+  if (fold) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = s0 + k < ns ? pm[(s0 + k) * HG] : make_float2(-INFINITY, 0.f);
+    for (int k = 0; k < 8; ++k) {
+      const int l = lg + k * LG;
+      s4[k] = (t < n && l < L) ? *reinterpret_cast<const float4*>(
+                                     A.logits + ((static_cast<int64_t>(g) * L + l) * A.lstride + t) * HG)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  float prior = 0.f;
+  int mypos = 0, mypage = 0;
+  if (tid < kPostTok && t < n - 1) {
+    prior = gs[t];
+    mypos = gp[t];
+    mypage = A.ptab[static_cast<int64_t>(g) * A.maxpages + t / kPageTokens];
+  }
+  float2 pm[kMergeBatch];
+  const int ml_l = tid / HG, ml_h = tid % HG;
+  const float2* pmb = reinterpret_cast<const float2*>(A.part_ml) +
+                      (static_cast<int64_t>(ml_l) * A.G + g) * A.S * HG + ml_h;
+  if (tid < L * HG) {
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) pm[k] = k < ns ? pmb[k * HG] : make_float2(-INFINITY, 0.f);
+  }
+  float po[2][kMergeBatch];
+  const float* pob = A.part_o + (static_cast<int64_t>(c) * A.G + g) * A.S * HG * D;
+  if (c < L) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + e * NT;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        po[e][k] = (idx < HG * D && k < ns) ? pob[k * HG * D + idx] : 0.f;
+    }
+  }
+
+  // ---- merge every layer's split statistics: (M, Z) per (layer, head) ------
+  for (int i = tid; i < L * HG; i += NT) {
+    float M = -INFINITY, Z = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+      float2 v[kMergeBatch];
+      if (i == tid && s0 == 0) {
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) v[k] = pm[k];
+      } else {
+        const float2* pb = reinterpret_cast<const float2*>(A.part_ml) +
+                           (static_cast<int64_t>(i / HG) * A.G + g) * A.S * HG + i % HG;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < ns ? pb[(s0 + k) * HG] : make_float2(-INFINITY, 0.f);
+      }
       float Mb = M;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) Mb = fmaxf(Mb, v[k].x);
+      for (int k = 0; k < kMergeBatch; ++k) Mb = fmaxf(Mb, v[k].x);
       float z = M == -INFINITY ? 0.f : Z * __expf(M - Mb);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) z += v[k].x == -INFINITY ? 0.f : v[k].y * __expf(v[k].x - Mb);
+      for (int k = 0; k < kMergeBatch; ++k) z += v[k].x == -INFINITY ? 0.f : v[k].y * __expf(v[k].x - Mb);
       M = Mb;
       Z = z;
     }
@@ -333,73 +432,95 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   __syncthreads();
 
-  // attention output of layer c
+  // ---- attention output of layer c -------------------------------------------
   if (c < L) {
     const int l = c;
-    const float2* pm = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * A.S * HG;
+    const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * A.S * HG;
     for (int i = tid; i < HG * ns; i += NT) {
       const int h = i / ns, s = i % ns;
-      const float ms = pm[s * HG + h].x;
+      const float ms = pml[s * HG + h].x;
       s_w[h * A.S + s] = ms == -INFINITY ? 0.f : __expf(ms - s_ml[(l * HG + h) * 2]);
     }
     __syncthreads();
-    const float* po = A.part_o + (static_cast<int64_t>(l) * A.G + g) * A.S * HG * D;
-    for (int idx = tid; idx < HG * D; idx += NT) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + e * NT;
+      if (idx >= HG * D) continue;
       const int h = idx / D, cc = idx % D;
       float o = 0.f;
-      for (int s0 = 0; s0 < ns; s0 += 8) {
-        float v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = s0 + k < ns ? po[(s0 + k) * HG * D + idx] : 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o += s0 + k < ns ? s_w[h * A.S + s0 + k] * v[k] : 0.f;
-      }
+      for (int k = 0; k < kMergeBatch; ++k) o += k < ns ? s_w[h * A.S + k] * po[e][k] : 0.f;
+      for (int s = kMergeBatch; s < ns; ++s) o += s_w[h * A.S + s] * pob[s * HG * D + idx];
       A.out[(static_cast<int64_t>(l * Bsz + b) * A.Hq + kvh * HG + h) * D + cc] = o / s_ml[(l * HG + h) * 2 + 1];
     }
   }
 
-  // probability mass per (layer, slot), then the layer-ordered fold
-  const int tbase = c * kPostTok;
-  if (A.refresh && tbase < n) {
-    const int tl = tid % kPostTok, lg = tid / kPostTok;
-    const int t = tbase + tl;
+  // ---- probability mass per (layer, slot), then the layer-ordered fold --------
+  float myscore = prior;
+  if (fold) {
     if (t < n) {
-      for (int l0 = lg; l0 < L; l0 += LG * 8) {
-        float4 s4[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int l = l0 + k * LG;
-          s4[k] = l < L ? *reinterpret_cast<const float4*>(
-                              A.logits + ((static_cast<int64_t>(g) * L + l) * A.cap + t) * HG)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int l = l0 + k * LG;
-          if (l >= L) continue;
-          const float* ml = &s_ml[l * HG * 2];
-          s_mass[l * kPostTok + tl] = __expf(s4[k].x - ml[0]) / ml[1] + __expf(s4[k].y - ml[2]) / ml[3] +
-                                      __expf(s4[k].z - ml[4]) / ml[5] + __expf(s4[k].w - ml[6]) / ml[7];
-        }
+      for (int k = 0; k < 8; ++k) {
+        const int l = lg + k * LG;
+        if (l >= L) continue;
+        const float* ml = &s_ml[l * HG * 2];
+        s_mass[l * kPostTok + tl] = __expf(s4[k].x - ml[0]) / ml[1] + __expf(s4[k].y - ml[2]) / ml[3] +
+                                    __expf(s4[k].z - ml[4]) / ml[5] + __expf(s4[k].w - ml[6]) / ml[7];
+      }
+      for (int l = lg + 8 * LG; l < L; l += LG) {  // more than 8 * LG layers
+        const float4 x = *reinterpret_cast<const float4*>(
+            A.logits + ((static_cast<int64_t>(g) * L + l) * A.lstride + t) * HG);
+        const float* ml = &s_ml[l * HG * 2];
+        s_mass[l * kPostTok + tl] = __expf(x.x - ml[0]) / ml[1] + __expf(x.y - ml[2]) / ml[3] +
+                                    __expf(x.z - ml[4]) / ml[5] + __expf(x.w - ml[6]) / ml[7];
       }
     }
     __syncthreads();
     if (tid < kPostTok && t < n) {
-      float m = (t == n - 1) ? 0.f : A.score[static_cast<int64_t>(g) * A.cap + t];
+      float m = (t == n - 1) ? 0.f : prior;
       const float keep = 1.0f - A.a;
       for (int l = 0; l < L; ++l) {
         const float mass = s_mass[l * kPostTok + tl];
         m = A.cumulative ? m + mass : A.a * mass + keep * m;
       }
-      st_coherent(A.score + static_cast<int64_t>(g) * A.cap + t, m);
+      st_coherent(gs + t, m);
+      myscore = m;
     }
   }
 
-  // Arrival: the group's last block finishes the step.  The only data other
-  // blocks hand over are the utilities, written through to device scope
-  // above; waiting for those stores before the arrival counter is bumped
-  // orders them before it, and the last block reads them with device-scope
-  // loads.  (No agent-scope fence: on this GPU it writes back the whole L2.)
+  // ---- block summary over slots other than the new token's -------------------
+  if (tid < kPostTok) {
+    const bool mine = t < n - 1;
+    unsigned long long key = ~0ull;
+    int slot = -1;
+    if (mine && is_cand(mypos)) {
+      key = (static_cast<unsigned long long>(float_key(myscore)) << 32) | static_cast<uint32_t>(mypos);
+      slot = t;
+    }
+    int page = mypage;
+    float sum = mine ? myscore : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long y = __shfl_xor(key, o, kWave);
+      const int ys = __shfl_xor(slot, o, kWave);
+      const int yp = __shfl_xor(page, o, kWave);
+      if (y < key) {
+        key = y;
+        slot = ys;
+        page = yp;
+      }
+    }
+    sum = wave_sum(sum);
+    if (tid == 0) {
+      const int64_t bi = static_cast<int64_t>(g) * A.max_blk + c;
+      st_coherent(A.blk_key + bi, key);
+      st_coherent(A.blk_slot + bi, slot);
+      st_coherent(A.blk_page + bi, page);
+      st_coherent(A.blk_sum + bi, sum);
+    }
+  }
+
+  // ---- arrival ----------------------------------------------------------------------
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
@@ -410,29 +531,78 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   __syncthreads();
   if (!s_last) return;
 
-  int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
-  float* gs = A.score + static_cast<int64_t>(g) * A.cap;
-  const int newest = A.nextpos[g];
-  if (!A.refresh) {
-    float sum = 0.f;
-    for (int base = 0; base < n - 1; base += NT * 8) {
-      float v[8];
+  // ---- the group's last block ------------------------------------------------
+  // Everything it may need is loaded in one batch: the block summaries, the
+  // new token's utility (observation step) and page, and, for the move of
+  // the new token into a hole, its K/V rows from the step inputs.
+  const bool one_over = A.do_select && n == A.B + 1;
+  constexpr int EPL = Vec16<T>::N;
+  constexpr int LPR = D / EPL;
+  constexpr int NCH = (64 * LPR + NT - 1) / NT;  // 16-byte row pieces per thread (L <= 64)
+  uint4 kpre[NCH], vpre[NCH];
+  if (one_over) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * NT + tid;
-        v[u] = i < n - 1 ? ld_state<true>(gs + i) : 0.f;
+    for (int u = 0; u < NCH; ++u) {
+      const int idx = u * NT + tid;
+      if (idx < L * LPR) {
+        const int64_t in = (static_cast<int64_t>((idx / LPR) * Bsz + b) * A.Hkv + kvh) * D + (idx % LPR) * EPL;
+        kpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.k_new) + in);
+        vpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.v_new) + in);
       }
+    }
+  }
+  const int newpage = A.ptab[static_cast<int64_t>(g) * A.maxpages + (n - 1) / kPageTokens];
+  const float newscore_obs = A.refresh ? ld_state<true>(gs + (n - 1)) : 0.f;
+  float part = 0.f;
+  unsigned long long bkey = ~0ull;
+  int bslot = -1, bpage = 0;
+  for (int i = tid; i < A.nblk; i += NT) {
+    const int64_t bi = static_cast<int64_t>(g) * A.max_blk + i;
+    part += ld_state<true>(A.blk_sum + bi);
+    const unsigned long long k2 = ld_state<true>(A.blk_key + bi);
+    const int s2 = ld_state<true>(A.blk_slot + bi);
+    const int p2 = ld_state<true>(A.blk_page + bi);
+    if (k2 < bkey) {
+      bkey = k2;
+      bslot = s2;
+      bpage = p2;
+    }
+  }
+  part = wave_sum(part);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(bkey, o, kWave);
+    const int ys = __shfl_xor(bslot, o, kWave);
+    const int yp = __shfl_xor(bpage, o, kWave);
+    if (y < bkey) {
+      bkey = y;
+      bslot = ys;
+      bpage = yp;
     }
-    sum = wave_sum(sum);
-    if ((tid % kWave) == 0) red[tid / kWave] = sum;
-    __syncthreads();
-    if (tid == 0) {
-      float tot = 0.f;
-      for (int w = 0; w < NT / kWave; ++w) tot += red[w];
-      st_coherent(gs + (n - 1), n > 1 ? tot / static_cast<float>(n - 1) : 0.f);
+  }
+  if (lane == 0) {
+    red[tid / kWave] = part;
+    s_key[tid / kWave] = bkey;
+    s_slot[tid / kWave] = bslot;
+    s_page[tid / kWave] = bpage;
+  }
+  __syncthreads();
+  float total = 0.f;
+  bkey = s_key[0];
+  bslot = s_slot[0];
+  bpage = s_page[0];
+  for (int w = 0; w < NT / kWave; ++w) {
+    total += red[w];
+    if (s_key[w] < bkey) {
+      bkey = s_key[w];
+      bslot = s_slot[w];
+      bpage = s_page[w];
     }
+  }
+  float newscore = newscore_obs;
+  if (!A.refresh) {
+    newscore = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
+    if (tid == 0) st_coherent(gs + (n - 1), newscore);
   }
   if (tid == 0) {
     st_coherent(gp + (n - 1), newest);
@@ -441,19 +611,56 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
   int final_n = n, nm = 0;
-  if (A.do_select && n > A.B) {
+  if (one_over) {
+    // one over budget: evict the smallest key, the new token included
+    if (is_cand(newest)) {
+      const unsigned long long kn =
+          (static_cast<unsigned long long>(float_key(newscore)) << 32) | static_cast<uint32_t>(newest);
+      if (kn < bkey) {
+        bkey = kn;
+        bslot = n - 1;
+        bpage = newpage;
+      }
+    }
+    final_n = A.B;
+    if (bslot < 0) {
+      if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
+    } else if (bslot < A.B) {
+      // the new token (slot B) fills the hole: state, then its K/V rows
+      const int ev = bslot, rd = ev % kPageTokens;
+      if (tid == 0) {
+        gp[ev] = newest;
+        gs[ev] = newscore;
+      }
+      T* kp = static_cast<T*>(A.kpool);
+      T* vp = static_cast<T*>(A.vpool);
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int idx = u * NT + tid;
+        if (idx >= L * LPR) continue;
+        const int l = idx / LPR, c0 = (idx % LPR) * EPL;
+        *reinterpret_cast<uint4*>(kp + kidx(l, bpage, rd, c0, A.P, D)) = kpre[u];
+        const T* ve = reinterpret_cast<const T*>(&vpre[u]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vp[vidx(l, bpage, rd, c0 + e, A.P, D)] = ve[e];
+      }
+    }
+  } else if (A.do_select && n > A.B) {
     int* src = A.mv_src + static_cast<int64_t>(g) * A.cap;
     int* dst = A.mv_dst + static_cast<int64_t>(g) * A.cap;
     nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag);
     final_n = A.B;
-    if (A.inline_moves)
+    if (A.inline_moves) {
       copy_moves<T, D, NT>(static_cast<T*>(A.kpool), static_cast<T*>(A.vpool),
                            A.ptab + static_cast<int64_t>(g) * A.maxpages, src, dst, nm, L, A.P, A.cap);
+      nm = 0;
+    }
   }
   if (tid == 0) {
     A.count[g] = final_n;
-    A.nmoves[g] = A.inline_moves ? 0 : nm;
+    A.nmoves[g] = nm;
   }
 }
 
@@ -491,27 +698,32 @@ __global__ __launch_bounds__(NT) void move_kernel(T* __restrict__ kpool, T* __re
                                                   int maxpages, int64_t cap, int per_block) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
-  constexpr int RPB = NT / LPR;
   const int g = blockIdx.y, l = blockIdx.z;
   const int nm = nmoves[g];
   const int j0 = blockIdx.x * per_block;
   const int j1 = min(nm, j0 + per_block);
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
-  const int sub = threadIdx.x % LPR;
-  for (int j = j0 + threadIdx.x / LPR; j < j1; j += RPB) {
-    const int s = mv_src[static_cast<int64_t>(g) * cap + j];
-    const int d = mv_dst[static_cast<int64_t>(g) * cap + j];
+  const int* ms = mv_src + static_cast<int64_t>(g) * cap;
+  const int* md = mv_dst + static_cast<int64_t>(g) * cap;
+  for (int idx = threadIdx.x; idx < (j1 - j0) * LPR; idx += NT) {
+    const int j = j0 + idx / LPR, sub = idx % LPR;
+    const int s = ms[j], d = md[j];
     if (s < 0 || s >= cap || d < 0 || d >= cap) continue;
-    const int64_t rs = pool_row(l, pt[s / kPageTokens], 0, s % kPageTokens, P, 1, kPageTokens) * D;
-    const int64_t rd = pool_row(l, pt[d / kPageTokens], 0, d % kPageTokens, P, 1, kPageTokens) * D;
-    *reinterpret_cast<uint4*>(kpool + rd + sub * EPL) =
-        *reinterpret_cast<const uint4*>(kpool + rs + sub * EPL);
-    *reinterpret_cast<uint4*>(vpool + rd + sub * EPL) =
-        *reinterpret_cast<const uint4*>(vpool + rs + sub * EPL);
+    *reinterpret_cast<uint4*>(kpool + kidx(l, pt[d / kPageTokens], d % kPageTokens, sub * EPL, P, D)) =
+        *reinterpret_cast<const uint4*>(kpool + kidx(l, pt[s / kPageTokens], s % kPageTokens, sub * EPL, P, D));
+  }
+  for (int idx = threadIdx.x; idx < (j1 - j0) * D; idx += NT) {
+    const int j = j0 + idx / D, c = idx % D;
+    const int s = ms[j], d = md[j];
+    if (s < 0 || s >= cap || d < 0 || d >= cap) continue;
+    vpool[vidx(l, pt[d / kPageTokens], d % kPageTokens, c, P, D)] =
+        vpool[vidx(l, pt[s / kPageTokens], s % kPageTokens, c, P, D)];
   }
 }
 
-// Prefill: copy k, v [L][Hkv][n][D] of one sequence into its groups' pages.
+// Prefill: copy k, v [L][Hkv][n][D] of one sequence into its groups' pages,
+// one page (16 tokens) per block; V goes through LDS to be stored
+// channel-major.  Rows of the last page beyond n are zero-filled.
 template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT) void scatter_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kpool, T* __restrict__ vpool,
@@ -519,18 +731,27 @@ __global__ __launch_bounds__(NT) void scatter_kernel(const T* __restrict__ k, co
                                                      int64_t n, int64_t P, int maxpages) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
-  constexpr int RPB = NT / LPR;
-  const int h = blockIdx.y, l = blockIdx.z;
+  __shared__ T tile[kPageTokens][D + EPL];
+  const int pg = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int g = seq * Hkv + h;
-  const int sub = threadIdx.x % LPR;
-  const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR; t < n;
-       t += static_cast<int64_t>(gridDim.x) * RPB) {
-    const int64_t src = ((static_cast<int64_t>(l) * Hkv + h) * n + t) * D + sub * EPL;
-    const int64_t dst = pool_row(l, pt[t / kPageTokens], 0, static_cast<int>(t % kPageTokens), P, 1,
-                                 kPageTokens) * D + sub * EPL;
-    *reinterpret_cast<uint4*>(kpool + dst) = *reinterpret_cast<const uint4*>(k + src);
-    *reinterpret_cast<uint4*>(vpool + dst) = *reinterpret_cast<const uint4*>(v + src);
+  const int page = ptab[static_cast<int64_t>(g) * maxpages + pg];
+  const int64_t tb = static_cast<int64_t>(pg) * kPageTokens;
+  for (int idx = threadIdx.x; idx < kPageTokens * LPR; idx += NT) {
+    const int r = idx / LPR, sub = idx % LPR;
+    const int64_t t = tb + r;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (t < n) {
+      const int64_t src = ((static_cast<int64_t>(l) * Hkv + h) * n + t) * D + sub * EPL;
+      kv = *reinterpret_cast<const uint4*>(k + src);
+      vv = *reinterpret_cast<const uint4*>(v + src);
+    }
+    *reinterpret_cast<uint4*>(kpool + kidx(l, page, r, sub * EPL, P, D)) = kv;
+    *reinterpret_cast<uint4*>(&tile[r][sub * EPL]) = vv;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < D * kPageTokens; idx += NT) {
+    const int c = idx / kPageTokens, r = idx % kPageTokens;
+    vpool[vidx(l, page, r, c, P, D)] = tile[r][c];
   }
 }
 
@@ -541,23 +762,20 @@ __global__ __launch_bounds__(NT) void group_copy_kernel(T* __restrict__ kd, T* _
                                                         const int* __restrict__ ptab, int g,
                                                         int64_t n, int64_t ld, int64_t P,
                                                         int maxpages, int dir) {
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int RPB = NT / LPR;
   const int l = blockIdx.y;
-  const int sub = threadIdx.x % LPR;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR; t < n;
-       t += static_cast<int64_t>(gridDim.x) * RPB) {
-    const int64_t dense = (static_cast<int64_t>(l) * ld + t) * D + sub * EPL;
-    const int64_t paged = pool_row(l, pt[t / kPageTokens], 0, static_cast<int>(t % kPageTokens), P,
-                                   1, kPageTokens) * D + sub * EPL;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; idx < n * D;
+       idx += static_cast<int64_t>(gridDim.x) * NT) {
+    const int64_t t = idx / D;
+    const int c = static_cast<int>(idx % D);
+    const int page = pt[t / kPageTokens], r = static_cast<int>(t % kPageTokens);
+    const int64_t dense = (static_cast<int64_t>(l) * ld + t) * D + c;
     if (dir == 0) {
-      *reinterpret_cast<uint4*>(kd + dense) = *reinterpret_cast<const uint4*>(kpool + paged);
-      *reinterpret_cast<uint4*>(vd + dense) = *reinterpret_cast<const uint4*>(vpool + paged);
+      kd[dense] = kpool[kidx(l, page, r, c, P, D)];
+      vd[dense] = vpool[vidx(l, page, r, c, P, D)];
     } else {
-      *reinterpret_cast<uint4*>(kpool + paged) = *reinterpret_cast<const uint4*>(kd + dense);
-      *reinterpret_cast<uint4*>(vpool + paged) = *reinterpret_cast<const uint4*>(vd + dense);
+      kpool[kidx(l, page, r, c, P, D)] = kd[dense];
+      vpool[vidx(l, page, r, c, P, D)] = vd[dense];
     }
   }
 }
@@ -593,8 +811,8 @@ hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd) {
 }
 
 template <typename T, int D>
-static hipError_t post_impl(kvev_ctx* c, float* out, int n_max, int refresh, int do_select,
-                            int64_t budget, int inline_moves) {
+static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
+                            int refresh, int do_select, int64_t budget, int inline_moves) {
   constexpr int NT = 256;
   const auto& cf = c->cfg;
   PostArgs A;
@@ -607,6 +825,13 @@ static hipError_t post_impl(kvev_ctx* c, float* out, int n_max, int refresh, int
   A.part_o = c->d.part_o;
   A.out = out;
   A.grpctr = c->d.grpctr;
+  A.blk_key = c->d.blk_key;
+  A.blk_slot = c->d.blk_slot;
+  A.blk_page = c->d.blk_page;
+  A.blk_sum = c->d.blk_sum;
+  A.max_blk = c->max_post_blocks;
+  A.k_new = k_new;
+  A.v_new = v_new;
   A.mv_src = c->d.mv_src;
   A.mv_dst = c->d.mv_dst;
   A.nmoves = c->d.nmoves;
@@ -618,7 +843,8 @@ static hipError_t post_impl(kvev_ctx* c, float* out, int n_max, int refresh, int
   A.G = c->G;
   A.Hkv = cf.n_kv_heads;
   A.Hq = cf.n_q_heads;
-  A.S = c->max_splits;
+  A.S = (n_max + kAttnChunk - 1) / kAttnChunk;
+  A.lstride = c->lstride;
   A.CT = kAttnChunk;
   A.maxpages = c->maxpages;
   A.cap = c->cap;
@@ -640,15 +866,15 @@ static hipError_t post_impl(kvev_ctx* c, float* out, int n_max, int refresh, int
   return hipGetLastError();
 }
 
-hipError_t launch_post(kvev_ctx* c, float* out, int n_max, int refresh, int do_select,
-                       int64_t budget, int inline_moves) {
+hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
+                       int refresh, int do_select, int64_t budget, int inline_moves) {
   if (c->HG != 4) return hipErrorInvalidValue;
   const int D = c->cfg.head_dim;
   if (c->cfg.dtype == KVEV_BF16)
-    return D == 128 ? post_impl<bf16_t, 128>(c, out, n_max, refresh, do_select, budget, inline_moves)
-                    : post_impl<bf16_t, 64>(c, out, n_max, refresh, do_select, budget, inline_moves);
-  return D == 128 ? post_impl<float, 128>(c, out, n_max, refresh, do_select, budget, inline_moves)
-                  : post_impl<float, 64>(c, out, n_max, refresh, do_select, budget, inline_moves);
+    return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves)
+                    : post_impl<bf16_t, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves);
+  return D == 128 ? post_impl<float, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves)
+                  : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves);
 }
 
 hipError_t launch_select(kvev_ctx* c, int64_t budget) {
@@ -662,7 +888,7 @@ hipError_t launch_select(kvev_ctx* c, int64_t budget) {
 
 template <typename T, int D>
 static hipError_t moves_impl(kvev_ctx* c, int max_moves) {
-  constexpr int NT = 256, PER = 64;
+  constexpr int NT = 256, PER = 16;
   dim3 grid((max_moves + PER - 1) / PER, c->G, c->cfg.n_layers);
   move_kernel<T, D, NT><<<grid, NT, 0, c->stream>>>(
       static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.mv_src,
@@ -680,10 +906,8 @@ hipError_t launch_moves(kvev_ctx* c, int max_moves) {
 template <typename T, int D>
 static hipError_t scatter_impl(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
   constexpr int NT = 256;
-  constexpr int RPB = NT / (D / Vec16<T>::N);
-  int64_t bx = (n + RPB - 1) / RPB;
-  if (bx > 4096) bx = 4096;
-  dim3 grid(static_cast<unsigned>(bx), c->cfg.n_kv_heads, c->cfg.n_layers);
+  const int64_t npages = (n + kPageTokens - 1) / kPageTokens;
+  dim3 grid(static_cast<unsigned>(npages), c->cfg.n_kv_heads, c->cfg.n_layers);
   scatter_kernel<T, D, NT><<<grid, NT, 0, c->stream>>>(
       static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(c->d.kpool),
       static_cast<T*>(c->d.vpool), c->d.ptab, seq, c->cfg.n_kv_heads, n, c->P, c->maxpages);
@@ -701,8 +925,7 @@ template <typename T, int D>
 static hipError_t group_copy_impl(kvev_ctx* c, int g, void* k, void* v, int64_t n, int64_t ld,
                                   int dir) {
   constexpr int NT = 256;
-  constexpr int RPB = NT / (D / Vec16<T>::N);
-  int64_t bx = (n + RPB - 1) / RPB;
+  int64_t bx = (n * D + NT - 1) / NT;
   if (bx < 1) return hipSuccess;
   if (bx > 4096) bx = 4096;
   dim3 grid(static_cast<unsigned>(bx), c->cfg.n_layers);

@@ -54,7 +54,7 @@ typedef enum { KVEV_F32 = 0, KVEV_BF16 = 1 } kvev_dtype;
 typedef enum { KVEV_EMA = 0, KVEV_CUMULATIVE = 1 } kvev_policy;
 
 typedef struct {
-  int32_t n_layers;         /* L */
+  int32_t n_layers;         /* L, 1..64 */
   int32_t n_q_heads;        /* Hq (multiple of n_kv_heads) */
   int32_t n_kv_heads;       /* Hkv */
   int32_t head_dim;         /* d: 64 or 128 */
