@@ -43,7 +43,29 @@ def algorithmic_bytes(w, n_tokens):
     return kv, kv + q + out + app + state + move
 
 
-def cpu_baseline(w, steps=3):
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_kernel_traffic_llama8b_32k.md")
+ATTN_SOURCES = [os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc", f) for f in ("attn.hip", "common.h")]
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed counter profile,
+    or None when the kernel source changed after the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(line.split(": ", 1) for line in text.splitlines()
+                if line.startswith(("traffic_bytes_per_launch: ", "kernel_source_sha256: ")))
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        h.update(open(f, "rb").read())
+    if vals.get("kernel_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(w, steps=300):
     """Time the CPU oracle on a bounded sample: steady steps of ONE (sequence,
     KV head) group at the workload's real shape (32 layers, budget+1 tokens,
     4 query heads, d=128), scaled to the whole step (8 groups)."""
@@ -167,7 +189,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "kernel": "attn_mfma_kernel",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
