@@ -22,6 +22,12 @@ GQA attention, 8k-131k contexts, 5-25% budgets):
   the other 64 channels (cosine 0.6 with u).  Epoch e of a multi-epoch run
   uses its own u_e; all epochs' heavy keys are planted at prefill.
 * New keys / values appended at decode steps have no heavy rows.
+* Block-granular workloads: the heavy positions of an epoch are shared by
+  every layer and KV head of a sequence (``heavy_shared``), so they mark
+  whole blocks; region labels are contiguous spans in the order system,
+  plan, user, tool, scratch with the configured fractions (cut points
+  floor(cumulative fraction * L0)); the block budget is the configured
+  fraction of the prefill's blocks, rounded half up.
 """
 from __future__ import annotations
 
@@ -124,6 +130,9 @@ class Workload:
     window_tokens: int = 32
     fp_windows: int = 0
     int2_windows: int = 0
+    heavy_shared: bool = False      # heavy positions per (sequence, epoch) only
+    budget_frac: float = 0.0        # block budget as a fraction of prefill blocks
+    decode_region: int = 4
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -173,11 +182,58 @@ class Workload:
         lo = 4
         if L0 - lo < self.n_heavy:
             return np.zeros(0, np.int64)
-        key = stream_key(self.seed, _META_HEAVY, layer, seq, kvh, epoch)
-        # distinct positions: sort hashed candidate ids and take the first n
-        cand = np.arange(lo, L0, dtype=np.int64)
-        h = _mix32_np(_mix32_np(cand) ^ key)
-        return np.sort(cand[np.lexsort((cand, h))[: self.n_heavy]])
+        if self.heavy_shared:
+            ck = (seq, epoch)
+        else:
+            ck = (layer, seq, kvh, epoch)
+        cache = self.extra.setdefault("_heavy", {})
+        if ck not in cache:
+            key = stream_key(self.seed, _META_HEAVY, *ck)
+            # distinct positions: sort hashed candidate ids and take the first n
+            cand = np.arange(lo, L0, dtype=np.int64)
+            h = _mix32_np(_mix32_np(cand) ^ key)
+            cache[ck] = np.sort(cand[np.lexsort((cand, h))[: self.n_heavy]])
+        return cache[ck]
+
+    def _heavy_rows(self, layer, seq, kvh):
+        """(positions, rows [n, d]) of every epoch's heavy keys for one
+        (layer, sequence, KV head); a position heavy in several epochs takes
+        the latest epoch's row."""
+        nc = self._norm_c()
+        owner = {}
+        for e in range(self.n_epochs):
+            for p in self.heavy_positions(layer, seq, kvh, e).tolist():
+                owner[p] = e
+        if not owner:
+            return np.zeros(0, np.int64), np.zeros((0, self.head_dim), np.float32)
+        pos = np.array(sorted(owner), dtype=np.int64)
+        rows = {}
+        for e in sorted(set(owner.values())):
+            u, w = self._directions(layer, seq, kvh, e)
+            rows[e] = (np.float32(nc * 0.6) * u + np.float32(nc * 0.8) * w).astype(np.float32)
+        return pos, np.stack([rows[owner[p]] for p in pos.tolist()])
+
+    def region_labels(self, seq):
+        """uint8 region id of every prefill position (contiguous spans)."""
+        L0 = self.prefill_lens[seq]
+        from fractions import Fraction
+        lab = np.zeros(L0, np.uint8)
+        cum = Fraction(0)
+        for r, f in enumerate(self.region_fracs):
+            lo = math.floor(cum * L0)
+            cum += Fraction(str(f))
+            hi = L0 if r == len(self.region_fracs) - 1 else math.floor(cum * L0)
+            lab[lo:hi] = r
+        return lab
+
+    def block_budget(self, seq):
+        nb = -(-self.prefill_lens[seq] // self.page_tokens)
+        return max(1, int(math.floor(self.budget_frac * nb + 0.5)))
+
+    def heavy_blocks(self, seq, epoch):
+        """Blocks holding epoch ``epoch``'s heavy keys (shared positions)."""
+        pos = self.heavy_positions(0, seq, 0, epoch)
+        return sorted(set((pos // self.page_tokens).tolist()))
 
     def epoch_of(self, t):
         if self.epoch_steps <= 0:
@@ -204,14 +260,40 @@ class Workload:
                 if self.structured:
                     ck, _ = self._structure(l, seq, h)
                     k = k * torch.from_numpy(ck).to(device)
-                    nc = self._norm_c()
-                    for e in range(self.n_epochs):
-                        pos = self.heavy_positions(l, seq, h, e)
-                        if len(pos) == 0:
-                            continue
-                        u, w = self._directions(l, seq, h, e)
-                        row = (np.float32(nc * 0.6) * u + np.float32(nc * 0.8) * w).astype(np.float32)
-                        k[torch.from_numpy(pos).to(device)] = torch.from_numpy(row).to(device)
+                    pos, rows = self._heavy_rows(l, seq, h)
+                    if len(pos):
+                        k[torch.from_numpy(pos).to(device)] = torch.from_numpy(rows).to(device)
+                kh.append(self._round(k))
+                vh.append(self._round(v))
+            Ks.append(torch.stack(kh))
+            Vs.append(torch.stack(vh))
+        return torch.stack(Ks), torch.stack(Vs)
+
+    def prefill_rows(self, seq, positions, device="cpu"):
+        """(K, V) of chosen prefill positions: [L, Hkv, len(positions), d],
+        bit-identical to the same rows of ``prefill_kv``."""
+        import torch
+        pos = np.asarray(positions, dtype=np.int64)
+        d = self.head_dim
+        idx = torch.from_numpy(pos[:, None] * d + np.arange(d)[None, :]).to(device)
+        table = _normal_table(device)
+        Ks, Vs = [], []
+        for l in range(self.n_layers):
+            kh, vh = [], []
+            for h in range(self.n_kv_heads):
+                hk = _mix32_t(_mix32_t(idx) ^ stream_key(self.seed, _K, l, seq, h))
+                hv = _mix32_t(_mix32_t(idx) ^ stream_key(self.seed, _V, l, seq, h))
+                k = table[hk >> 16]
+                v = table[hv >> 16]
+                if self.structured:
+                    ck, _ = self._structure(l, seq, h)
+                    k = k * torch.from_numpy(ck).to(device)
+                    hp, rows = self._heavy_rows(l, seq, h)
+                    where = np.searchsorted(hp, pos)
+                    hit = np.flatnonzero((where < len(hp)) & (hp[np.minimum(where, len(hp) - 1)] == pos)) \
+                        if len(hp) else np.zeros(0, np.int64)
+                    if len(hit):
+                        k[torch.from_numpy(hit).to(device)] = torch.from_numpy(rows[where[hit]]).to(device)
                 kh.append(self._round(k))
                 vh.append(self._round(v))
             Ks.append(torch.stack(kh))
@@ -290,6 +372,7 @@ def workload(name: str) -> Workload:
         return Workload("lrfu_64seq_4k16k_blocks20pct", 32, 32, 8, 128, "bf16",
                         _lengths(1004, 64, 4096, 16384), 1024, seed=1004, alpha_new=0.05,
                         policy="lrfu_block", beta=0.001, n_epochs=32, epoch_steps=32,
+                        n_heavy=16, heavy_shared=True, budget_frac=0.2,
                         region_fracs=(0.1, 0.1, 0.2, 0.4, 0.2),
                         region_half_lives=(170.0, 100.0, 60.0, 30.0, 15.0), pinned_regions=(0,))
     if name == "qevict131k":

@@ -37,7 +37,8 @@ __all__ = [
     "lrfu_priority", "layer_fold", "layer_fold_weights", "decode_attention",
     "group_mass", "select_keep", "hole_fill_moves", "apply_moves",
     "tier_capacities", "route_tiers", "int2_quantize", "int2_dequantize",
-    "TokenModeOracle", "region_decay_rates",
+    "TokenModeOracle", "region_decay_rates", "block_survival", "block_priority",
+    "select_blocks", "BlockLRFUOracle",
 ]
 
 
@@ -488,3 +489,256 @@ class TokenModeOracle:
     def positions(self, seq, h):
         g = self.groups[(seq, h)]
         return g.pos[:g.n].copy()
+
+
+# ---------------------------------------------------------------------------
+# Block-granular LRFU eviction with region decay and re-admission
+# ---------------------------------------------------------------------------
+
+def block_survival(labels, idle, beta, rates):
+    """Mean idle-time survival of a block's tokens.
+
+    ``(1/|b|) sum_i exp(-(beta + lambda_{r(i)}) * idle)``: the recency factor
+    ``exp(-beta*idle)`` of [LRFU-fig] times the region decay
+    ``exp(-lambda_r*idle)`` of [MemDecay] §III-C Eq.4, averaged over the
+    block's tokens as [MemDecay] §III-D Eq.5 averages a page's scores.
+    ``labels``: region id of each token of the block; ``rates``: lambda per
+    region.  With every lambda at 0 this is ``exp(-beta*idle)``.
+    """
+    lam = np.asarray(rates, dtype=np.float64)[np.asarray(labels, dtype=np.int64)]
+    return float(np.mean(np.exp(-(beta + lam) * float(idle))))
+
+
+def block_priority(score, labels, idle, beta, rates):
+    """Eviction priority ``(1 - score) * (1 - survival)`` of one block.
+
+    [LRFU-fig] priority ``(1 - score)(1 - exp(-beta*idle))``, with the
+    survival term extended by the block's region decay (reading: the decay
+    of [MemDecay] multiplies the recency term; with no region decay this is
+    exactly the figure's formula).  The HIGHER priority is evicted.
+    """
+    return (1.0 - float(score)) * (1.0 - block_survival(labels, idle, beta, rates))
+
+
+def select_blocks(ids, prio, pinned, budget):
+    """Blocks kept: the pinned ones plus the lowest-priority rest.
+
+    [MemDecay] §III-A Eq.1 with the pinned set forced, §III-D: non-pinned
+    pages go in ascending score order; here the score to keep is low
+    priority.  Reading: equal priorities keep the higher block id (the more
+    recent block).  Returns the sorted list of kept ids.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    prio = np.asarray(prio, dtype=np.float64)
+    pinned = np.asarray(pinned, dtype=bool)
+    if len(ids) <= budget:
+        return sorted(ids.tolist())
+    room = budget - int(pinned.sum())
+    if room < 0:
+        raise ValueError("pinned blocks exceed the budget")
+    cand = np.flatnonzero(~pinned)
+    # kept first: ascending priority, then descending id
+    order = cand[np.lexsort((-ids[cand], prio[cand]))]
+    kept = ids[pinned].tolist() + ids[order[:room]].tolist()
+    return sorted(kept)
+
+
+@dataclass
+class _BlockSeq:
+    """One sequence of the block-granular mode, indexed by position."""
+    K: np.ndarray            # [L, Hkv, cap, d] float32 (exact copies of inputs)
+    V: np.ndarray
+    labels: list             # region id of every position so far
+    npos: int                # positions 0 .. npos-1 exist
+    budget: int              # blocks
+    score: dict = field(default_factory=dict)   # block id -> fp64 score
+    tref: dict = field(default_factory=dict)    # block id -> last access step
+    resident: set = field(default_factory=set)  # block ids in the cache
+    last_mass: dict = field(default_factory=dict)
+    last_nres: int = 0       # resident tokens during the last step
+
+
+@dataclass
+class BlockLRFUOracle:
+    """Per-(sequence, block) LRFU state, region decay, pinning, re-admission.
+
+    Follows [LRFU-fig] (block unit of 16 tokens over every head and layer;
+    EMA score; priority; an evicted block's score persists and is restored
+    on re-admission) and [MemDecay] §III (region labels, pinned system
+    region, the decay clock of Eq.3 with a threshold scaled to the uniform
+    level, per-page eviction until the budget holds).
+
+    Readings:
+
+    * Block mass at step t: the attention probability landing on the
+      block's tokens, summed over every layer and query head and divided by
+      ``Hq * L`` (so masses over resident blocks sum to 1).
+    * Score: 0 when the block enters (prefill or its first decode token);
+      ``score <- ema(score, mass)`` for resident blocks every step; frozen
+      while evicted; unchanged by re-admission.
+    * Clock: ``tref`` is the insertion step (0 for prefill blocks, t for a
+      block opened by step t's token), set to t when the block's mean mass
+      per token is at least ``tau_mult / |K_t|`` (|K_t| the resident token
+      count, [MemDecay] §IV-A uses tau = 2/|K_t|), and to the current step
+      count on re-admission.  ``idle = t - tref``.
+    * Pinned: every block holding a token of a pinned region ([MemDecay]
+      §IV-A: pinning protects whole pages) and the block holding the newest
+      token (it is still being filled).
+    * Decode tokens take ``decode_region`` (the scratch region).
+    * Eviction happens once per step after the update whenever more than
+      ``budget`` blocks are resident.
+    """
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    alpha_new: float
+    beta: float
+    half_lives: tuple
+    pinned_regions: tuple = (0,)
+    decode_region: int = 4
+    tau_mult: float = 2.0
+    page: int = 16
+    capacity: int = 0
+    seqs: dict = field(default_factory=dict)
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def rates(self):
+        return region_decay_rates(self.half_lives)
+
+    def prefill(self, seq, K, V, labels, budget):
+        """Store a sequence's prefill K/V ([L, Hkv, n, d]) and region labels."""
+        K = np.asarray(K, dtype=np.float32)
+        V = np.asarray(V, dtype=np.float32)
+        L, H, n, d = K.shape
+        cap = max(self.capacity, n + 1)
+        s = _BlockSeq(K=np.zeros((L, H, cap, d), np.float32), V=np.zeros((L, H, cap, d), np.float32),
+                      labels=[int(x) for x in labels], npos=n, budget=int(budget))
+        if len(s.labels) != n:
+            raise ValueError("one region label per prefill token")
+        s.K[:, :, :n] = K
+        s.V[:, :, :n] = V
+        for j in range((n + self.page - 1) // self.page):
+            s.score[j] = 0.0
+            s.tref[j] = 0
+            s.resident.add(j)
+        self.seqs[seq] = s
+
+    # -- block views ------------------------------------------------------
+    def block_positions(self, seq, j):
+        s = self.seqs[seq]
+        return list(range(j * self.page, min((j + 1) * self.page, s.npos)))
+
+    def tail_block(self, seq):
+        return (self.seqs[seq].npos - 1) // self.page
+
+    def is_pinned(self, seq, j):
+        s = self.seqs[seq]
+        if j == self.tail_block(seq):
+            return True
+        return any(s.labels[i] in self.pinned_regions for i in self.block_positions(seq, j))
+
+    def priority(self, seq, j, t):
+        s = self.seqs[seq]
+        labels = [s.labels[i] for i in self.block_positions(seq, j)]
+        return block_priority(s.score[j], labels, t - s.tref[j], self.beta, self.rates)
+
+    def resident_positions(self, seq):
+        s = self.seqs[seq]
+        pos = []
+        for j in sorted(s.resident):
+            pos.extend(self.block_positions(seq, j))
+        return np.asarray(pos, dtype=np.int64)
+
+    # -- the step -----------------------------------------------------------
+    def _grow(self, s):
+        if s.npos < s.K.shape[2]:
+            return
+        extra = max(64, s.K.shape[2] // 4)
+        pad = lambda a: np.concatenate(
+            [a, np.zeros(a.shape[:2] + (extra,) + a.shape[3:], a.dtype)], axis=2)
+        s.K, s.V = pad(s.K), pad(s.V)
+
+    def decode_step(self, t, q, k_new, v_new, seqs):
+        """Append, attend over the resident blocks, update score and clock.
+
+        ``q``: [L, len(seqs), Hq, d]; ``k_new``, ``v_new``: [L, len(seqs),
+        Hkv, d].  Returns ``out`` [L, len(seqs), Hq, d] (fp64).
+        """
+        q = np.asarray(q, dtype=np.float32)
+        k_new = np.asarray(k_new, dtype=np.float32)
+        v_new = np.asarray(v_new, dtype=np.float32)
+        L, Hq, Hg, pg = self.n_layers, self.n_q_heads, self.group_size, self.page
+        out = np.zeros((L, len(seqs), Hq, self.head_dim))
+        for bi, seq in enumerate(seqs):
+            s = self.seqs[seq]
+            self._grow(s)
+            p_new = s.npos
+            s.K[:, :, p_new] = k_new[:, bi]
+            s.V[:, :, p_new] = v_new[:, bi]
+            s.labels.append(self.decode_region)
+            s.npos += 1
+            if p_new % pg == 0:                      # the token opens a block
+                j = p_new // pg
+                s.score[j] = 0.0
+                s.tref[j] = t
+                s.resident.add(j)
+            pos = self.resident_positions(seq)
+            tok_mass = np.zeros(len(pos))
+            for l in range(L):
+                for h in range(self.n_kv_heads):
+                    o, p, _ = decode_attention(q[l, bi, h * Hg:(h + 1) * Hg],
+                                               s.K[l, h, pos], s.V[l, h, pos])
+                    out[l, bi, h * Hg:(h + 1) * Hg] = o
+                    tok_mass += p.sum(axis=0)
+            tok_mass /= Hq * L
+            n_res = len(pos)
+            s.last_nres = n_res
+            s.last_mass = {}
+            at = 0
+            for j in sorted(s.resident):
+                nb = len(self.block_positions(seq, j))
+                mass = float(tok_mass[at:at + nb].sum())
+                at += nb
+                s.last_mass[j] = mass
+                s.score[j] = ema_update(s.score[j], mass, self.alpha_new)
+                if mass / nb >= self.tau_mult / n_res:
+                    s.tref[j] = t
+        return out
+
+    def evict(self, t, seqs=None):
+        """Evict down to each sequence's block budget at clock ``t``."""
+        for seq in (self.seqs if seqs is None else seqs):
+            s = self.seqs[seq]
+            if len(s.resident) <= s.budget:
+                continue
+            ids = sorted(s.resident)
+            prio = [self.priority(seq, j, t) for j in ids]
+            pinned = [self.is_pinned(seq, j) for j in ids]
+            s.resident = set(select_blocks(ids, prio, pinned, s.budget))
+
+    def readmit(self, seq, j, t):
+        """Bring evicted block ``j`` back: score restored, clock set to t.
+
+        [LRFU-fig]: an evicted block's key and score persist and are
+        restored on re-admission rather than reset.
+        """
+        s = self.seqs[seq]
+        if j in s.resident or j not in s.score:
+            raise ValueError("block is resident or was never cached")
+        s.resident.add(j)
+        s.tref[j] = t
+
+    # -- views used by tests ------------------------------------------------
+    def block_state(self, seq):
+        """(ids, score, tref, resident) over every block seen so far."""
+        s = self.seqs[seq]
+        ids = np.arange((s.npos + self.page - 1) // self.page)
+        score = np.array([s.score[j] for j in ids], dtype=np.float64)
+        tref = np.array([s.tref[j] for j in ids], dtype=np.int64)
+        res = np.array([j in s.resident for j in ids], dtype=bool)
+        return ids, score, tref, res
