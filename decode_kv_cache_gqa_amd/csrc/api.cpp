@@ -97,7 +97,9 @@ void free_all(kvev_ctx* c) {
   auto& d = c->d;
   void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
-                  d.grpctr, d.blk_key, d.blk_slot, d.blk_page, d.blk_sum};
+                  d.grpctr, d.blk_key, d.blk_slot, d.blk_page, d.blk_sum, d.btab, d.nres,
+                  d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
+                  d.rd_ids};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -146,6 +148,9 @@ void kvev_config_init(kvev_config* cfg) {
   cfg->alpha_new = 0.05f;
   cfg->refresh_interval = 1;
   cfg->dtype = KVEV_BF16;
+  cfg->beta = 0.001f;
+  cfg->decode_region = 4;
+  cfg->access_tau_mult = 2.0f;
 }
 
 kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out) {
@@ -166,12 +171,30 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
   if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
-  if (f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE) return bad("unsupported policy");
-  if (f.policy == KVEV_EMA && !(f.alpha_new > 0.f && f.alpha_new <= 1.f))
+  if (f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE && f.policy != KVEV_LRFU_BLOCK)
+    return bad("unsupported policy");
+  if ((f.policy == KVEV_EMA || f.policy == KVEV_LRFU_BLOCK) && !(f.alpha_new > 0.f && f.alpha_new <= 1.f))
     return bad("alpha_new must be in (0, 1]");
+  const bool block = f.policy == KVEV_LRFU_BLOCK;
+  if (block) {
+    if (f.max_tokens > static_cast<int64_t>(kMaxBlockEntries) * kPageTokens)
+      return bad("block mode: max_tokens must be <= 65536");
+    if (f.n_sink != 0 || f.n_recent != 0) return bad("block mode: n_sink and n_recent must be 0");
+    if (f.refresh_interval != 1 || f.score_free != 0)
+      return bad("block mode: refresh_interval must be 1 and score_free 0");
+    if (!(f.beta >= 0.f) || !std::isfinite(f.beta)) return bad("block mode: beta must be finite and >= 0");
+    if (f.decode_region < 0 || f.decode_region >= kRegions) return bad("block mode: decode_region out of range");
+    if ((f.pinned_region_mask >> f.decode_region) & 1u) return bad("block mode: decode_region is pinned");
+    if (f.pinned_region_mask >> kRegions) return bad("block mode: pinned_region_mask has bits above 7");
+    if (!(f.access_tau_mult > 0.f) || !std::isfinite(f.access_tau_mult))
+      return bad("block mode: access_tau_mult must be > 0");
+    if (f.n_kv_heads > 64 || f.n_layers * f.n_kv_heads > 1024)
+      return bad("block mode: at most 64 KV heads and 1024 (layer, KV head) pairs");
+  }
   if (f.refresh_interval < 1) return bad("refresh_interval must be >= 1");
   if (f.n_sink < 0 || f.n_recent < 0) return bad("n_sink and n_recent must be >= 0");
   if (f.budget < 1) return bad("budget must be >= 1");
+  if (block && f.budget > kMaxBlockEntries) return bad("block mode: budget must be <= 4096 blocks");
   if (f.n_sink + f.n_recent > f.budget) return bad("n_sink + n_recent exceeds the budget");
   if (f.max_tokens < 2 || f.max_tokens > (1ll << 30)) return bad("max_tokens out of range");
   if (f.n_layers > 64) return bad("n_layers must be <= 64");
@@ -191,6 +214,18 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
   c->count.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
+  c->block_mode = block;
+  if (block) {
+    c->maxblk = c->maxpages;
+    for (int r = 0; r < kRegions; ++r) {
+      const double hl = f.region_half_life[r];
+      c->lam[r] = (hl > 0.0 && std::isfinite(hl)) ? static_cast<float>(std::log(2.0) / hl) : 0.f;
+    }
+    c->nres.assign(f.batch, 0);
+    c->npos.assign(f.batch, 0);
+    c->bbudget.assign(f.batch, static_cast<int>(f.budget));
+    c->npinned.assign(f.batch, 0);
+  }
   c->pages.assign(c->G, {});
   c->free_pages.resize(c->P);  // popped from the back: lowest page first
   for (int64_t i = 0; i < c->P; ++i) c->free_pages[i] = static_cast<int>(c->P - 1 - i);
@@ -222,6 +257,20 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.blk_slot, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_page, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_sum, static_cast<size_t>(G) * c->max_post_blocks));
+  if (block) {
+    const size_t Bs = f.batch;
+    A(dalloc(&d.btab, Bs * c->maxpages));
+    A(dalloc(&d.nres, Bs));
+    A(dalloc(&d.bscore, Bs * c->maxblk));
+    A(dalloc(&d.btref, Bs * c->maxblk));
+    A(dalloc(&d.bres, Bs * c->maxblk));
+    A(dalloc(&d.bcnt, Bs * c->maxblk * kRegions));
+    A(dalloc(&d.fstack, static_cast<size_t>(G) * c->maxpages));
+    A(dalloc(&d.ftop, G));
+    A(dalloc(&d.bmass, Bs * c->maxpages));
+    A(dalloc(&d.bbudget, Bs));
+    A(dalloc(&d.rd_ids, c->maxpages));
+  }
   if (e != hipSuccess) {
     g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
     free_all(c);
@@ -241,6 +290,26 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(hipMemsetAsync(d.grpctr, 0, sizeof(unsigned) * G, c->stream));
   A(hipMemsetAsync(d.mv_src, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.mv_dst, 0, sizeof(int) * G * c->cap, c->stream));
+  if (block) {
+    const size_t Bs = f.batch;
+    A(hipMemsetAsync(d.btab, 0, sizeof(int) * Bs * c->maxpages, c->stream));
+    A(hipMemsetAsync(d.nres, 0, sizeof(int) * Bs, c->stream));
+    A(hipMemsetAsync(d.bscore, 0, sizeof(float) * Bs * c->maxblk, c->stream));
+    A(hipMemsetAsync(d.btref, 0, sizeof(int) * Bs * c->maxblk, c->stream));
+    A(hipMemsetAsync(d.bres, 0, sizeof(int) * Bs * c->maxblk, c->stream));
+    A(hipMemsetAsync(d.bcnt, 0, Bs * c->maxblk * kRegions, c->stream));
+    A(hipMemsetAsync(d.bmass, 0, sizeof(float) * Bs * c->maxpages, c->stream));
+    A(hipMemsetAsync(d.rd_ids, 0, sizeof(int) * c->maxpages, c->stream));
+    std::vector<int> stack(static_cast<size_t>(G) * c->maxpages), top(G, c->maxpages);
+    for (int64_t g = 0; g < G; ++g)
+      for (int i = 0; i < c->maxpages; ++i)  // popped from the top: lowest page first
+        stack[g * c->maxpages + i] = static_cast<int>(g * c->maxpages + (c->maxpages - 1 - i));
+    std::vector<int> bud(Bs, static_cast<int>(f.budget));
+    A(hipMemcpyAsync(d.fstack, stack.data(), sizeof(int) * stack.size(), hipMemcpyHostToDevice, c->stream));
+    A(hipMemcpyAsync(d.ftop, top.data(), sizeof(int) * G, hipMemcpyHostToDevice, c->stream));
+    A(hipMemcpyAsync(d.bbudget, bud.data(), sizeof(int) * Bs, hipMemcpyHostToDevice, c->stream));
+    A(hipStreamSynchronize(c->stream));  // host vectors above are local
+  }
   A(hipStreamSynchronize(c->stream));
   if (e != hipSuccess) {
     g_create_error = std::string("device initialisation failed: ") + hipGetErrorString(e);
@@ -260,12 +329,101 @@ kvev_status kvev_destroy(kvev_ctx* c) {
   return KVEV_OK;
 }
 
-kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v, int64_t n) {
+// Block mode: install a sequence's block table, page tables, free-page
+// stacks and block state for blocks 0..nb-1 of which `resident` are cached
+// (ascending ids, the last one the block holding the newest token), then
+// scatter the resident tokens' K/V.  Shared by prefill and import.
+static kvev_status block_install(kvev_ctx* c, int seq, int64_t npos, const std::vector<int>& resident,
+                                 const float* score, const int32_t* tref, const void* k,
+                                 const void* v) {
+  const int Hkv = c->cfg.n_kv_heads;
+  const int nb = static_cast<int>((npos + c->PT - 1) / c->PT);
+  const int nr = static_cast<int>(resident.size());
+  const int fill = static_cast<int>(npos - static_cast<int64_t>(c->PT) * (nb - 1));
+  const int64_t cnt = static_cast<int64_t>(c->PT) * (nr - 1) + fill;
+  std::vector<int> btab(resident), top(Hkv, c->maxpages - nr);
+  std::vector<int> ptab(static_cast<size_t>(Hkv) * c->maxpages), stack(ptab.size());
+  for (int h = 0; h < Hkv; ++h) {
+    const int g = seq * Hkv + h;
+    for (int i = 0; i < c->maxpages; ++i) {
+      const int page = g * c->maxpages + i;
+      if (i < nr) ptab[static_cast<size_t>(h) * c->maxpages + i] = page;
+      else stack[static_cast<size_t>(h) * c->maxpages + (c->maxpages - 1 - i)] = page;
+    }
+  }
+  std::vector<float> bscore(c->maxblk, 0.f);
+  std::vector<int> btref(c->maxblk, 0), bres(c->maxblk, 0), posv(cnt);
+  for (int j = 0; j < nb; ++j) {
+    bscore[j] = score ? score[j] : 0.f;
+    btref[j] = tref ? tref[j] : 0;
+  }
+  for (int i = 0; i < nr; ++i) {
+    bres[resident[i]] = 1;
+    const int len = i == nr - 1 ? fill : c->PT;
+    for (int r = 0; r < len; ++r) posv[static_cast<size_t>(i) * c->PT + r] = resident[i] * c->PT + r;
+  }
+  const int64_t brow = static_cast<int64_t>(seq) * c->maxpages, bblk = static_cast<int64_t>(seq) * c->maxblk;
+  const int nr32 = nr, cnt32 = static_cast<int>(cnt), np32 = static_cast<int>(npos);
+  auto H2D = [&](void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, c->stream);
+  };
+  KVEV_HIP(c, H2D(c->d.btab + brow, btab.data(), sizeof(int) * nr));
+  KVEV_HIP(c, H2D(c->d.nres + seq, &nr32, sizeof(int)));
+  KVEV_HIP(c, H2D(c->d.bscore + bblk, bscore.data(), sizeof(float) * c->maxblk));
+  KVEV_HIP(c, H2D(c->d.btref + bblk, btref.data(), sizeof(int) * c->maxblk));
+  KVEV_HIP(c, H2D(c->d.bres + bblk, bres.data(), sizeof(int) * c->maxblk));
+  for (int h = 0; h < Hkv; ++h) {
+    const int g = seq * Hkv + h;
+    KVEV_HIP(c, H2D(c->d.ptab + static_cast<int64_t>(g) * c->maxpages,
+                    ptab.data() + static_cast<size_t>(h) * c->maxpages, sizeof(int) * c->maxpages));
+    KVEV_HIP(c, H2D(c->d.fstack + static_cast<int64_t>(g) * c->maxpages,
+                    stack.data() + static_cast<size_t>(h) * c->maxpages, sizeof(int) * c->maxpages));
+    KVEV_HIP(c, H2D(c->d.ftop + g, &top[h], sizeof(int)));
+    KVEV_HIP(c, H2D(c->d.pos + static_cast<int64_t>(g) * c->cap, posv.data(), sizeof(int) * cnt));
+    KVEV_HIP(c, H2D(c->d.count + g, &cnt32, sizeof(int)));
+    KVEV_HIP(c, H2D(c->d.nextpos + g, &np32, sizeof(int)));
+  }
+  KVEV_HIP(c, launch_prefill_scatter(c, seq, k, v, cnt));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));  // host vectors above are local
+  for (int h = 0; h < Hkv; ++h) c->count[seq * Hkv + h] = cnt;
+  c->nres[seq] = nr;
+  c->npos[seq] = npos;
+  return KVEV_OK;
+}
+
+static kvev_status block_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n,
+                                 const uint8_t* labels) {
+  const int nb = static_cast<int>((n + c->PT - 1) / c->PT);
+  std::vector<uint8_t> cnt8(static_cast<size_t>(c->maxblk) * kRegions, 0);
+  int pinned = 0;
+  for (int j = 0; j < nb; ++j) {
+    bool pin = false;
+    for (int64_t i = static_cast<int64_t>(j) * c->PT; i < std::min<int64_t>(n, (j + 1) * c->PT); ++i) {
+      const int r = labels ? labels[i] : c->cfg.decode_region;
+      if (r < 0 || r >= kRegions) return fail(c, KVEV_EINVAL, "region label out of range");
+      cnt8[static_cast<size_t>(j) * kRegions + r] += 1;
+      if ((c->cfg.pinned_region_mask >> r) & 1u) pin = true;
+    }
+    pinned += pin;
+  }
+  KVEV_HIP(c, hipMemcpyAsync(c->d.bcnt + static_cast<int64_t>(seq) * c->maxblk * kRegions, cnt8.data(),
+                             cnt8.size(), hipMemcpyHostToDevice, c->stream));
+  std::vector<int> resident(nb);
+  for (int j = 0; j < nb; ++j) resident[j] = j;
+  if (kvev_status s = block_install(c, seq, n, resident, nullptr, nullptr, k, v)) return s;
+  c->npinned[seq] = pinned;
+  c->prefilled[seq] = 1;
+  return KVEV_OK;
+}
+
+kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v, int64_t n,
+                         const uint8_t* labels) {
   KVEV_LIVE(c);
   if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
   if (!k || !v) return fail(c, KVEV_EINVAL, "null k or v");
   if (c->t > 0) return fail(c, KVEV_ESTATE, "prefill after the first decode step");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
+  if (c->block_mode) return block_prefill(c, seq, k, v, n, labels);
   const int Hkv = c->cfg.n_kv_heads;
   std::vector<int> upd;
   for (int h = 0; h < Hkv; ++h) {
@@ -297,6 +455,95 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
     c->count[g] = n;
   }
   c->prefilled[seq] = 1;
+  return KVEV_OK;
+}
+
+// Block mode: the per-sequence budget a selection uses, checked against the
+// blocks it must keep (pinned by region labels, plus the block being filled).
+static kvev_status block_budget(kvev_ctx* c, int b, int64_t override_budget, int* B) {
+  const int64_t bb = override_budget > 0 ? override_budget : c->bbudget[b];
+  if (bb > kMaxBlockEntries) return fail(c, KVEV_EINVAL, "budget out of range");
+  if (bb < c->npinned[b] + 1) return fail(c, KVEV_EINVAL, "budget below the pinned blocks of a sequence");
+  *B = static_cast<int>(bb);
+  return KVEV_OK;
+}
+
+static int block_fill(const kvev_ctx* c, int64_t npos) {
+  return static_cast<int>(npos - static_cast<int64_t>(c->PT) * ((npos - 1) / c->PT));
+}
+
+// Block mode step: open (slot and block of the new token), attention,
+// split merge, block mass, policy (score and clock update; selection and
+// table compaction when do_select).
+static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                              float* out, bool do_select, int64_t override_budget) {
+  if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
+  const int Bsz = c->cfg.batch, Hkv = c->cfg.n_kv_heads;
+  std::vector<int> Bs(Bsz, 0);
+  int64_t n_max = 0;
+  for (int b = 0; b < Bsz; ++b) {
+    if (!c->prefilled[b]) return fail(c, KVEV_ESTATE, "a sequence has no prefill");
+    if (c->npos[b] + 1 > c->cap) return fail(c, KVEV_ESTATE, "position capacity exhausted");
+    if (do_select)
+      if (kvev_status s = block_budget(c, b, override_budget, &Bs[b])) return s;
+    const bool opens = c->npos[b] % c->PT == 0;
+    if (opens && c->nres[b] + 1 > c->maxpages) return fail(c, KVEV_ESTATE, "block table full");
+    n_max = std::max(n_max, c->count[b * Hkv] + 1);
+  }
+  const int64_t t = c->t + 1;
+  c->lstride = (n_max + 15) / 16 * 16;
+  const int nm = static_cast<int>(n_max);
+  {
+    ProfScope p(c, "open");
+    KVEV_HIP(c, launch_block_open(c, nm, static_cast<int>(t)));
+  }
+  {
+    ProfScope p(c, "attn");
+    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, nm, 1));
+  }
+  {
+    ProfScope p(c, "merge");
+    KVEV_HIP(c, launch_block_merge(c, out, nm));
+  }
+  {
+    ProfScope p(c, "mass");
+    KVEV_HIP(c, launch_block_mass(c, nm));
+  }
+  {
+    ProfScope p(c, "policy");
+    KVEV_HIP(c, launch_block_policy(c, static_cast<int>(t), 1, do_select ? 1 : 0, 1,
+                                    static_cast<int>(override_budget > 0 ? override_budget : 0)));
+  }
+  for (int b = 0; b < Bsz; ++b) {
+    if (c->npos[b] % c->PT == 0) c->nres[b] += 1;
+    c->npos[b] += 1;
+    if (do_select && c->nres[b] > Bs[b]) c->nres[b] = Bs[b];
+    const int64_t cnt = static_cast<int64_t>(c->PT) * (c->nres[b] - 1) + block_fill(c, c->npos[b]);
+    for (int h = 0; h < Hkv; ++h) c->count[b * Hkv + h] = cnt;
+  }
+  c->t = t;
+  return KVEV_OK;
+}
+
+static kvev_status block_evict(kvev_ctx* c, int64_t override_budget) {
+  const int Bsz = c->cfg.batch, Hkv = c->cfg.n_kv_heads;
+  std::vector<int> Bs(Bsz, 0);
+  bool any = false;
+  for (int b = 0; b < Bsz; ++b) {
+    if (kvev_status s = block_budget(c, b, override_budget, &Bs[b])) return s;
+    any = any || c->nres[b] > Bs[b];
+  }
+  if (!any) return KVEV_OK;
+  {
+    ProfScope p(c, "policy");
+    KVEV_HIP(c, launch_block_policy(c, static_cast<int>(c->t), 0, 1, 0,
+                                    static_cast<int>(override_budget > 0 ? override_budget : 0)));
+  }
+  for (int b = 0; b < Bsz; ++b) {
+    if (c->nres[b] > Bs[b]) c->nres[b] = Bs[b];
+    const int64_t cnt = static_cast<int64_t>(c->PT) * (c->nres[b] - 1) + block_fill(c, c->npos[b]);
+    for (int h = 0; h < Hkv; ++h) c->count[b * Hkv + h] = cnt;
+  }
   return KVEV_OK;
 }
 
@@ -355,12 +602,14 @@ static kvev_status check_budget(kvev_ctx* c, int64_t budget, int64_t* B) {
 kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                              float* out) {
   KVEV_LIVE(c);
+  if (c->block_mode) return block_step(c, q, k_new, v_new, out, false, 0);
   return run_step(c, q, k_new, v_new, out, false, c->cfg.budget);
 }
 
 kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out,
                       int64_t budget) {
   KVEV_LIVE(c);
+  if (c->block_mode) return block_step(c, q, k_new, v_new, out, true, budget);
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   return run_step(c, q, k_new, v_new, out, true, B);
@@ -368,6 +617,7 @@ kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void*
 
 kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   KVEV_LIVE(c);
+  if (c->block_mode) return block_evict(c, budget);
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   int64_t max_moves = 0;
@@ -401,11 +651,102 @@ static kvev_status group_index(kvev_ctx* c, int32_t seq, int32_t h, int* g) {
   return KVEV_OK;
 }
 
+kvev_status kvev_block_state(kvev_ctx* c, int32_t seq, float* score, int32_t* tref,
+                             uint8_t* resident, int64_t cap, int64_t* n_blocks) {
+  KVEV_LIVE(c);
+  if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_ERANGE, "sequence index out of range");
+  const int64_t nb = (c->npos[seq] + c->PT - 1) / c->PT;
+  if (n_blocks) *n_blocks = nb;
+  if (cap < nb) return fail(c, KVEV_ERANGE, "destination too small");
+  const int64_t bblk = static_cast<int64_t>(seq) * c->maxblk;
+  std::vector<int> res(nb);
+  if (score)
+    KVEV_HIP(c, hipMemcpyAsync(score, c->d.bscore + bblk, sizeof(float) * nb, hipMemcpyDeviceToHost, c->stream));
+  if (tref)
+    KVEV_HIP(c, hipMemcpyAsync(tref, c->d.btref + bblk, sizeof(int) * nb, hipMemcpyDeviceToHost, c->stream));
+  if (resident && nb)
+    KVEV_HIP(c, hipMemcpyAsync(res.data(), c->d.bres + bblk, sizeof(int) * nb, hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  if (resident)
+    for (int64_t j = 0; j < nb; ++j) resident[j] = res[j] ? 1 : 0;
+  return KVEV_OK;
+}
+
+kvev_status kvev_set_budget(kvev_ctx* c, int32_t seq, int64_t budget) {
+  KVEV_LIVE(c);
+  if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (budget < c->npinned[seq] + 1 || budget > kMaxBlockEntries)
+    return fail(c, KVEV_EINVAL, "budget below the pinned blocks or out of range");
+  const int b32 = static_cast<int>(budget);
+  KVEV_HIP(c, hipMemcpyAsync(c->d.bbudget + seq, &b32, sizeof(int), hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  c->bbudget[seq] = b32;
+  return KVEV_OK;
+}
+
+kvev_status kvev_readmit(kvev_ctx* c, int32_t seq, int64_t n, const int64_t* ids, const void* k,
+                         const void* v) {
+  KVEV_LIVE(c);
+  if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (!c->prefilled[seq]) return fail(c, KVEV_ESTATE, "sequence has no prefill");
+  if (n < 1 || !ids || !k || !v) return fail(c, KVEV_EINVAL, "null argument or n < 1");
+  if (c->nres[seq] + n > c->maxpages || c->count[seq * c->cfg.n_kv_heads] + c->PT * n + 1 > c->cap)
+    return fail(c, KVEV_ENOMEM, "block table full");
+  const int64_t tail = (c->npos[seq] - 1) / c->PT;
+  std::vector<int> res(tail + 1);
+  KVEV_HIP(c, hipMemcpyAsync(res.data(), c->d.bres + static_cast<int64_t>(seq) * c->maxblk,
+                             sizeof(int) * (tail + 1), hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  std::vector<int> id32(n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= tail) return fail(c, KVEV_EINVAL, "block id unknown or still being filled");
+    if (res[ids[i]]) return fail(c, KVEV_EINVAL, "block is resident (or listed twice)");
+    res[ids[i]] = 1;
+    id32[i] = static_cast<int>(ids[i]);
+  }
+  const int e0 = c->nres[seq] - 1;
+  KVEV_HIP(c, hipMemcpyAsync(c->d.rd_ids, id32.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+  {
+    ProfScope p(c, "readmit");
+    KVEV_HIP(c, launch_block_readmit(c, seq, static_cast<int>(n), c->d.rd_ids, static_cast<int>(c->t)));
+    KVEV_HIP(c, launch_scatter_at(c, seq, k, v, c->PT * n, e0));
+  }
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));  // id32 is local
+  c->nres[seq] += static_cast<int>(n);
+  for (int h = 0; h < c->cfg.n_kv_heads; ++h) c->count[seq * c->cfg.n_kv_heads + h] += c->PT * n;
+  return KVEV_OK;
+}
+
+kvev_status kvev_import_blocks(kvev_ctx* c, int32_t seq, int64_t n_blocks, const float* score,
+                               const int32_t* tref, const uint8_t* resident, int64_t n_tokens,
+                               const void* k, const void* v) {
+  KVEV_LIVE(c);
+  if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (!c->prefilled[seq]) return fail(c, KVEV_ESTATE, "sequence has no prefill");
+  if (!score || !tref || !resident || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
+  const int64_t nb = (c->npos[seq] + c->PT - 1) / c->PT;
+  if (n_blocks != nb) return fail(c, KVEV_EINVAL, "n_blocks must equal the blocks seen");
+  if (!resident[nb - 1]) return fail(c, KVEV_EINVAL, "the block being filled must be resident");
+  std::vector<int> ids;
+  for (int64_t j = 0; j < nb; ++j)
+    if (resident[j]) ids.push_back(static_cast<int>(j));
+  if (static_cast<int64_t>(ids.size()) > c->maxpages) return fail(c, KVEV_EINVAL, "too many resident blocks");
+  const int64_t want = static_cast<int64_t>(c->PT) * (static_cast<int64_t>(ids.size()) - 1) +
+                       block_fill(c, c->npos[seq]);
+  if (n_tokens != want) return fail(c, KVEV_EINVAL, "n_tokens does not match the resident blocks");
+  return block_install(c, seq, c->npos[seq], ids, score, tref, k, v);
+}
+
 kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t cap,
                         int64_t* n_written) {
   KVEV_LIVE(c);
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  if (c->block_mode) return kvev_block_state(c, seq, dst, nullptr, nullptr, cap, n_written);
   const int64_t n = c->count[g];
   if (n_written) *n_written = n;
   if (!dst || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
@@ -447,6 +788,7 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   KVEV_LIVE(c);
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  if (c->block_mode) return fail(c, KVEV_EINVAL, "block mode: use kvev_import_blocks");
   if (!positions || !scores || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_ERANGE, "n out of range");
   int maxp = 0;
@@ -478,6 +820,15 @@ kvev_status kvev_sync(kvev_ctx* c) {
     c->err = "device consistency check failed (flag " + std::to_string(flag) + ")";
     return KVEV_ESTATE;
   }
+  // the host's slot counts size every launch: they must match the device's
+  std::vector<int> dc(c->G);
+  KVEV_HIP(c, hipMemcpy(dc.data(), c->d.count, sizeof(int) * c->G, hipMemcpyDeviceToHost));
+  for (int g = 0; g < c->G; ++g)
+    if (dc[g] != c->count[g]) {
+      c->sticky = true;
+      c->err = "device slot count of group " + std::to_string(g) + " differs from the host's";
+      return KVEV_ESTATE;
+    }
   return KVEV_OK;
 }
 

@@ -1,0 +1,474 @@
+// Block-granular LRFU mode: eviction per (sequence, 16-token block) over every
+// layer and KV head.
+//
+// Sources: the "Attention-Aware Block Eviction" figure page (KV-cache docs,
+// chapter 7: block unit, EMA score, priority (1 - score)(1 - e^{-beta idle}),
+// score persistence across eviction and re-admission) and "MemDecay"
+// section III (region labels, pinned system region, decay clock of Eq.3 with
+// the threshold scaled to the uniform level, per-page eviction, Eq.7 rates).
+//
+// Layout.  Every KV head of a sequence shares one block table: entry e of
+// sequence b holds logical block btab[b][e] (block id = position / 16), and
+// group g = b*Hkv + h stores that block's tokens in physical page
+// ptab[g][e].  Entries are kept in table order across evictions (stable
+// compaction) and the block holding the newest token is always the last
+// entry, so slot s of a group is token 16*btab[s/16] + s%16 and the groups'
+// slot counts stay 16*(entries-1) + tail fill.  Each group owns the pages
+// [g*maxpages, (g+1)*maxpages) and keeps the unused ones on a device-side
+// stack, so eviction and block opening never wait for the host.
+#include "kvev_internal.h"
+
+namespace kvev {
+
+struct BlockArgs {
+  int* count;
+  int* pos;
+  int* nextpos;
+  int* ptab;
+  int* btab;
+  int* nres;
+  float* bscore;
+  int* btref;
+  int* bres;
+  uint8_t* bcnt;
+  int* fstack;
+  int* ftop;
+  float* bmass;
+  const int* bbudget;
+  int* errflag;
+  const float* logits;
+  float* ml;
+  const float* part_ml;
+  const float* part_o;
+  float* out;
+  int L, G, Hkv, Hq, HG, D, maxpages, maxblk, S, batch;
+  int64_t cap, lstride;
+  float alpha, beta, tau;
+  float lam[kRegions];
+  unsigned pinned_mask;
+  int decode_region;
+  int t;
+};
+
+// ---------------------------------------------------------------------------
+// Open: before attention, give the new token its slot.  When the token's
+// position starts a block, pop one page per KV head, append the block as the
+// new last table entry with score 0 and clock t, and count the token in its
+// block's region composition.  One block of threads per sequence.
+// ---------------------------------------------------------------------------
+__global__ void blk_open_kernel(BlockArgs A, int n_max) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int g0 = b * A.Hkv;
+  const int newest = A.nextpos[g0];
+  const int cnt = A.count[g0];
+  if (cnt + 1 > n_max || newest / kPageTokens >= A.maxblk) {
+    // the host's launch shape does not cover this sequence: refuse to let
+    // the attention run past it (the context fails at the next sync)
+    if (tid < A.Hkv) A.count[g0 + tid] = n_max - 1;
+    if (tid == 0) atomicOr(A.errflag, 16);
+    return;
+  }
+  const bool opens = newest % kPageTokens == 0;
+  const int e = A.nres[b];
+  const int j = newest / kPageTokens;
+  if (opens && e >= A.maxpages) {
+    if (tid == 0) atomicOr(A.errflag, 8);
+    return;
+  }
+  if (tid < A.Hkv) {
+    const int g = g0 + tid;
+    if (opens) {
+      const int top = A.ftop[g];
+      if (top <= 0) {
+        atomicOr(A.errflag, 8);
+      } else {
+        A.ptab[static_cast<int64_t>(g) * A.maxpages + e] = A.fstack[static_cast<int64_t>(g) * A.maxpages + top - 1];
+        A.ftop[g] = top - 1;
+      }
+    }
+    A.pos[static_cast<int64_t>(g) * A.cap + cnt] = newest;
+    A.nextpos[g] = newest + 1;
+  }
+  if (tid == 0) {
+    const int64_t bj = static_cast<int64_t>(b) * A.maxblk + j;
+    if (opens) {
+      A.btab[static_cast<int64_t>(b) * A.maxpages + e] = j;
+      A.nres[b] = e + 1;
+      A.bscore[bj] = 0.f;
+      A.btref[bj] = A.t;
+      A.bres[bj] = 1;
+      for (int r = 0; r < kRegions; ++r) A.bcnt[bj * kRegions + r] = 0;
+    }
+    A.bcnt[bj * kRegions + A.decode_region] += 1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge the attention splits of one (layer, group): per-head global (max,
+// sum) into ml and the normalised output into out.
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(NT) void blk_merge_kernel(BlockArgs A) {
+  const int l = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int b = g / A.Hkv, kvh = g % A.Hkv;
+  const int HG = A.HG, D = A.D, S = A.S;
+  extern __shared__ float sh[];
+  float* s_w = sh;             // [HG][S] split weights
+  float* s_mz = sh + HG * S;   // [HG][2]
+  const float2* pm = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * S * HG;
+  // splits past the group's own token count were not written this step
+  const int ns = (A.count[g] + 1 + kAttnChunk - 1) / kAttnChunk;
+  if (tid < HG) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * HG + tid].x);
+    float Z = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float2 v = pm[s * HG + tid];
+      const float w = v.x == -INFINITY ? 0.f : __expf(v.x - M);
+      s_w[tid * S + s] = w;
+      Z += v.y * w;
+    }
+    s_mz[tid * 2] = M;
+    s_mz[tid * 2 + 1] = Z;
+    reinterpret_cast<float2*>(A.ml)[(static_cast<int64_t>(l) * A.G + g) * HG + tid] =
+        make_float2(M, Z);
+  }
+  __syncthreads();
+  const float* po = A.part_o + (static_cast<int64_t>(l) * A.G + g) * S * HG * D;
+  for (int idx = tid; idx < HG * D; idx += NT) {
+    const int h = idx / D;
+    float o = 0.f;
+    for (int s = 0; s < ns; ++s) o += s_w[h * S + s] * po[static_cast<int64_t>(s) * HG * D + idx];
+    A.out[(static_cast<int64_t>(l * A.batch + b) * A.Hq + kvh * HG) * D + idx] = o / s_mz[h * 2 + 1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mass: per table entry, the probability landing on the block's tokens,
+// summed over every layer, KV head and query head.  Block (4 entries,
+// sequence); thread (slot of 64, quarter of the (layer, KV head) pairs).
+// ---------------------------------------------------------------------------
+constexpr int kMassNT = 256;
+__global__ __launch_bounds__(kMassNT) void blk_mass_kernel(BlockArgs A) {
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int g0 = b * A.Hkv;
+  const int nres = A.nres[b];
+  const int e0 = blockIdx.x * 4;
+  if (e0 >= nres) return;
+  const int n = A.count[g0] + 1;  // slots including the new token
+  extern __shared__ float sh[];
+  float* s_ml = sh;                            // [L][Hkv][4][2]
+  float* s_red = sh + A.L * A.Hkv * 8;         // [4][64]
+  const int nml = A.L * A.Hkv * 8;
+  for (int i = tid; i < nml; i += kMassNT) {
+    const int l = i / (A.Hkv * 8), rest = i % (A.Hkv * 8);
+    s_ml[i] = A.ml[((static_cast<int64_t>(l) * A.G + g0) * 4) * 2 + rest];
+  }
+  __syncthreads();
+  const int sl = tid % 64, part = tid / 64;
+  const int slot = e0 * kPageTokens + sl;
+  float acc = 0.f;
+  if (slot < n) {
+    for (int i = part; i < A.L * A.Hkv; i += 4) {
+      const int l = i / A.Hkv, h = i % A.Hkv;
+      const float4 x = *reinterpret_cast<const float4*>(
+          A.logits + ((static_cast<int64_t>(g0 + h) * A.L + l) * A.lstride + slot) * 4);
+      const float* m = &s_ml[i * 8];
+      acc += __expf(x.x - m[0]) / m[1] + __expf(x.y - m[2]) / m[3] + __expf(x.z - m[4]) / m[5] +
+             __expf(x.w - m[6]) / m[7];
+    }
+  }
+  s_red[part * 64 + sl] = acc;
+  __syncthreads();
+  if (tid < 64) {
+    float v = s_red[tid] + s_red[64 + tid] + s_red[128 + tid] + s_red[192 + tid];
+    v = row16_sum(v);
+    const int e = e0 + tid / kPageTokens;
+    if ((tid % kPageTokens) == 0 && e < nres) A.bmass[static_cast<int64_t>(b) * A.maxpages + e] = v;
+  }
+}
+
+// Exclusive prefix sum of one int per thread over the block (NT threads).
+template <int NT>
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) s_tmp[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < NT / kWave; ++i) {
+    if (i < w) base += s_tmp[i];
+    tot += s_tmp[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// Policy: per sequence, the score / clock update of every resident block
+// (update), then (do_select) the priority of every block, the selection of
+// the budget's lowest priorities with the pinned blocks forced, and the
+// stable compaction of the block table, page tables and positions; evicted
+// pages return to their group's stack.  appended: the step's new token is
+// resident but not yet counted in count[].
+// ---------------------------------------------------------------------------
+constexpr int kPolNT = 256;
+__global__ __launch_bounds__(kPolNT) void blk_policy_kernel(BlockArgs A, int update, int do_select,
+                                                            int appended, int budget_override) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int g0 = b * A.Hkv;
+  const int nres = A.nres[b];
+  const int cnt = A.count[g0] + (appended ? 1 : 0);
+  const int fill = cnt - kPageTokens * (nres - 1);
+  const int B = budget_override > 0 ? budget_override : A.bbudget[b];
+  const bool sel = do_select && nres > B;
+  // LDS: the keys (later the new block table in their first half and the
+  // staged table rows in their second half), then the new index per entry
+  extern __shared__ unsigned char shb[];
+  unsigned long long* s_key = reinterpret_cast<unsigned long long*>(shb);   // [maxpages]
+  int* s_btab = reinterpret_cast<int*>(s_key);                             // [maxpages], after ranking
+  int* s_row = s_btab + A.maxpages;                                        // [maxpages], after ranking
+  int* s_new = reinterpret_cast<int*>(s_key + A.maxpages);                 // [maxpages]
+  __shared__ int s_tmp[kPolNT / kWave];
+  const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
+  const int64_t bblk = static_cast<int64_t>(b) * A.maxblk;
+  const float inv = 1.0f / static_cast<float>(A.Hq * A.L);
+  const float thr = A.tau / static_cast<float>(cnt);
+
+  for (int e = tid; e < nres; e += kPolNT) {
+    const int j = A.btab[brow + e];
+    const int nb = (e == nres - 1) ? fill : kPageTokens;
+    float sc = A.bscore[bblk + j];
+    int tr = A.btref[bblk + j];
+    if (update) {
+      const float mass = A.bmass[brow + e] * inv;
+      sc = A.alpha * mass + (1.0f - A.alpha) * sc;
+      A.bscore[bblk + j] = sc;
+      if (mass / static_cast<float>(nb) >= thr) {
+        tr = A.t;
+        A.btref[bblk + j] = tr;
+      }
+    }
+    if (sel) {
+      const float idle = static_cast<float>(A.t - tr);
+      bool pin = e == nres - 1;
+      float surv = 0.f;
+      const uint8_t* cnt8 = A.bcnt + (bblk + j) * kRegions;
+#pragma unroll
+      for (int r = 0; r < kRegions; ++r) {
+        const int c8 = cnt8[r];
+        if (c8 == 0) continue;
+        surv += static_cast<float>(c8) * __expf(-(A.beta + A.lam[r]) * idle);
+        if ((A.pinned_mask >> r) & 1u) pin = true;
+      }
+      surv /= static_cast<float>(nb);
+      const float prio = (1.0f - sc) * (1.0f - surv);
+      // larger key is kept: lower priority first, then the higher block id
+      s_key[e] = pin ? ~0ull
+                     : (static_cast<unsigned long long>(~float_key(prio)) << 32) | static_cast<uint32_t>(j);
+    }
+  }
+  if (!sel) {
+    if (appended && tid < A.Hkv) A.count[g0 + tid] = cnt;
+    return;
+  }
+  __syncthreads();
+
+  // keep iff fewer than B keys are larger (pinned keys are all ~0: rank 0)
+  const int per = (nres + kPolNT - 1) / kPolNT;
+  const int e_lo = min(nres, tid * per), e_hi = min(nres, e_lo + per);
+  int mine = 0;
+  for (int e = e_lo; e < e_hi; ++e) {
+    const unsigned long long k = s_key[e];
+    int r = 0;
+    if (k != ~0ull)
+      for (int e2 = 0; e2 < nres; ++e2) r += s_key[e2] > k;
+    const int keep = r < B;
+    s_new[e] = keep;
+    mine += keep;
+  }
+  int kept = 0;
+  int base = block_exclusive_scan<kPolNT>(mine, s_tmp, &kept);
+  // s_new[e] becomes the new index of a kept entry, or -1 - (evicted rank)
+  for (int e = e_lo; e < e_hi; ++e) {
+    const int keep = s_new[e];
+    s_new[e] = keep ? base : -1 - (e - base);
+    base += keep;
+  }
+  if (kept != B && tid == 0) atomicOr(A.errflag, 32);
+  __syncthreads();
+
+  // block table (built in LDS over the keys, which are no longer read),
+  // evicted flags, then one page table per KV head
+  for (int e = tid; e < nres; e += kPolNT) {
+    const int ni = s_new[e];
+    const int j = A.btab[brow + e];
+    if (ni >= 0) s_btab[ni] = j;
+    else A.bres[bblk + j] = 0;
+  }
+  __syncthreads();
+  for (int e = tid; e < kept; e += kPolNT) A.btab[brow + e] = s_btab[e];
+  for (int h = 0; h < A.Hkv; ++h) {
+    const int g = g0 + h;
+    const int64_t grow = static_cast<int64_t>(g) * A.maxpages;
+    const int top = A.ftop[g];
+    for (int e = tid; e < nres; e += kPolNT) s_row[e] = A.ptab[grow + e];
+    __syncthreads();
+    for (int e = tid; e < nres; e += kPolNT) {
+      const int ni = s_new[e];
+      if (ni >= 0) A.ptab[grow + ni] = s_row[e];
+      else A.fstack[grow + top + (-1 - ni)] = s_row[e];
+    }
+    __syncthreads();
+    if (tid == 0) A.ftop[g] = top + (nres - kept);
+  }
+  // positions of every kept slot (slot 16*i + r holds token 16*btab[i] + r)
+  const int new_cnt = kPageTokens * (kept - 1) + fill;
+  for (int i = tid; i < new_cnt * A.Hkv; i += kPolNT) {
+    const int h = i / new_cnt, s = i % new_cnt;
+    A.pos[static_cast<int64_t>(g0 + h) * A.cap + s] = s_btab[s / kPageTokens] * kPageTokens + s % kPageTokens;
+  }
+  if (tid < A.Hkv) A.count[g0 + tid] = new_cnt;
+  if (tid == 0) A.nres[b] = kept;
+}
+
+// ---------------------------------------------------------------------------
+// Re-admission of n evicted blocks of sequence b: they take table entries
+// [tail, tail + n) with their persisted score and clock t, the tail entry
+// moves behind them, pages come from the groups' stacks.  One block.
+// ---------------------------------------------------------------------------
+__global__ void blk_readmit_kernel(BlockArgs A, int b, int n, const int* __restrict__ ids) {
+  const int tid = threadIdx.x;
+  const int g0 = b * A.Hkv;
+  const int e_tail = A.nres[b] - 1;
+  const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
+  const int64_t bblk = static_cast<int64_t>(b) * A.maxblk;
+  if (tid < A.Hkv) {
+    const int g = g0 + tid;
+    const int64_t grow = static_cast<int64_t>(g) * A.maxpages;
+    const int tail_page = A.ptab[grow + e_tail];
+    int top = A.ftop[g];
+    if (top < n) {
+      atomicOr(A.errflag, 8);
+      return;
+    }
+    for (int i = 0; i < n; ++i) A.ptab[grow + e_tail + i] = A.fstack[grow + --top];
+    A.ptab[grow + e_tail + n] = tail_page;
+    A.ftop[g] = top;
+    const int fill = A.count[g] - kPageTokens * e_tail;
+    A.count[g] += kPageTokens * n;
+    // positions of the new entries and of the moved tail
+    const int tail_j = A.btab[brow + e_tail];
+    int* pg = A.pos + static_cast<int64_t>(g) * A.cap;
+    for (int i = 0; i < n; ++i)
+      for (int r = 0; r < kPageTokens; ++r) pg[kPageTokens * (e_tail + i) + r] = ids[i] * kPageTokens + r;
+    for (int r = 0; r < fill; ++r) pg[kPageTokens * (e_tail + n) + r] = tail_j * kPageTokens + r;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int tail_j = A.btab[brow + e_tail];
+    for (int i = 0; i < n; ++i) {
+      A.btab[brow + e_tail + i] = ids[i];
+      A.bres[bblk + ids[i]] = 1;
+      A.btref[bblk + ids[i]] = A.t;
+    }
+    A.btab[brow + e_tail + n] = tail_j;
+    A.nres[b] = e_tail + 1 + n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static BlockArgs block_args(kvev_ctx* c, float* out, int n_max) {
+  const auto& cf = c->cfg;
+  BlockArgs A;
+  A.count = c->d.count;
+  A.pos = c->d.pos;
+  A.nextpos = c->d.nextpos;
+  A.ptab = c->d.ptab;
+  A.btab = c->d.btab;
+  A.nres = c->d.nres;
+  A.bscore = c->d.bscore;
+  A.btref = c->d.btref;
+  A.bres = c->d.bres;
+  A.bcnt = c->d.bcnt;
+  A.fstack = c->d.fstack;
+  A.ftop = c->d.ftop;
+  A.bmass = c->d.bmass;
+  A.bbudget = c->d.bbudget;
+  A.errflag = c->d.errflag;
+  A.logits = c->d.logits;
+  A.ml = c->d.ml;
+  A.part_ml = c->d.part_ml;
+  A.part_o = c->d.part_o;
+  A.out = out;
+  A.L = cf.n_layers;
+  A.G = c->G;
+  A.Hkv = cf.n_kv_heads;
+  A.Hq = cf.n_q_heads;
+  A.HG = c->HG;
+  A.D = cf.head_dim;
+  A.maxpages = c->maxpages;
+  A.maxblk = c->maxblk;
+  A.S = (n_max + kAttnChunk - 1) / kAttnChunk;
+  A.batch = cf.batch;
+  A.cap = c->cap;
+  A.lstride = c->lstride;
+  A.alpha = cf.alpha_new;
+  A.beta = cf.beta;
+  A.tau = cf.access_tau_mult;
+  for (int r = 0; r < kRegions; ++r) A.lam[r] = c->lam[r];
+  A.pinned_mask = cf.pinned_region_mask;
+  A.decode_region = cf.decode_region;
+  A.t = static_cast<int>(c->t);
+  return A;
+}
+
+hipError_t launch_block_open(kvev_ctx* c, int n_max, int t) {
+  BlockArgs A = block_args(c, nullptr, n_max);
+  A.t = t;
+  blk_open_kernel<<<c->cfg.batch, 64, 0, c->stream>>>(A, n_max);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max) {
+  BlockArgs A = block_args(c, out, n_max);
+  dim3 grid(c->cfg.n_layers, c->G);
+  const size_t shm = (static_cast<size_t>(c->HG) * A.S + c->HG * 2) * sizeof(float);
+  blk_merge_kernel<256><<<grid, 256, shm, c->stream>>>(A);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
+  BlockArgs A = block_args(c, nullptr, n_max);
+  dim3 grid((n_max + 63) / 64, c->cfg.batch);
+  const size_t shm = (static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 8 + 256) * sizeof(float);
+  blk_mass_kernel<<<grid, kMassNT, shm, c->stream>>>(A);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
+                               int budget_override) {
+  BlockArgs A = block_args(c, nullptr, 1);
+  A.t = t;
+  const size_t shm = static_cast<size_t>(c->maxpages) * (8 + 4);
+  blk_policy_kernel<<<c->cfg.batch, kPolNT, shm, c->stream>>>(A, update, do_select, appended,
+                                                              budget_override);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, int t) {
+  BlockArgs A = block_args(c, nullptr, 1);
+  A.t = t;
+  blk_readmit_kernel<<<1, 64, 0, c->stream>>>(A, b, n, ids_dev);
+  return hipGetLastError();
+}
+
+}  // namespace kvev

@@ -14,6 +14,8 @@ namespace kvev {
 constexpr int kAttnChunk = 256;   // slots per attention split
 constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies itself
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
+constexpr int kRegions = 8;       // region labels of the block-granular mode
+constexpr int kMaxBlockEntries = 4096;  // block-table entries per sequence (block mode)
 
 // Device buffers of one context.  Groups are (sequence, KV head) pairs,
 // g = seq * Hkv + kv_head; slots of a group are its cached tokens in order.
@@ -38,6 +40,18 @@ struct DevState {
   int* blk_slot = nullptr;                // [G][max_post_blocks] its slot
   int* blk_page = nullptr;                // [G][max_post_blocks] that slot's page
   float* blk_sum = nullptr;               // [G][max_post_blocks] per-block utility sum
+  // block-granular mode
+  int* btab = nullptr;      // [batch][maxpages] logical block of each table entry
+  int* nres = nullptr;      // [batch] table entries (resident blocks)
+  float* bscore = nullptr;  // [batch][maxblk] score of every logical block (kept when evicted)
+  int* btref = nullptr;     // [batch][maxblk] step of the last access / insertion
+  int* bres = nullptr;      // [batch][maxblk] 1 while resident
+  uint8_t* bcnt = nullptr;  // [batch][maxblk][kRegions] tokens of each region in the block
+  int* fstack = nullptr;    // [G][maxpages] free pages of each group
+  int* ftop = nullptr;      // [G] free pages on the stack
+  float* bmass = nullptr;   // [batch][maxpages] step mass per table entry (unnormalised)
+  int* bbudget = nullptr;   // [batch] retained blocks per sequence
+  int* rd_ids = nullptr;    // [maxpages] block ids of one re-admission call
 };
 
 struct Profiler {
@@ -74,12 +88,22 @@ struct kvev_ctx {
   std::string err;
   kvev::Profiler prof;
   std::vector<int> ptab_upd;                // scratch for page-table updates
+  // block-granular mode
+  bool block_mode = false;
+  int maxblk = 0;
+  float lam[kvev::kRegions] = {};
+  std::vector<int> nres;                    // host mirror of resident blocks per sequence
+  std::vector<int64_t> npos;                // next position per sequence
+  std::vector<int> bbudget;                 // per-sequence block budget
+  std::vector<int> npinned;                 // blocks pinned by region labels per sequence
 };
 
 namespace kvev {
 
 // Launchers (defined in the .hip translation units).  All are stream-ordered.
 hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
+// scatter into table entries [e0, e0 + ceil(n/16)) of every KV head of `seq`
+hipError_t launch_scatter_at(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n, int e0);
 hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
 hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                             int n_max, int write_logits);
@@ -89,5 +113,12 @@ hipError_t launch_select(kvev_ctx* c, int64_t budget);
 hipError_t launch_moves(kvev_ctx* c, int max_moves);
 hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);
 hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n);
+// block-granular mode (block.hip)
+hipError_t launch_block_open(kvev_ctx* c, int n_max, int t);
+hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max);
+hipError_t launch_block_mass(kvev_ctx* c, int n_max);
+hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
+                               int budget_override);
+hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, int t);
 
 }  // namespace kvev

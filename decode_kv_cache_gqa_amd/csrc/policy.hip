@@ -721,20 +721,21 @@ __global__ __launch_bounds__(NT) void move_kernel(T* __restrict__ kpool, T* __re
   }
 }
 
-// Prefill: copy k, v [L][Hkv][n][D] of one sequence into its groups' pages,
-// one page (16 tokens) per block; V goes through LDS to be stored
-// channel-major.  Rows of the last page beyond n are zero-filled.
+// Prefill: copy k, v [L][Hkv][n][D] of one sequence into its groups' pages
+// (table entries e0, e0 + 1, ...), one page (16 tokens) per block; V goes
+// through LDS to be stored channel-major.  Rows of the last page beyond n
+// are zero-filled.
 template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT) void scatter_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                      T* __restrict__ kpool, T* __restrict__ vpool,
                                                      const int* __restrict__ ptab, int seq, int Hkv,
-                                                     int64_t n, int64_t P, int maxpages) {
+                                                     int64_t n, int64_t P, int maxpages, int e0) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
   __shared__ T tile[kPageTokens][D + EPL];
   const int pg = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int g = seq * Hkv + h;
-  const int page = ptab[static_cast<int64_t>(g) * maxpages + pg];
+  const int page = ptab[static_cast<int64_t>(g) * maxpages + e0 + pg];
   const int64_t tb = static_cast<int64_t>(pg) * kPageTokens;
   for (int idx = threadIdx.x; idx < kPageTokens * LPR; idx += NT) {
     const int r = idx / LPR, sub = idx % LPR;
@@ -904,21 +905,27 @@ hipError_t launch_moves(kvev_ctx* c, int max_moves) {
 }
 
 template <typename T, int D>
-static hipError_t scatter_impl(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
+static hipError_t scatter_impl(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n, int e0) {
   constexpr int NT = 256;
   const int64_t npages = (n + kPageTokens - 1) / kPageTokens;
+  if (e0 < 0 || e0 + npages > c->maxpages) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(npages), c->cfg.n_kv_heads, c->cfg.n_layers);
   scatter_kernel<T, D, NT><<<grid, NT, 0, c->stream>>>(
       static_cast<const T*>(k), static_cast<const T*>(v), static_cast<T*>(c->d.kpool),
-      static_cast<T*>(c->d.vpool), c->d.ptab, seq, c->cfg.n_kv_heads, n, c->P, c->maxpages);
+      static_cast<T*>(c->d.vpool), c->d.ptab, seq, c->cfg.n_kv_heads, n, c->P, c->maxpages, e0);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
+hipError_t launch_scatter_at(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n, int e0) {
   const int D = c->cfg.head_dim;
-  if (c->cfg.dtype == KVEV_BF16) return D == 128 ? scatter_impl<bf16_t, 128>(c, seq, k, v, n)
-                                                 : scatter_impl<bf16_t, 64>(c, seq, k, v, n);
-  return D == 128 ? scatter_impl<float, 128>(c, seq, k, v, n) : scatter_impl<float, 64>(c, seq, k, v, n);
+  if (c->cfg.dtype == KVEV_BF16) return D == 128 ? scatter_impl<bf16_t, 128>(c, seq, k, v, n, e0)
+                                                 : scatter_impl<bf16_t, 64>(c, seq, k, v, n, e0);
+  return D == 128 ? scatter_impl<float, 128>(c, seq, k, v, n, e0)
+                  : scatter_impl<float, 64>(c, seq, k, v, n, e0);
+}
+
+hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
+  return launch_scatter_at(c, seq, k, v, n, 0);
 }
 
 template <typename T, int D>

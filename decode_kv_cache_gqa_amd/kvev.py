@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libkvev.so")
 
 OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-EMA, CUMULATIVE = 0, 1
+EMA, CUMULATIVE, LRFU_BLOCK = 0, 1, 2
+MAX_REGIONS = 8
 _STATUS = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EHIP: "EHIP", ESTATE: "ESTATE", ERANGE: "ERANGE"}
 
 
@@ -37,6 +38,9 @@ class Config(ctypes.Structure):
         ("refresh_interval", ctypes.c_int32), ("score_free", ctypes.c_int32),
         ("n_sink", ctypes.c_int32), ("n_recent", ctypes.c_int32),
         ("budget", ctypes.c_int64),
+        ("beta", ctypes.c_float), ("region_half_life", ctypes.c_float * 8),
+        ("pinned_region_mask", ctypes.c_uint32), ("decode_region", ctypes.c_int32),
+        ("access_tau_mult", ctypes.c_float),
     ]
 
 
@@ -46,7 +50,8 @@ _SIGS = {
     "kvev_config_init": (None, [ctypes.POINTER(Config)]),
     "kvev_create": (ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
     "kvev_destroy": (ctypes.c_int, [ctypes.c_void_p]),
-    "kvev_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]),
+    "kvev_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_void_p]),
     "kvev_decode_step": (ctypes.c_int, [ctypes.c_void_p] * 5),
     "kvev_evict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
     "kvev_step": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64]),
@@ -58,6 +63,14 @@ _SIGS = {
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "kvev_import_group": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvev_set_budget": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
+    "kvev_readmit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "kvev_block_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_import_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
     "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
@@ -148,12 +161,18 @@ class Context:
         return lib().kvev_step_index(self._h)
 
     # -- C ABI ---------------------------------------------------------------
-    def prefill(self, seq, k, v):
+    def prefill(self, seq, k, v, region_labels=None):
         c = self.cfg
         n = k.shape[2]
         shape = (c.n_layers, c.n_kv_heads, n, c.head_dim)
+        lab = None
+        if region_labels is not None:
+            lab = np.ascontiguousarray(region_labels, dtype=np.uint8)
+            if lab.shape != (n,):
+                raise ValueError(f"region_labels has shape {lab.shape}, expected ({n},)")
         self._check(lib().kvev_prefill(self._h, seq, _ptr(k, self.dtype, shape, "k"),
-                                       _ptr(v, self.dtype, shape, "v"), n))
+                                       _ptr(v, self.dtype, shape, "v"), n,
+                                       None if lab is None else lab.ctypes.data_as(ctypes.c_void_p)))
 
     def decode_step(self, q, k_new, v_new, out):
         import torch
@@ -215,6 +234,46 @@ class Context:
             scores.ctypes.data_as(ctypes.c_void_p), _ptr(k, self.dtype, shape, "k"),
             _ptr(v, self.dtype, shape, "v")))
 
+    # -- block-granular mode ----------------------------------------------------
+    def set_budget(self, seq, budget):
+        self._check(lib().kvev_set_budget(self._h, seq, int(budget)))
+
+    def readmit(self, seq, block_ids, k, v):
+        """k, v: [L, Hkv, 16 * len(block_ids), d] holding the blocks' tokens."""
+        c = self.cfg
+        ids = np.ascontiguousarray(block_ids, dtype=np.int64)
+        shape = (c.n_layers, c.n_kv_heads, 16 * ids.shape[0], c.head_dim)
+        self._check(lib().kvev_readmit(self._h, seq, ids.shape[0], ids.ctypes.data_as(ctypes.c_void_p),
+                                       _ptr(k, self.dtype, shape, "k"), _ptr(v, self.dtype, shape, "v")))
+
+    def block_state(self, seq):
+        """(score float32, tref int32, resident bool) over every block seen."""
+        cap = (self.cfg.max_tokens + 15) // 16
+        sc = np.zeros(cap, np.float32)
+        tr = np.zeros(cap, np.int32)
+        rs = np.zeros(cap, np.uint8)
+        n = ctypes.c_int64()
+        self._check(lib().kvev_block_state(self._h, seq, sc.ctypes.data_as(ctypes.c_void_p),
+                                           tr.ctypes.data_as(ctypes.c_void_p),
+                                           rs.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)))
+        m = n.value
+        return sc[:m].copy(), tr[:m].copy(), rs[:m].astype(bool)
+
+    def import_blocks(self, seq, score, tref, resident, k, v):
+        c = self.cfg
+        score = np.ascontiguousarray(score, dtype=np.float32)
+        tref = np.ascontiguousarray(tref, dtype=np.int32)
+        res = np.ascontiguousarray(resident, dtype=np.uint8)
+        nb = score.shape[0]
+        if tref.shape[0] != nb or res.shape[0] != nb:
+            raise ValueError("score, tref and resident differ in length")
+        n_tok = k.shape[2]
+        shape = (c.n_layers, c.n_kv_heads, n_tok, c.head_dim)
+        self._check(lib().kvev_import_blocks(
+            self._h, seq, nb, score.ctypes.data_as(ctypes.c_void_p), tref.ctypes.data_as(ctypes.c_void_p),
+            res.ctypes.data_as(ctypes.c_void_p), n_tok, _ptr(k, self.dtype, shape, "k"),
+            _ptr(v, self.dtype, shape, "v")))
+
     def sync(self):
         self._check(lib().kvev_sync(self._h))
 
@@ -232,8 +291,20 @@ class Context:
 
 
 def context_for(w, max_steps=None, budget=None, stream=None):
-    """A context configured for a synth.Workload (token-granular policies)."""
+    """A context configured for a synth.Workload."""
     steps = w.steps if max_steps is None else max_steps
+    if w.policy == "lrfu_block":
+        cfg = make_config(
+            n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+            head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,
+            max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=LRFU_BLOCK,
+            alpha_new=w.alpha_new, budget=max(w.block_budget(b) for b in range(w.batch))
+            if budget is None else budget, beta=w.beta,
+            pinned_region_mask=sum(1 << r for r in w.pinned_regions), decode_region=w.decode_region,
+            access_tau_mult=2.0)
+        for r, hl in enumerate(w.region_half_lives):
+            cfg.region_half_life[r] = hl
+        return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
         head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,

@@ -50,8 +50,20 @@ typedef enum { KVEV_F32 = 0, KVEV_BF16 = 1 } kvev_dtype;
  *  EMA:        score <- alpha_new*mass + (1-alpha_new)*score, applied once per
  *              layer in ascending layer order ("What Matters ...", section
  *              3.1 Eq.4 and appendix E "Layer scoring").
- *  CUMULATIVE: score <- score + mass per layer (same page, Eq.3).          */
-typedef enum { KVEV_EMA = 0, KVEV_CUMULATIVE = 1 } kvev_policy;
+ *  CUMULATIVE: score <- score + mass per layer (same page, Eq.3).
+ *  LRFU_BLOCK: one score per (sequence, 16-token block) over every layer
+ *              and head: the block's attention mass summed over layers and
+ *              query heads and divided by n_q_heads * n_layers, folded once
+ *              per step by the EMA rule; eviction priority
+ *              (1 - score)(1 - survival), survival = the block's mean over
+ *              its tokens of exp(-(beta + lambda_region) * idle) ("Attention-
+ *              Aware Block Eviction" figure page; "MemDecay" section III-C
+ *              Eq.3-4 and section IV-B Eq.7 for lambda = ln2 / half-life).
+ *              Lower priority is kept.  Selection groups are sequences and
+ *              budgets count blocks.                                          */
+typedef enum { KVEV_EMA = 0, KVEV_CUMULATIVE = 1, KVEV_LRFU_BLOCK = 2 } kvev_policy;
+
+#define KVEV_MAX_REGIONS 8
 
 typedef struct {
   int32_t n_layers;         /* L, 1..64 */
@@ -70,7 +82,20 @@ typedef struct {
                                (same page, section 3.2 "Score-Free") */
   int32_t n_sink;           /* positions < n_sink are never evicted */
   int32_t n_recent;         /* the n_recent newest positions are never evicted */
-  int64_t budget;           /* retained tokens per (sequence, KV head) */
+  int64_t budget;           /* retained tokens per (sequence, KV head); LRFU_BLOCK:
+                               retained blocks per sequence (default for all) */
+  /* KVEV_LRFU_BLOCK only (ignored by the token policies).  In this mode
+   * max_tokens bounds the positions a sequence reaches (prefill + steps) and
+   * may be at most 65536; n_sink, n_recent must be 0, refresh_interval 1,
+   * score_free 0 (protection comes from pinned regions). */
+  float beta;                                 /* recency rate (>= 0), e.g. 0.001 */
+  float region_half_life[KVEV_MAX_REGIONS];   /* steps; <= 0: that region does not decay */
+  uint32_t pinned_region_mask;                /* bit r: blocks holding a region-r token are
+                                                 never evicted */
+  int32_t decode_region;                      /* region of decoded tokens, 0..7, not pinned */
+  float access_tau_mult;                      /* a block is accessed when its mass per token
+                                                 is >= access_tau_mult / (resident tokens);
+                                                 "MemDecay" section IV-A uses 2 */
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -90,11 +115,17 @@ kvev_status kvev_destroy(kvev_ctx* ctx);
 /* Load the prefill cache of sequence `seq` (0 <= seq < batch): device k, v
  * laid out [n_layers][n_kv_heads][n_tokens][head_dim].  Positions are
  * 0..n_tokens-1 and every utility starts at 0 ("What Matters ...", appendix
- * E "Momentum initialization").  Must be called for every sequence before
- * the first decode step, and not after it.  Errors: KVEV_EINVAL (n_tokens < 1
- * or + decode headroom > max_tokens), KVEV_ESTATE, KVEV_ENOMEM (pool). */
+ * E "Momentum initialization").  region_labels: host, one label (0..7) per
+ * token, used by KVEV_LRFU_BLOCK (NULL: every token takes decode_region;
+ * ignored by the token policies).  In LRFU_BLOCK mode every block starts
+ * resident with score 0 and clock 0; the blocks pinned by the labels plus
+ * the last block must fit the budget each selection uses (checked by
+ * kvev_set_budget and by every selecting call).  Must be called for every
+ * sequence before the first decode step, and not after it.
+ * Errors: KVEV_EINVAL (n_tokens < 1 or + decode headroom > max_tokens, a
+ * label out of range), KVEV_ESTATE, KVEV_ENOMEM (pool). */
 kvev_status kvev_prefill(kvev_ctx* ctx, int32_t seq, const void* k, const void* v,
-                         int64_t n_tokens);
+                         int64_t n_tokens, const uint8_t* region_labels);
 
 /* Decode step t (counted by the context from 1): append k_new/v_new at the
  * next position of every (layer, sequence, KV head); run GQA decode
@@ -136,7 +167,9 @@ kvev_status kvev_step(kvev_ctx* ctx, const void* q, const void* k_new, const voi
                       float* out, int64_t budget);
 
 /* Copy the utilities of group (seq, kv_head) in slot order into host `dst`
- * (capacity `cap` floats); *n_written = the group's token count.
+ * (capacity `cap` floats); *n_written = the group's token count.  In
+ * LRFU_BLOCK mode: the scores of every block the sequence has had, by block
+ * id (kv_head must be a valid head; scores are shared by all heads).
  * Synchronises.  Errors: KVEV_ERANGE (cap too small / bad indices). */
 kvev_status kvev_scores(kvev_ctx* ctx, int32_t seq, int32_t kv_head, float* dst,
                         int64_t cap, int64_t* n_written);
@@ -161,6 +194,43 @@ kvev_status kvev_import_group(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int64
                               const int32_t* positions, const float* scores,
                               const void* k, const void* v);
 
+/* ---- KVEV_LRFU_BLOCK mode ---------------------------------------------- */
+
+/* Set the retained-block budget of sequence `seq` (used by kvev_step and
+ * kvev_evict when their budget argument is <= 0).  Errors: KVEV_EINVAL (not
+ * block mode, budget below the sequence's pinned blocks + 1). */
+kvev_status kvev_set_budget(kvev_ctx* ctx, int32_t seq, int64_t budget);
+
+/* Re-admit n evicted blocks of sequence `seq`: host block_ids (ids are
+ * position / 16; each evicted, not the block being filled), device k, v
+ * [n_layers][n_kv_heads][16 * n][head_dim] holding the blocks' tokens in
+ * the order of block_ids.  Each block returns with the score it had when it
+ * was evicted (the "Attention-Aware Block Eviction" figure page: the
+ * block's key and score persist and are restored rather than reset) and
+ * its clock set to the current step count.  The resident count may then
+ * exceed the budget until the next selection.  Synchronises (validation
+ * reads the residency flags).  Errors: KVEV_EINVAL (not block mode, a block
+ * resident or unknown, duplicates), KVEV_ENOMEM (no free pages). */
+kvev_status kvev_readmit(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* block_ids,
+                         const void* k, const void* v);
+
+/* Copy the state of every block sequence `seq` has had so far (ids
+ * 0..*n_blocks-1) to host buffers: score, clock (step of the last access or
+ * insertion), resident flag.  Any of the three may be NULL.  Synchronises.
+ * Errors: KVEV_EINVAL (not block mode), KVEV_ERANGE (cap too small). */
+kvev_status kvev_block_state(kvev_ctx* ctx, int32_t seq, float* score, int32_t* tref,
+                             uint8_t* resident, int64_t cap, int64_t* n_blocks);
+
+/* Replace the block state of sequence `seq`: host score, tref, resident for
+ * blocks 0..n_blocks-1 (n_blocks must equal the count of blocks seen; the
+ * last block must be resident), and device k, v [n_layers][n_kv_heads]
+ * [n_tokens][head_dim] with the resident blocks' tokens in ascending block
+ * order (n_tokens must equal those blocks' token count).  Used to put both
+ * sides of a comparison on the same state.  Errors: KVEV_EINVAL. */
+kvev_status kvev_import_blocks(kvev_ctx* ctx, int32_t seq, int64_t n_blocks, const float* score,
+                               const int32_t* tref, const uint8_t* resident, int64_t n_tokens,
+                               const void* k, const void* v);
+
 /* Wait for all work queued on the context's stream; report a HIP error. */
 kvev_status kvev_sync(kvev_ctx* ctx);
 
@@ -171,7 +241,10 @@ int64_t kvev_step_index(const kvev_ctx* ctx);
  * around every launch of the named kernel while enabled.  `kernel`:
  * "attn" (append + split attention), "post" (split merge, probability pass,
  * fold, and in kvev_step selection + compaction), "select" and "move"
- * (kvev_evict; "move" also in kvev_step when many slots move).
+ * (kvev_evict; "move" also in kvev_step when many slots move).  LRFU_BLOCK
+ * mode: "open" (slot and block of the new token), "attn", "merge" (split
+ * merge and output), "mass" (block mass), "policy" (score, clock, priority,
+ * selection, table compaction), "readmit".
  * *total_ms / *launches cover the launches since the last reset. */
 kvev_status kvev_profile_enable(kvev_ctx* ctx, int32_t enable);
 kvev_status kvev_profile_reset(kvev_ctx* ctx);

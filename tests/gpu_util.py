@@ -178,3 +178,156 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                 f"resyncs {st.near_tie_resyncs} ({time.time() - t_start:.1f}s)")
     ctx.close()
     return st
+
+
+# ---------------------------------------------------------------------------
+# Block-granular LRFU mode
+# ---------------------------------------------------------------------------
+
+def block_rows(w, b, ids, device="cuda"):
+    """K, V [L, Hkv, 16*len(ids), d] of blocks `ids` of sequence b: prefill
+    rows regenerated from the seed, decoded rows from the step inputs that
+    appended them."""
+    import torch
+    L0 = w.prefill_lens[b]
+    pos = np.concatenate([np.arange(16 * j, 16 * j + 16) for j in ids]).astype(np.int64)
+    K = torch.empty((w.n_layers, w.n_kv_heads, len(pos), w.head_dim), dtype=w.torch_dtype, device=device)
+    V = torch.empty_like(K)
+    pre = np.flatnonzero(pos < L0)
+    if len(pre):
+        Kp, Vp = w.prefill_rows(b, pos[pre], device=device)
+        idx = torch.from_numpy(pre).to(device)
+        K[:, :, idx] = Kp
+        V[:, :, idx] = Vp
+    for i in np.flatnonzero(pos >= L0).tolist():
+        _, kn, vn = w.step_inputs(int(pos[i]) - L0 + 1, device=device, seqs=[b])
+        K[:, :, i] = kn[:, 0]
+        V[:, :, i] = vn[:, 0]
+    return K.contiguous(), V.contiguous()
+
+
+def _epoch_start(w, t):
+    return w.epoch_steps > 0 and t > 1 and (t - 1) % w.epoch_steps == 0 and w.epoch_of(t) > w.epoch_of(t - 1)
+
+
+def run_block_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", fused=True,
+                       readmit=True, kv_every=4):
+    """Run `steps` block-LRFU decode steps of workload `w` on the GPU and the
+    oracle, with re-admission of each new epoch's heavy blocks."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    rtol = rtol if rtol is not None else (1e-5 if w.dtype == "f32" else 2e-3)
+    sample = list(range(w.batch)) if sample_seqs is None else list(sample_seqs)
+    log(f"[block] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:6]} steps={steps} "
+        f"sample={sample} fused={fused}")
+    t_start = time.time()
+    ctx = kvev.context_for(w, max_steps=steps)
+    o = orc.BlockLRFUOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, alpha_new=w.alpha_new,
+                            beta=w.beta, half_lives=tuple(w.region_half_lives),
+                            pinned_regions=tuple(w.pinned_regions), decode_region=w.decode_region,
+                            capacity=max(w.prefill_lens) + steps + 1)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=device)
+        lab = w.region_labels(b)
+        ctx.prefill(b, K.contiguous(), V.contiguous(), lab)
+        ctx.set_budget(b, w.block_budget(b))
+        if b in sample:
+            o.prefill(b, K.float().cpu().numpy(), V.float().cpu().numpy(), lab, w.block_budget(b))
+        del K, V
+    torch.cuda.synchronize()
+    log(f"[block] prefill done in {time.time() - t_start:.1f}s")
+    st = Stats()
+    st.readmitted = 0
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
+    for t in range(1, steps + 1):
+        if readmit and _epoch_start(w, t):
+            e = w.epoch_of(t)
+            for b in range(w.batch):
+                if b in sample:
+                    res = o.seqs[b].resident
+                else:
+                    res = set(np.flatnonzero(ctx.block_state(b)[2]).tolist())
+                tail = (w.prefill_lens[b] + t - 2) // 16
+                ids = [j for j in w.heavy_blocks(b, e) if j not in res and j < tail]
+                if not ids:
+                    continue
+                Kr, Vr = block_rows(w, b, ids, device)
+                ctx.readmit(b, ids, Kr, Vr)
+                st.readmitted += len(ids)
+                if b in sample:
+                    for j in ids:
+                        o.readmit(b, j, t - 1)
+        q, kn, vn = w.step_inputs(t, device=device)
+        if fused:
+            ctx.step(q, kn, vn, out)
+        else:
+            ctx.decode_step(q, kn, vn, out)
+        qs = q[:, sample].float().cpu().numpy()
+        ref_out = o.decode_step(t, qs, kn[:, sample].float().cpu().numpy(),
+                                vn[:, sample].float().cpu().numpy(), sample)
+        gout = out.cpu().numpy()
+        Hg = w.group_size
+        for bi, b in enumerate(sample):
+            for l in range(w.n_layers):
+                for h in range(w.n_kv_heads):
+                    st.max_out_err = max(st.max_out_err, check_out(
+                        gout[l, b, h * Hg:(h + 1) * Hg], ref_out[l, bi, h * Hg:(h + 1) * Hg], rtol,
+                        f"step {t} out l={l} b={b} kvh={h}"))
+        if not fused:
+            for b in sample:
+                gsc, gtr, _ = ctx.block_state(b)
+                _, osc, otr, _ = o.block_state(b)
+                st.max_score_err = max(st.max_score_err, check_scores(gsc, osc, rtol, f"step {t} pre-evict b={b}"))
+            ctx.evict()
+        o.evict(t, seqs=sample)
+        for b in sample:
+            s = o.seqs[b]
+            gsc, gtr, gres = ctx.block_state(b)
+            ids, osc, otr, ores = o.block_state(b)
+            assert len(gsc) == len(ids), f"step {t} b={b}: {len(gsc)} blocks on the GPU, {len(ids)} in the oracle"
+            exempt = False
+            for j in np.flatnonzero(gtr != otr).tolist():
+                # an access decision at the threshold: mass per token within 1e-5 of tau/|K|
+                nb = len(o.block_positions(b, j))
+                thr = 2.0 / s.last_nres
+                r = s.last_mass.get(j, -1.0) / nb
+                assert j in s.last_mass and abs(r - thr) <= 1e-5 * thr, (
+                    f"step {t} b={b} block {j}: clock gpu {gtr[j]} oracle {otr[j]} (mass/token {r:.6e}, "
+                    f"threshold {thr:.6e})")
+                exempt = True
+            if not exempt and not np.array_equal(gres, ores):
+                kept = [j for j in np.flatnonzero(ores) if not o.is_pinned(b, j)]
+                theta = max(o.priority(b, j, t) for j in kept) if kept else 0.0
+                diff = np.flatnonzero(gres != ores).tolist()
+                gaps = [abs(o.priority(b, j, t) - theta) for j in diff]
+                assert max(gaps) < 1e-5, (f"step {t} b={b}: resident blocks differ ({diff}) with oracle "
+                                          f"priority gap {max(gaps):.3e} >= 1e-5")
+                exempt = True
+            if exempt:
+                st.near_tie_resyncs += 1
+                st.notes.append(f"t={t} b={b} near-tie resync")
+                pos = o.resident_positions(b)
+                kk = torch.from_numpy(s.K[:, :, pos].copy()).to(w.torch_dtype).to(device).contiguous()
+                vv = torch.from_numpy(s.V[:, :, pos].copy()).to(w.torch_dtype).to(device).contiguous()
+                ctx.import_blocks(b, osc.astype(np.float32), otr.astype(np.int32), ores, kk, vv)
+                continue
+            st.max_score_err = max(st.max_score_err, check_scores(gsc, osc, rtol, f"step {t} scores b={b}"))
+            if kv_every and (t % kv_every == 0 or t == steps):
+                for h in range(w.n_kv_heads):
+                    gpos = ctx.retained(b, h)
+                    np.testing.assert_array_equal(np.sort(gpos), o.resident_positions(b),
+                                                  err_msg=f"step {t} b={b} kvh={h} retained positions")
+                    gk, gv = ctx.export_kv(b, h)
+                    rk = torch.from_numpy(s.K[:, h, gpos].copy()).to(w.torch_dtype)
+                    rv = torch.from_numpy(s.V[:, h, gpos].copy()).to(w.torch_dtype)
+                    assert torch.equal(gk.cpu(), rk), f"step {t} K differs b={b} kvh={h}"
+                    assert torch.equal(gv.cpu(), rv), f"step {t} V differs b={b} kvh={h}"
+                    st.kv_checks += 1
+        st.steps = t
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[block] step {t}: out_err {st.max_out_err:.2e} score_err {st.max_score_err:.2e} "
+                f"resyncs {st.near_tie_resyncs} readmitted {st.readmitted} ({time.time() - t_start:.1f}s)")
+    ctx.sync()
+    ctx.close()
+    return st

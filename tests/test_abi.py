@@ -77,6 +77,15 @@ def _create(**kw):
     (dict(max_tokens=1), "max_tokens"),
     (dict(batch=0), ">= 1"),
     (dict(policy=9), "policy"),
+    (dict(policy=kvev.LRFU_BLOCK, max_tokens=70000), "65536"),
+    (dict(policy=kvev.LRFU_BLOCK, n_sink=4), "n_sink"),
+    (dict(policy=kvev.LRFU_BLOCK, refresh_interval=4), "refresh_interval"),
+    (dict(policy=kvev.LRFU_BLOCK, beta=-1.0), "beta"),
+    (dict(policy=kvev.LRFU_BLOCK, decode_region=8), "decode_region"),
+    (dict(policy=kvev.LRFU_BLOCK, decode_region=0, pinned_region_mask=1), "pinned"),
+    (dict(policy=kvev.LRFU_BLOCK, pinned_region_mask=0x100), "mask"),
+    (dict(policy=kvev.LRFU_BLOCK, access_tau_mult=0.0), "access_tau_mult"),
+    (dict(policy=kvev.LRFU_BLOCK, budget=5000), "4096"),
 ])
 def test_create_rejects_bad_config(bad, msg):
     st, err, h = _create(**bad)
@@ -98,3 +107,13 @@ def test_config_defaults():
     c = kvev.config_init()
     assert c.page_tokens == 16 and c.refresh_interval == 1 and c.policy == kvev.EMA
     assert abs(c.alpha_new - 0.05) < 1e-7
+    assert abs(c.beta - 0.001) < 1e-9 and c.decode_region == 4 and c.access_tau_mult == 2.0
+    assert c.pinned_region_mask == 0 and list(c.region_half_life) == [0.0] * 8
+
+
+def test_block_entry_points_reject_null_context():
+    L = kvev.lib()
+    assert L.kvev_set_budget(None, 0, 5) == kvev.EINVAL
+    assert L.kvev_readmit(None, 0, 1, None, None, None) == kvev.EINVAL
+    assert L.kvev_block_state(None, 0, None, None, None, 0, None) == kvev.EINVAL
+    assert L.kvev_import_blocks(None, 0, 1, None, None, None, 0, None, None) == kvev.EINVAL
