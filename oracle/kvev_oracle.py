@@ -38,7 +38,7 @@ __all__ = [
     "group_mass", "select_keep", "hole_fill_moves", "apply_moves",
     "tier_capacities", "route_tiers", "int2_quantize", "int2_dequantize",
     "TokenModeOracle", "region_decay_rates", "block_survival", "block_priority",
-    "select_blocks", "BlockLRFUOracle",
+    "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
 ]
 
 
@@ -251,30 +251,33 @@ def route_tiers(scores, candidates, k_f, k_q):
     return F, Q, E
 
 
-def _int2_params(x32):
-    """Asymmetric min-max parameters of one group, stored as fp16.
+def _int2_params(x32, axis):
+    """Asymmetric min-max parameters of each group, stored as fp16.
 
     Reading of [QEvict] §4.4 line 11 (asymmetric, KIVI-style): zero = min,
     scale = (max - min) / 3, both rounded to fp16 (round to nearest even);
-    the subtraction and division are single IEEE fp32 operations.
+    the subtraction and division are single IEEE fp32 operations.  The
+    groups run along ``axis`` of the fp32 array ``x32``.
     """
-    lo = np.float32(x32.min())
-    hi = np.float32(x32.max())
-    span = np.float32(hi - lo)
-    scale = np.float16(np.float32(span / np.float32(3.0)))
-    zero = np.float16(lo)
+    lo = x32.min(axis=axis, keepdims=True).astype(np.float32)
+    hi = x32.max(axis=axis, keepdims=True).astype(np.float32)
+    span = (hi - lo).astype(np.float32)
+    scale = (span / np.float32(3.0)).astype(np.float32).astype(np.float16)
+    zero = lo.astype(np.float16)
     return scale, zero
 
 
 def _int2_codes(x32, scale16, zero16):
-    """Codes ``clamp(rint((x - zero)/scale), 0, 3)`` in IEEE fp32."""
-    s = np.float32(scale16)
-    z = np.float32(zero16)
-    if s == np.float32(0.0):
-        return np.zeros(x32.shape, dtype=np.uint8)
-    t = (x32.astype(np.float32) - z).astype(np.float32)      # fp32 subtract
-    t = (t / s).astype(np.float32)                           # fp32 divide
-    return np.clip(np.rint(t), 0, 3).astype(np.uint8)        # ties to even
+    """Codes ``clamp(rint((x - zero)/scale), 0, 3)`` in IEEE fp32; a group
+    whose scale is 0 (all values equal) takes code 0."""
+    s = np.broadcast_to(scale16.astype(np.float32), x32.shape)
+    z = zero16.astype(np.float32)
+    t = (x32 - z).astype(np.float32)                          # fp32 subtract
+    flat = s == np.float32(0.0)
+    t = (t / np.where(flat, np.float32(1.0), s)).astype(np.float32)  # fp32 divide
+    codes = np.clip(np.rint(t), 0, 3).astype(np.uint8)         # ties to even
+    codes[flat] = 0
+    return codes
 
 
 def int2_quantize(x, axis_groups):
@@ -285,31 +288,22 @@ def int2_quantize(x, axis_groups):
     ``axis_groups="token32"``: one (scale, zero) per token per 32-channel
     group (values, "per-token-value"; the 32-channel grouping is the
     workload's stated group size).
-    Returns (codes uint8 [T, C], scales fp16, zeros fp16).
+    Returns (codes uint8 [T, C], scales fp16, zeros fp16): scales and zeros
+    are [C] in channel mode and [T, C/32] in token32 mode.
     """
     x = np.asarray(x, dtype=np.float32)
     T, C = x.shape
-    codes = np.zeros((T, C), dtype=np.uint8)
     if axis_groups == "channel":
-        scales = np.zeros(C, dtype=np.float16)
-        zeros = np.zeros(C, dtype=np.float16)
-        for c in range(C):
-            s, z = _int2_params(x[:, c])
-            scales[c], zeros[c] = s, z
-            codes[:, c] = _int2_codes(x[:, c], s, z)
-    elif axis_groups == "token32":
+        s, z = _int2_params(x, axis=0)                 # [1, C]
+        codes = _int2_codes(x, s, z)
+        return codes, s[0], z[0]
+    if axis_groups == "token32":
         ng = C // 32
-        scales = np.zeros((T, ng), dtype=np.float16)
-        zeros = np.zeros((T, ng), dtype=np.float16)
-        for t in range(T):
-            for g in range(ng):
-                seg = x[t, 32 * g:32 * (g + 1)]
-                s, z = _int2_params(seg)
-                scales[t, g], zeros[t, g] = s, z
-                codes[t, 32 * g:32 * (g + 1)] = _int2_codes(seg, s, z)
-    else:
-        raise ValueError(axis_groups)
-    return codes, scales, zeros
+        xg = x.reshape(T, ng, 32)
+        s, z = _int2_params(xg, axis=2)                # [T, ng, 1]
+        codes = _int2_codes(xg, s, z).reshape(T, C)
+        return codes, s[..., 0], z[..., 0]
+    raise ValueError(axis_groups)
 
 
 def int2_dequantize(codes, scales, zeros, axis_groups):
@@ -742,3 +736,228 @@ class BlockLRFUOracle:
         tref = np.array([s.tref[j] for j in ids], dtype=np.int64)
         res = np.array([j in s.resident for j in ids], dtype=bool)
         return ids, score, tref, res
+
+
+# ---------------------------------------------------------------------------
+# Two-tier window routing: full precision / INT2 / evicted (QEvict)
+# ---------------------------------------------------------------------------
+
+def bf16_round(x):
+    """fp32 -> nearest bf16 (ties to even), returned as fp32 (torch CPU cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
+
+
+@dataclass
+class _TierLayer:
+    """One layer's windows: FP storage, ledger, tier and cumulative score."""
+    K: np.ndarray            # [Hkv, cap, d] fp32: full-precision values by position
+    V: np.ndarray
+    Keff: np.ndarray         # [Hkv, cap, d] fp32: what attention reads (FP or INT2 reconstruction)
+    Veff: np.ndarray
+    tier: dict = field(default_factory=dict)     # window -> "F" | "Q" | "E"
+    S: dict = field(default_factory=dict)        # window -> cumulative score (fp64)
+    ledger: dict = field(default_factory=dict)   # window -> per-head INT2 codes + params
+
+
+@dataclass
+class TieredOracle:
+    """Per-layer window routing over a full-precision tier, a recoverable
+    INT2 tier and permanent eviction ([QEvict] technical review, §4).
+
+    Windows are the routing unit: window w holds positions
+    [w*W, (w+1)*W).  Readings:
+
+    * Pinned windows hold a sink position (< n_sink); local windows hold
+      one of the n_recent newest positions or are not yet full.  Both stay
+      full precision and are never routed.  Every other window is "aged";
+      a window is routed from the step it ages out of the local region
+      ([QEvict] §4.1 protected sink prefix and recent region; §4.4 Eq.4).
+    * All windows start full precision ([QEvict] §2, Stage 1).
+    * Score ([QEvict] §4.2 Eq.1 with a routing interval of one step): at
+      every step each accessible window gains the attention probability
+      landing on its tokens, summed over the layer's query heads and
+      divided by Hq.  Scores start at 0 at the first decode step; a window
+      opened during decoding starts at 0.  Evicted windows keep their last
+      score and gain nothing.
+    * Routing, per layer after every step ([QEvict] §4.4 Eq.4-5 and
+      Algorithm 1): candidates = aged windows not evicted; F = the K_f best
+      by (score, window index), Q = the next K_q, the rest evicted for good.
+    * A window entering Q is quantized only if it has no ledger entry yet
+      (its first demotion); otherwise the stored codes are reused.  Keys
+      are quantized per channel over the window's tokens, values per token
+      in 32-channel groups ([QEvict] §4.4 lines 9-14; ``int2_quantize``).
+    * A window promoted from Q to F gets its dequantized values rounded to
+      bf16 as its full-precision storage (reading: the synthetic keys carry
+      no rotary embedding, so there is none to re-apply).
+    * Attention reads full-precision windows from storage and INT2 windows
+      through their fp32 reconstruction ``code*scale + zero``
+      ([QEvict] §4.1, the accessible keys and values).
+
+    Layers are independent, so the object may hold any subset of them.
+    """
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    k_f: int
+    k_q: int
+    window: int = 32
+    n_sink: int = 0
+    n_recent: int = 0
+    capacity: int = 0
+    layers: dict = field(default_factory=dict)
+    npos: int = 0
+    last_mass: dict = field(default_factory=dict)
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def prefill(self, K, V, layers=None):
+        """Store the prefill cache: ``K``, ``V`` [len(layers), Hkv, n, d]."""
+        K = np.asarray(K, dtype=np.float32)
+        V = np.asarray(V, dtype=np.float32)
+        nl, H, n, d = K.shape
+        layers = list(range(nl)) if layers is None else list(layers)
+        cap = max(self.capacity, n + 1)
+        for j, l in enumerate(layers):
+            st = _TierLayer(K=np.zeros((H, cap, d), np.float32), V=np.zeros((H, cap, d), np.float32),
+                            Keff=np.zeros((H, cap, d), np.float32), Veff=np.zeros((H, cap, d), np.float32))
+            for arr in (st.K, st.Keff):
+                arr[:, :n] = K[j]
+            for arr in (st.V, st.Veff):
+                arr[:, :n] = V[j]
+            for w in range(self.n_windows(n)):
+                st.tier[w] = "F"
+                st.S[w] = 0.0
+            self.layers[l] = st
+        self.npos = n
+
+    # -- window geometry ----------------------------------------------------
+    def n_windows(self, npos=None):
+        npos = self.npos if npos is None else npos
+        return -(-npos // self.window)
+
+    def is_pinned(self, w):
+        return w * self.window < self.n_sink
+
+    def is_aged(self, w):
+        """Full, older than the n_recent newest positions, and not pinned."""
+        recent_lo = self.npos - self.n_recent
+        return not self.is_pinned(w) and (w + 1) * self.window <= recent_lo
+
+    def window_positions(self, w):
+        return np.arange(w * self.window, min((w + 1) * self.window, self.npos))
+
+    def accessible_positions(self, l):
+        st = self.layers[l]
+        ws = [w for w in range(self.n_windows()) if st.tier[w] != "E"]
+        return np.concatenate([self.window_positions(w) for w in ws]).astype(np.int64), ws
+
+    # -- the step ---------------------------------------------------------
+    def _grow(self, st):
+        if self.npos < st.K.shape[1]:
+            return
+        extra = max(64, st.K.shape[1] // 4)
+        for name in ("K", "V", "Keff", "Veff"):
+            a = getattr(st, name)
+            setattr(st, name, np.concatenate([a, np.zeros((a.shape[0], extra, a.shape[2]), a.dtype)], 1))
+
+    def decode_step(self, t, q, k_new, v_new):
+        """Append, attend over the accessible windows, add window masses.
+
+        ``q``: [len(held layers), Hq, d]; ``k_new``, ``v_new``: [len(held
+        layers), Hkv, d] (held layers in ascending order).  Returns ``out``
+        [len(held layers), Hq, d] in fp64.
+        """
+        q = np.asarray(q, dtype=np.float32)
+        k_new = np.asarray(k_new, dtype=np.float32)
+        v_new = np.asarray(v_new, dtype=np.float32)
+        held = sorted(self.layers)
+        p = self.npos
+        for j, l in enumerate(held):
+            st = self.layers[l]
+            self._grow(st)
+            for arr in (st.K, st.Keff):
+                arr[:, p] = k_new[j]
+            for arr in (st.V, st.Veff):
+                arr[:, p] = v_new[j]
+            w = p // self.window
+            if w not in st.tier:                     # the token opens a window
+                st.tier[w] = "F"
+                st.S[w] = 0.0
+        self.npos = p + 1
+        Hg = self.group_size
+        out = np.zeros((len(held), self.n_q_heads, self.head_dim))
+        self.last_mass = {}
+        for j, l in enumerate(held):
+            st = self.layers[l]
+            pos, ws = self.accessible_positions(l)
+            tok_mass = np.zeros(len(pos))
+            for h in range(self.n_kv_heads):
+                o, pr, _ = decode_attention(q[j, h * Hg:(h + 1) * Hg], st.Keff[h, pos], st.Veff[h, pos])
+                out[j, h * Hg:(h + 1) * Hg] = o
+                tok_mass += pr.sum(axis=0)
+            tok_mass /= self.n_q_heads
+            at = 0
+            masses = {}
+            for w in ws:
+                nb = len(self.window_positions(w))
+                masses[w] = float(tok_mass[at:at + nb].sum())
+                at += nb
+                st.S[w] = cumulative_update(st.S[w], masses[w])
+            self.last_mass[l] = masses
+        return out
+
+    def _quantize_window(self, st, w):
+        sl = slice(w * self.window, (w + 1) * self.window)
+        entry = []
+        for h in range(self.n_kv_heads):
+            kc, ks, kz = int2_quantize(st.K[h, sl], "channel")
+            vc, vs, vz = int2_quantize(st.V[h, sl], "token32")
+            entry.append((kc, ks, kz, vc, vs, vz))
+        st.ledger[w] = entry
+
+    def _reconstruct(self, st, w):
+        sl = slice(w * self.window, (w + 1) * self.window)
+        for h, (kc, ks, kz, vc, vs, vz) in enumerate(st.ledger[w]):
+            st.Keff[h, sl] = int2_dequantize(kc, ks, kz, "channel")
+            st.Veff[h, sl] = int2_dequantize(vc, vs, vz, "token32")
+
+    def route(self):
+        """One routing event in every held layer (after the step's attention)."""
+        for l, st in self.layers.items():
+            cand = [w for w in range(self.n_windows()) if self.is_aged(w) and st.tier[w] != "E"]
+            S = np.zeros(self.n_windows())
+            for w in cand:
+                S[w] = st.S[w]
+            F, Q, E = route_tiers(S, cand, self.k_f, self.k_q)
+            sl = lambda w: slice(w * self.window, (w + 1) * self.window)
+            for w in Q:
+                if w not in st.ledger:                   # first demotion: quantize once
+                    self._quantize_window(st, w)
+                self._reconstruct(st, w)
+                st.tier[w] = "Q"
+            for w in F:
+                if st.tier[w] == "Q":                    # promotion: dequantize into bf16 storage
+                    self._reconstruct(st, w)
+                    st.K[:, sl(w)] = bf16_round(st.Keff[:, sl(w)])
+                    st.V[:, sl(w)] = bf16_round(st.Veff[:, sl(w)])
+                st.Keff[:, sl(w)] = st.K[:, sl(w)]
+                st.Veff[:, sl(w)] = st.V[:, sl(w)]
+                st.tier[w] = "F"
+            for w in E:
+                st.tier[w] = "E"
+
+    # -- views used by tests ------------------------------------------------
+    def window_state(self, l):
+        """(scores [nw] fp64, tiers [nw] uint8: 0 full precision, 1 INT2,
+        2 evicted, ledger [nw] bool) for windows 0 .. n_windows-1."""
+        st = self.layers[l]
+        nw = self.n_windows()
+        code = {"F": 0, "Q": 1, "E": 2}
+        return (np.array([st.S[w] for w in range(nw)], np.float64),
+                np.array([code[st.tier[w]] for w in range(nw)], np.uint8),
+                np.array([w in st.ledger for w in range(nw)], bool))
