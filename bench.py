@@ -10,7 +10,8 @@ between two device synchronisations; inputs are resident in HBM before the
 timed region.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: the path runs on one
-GPU.
+GPU.  ``--workload qevict131k`` times the two-tier window path instead
+(131,072-token prefill, 205 full-precision and 819 INT2 windows per layer).
 """
 from __future__ import annotations
 
@@ -98,6 +99,111 @@ def cpu_baseline(w, steps=300):
                       f"groups at {w.n_layers} layers x {B + 1} tokens, scaled x{w.n_kv_heads * w.batch}"}
 
 
+def tier_bytes(w, n_fp_tokens, n_q):
+    """Bytes of a steady tiered step: the full-precision tokens' K/V (512 B per
+    token and KV head) and the INT2 windows' records (3,072 B: 2-bit codes of
+    32 x 128 keys and values, fp16 scale and zero per key channel and per
+    value token-group) in every layer, plus q, the fp32 output, the appended
+    token and the window scores read and written."""
+    L, Hkv, Hq, d = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    kv = L * Hkv * (n_fp_tokens * 2 * d * 2 + n_q * 3072)
+    extra = L * Hq * d * 2 + L * Hq * d * 4 + L * Hkv * 2 * d * 2 + L * (n_fp_tokens // 32 + n_q) * 4 * 2
+    return kv, kv + extra
+
+
+def tier_cpu_baseline(w, steps=3):
+    """The CPU oracle on one layer of the tiered workload: the first routing
+    event untimed, then `steps` steady steps timed and scaled to all layers."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
+                         k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
+                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 2)
+    K, V = w.prefill_kv(0, layers=[0])
+    o.prefill(K.float().numpy(), V.float().numpy(), layers=[0])
+    del K, V
+    ins = [tuple(x[:1, 0].float().numpy() for x in w.step_inputs(t, seqs=[0])) for t in range(1, steps + 2)]
+    o.decode_step(1, *ins[0])
+    o.route()
+    t0 = time.perf_counter()
+    for t in range(2, steps + 2):
+        o.decode_step(t, *ins[t - 1])
+        o.route()
+    per_layer = (time.perf_counter() - t0) / steps
+    return {"value": 1.0 / (per_layer * w.n_layers), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} steady steps of layer 0 of {w.n_layers} after the first routing event "
+                      f"({w.prefill_lens[0]}-token prefill), scaled x{w.n_layers}"}
+
+
+def run_tier(args, w):
+    import numpy as np
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    total = args.warmup + args.steps
+    ctx = kvev.context_for(w, max_steps=total)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    del K, V
+    inputs = [w.step_inputs(t, device="cuda") for t in range(1, total + 1)]
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for t in range(args.warmup):
+        ctx.step(*inputs[t], out)
+    ctx.sync()
+    ctx.profile(True)
+    ctx.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        ctx.step(*inputs[t], out)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ctx.sync()
+    prof = {k: ctx.profile_read(k) for k in ("append", "attn", "merge", "route")}
+    _, tiers, _ = ctx.tier_state(0)
+    npos = w.prefill_lens[0] + total
+    ctx.close()
+    n_fp_win = int((tiers == 0).sum())
+    n_q = int((tiers == 1).sum())
+    n_fp_tokens = n_fp_win * 32 - (-npos % 32)
+    kv_bytes, step_bytes = tier_bytes(w, n_fp_tokens, n_q)
+    ms_step = dt * 1e3 / args.steps
+    attn_ms, attn_n = prof["attn"]
+    attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
+    attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
+    policy_ms = sum(prof[k][0] for k in ("merge", "route")) / args.steps
+    result = {
+        "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
+        "value": round(args.steps / dt, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded outlier-channel / heavy-key generator, heavy keys re-targeted every 32 steps)",
+        "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "batch": 1, "prefill": w.prefill_lens[0], "window": w.window_tokens,
+                   "fp_windows": w.fp_windows, "int2_windows": w.int2_windows, "n_sink": w.n_sink,
+                   "n_recent": w.n_recent},
+        "listed_windows": {"full_precision": n_fp_win, "int2": n_q},
+        "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
+        "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,
+        "kernel_avg_us": {k: round(v[0] / max(v[1], 1) * 1e3, 3) for k, v in prof.items() if v[1]},
+        "roofline": {
+            "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
+            "traffic": None, "kernel": "tier_attn_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = tier_cpu_baseline(w)
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +233,8 @@ def main():
         return
 
     w = synth.workload(args.workload)
+    if w.policy == "tiered_int2":
+        return run_tier(args, w)
     total = args.warmup + args.steps
     dev = "cuda"
     ctx = kvev.context_for(w, max_steps=total)

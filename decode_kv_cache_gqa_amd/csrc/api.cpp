@@ -8,71 +8,13 @@
 #include <new>
 #include <string>
 
-#include "kvev_internal.h"
+#include "host_util.h"
 
 using namespace kvev;
 
 namespace {
 
 std::string g_create_error;
-
-kvev_status fail(kvev_ctx* c, kvev_status s, const std::string& msg) {
-  if (c) c->err = msg;
-  return s;
-}
-
-kvev_status hip_fail(kvev_ctx* c, hipError_t e, const char* where) {
-  c->sticky = true;
-  c->err = std::string(where) + ": " + hipGetErrorString(e);
-  return KVEV_EHIP;
-}
-
-#define KVEV_HIP(c, expr)                                   \
-  do {                                                      \
-    hipError_t e_ = (expr);                                 \
-    if (e_ != hipSuccess) return hip_fail((c), e_, #expr);  \
-  } while (0)
-
-#define KVEV_LIVE(c)                                                          \
-  do {                                                                        \
-    if (!(c)) return KVEV_EINVAL;                                             \
-    if ((c)->sticky) return KVEV_ESTATE;                                      \
-  } while (0)
-
-template <typename T>
-hipError_t dalloc(T** p, size_t count) {
-  *p = nullptr;
-  if (count == 0) return hipSuccess;
-  return hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T));
-}
-
-// Profiling: events around named launches on the context's stream.
-struct ProfScope {
-  kvev_ctx* c;
-  const char* name;
-  hipEvent_t a = nullptr;
-  ProfScope(kvev_ctx* c_, const char* n) : c(c_), name(n) {
-    if (!c->prof.enabled) return;
-    a = take_event();
-    hipEventRecord(a, c->stream);
-  }
-  hipEvent_t take_event() {
-    if (!c->prof.pool.empty()) {
-      hipEvent_t e = c->prof.pool.back();
-      c->prof.pool.pop_back();
-      return e;
-    }
-    hipEvent_t e;
-    hipEventCreate(&e);
-    return e;
-  }
-  ~ProfScope() {
-    if (!c->prof.enabled) return;
-    hipEvent_t b = take_event();
-    hipEventRecord(b, c->stream);
-    c->prof.pending.push_back({name, a, b});
-  }
-};
 
 void prof_drain(kvev_ctx* c) {
   for (auto& r : c->prof.pending) {
@@ -103,6 +45,7 @@ void free_all(kvev_ctx* c) {
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
+  tier_free(c);
   for (auto& r : c->prof.pending) {
     hipEventDestroy(r.a);
     hipEventDestroy(r.b);
@@ -138,6 +81,37 @@ void release_pages(kvev_ctx* c, int g, int64_t n_slots) {
 
 }  // namespace
 
+// Tiered mode: windows of 32 positions, storage for every window the
+// sequence can reach, chunk partials for two lists of them.
+static kvev_status tier_create(const kvev_config& f, void* hip_stream, kvev_ctx** out) {
+  kvev_ctx* c = new (std::nothrow) kvev_ctx();
+  if (!c) {
+    g_create_error = "out of host memory";
+    return KVEV_EINVAL;
+  }
+  c->cfg = f;
+  c->stream = static_cast<hipStream_t>(hip_stream);
+  hipGetDevice(&c->device);
+  c->G = f.n_kv_heads;
+  c->HG = f.n_q_heads / f.n_kv_heads;
+  c->cap = f.max_tokens;
+  c->elem = 2;
+  c->count.assign(c->G, 0);
+  c->prefilled.assign(1, 0);
+  c->tier_mode = true;
+  c->tw.NW = static_cast<int>((c->cap + kTierWin - 1) / kTierWin);
+  c->tw.maxch = 2 * ((c->tw.NW + 7) / 8);
+  const hipError_t e = tier_alloc(c);
+  if (e != hipSuccess) {
+    g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
+    free_all(c);
+    delete c;
+    return e == hipErrorOutOfMemory ? KVEV_ENOMEM : KVEV_EHIP;
+  }
+  *out = c;
+  return KVEV_OK;
+}
+
 extern "C" {
 
 void kvev_config_init(kvev_config* cfg) {
@@ -151,6 +125,7 @@ void kvev_config_init(kvev_config* cfg) {
   cfg->beta = 0.001f;
   cfg->decode_region = 4;
   cfg->access_tau_mult = 2.0f;
+  cfg->window_tokens = kTierWin;
 }
 
 kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out) {
@@ -171,8 +146,23 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
   if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
-  if (f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE && f.policy != KVEV_LRFU_BLOCK)
+  if (f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE && f.policy != KVEV_LRFU_BLOCK &&
+      f.policy != KVEV_TIERED_INT2)
     return bad("unsupported policy");
+  const bool tiered = f.policy == KVEV_TIERED_INT2;
+  if (tiered) {
+    if (f.dtype != KVEV_BF16 || f.head_dim != kTierD) return bad("tiered mode: bf16 and head_dim 128 only");
+    if (f.batch != 1) return bad("tiered mode: batch must be 1");
+    if (f.window_tokens != kTierWin) return bad("tiered mode: window_tokens must be 32");
+    if (f.fp_windows < 0 || f.int2_windows < 0) return bad("tiered mode: tier capacities must be >= 0");
+    if (f.max_tokens > static_cast<int64_t>(kTierMaxWin) * kTierWin)
+      return bad("tiered mode: max_tokens must be <= 196608");
+    if (f.refresh_interval != 1 || f.score_free != 0)
+      return bad("tiered mode: refresh_interval must be 1 and score_free 0");
+    if (f.n_sink < 0 || f.n_recent < 0) return bad("n_sink and n_recent must be >= 0");
+    if (f.n_layers > 64) return bad("n_layers must be <= 64");
+    if (f.max_tokens < 2) return bad("max_tokens out of range");
+  }
   if ((f.policy == KVEV_EMA || f.policy == KVEV_LRFU_BLOCK) && !(f.alpha_new > 0.f && f.alpha_new <= 1.f))
     return bad("alpha_new must be in (0, 1]");
   const bool block = f.policy == KVEV_LRFU_BLOCK;
@@ -191,6 +181,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     if (f.n_kv_heads > 64 || f.n_layers * f.n_kv_heads > 1024)
       return bad("block mode: at most 64 KV heads and 1024 (layer, KV head) pairs");
   }
+  if (tiered) return tier_create(f, hip_stream, out);
   if (f.refresh_interval < 1) return bad("refresh_interval must be >= 1");
   if (f.n_sink < 0 || f.n_recent < 0) return bad("n_sink and n_recent must be >= 0");
   if (f.budget < 1) return bad("budget must be >= 1");
@@ -424,6 +415,7 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
   if (c->t > 0) return fail(c, KVEV_ESTATE, "prefill after the first decode step");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
   if (c->block_mode) return block_prefill(c, seq, k, v, n, labels);
+  if (c->tier_mode) return tier_prefill(c, seq, k, v, n);
   const int Hkv = c->cfg.n_kv_heads;
   std::vector<int> upd;
   for (int h = 0; h < Hkv; ++h) {
@@ -603,6 +595,7 @@ kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, cons
                              float* out) {
   KVEV_LIVE(c);
   if (c->block_mode) return block_step(c, q, k_new, v_new, out, false, 0);
+  if (c->tier_mode) return tier_decode(c, q, k_new, v_new, out);
   return run_step(c, q, k_new, v_new, out, false, c->cfg.budget);
 }
 
@@ -610,6 +603,10 @@ kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void*
                       int64_t budget) {
   KVEV_LIVE(c);
   if (c->block_mode) return block_step(c, q, k_new, v_new, out, true, budget);
+  if (c->tier_mode) {
+    if (kvev_status s = tier_decode(c, q, k_new, v_new, out)) return s;
+    return tier_route(c);
+  }
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   return run_step(c, q, k_new, v_new, out, true, B);
@@ -618,6 +615,7 @@ kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void*
 kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   KVEV_LIVE(c);
   if (c->block_mode) return block_evict(c, budget);
+  if (c->tier_mode) return tier_route(c);
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   int64_t max_moves = 0;
@@ -744,6 +742,10 @@ kvev_status kvev_import_blocks(kvev_ctx* c, int32_t seq, int64_t n_blocks, const
 kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t cap,
                         int64_t* n_written) {
   KVEV_LIVE(c);
+  if (c->tier_mode) {
+    if (seq != 0) return fail(c, KVEV_ERANGE, "tiered mode: the only sequence is 0");
+    return tier_scores(c, h, dst, cap, n_written);
+  }
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return kvev_block_state(c, seq, dst, nullptr, nullptr, cap, n_written);
@@ -759,6 +761,7 @@ kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t
 kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* positions, int64_t cap,
                           int64_t* n_out) {
   KVEV_LIVE(c);
+  if (c->tier_mode) return fail(c, KVEV_EINVAL, "tiered mode: use the kvev_tier_* calls");
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   const int64_t n = c->count[g];
@@ -773,6 +776,7 @@ kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* position
 kvev_status kvev_export_kv(kvev_ctx* c, int32_t seq, int32_t h, void* k_out, void* v_out,
                            int64_t cap, int64_t* n_out) {
   KVEV_LIVE(c);
+  if (c->tier_mode) return fail(c, KVEV_EINVAL, "tiered mode: use the kvev_tier_* calls");
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   const int64_t n = c->count[g];
@@ -786,6 +790,7 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
                               const int32_t* positions, const float* scores, const void* k,
                               const void* v) {
   KVEV_LIVE(c);
+  if (c->tier_mode) return fail(c, KVEV_EINVAL, "tiered mode: use the kvev_tier_* calls");
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return fail(c, KVEV_EINVAL, "block mode: use kvev_import_blocks");
@@ -820,6 +825,7 @@ kvev_status kvev_sync(kvev_ctx* c) {
     c->err = "device consistency check failed (flag " + std::to_string(flag) + ")";
     return KVEV_ESTATE;
   }
+  if (c->tier_mode) return KVEV_OK;
   // the host's slot counts size every launch: they must match the device's
   std::vector<int> dc(c->G);
   KVEV_HIP(c, hipMemcpy(dc.data(), c->d.count, sizeof(int) * c->G, hipMemcpyDeviceToHost));

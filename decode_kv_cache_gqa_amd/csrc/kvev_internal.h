@@ -16,6 +16,12 @@ constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies its
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
 constexpr int kRegions = 8;       // region labels of the block-granular mode
 constexpr int kMaxBlockEntries = 4096;  // block-table entries per sequence (block mode)
+// two-tier window mode
+constexpr int kTierWin = 32;            // tokens per routing window
+constexpr int kTierD = 128;             // head dim of the tiered mode
+constexpr int kTierLedgerBytes = 3072;  // INT2 record per (layer, KV head, window)
+constexpr int kTierMaxWin = 6144;       // windows per sequence (196608 positions)
+constexpr int kTierXferBlocks = 64;     // blocks per (layer, KV head) of the transition kernel
 
 // Device buffers of one context.  Groups are (sequence, KV head) pairs,
 // g = seq * Hkv + kv_head; slots of a group are its cached tokens in order.
@@ -52,6 +58,53 @@ struct DevState {
   float* bmass = nullptr;   // [batch][maxpages] step mass per table entry (unnormalised)
   int* bbudget = nullptr;   // [batch] retained blocks per sequence
   int* rd_ids = nullptr;    // [maxpages] block ids of one re-admission call
+};
+
+// Device buffers of the two-tier window mode ([L][Hkv][NW] windows).
+struct TierDev {
+  uint16_t* kfp = nullptr;   // [L][Hkv][NW][32][128] bf16 keys, token-major
+  uint16_t* vfp = nullptr;   // [L][Hkv][NW][128][32] bf16 values, channel-major
+  uint8_t* ledger = nullptr; // [L][Hkv][NW][3072] INT2 codes and parameters
+  uint8_t* tier = nullptr;   // [L][NW] 0 full precision, 1 INT2, 2 evicted
+  uint8_t* hasled = nullptr; // [L][NW] 1 once the window has been quantized
+  uint8_t* forced = nullptr; // [L][NW] tiers imported by kvev_tier_import
+  float* S = nullptr;        // [L][NW] cumulative window score
+  int* fplist = nullptr;     // [L][NW] full-precision windows (pinned, local, routed)
+  int* qlist = nullptr;      // [L][NW] INT2 windows
+  int* jobs = nullptr;       // [L][NW] transition jobs: window << 2 | kind (1 quantize, 2 promote)
+  int* njobs = nullptr;      // [L]
+  float* emass = nullptr;    // [L][Hkv][NW][4] per listed window and head: sum exp(s - chunk max)
+};
+
+// Host mirror of the tiered mode (the list lengths are equal in every
+// layer: every layer routes the same number of candidates).
+struct TierHost {
+  int NW = 0, maxch = 0;
+  int64_t npos = 0;  // positions 0 .. npos-1 exist
+  int n_fp = 0;      // full-precision windows listed (pinned + local + routed F)
+  int n_q = 0;       // INT2 windows listed
+  int n_kept = 0;    // routed windows in F or Q after the last routing event
+  int na_prev = 0;   // aged windows at the last routing event
+};
+
+// Kernel arguments of the tiered mode.
+struct TierArgs {
+  uint16_t* kfp;
+  uint16_t* vfp;
+  uint8_t* ledger;
+  uint8_t* tier;
+  uint8_t* hasled;
+  float* S;
+  int* fplist;
+  int* qlist;
+  int* jobs;
+  int* njobs;
+  float* part_ml;  // [L][Hkv][maxch][4][2]
+  float* part_o;   // [L][Hkv][maxch][4][128]
+  float* ml;       // [L][Hkv][4][2]
+  float* emass;
+  int* errflag;
+  int L, Hkv, Hq, NW, maxch;
 };
 
 struct Profiler {
@@ -96,6 +149,10 @@ struct kvev_ctx {
   std::vector<int64_t> npos;                // next position per sequence
   std::vector<int> bbudget;                 // per-sequence block budget
   std::vector<int> npinned;                 // blocks pinned by region labels per sequence
+  // two-tier window mode
+  bool tier_mode = false;
+  kvev::TierDev td;
+  kvev::TierHost tw;
 };
 
 namespace kvev {
@@ -120,5 +177,20 @@ hipError_t launch_block_mass(kvev_ctx* c, int n_max);
 hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
                                int budget_override);
 hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, int t);
+// two-tier window mode (tier.hip)
+hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n);
+hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new);
+hipError_t launch_tier_attention(kvev_ctx* c, const void* q);
+hipError_t launch_tier_merge(kvev_ctx* c, float* out);
+hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp_fp, int exp_q,
+                             const uint8_t* forced_dev);
+hipError_t launch_tier_export(kvev_ctx* c, int l, int h, void* k_out, void* v_out, int nwin);
+// host side of the tiered mode (tier_api.cpp)
+hipError_t tier_alloc(kvev_ctx* c);
+void tier_free(kvev_ctx* c);
+kvev_status tier_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
+kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out);
+kvev_status tier_route(kvev_ctx* c);
+kvev_status tier_scores(kvev_ctx* c, int layer, float* dst, int64_t cap, int64_t* n);
 
 }  // namespace kvev

@@ -1,0 +1,890 @@
+// Two-tier window mode: per-layer routing of 32-token windows between a
+// full-precision tier, a recoverable INT2 tier and permanent eviction.
+//
+// Source: the technical review of "QEvict: Recoverable Quantized KV Eviction
+// for Attention-Drift-Robust Long-Context Decoding", section 4: the
+// accessible keys and values are the full-precision windows plus the
+// reconstructions of the INT2 windows (section 4.1, (Attention)); each
+// window's score accumulates its attention mass averaged over the layer's
+// query heads (section 4.2, Eq.1); at each routing event the candidates are
+// ranked, the best K_f stay in full precision, the next K_q go to the INT2
+// tier and the rest are evicted for good (section 4.4, Eq.4-6); a window is
+// quantized once, at its first demotion, keys per channel and values per
+// token, and its codes are reused by every later demotion and promotion
+// (section 4.4, Algorithm 1).  The routing interval here is one step.
+//
+// Layout, per (layer l, KV head h) and window w (positions [32w, 32w+32)):
+//   kfp    [L][Hkv][NW][32][128] bf16  keys, token-major
+//   vfp    [L][Hkv][NW][128][32] bf16  values, channel-major (a channel's 32
+//          tokens are 64 contiguous bytes: the p.V operand of the matrix cores)
+//   ledger [L][Hkv][NW][3072 B]   INT2 record:
+//     [0, 1024)     key codes, 16 B per lane of a wave (see below)
+//     [1024, 2048)  value codes, 16 B per lane
+//     [2048, 2304)  key scale per channel, fp16 [128]
+//     [2304, 2560)  key zero point per channel, fp16 [128]
+//     [2560, 2816)  value scale per (token, 32-channel group), fp16 [32][4]
+//     [2816, 3072)  value zero point, fp16 [32][4]
+// Full-precision storage is never released: a demoted window keeps it, so a
+// promotion only rewrites it and nothing moves when tiers change.
+//
+// Code records.  A 2-bit code c = b0 + 2 b1 is stored as two bit planes.  In
+// the matrix-core products a plane is a B operand of 8 bf16 values in {0,1}
+// (made from the bits with one AND and one 24-bit multiply per pair), and
+// the A operand of the second plane is doubled, so the product sums
+// code * operand exactly.  Lane (r16, q4) = lane r16 + 16 q4 of a wave owns
+// four 32-bit words: plane 0 / plane 1, two words each; bit pi (low half)
+// and bit 16 + pi (high half) of a word are the two codes of pair pi.
+//   keys:   word (plane b, n-tile j) pair pi = 4s + p holds tokens 16j + r16,
+//           channels 32s + 8q4 + 2p (+1 in the high half), s = k-step 0..3
+//   values: word (plane b, half) pair pi = 4(ct % 4) + p, ct = 4 half + ..,
+//           holds channel 16ct + r16, tokens 8q4 + 2p (+1 in the high half)
+#include "kvev_internal.h"
+
+namespace kvev {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int D = kTierD;  // head dim
+constexpr int HG = 4;      // query heads per KV head
+constexpr int W = kTierWin;
+constexpr int kRecK = 0, kRecV = 1024, kRecSK = 2048, kRecZK = 2304, kRecSV = 2560, kRecZV = 2816;
+
+__device__ __forceinline__ bf16x8_t as_b8(const uint4& r) {
+  bf16x8_t v;
+  __builtin_memcpy(&v, &r, sizeof(v));
+  return v;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  const uint16_t b = static_cast<uint16_t>(bits);
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+__device__ __forceinline__ uint16_t f2h(float f) {
+  const _Float16 h = static_cast<_Float16>(f);  // round to nearest even
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+// Pair pi (0..15) of a bit-plane word as two bf16 values in {0, 1}.
+template <int PI>
+__device__ __forceinline__ uint32_t plane_pair(uint32_t w) {
+  constexpr int sh = PI & 7;
+  const uint32_t x = PI < 8 ? w : (w >> 8);
+  return __umul24(x & (0x00010001u << sh), 0x3F80u >> sh);
+}
+
+// B operand (4 pairs) of pairs 4p0 .. 4p0+3 of one plane word.
+template <int P0>
+__device__ __forceinline__ bf16x8_t plane_operand(uint32_t w) {
+  return as_b8(make_uint4(plane_pair<4 * P0 + 0>(w), plane_pair<4 * P0 + 1>(w),
+                          plane_pair<4 * P0 + 2>(w), plane_pair<4 * P0 + 3>(w)));
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& r, int i) {
+  return i == 0 ? r.x : (i == 1 ? r.y : (i == 2 ? r.z : r.w));
+}
+
+// A operand of 8 fp32 values split into bf16 high parts (rows 0..3) and
+// low parts (rows 4..7); rows 8..15 are zero.  `scale2` doubles the values
+// (exactly) for the second bit plane.
+__device__ __forceinline__ void split_rows(const float* x, int r16, bf16x8_t& a1, bf16x8_t& a2) {
+  uint32_t p1[8], p2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t hi = bf16_rne(x[e]);
+    const uint32_t lo = bf16_rne(x[e] - __uint_as_float(hi << 16));
+    const uint32_t v = r16 < 4 ? hi : (r16 < 8 ? lo : 0u);
+    p1[e] = v;
+    // doubling a bf16 adds one to its exponent (zero stays zero)
+    p2[e] = (v & 0x7fffu) ? v + 0x80u : v;
+  }
+  a1 = as_b8(make_uint4(p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p1[4] | (p1[5] << 16),
+                        p1[6] | (p1[7] << 16)));
+  a2 = as_b8(make_uint4(p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16), p2[4] | (p2[5] << 16),
+                        p2[6] | (p2[7] << 16)));
+}
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Prefill: windows [0, nwin) of every (layer, KV head) from k, v
+// [L][Hkv][n][128]; tokens past n are zero.  Block (w, h, l), 256 threads.
+// Also resets the window state of layer l (h == 0).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v, int n) {
+  __shared__ uint16_t vt[W][D + 2];
+  const int w = blockIdx.x, h = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  const int64_t src0 = lh * n;
+  uint16_t* kd = A.kfp + (lh * A.NW + w) * W * D;
+  uint16_t* vd = A.vfp + (lh * A.NW + w) * W * D;
+  for (int i = tid; i < W * D; i += 256) {
+    const int r = i / D, c = i % D;
+    const int p = w * W + r;
+    const bool in = p < n;
+    kd[i] = in ? k[(src0 + p) * D + c] : 0;
+    vt[r][c] = in ? v[(src0 + p) * D + c] : 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < W * D; i += 256) {
+    const int c = i / W, r = i % W;
+    vd[i] = vt[r][c];
+  }
+  if (h == 0 && tid == 0) {
+    const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
+    A.fplist[lw] = w;
+    A.tier[lw] = 0;
+    A.hasled[lw] = 0;
+    A.S[lw] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: the new token (position npos) into its window's storage.  When it
+// opens a window, that window starts full precision with score 0 and joins
+// the full-precision list at index n_fp.  Block (h, l), 128 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint16_t* __restrict__ k_new,
+                                                          const uint16_t* __restrict__ v_new, int npos,
+                                                          int n_fp) {
+  const int h = blockIdx.x, l = blockIdx.y, c = threadIdx.x;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  const int w = npos / W, r = npos % W;
+  A.kfp[((lh * A.NW + w) * W + r) * D + c] = k_new[lh * D + c];
+  A.vfp[(lh * A.NW + w) * W * D + c * W + r] = v_new[lh * D + c];
+  if (r == 0 && h == 0 && c == 0) {
+    const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
+    A.fplist[static_cast<int64_t>(l) * A.NW + n_fp] = w;
+    A.tier[lw] = 0;
+    A.hasled[lw] = 0;
+    A.S[lw] = 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention over the accessible windows of (layer l, KV head h).  Block
+// (chunk, h, l) of 4 waves; a wave takes 2 consecutive windows of a list
+// (64 tokens), a chunk 8.  Chunks [0, nch_f) cover the full-precision list,
+// the rest the INT2 list.  Writes the chunk's (max, sum) and unnormalised
+// output per head, and per window and head the sum of exp(s - chunk max)
+// over the window's tokens (its attention mass before normalisation).
+//   q.K: A = the 4 query rows, B = K^T (n-tiles of 16 tokens, k-steps of 32
+//     channels).  INT2: logit = sum_c (q_c s_c) code_c + sum_c q_c z_c, with
+//     q s split into bf16 high (rows 0..3) and low (rows 4..7) parts.
+//   p.V: A = P (high / low rows), B = V (a k-step is one window).  INT2:
+//     out_c = sum_t (p_t s_tg) code_tc + sum_t p_t z_tg, g = c / 32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16_t* __restrict__ q,
+                                                        int n_fp, int n_q, int nch_f, int npos,
+                                                        float scale) {
+  __shared__ __align__(16) float p_lds[4][HG][64];
+  __shared__ __align__(16) float o_lds[4][HG][D];
+  __shared__ float wstat[4][HG][2];
+  __shared__ float e_lds[4][2][HG];
+
+  const int chunk = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const bool isq = chunk >= nch_f;
+  const int base = (isq ? chunk - nch_f : chunk) * 8;
+  const int nlist = isq ? n_q : n_fp;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  const int* list = (isq ? A.qlist : A.fplist) + static_cast<int64_t>(l) * A.NW;
+  int win[2];
+  bool live[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = base + 2 * wave + k;
+    live[k] = idx < nlist;
+    win[k] = live[k] ? list[idx] : 0;
+  }
+
+  // the lane's query row (head r16 & 3) on channels 32s + 8q4 .. +8
+  uint4 qraw[4];
+  {
+    const uint16_t* qp = q + (static_cast<int64_t>(l) * A.Hq + h * HG + (r16 & 3)) * D + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qp + 32 * s);
+  }
+
+  float sv[4][HG];      // logits of n-tile jj = 2k + j (lanes q4 == 0 hold them)
+  f32x4_t oacc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float bz[4] = {0.f, 0.f, 0.f, 0.f};  // INT2: sum_t p_t z_tg per group (lanes r16 < 4)
+
+  if (!isq) {
+    // ---- full-precision windows -------------------------------------------
+    bf16x8_t qa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = as_b8(r16 < HG ? qraw[s] : make_uint4(0, 0, 0, 0));
+    uint4 kr[4][4], vr[2][8];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int k = jj >> 1;
+      const uint16_t* kb = A.kfp + ((lh * A.NW + win[k]) * W + 16 * (jj & 1) + r16) * D + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kr[jj][s] = live[k] ? *reinterpret_cast<const uint4*>(kb + 32 * s) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint16_t* vb = A.vfp + (lh * A.NW + win[k]) * W * D + r16 * W + 8 * q4;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+        vr[k][ct] = live[k] ? *reinterpret_cast<const uint4*>(vb + 16 * ct * W) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma(qa[s], as_b8(kr[jj][s]), acc);
+      const int k = jj >> 1;
+      const int p = win[k] * W + 16 * (jj & 1) + r16;
+      const bool valid = q4 == 0 && live[k] && p < npos;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) sv[jj][hh] = valid ? acc[hh] * scale : -INFINITY;
+    }
+    // softmax statistics of the wave, probabilities to LDS
+    float mh[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      float m = fmaxf(fmaxf(sv[0][hh], sv[1][hh]), fmaxf(sv[2][hh], sv[3][hh]));
+      mh[hh] = row16_max(m);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pv = mh[hh] == -INFINITY ? 0.f : __expf(sv[jj][hh] - mh[hh]);
+        sv[jj][hh] = pv;
+        if (jj < 2) e0 += pv; else e1 += pv;
+      }
+      e0 = row16_sum(e0);
+      e1 = row16_sum(e1);
+      if (lane == 0) {
+        e_lds[wave][0][hh] = e0;
+        e_lds[wave][1][hh] = e1;
+        wstat[wave][hh][0] = mh[hh];
+        wstat[wave][hh][1] = e0 + e1;
+      }
+    }
+    if (q4 == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) p_lds[wave][hh][16 * jj + r16] = sv[jj][hh];
+    }
+    __syncthreads();
+    // p.V: one k-step per window, P in high / low rows
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float4 a = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
+      const float4 b = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
+      const float pv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      bf16x8_t pa, pa2;
+      split_rows(pv, r16, pa, pa2);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) oacc[ct] = mfma(pa, as_b8(vr[k][ct]), oacc[ct]);
+    }
+  } else {
+    // ---- INT2 windows -------------------------------------------------------
+    float qf[4][8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float t[8];
+      Vec16<bf16_t>::widen(qraw[s], t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = t[e];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
+      uint4 kc = make_uint4(0, 0, 0, 0);
+      float bias = 0.f;
+      bf16x8_t a1[4], a2[4];
+      if (live[k]) {
+        kc = *reinterpret_cast<const uint4*>(rec + kRecK + 16 * lane);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSK + 2 * (32 * s + 8 * q4));
+          const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZK + 2 * (32 * s + 8 * q4));
+          const uint32_t sw[4] = {sr.x, sr.y, sr.z, sr.w}, zw[4] = {zr.x, zr.y, zr.z, zr.w};
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sc = h2f(sw[e >> 1] >> (16 * (e & 1)));
+            const float zp = h2f(zw[e >> 1] >> (16 * (e & 1)));
+            x[e] = qf[s][e] * sc;
+            bias = fmaf(qf[s][e], zp, bias);
+          }
+          split_rows(x, r16, a1[s], a2[s]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a1[s] = a2[s] = as_b8(make_uint4(0, 0, 0, 0));
+      }
+      // full sum_c q_c z_c of head r16 & 3 (lanes r16 = 0..3 of every q4)
+      bias += __shfl_xor(bias, 16, kWave);
+      bias += __shfl_xor(bias, 32, kWave);
+      float bb[HG];
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) bb[hh] = __shfl(bias, hh, kWave);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4_t acc = q4 == 0 ? f32x4_t{bb[0], bb[1], bb[2], bb[3]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint32_t w0 = word_of(kc, j), w1 = word_of(kc, 2 + j);
+        acc = mfma(a1[0], plane_operand<0>(w0), acc);
+        acc = mfma(a2[0], plane_operand<0>(w1), acc);
+        acc = mfma(a1[1], plane_operand<1>(w0), acc);
+        acc = mfma(a2[1], plane_operand<1>(w1), acc);
+        acc = mfma(a1[2], plane_operand<2>(w0), acc);
+        acc = mfma(a2[2], plane_operand<2>(w1), acc);
+        acc = mfma(a1[3], plane_operand<3>(w0), acc);
+        acc = mfma(a2[3], plane_operand<3>(w1), acc);
+        const bool valid = q4 == 0 && live[k];
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+          const float lg = acc[hh] + __shfl_xor(acc[hh], 16, kWave);
+          sv[2 * k + j][hh] = valid ? lg * scale : -INFINITY;
+        }
+      }
+    }
+    float mh[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      float m = fmaxf(fmaxf(sv[0][hh], sv[1][hh]), fmaxf(sv[2][hh], sv[3][hh]));
+      mh[hh] = row16_max(m);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      float e0 = 0.f, e1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pv = mh[hh] == -INFINITY ? 0.f : __expf(sv[jj][hh] - mh[hh]);
+        sv[jj][hh] = pv;
+        if (jj < 2) e0 += pv; else e1 += pv;
+      }
+      e0 = row16_sum(e0);
+      e1 = row16_sum(e1);
+      if (lane == 0) {
+        e_lds[wave][0][hh] = e0;
+        e_lds[wave][1][hh] = e1;
+        wstat[wave][hh][0] = mh[hh];
+        wstat[wave][hh][1] = e0 + e1;
+      }
+    }
+    if (q4 == 0) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) p_lds[wave][hh][16 * jj + r16] = sv[jj][hh];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (!live[k]) continue;  // wave-uniform
+      const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
+      const uint4 vc = *reinterpret_cast<const uint4*>(rec + kRecV + 16 * lane);
+      const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
+      const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
+      const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
+      // scale and zero point of tokens 8q4 .. +8, groups 0..3 ([token][group] fp16)
+      uint32_t sw[16], zw[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * q4 + 8 * u));
+        const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * q4 + 8 * u));
+        sw[4 * u] = sr.x; sw[4 * u + 1] = sr.y; sw[4 * u + 2] = sr.z; sw[4 * u + 3] = sr.w;
+        zw[4 * u] = zr.x; zw[4 * u + 1] = zr.y; zw[4 * u + 2] = zr.z; zw[4 * u + 3] = zr.w;
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 4 * e + g;  // fp16 index of (token 8q4 + e, group g)
+          const float sc = h2f(sw[idx >> 1] >> (16 * (idx & 1)));
+          const float zp = h2f(zw[idx >> 1] >> (16 * (idx & 1)));
+          x[e] = pv[e] * sc;
+          bz[g] = fmaf(pv[e], zp, bz[g]);
+        }
+        bf16x8_t pa, pa2;
+        split_rows(x, r16, pa, pa2);
+        const uint32_t w0 = word_of(vc, g >> 1), w1 = word_of(vc, 2 + (g >> 1));
+        // tiles ct = 2g, 2g + 1 sit at pairs 4 (ct % 4) .. of word ct / 4
+        if ((g & 1) == 0) {
+          oacc[2 * g] = mfma(pa, plane_operand<0>(w0), oacc[2 * g]);
+          oacc[2 * g] = mfma(pa2, plane_operand<0>(w1), oacc[2 * g]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<1>(w0), oacc[2 * g + 1]);
+          oacc[2 * g + 1] = mfma(pa2, plane_operand<1>(w1), oacc[2 * g + 1]);
+        } else {
+          oacc[2 * g] = mfma(pa, plane_operand<2>(w0), oacc[2 * g]);
+          oacc[2 * g] = mfma(pa2, plane_operand<2>(w1), oacc[2 * g]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<3>(w0), oacc[2 * g + 1]);
+          oacc[2 * g + 1] = mfma(pa2, plane_operand<3>(w1), oacc[2 * g + 1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bz[g] += __shfl_xor(bz[g], 16, kWave);
+      bz[g] += __shfl_xor(bz[g], 32, kWave);
+    }
+  }
+
+  // the wave's output: high rows (q4 == 0) + low rows (q4 == 1) + zero-point terms
+  float bzh[HG][4];
+#pragma unroll
+  for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bzh[hh][g] = isq ? __shfl(bz[g], hh, kWave) : 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float o = oacc[ct][hh] + __shfl_xor(oacc[ct][hh], 16, kWave) + bzh[hh][ct >> 1];
+      if (q4 == 0) o_lds[wave][hh][16 * ct + r16] = o;
+    }
+  }
+  __syncthreads();
+
+  // merge the block's waves into one partial
+  const int nch = gridDim.x;
+  const int64_t pb = lh * A.maxch + chunk;
+  for (int idx = tid; idx < HG * D; idx += 256) {
+    const int hh = idx / D, c = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wstat[w][hh][0]);
+    float o = 0.f, Z = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = wstat[w][hh][0] == -INFINITY ? 0.f : __expf(wstat[w][hh][0] - M);
+      o += f * o_lds[w][hh][c];
+      Z += f * wstat[w][hh][1];
+    }
+    A.part_o[pb * HG * D + idx] = o;
+    if (c == 0) {
+      A.part_ml[(pb * HG + hh) * 2 + 0] = M;
+      A.part_ml[(pb * HG + hh) * 2 + 1] = Z;
+    }
+  }
+  if (tid < 8 * HG) {
+    const int slot = tid / HG, hh = tid % HG;  // slot = 2 * wave + k
+    const int wv = slot >> 1, k = slot & 1;
+    const int idx = base + slot;
+    if (idx < nlist) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, wstat[w][hh][0]);
+      const float f = wstat[wv][hh][0] == -INFINITY ? 0.f : __expf(wstat[wv][hh][0] - M);
+      const int cidx = (isq ? n_fp : 0) + idx;
+      A.emass[(lh * A.NW + cidx) * HG + hh] = e_lds[wv][k][hh] * f;
+    }
+  }
+  (void)nch;
+}
+
+// ---------------------------------------------------------------------------
+// Merge the chunks of (layer l, KV head h): out and the global (max, sum).
+// Block (h, l), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_merge_kernel(TierArgs A, float* __restrict__ out, int nch) {
+  const int h = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  for (int idx = tid; idx < HG * D; idx += 256) {
+    const int hh = idx / D, c = idx % D;
+    float M = -INFINITY;
+    for (int s = 0; s < nch; ++s) M = fmaxf(M, A.part_ml[((lh * A.maxch + s) * HG + hh) * 2]);
+    float o = 0.f, Z = 0.f;
+    for (int s = 0; s < nch; ++s) {
+      const int64_t pb = lh * A.maxch + s;
+      const float m = A.part_ml[(pb * HG + hh) * 2];
+      const float f = m == -INFINITY ? 0.f : __expf(m - M);
+      Z += f * A.part_ml[(pb * HG + hh) * 2 + 1];
+      o += f * A.part_o[pb * HG * D + idx];
+    }
+    out[(static_cast<int64_t>(l) * A.Hq + h * HG + hh) * D + c] = o / Z;
+    if (c == 0) {
+      A.ml[(lh * HG + hh) * 2] = M;
+      A.ml[(lh * HG + hh) * 2 + 1] = Z;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Window mass of every accessible window of layer l, added to its score:
+// (1/Hq) sum over KV heads and their query heads of the window's
+// probability mass.  Block (x, l), 256 threads, one window per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, int n_q, int nch_f) {
+  const int l = blockIdx.y;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n_fp + n_q) return;
+  const bool isq = idx >= n_fp;
+  const int chunk = isq ? nch_f + (idx - n_fp) / 8 : idx / 8;
+  const int w = isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
+                    : A.fplist[static_cast<int64_t>(l) * A.NW + idx];
+  float acc = 0.f;
+  for (int h = 0; h < A.Hkv; ++h) {
+    const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float mb = A.part_ml[((lh * A.maxch + chunk) * HG + hh) * 2];
+      const float M = A.ml[(lh * HG + hh) * 2], Z = A.ml[(lh * HG + hh) * 2 + 1];
+      const float f = mb == -INFINITY ? 0.f : __expf(mb - M) / Z;
+      acc += A.emass[(lh * A.NW + idx) * HG + hh] * f;
+    }
+  }
+  A.S[static_cast<int64_t>(l) * A.NW + w] += acc / static_cast<float>(A.Hq);
+}
+
+// ---------------------------------------------------------------------------
+// Routing event of layer l (one block of 1024 threads per layer).
+// Candidates are the aged windows (w >= np, 32(w+1) <= recent_lo) not yet
+// evicted; each is ranked by (score, window) descending; rank < k_f stays /
+// becomes full precision, rank < k_f + k_q INT2, the rest evicted.  With
+// `forced` the tiers of every window are taken from it instead (state
+// import).  Emits the quantize (first demotion) and promote jobs, then
+// rebuilds the full-precision and INT2 lists in window order.  The counts
+// must equal the host's (exp_fp, exp_q); otherwise errflag bit 32.
+// ---------------------------------------------------------------------------
+constexpr int kRouteNT = 1024;
+
+__global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw, int np, int recent_lo,
+                                                              int k_f, int k_q, int exp_fp, int exp_q,
+                                                              const uint8_t* __restrict__ forced) {
+  __shared__ unsigned long long keys[kTierMaxWin];
+  __shared__ uint8_t tl[kTierMaxWin];
+  __shared__ uint8_t hl[kTierMaxWin];
+  __shared__ int ncand, njobs, wsum[2][kRouteNT / kWave], base[2];
+  const int l = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int64_t lw0 = static_cast<int64_t>(l) * A.NW;
+  if (tid == 0) {
+    ncand = 0;
+    njobs = 0;
+  }
+  for (int w = tid; w < nw; w += kRouteNT) {
+    tl[w] = A.tier[lw0 + w];
+    hl[w] = A.hasled[lw0 + w];
+  }
+  __syncthreads();
+  auto aged = [&](int w) { return w >= np && (w + 1) * W <= recent_lo; };
+  if (!forced) {
+    for (int w = tid; w < nw; w += kRouteNT) {
+      if (aged(w) && tl[w] != 2) {
+        const int i = atomicAdd(&ncand, 1);
+        keys[i] = (static_cast<unsigned long long>(float_key(A.S[lw0 + w])) << 32) | static_cast<unsigned>(w);
+      }
+    }
+    __syncthreads();
+    const int nc = ncand;
+    // exact rank of each candidate; keys are distinct (window ids)
+    for (int i = tid; i < nc; i += kRouteNT) {
+      const unsigned long long ki = keys[i];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += keys[j] > ki;
+      const int w = static_cast<int>(ki & 0xffffffffu);
+      const uint8_t nt = rank < k_f ? 0 : (rank < k_f + k_q ? 1 : 2);
+      const uint8_t ot = tl[w];
+      if (nt == 1 && !hl[w]) {
+        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 1;
+        hl[w] = 1;
+      } else if (nt == 0 && ot == 1) {
+        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 2;
+      }
+      tl[w] = nt;
+    }
+  } else {
+    for (int w = tid; w < nw; w += kRouteNT) {
+      const uint8_t nt = forced[lw0 + w];
+      const uint8_t ot = tl[w];
+      if (nt == 1 && !hl[w]) {
+        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 1;
+        hl[w] = 1;
+      } else if (nt == 0 && ot == 1) {
+        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 2;
+      }
+      tl[w] = nt;
+    }
+  }
+  __syncthreads();
+  // stable compaction of the two lists (ballot + prefix sum per 1024 windows)
+  if (tid == 0) {
+    base[0] = 0;
+    base[1] = 0;
+  }
+  __syncthreads();
+  for (int w0 = 0; w0 < nw; w0 += kRouteNT) {
+    const int w = w0 + tid;
+    const bool isF = w < nw && tl[w] == 0;
+    const bool isQ = w < nw && tl[w] == 1;
+    const unsigned long long bF = __ballot(isF), bQ = __ballot(isQ);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    if (lane == 0) {
+      wsum[0][wv] = __popcll(bF);
+      wsum[1][wv] = __popcll(bQ);
+    }
+    __syncthreads();
+    int offF = base[0] + __popcll(bF & below), offQ = base[1] + __popcll(bQ & below);
+    for (int u = 0; u < wv; ++u) {
+      offF += wsum[0][u];
+      offQ += wsum[1][u];
+    }
+    if (isF) A.fplist[lw0 + offF] = w;
+    if (isQ) A.qlist[lw0 + offQ] = w;
+    __syncthreads();
+    if (tid == 0) {
+      for (int u = 0; u < kRouteNT / kWave; ++u) {
+        base[0] += wsum[0][u];
+        base[1] += wsum[1][u];
+      }
+    }
+    __syncthreads();
+  }
+  for (int w = tid; w < nw; w += kRouteNT) {
+    A.tier[lw0 + w] = tl[w];
+    A.hasled[lw0 + w] = hl[w];
+  }
+  if (tid == 0) {
+    A.njobs[l] = njobs;
+    if (base[0] != exp_fp || base[1] != exp_q) atomicOr(A.errflag, 32);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tier transitions of layer l: quantize a window's full-precision values
+// into its ledger record (first demotion) or write its reconstruction,
+// rounded to bf16, into its full-precision storage (promotion).  Block
+// (x, h, l), 256 threads, jobs x, x + gridDim.x, ...
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void int2_group(const float* x, int n, int stride, float& sc, float& zp,
+                                           uint16_t& s16, uint16_t& z16) {
+  float lo = x[0], hi = x[0];
+  for (int i = 1; i < n; ++i) {
+    lo = fminf(lo, x[i * stride]);
+    hi = fmaxf(hi, x[i * stride]);
+  }
+  const float span = __fsub_rn(hi, lo);
+  s16 = f2h(__fdiv_rn(span, 3.0f));
+  z16 = f2h(lo);
+  sc = h2f(s16);
+  zp = h2f(z16);
+}
+
+__device__ __forceinline__ uint8_t int2_code(float x, float sc, float zp) {
+  if (sc == 0.f) return 0;
+  const float t = __fdiv_rn(__fsub_rn(x, zp), sc);
+  const float r = __builtin_rintf(t);  // ties to even
+  return static_cast<uint8_t>(fminf(fmaxf(r, 0.f), 3.f));
+}
+
+__global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
+  __shared__ float xk[W][D + 1];
+  __shared__ float xv[W][D + 1];
+  __shared__ uint8_t ck[W][D];
+  __shared__ uint8_t cv[W][D];
+  const int h = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  const int nj = A.njobs[l];
+  for (int j = blockIdx.x; j < nj; j += gridDim.x) {
+    const int job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
+    const int w = job >> 2, kind = job & 3;
+    uint16_t* kd = A.kfp + (lh * A.NW + w) * W * D;
+    uint16_t* vd = A.vfp + (lh * A.NW + w) * W * D;
+    uint8_t* rec = A.ledger + (lh * A.NW + w) * static_cast<int64_t>(kTierLedgerBytes);
+    uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
+    uint32_t* rec32 = reinterpret_cast<uint32_t*>(rec);
+    if (kind == 1) {
+      for (int i = tid; i < W * D; i += 256) {
+        xk[i / D][i % D] = __uint_as_float(static_cast<uint32_t>(kd[i]) << 16);
+        xv[i % W][i / W] = __uint_as_float(static_cast<uint32_t>(vd[i]) << 16);
+      }
+      __syncthreads();
+      if (tid < D) {  // keys: one channel over the window's tokens
+        const int c = tid;
+        float sc, zp;
+        uint16_t s16, z16;
+        int2_group(&xk[0][c], W, D + 1, sc, zp, s16, z16);
+        rec16[kRecSK / 2 + c] = s16;
+        rec16[kRecZK / 2 + c] = z16;
+        for (int r = 0; r < W; ++r) ck[r][c] = int2_code(xk[r][c], sc, zp);
+      } else {  // values: one token's 32-channel group
+        const int r = (tid - D) / 4, g = (tid - D) % 4;
+        float sc, zp;
+        uint16_t s16, z16;
+        int2_group(&xv[r][32 * g], 32, 1, sc, zp, s16, z16);
+        rec16[kRecSV / 2 + 4 * r + g] = s16;
+        rec16[kRecZV / 2 + 4 * r + g] = z16;
+        for (int c = 32 * g; c < 32 * g + 32; ++c) cv[r][c] = int2_code(xv[r][c], sc, zp);
+      }
+      __syncthreads();
+      {
+        // thread = (lane, word): lane = tid / 4, word = tid % 4 (plane word / 2, part word % 2)
+        const int ln = tid >> 2, wd = tid & 3, r16 = ln & 15, q4 = ln >> 4;
+        const int plane = wd >> 1, part = wd & 1;
+        uint32_t kw = 0, vw = 0;
+#pragma unroll
+        for (int pi = 0; pi < 16; ++pi)
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int p = pi & 3, e = 2 * p + hi;
+            // keys: n-tile part, k-step pi / 4
+            const int tk = 16 * part + r16, ckk = 32 * (pi >> 2) + 8 * q4 + e;
+            kw |= static_cast<uint32_t>((ck[tk][ckk] >> plane) & 1) << (pi + 16 * hi);
+            // values: tile 4 part + pi / 4
+            const int ct = 4 * part + (pi >> 2);
+            const int cvc = 16 * ct + r16, tv = 8 * q4 + e;
+            vw |= static_cast<uint32_t>((cv[tv][cvc] >> plane) & 1) << (pi + 16 * hi);
+          }
+        rec32[(kRecK / 4) + 4 * ln + 2 * plane + part] = kw;
+        rec32[(kRecV / 4) + 4 * ln + 2 * plane + part] = vw;
+      }
+      __syncthreads();
+    } else if (kind == 2) {
+      for (int i = tid; i < W * D; i += 256) {
+        {  // key element (token r, channel c)
+          const int r = i / D, c = i % D;
+          const int r16 = r & 15, part = r >> 4, s = c >> 5, q4 = (c & 31) >> 3, e = c & 7;
+          const int ln = q4 * 16 + r16, pi = 4 * s + (e >> 1), bit = pi + 16 * (e & 1);
+          const uint32_t w0 = rec32[kRecK / 4 + 4 * ln + part], w1 = rec32[kRecK / 4 + 4 * ln + 2 + part];
+          const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+          const float sc = h2f(rec16[kRecSK / 2 + c]), zp = h2f(rec16[kRecZK / 2 + c]);
+          const float x = __fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp);
+          kd[i] = static_cast<uint16_t>(bf16_rne(x));
+        }
+        {  // value element (channel c, token r): channel-major index i
+          const int c = i / W, r = i % W;
+          const int r16 = c & 15, ct = c >> 4, q4 = r >> 3, e = r & 7;
+          const int ln = q4 * 16 + r16, part = ct >> 2, pi = 4 * (ct & 3) + (e >> 1), bit = pi + 16 * (e & 1);
+          const uint32_t w0 = rec32[kRecV / 4 + 4 * ln + part], w1 = rec32[kRecV / 4 + 4 * ln + 2 + part];
+          const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+          const int g = c >> 5;
+          const float sc = h2f(rec16[kRecSV / 2 + 4 * r + g]), zp = h2f(rec16[kRecZV / 2 + 4 * r + g]);
+          const float x = __fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp);
+          vd[i] = static_cast<uint16_t>(bf16_rne(x));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Export of the full-precision storage of (layer l, KV head h), windows
+// [0, nwin), token-major: k_out, v_out [nwin * 32][128].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_export_kernel(TierArgs A, int l, int h, uint16_t* __restrict__ k_out,
+                                                          uint16_t* __restrict__ v_out) {
+  const int w = blockIdx.x, tid = threadIdx.x;
+  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  const uint16_t* ks = A.kfp + (lh * A.NW + w) * W * D;
+  const uint16_t* vs = A.vfp + (lh * A.NW + w) * W * D;
+  for (int i = tid; i < W * D; i += 256) {
+    const int r = i / D, c = i % D;
+    k_out[static_cast<int64_t>(w) * W * D + i] = ks[i];
+    v_out[static_cast<int64_t>(w) * W * D + i] = vs[c * W + r];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static TierArgs tier_args(kvev_ctx* c) {
+  TierArgs a;
+  a.kfp = c->td.kfp;
+  a.vfp = c->td.vfp;
+  a.ledger = c->td.ledger;
+  a.tier = c->td.tier;
+  a.hasled = c->td.hasled;
+  a.S = c->td.S;
+  a.fplist = c->td.fplist;
+  a.qlist = c->td.qlist;
+  a.jobs = c->td.jobs;
+  a.njobs = c->td.njobs;
+  a.part_ml = c->d.part_ml;
+  a.part_o = c->d.part_o;
+  a.ml = c->d.ml;
+  a.emass = c->td.emass;
+  a.errflag = c->d.errflag;
+  a.L = c->cfg.n_layers;
+  a.Hkv = c->cfg.n_kv_heads;
+  a.Hq = c->cfg.n_q_heads;
+  a.NW = c->tw.NW;
+  a.maxch = c->tw.maxch;
+  return a;
+}
+
+hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n) {
+  const int nwin = static_cast<int>((n + W - 1) / W);
+  dim3 grid(nwin, c->cfg.n_kv_heads, c->cfg.n_layers);
+  tier_prefill_kernel<<<grid, 256, 0, c->stream>>>(tier_args(c), static_cast<const uint16_t*>(k),
+                                                   static_cast<const uint16_t*>(v), static_cast<int>(n));
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new) {
+  dim3 grid(c->cfg.n_kv_heads, c->cfg.n_layers);
+  tier_append_kernel<<<grid, D, 0, c->stream>>>(tier_args(c), static_cast<const uint16_t*>(k_new),
+                                                static_cast<const uint16_t*>(v_new),
+                                                static_cast<int>(c->tw.npos), c->tw.n_fp);
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
+  const int nch_f = (c->tw.n_fp + 7) / 8, nch_q = (c->tw.n_q + 7) / 8;
+  const int npos = static_cast<int>(c->tw.npos);
+  TierArgs a = tier_args(c);
+  dim3 grid(nch_f + nch_q, c->cfg.n_kv_heads, c->cfg.n_layers);
+  tier_attn_kernel<<<grid, 256, 0, c->stream>>>(a, static_cast<const uint16_t*>(q), c->tw.n_fp, c->tw.n_q,
+                                                nch_f, npos, 1.0f / sqrtf(static_cast<float>(D)));
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
+  const int nch_f = (c->tw.n_fp + 7) / 8, nch_q = (c->tw.n_q + 7) / 8;
+  TierArgs a = tier_args(c);
+  hipError_t e;
+  dim3 gm(c->cfg.n_kv_heads, c->cfg.n_layers);
+  tier_merge_kernel<<<gm, 256, 0, c->stream>>>(a, out, nch_f + nch_q);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntot = c->tw.n_fp + c->tw.n_q;
+  dim3 gs((ntot + 255) / 256, c->cfg.n_layers);
+  tier_mass_kernel<<<gs, 256, 0, c->stream>>>(a, c->tw.n_fp, c->tw.n_q, nch_f);
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp_fp, int exp_q,
+                             const uint8_t* forced_dev) {
+  TierArgs a = tier_args(c);
+  tier_route_kernel<<<c->cfg.n_layers, kRouteNT, 0, c->stream>>>(
+      a, nw, np, recent_lo, c->cfg.fp_windows, c->cfg.int2_windows, exp_fp, exp_q, forced_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 gx(kTierXferBlocks, c->cfg.n_kv_heads, c->cfg.n_layers);
+  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tier_export(kvev_ctx* c, int l, int h, void* k_out, void* v_out, int nwin) {
+  tier_export_kernel<<<nwin, 256, 0, c->stream>>>(tier_args(c), l, h, static_cast<uint16_t*>(k_out),
+                                                  static_cast<uint16_t*>(v_out));
+  return hipGetLastError();
+}
+
+}  // namespace kvev

@@ -1,0 +1,270 @@
+// Host side of the two-tier window mode: allocation, step sequencing, the
+// per-layer tier counts, and the copy-out / import calls.
+//
+// The counts of the routing state machine are a function of positions
+// alone, so the host knows every launch shape without reading the device:
+// windows [0, np) hold sink positions (pinned), windows [np, na + np) are
+// aged (full and older than the n_recent newest positions) and the rest are
+// local.  Aged windows not evicted are the candidates of a routing event:
+// those kept by the previous event plus the windows aged since.  Of them
+// min(K_f, n) stay full precision and min(K_q, n - that) go to INT2
+// ("QEvict" review, section 4.4, Eq.4-5).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "host_util.h"
+
+namespace kvev {
+
+namespace {
+
+struct Counts {
+  int nw, np, recent_lo, na;
+};
+
+Counts tier_counts(const kvev_ctx* c) {
+  Counts k;
+  const int64_t npos = c->tw.npos;
+  k.nw = static_cast<int>((npos + kTierWin - 1) / kTierWin);
+  k.np = c->cfg.n_sink > 0 ? std::min(k.nw, (c->cfg.n_sink + kTierWin - 1) / kTierWin) : 0;
+  const int64_t rl = npos - c->cfg.n_recent;
+  k.recent_lo = static_cast<int>(std::max<int64_t>(rl, -1));
+  const int64_t full = rl >= 0 ? rl / kTierWin : 0;
+  k.na = static_cast<int>(std::max<int64_t>(0, full - k.np));
+  return k;
+}
+
+}  // namespace
+
+void tier_free(kvev_ctx* c) {
+  auto& t = c->td;
+  void* ptrs[] = {t.kfp, t.vfp, t.ledger, t.tier, t.hasled, t.forced, t.S,
+                  t.fplist, t.qlist, t.jobs, t.njobs, t.emass};
+  for (void* p : ptrs)
+    if (p) hipFree(p);
+  t = TierDev{};
+}
+
+hipError_t tier_alloc(kvev_ctx* c) {
+  const auto& f = c->cfg;
+  auto& t = c->td;
+  auto& d = c->d;
+  const int64_t L = f.n_layers, H = f.n_kv_heads, NW = c->tw.NW;
+  const size_t win = static_cast<size_t>(L) * H * NW;
+  const size_t lw = static_cast<size_t>(L) * NW;
+  hipError_t e = hipSuccess;
+  auto A = [&](hipError_t r) {
+    if (e == hipSuccess && r != hipSuccess) e = r;
+  };
+  A(dalloc(&t.kfp, win * kTierWin * kTierD));
+  A(dalloc(&t.vfp, win * kTierWin * kTierD));
+  A(dalloc(&t.ledger, win * kTierLedgerBytes));
+  A(dalloc(&t.tier, lw));
+  A(dalloc(&t.hasled, lw));
+  A(dalloc(&t.forced, lw));
+  A(dalloc(&t.S, lw));
+  A(dalloc(&t.fplist, lw));
+  A(dalloc(&t.qlist, lw));
+  A(dalloc(&t.jobs, lw));
+  A(dalloc(&t.njobs, L));
+  A(dalloc(&t.emass, win * 4));
+  const size_t parts = static_cast<size_t>(L) * H * c->tw.maxch * 4;
+  A(dalloc(&d.part_ml, parts * 2));
+  A(dalloc(&d.part_o, parts * kTierD));
+  A(dalloc(&d.ml, static_cast<size_t>(L) * H * 4 * 2));
+  A(dalloc(&d.errflag, 1));
+  if (e != hipSuccess) return e;
+  // zero the storage so that unwritten rows are finite
+  A(hipMemsetAsync(t.kfp, 0, win * kTierWin * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.vfp, 0, win * kTierWin * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.ledger, 0, win * kTierLedgerBytes, c->stream));
+  A(hipMemsetAsync(t.tier, 0, lw, c->stream));
+  A(hipMemsetAsync(t.hasled, 0, lw, c->stream));
+  A(hipMemsetAsync(t.S, 0, lw * sizeof(float), c->stream));
+  A(hipMemsetAsync(t.njobs, 0, L * sizeof(int), c->stream));
+  // list entries past the live lengths stay valid window ids (0)
+  A(hipMemsetAsync(t.fplist, 0, lw * sizeof(int), c->stream));
+  A(hipMemsetAsync(t.qlist, 0, lw * sizeof(int), c->stream));
+  A(hipMemsetAsync(t.jobs, 0, lw * sizeof(int), c->stream));
+  A(hipMemsetAsync(d.errflag, 0, sizeof(int), c->stream));
+  A(hipStreamSynchronize(c->stream));
+  return e;
+}
+
+kvev_status tier_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
+  if (seq != 0) return fail(c, KVEV_EINVAL, "tiered mode: the only sequence is 0");
+  if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
+  KVEV_HIP(c, launch_tier_prefill(c, k, v, n));
+  auto& tw = c->tw;
+  tw.npos = n;
+  tw.n_fp = static_cast<int>((n + kTierWin - 1) / kTierWin);
+  tw.n_q = 0;
+  tw.n_kept = 0;
+  tw.na_prev = 0;
+  c->prefilled[0] = 1;
+  return KVEV_OK;
+}
+
+kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out) {
+  if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
+  if (!c->prefilled[0]) return fail(c, KVEV_ESTATE, "the sequence has no prefill");
+  auto& tw = c->tw;
+  if (tw.npos + 1 > c->cap) return fail(c, KVEV_ESTATE, "position capacity exhausted");
+  const bool opens = tw.npos % kTierWin == 0;
+  {
+    ProfScope p(c, "append");
+    KVEV_HIP(c, launch_tier_append(c, k_new, v_new));
+  }
+  if (opens) tw.n_fp += 1;
+  tw.npos += 1;
+  {
+    ProfScope p(c, "attn");
+    KVEV_HIP(c, launch_tier_attention(c, q));
+  }
+  {
+    ProfScope p(c, "merge");
+    KVEV_HIP(c, launch_tier_merge(c, out));
+  }
+  c->t += 1;
+  return KVEV_OK;
+}
+
+kvev_status tier_route(kvev_ctx* c) {
+  if (!c->prefilled[0]) return fail(c, KVEV_ESTATE, "the sequence has no prefill");
+  auto& tw = c->tw;
+  const Counts k = tier_counts(c);
+  const int cand = tw.n_kept + (k.na - tw.na_prev);
+  const int nF = std::min(c->cfg.fp_windows, cand);
+  const int nQ = std::min(c->cfg.int2_windows, cand - nF);
+  const int exp_fp = k.np + (k.nw - k.np - k.na) + nF;
+  {
+    ProfScope p(c, "route");
+    KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, exp_fp, nQ, nullptr));
+  }
+  tw.n_fp = exp_fp;
+  tw.n_q = nQ;
+  tw.n_kept = nF + nQ;
+  tw.na_prev = k.na;
+  return KVEV_OK;
+}
+
+kvev_status tier_scores(kvev_ctx* c, int layer, float* dst, int64_t cap, int64_t* n) {
+  return kvev_tier_state(c, layer, dst, nullptr, nullptr, cap, n);
+}
+
+}  // namespace kvev
+
+using namespace kvev;
+
+extern "C" {
+
+kvev_status kvev_tier_state(kvev_ctx* c, int32_t layer, float* score, uint8_t* tier, uint8_t* ledger,
+                            int64_t cap, int64_t* n_windows) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, KVEV_EINVAL, "layer out of range");
+  const int64_t nw = (c->tw.npos + kTierWin - 1) / kTierWin;
+  if (n_windows) *n_windows = nw;
+  if (cap < nw) return fail(c, KVEV_ERANGE, "destination too small");
+  const int64_t off = static_cast<int64_t>(layer) * c->tw.NW;
+  if (score)
+    KVEV_HIP(c, hipMemcpyAsync(score, c->td.S + off, sizeof(float) * nw, hipMemcpyDeviceToHost, c->stream));
+  if (tier) KVEV_HIP(c, hipMemcpyAsync(tier, c->td.tier + off, nw, hipMemcpyDeviceToHost, c->stream));
+  if (ledger)
+    KVEV_HIP(c, hipMemcpyAsync(ledger, c->td.hasled + off, nw, hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  return KVEV_OK;
+}
+
+kvev_status kvev_tier_export(kvev_ctx* c, int32_t layer, int32_t h, void* k_out, void* v_out,
+                             int64_t cap, int64_t* n_rows) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  if (layer < 0 || layer >= c->cfg.n_layers || h < 0 || h >= c->cfg.n_kv_heads)
+    return fail(c, KVEV_EINVAL, "layer or KV head out of range");
+  const int nw = static_cast<int>((c->tw.npos + kTierWin - 1) / kTierWin);
+  const int64_t rows = static_cast<int64_t>(nw) * kTierWin;
+  if (n_rows) *n_rows = rows;
+  if (!k_out || !v_out || cap < rows) return fail(c, KVEV_ERANGE, "destination too small");
+  if (nw > 0) KVEV_HIP(c, launch_tier_export(c, layer, h, k_out, v_out, nw));
+  return KVEV_OK;
+}
+
+kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, uint8_t* k_codes,
+                             uint16_t* k_scale, uint16_t* k_zero, uint8_t* v_codes, uint16_t* v_scale,
+                             uint16_t* v_zero) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  const int nw = static_cast<int>((c->tw.npos + kTierWin - 1) / kTierWin);
+  if (layer < 0 || layer >= c->cfg.n_layers || h < 0 || h >= c->cfg.n_kv_heads || w < 0 || w >= nw)
+    return fail(c, KVEV_EINVAL, "layer, KV head or window out of range");
+  if (!k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero)
+    return fail(c, KVEV_EINVAL, "null argument");
+  uint8_t flag = 0;
+  const int64_t lw = static_cast<int64_t>(layer) * c->tw.NW + w;
+  std::vector<uint8_t> rec(kTierLedgerBytes);
+  const int64_t roff = ((static_cast<int64_t>(layer) * c->cfg.n_kv_heads + h) * c->tw.NW + w) * kTierLedgerBytes;
+  KVEV_HIP(c, hipMemcpyAsync(&flag, c->td.hasled + lw, 1, hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(rec.data(), c->td.ledger + roff, kTierLedgerBytes, hipMemcpyDeviceToHost,
+                             c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  if (!flag) return fail(c, KVEV_EINVAL, "window has never been quantized");
+  uint32_t words[2][256];
+  std::memcpy(words[0], rec.data(), 1024);
+  std::memcpy(words[1], rec.data() + 1024, 1024);
+  // lane (r16, q4) owns words 4*lane + 2*plane + part (layout in tier.hip)
+  for (int r = 0; r < kTierWin; ++r)
+    for (int ch = 0; ch < kTierD; ++ch) {
+      {  // key (token r, channel ch)
+        const int r16 = r & 15, part = r >> 4, s = ch >> 5, q4 = (ch & 31) >> 3, e = ch & 7;
+        const int ln = q4 * 16 + r16, bit = 4 * s + (e >> 1) + 16 * (e & 1);
+        const uint32_t b0 = (words[0][4 * ln + part] >> bit) & 1u, b1 = (words[0][4 * ln + 2 + part] >> bit) & 1u;
+        k_codes[r * kTierD + ch] = static_cast<uint8_t>(b0 | (b1 << 1));
+      }
+      {  // value (token r, channel ch)
+        const int r16 = ch & 15, ct = ch >> 4, q4 = r >> 3, e = r & 7;
+        const int ln = q4 * 16 + r16, part = ct >> 2, bit = 4 * (ct & 3) + (e >> 1) + 16 * (e & 1);
+        const uint32_t b0 = (words[1][4 * ln + part] >> bit) & 1u, b1 = (words[1][4 * ln + 2 + part] >> bit) & 1u;
+        v_codes[r * kTierD + ch] = static_cast<uint8_t>(b0 | (b1 << 1));
+      }
+    }
+  std::memcpy(k_scale, rec.data() + 2048, 256);
+  std::memcpy(k_zero, rec.data() + 2304, 256);
+  std::memcpy(v_scale, rec.data() + 2560, 256);
+  std::memcpy(v_zero, rec.data() + 2816, 256);
+  return KVEV_OK;
+}
+
+kvev_status kvev_tier_import(kvev_ctx* c, int32_t layer, int64_t n_windows, const float* score,
+                             const uint8_t* tier) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, KVEV_EINVAL, "layer out of range");
+  if (!score || !tier) return fail(c, KVEV_EINVAL, "null argument");
+  if (!c->prefilled[0]) return fail(c, KVEV_ESTATE, "the sequence has no prefill");
+  const Counts k = tier_counts(c);
+  if (n_windows != k.nw) return fail(c, KVEV_EINVAL, "n_windows must equal the windows seen");
+  int nf = 0, nq = 0;
+  for (int w = 0; w < k.nw; ++w) {
+    if (tier[w] > 2) return fail(c, KVEV_EINVAL, "tier code out of range");
+    nf += tier[w] == 0;
+    nq += tier[w] == 1;
+    const bool aged = w >= k.np && (w + 1) * kTierWin <= k.recent_lo;
+    if (!aged && tier[w] != 0) return fail(c, KVEV_EINVAL, "pinned and local windows must be full precision");
+  }
+  if (nf != c->tw.n_fp || nq != c->tw.n_q)
+    return fail(c, KVEV_EINVAL, "tier counts differ from the context's");
+  const int64_t off = static_cast<int64_t>(layer) * c->tw.NW;
+  const size_t lw = static_cast<size_t>(c->cfg.n_layers) * c->tw.NW;
+  KVEV_HIP(c, hipMemcpyAsync(c->td.forced, c->td.tier, lw, hipMemcpyDeviceToDevice, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(c->td.forced + off, tier, k.nw, hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(c->td.S + off, score, sizeof(float) * k.nw, hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, c->tw.n_fp, c->tw.n_q, c->td.forced));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));  // host buffers are the caller's
+  return KVEV_OK;
+}
+
+}  // extern "C"

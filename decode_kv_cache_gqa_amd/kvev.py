@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkvev.so")
 
 OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
-EMA, CUMULATIVE, LRFU_BLOCK = 0, 1, 2
+EMA, CUMULATIVE, LRFU_BLOCK, TIERED_INT2 = 0, 1, 2, 3
 MAX_REGIONS = 8
 _STATUS = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EHIP: "EHIP", ESTATE: "ESTATE", ERANGE: "ERANGE"}
 
@@ -41,6 +41,8 @@ class Config(ctypes.Structure):
         ("beta", ctypes.c_float), ("region_half_life", ctypes.c_float * 8),
         ("pinned_region_mask", ctypes.c_uint32), ("decode_region", ctypes.c_int32),
         ("access_tau_mult", ctypes.c_float),
+        ("window_tokens", ctypes.c_int32), ("fp_windows", ctypes.c_int32),
+        ("int2_windows", ctypes.c_int32),
     ]
 
 
@@ -71,6 +73,14 @@ _SIGS = {
     "kvev_import_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_void_p]),
+    "kvev_tier_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_tier_export": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_tier_ledger": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+                         + [ctypes.c_void_p] * 6),
+    "kvev_tier_import": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
     "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
@@ -274,6 +284,53 @@ class Context:
             res.ctypes.data_as(ctypes.c_void_p), n_tok, _ptr(k, self.dtype, shape, "k"),
             _ptr(v, self.dtype, shape, "v")))
 
+    # -- two-tier window mode -----------------------------------------------------
+    def tier_state(self, layer):
+        """(score float32, tier uint8 (0 FP, 1 INT2, 2 evicted), ledger bool) by window."""
+        cap = (self.cfg.max_tokens + 31) // 32
+        sc = np.zeros(cap, np.float32)
+        tr = np.zeros(cap, np.uint8)
+        lg = np.zeros(cap, np.uint8)
+        n = ctypes.c_int64()
+        self._check(lib().kvev_tier_state(self._h, layer, sc.ctypes.data_as(ctypes.c_void_p),
+                                          tr.ctypes.data_as(ctypes.c_void_p),
+                                          lg.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)))
+        m = n.value
+        return sc[:m].copy(), tr[:m].copy(), lg[:m].astype(bool)
+
+    def tier_export(self, layer, kv_head):
+        """Full-precision storage of (layer, KV head) by position: k, v [32 * windows, d]."""
+        import torch
+        c = self.cfg
+        cap = ((c.max_tokens + 31) // 32) * 32
+        k = torch.empty((cap, c.head_dim), dtype=self.dtype, device="cuda")
+        v = torch.empty_like(k)
+        n = ctypes.c_int64()
+        self._check(lib().kvev_tier_export(self._h, layer, kv_head, _ptr(k), _ptr(v), cap, ctypes.byref(n)))
+        self.sync()
+        return k[: n.value].clone(), v[: n.value].clone()
+
+    def tier_ledger(self, layer, kv_head, window):
+        """INT2 record: (k_codes [32,128], k_scale [128], k_zero [128], v_codes [32,128],
+        v_scale [32,4], v_zero [32,4]); parameters as float16."""
+        kc = np.zeros((32, self.cfg.head_dim), np.uint8)
+        vc = np.zeros_like(kc)
+        ks = np.zeros(128, np.uint16)
+        kz = np.zeros(128, np.uint16)
+        vs = np.zeros((32, 4), np.uint16)
+        vz = np.zeros((32, 4), np.uint16)
+        args = [a.ctypes.data_as(ctypes.c_void_p) for a in (kc, ks, kz, vc, vs, vz)]
+        self._check(lib().kvev_tier_ledger(self._h, layer, kv_head, window, *args))
+        return kc, ks.view(np.float16), kz.view(np.float16), vc, vs.view(np.float16), vz.view(np.float16)
+
+    def tier_import(self, layer, score, tier):
+        score = np.ascontiguousarray(score, dtype=np.float32)
+        tier = np.ascontiguousarray(tier, dtype=np.uint8)
+        if score.shape != tier.shape:
+            raise ValueError("score and tier differ in length")
+        self._check(lib().kvev_tier_import(self._h, layer, score.shape[0], score.ctypes.data_as(ctypes.c_void_p),
+                                           tier.ctypes.data_as(ctypes.c_void_p)))
+
     def sync(self):
         self._check(lib().kvev_sync(self._h))
 
@@ -304,6 +361,14 @@ def context_for(w, max_steps=None, budget=None, stream=None):
             access_tau_mult=2.0)
         for r, hl in enumerate(w.region_half_lives):
             cfg.region_half_life[r] = hl
+        return Context(cfg, stream=stream)
+    if w.policy == "tiered_int2":
+        cfg = make_config(
+            n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+            head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,
+            max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=TIERED_INT2,
+            n_sink=w.n_sink, n_recent=w.n_recent, budget=1, window_tokens=w.window_tokens,
+            fp_windows=w.fp_windows, int2_windows=w.int2_windows)
         return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

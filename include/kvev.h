@@ -61,7 +61,34 @@ typedef enum { KVEV_F32 = 0, KVEV_BF16 = 1 } kvev_dtype;
  *              Eq.3-4 and section IV-B Eq.7 for lambda = ln2 / half-life).
  *              Lower priority is kept.  Selection groups are sequences and
  *              budgets count blocks.                                          */
-typedef enum { KVEV_EMA = 0, KVEV_CUMULATIVE = 1, KVEV_LRFU_BLOCK = 2 } kvev_policy;
+/*  TIERED_INT2: routing of 32-token windows per layer between a
+ *              full-precision tier, a recoverable INT2 tier and permanent
+ *              eviction (technical review of "QEvict", section 4).  Every
+ *              accessible window's score is the running sum over steps of
+ *              the attention probability landing on its tokens, summed over
+ *              the layer's query heads and divided by n_q_heads (section
+ *              4.2, Eq.1, routing interval one step).  After each step, per
+ *              layer, the candidate windows (not evicted, not holding a
+ *              sink position, and older than the n_recent newest positions)
+ *              are ranked by (score, window index): the best fp_windows are
+ *              full precision, the next int2_windows INT2, the rest evicted
+ *              for good (section 4.4, Eq.4-6).  A window is quantized once,
+ *              at its first demotion (keys: scale and zero point per channel
+ *              over the window's tokens; values: per token and 32-channel
+ *              group; asymmetric min-max, scale = (max - min) / 3 and zero =
+ *              min stored as fp16, codes = clamp(rint((x - zero) / scale),
+ *              0, 3) in fp32), and its codes are reused by every later
+ *              demotion; a promotion writes the reconstruction code * scale
+ *              + zero, rounded to bf16, as the window's full-precision values
+ *              (section 4.4, Algorithm 1; no rotary embedding is re-applied).
+ *              Attention reads INT2 windows through their reconstruction in
+ *              the kernel (section 4.1).  Selection groups are layers.        */
+typedef enum {
+  KVEV_EMA = 0,
+  KVEV_CUMULATIVE = 1,
+  KVEV_LRFU_BLOCK = 2,
+  KVEV_TIERED_INT2 = 3
+} kvev_policy;
 
 #define KVEV_MAX_REGIONS 8
 
@@ -96,10 +123,18 @@ typedef struct {
   float access_tau_mult;                      /* a block is accessed when its mass per token
                                                  is >= access_tau_mult / (resident tokens);
                                                  "MemDecay" section IV-A uses 2 */
+  /* KVEV_TIERED_INT2 only: dtype bf16, head_dim 128, 4 query heads per KV
+   * head, batch 1, max_tokens <= 196608, refresh_interval 1, score_free 0;
+   * budget is ignored (the tier capacities replace it).  n_sink positions
+   * (their windows) and the n_recent newest positions (their windows) stay
+   * full precision and are never routed. */
+  int32_t window_tokens;                      /* tokens per window; must be 32 */
+  int32_t fp_windows;                         /* K_f: routed windows kept in full precision */
+  int32_t int2_windows;                       /* K_q: routed windows kept in INT2 */
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
- * refresh_interval 1, no protection; shape fields zero. */
+ * refresh_interval 1, no protection, window_tokens 32; shape fields zero. */
 void kvev_config_init(kvev_config* cfg);
 
 /* Validate *cfg, allocate the page pool and all per-step state on the
@@ -231,6 +266,53 @@ kvev_status kvev_import_blocks(kvev_ctx* ctx, int32_t seq, int64_t n_blocks, con
                                const int32_t* tref, const uint8_t* resident, int64_t n_tokens,
                                const void* k, const void* v);
 
+/* ---- KVEV_TIERED_INT2 mode ---------------------------------------------
+ * In this mode kvev_prefill takes seq 0; kvev_decode_step appends, attends
+ * over the full-precision and INT2 windows of every layer and adds each
+ * accessible window's mass to its score; kvev_evict (its budget argument is
+ * ignored) runs one routing event in every layer with the tier transitions
+ * (quantize on first demotion, dequantize on promotion); kvev_step is the
+ * two.  kvev_scores(ctx, 0, layer, ...) returns the layer's window scores
+ * by window index.  kvev_retained and kvev_export_kv do not apply (use the
+ * calls below). */
+
+/* Copy the window state of `layer` (windows 0..*n_windows-1, window w =
+ * positions [32w, 32w+32)) to host buffers: score, tier (0 full precision,
+ * 1 INT2, 2 evicted), ledger flag (1 once quantized).  Any may be NULL.
+ * Synchronises.  Errors: KVEV_EINVAL (not tiered mode, bad layer),
+ * KVEV_ERANGE (cap too small). */
+kvev_status kvev_tier_state(kvev_ctx* ctx, int32_t layer, float* score, uint8_t* tier,
+                            uint8_t* ledger, int64_t cap, int64_t* n_windows);
+
+/* Copy the full-precision storage of (layer, kv_head) for windows
+ * 0..nw-1 into device k_out, v_out, each [32 * nw][128] bf16 by position
+ * (rows of evicted windows and of INT2 windows hold whatever the storage
+ * holds: the original values, or the last promotion's).  cap = rows the
+ * buffers hold; *n_rows = 32 * nw.  Stream-ordered.  Errors: KVEV_EINVAL,
+ * KVEV_ERANGE. */
+kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void* k_out,
+                             void* v_out, int64_t cap, int64_t* n_rows);
+
+/* Copy and unpack the INT2 record of (layer, kv_head, window) to host
+ * buffers: k_codes [32][128] (token, channel), k_scale / k_zero [128] fp16
+ * bits, v_codes [32][128], v_scale / v_zero [32][4] fp16 bits (token,
+ * 32-channel group).  Synchronises.  Errors: KVEV_EINVAL (not tiered mode,
+ * bad indices, window never quantized). */
+kvev_status kvev_tier_ledger(kvev_ctx* ctx, int32_t layer, int32_t kv_head, int32_t window,
+                             uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
+                             uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero);
+
+/* Replace the window state of `layer`: host score and tier (as in
+ * kvev_tier_state) for windows 0..n_windows-1 (n_windows must equal the
+ * windows seen).  The tier change of each window is applied as a routing
+ * event would apply it (quantize a window entering INT2 without a record,
+ * write the reconstruction of a window promoted from INT2).  The tier
+ * counts must equal the context's (pinned and local windows full
+ * precision).  Used to put both sides of a comparison on the same state.
+ * Errors: KVEV_EINVAL. */
+kvev_status kvev_tier_import(kvev_ctx* ctx, int32_t layer, int64_t n_windows, const float* score,
+                             const uint8_t* tier);
+
 /* Wait for all work queued on the context's stream; report a HIP error. */
 kvev_status kvev_sync(kvev_ctx* ctx);
 
@@ -244,7 +326,10 @@ int64_t kvev_step_index(const kvev_ctx* ctx);
  * (kvev_evict; "move" also in kvev_step when many slots move).  LRFU_BLOCK
  * mode: "open" (slot and block of the new token), "attn", "merge" (split
  * merge and output), "mass" (block mass), "policy" (score, clock, priority,
- * selection, table compaction), "readmit".
+ * selection, table compaction), "readmit".  TIERED_INT2 mode: "append",
+ * "attn" (attention over the full-precision and INT2 windows), "merge" (split
+ * merge and window mass into the scores), "route" (routing and tier
+ * transitions).
  * *total_ms / *launches cover the launches since the last reset. */
 kvev_status kvev_profile_enable(kvev_ctx* ctx, int32_t enable);
 kvev_status kvev_profile_reset(kvev_ctx* ctx);

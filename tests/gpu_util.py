@@ -331,3 +331,122 @@ def run_block_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", 
     ctx.sync()
     ctx.close()
     return st
+
+
+# ---------------------------------------------------------------------------
+# Two-tier window mode (full precision / INT2 / evicted per layer)
+# ---------------------------------------------------------------------------
+
+def _tier_boundaries(S, tiers, cand):
+    """The oracle's lowest full-precision and lowest INT2 candidate scores."""
+    f = [S[w] for w in cand if tiers[w] == 0]
+    q = [S[w] for w in cand if tiers[w] == 1]
+    return [x for x in (min(f) if f else None, min(q) if q else None) if x is not None]
+
+
+def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda", fused=True,
+                      kv_every=4, ledger_every=4):
+    """Run `steps` decode + routing steps of tiered workload `w` on the GPU and
+    the oracle (the oracle holds `sample_layers`)."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    layers = list(range(w.n_layers)) if sample_layers is None else sorted(sample_layers)
+    log(f"[tier] {w.name}: L={w.n_layers} L0={w.prefill_lens[0]} steps={steps} K_f={w.fp_windows} "
+        f"K_q={w.int2_windows} sink={w.n_sink} recent={w.n_recent} layers={layers} fused={fused}")
+    t_start = time.time()
+    ctx = kvev.context_for(w, max_steps=steps)
+    o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
+                         k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
+                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1)
+    K, V = w.prefill_kv(0, device=device)
+    ctx.prefill(0, K.contiguous(), V.contiguous())
+    del K, V
+    Kc, Vc = w.prefill_kv(0, device="cpu", layers=layers)
+    o.prefill(Kc.float().numpy(), Vc.float().numpy(), layers=layers)
+    del Kc, Vc
+    torch.cuda.synchronize()
+    log(f"[tier] prefill done in {time.time() - t_start:.1f}s")
+    st = Stats()
+    st.ledger_checks = 0
+    st.promotions = 0
+    Hg = w.group_size
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
+    for t in range(1, steps + 1):
+        q, kn, vn = w.step_inputs(t, device=device)
+        if fused:
+            ctx.step(q, kn, vn, out)
+        else:
+            ctx.decode_step(q, kn, vn, out)
+        sel = torch.tensor(layers)
+        ref_out = o.decode_step(t, q[sel, 0].float().cpu().numpy(), kn[sel, 0].float().cpu().numpy(),
+                                vn[sel, 0].float().cpu().numpy())
+        gout = out.cpu().numpy()
+        for j, l in enumerate(layers):
+            for h in range(w.n_kv_heads):
+                st.max_out_err = max(st.max_out_err, check_out(
+                    gout[l, 0, h * Hg:(h + 1) * Hg], ref_out[j, h * Hg:(h + 1) * Hg], rtol,
+                    f"step {t} out l={l} kvh={h}"))
+        if not fused:
+            for l in layers:
+                gs, _, _ = ctx.tier_state(l)
+                os_, ot, _ = o.window_state(l)
+                live = ot != 2
+                st.max_score_err = max(st.max_score_err, check_scores(
+                    gs[live], os_[live], rtol, f"step {t} pre-route scores l={l}"))
+            ctx.evict()
+        prev = {l: o.window_state(l)[1] for l in layers}
+        nw_pre = o.n_windows()
+        o.route()
+        for l in layers:
+            gs, gt, gl = ctx.tier_state(l)
+            os_, ot, ol = o.window_state(l)
+            assert len(gt) == len(ot), f"step {t} l={l}: {len(gt)} windows on the GPU, {len(ot)} in the oracle"
+            st.promotions += int(((prev[l] == 1) & (ot == 0)).sum())
+            if not np.array_equal(gt, ot) or not np.array_equal(gl, ol):
+                cand = [x for x in range(nw_pre) if o.is_aged(x) and prev[l][x] != 2]
+                thetas = _tier_boundaries(os_, ot, cand)
+                diff = np.flatnonzero((gt != ot) | (gl != ol)).tolist()
+                gaps = [min(abs(os_[x] - th) for th in thetas) for x in diff]
+                assert max(gaps) < 1e-5, (f"step {t} l={l}: tiers differ at windows {diff[:8]} "
+                                          f"(gpu {gt[diff[:8]]}, oracle {ot[diff[:8]]}) with oracle "
+                                          f"score gap {max(gaps):.3e} >= 1e-5")
+                st.near_tie_resyncs += 1
+                st.notes.append(f"t={t} l={l} near-tie resync ({len(diff)} windows)")
+                ctx.tier_import(l, os_.astype(np.float32), ot)
+                continue
+            st.max_score_err = max(st.max_score_err, check_scores(gs, os_, rtol, f"step {t} scores l={l}"))
+            st.exact_selection_checks += 1
+            if kv_every and (t % kv_every == 0 or t == 1 or t == steps):
+                lay = o.layers[l]
+                rows = np.concatenate([np.arange(32 * x, min(32 * x + 32, o.npos)) for x in np.flatnonzero(ot == 0)])
+                for h in range(w.n_kv_heads):
+                    gk, gv = ctx.tier_export(l, h)
+                    idx = torch.from_numpy(rows)
+                    rk = torch.from_numpy(lay.K[h, rows].copy()).to(w.torch_dtype)
+                    rv = torch.from_numpy(lay.V[h, rows].copy()).to(w.torch_dtype)
+                    assert torch.equal(gk.cpu()[idx], rk), f"step {t} l={l} kvh={h}: full-precision K differs"
+                    assert torch.equal(gv.cpu()[idx], rv), f"step {t} l={l} kvh={h}: full-precision V differs"
+                    st.kv_checks += 1
+            if ledger_every and (t % ledger_every == 0 or t == 1):
+                lay = o.layers[l]
+                wins = np.flatnonzero(ol)
+                if len(wins) > 24:
+                    wins = wins[np.linspace(0, len(wins) - 1, 24).astype(int)]
+                for x in wins.tolist():
+                    for h in range(w.n_kv_heads):
+                        got = ctx.tier_ledger(l, h, x)
+                        ref = lay.ledger[x][h]
+                        for a, b, name in zip(got, ref, ("k_codes", "k_scale", "k_zero", "v_codes",
+                                                           "v_scale", "v_zero")):
+                            assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8)), (
+                                f"step {t} l={l} kvh={h} window {x}: ledger {name} differs")
+                        st.ledger_checks += 1
+        st.steps = t
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[tier] step {t}: out_err {st.max_out_err:.2e} score_err {st.max_score_err:.2e} "
+                f"resyncs {st.near_tie_resyncs} promotions {st.promotions} ledger {st.ledger_checks} "
+                f"({time.time() - t_start:.1f}s)")
+    ctx.sync()
+    ctx.close()
+    return st

@@ -86,6 +86,13 @@ def _create(**kw):
     (dict(policy=kvev.LRFU_BLOCK, pinned_region_mask=0x100), "mask"),
     (dict(policy=kvev.LRFU_BLOCK, access_tau_mult=0.0), "access_tau_mult"),
     (dict(policy=kvev.LRFU_BLOCK, budget=5000), "4096"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.F32, head_dim=128), "bf16"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=64), "head_dim 128"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, batch=2), "batch"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, window_tokens=16), "window_tokens"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, fp_windows=-1), "capacities"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, max_tokens=200000), "196608"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
 ])
 def test_create_rejects_bad_config(bad, msg):
     st, err, h = _create(**bad)
@@ -109,6 +116,15 @@ def test_config_defaults():
     assert abs(c.alpha_new - 0.05) < 1e-7
     assert abs(c.beta - 0.001) < 1e-9 and c.decode_region == 4 and c.access_tau_mult == 2.0
     assert c.pinned_region_mask == 0 and list(c.region_half_life) == [0.0] * 8
+    assert c.window_tokens == 32 and c.fp_windows == 0 and c.int2_windows == 0
+
+
+def test_tier_entry_points_reject_null_context():
+    L = kvev.lib()
+    assert L.kvev_tier_state(None, 0, None, None, None, 0, None) == kvev.EINVAL
+    assert L.kvev_tier_export(None, 0, 0, None, None, 0, None) == kvev.EINVAL
+    assert L.kvev_tier_ledger(None, 0, 0, 0, None, None, None, None, None, None) == kvev.EINVAL
+    assert L.kvev_tier_import(None, 0, 0, None, None) == kvev.EINVAL
 
 
 def test_block_entry_points_reject_null_context():

@@ -1,0 +1,70 @@
+"""GPU parity of the two-tier window path (append, attention over full-
+precision and INT2 windows with in-kernel reconstruction, cumulative window
+scores, per-layer routing, quantization on first demotion, promotion) against
+the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+from conftest import gpu_available
+from decode_kv_cache_gqa_amd import synth
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _gu():
+    import gpu_util
+    return gpu_util
+
+
+def _scaled(**kw):
+    base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, prefill_lens=(1500,), fp_windows=5,
+                int2_windows=12, n_epochs=3, epoch_steps=16)
+    base.update(kw)
+    return synth.workload("qevict131k").scaled(**base)
+
+
+def test_tier_fused_step_with_drift():
+    """2 layers, 47 windows (a ragged last one), 48 steps over 3 re-targeted
+    heavy-key epochs: promotions, demotions with reused codes, evictions as
+    windows age out of the recent region."""
+    st = _gu().run_tier_lockstep(_scaled(), 48)
+    assert st.steps == 48 and st.ledger_checks > 0 and st.kv_checks > 0
+
+
+def test_tier_separate_calls():
+    st = _gu().run_tier_lockstep(_scaled(prefill_lens=(1024,)), 40, fused=False)
+    assert st.steps == 40
+
+
+def test_tier_no_int2_tier_and_no_protection():
+    """Two-tier without the INT2 tier (K_q = 0) and no sinks or recent window."""
+    w = _scaled(int2_windows=0, n_sink=0, n_recent=0, prefill_lens=(900,))
+    st = _gu().run_tier_lockstep(w, 36)
+    assert st.steps == 36
+
+
+def test_tier_everything_fits():
+    """Capacities above the window count: nothing is quantized or evicted."""
+    w = _scaled(fp_windows=100, int2_windows=100, prefill_lens=(700,))
+    st = _gu().run_tier_lockstep(w, 20)
+    assert st.ledger_checks == 0
+
+
+def test_tier_large_int2_share():
+    """A big INT2 tier (most routed windows quantized): 8 KV heads, 4 layers."""
+    w = _scaled(n_layers=4, n_q_heads=32, n_kv_heads=8, prefill_lens=(4000,), fp_windows=8,
+                int2_windows=60, epoch_steps=8, n_epochs=4)
+    st = _gu().run_tier_lockstep(w, 32, sample_layers=[0, 3])
+    assert st.steps == 32
+
+
+def test_qevict131k_full_size_sampled():
+    """The full 32-layer, 131,072-token workload (205 full-precision and 819
+    INT2 windows per layer, 5 sinks, 32 recent) in the benchmark's launch
+    configuration; the oracle holds layers 0 and 31.  34 steps: the first
+    routing event over 4,094 candidates, the first aged-out window at step
+    32 and the first heavy-key re-targeting at step 33."""
+    w = synth.workload("qevict131k")
+    st = _gu().run_tier_lockstep(w, 34, sample_layers=[0, 31], kv_every=16, ledger_every=16)
+    assert st.steps == 34 and st.ledger_checks > 0
