@@ -254,7 +254,7 @@ def route_tiers(scores, candidates, k_f, k_q):
 def _int2_params(x32, axis):
     """Asymmetric min-max parameters of each group, stored as fp16.
 
-    Reading of [QEvict] §4.4 line 11 (asymmetric, KIVI-style): zero = min,
+    Reading of [QEvict] §4.4, Algorithm 1 (asymmetric, KIVI-style): zero = min,
     scale = (max - min) / 3, both rounded to fp16 (round to nearest even);
     the subtraction and division are single IEEE fp32 operations.  The
     groups run along ``axis`` of the fp32 array ``x32``.
@@ -284,7 +284,7 @@ def int2_quantize(x, axis_groups):
     """Quantize a [tokens, channels] fp32 tile to 2-bit codes.
 
     ``axis_groups="channel"``: one (scale, zero) per channel over all tokens
-    of the tile (keys, [QEvict] §4.4 line 11 "per-channel-key").
+    of the tile (keys, [QEvict] §4.4 Algorithm 1: keys per channel).
     ``axis_groups="token32"``: one (scale, zero) per token per 32-channel
     group (values, "per-token-value"; the 32-channel grouping is the
     workload's stated group size).
@@ -787,7 +787,7 @@ class TieredOracle:
     * A window entering Q is quantized only if it has no ledger entry yet
       (its first demotion); otherwise the stored codes are reused.  Keys
       are quantized per channel over the window's tokens, values per token
-      in 32-channel groups ([QEvict] §4.4 lines 9-14; ``int2_quantize``).
+      in 32-channel groups ([QEvict] §4.4 Algorithm 1; ``int2_quantize``).
     * A window promoted from Q to F gets its dequantized values rounded to
       bf16 as its full-precision storage (reading: the synthetic keys carry
       no rotary embedding, so there is none to re-apply).

@@ -7,7 +7,7 @@ no INT2 tier), full softmax attention when nothing is routed away, the
 conservation of attention mass in the cumulative score (softmax rows sum to
 one, Eq.1 divides by Hq), the tier sizes and ordering of Eq.5, the
 absorbing eviction state of Eq.6, and the once-only quantization of the
-ledger (Algorithm 1, lines 9-14) checked against the quantizer applied to
+ledger (§4.4 Algorithm 1) checked against the quantizer applied to
 the original inputs.
 """
 import math
@@ -165,7 +165,7 @@ def test_routing_sizes_order_and_absorbing_eviction():
 
 
 def test_ledger_is_written_once_from_the_original_values():
-    """Algorithm 1 lines 9-17: a window's codes come from its original
+    """§4.4 Algorithm 1: a window's codes come from its original
     full-precision values at its first demotion and are reused through every
     later promotion and demotion; a promoted window's storage is its
     reconstruction rounded to bf16, and INT2 windows are attended through
