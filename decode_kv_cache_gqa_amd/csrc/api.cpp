@@ -235,7 +235,9 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.score, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.count, G));
   A(dalloc(&d.nextpos, G));
-  A(dalloc(&d.logits, static_cast<size_t>(G) * L * c->cap * HG));
+  // the logit stride is the step's slot count rounded up to 16, which can
+  // exceed a capacity that is not a multiple of 16
+  A(dalloc(&d.logits, static_cast<size_t>(G) * L * ((c->cap + 15) / 16 * 16) * HG));
   A(dalloc(&d.part_ml, static_cast<size_t>(L) * G * c->max_splits * HG * 2));
   A(dalloc(&d.part_o, static_cast<size_t>(L) * G * c->max_splits * HG * D));
   A(dalloc(&d.ml, static_cast<size_t>(L) * G * HG * 2));

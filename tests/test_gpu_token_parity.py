@@ -112,6 +112,15 @@ def test_edge_budget_not_binding_and_tiny_prefill():
     _gu().run_token_lockstep(w, 30)
 
 
+def test_capacity_not_multiple_of_16_filled():
+    """The budget never binds and the slot capacity (prefill + steps + 1 = 45)
+    is not a multiple of 16: on the last steps the logit rows, whose stride is
+    the slot count rounded up to 16 (48), must stay inside their buffer."""
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(20,), budget=100,
+                                             n_sink=1, n_recent=2)
+    _gu().run_token_lockstep(w, 24)
+
+
 def test_equal_scores_resolved_by_position():
     """All-zero keys give every token the same logits, so utilities tie
     exactly; the cut must fall by position (more recent kept)."""
