@@ -11,7 +11,9 @@ timed region.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: the path runs on one
 GPU.  ``--workload qevict131k`` times the two-tier window path instead
-(131,072-token prefill, 205 full-precision and 819 INT2 windows per layer).
+(131,072-token prefill, 205 full-precision and 819 INT2 windows per layer),
+``--workload lrfu64`` the block-LRFU path (64 sequences of 4k-16k tokens,
+20% block budgets).
 """
 from __future__ import annotations
 
@@ -140,6 +142,110 @@ def tier_cpu_baseline(w, steps=3):
                       f"({w.prefill_lens[0]}-token prefill), scaled x{w.n_layers}"}
 
 
+def block_cpu_baseline(w, steps=40):
+    """The CPU oracle on the median-length sequence of the block workload:
+    its prefill and first eviction untimed, then `steps` steady steps timed
+    and scaled to every sequence."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    b = int(np.argsort(w.prefill_lens)[len(w.prefill_lens) // 2])
+    o = orc.BlockLRFUOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, alpha_new=w.alpha_new,
+                            beta=w.beta, half_lives=tuple(w.region_half_lives),
+                            pinned_regions=tuple(w.pinned_regions), decode_region=w.decode_region,
+                            capacity=w.prefill_lens[b] + steps + 2)
+    K, V = w.prefill_kv(b)
+    o.prefill(b, K.float().numpy(), V.float().numpy(), w.region_labels(b), w.block_budget(b))
+    del K, V
+    ins = [tuple(x.float().numpy() for x in w.step_inputs(t, seqs=[b])) for t in range(1, steps + 2)]
+    o.decode_step(1, *ins[0], [b])
+    o.evict(1, seqs=[b])
+    t0 = time.perf_counter()
+    for t in range(2, steps + 2):
+        o.decode_step(t, *ins[t - 1], [b])
+        o.evict(t, seqs=[b])
+    per_seq = (time.perf_counter() - t0) / steps
+    return {"value": 1.0 / (per_seq * w.batch), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} steady steps of sequence {b} ({w.prefill_lens[b]}-token prefill, the median) "
+                      f"of {w.batch} after its first eviction, scaled x{w.batch}"}
+
+
+def run_block(args, w):
+    """Steady kvev_step calls of the block-LRFU workload (all sequences each
+    step; the epochs' re-admissions are not part of the timed steps)."""
+    import numpy as np
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    total = args.warmup + args.steps
+    ctx = kvev.context_for(w, max_steps=total)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device="cuda")
+        ctx.prefill(b, K.contiguous(), V.contiguous(), w.region_labels(b))
+        ctx.set_budget(b, w.block_budget(b))
+        del K, V
+    inputs = [w.step_inputs(t, device="cuda") for t in range(1, total + 1)]
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for t in range(args.warmup):
+        ctx.step(*inputs[t], out)
+    ctx.sync()
+    ctx.profile(True)
+    ctx.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total):
+        ctx.step(*inputs[t], out)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ctx.sync()
+    names = ("open", "attn", "merge", "mass", "policy")
+    prof = {k: ctx.profile_read(k) for k in names}
+    # resident tokens read by a steady step: every resident block is full
+    # except the sequence's last one (the new token's)
+    n_tok = 0
+    for b in range(w.batch):
+        _, _, res = ctx.block_state(b)
+        npos = w.prefill_lens[b] + total
+        n_tok += int(res.sum()) * 16 - (-npos % 16)
+    ctx.close()
+    L, Hkv, Hq, d = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
+    kv_bytes = L * Hkv * n_tok * 2 * d * 2
+    step_bytes = kv_bytes + w.batch * (L * Hq * d * 2 + L * Hq * d * 4 + L * Hkv * 2 * d * 2)
+    ms_step = dt * 1e3 / args.steps
+    attn_ms, attn_n = prof["attn"]
+    attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
+    attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
+    policy_ms = sum(prof[k][0] for k in ("merge", "mass", "policy")) / args.steps
+    result = {
+        "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
+        "value": round(args.steps / dt, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator: region labels, shared heavy blocks re-targeted per epoch)",
+        "config": {"workload": w.name, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "batch": w.batch, "prefill": [min(w.prefill_lens), max(w.prefill_lens)],
+                   "block_budget_frac": w.budget_frac, "alpha_new": w.alpha_new, "beta": w.beta},
+        "resident_tokens": n_tok,
+        "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
+        "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,
+        "kernel_avg_us": {k: round(v[0] / max(v[1], 1) * 1e3, 3) for k, v in prof.items() if v[1]},
+        "roofline": {
+            "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
+            "traffic": None, "kernel": "attn_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = block_cpu_baseline(w)
+    print(json.dumps(result))
+
+
 def run_tier(args, w):
     import numpy as np
     import torch
@@ -235,6 +341,8 @@ def main():
     w = synth.workload(args.workload)
     if w.policy == "tiered_int2":
         return run_tier(args, w)
+    if w.policy == "lrfu_block":
+        return run_block(args, w)
     total = args.warmup + args.steps
     dev = "cuda"
     ctx = kvev.context_for(w, max_steps=total)
