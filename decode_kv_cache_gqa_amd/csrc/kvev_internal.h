@@ -21,7 +21,7 @@ constexpr int kTierWin = 32;            // tokens per routing window
 constexpr int kTierD = 128;             // head dim of the tiered mode
 constexpr int kTierLedgerBytes = 3072;  // INT2 record per (layer, KV head, window)
 constexpr int kTierMaxWin = 6144;       // windows per sequence (196608 positions)
-constexpr int kTierXferBlocks = 64;     // blocks per (layer, KV head) of the transition kernel
+constexpr int kTierXferBlocks = 64;     // blocks per layer of the transition kernel
 
 // Device buffers of one context.  Groups are (sequence, KV head) pairs,
 // g = seq * Hkv + kv_head; slots of a group are its cached tokens in order.

@@ -28,9 +28,9 @@
 // promotion only rewrites it and nothing moves when tiers change.
 //
 // Code records.  A 2-bit code c = b0 + 2 b1 is stored as two bit planes.  In
-// the matrix-core products a plane is a B operand of 8 bf16 values in {0,1}
-// (made from the bits with one AND and one 24-bit multiply per pair), and
-// the A operand of the second plane is doubled, so the product sums
+// the matrix-core products plane 0 is a B operand of 8 bf16 values in {0,1}
+// and plane 1 one in {0,2} (made from the bits with one AND and one 24-bit
+// multiply per pair), so the two products with the same A operand sum
 // code * operand exactly.  Lane (r16, q4) = lane r16 + 16 q4 of a wave owns
 // four 32-bit words: plane 0 / plane 1, two words each; bit pi (low half)
 // and bit 16 + pi (high half) of a word are the two codes of pair pi.
@@ -72,43 +72,50 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return b;
 }
 
-// Pair pi (0..15) of a bit-plane word as two bf16 values in {0, 1}.
-template <int PI>
+// Pair pi (0..15) of a bit-plane word as two bf16 values in {0, v}: v = 1
+// for plane 0 and v = 2 for plane 1, so a product with the plane sums
+// code * operand exactly (c = b0 + 2 b1).
+template <int PI, int PLANE>
 __device__ __forceinline__ uint32_t plane_pair(uint32_t w) {
   constexpr int sh = PI & 7;
+  constexpr uint32_t v = PLANE ? 0x4000u : 0x3F80u;  // bf16 2.0 / 1.0 (low bits zero, so v >> sh is exact)
   const uint32_t x = PI < 8 ? w : (w >> 8);
-  return __umul24(x & (0x00010001u << sh), 0x3F80u >> sh);
+  return __umul24(x & (0x00010001u << sh), v >> sh);
 }
 
 // B operand (4 pairs) of pairs 4p0 .. 4p0+3 of one plane word.
-template <int P0>
+template <int P0, int PLANE>
 __device__ __forceinline__ bf16x8_t plane_operand(uint32_t w) {
-  return as_b8(make_uint4(plane_pair<4 * P0 + 0>(w), plane_pair<4 * P0 + 1>(w),
-                          plane_pair<4 * P0 + 2>(w), plane_pair<4 * P0 + 3>(w)));
+  return as_b8(make_uint4(plane_pair<4 * P0 + 0, PLANE>(w), plane_pair<4 * P0 + 1, PLANE>(w),
+                          plane_pair<4 * P0 + 2, PLANE>(w), plane_pair<4 * P0 + 3, PLANE>(w)));
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& r, int i) {
   return i == 0 ? r.x : (i == 1 ? r.y : (i == 2 ? r.z : r.w));
 }
 
+// Two fp32 values rounded to nearest-even bf16, packed (low half first).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  uint32_t u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+
 // A operand of 8 fp32 values split into bf16 high parts (rows 0..3) and
-// low parts (rows 4..7); rows 8..15 are zero.  `scale2` doubles the values
-// (exactly) for the second bit plane.
-__device__ __forceinline__ void split_rows(const float* x, int r16, bf16x8_t& a1, bf16x8_t& a2) {
-  uint32_t p1[8], p2[8];
+// low parts (rows 4..7); rows 8..15 are zero.  high + low carries 16
+// significant bits of each value.
+__device__ __forceinline__ bf16x8_t split_rows(const float* x, int r16) {
+  uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t hi = bf16_rne(x[e]);
-    const uint32_t lo = bf16_rne(x[e] - __uint_as_float(hi << 16));
-    const uint32_t v = r16 < 4 ? hi : (r16 < 8 ? lo : 0u);
-    p1[e] = v;
-    // doubling a bf16 adds one to its exponent (zero stays zero)
-    p2[e] = (v & 0x7fffu) ? v + 0x80u : v;
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t hi = pack_bf16(x[2 * p], x[2 * p + 1]);
+    const uint32_t lo = pack_bf16(x[2 * p] - __uint_as_float(hi << 16),
+                                  x[2 * p + 1] - __uint_as_float(hi & 0xffff0000u));
+    w[p] = r16 < 4 ? hi : (r16 < 8 ? lo : 0u);
   }
-  a1 = as_b8(make_uint4(p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p1[4] | (p1[5] << 16),
-                        p1[6] | (p1[7] << 16)));
-  a2 = as_b8(make_uint4(p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16), p2[4] | (p2[5] << 16),
-                        p2[6] | (p2[7] << 16)));
+  return as_b8(make_uint4(w[0], w[1], w[2], w[3]));
 }
 
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
@@ -186,7 +193,10 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
 //   p.V: A = P (high / low rows), B = V (a k-step is one window).  INT2:
 //     out_c = sum_t (p_t s_tg) code_tc + sum_t p_t z_tg, g = c / 32.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16_t* __restrict__ q,
+// Three waves per SIMD: the INT2 windows are bound by vector arithmetic and
+// memory latency, and the register cap this sets (168) costs no spills.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tier_attn_kernel(
+    TierArgs A, const uint16_t* __restrict__ q,
                                                         int n_fp, int n_q, int nch_f, int npos,
                                                         float scale) {
   __shared__ __align__(16) float p_lds[4][HG][64];
@@ -296,8 +306,7 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
       const float4 a = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
       const float4 b = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
       const float pv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      bf16x8_t pa, pa2;
-      split_rows(pv, r16, pa, pa2);
+      const bf16x8_t pa = split_rows(pv, r16);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) oacc[ct] = mfma(pa, as_b8(vr[k][ct]), oacc[ct]);
     }
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
       const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
       uint4 kc = make_uint4(0, 0, 0, 0);
       float bias = 0.f;
-      bf16x8_t a1[4], a2[4];
+      bf16x8_t a1[4];
       if (live[k]) {
         kc = *reinterpret_cast<const uint4*>(rec + kRecK + 16 * lane);
 #pragma unroll
@@ -332,11 +341,11 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
             x[e] = qf[s][e] * sc;
             bias = fmaf(qf[s][e], zp, bias);
           }
-          split_rows(x, r16, a1[s], a2[s]);
+          a1[s] = split_rows(x, r16);
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a1[s] = a2[s] = as_b8(make_uint4(0, 0, 0, 0));
+        for (int s = 0; s < 4; ++s) a1[s] = as_b8(make_uint4(0, 0, 0, 0));
       }
       // full sum_c q_c z_c of head r16 & 3 (lanes r16 = 0..3 of every q4)
       bias += __shfl_xor(bias, 16, kWave);
@@ -348,14 +357,14 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
       for (int j = 0; j < 2; ++j) {
         f32x4_t acc = q4 == 0 ? f32x4_t{bb[0], bb[1], bb[2], bb[3]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
         const uint32_t w0 = word_of(kc, j), w1 = word_of(kc, 2 + j);
-        acc = mfma(a1[0], plane_operand<0>(w0), acc);
-        acc = mfma(a2[0], plane_operand<0>(w1), acc);
-        acc = mfma(a1[1], plane_operand<1>(w0), acc);
-        acc = mfma(a2[1], plane_operand<1>(w1), acc);
-        acc = mfma(a1[2], plane_operand<2>(w0), acc);
-        acc = mfma(a2[2], plane_operand<2>(w1), acc);
-        acc = mfma(a1[3], plane_operand<3>(w0), acc);
-        acc = mfma(a2[3], plane_operand<3>(w1), acc);
+        acc = mfma(a1[0], plane_operand<0, 0>(w0), acc);
+        acc = mfma(a1[0], plane_operand<0, 1>(w1), acc);
+        acc = mfma(a1[1], plane_operand<1, 0>(w0), acc);
+        acc = mfma(a1[1], plane_operand<1, 1>(w1), acc);
+        acc = mfma(a1[2], plane_operand<2, 0>(w0), acc);
+        acc = mfma(a1[2], plane_operand<2, 1>(w1), acc);
+        acc = mfma(a1[3], plane_operand<3, 0>(w0), acc);
+        acc = mfma(a1[3], plane_operand<3, 1>(w1), acc);
         const bool valid = q4 == 0 && live[k];
 #pragma unroll
         for (int hh = 0; hh < HG; ++hh) {
@@ -423,20 +432,19 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
           x[e] = pv[e] * sc;
           bz[g] = fmaf(pv[e], zp, bz[g]);
         }
-        bf16x8_t pa, pa2;
-        split_rows(x, r16, pa, pa2);
+        const bf16x8_t pa = split_rows(x, r16);
         const uint32_t w0 = word_of(vc, g >> 1), w1 = word_of(vc, 2 + (g >> 1));
         // tiles ct = 2g, 2g + 1 sit at pairs 4 (ct % 4) .. of word ct / 4
         if ((g & 1) == 0) {
-          oacc[2 * g] = mfma(pa, plane_operand<0>(w0), oacc[2 * g]);
-          oacc[2 * g] = mfma(pa2, plane_operand<0>(w1), oacc[2 * g]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<1>(w0), oacc[2 * g + 1]);
-          oacc[2 * g + 1] = mfma(pa2, plane_operand<1>(w1), oacc[2 * g + 1]);
+          oacc[2 * g] = mfma(pa, plane_operand<0, 0>(w0), oacc[2 * g]);
+          oacc[2 * g] = mfma(pa, plane_operand<0, 1>(w1), oacc[2 * g]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<1, 0>(w0), oacc[2 * g + 1]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<1, 1>(w1), oacc[2 * g + 1]);
         } else {
-          oacc[2 * g] = mfma(pa, plane_operand<2>(w0), oacc[2 * g]);
-          oacc[2 * g] = mfma(pa2, plane_operand<2>(w1), oacc[2 * g]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<3>(w0), oacc[2 * g + 1]);
-          oacc[2 * g + 1] = mfma(pa2, plane_operand<3>(w1), oacc[2 * g + 1]);
+          oacc[2 * g] = mfma(pa, plane_operand<2, 0>(w0), oacc[2 * g]);
+          oacc[2 * g] = mfma(pa, plane_operand<2, 1>(w1), oacc[2 * g]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<3, 0>(w0), oacc[2 * g + 1]);
+          oacc[2 * g + 1] = mfma(pa, plane_operand<3, 1>(w1), oacc[2 * g + 1]);
         }
       }
     }
@@ -501,30 +509,64 @@ __global__ __launch_bounds__(256) void tier_attn_kernel(TierArgs A, const uint16
 }
 
 // ---------------------------------------------------------------------------
-// Merge the chunks of (layer l, KV head h): out and the global (max, sum).
-// Block (h, l), 256 threads.
+// Merge the chunks of query head hh of (layer l, KV head h): its output and
+// global (max, sum).  Block (hh, h, l), 256 threads, dynamic LDS of 2 * nch
+// floats.  The chunks' (max, sum) are staged in LDS; wave 0 reduces M and Z
+// and turns each chunk's max m into its weight e^(m - M).  Output channel c
+// is summed by threads c (even chunks) and c + 128 (odd chunks),
+// kMergeLoads independent loads at a time, and the halves are added in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kMergeLoads = 32;
+
 __global__ __launch_bounds__(256) void tier_merge_kernel(TierArgs A, float* __restrict__ out, int nch) {
-  const int h = blockIdx.x, l = blockIdx.y, tid = threadIdx.x;
+  extern __shared__ float mlds[];
+  float* sm = mlds;        // [nch]: chunk max, then its weight
+  float* sz = mlds + nch;  // [nch]: chunk sum
+  __shared__ float s_Z, half[D];
+  const int hh = blockIdx.x, h = blockIdx.y, l = blockIdx.z, tid = threadIdx.x, lane = tid % kWave;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
-  for (int idx = tid; idx < HG * D; idx += 256) {
-    const int hh = idx / D, c = idx % D;
+  const float* pml = A.part_ml + lh * A.maxch * HG * 2;
+  for (int c = tid; c < nch; c += 256) {
+    sm[c] = pml[(c * HG + hh) * 2];
+    sz[c] = pml[(c * HG + hh) * 2 + 1];
+  }
+  __syncthreads();
+  if (tid < kWave) {
     float M = -INFINITY;
-    for (int s = 0; s < nch; ++s) M = fmaxf(M, A.part_ml[((lh * A.maxch + s) * HG + hh) * 2]);
-    float o = 0.f, Z = 0.f;
-    for (int s = 0; s < nch; ++s) {
-      const int64_t pb = lh * A.maxch + s;
-      const float m = A.part_ml[(pb * HG + hh) * 2];
+    for (int c = lane; c < nch; c += kWave) M = fmaxf(M, sm[c]);
+    M = wave_max(M);
+    float Z = 0.f;
+    for (int c = lane; c < nch; c += kWave) {
+      const float m = sm[c];
       const float f = m == -INFINITY ? 0.f : __expf(m - M);
-      Z += f * A.part_ml[(pb * HG + hh) * 2 + 1];
-      o += f * A.part_o[pb * HG * D + idx];
+      sm[c] = f;
+      Z += f * sz[c];
     }
-    out[(static_cast<int64_t>(l) * A.Hq + h * HG + hh) * D + c] = o / Z;
-    if (c == 0) {
+    Z = wave_sum(Z);
+    if (lane == 0) {
+      s_Z = Z;
       A.ml[(lh * HG + hh) * 2] = M;
       A.ml[(lh * HG + hh) * 2 + 1] = Z;
     }
   }
+  __syncthreads();
+  const int ch = tid % D, par = tid / D;  // channel, chunk parity
+  const float* po = A.part_o + (lh * A.maxch * HG + hh) * D + ch;
+  float o = 0.f;
+  for (int c0 = par; c0 < nch; c0 += 2 * kMergeLoads) {
+    float v[kMergeLoads];
+#pragma unroll
+    for (int k = 0; k < kMergeLoads; ++k) {
+      const int c = c0 + 2 * k;
+      v[k] = c < nch ? po[static_cast<int64_t>(c) * HG * D] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeLoads; ++k)
+      if (c0 + 2 * k < nch) o = fmaf(sm[c0 + 2 * k], v[k], o);
+  }
+  if (par == 1) half[ch] = o;
+  __syncthreads();
+  if (par == 0) out[(static_cast<int64_t>(l) * A.Hq + h * HG + hh) * D + ch] = (o + half[ch]) / s_Z;
 }
 
 // ---------------------------------------------------------------------------
@@ -541,15 +583,28 @@ __global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, in
   const int w = isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
                     : A.fplist[static_cast<int64_t>(l) * A.NW + idx];
   float acc = 0.f;
-  for (int h = 0; h < A.Hkv; ++h) {
-    const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  // the KV heads in batches of 8, every load of a batch issued before use
+  for (int h0 = 0; h0 < A.Hkv; h0 += 8) {
+    float mb[8][HG], M[8][HG], Z[8][HG], em[8][HG];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const float mb = A.part_ml[((lh * A.maxch + chunk) * HG + hh) * 2];
-      const float M = A.ml[(lh * HG + hh) * 2], Z = A.ml[(lh * HG + hh) * 2 + 1];
-      const float f = mb == -INFINITY ? 0.f : __expf(mb - M) / Z;
-      acc += A.emass[(lh * A.NW + idx) * HG + hh] * f;
+    for (int k = 0; k < 8; ++k) {
+      const int h = min(h0 + k, A.Hkv - 1);
+      const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        mb[k][hh] = A.part_ml[((lh * A.maxch + chunk) * HG + hh) * 2];
+        M[k][hh] = A.ml[(lh * HG + hh) * 2];
+        Z[k][hh] = A.ml[(lh * HG + hh) * 2 + 1];
+        em[k][hh] = A.emass[(lh * A.NW + idx) * HG + hh];
+      }
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float f = mb[k][hh] == -INFINITY ? 0.f : __expf(mb[k][hh] - M[k][hh]) / Z[k][hh];
+        if (h0 + k < A.Hkv) acc += em[k][hh] * f;
+      }
   }
   A.S[static_cast<int64_t>(l) * A.NW + w] += acc / static_cast<float>(A.Hq);
 }
@@ -671,7 +726,9 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
 // Tier transitions of layer l: quantize a window's full-precision values
 // into its ledger record (first demotion) or write its reconstruction,
 // rounded to bf16, into its full-precision storage (promotion).  Block
-// (x, h, l), 256 threads, jobs x, x + gridDim.x, ...
+// (x, l), 256 threads, takes the layer's (job, KV head) pairs x, x + gridDim.x,
+// ...: a step with few transitions launches few blocks per layer, and the
+// first routing event still spreads its many jobs over all of them.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void int2_group(const float* x, int n, int stride, float& sc, float& zp,
                                            uint16_t& s16, uint16_t& z16) {
@@ -699,10 +756,13 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
   __shared__ float xv[W][D + 1];
   __shared__ uint8_t ck[W][D];
   __shared__ uint8_t cv[W][D];
-  const int h = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
-  const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
+  __shared__ uint32_t recl[kTierLedgerBytes / 4];
+  const int l = blockIdx.y, tid = threadIdx.x;
   const int nj = A.njobs[l];
-  for (int j = blockIdx.x; j < nj; j += gridDim.x) {
+  // the layer's (job, KV head) pairs, strided over the blocks of the layer
+  for (int p = blockIdx.x; p < nj * A.Hkv; p += gridDim.x) {
+    const int j = p / A.Hkv, h = p % A.Hkv;
+    const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
     const int job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
     const int w = job >> 2, kind = job & 3;
     uint16_t* kd = A.kfp + (lh * A.NW + w) * W * D;
@@ -711,9 +771,28 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
     uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
     uint32_t* rec32 = reinterpret_cast<uint32_t*>(rec);
     if (kind == 1) {
-      for (int i = tid; i < W * D; i += 256) {
-        xk[i / D][i % D] = __uint_as_float(static_cast<uint32_t>(kd[i]) << 16);
-        xv[i % W][i / W] = __uint_as_float(static_cast<uint32_t>(vd[i]) << 16);
+      // stage the window in LDS as fp32: 8 consecutive elements of K
+      // (token-major) and of V (channel-major) per 16-byte load, all loads
+      // of the thread issued before the first store
+      uint4 kr[2], vr[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i0 = 8 * (tid + 256 * u);
+        kr[u] = *reinterpret_cast<const uint4*>(kd + i0);
+        vr[u] = *reinterpret_cast<const uint4*>(vd + i0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i0 = 8 * (tid + 256 * u);
+        const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+        const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t kb = (kw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t vb = (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          xk[(i0 + e) / D][(i0 + e) % D] = __uint_as_float(kb << 16);
+          xv[(i0 + e) % W][(i0 + e) / W] = __uint_as_float(vb << 16);
+        }
       }
       __syncthreads();
       if (tid < D) {  // keys: one channel over the window's tokens
@@ -757,29 +836,54 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
       }
       __syncthreads();
     } else if (kind == 2) {
-      for (int i = tid; i < W * D; i += 256) {
-        {  // key element (token r, channel c)
-          const int r = i / D, c = i % D;
-          const int r16 = r & 15, part = r >> 4, s = c >> 5, q4 = (c & 31) >> 3, e = c & 7;
-          const int ln = q4 * 16 + r16, pi = 4 * s + (e >> 1), bit = pi + 16 * (e & 1);
-          const uint32_t w0 = rec32[kRecK / 4 + 4 * ln + part], w1 = rec32[kRecK / 4 + 4 * ln + 2 + part];
-          const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
-          const float sc = h2f(rec16[kRecSK / 2 + c]), zp = h2f(rec16[kRecZK / 2 + c]);
-          const float x = __fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp);
-          kd[i] = static_cast<uint16_t>(bf16_rne(x));
+      // the record into LDS (3,072 B, three words per thread), then 8
+      // consecutive elements of K (one token) and of V (one channel) per
+      // thread and 16-byte store
+      uint32_t rw[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) rw[u] = rec32[tid + 256 * u];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) recl[tid + 256 * u] = rw[u];
+      __syncthreads();
+      const uint16_t* rl16 = reinterpret_cast<const uint16_t*>(recl);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i0 = 8 * (tid + 256 * u);
+        uint32_t ko[4], vo[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t kb, vb;
+          {  // key element (token r, channel c)
+            const int i = i0 + e, r = i / D, c = i % D;
+            const int r16 = r & 15, part = r >> 4, s4 = c >> 5, q4 = (c & 31) >> 3, ee = c & 7;
+            const int ln = q4 * 16 + r16, pi = 4 * s4 + (ee >> 1), bit = pi + 16 * (ee & 1);
+            const uint32_t w0 = recl[kRecK / 4 + 4 * ln + part], w1 = recl[kRecK / 4 + 4 * ln + 2 + part];
+            const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+            const float sc = h2f(rl16[kRecSK / 2 + c]), zp = h2f(rl16[kRecZK / 2 + c]);
+            kb = bf16_rne(__fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp));
+          }
+          {  // value element (channel c, token r): channel-major index
+            const int i = i0 + e, c = i / W, r = i % W;
+            const int r16 = c & 15, ct = c >> 4, q4 = r >> 3, ee = r & 7;
+            const int ln = q4 * 16 + r16, part = ct >> 2, pi = 4 * (ct & 3) + (ee >> 1), bit = pi + 16 * (ee & 1);
+            const uint32_t w0 = recl[kRecV / 4 + 4 * ln + part], w1 = recl[kRecV / 4 + 4 * ln + 2 + part];
+            const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+            const int g = c >> 5;
+            const float sc = h2f(rl16[kRecSV / 2 + 4 * r + g]), zp = h2f(rl16[kRecZV / 2 + 4 * r + g]);
+            vb = bf16_rne(__fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp));
+          }
+          if (e & 1) {
+            ko[e >> 1] |= kb << 16;
+            vo[e >> 1] |= vb << 16;
+          } else {
+            ko[e >> 1] = kb;
+            vo[e >> 1] = vb;
+          }
         }
-        {  // value element (channel c, token r): channel-major index i
-          const int c = i / W, r = i % W;
-          const int r16 = c & 15, ct = c >> 4, q4 = r >> 3, e = r & 7;
-          const int ln = q4 * 16 + r16, part = ct >> 2, pi = 4 * (ct & 3) + (e >> 1), bit = pi + 16 * (e & 1);
-          const uint32_t w0 = rec32[kRecV / 4 + 4 * ln + part], w1 = rec32[kRecV / 4 + 4 * ln + 2 + part];
-          const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
-          const int g = c >> 5;
-          const float sc = h2f(rec16[kRecSV / 2 + 4 * r + g]), zp = h2f(rec16[kRecZV / 2 + 4 * r + g]);
-          const float x = __fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp);
-          vd[i] = static_cast<uint16_t>(bf16_rne(x));
-        }
+        *reinterpret_cast<uint4*>(kd + i0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+        *reinterpret_cast<uint4*>(vd + i0) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
       }
+      __syncthreads();  // recl is reused by the block's next job
     }
   }
 }
@@ -859,8 +963,9 @@ hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
   const int nch_f = (c->tw.n_fp + 7) / 8, nch_q = (c->tw.n_q + 7) / 8;
   TierArgs a = tier_args(c);
   hipError_t e;
-  dim3 gm(c->cfg.n_kv_heads, c->cfg.n_layers);
-  tier_merge_kernel<<<gm, 256, 0, c->stream>>>(a, out, nch_f + nch_q);
+  dim3 gm(HG, c->cfg.n_kv_heads, c->cfg.n_layers);
+  const size_t shm = sizeof(float) * 2 * static_cast<size_t>(nch_f + nch_q);
+  tier_merge_kernel<<<gm, 256, shm, c->stream>>>(a, out, nch_f + nch_q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntot = c->tw.n_fp + c->tw.n_q;
@@ -876,7 +981,7 @@ hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp
       a, nw, np, recent_lo, c->cfg.fp_windows, c->cfg.int2_windows, exp_fp, exp_q, forced_dev);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 gx(kTierXferBlocks, c->cfg.n_kv_heads, c->cfg.n_layers);
+  dim3 gx(kTierXferBlocks, c->cfg.n_layers);
   tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a);
   return hipGetLastError();
 }
