@@ -432,8 +432,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   __syncthreads();
 
-  // ---- attention output of layer c -------------------------------------------
-  if (c < L) {
+  // ---- attention output of layer c (after the block's arrival: the
+  // selection does not wait on it) ------------------------------------------------
+  auto write_output = [&]() {
+    if (c >= L) return;
     const int l = c;
     const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * A.S * HG;
     for (int i = tid; i < HG * ns; i += NT) {
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       for (int s = kMergeBatch; s < ns; ++s) o += s_w[h * A.S + s] * pob[s * HG * D + idx];
       A.out[(static_cast<int64_t>(l * Bsz + b) * A.Hq + kvh * HG + h) * D + cc] = o / s_ml[(l * HG + h) * 2 + 1];
     }
-  }
+  };
 
   // ---- probability mass per (layer, slot), then the layer-ordered fold --------
   float myscore = prior;
@@ -529,7 +531,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     s_last = (old == static_cast<unsigned>(A.nblk - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last) {
+    write_output();
+    return;
+  }
 
   // ---- the group's last block ------------------------------------------------
   // Everything it may need is loaded in one batch: the block summaries, the
@@ -541,14 +546,14 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   constexpr int NCH = (64 * LPR + NT - 1) / NT;  // 16-byte row pieces per thread (L <= 64)
   uint4 kpre[NCH], vpre[NCH];
   if (one_over) {
+    // unconditional loads (index clamped into the rows): a conditionally
+    // written array would be placed in scratch and its loads serialised
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int idx = u * NT + tid;
-      if (idx < L * LPR) {
-        const int64_t in = (static_cast<int64_t>((idx / LPR) * Bsz + b) * A.Hkv + kvh) * D + (idx % LPR) * EPL;
-        kpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.k_new) + in);
-        vpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.v_new) + in);
-      }
+      const int idx = min(u * NT + tid, L * LPR - 1);
+      const int64_t in = (static_cast<int64_t>((idx / LPR) * Bsz + b) * A.Hkv + kvh) * D + (idx % LPR) * EPL;
+      kpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.k_new) + in);
+      vpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.v_new) + in);
     }
   }
   const int newpage = A.ptab[static_cast<int64_t>(g) * A.maxpages + (n - 1) / kPageTokens];
@@ -609,8 +614,11 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     A.nextpos[g] = newest + 1;
     A.grpctr[g] = 0u;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (!one_over) {
+    // the full selection below reads the new token's state back
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
 
   int final_n = n, nm = 0;
   if (one_over) {
@@ -642,9 +650,15 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
         if (idx >= L * LPR) continue;
         const int l = idx / LPR, c0 = (idx % LPR) * EPL;
         *reinterpret_cast<uint4*>(kp + kidx(l, bpage, rd, c0, A.P, D)) = kpre[u];
-        const T* ve = reinterpret_cast<const T*>(&vpre[u]);
+        const uint32_t vw[4] = {vpre[u].x, vpre[u].y, vpre[u].z, vpre[u].w};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) vp[vidx(l, bpage, rd, c0 + e, A.P, D)] = ve[e];
+        for (int e = 0; e < EPL; ++e) {
+          // element e of the 16-byte piece (bf16: half words; fp32: words)
+          const uint32_t bits = EPL == 8 ? (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu : vw[e & 3];
+          T x;
+          __builtin_memcpy(&x, &bits, sizeof(T));
+          vp[vidx(l, bpage, rd, c0 + e, A.P, D)] = x;
+        }
       }
     }
   } else if (A.do_select && n > A.B) {
@@ -662,6 +676,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     A.count[g] = final_n;
     A.nmoves[g] = nm;
   }
+  write_output();
 }
 
 // Standalone selection (kvev_evict): one block per group.
