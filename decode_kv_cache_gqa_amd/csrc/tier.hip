@@ -649,11 +649,20 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     }
     __syncthreads();
     const int nc = ncand;
-    // exact rank of each candidate; keys are distinct (window ids)
+    // exact rank of each candidate; keys are distinct (window ids).  Eight
+    // independent partial counts keep eight LDS reads in flight.
     for (int i = tid; i < nc; i += kRouteNT) {
       const unsigned long long ki = keys[i];
+      int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      int j = 0;
+      for (; j + 8 <= nc; j += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) part[u] += keys[j + u] > ki;
+      }
+      for (; j < nc; ++j) part[0] += keys[j] > ki;
       int rank = 0;
-      for (int j = 0; j < nc; ++j) rank += keys[j] > ki;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rank += part[u];
       const int w = static_cast<int>(ki & 0xffffffffu);
       const uint8_t nt = rank < k_f ? 0 : (rank < k_f + k_q ? 1 : 2);
       const uint8_t ot = tl[w];
