@@ -64,15 +64,17 @@ def algorithmic_bytes(w, n_tokens):
 
     K/V of the retained cache read once in every layer, q read, fp32 output
     written, appended K/V written, utility read + written, and the K/V of
-    one compaction move read + written in every layer.
+    one compaction move read + written in every layer, for every sequence
+    of the batch.
     """
-    L, Hkv, Hq, d = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
-    kv = L * Hkv * n_tokens * 2 * d * 2
-    q = L * Hq * d * 2
-    out = L * Hq * d * 4
-    app = L * Hkv * 2 * d * 2
-    state = Hkv * n_tokens * 4 * 2
-    move = L * Hkv * 2 * d * 2 * 2
+    L, Hkv, Hq, d, B = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim, w.batch
+    el = 4 if w.dtype == "f32" else 2
+    kv = B * L * Hkv * n_tokens * 2 * d * el
+    q = B * L * Hq * d * el
+    out = B * L * Hq * d * 4
+    app = B * L * Hkv * 2 * d * el
+    state = B * Hkv * n_tokens * 4 * 2
+    move = B * L * Hkv * 2 * d * el * 2
     return kv, kv + q + out + app + state + move
 
 
@@ -394,7 +396,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic (seeded outlier-channel / heavy-key generator)",
         "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "batch": w.batch,
