@@ -176,6 +176,27 @@ def test_llama8b_32k_full_size_sampled():
     assert st.steps == 6
 
 
+def test_lazy16x8k_full_size_sampled():
+    """The full batched lazy workload (16 sequences, 8,192-token prefill, 32
+    layers, budget 2,048, observations at t = 1, 9, 17, ...) in the
+    benchmark's launch configuration; the oracle follows two sequences' first
+    and last KV heads through the first eviction, the unobserved steps and
+    the observation at t = 9."""
+    w = synth.workload("lazy16x8k")
+    st = _gu().run_token_lockstep(w, 10, sample_seqs=[0, 15], sample_heads=[0, 7], kv_every=5,
+                                  ctx_steps=w.steps, fused=True)
+    assert st.steps == 10
+
+
+def test_scorefree16x8k_full_size_sampled():
+    """The full batched score-free workload (scores observed at t = 1 only,
+    new tokens take the mean) in the benchmark's launch configuration."""
+    w = synth.workload("scorefree16x8k")
+    st = _gu().run_token_lockstep(w, 6, sample_seqs=[7], sample_heads=[3], kv_every=3, ctx_steps=w.steps,
+                                  fused=True)
+    assert st.steps == 6
+
+
 def test_llama8b_32k_full_size_fused_sampled():
     w = synth.workload("llama8b_32k")
     st = _gu().run_token_lockstep(w, 6, sample_heads=[3], kv_every=3, ctx_steps=w.steps, fused=True)
