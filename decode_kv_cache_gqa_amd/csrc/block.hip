@@ -107,6 +107,7 @@ __global__ void blk_open_kernel(BlockArgs A, int n_max) {
 // Merge the attention splits of one (layer, group): per-head global (max,
 // sum) into ml and the normalised output into out.
 // ---------------------------------------------------------------------------
+constexpr int kBlkMergeLoads = 16;
 template <int NT>
 __global__ __launch_bounds__(NT) void blk_merge_kernel(BlockArgs A) {
   const int l = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
@@ -115,15 +116,19 @@ __global__ __launch_bounds__(NT) void blk_merge_kernel(BlockArgs A) {
   extern __shared__ float sh[];
   float* s_w = sh;             // [HG][S] split weights
   float* s_mz = sh + HG * S;   // [HG][2]
+  float2* s_pm = reinterpret_cast<float2*>(s_mz + HG * 2);  // [S][HG] split (max, sum)
   const float2* pm = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * S * HG;
   // splits past the group's own token count were not written this step
   const int ns = (A.count[g] + 1 + kAttnChunk - 1) / kAttnChunk;
+  // the splits' statistics in one batch of loads
+  for (int i = tid; i < ns * HG; i += NT) s_pm[i] = pm[i];
+  __syncthreads();
   if (tid < HG) {
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * HG + tid].x);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, s_pm[s * HG + tid].x);
     float Z = 0.f;
     for (int s = 0; s < ns; ++s) {
-      const float2 v = pm[s * HG + tid];
+      const float2 v = s_pm[s * HG + tid];
       const float w = v.x == -INFINITY ? 0.f : __expf(v.x - M);
       s_w[tid * S + s] = w;
       Z += v.y * w;
@@ -138,7 +143,16 @@ __global__ __launch_bounds__(NT) void blk_merge_kernel(BlockArgs A) {
   for (int idx = tid; idx < HG * D; idx += NT) {
     const int h = idx / D;
     float o = 0.f;
-    for (int s = 0; s < ns; ++s) o += s_w[h * S + s] * po[static_cast<int64_t>(s) * HG * D + idx];
+    // kBlkMergeLoads independent loads per batch, summed in split order
+    for (int s0 = 0; s0 < ns; s0 += kBlkMergeLoads) {
+      float v[kBlkMergeLoads];
+#pragma unroll
+      for (int k = 0; k < kBlkMergeLoads; ++k)
+        v[k] = s0 + k < ns ? po[static_cast<int64_t>(s0 + k) * HG * D + idx] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kBlkMergeLoads; ++k)
+        if (s0 + k < ns) o += s_w[h * S + s0 + k] * v[k];
+    }
     A.out[(static_cast<int64_t>(l * A.batch + b) * A.Hq + kvh * HG) * D + idx] = o / s_mz[h * 2 + 1];
   }
 }
@@ -149,6 +163,7 @@ __global__ __launch_bounds__(NT) void blk_merge_kernel(BlockArgs A) {
 // sequence); thread (slot of 64, quarter of the (layer, KV head) pairs).
 // ---------------------------------------------------------------------------
 constexpr int kMassNT = 256;
+constexpr int kMassLoads = 16;
 __global__ __launch_bounds__(kMassNT) void blk_mass_kernel(BlockArgs A) {
   const int b = blockIdx.y, tid = threadIdx.x;
   const int g0 = b * A.Hkv;
@@ -169,13 +184,27 @@ __global__ __launch_bounds__(kMassNT) void blk_mass_kernel(BlockArgs A) {
   const int slot = e0 * kPageTokens + sl;
   float acc = 0.f;
   if (slot < n) {
-    for (int i = part; i < A.L * A.Hkv; i += 4) {
-      const int l = i / A.Hkv, h = i % A.Hkv;
-      const float4 x = *reinterpret_cast<const float4*>(
-          A.logits + ((static_cast<int64_t>(g0 + h) * A.L + l) * A.lstride + slot) * 4);
-      const float* m = &s_ml[i * 8];
-      acc += __expf(x.x - m[0]) / m[1] + __expf(x.y - m[2]) / m[3] + __expf(x.z - m[4]) / m[5] +
-             __expf(x.w - m[6]) / m[7];
+    // the thread's (layer, KV head) pairs part, part + 4, ... in batches of
+    // kMassLoads independent loads (indices clamped into the pairs; the
+    // clamped ones are not summed), summed in pair order
+    const int np = A.L * A.Hkv;
+    for (int i0 = part; i0 < np; i0 += 4 * kMassLoads) {
+      float4 x[kMassLoads];
+#pragma unroll
+      for (int k = 0; k < kMassLoads; ++k) {
+        const int i = min(i0 + 4 * k, np - 1);
+        const int l = i / A.Hkv, h = i % A.Hkv;
+        x[k] = *reinterpret_cast<const float4*>(
+            A.logits + ((static_cast<int64_t>(g0 + h) * A.L + l) * A.lstride + slot) * 4);
+      }
+#pragma unroll
+      for (int k = 0; k < kMassLoads; ++k) {
+        const int i = i0 + 4 * k;
+        if (i >= np) continue;
+        const float* m = &s_ml[i * 8];
+        acc += __expf(x[k].x - m[0]) / m[1] + __expf(x[k].y - m[2]) / m[3] + __expf(x[k].z - m[4]) / m[5] +
+               __expf(x[k].w - m[6]) / m[7];
+      }
     }
   }
   s_red[part * 64 + sl] = acc;
@@ -441,7 +470,7 @@ hipError_t launch_block_open(kvev_ctx* c, int n_max, int t) {
 hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max) {
   BlockArgs A = block_args(c, out, n_max);
   dim3 grid(c->cfg.n_layers, c->G);
-  const size_t shm = (static_cast<size_t>(c->HG) * A.S + c->HG * 2) * sizeof(float);
+  const size_t shm = (static_cast<size_t>(c->HG) * A.S * 3 + c->HG * 2) * sizeof(float);
   blk_merge_kernel<256><<<grid, 256, shm, c->stream>>>(A);
   return hipGetLastError();
 }
