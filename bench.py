@@ -78,22 +78,25 @@ def algorithmic_bytes(w, n_tokens):
     return kv, kv + q + out + app + state + move
 
 
+CSRC = os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_kernel_traffic_llama8b_32k.md")
-ATTN_SOURCES = [os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc", f) for f in ("attn.hip", "common.h")]
+ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "common.h")]
+TIER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tier_attn_kernel_traffic_qevict131k.md")
+TIER_SOURCES = [os.path.join(CSRC, f) for f in ("tier.hip", "common.h")]
 
 
-def measured_traffic():
-    """HBM bytes per attention launch from the committed counter profile,
-    or None when the kernel source changed after the counters were taken."""
+def measured_traffic(profile=TRAFFIC_PROFILE, sources=ATTN_SOURCES):
+    """HBM bytes per attention launch from a committed counter profile, or
+    None when the kernel source changed after the counters were taken."""
     import hashlib
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(profile).read()
     except OSError:
         return None
     vals = dict(line.split(": ", 1) for line in text.splitlines()
                 if line.startswith(("traffic_bytes_per_launch: ", "kernel_source_sha256: ")))
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in sources:
         h.update(open(f, "rb").read())
     if vals.get("kernel_source_sha256", "").strip() != h.hexdigest():
         return None
@@ -318,7 +321,8 @@ def run_tier(args, w):
         "roofline": {
             "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": None, "kernel": "tier_attn_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+            "traffic": measured_traffic(TIER_TRAFFIC_PROFILE, TIER_SOURCES), "kernel": "tier_attn_kernel",
+            "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
     if not args.no_cpu_baseline:
