@@ -123,3 +123,12 @@ def test_full_size_lrfu64_sampled():
     b = int(np.argmin(w.prefill_lens))
     st = _gu().run_block_lockstep(w, 3, sample_seqs=[b], readmit=False, kv_every=3)
     assert st.steps == 3
+
+
+def test_block_max_positions_sampled():
+    """One sequence of 65,520 tokens (4,095 blocks, 20% budget of 819) stepped
+    toward the mode's 65,536-position bound, 4 layers, oracle on the whole
+    sequence."""
+    w = synth.workload("lrfu64").scaled(n_layers=4, prefill_lens=(65520,))
+    st = _gu().run_block_lockstep(w, 4, readmit=False, kv_every=4)
+    assert st.steps == 4

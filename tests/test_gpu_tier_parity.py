@@ -68,3 +68,13 @@ def test_qevict131k_full_size_sampled():
     w = synth.workload("qevict131k")
     st = _gu().run_tier_lockstep(w, 34, sample_layers=[0, 31], kv_every=16, ledger_every=16)
     assert st.steps == 34 and st.ledger_checks > 0
+
+
+def test_tier_max_capacity_sampled():
+    """A 196,600-token prefill stepped to the mode's 196,608-position capacity
+    (6,144 windows per layer, the routing kernel's LDS bound), 4 layers; the
+    oracle holds layer 3 through the first routing event over about 6,140
+    candidates and every step up to the last position."""
+    w = synth.workload("qevict131k").scaled(n_layers=4, prefill_lens=(196600,))
+    st = _gu().run_tier_lockstep(w, 7, sample_layers=[3], kv_every=7, ledger_every=7)
+    assert st.steps == 7
