@@ -649,8 +649,9 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     }
     __syncthreads();
     const int nc = ncand;
-    // exact rank of each candidate; keys are distinct (window ids).  Eight
-    // independent partial counts keep eight LDS reads in flight.
+    // exact rank of each candidate; keys are distinct (window ids).  Every
+    // lane of a wave reads the same key (an LDS broadcast); eight
+    // independent partial counts keep eight reads in flight.
     for (int i = tid; i < nc; i += kRouteNT) {
       const unsigned long long ki = keys[i];
       int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -688,38 +689,51 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     }
   }
   __syncthreads();
-  // stable compaction of the two lists (ballot + prefix sum per 1024 windows)
-  if (tid == 0) {
-    base[0] = 0;
-    base[1] = 0;
+  // stable compaction of the two lists: thread tid owns the consecutive
+  // windows [tid * E, tid * E + E); one block-wide exclusive scan of the
+  // per-thread counts gives each thread its offsets in both lists
+  const int E = (nw + kRouteNT - 1) / kRouteNT;
+  int cF = 0, cQ = 0;
+  for (int e = 0; e < E; ++e) {
+    const int w = tid * E + e;
+    if (w < nw) {
+      cF += tl[w] == 0;
+      cQ += tl[w] == 1;
+    }
+  }
+  int xF = cF, xQ = cQ;  // inclusive scan within the wave
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int yF = __shfl_up(xF, o, kWave), yQ = __shfl_up(xQ, o, kWave);
+    if (lane >= o) {
+      xF += yF;
+      xQ += yQ;
+    }
+  }
+  if (lane == kWave - 1) {
+    wsum[0][wv] = xF;
+    wsum[1][wv] = xQ;
   }
   __syncthreads();
-  for (int w0 = 0; w0 < nw; w0 += kRouteNT) {
-    const int w = w0 + tid;
-    const bool isF = w < nw && tl[w] == 0;
-    const bool isQ = w < nw && tl[w] == 1;
-    const unsigned long long bF = __ballot(isF), bQ = __ballot(isQ);
-    const unsigned long long below = (1ull << lane) - 1ull;
-    if (lane == 0) {
-      wsum[0][wv] = __popcll(bF);
-      wsum[1][wv] = __popcll(bQ);
-    }
-    __syncthreads();
-    int offF = base[0] + __popcll(bF & below), offQ = base[1] + __popcll(bQ & below);
-    for (int u = 0; u < wv; ++u) {
+  int offF = xF - cF, offQ = xQ - cQ, totF = 0, totQ = 0;
+  for (int u = 0; u < kRouteNT / kWave; ++u) {
+    if (u < wv) {
       offF += wsum[0][u];
       offQ += wsum[1][u];
     }
-    if (isF) A.fplist[lw0 + offF] = w;
-    if (isQ) A.qlist[lw0 + offQ] = w;
-    __syncthreads();
-    if (tid == 0) {
-      for (int u = 0; u < kRouteNT / kWave; ++u) {
-        base[0] += wsum[0][u];
-        base[1] += wsum[1][u];
-      }
+    totF += wsum[0][u];
+    totQ += wsum[1][u];
+  }
+  for (int e = 0; e < E; ++e) {
+    const int w = tid * E + e;
+    if (w < nw) {
+      if (tl[w] == 0) A.fplist[lw0 + offF++] = w;
+      else if (tl[w] == 1) A.qlist[lw0 + offQ++] = w;
     }
-    __syncthreads();
+  }
+  if (tid == 0) {
+    base[0] = totF;
+    base[1] = totQ;
   }
   for (int w = tid; w < nw; w += kRouteNT) {
     A.tier[lw0 + w] = tl[w];
