@@ -39,6 +39,8 @@ __all__ = [
     "tier_capacities", "route_tiers", "int2_quantize", "int2_dequantize",
     "TokenModeOracle", "region_decay_rates", "block_survival", "block_priority",
     "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
+    "vnorm_weights", "normalized_entropy", "scored_mass", "SCORERS",
+    "PooledTokenOracle",
 ]
 
 
@@ -159,6 +161,73 @@ def group_mass(p):
     scale, invisible to ranking per [InertiaKV] Corollary 2).
     """
     return np.asarray(p, dtype=np.float64).sum(axis=0)
+
+
+def vnorm_weights(V):
+    """Mean-normalised l2 norms of the value states of the cached tokens.
+
+    [InertiaKV] §5.1 and App. E: VNorm multiplies each head's
+    attention on token i by ||v_i|| divided by the mean of ||v_j|| over the
+    tokens the head attends to.  ``V``: [n, d] of one KV head at one layer.
+    Reading: when every value row is zero the weights are 1 (the scorer
+    falls back to plain attention) instead of 0/0.
+    """
+    V = np.asarray(V, dtype=np.float64)
+    norms = np.sqrt((V * V).sum(axis=1))
+    mean = norms.mean()
+    if mean == 0.0:
+        return np.ones_like(norms)
+    return norms / mean
+
+
+def normalized_entropy(p):
+    """Shannon entropy of each head's attention row, divided by ln(n).
+
+    [InertiaKV] §5.1 and App. E: entropy weighting multiplies a layer's
+    contribution by the normalised entropy of its attention distribution.
+    ``p``: [H, n].  Returns [H] in [0, 1]; 0 log 0 = 0.  Reading: with a
+    single token (ln 1 = 0) the weight is 1.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    n = p.shape[1]
+    if n < 2:
+        return np.ones(p.shape[0])
+    t = np.zeros_like(p)
+    nz = p > 0
+    t[nz] = -p[nz] * np.log(p[nz])
+    return t.sum(axis=1) / math.log(n)
+
+
+SCORERS = ("attention", "vnorm", "entropy", "vnorm+entropy")
+
+
+def scored_mass(p, V, scorer="attention"):
+    """Per-token observation of one layer for a state fed by the heads ``p``.
+
+    ``p``: [H, n] probabilities of the heads pooled into the state (one KV
+    head's query group), ``V``: [n, d] that KV head's value states.
+
+    * "attention": the group sum of probabilities (``group_mass``);
+    * "vnorm": each head's probability times ``vnorm_weights(V)`` before the
+      group sum;
+    * "entropy": the group sum times one per-layer scalar, the mean over the
+      pooled heads of ``normalized_entropy`` (reading: the page names one
+      scalar per layer and does not say how heads combine; the mean keeps it
+      in [0, 1]);
+    * "vnorm+entropy": both factors.
+    Both modifications act on the step's observation, before the temporal
+    fold ([InertiaKV] §5.1).
+    """
+    if scorer not in SCORERS:
+        raise ValueError(scorer)
+    p = np.asarray(p, dtype=np.float64)
+    if "vnorm" in scorer:
+        G = (p * vnorm_weights(V)[None, :]).sum(axis=0)
+    else:
+        G = group_mass(p)
+    if "entropy" in scorer:
+        G = G * normalized_entropy(p).mean()
+    return G
 
 
 # ---------------------------------------------------------------------------
@@ -358,6 +427,7 @@ class TokenModeOracle:
     * Eviction happens once per step after all layers, whenever the group
       holds more than ``budget`` tokens, including non-refresh steps with
       the stale utility ([InertiaKV] App. E "Eviction on non-refresh steps").
+    * ``scorer``: the observation folded per layer, see ``scored_mass``.
     """
     n_layers: int
     n_q_heads: int
@@ -371,6 +441,7 @@ class TokenModeOracle:
     n_sink: int = 0
     n_recent: int = 0
     capacity: int = 0
+    scorer: str = "attention"
     groups: dict = field(default_factory=dict)
     prefill_len: dict = field(default_factory=dict)
     last_G: dict = field(default_factory=dict)
@@ -454,7 +525,7 @@ class TokenModeOracle:
                                                g.K[l, :g.n], g.V[l, :g.n])
                     out[l, bi, h * Hg:(h + 1) * Hg] = o
                     if refresh:
-                        G = group_mass(p)
+                        G = scored_mass(p, g.V[l, :g.n], self.scorer)
                         self.last_G[(l, seq, h)] = G
                         g.m[:g.n] = layer_fold(g.m[:g.n], [G], self.alpha_new,
                                                self.policy)
@@ -483,6 +554,150 @@ class TokenModeOracle:
     def positions(self, seq, h):
         g = self.groups[(seq, h)]
         return g.pos[:g.n].copy()
+
+
+class _SeqState:
+    """State of one sequence in the pooled mode, in slot order."""
+
+    def __init__(self, L, Hkv, cap, d):
+        self.K = np.zeros((L, Hkv, cap, d), np.float32)
+        self.V = np.zeros((L, Hkv, cap, d), np.float32)
+        self.pos = np.zeros(cap, np.int64)
+        self.m = np.zeros(cap, np.float64)
+        self.n = 0
+
+
+@dataclass
+class PooledTokenOracle:
+    """One utility per (sequence, position), pooled over every query head.
+
+    [InertiaKV] §3.1 Eq.1: the step's score of token i is the mean over all
+    H attention heads of their probability on i; App. E: for GQA each KV
+    head's attention serves its query-head group before the pooling.  One
+    retained set per sequence: every KV head at every layer holds the same
+    positions, in the same slots, so selection and compaction act on all of
+    them together.  Aggregation, refresh cadence, new-token rule, protection
+    and eviction are those of ``TokenModeOracle``.
+
+    Scorers ([InertiaKV] §5.1, App. E): "vnorm" weights each head's
+    probabilities by the VNorm weights of its own KV head's values before the
+    mean; "entropy" multiplies the layer's pooled score by the mean over all
+    H heads of their normalised entropy.
+    """
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    budget: int
+    alpha_new: float
+    policy: str = "ema"
+    refresh_interval: int = 1
+    score_free: bool = False
+    n_sink: int = 0
+    n_recent: int = 0
+    capacity: int = 0
+    scorer: str = "attention"
+    seqs: dict = field(default_factory=dict)
+    prefill_len: dict = field(default_factory=dict)
+    last_G: dict = field(default_factory=dict)
+
+    @property
+    def group_size(self):
+        return self.n_q_heads // self.n_kv_heads
+
+    def prefill(self, seq, K, V):
+        """``K``, ``V``: [L, Hkv, n, d]; positions 0..n-1, utility 0."""
+        K = np.asarray(K, dtype=np.float32)
+        V = np.asarray(V, dtype=np.float32)
+        L, Hkv, n, d = K.shape
+        st = _SeqState(L, Hkv, max(self.capacity, n + 1), d)
+        st.K[:, :, :n] = K
+        st.V[:, :, :n] = V
+        st.pos[:n] = np.arange(n)
+        st.n = n
+        self.seqs[seq] = st
+        self.prefill_len[seq] = n
+
+    def is_refresh(self, t):
+        if self.score_free:
+            return t == 1
+        return (t - 1) % self.refresh_interval == 0
+
+    def _grow(self, st):
+        if st.n < st.K.shape[2]:
+            return
+        extra = max(64, st.K.shape[2] // 4)
+        pad = lambda a: np.concatenate(
+            [a, np.zeros(a.shape[:2] + (extra,) + a.shape[3:], a.dtype)], axis=2)
+        st.K, st.V = pad(st.K), pad(st.V)
+        st.pos = np.concatenate([st.pos, np.zeros(extra, np.int64)])
+        st.m = np.concatenate([st.m, np.zeros(extra, np.float64)])
+
+    def decode_step(self, t, q, k_new, v_new, seqs):
+        """Same arguments and result as ``TokenModeOracle.decode_step``."""
+        if self.scorer not in SCORERS:
+            raise ValueError(self.scorer)
+        q = np.asarray(q, dtype=np.float32)
+        k_new = np.asarray(k_new, dtype=np.float32)
+        v_new = np.asarray(v_new, dtype=np.float32)
+        refresh = self.is_refresh(t)
+        Hg, H = self.group_size, self.n_q_heads
+        for bi, seq in enumerate(seqs):
+            st = self.seqs[seq]
+            init = 0.0 if refresh else float(st.m[:st.n].mean())
+            self._grow(st)
+            st.K[:, :, st.n] = k_new[:, bi]
+            st.V[:, :, st.n] = v_new[:, bi]
+            st.pos[st.n] = self.prefill_len[seq] + t - 1
+            st.m[st.n] = init
+            st.n += 1
+        out = np.zeros((self.n_layers, len(seqs), H, self.head_dim))
+        self.last_G = {}
+        for l in range(self.n_layers):
+            for bi, seq in enumerate(seqs):
+                st = self.seqs[seq]
+                n = st.n
+                pooled = np.zeros(n)
+                ent = []
+                for h in range(self.n_kv_heads):
+                    Vh = st.V[l, h, :n]
+                    o, p, _ = decode_attention(q[l, bi, h * Hg:(h + 1) * Hg], st.K[l, h, :n], Vh)
+                    out[l, bi, h * Hg:(h + 1) * Hg] = o
+                    if "vnorm" in self.scorer:
+                        pooled += (p * vnorm_weights(Vh)[None, :]).sum(axis=0)
+                    else:
+                        pooled += p.sum(axis=0)
+                    ent.extend(normalized_entropy(p).tolist())
+                G = pooled / H
+                if "entropy" in self.scorer:
+                    G = G * float(np.mean(ent))
+                if refresh:
+                    self.last_G[(l, seq)] = G
+                    st.m[:n] = layer_fold(st.m[:n], [G], self.alpha_new, self.policy)
+        return out
+
+    def evict(self, budget=None):
+        """Select and compact every sequence that exceeds the budget; the
+        moves apply to every KV head and layer."""
+        B = self.budget if budget is None else budget
+        for st in self.seqs.values():
+            if st.n <= B:
+                continue
+            keep = select_keep(st.m[:st.n], st.pos[:st.n], B, self.n_sink, self.n_recent)
+            for src, dst in hole_fill_moves(keep, B):
+                st.K[:, :, dst] = st.K[:, :, src]
+                st.V[:, :, dst] = st.V[:, :, src]
+                st.pos[dst] = st.pos[src]
+                st.m[dst] = st.m[src]
+            st.n = B
+
+    def scores(self, seq):
+        st = self.seqs[seq]
+        return st.m[:st.n].copy()
+
+    def positions(self, seq):
+        st = self.seqs[seq]
+        return st.pos[:st.n].copy()
 
 
 # ---------------------------------------------------------------------------
