@@ -41,7 +41,7 @@ void free_all(kvev_ctx* c) {
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
                   d.grpctr, d.blk_key, d.blk_slot, d.blk_page, d.blk_sum, d.btab, d.nres,
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
-                  d.rd_ids};
+                  d.rd_ids, d.part_u, d.vnorm, d.part_vn};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -142,7 +142,17 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.n_layers < 1 || f.n_q_heads < 1 || f.n_kv_heads < 1 || f.batch < 1)
     return bad("n_layers, n_q_heads, n_kv_heads and batch must be >= 1");
   if (f.n_q_heads % f.n_kv_heads != 0) return bad("n_q_heads must be a multiple of n_kv_heads");
-  if (f.n_q_heads / f.n_kv_heads != 4) return bad("query group size must be 4");
+  const int hg = f.n_q_heads / f.n_kv_heads;
+  if (hg < 1 || hg > kMaxGroupSize) return bad("query group size must be 1..8");
+  if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) && hg != 4)
+    return bad("block and tiered modes: query group size must be 4");
+  if (f.scorer & ~(KVEV_SCORE_VNORM | KVEV_SCORE_ENTROPY)) return bad("unknown scorer bits");
+  if (f.granularity != KVEV_PER_KV_HEAD && f.granularity != KVEV_PER_SEQUENCE)
+    return bad("unknown granularity");
+  if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
+      (f.scorer != 0 || f.granularity != KVEV_PER_KV_HEAD))
+    return bad("scorer variants and granularity apply to the token policies only");
+  if (f.granularity != KVEV_PER_KV_HEAD) return bad("per-sequence granularity is not available");
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
   if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
@@ -189,6 +199,13 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.n_sink + f.n_recent > f.budget) return bad("n_sink + n_recent exceeds the budget");
   if (f.max_tokens < 2 || f.max_tokens > (1ll << 30)) return bad("max_tokens out of range");
   if (f.n_layers > 64) return bad("n_layers must be <= 64");
+  {
+    // the post kernel stages per-layer statistics and one layer's split
+    // weights in LDS: (3 L HG + HG S + 65 L) floats must fit 64 KiB
+    const int64_t S = (f.max_tokens + kAttnChunk - 1) / kAttnChunk;
+    const int64_t lds = (3ll * f.n_layers * hg + hg * S + 65ll * f.n_layers) * 4;
+    if (!block && lds > 65536) return bad("max_tokens too large for this layer count and group size");
+  }
 
   kvev_ctx* c = new (std::nothrow) kvev_ctx();
   if (!c) return bad("out of host memory");
@@ -241,6 +258,11 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.part_ml, static_cast<size_t>(L) * G * c->max_splits * HG * 2));
   A(dalloc(&d.part_o, static_cast<size_t>(L) * G * c->max_splits * HG * D));
   A(dalloc(&d.ml, static_cast<size_t>(L) * G * HG * 2));
+  if (f.scorer & KVEV_SCORE_ENTROPY) A(dalloc(&d.part_u, static_cast<size_t>(L) * G * c->max_splits * HG));
+  if (f.scorer & KVEV_SCORE_VNORM) {
+    A(dalloc(&d.vnorm, static_cast<size_t>(G) * L * ((c->cap + 15) / 16 * 16)));
+    A(dalloc(&d.part_vn, static_cast<size_t>(L) * G * c->max_splits));
+  }
   A(dalloc(&d.mv_src, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.mv_dst, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.nmoves, G));

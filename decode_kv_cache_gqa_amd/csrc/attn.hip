@@ -39,34 +39,47 @@ __device__ __forceinline__ void put16(uint4& r, int e, uint32_t x) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16, head_dim 128, group of 4 query heads: q.K^T and p.V on the matrix
-// cores (v_mfma_f32_16x16x32_bf16), 64 slots (4 pages) per wave.
-//   q.K^T: A = the 4 query rows (rows 4..15 zero), B = K^T; lane (r16, q4)
-//     loads slot r16 of a page, channels 32*s + 8*q4 .. +8 (k-step s);
-//     lane r16 of row 0 receives the 4 heads' logits of slot r16.
-//   p.V:   A = P (4 rows), B = V; 32 slots (2 pages) per k-step.  Lane
+// bf16, head_dim 128, group of HG <= 8 query heads: q.K^T and p.V on the
+// matrix cores (v_mfma_f32_16x16x32_bf16), 64 slots (4 pages) per wave.
+//   q.K^T: A = the HG query rows (rows HG..15 zero), B = K^T; lane (r16, q4)
+//     loads slot r16 of a page, channels 32*s + 8*q4 .. +8 (k-step s); the
+//     lanes of quarter q4 receive rows 4*q4 .. 4*q4+3, i.e. the logits of
+//     heads 4*q4 + i for slot r16.
+//   p.V:   A = P (HG rows), B = V; 32 slots (2 pages) per k-step.  Lane
 //     (r16, q4) loads channel 16*ct + r16, slots 8*(q4 & 1) .. +8 of page
 //     2k + (q4 >> 1): 16 contiguous bytes of the channel-major V page.  P is
 //     split into bf16 hi + lo parts (two products), so the rounding of P is
 //     at most 2^-18 relative.
 // Every load of the wave is issued before the first use.
+// Optional outputs for the scorer variants ("What Matters ...", section 5.1
+// and appendix E):
+//   part_u  [L][G][S][HG]: sum over the split's slots of e^{s - m}(m - s),
+//           m the split maximum (the entropy of a head's distribution is
+//           ln Z + (sum p (M - s)), assembled from these after the merge);
+//   vnorm   [G][L][lstride]: the l2 norm of every slot's value row, and
+//   part_vn [L][G][S]: its sum over the split's slots.
 // ---------------------------------------------------------------------------
-template <int NW>
+template <int NW, int HG, bool SC>
 __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const int* __restrict__ ptab, const int* __restrict__ count, float* __restrict__ logits,
-    float* __restrict__ part_ml, float* __restrict__ part_o, int L, int G, int Hkv, int Hq,
+    float* __restrict__ part_ml, float* __restrict__ part_o, float* __restrict__ part_u,
+    float* __restrict__ vnorm, float* __restrict__ part_vn, int L, int G, int Hkv, int Hq,
     int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits) {
-  constexpr int D = 128, HG = 4, NG = 4, WT = NG * 16;
+  static_assert(HG >= 1 && HG <= 8, "group size");
+  constexpr int D = 128, NG = 4, WT = NG * 16;
   __shared__ __align__(16) float p_lds[NW][HG][WT];
   __shared__ __align__(16) float wstat[NW][HG][2];
+  __shared__ float wstat_u[SC ? NW : 1][HG];
+  __shared__ float wvn[NW];
   __shared__ __align__(16) float o_lds[NW][HG][D];
 
   const int split = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform: keep it scalar
   const int r16 = lane & 15, q4 = lane >> 4;
+  const int h0 = 4 * q4;  // first head of this lane's output rows
   const int t0 = split * NW * WT, wt0 = t0 + wave * WT;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
   // page indices do not depend on the count: load them alongside it
@@ -78,10 +91,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
   const int B = G / Hkv, b = g / Hkv, kvh = g % Hkv;
   const int tnew = n - 1;
   const int64_t new_off = (static_cast<int64_t>(l * B + b) * Hkv + kvh) * D;
+  // SC: compiled with the scorer variants' outputs (present when non-null)
+  const bool ent = SC && part_u != nullptr, vn = SC && vnorm != nullptr;
 
   bf16x8 qa[4];
   {
-    const uint16_t* qp = q + (static_cast<int64_t>(l * B + b) * Hq + kvh * HG + (r16 & 3)) * D + 8 * q4;
+    const uint16_t* qp = q + (static_cast<int64_t>(l * B + b) * Hq + kvh * HG + min(r16, HG - 1)) * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 r = *reinterpret_cast<const uint4*>(qp + 32 * s);
@@ -137,50 +152,97 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     }
   }
 
-  // q.K^T
-  float sv[NG][HG];
+  // l2 norms of the value rows (VNorm scorer): lane (r16, q4) holds 8 slots
+  // of 8 channels per k-step; the row sums over r16 give each slot's norm
+  float vnsum = 0.f;
+  if (vn) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float ss[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss[e] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const uint32_t w[4] = {vr[k][ct].x, vr[k][ct].y, vr[k][ct].z, vr[k][ct].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+          ss[e] += x * x;
+        }
+      }
+      float mine = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = row16_sum(ss[e]);
+        mine = r16 == e ? t : mine;
+      }
+      const int tk = wt0 + 16 * (2 * k + (q4 >> 1)) + 8 * (q4 & 1) + r16;
+      if (r16 < 8 && tk < n) {
+        const float nv = sqrtf(mine);
+        vnorm[(static_cast<int64_t>(g) * L + l) * lstride + tk] = nv;
+        vnsum += nv;
+      }
+    }
+    vnsum = wave_sum(vnsum);
+    if (lane == 0) wvn[wave] = vnsum;
+  }
+
+  // q.K^T: sv[j][i] is the logit of head h0 + i for slot 16 j + r16
+  float sv[NG][4];
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(kr[j][s]), acc, 0, 0, 0);
     const int tk = wt0 + 16 * j + r16;
-    const bool valid = q4 == 0 && tk < n;
 #pragma unroll
-    for (int h = 0; h < HG; ++h) sv[j][h] = valid ? acc[h] * scale : -INFINITY;
-    if (valid && write_logits)
-      *reinterpret_cast<float4*>(logits + ((static_cast<int64_t>(g) * L + l) * lstride + tk) * HG) =
-          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
+    for (int i = 0; i < 4; ++i) sv[j][i] = (h0 + i < HG && tk < n) ? acc[i] * scale : -INFINITY;
+    if (h0 < HG && tk < n && write_logits) {
+      float* dst = logits + ((static_cast<int64_t>(g) * L + l) * lstride + tk) * HG + h0;
+      if constexpr (HG % 4 == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (h0 + i < HG) dst[i] = sv[j][i];
+      }
+    }
   }
 
-  // per-head max and sum over the wave's slots (all live logits sit in lanes 0..15)
-  float mh[HG], lh[HG];
+  // per-head max and sum over the wave's slots (a head's logits sit in the
+  // 16 lanes of one quarter)
+  float mh[4], lh[4], uh[4];
 #pragma unroll
-  for (int h = 0; h < HG; ++h) {
-    float m = sv[0][h];
+  for (int i = 0; i < 4; ++i) {
+    float m = sv[0][i];
 #pragma unroll
-    for (int j = 1; j < NG; ++j) m = fmaxf(m, sv[j][h]);
-    mh[h] = row16_max(m);
-    float sum = 0.f;
+    for (int j = 1; j < NG; ++j) m = fmaxf(m, sv[j][i]);
+    mh[i] = row16_max(m);
+    float sum = 0.f, u = 0.f;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const float p = mh[h] == -INFINITY ? 0.f : __expf(sv[j][h] - mh[h]);
-      sv[j][h] = p;
+      const float p = mh[i] == -INFINITY ? 0.f : __expf(sv[j][i] - mh[i]);
+      if (ent) u += p > 0.f ? p * (mh[i] - sv[j][i]) : 0.f;  // masked slots: p = 0
+      sv[j][i] = p;
       sum += p;
     }
-    lh[h] = row16_sum(sum);
+    lh[i] = row16_sum(sum);
+    uh[i] = ent ? row16_sum(u) : 0.f;
   }
-  if (q4 == 0) {
+  if (h0 < HG) {
 #pragma unroll
     for (int j = 0; j < NG; ++j)
 #pragma unroll
-      for (int h = 0; h < HG; ++h) p_lds[wave][h][16 * j + r16] = sv[j][h];
-  }
-  if (lane == 0) {
+      for (int i = 0; i < 4; ++i)
+        if (h0 + i < HG) p_lds[wave][h0 + i][16 * j + r16] = sv[j][i];
+    if (r16 == 0) {
 #pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      wstat[wave][h][0] = mh[h];
-      wstat[wave][h][1] = lh[h];
+      for (int i = 0; i < 4; ++i) {
+        if (h0 + i >= HG) continue;
+        wstat[wave][h0 + i][0] = mh[i];
+        wstat[wave][h0 + i][1] = lh[i];
+        if (ent) wstat_u[wave][h0 + i] = uh[i];
+      }
     }
   }
   __syncthreads();
@@ -191,8 +253,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
   for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const float4 a = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
-    const float4 c = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
+    const float* prow = &p_lds[wave][min(r16, HG - 1)][32 * k + 8 * q4];
+    const float4 a = *reinterpret_cast<const float4*>(prow);
+    const float4 c = *reinterpret_cast<const float4*>(prow + 4);
     const float pv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
     uint32_t h16[8], l16[8];
 #pragma unroll
@@ -212,11 +275,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
       oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vb, oacc[ct], 0, 0, 0);
     }
   }
-  if (q4 == 0) {
+  if (h0 < HG) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int h = 0; h < HG; ++h) o_lds[wave][h][16 * ct + r16] = oacc[ct][h];
+      for (int i = 0; i < 4; ++i)
+        if (h0 + i < HG) o_lds[wave][h0 + i][16 * ct + r16] = oacc[ct][i];
   }
   __syncthreads();
 
@@ -227,18 +291,28 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, wstat[w][h][0]);
-    float o = 0.f, Z = 0.f;
+    float o = 0.f, Z = 0.f, U = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = wstat[w][h][0] == -INFINITY ? 0.f : __expf(wstat[w][h][0] - M);
+      const float mw = wstat[w][h][0];
+      const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
       o += f * o_lds[w][h][c];
       Z += f * wstat[w][h][1];
+      // sum p (M - s) = sum_w f (u_w + (M - m_w) l_w)
+      if (ent && mw != -INFINITY) U += f * (wstat_u[w][h] + (M - mw) * wstat[w][h][1]);
     }
     part_o[pbase * HG * D + idx] = o;
     if (c == 0) {
       part_ml[(pbase * HG + h) * 2 + 0] = M;
       part_ml[(pbase * HG + h) * 2 + 1] = Z;
+      if (ent) part_u[pbase * HG + h] = U;
     }
+  }
+  if (vn && tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) t += wvn[w];
+    part_vn[pbase] = t;
   }
 }
 
@@ -248,12 +322,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
 // adds; p.V reads the channel-major V pages element-wise.  Used for the
 // fp32 cache and for head_dim 64.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int HG, int NT, int CT>
+template <typename T, int D, int HG, int NT, int CT, bool SC>
 __global__ __launch_bounds__(NT) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ ptab,
     const int* __restrict__ count, float* __restrict__ logits, float* __restrict__ part_ml,
-    float* __restrict__ part_o, int L, int G, int Hkv, int Hq, int64_t P, int maxpages,
+    float* __restrict__ part_o, float* __restrict__ part_u, float* __restrict__ vnorm,
+    float* __restrict__ part_vn, int L, int G, int Hkv, int Hq, int64_t P, int maxpages,
     int64_t lstride, int S, float scale, int write_logits) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPT = D / EPL;
@@ -264,7 +339,10 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
 
   __shared__ float s_lds[CT][HG];
   __shared__ float red[NW][HG];
+  __shared__ float red_u[NW][HG];
+  __shared__ float red_vn[NW];
   __shared__ float o_lds[NW][HG][D];
+  const bool ent = SC && part_u != nullptr, vn = SC && vnorm != nullptr;
 
   const int split = blockIdx.x, g = blockIdx.y, l = blockIdx.z;
   const int n = count[g] + 1;
@@ -353,25 +431,38 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
     sm[h] = 0.f;
   }
   __syncthreads();
+  float uu[HG];
+#pragma unroll
+  for (int h = 0; h < HG; ++h) uu[h] = 0.f;
   for (int i = tid; i < cnt; i += NT)
 #pragma unroll
     for (int h = 0; h < HG; ++h) {
-      const float p = __expf(s_lds[i][h] - mx[h]);
+      const float s = s_lds[i][h];
+      const float p = __expf(s - mx[h]);
       s_lds[i][h] = p;
       sm[h] += p;
+      if (ent) uu[h] += p * (mx[h] - s);
     }
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
     const float w = wave_sum(sm[h]);
     if (lane == 0) red[wave][h] = w;
+    if (ent) {
+      const float u = wave_sum(uu[h]);
+      if (lane == 0) red_u[wave][h] = u;
+    }
   }
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < HG; ++h) {
-    float w = 0.f;
+    float w = 0.f, u = 0.f;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) w += red[k][h];
+    for (int k = 0; k < NW; ++k) {
+      w += red[k][h];
+      if (ent) u += red_u[k][h];
+    }
     sm[h] = w;
+    uu[h] = u;
   }
 
   float acc[HG][EPL];
@@ -379,8 +470,10 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   for (int h = 0; h < HG; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  float vnsum = 0.f;
   for (int base = wave * TPW; base < cnt; base += NW * TPW) {
     const int i = base + tslot;
+    float ss = 0.f;
     if (i < cnt) {
       const int t = t0 + i;
       const int page = pt[t / kPageTokens], r = t % kPageTokens;
@@ -402,7 +495,22 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];
       }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss += vf[e] * vf[e];
     }
+    if (vn) {  // the row's squared norm over its LPT lanes (wave-uniform loop)
+#pragma unroll
+      for (int o = LPT / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+      if (i < cnt && sub == 0) {
+        const float nv = sqrtf(ss);
+        vnorm[(static_cast<int64_t>(g) * L + l) * lstride + t0 + i] = nv;
+        vnsum += nv;
+      }
+    }
+  }
+  if (vn) {
+    vnsum = wave_sum(vnsum);
+    if (lane == 0) red_vn[wave] = vnsum;
   }
 #pragma unroll
   for (int o = LPT; o < kWave; o <<= 1)
@@ -426,6 +534,13 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   if (tid < HG) {
     part_ml[(pbase * HG + tid) * 2 + 0] = mx[tid];
     part_ml[(pbase * HG + tid) * 2 + 1] = sm[tid];
+    if (ent) part_u[pbase * HG + tid] = uu[tid];
+  }
+  if (vn && tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) t += red_vn[k];
+    part_vn[pbase] = t;
   }
 }
 
@@ -433,18 +548,29 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
 constexpr int kMfmaNW = 4;
 static_assert(kMfmaNW * 64 == kAttnChunk, "split size");
 
-template <typename T, int D>
+template <typename T, int D, int HG>
 static hipError_t attention_valu(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                                  int n_max, int write_logits) {
   constexpr int NT = 256;
   const auto& cf = c->cfg;
   const int splits = (n_max + kAttnChunk - 1) / kAttnChunk;
   dim3 grid(splits, c->G, cf.n_layers);
-  attn_valu_kernel<T, D, 4, NT, kAttnChunk><<<grid, NT, 0, c->stream>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k_new), static_cast<const T*>(v_new),
-      static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.count,
-      c->d.logits, c->d.part_ml, c->d.part_o, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
-      c->maxpages, c->lstride, splits, 1.0f / sqrtf(static_cast<float>(D)), write_logits);
+  // the scorer variants' outputs are needed only with the logits
+  float* pu = write_logits ? c->d.part_u : nullptr;
+  float* vn = write_logits ? c->d.vnorm : nullptr;
+  float* pvn = write_logits ? c->d.part_vn : nullptr;
+  auto launch = [&](auto kern) {
+    kern<<<grid, NT, 0, c->stream>>>(
+        static_cast<const T*>(q), static_cast<const T*>(k_new), static_cast<const T*>(v_new),
+        static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.count,
+        c->d.logits, c->d.part_ml, c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads,
+        cf.n_q_heads, c->P, c->maxpages, c->lstride, splits, 1.0f / sqrtf(static_cast<float>(D)),
+        write_logits);
+  };
+  if (pu || vn)
+    launch(attn_valu_kernel<T, D, HG, NT, kAttnChunk, true>);
+  else
+    launch(attn_valu_kernel<T, D, HG, NT, kAttnChunk, false>);
   return hipGetLastError();
 }
 
@@ -452,21 +578,32 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
                             int n_max, int write_logits) {
   const auto& cf = c->cfg;
   const int D = cf.head_dim;
-  if (c->HG != 4) return hipErrorInvalidValue;
-  if (cf.dtype == KVEV_BF16 && D == 128) {
-    const int splits = (n_max + kAttnChunk - 1) / kAttnChunk;
-    dim3 grid(splits, c->G, cf.n_layers);
-    attn_mfma_kernel<kMfmaNW><<<grid, kMfmaNW * kWave, 0, c->stream>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
-        static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
-        static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.logits, c->d.part_ml,
-        c->d.part_o, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P, c->maxpages, c->lstride,
-        splits, 1.0f / sqrtf(128.0f), write_logits);
-    return hipGetLastError();
-  }
-  if (cf.dtype == KVEV_BF16) return attention_valu<bf16_t, 64>(c, q, k_new, v_new, n_max, write_logits);
-  if (D == 128) return attention_valu<float, 128>(c, q, k_new, v_new, n_max, write_logits);
-  return attention_valu<float, 64>(c, q, k_new, v_new, n_max, write_logits);
+  return with_group(c->HG, [&](auto hg) -> hipError_t {
+    constexpr int HG = decltype(hg)::value;
+    if (cf.dtype == KVEV_BF16 && D == 128) {
+      const int splits = (n_max + kAttnChunk - 1) / kAttnChunk;
+      dim3 grid(splits, c->G, cf.n_layers);
+      float* pu = write_logits ? c->d.part_u : nullptr;
+      float* vn = write_logits ? c->d.vnorm : nullptr;
+      float* pvn = write_logits ? c->d.part_vn : nullptr;
+      auto launch = [&](auto kern) {
+        kern<<<grid, kMfmaNW * kWave, 0, c->stream>>>(
+            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+            static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
+            static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.logits, c->d.part_ml,
+            c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
+            c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f), write_logits);
+      };
+      if (pu || vn)
+        launch(attn_mfma_kernel<kMfmaNW, HG, true>);
+      else
+        launch(attn_mfma_kernel<kMfmaNW, HG, false>);
+      return hipGetLastError();
+    }
+    if (cf.dtype == KVEV_BF16) return attention_valu<bf16_t, 64, HG>(c, q, k_new, v_new, n_max, write_logits);
+    if (D == 128) return attention_valu<float, 128, HG>(c, q, k_new, v_new, n_max, write_logits);
+    return attention_valu<float, 64, HG>(c, q, k_new, v_new, n_max, write_logits);
+  });
 }
 
 }  // namespace kvev

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/kvev.h"
@@ -37,6 +38,9 @@ struct DevState {
   float* part_ml = nullptr;// [L][G][S][HG][2] per-split (max, sum), S = splits of the step
   float* part_o = nullptr; // [L][G][S][HG][D] per-split unnormalised output
   float* ml = nullptr;     // [L][G][HG][2] global (max, sum)
+  float* part_u = nullptr; // [L][G][S][HG] entropy partials (entropy scorer only)
+  float* vnorm = nullptr;  // [G][L][lstride] value-row norms (VNorm scorer only)
+  float* part_vn = nullptr;// [L][G][S] per-split sums of vnorm (VNorm scorer only)
   int* mv_src = nullptr;   // [G][cap] compaction moves
   int* mv_dst = nullptr;   // [G][cap]
   int* nmoves = nullptr;   // [G]
@@ -157,6 +161,21 @@ struct kvev_ctx {
 
 namespace kvev {
 
+// Calls fn(std::integral_constant<int, HG>) for a query group size 1..8.
+template <typename Fn>
+inline hipError_t with_group(int hg, Fn&& fn) {
+  switch (hg) {
+    case 1: return fn(std::integral_constant<int, 1>{});
+    case 2: return fn(std::integral_constant<int, 2>{});
+    case 3: return fn(std::integral_constant<int, 3>{});
+    case 4: return fn(std::integral_constant<int, 4>{});
+    case 5: return fn(std::integral_constant<int, 5>{});
+    case 6: return fn(std::integral_constant<int, 6>{});
+    case 7: return fn(std::integral_constant<int, 7>{});
+    case 8: return fn(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
 // Launchers (defined in the .hip translation units).  All are stream-ordered.
 hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
 // scatter into table entries [e0, e0 + ceil(n/16)) of every KV head of `seq`

@@ -292,7 +292,10 @@ __device__ void copy_moves(T* __restrict__ kpool, T* __restrict__ vpool, const i
 //    layer: mass_l[t] = sum_{h in group} exp(s_l[h][t] - M_l[h]) / Z_l[h],
 //    m <- a*mass + (1-a)*m (EMA) or m <- m + mass (cumulative), l = 0..L-1
 //    ("What Matters ...", section 3.1 Eq.1 pooled per KV head, Eq.3/Eq.4,
-//    appendix E "Layer scoring"); the new token starts at 0;
+//    appendix E "Layer scoring"); the new token starts at 0.  The scorer
+//    variants of section 5.1 scale mass_l[t] by the slot's value norm over
+//    the layer's mean norm (VNorm) and by the mean over the group's heads of
+//    H_h / ln n, H_h = ln Z + sum_t p (M - s) (entropy weighting);
 //  * publishes, for its slots other than the new token's, the minimum
 //    eviction key (order-preserving score key, position) over the
 //    unprotected slots and the sum of the utilities.
@@ -318,6 +321,9 @@ struct PostArgs {
   const float* logits;
   const float* part_ml;
   const float* part_o;
+  const float* part_u;   // entropy partials, or null
+  const float* vnorm;    // value-row norms, or null
+  const float* part_vn;  // per-split norm sums (with vnorm)
   float* out;
   unsigned* grpctr;
   unsigned long long* blk_key;
@@ -339,15 +345,39 @@ struct PostArgs {
   int cumulative, refresh, do_select, B, n_sink, n_recent, inline_moves, nblk;
 };
 
-template <typename T, int D, int HG, int NT>
+// HG consecutive fp32 logits (one slot of one layer)
+template <int HG>
+__device__ __forceinline__ void load_heads(const float* p, float* x) {
+  if constexpr (HG % 4 == 0) {
+#pragma unroll
+    for (int h = 0; h < HG; h += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(p + h);
+      x[h] = v.x; x[h + 1] = v.y; x[h + 2] = v.z; x[h + 3] = v.w;
+    }
+  } else if constexpr (HG % 2 == 0) {
+#pragma unroll
+    for (int h = 0; h < HG; h += 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p + h);
+      x[h] = v.x; x[h + 1] = v.y;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < HG; ++h) x[h] = p[h];
+  }
+}
+
+template <typename T, int D, int HG, int NT, bool SC>
 __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   static_assert(NT % kPostTok == 0 && NT >= 256, "block shape");
   constexpr int LG = NT / kPostTok;  // layer lanes per slot
+  constexpr int EO = (HG * D + NT - 1) / NT;  // output elements per thread
   extern __shared__ float dyn[];
   const int L = A.L;
   float* s_ml = dyn;                        // [L][HG][2]
   float* s_w = dyn + L * HG * 2;            // [HG][S] split weights of this block's layer
   float* s_mass = s_w + HG * A.S;           // [L][kPostTok]
+  float* s_ent = s_mass + L * kPostTok;     // [L][HG] normalised entropies (entropy scorer)
+  float* s_vw = s_ent + L * HG;             // [L] n / sum of the value norms (VNorm scorer)
   __shared__ float red[NT / kWave];
   __shared__ unsigned long long s_key[NT / kWave];
   __shared__ int s_slot[NT / kWave];
@@ -362,19 +392,23 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
   float* gs = A.score + static_cast<int64_t>(g) * A.cap;
   auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
+  // SC: compiled with the scorer variants (active when their inputs are non-null)
+  const bool ent = SC && A.part_u != nullptr, vn = SC && A.vnorm != nullptr;
 
   // ---- issue every load of the block ---------------------------------------
   const int tl = tid % kPostTok, lg = tid / kPostTok;
   const int t = tbase + tl;
   const bool fold = A.refresh && tbase < n;
-  float4 s4[8];
+  float sx[8][HG];
+  float vx[8];
   if (fold) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int l = lg + k * LG;
-      s4[k] = (t < n && l < L) ? *reinterpret_cast<const float4*>(
-                                     A.logits + ((static_cast<int64_t>(g) * L + l) * A.lstride + t) * HG)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = t < n && l < L;
+      const int64_t r = (static_cast<int64_t>(g) * L + (in ? l : 0)) * A.lstride + (in ? t : 0);
+      load_heads<HG>(A.logits + r * HG, sx[k]);
+      vx[k] = vn ? A.vnorm[r] : 1.f;
     }
   }
   float prior = 0.f;
@@ -392,11 +426,11 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) pm[k] = k < ns ? pmb[k * HG] : make_float2(-INFINITY, 0.f);
   }
-  float po[2][kMergeBatch];
+  float po[EO][kMergeBatch];
   const float* pob = A.part_o + (static_cast<int64_t>(c) * A.G + g) * A.S * HG * D;
   if (c < L) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < EO; ++e) {
       const int idx = tid + e * NT;
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k)
@@ -406,22 +440,34 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 
   // ---- merge every layer's split statistics: (M, Z) per (layer, head) ------
   for (int i = tid; i < L * HG; i += NT) {
-    float M = -INFINITY, Z = 0.f;
+    float M = -INFINITY, Z = 0.f, U = 0.f;
+    const int64_t sb = (static_cast<int64_t>(i / HG) * A.G + g) * A.S * HG + i % HG;
     for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
       float2 v[kMergeBatch];
       if (i == tid && s0 == 0) {
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) v[k] = pm[k];
       } else {
-        const float2* pb = reinterpret_cast<const float2*>(A.part_ml) +
-                           (static_cast<int64_t>(i / HG) * A.G + g) * A.S * HG + i % HG;
+        const float2* pb = reinterpret_cast<const float2*>(A.part_ml) + sb;
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) v[k] = s0 + k < ns ? pb[(s0 + k) * HG] : make_float2(-INFINITY, 0.f);
       }
       float Mb = M;
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) Mb = fmaxf(Mb, v[k].x);
-      float z = M == -INFINITY ? 0.f : Z * __expf(M - Mb);
+      const float f0 = M == -INFINITY ? 0.f : __expf(M - Mb);
+      float z = Z * f0;
+      if (ent) {
+        // sum p (Mb - s) over the merged splits: shift the running part to Mb
+        float u = M == -INFINITY ? 0.f : f0 * (U + (Mb - M) * Z);
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          if (v[k].x == -INFINITY) continue;
+          const float f = __expf(v[k].x - Mb);
+          u += f * (A.part_u[sb + (s0 + k) * HG] + (Mb - v[k].x) * v[k].y);
+        }
+        U = u;
+      }
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) z += v[k].x == -INFINITY ? 0.f : v[k].y * __expf(v[k].x - Mb);
       M = Mb;
@@ -429,6 +475,15 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
     s_ml[i * 2 + 0] = M;
     s_ml[i * 2 + 1] = Z;
+    if (ent) s_ent[i] = n > 1 ? (__logf(Z) + U / Z) / __logf(static_cast<float>(n)) : 1.f;
+  }
+  if (vn && fold) {
+    for (int l = tid; l < L; l += NT) {
+      const float* pv = A.part_vn + (static_cast<int64_t>(l) * A.G + g) * A.S;
+      float sum = 0.f;
+      for (int s = 0; s < ns; ++s) sum += pv[s];
+      s_vw[l] = sum > 0.f ? static_cast<float>(n) / sum : 0.f;
+    }
   }
   __syncthreads();
 
@@ -445,7 +500,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < EO; ++e) {
       const int idx = tid + e * NT;
       if (idx >= HG * D) continue;
       const int h = idx / D, cc = idx % D;
@@ -458,6 +513,22 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   };
 
   // ---- probability mass per (layer, slot), then the layer-ordered fold --------
+  // mass of one layer's slot: the group's probabilities, times the scorer
+  // variants' factors
+  auto slot_mass = [&](int l, const float* x, float v) {
+    const float* ml = &s_ml[l * HG * 2];
+    float m = 0.f;
+#pragma unroll
+    for (int h = 0; h < HG; ++h) m += __expf(x[h] - ml[2 * h]) / ml[2 * h + 1];
+    if (vn) m *= s_vw[l] > 0.f ? v * s_vw[l] : 1.f;
+    if (ent) {
+      float e = 0.f;
+#pragma unroll
+      for (int h = 0; h < HG; ++h) e += s_ent[l * HG + h];
+      m *= e * (1.0f / HG);
+    }
+    return m;
+  };
   float myscore = prior;
   if (fold) {
     if (t < n) {
@@ -465,16 +536,13 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       for (int k = 0; k < 8; ++k) {
         const int l = lg + k * LG;
         if (l >= L) continue;
-        const float* ml = &s_ml[l * HG * 2];
-        s_mass[l * kPostTok + tl] = __expf(s4[k].x - ml[0]) / ml[1] + __expf(s4[k].y - ml[2]) / ml[3] +
-                                    __expf(s4[k].z - ml[4]) / ml[5] + __expf(s4[k].w - ml[6]) / ml[7];
+        s_mass[l * kPostTok + tl] = slot_mass(l, sx[k], vx[k]);
       }
       for (int l = lg + 8 * LG; l < L; l += LG) {  // more than 8 * LG layers
-        const float4 x = *reinterpret_cast<const float4*>(
-            A.logits + ((static_cast<int64_t>(g) * L + l) * A.lstride + t) * HG);
-        const float* ml = &s_ml[l * HG * 2];
-        s_mass[l * kPostTok + tl] = __expf(x.x - ml[0]) / ml[1] + __expf(x.y - ml[2]) / ml[3] +
-                                    __expf(x.z - ml[4]) / ml[5] + __expf(x.w - ml[6]) / ml[7];
+        const int64_t r = (static_cast<int64_t>(g) * L + l) * A.lstride + t;
+        float x[HG];
+        load_heads<HG>(A.logits + r * HG, x);
+        s_mass[l * kPostTok + tl] = slot_mass(l, x, vn ? A.vnorm[r] : 1.f);
       }
     }
     __syncthreads();
@@ -839,6 +907,9 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.logits = c->d.logits;
   A.part_ml = c->d.part_ml;
   A.part_o = c->d.part_o;
+  A.part_u = refresh ? c->d.part_u : nullptr;
+  A.vnorm = refresh ? c->d.vnorm : nullptr;
+  A.part_vn = refresh ? c->d.part_vn : nullptr;
   A.out = out;
   A.grpctr = c->d.grpctr;
   A.blk_key = c->d.blk_key;
@@ -876,15 +947,20 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   const int tok_blocks = (n_max + kPostTok - 1) / kPostTok;
   A.nblk = tok_blocks > cf.n_layers ? tok_blocks : cf.n_layers;
   dim3 grid(A.nblk, c->G);
-  const size_t shm = (static_cast<size_t>(cf.n_layers) * c->HG * 2 + static_cast<size_t>(c->HG) * A.S +
-                      static_cast<size_t>(cf.n_layers) * kPostTok) * sizeof(float);
-  post_kernel<T, D, 4, NT><<<grid, NT, shm, c->stream>>>(A);
-  return hipGetLastError();
+  const size_t shm = (static_cast<size_t>(cf.n_layers) * c->HG * 3 + static_cast<size_t>(c->HG) * A.S +
+                      static_cast<size_t>(cf.n_layers) * (kPostTok + 1)) * sizeof(float);
+  return with_group(c->HG, [&](auto hg) -> hipError_t {
+    constexpr int HG = decltype(hg)::value;
+    if (A.part_u || A.vnorm)
+      post_kernel<T, D, HG, NT, true><<<grid, NT, shm, c->stream>>>(A);
+    else
+      post_kernel<T, D, HG, NT, false><<<grid, NT, shm, c->stream>>>(A);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
                        int refresh, int do_select, int64_t budget, int inline_moves) {
-  if (c->HG != 4) return hipErrorInvalidValue;
   const int D = c->cfg.head_dim;
   if (c->cfg.dtype == KVEV_BF16)
     return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves)

@@ -18,7 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libkvev.so")
 OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 EMA, CUMULATIVE, LRFU_BLOCK, TIERED_INT2 = 0, 1, 2, 3
+SCORE_VNORM, SCORE_ENTROPY = 1, 2
+PER_KV_HEAD, PER_SEQUENCE = 0, 1
 MAX_REGIONS = 8
+_SCORER_BITS = {"attention": 0, "vnorm": SCORE_VNORM, "entropy": SCORE_ENTROPY,
+                "vnorm+entropy": SCORE_VNORM | SCORE_ENTROPY}
+_GRANULARITY = {"kv_head": PER_KV_HEAD, "sequence": PER_SEQUENCE}
 _STATUS = {EINVAL: "EINVAL", ENOMEM: "ENOMEM", EHIP: "EHIP", ESTATE: "ESTATE", ERANGE: "ERANGE"}
 
 
@@ -43,6 +48,7 @@ class Config(ctypes.Structure):
         ("access_tau_mult", ctypes.c_float),
         ("window_tokens", ctypes.c_int32), ("fp_windows", ctypes.c_int32),
         ("int2_windows", ctypes.c_int32),
+        ("scorer", ctypes.c_int32), ("granularity", ctypes.c_int32),
     ]
 
 
@@ -376,5 +382,6 @@ def context_for(w, max_steps=None, budget=None, stream=None):
         max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16,
         policy=CUMULATIVE if w.policy == "cumulative" else EMA, alpha_new=w.alpha_new,
         refresh_interval=w.refresh_interval, score_free=1 if w.score_free else 0,
-        n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget)
+        n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget,
+        scorer=_SCORER_BITS[w.scorer], granularity=_GRANULARITY[w.granularity])
     return Context(cfg, stream=stream)

@@ -133,6 +133,8 @@ class Workload:
     heavy_shared: bool = False      # heavy positions per (sequence, epoch) only
     budget_frac: float = 0.0        # block budget as a fraction of prefill blocks
     decode_region: int = 4
+    scorer: str = "attention"       # attention | vnorm | entropy | vnorm+entropy
+    granularity: str = "kv_head"    # kv_head | sequence
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property

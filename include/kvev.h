@@ -92,9 +92,33 @@ typedef enum {
 
 #define KVEV_MAX_REGIONS 8
 
+/* Scorer variants of the token policies ("What Matters ...", section 5.1 and
+ * appendix E), a bit mask; both act on a layer's observation before the
+ * temporal fold.
+ *  VNORM:   each head's probability on a token is multiplied by the l2 norm
+ *           of that token's value row divided by the mean of those norms over
+ *           the tokens the head attends to (at that layer and KV head; all
+ *           norms zero: factor 1).
+ *  ENTROPY: a layer's observation is multiplied by one scalar, the mean over
+ *           the heads pooled into the state of H / ln n, H the Shannon
+ *           entropy of the head's attention distribution over its n tokens
+ *           (n == 1: factor 1).                                               */
+typedef enum { KVEV_SCORE_VNORM = 1, KVEV_SCORE_ENTROPY = 2 } kvev_scorer;
+
+/* What one utility belongs to (token policies).
+ *  PER_KV_HEAD:  one utility per (sequence, KV head, token): the sum of the
+ *                KV head's query-group probabilities; budgets and retained
+ *                sets are per (sequence, KV head).
+ *  PER_SEQUENCE: one utility per (sequence, token): the mean over all query
+ *                heads of their probabilities ("What Matters ...", section
+ *                3.1 Eq.1; appendix E for GQA); one retained set per
+ *                sequence, shared by every KV head and layer.                 */
+typedef enum { KVEV_PER_KV_HEAD = 0, KVEV_PER_SEQUENCE = 1 } kvev_granularity;
+
 typedef struct {
   int32_t n_layers;         /* L, 1..64 */
-  int32_t n_q_heads;        /* Hq (multiple of n_kv_heads) */
+  int32_t n_q_heads;        /* Hq: n_kv_heads times 1..8 (times 4 in the block
+                               and tiered modes) */
   int32_t n_kv_heads;       /* Hkv */
   int32_t head_dim;         /* d: 64 or 128 */
   int32_t batch;            /* sequences stepped together */
@@ -131,6 +155,9 @@ typedef struct {
   int32_t window_tokens;                      /* tokens per window; must be 32 */
   int32_t fp_windows;                         /* K_f: routed windows kept in full precision */
   int32_t int2_windows;                       /* K_q: routed windows kept in INT2 */
+  /* KVEV_EMA and KVEV_CUMULATIVE only (0 in the other modes). */
+  int32_t scorer;                             /* kvev_scorer bit mask; 0: attention */
+  int32_t granularity;                        /* kvev_granularity */
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -140,8 +167,9 @@ void kvev_config_init(kvev_config* cfg);
 /* Validate *cfg, allocate the page pool and all per-step state on the
  * current HIP device, bind `hip_stream` (a hipStream_t; NULL = default
  * stream).  On success *out owns everything until kvev_destroy.
- * Errors: KVEV_EINVAL (bad config: d not 64/128, Hq % Hkv != 0, budget < 1,
- * n_sink + n_recent > budget, page_tokens != 16, ...), KVEV_ENOMEM, KVEV_EHIP. */
+ * Errors: KVEV_EINVAL (bad config: d not 64/128, Hq % Hkv != 0 or a group
+ * size outside 1..8, budget < 1, n_sink + n_recent > budget, page_tokens !=
+ * 16, ...), KVEV_ENOMEM, KVEV_EHIP. */
 kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out);
 
 /* Free everything the context owns (synchronises its stream).  NULL is a no-op. */

@@ -83,7 +83,7 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                             alpha_new=w.alpha_new, policy=w.policy if w.policy == "cumulative" else "ema",
                             refresh_interval=w.refresh_interval, score_free=w.score_free,
                             n_sink=w.n_sink, n_recent=w.n_recent,
-                            capacity=max(w.prefill_lens) + steps + 1)
+                            capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
     for b in range(w.batch):
         K, V = w.prefill_kv(b, device=device)
         ctx.prefill(b, K.contiguous(), V.contiguous())

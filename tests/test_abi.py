@@ -66,7 +66,14 @@ def _create(**kw):
 @pytest.mark.parametrize("bad,msg", [
     (dict(head_dim=96), "head_dim"),
     (dict(n_q_heads=7), "multiple"),
-    (dict(n_q_heads=16), "group size"),
+    (dict(n_q_heads=18), "group size"),
+    (dict(n_q_heads=4, n_kv_heads=2, policy=kvev.LRFU_BLOCK), "group size must be 4"),
+    (dict(n_q_heads=16, n_kv_heads=2, policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128),
+     "group size must be 4"),
+    (dict(scorer=4), "scorer"),
+    (dict(granularity=2), "granularity"),
+    (dict(policy=kvev.LRFU_BLOCK, scorer=kvev.SCORE_VNORM), "token policies"),
+    (dict(n_layers=64, n_q_heads=16, max_tokens=1 << 20), "max_tokens too large"),
     (dict(budget=0), "budget"),
     (dict(n_sink=8, n_recent=4), "exceeds the budget"),
     (dict(page_tokens=32), "page_tokens"),

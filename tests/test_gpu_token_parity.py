@@ -201,3 +201,51 @@ def test_llama8b_32k_full_size_fused_sampled():
     w = synth.workload("llama8b_32k")
     st = _gu().run_token_lockstep(w, 6, sample_heads=[3], kv_every=3, ctx_steps=w.steps, fused=True)
     assert st.steps == 6
+
+
+# --- query group sizes other than 4 ----------------------------------------------
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 8), (20, 4), (30, 5), (28, 4), (32, 4)])
+def test_group_sizes_matrix_core_path(hq, hkv):
+    """bf16, head_dim 128 (matrix-core kernel) with 1..8 query heads per KV
+    head; (28, 4) is the Qwen2.5-7B attention shape."""
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, n_q_heads=hq, n_kv_heads=hkv,
+                                             prefill_lens=(700, 433), budget=120)
+    _gu().run_token_lockstep(w, 12)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128)])
+def test_group_size_7_vector_path(dtype, d):
+    w = synth.workload("tiny").scaled(n_q_heads=14, n_kv_heads=2, head_dim=d, dtype=dtype,
+                                      prefill_lens=(300,), budget=90)
+    _gu().run_token_lockstep(w, 16)
+
+
+# --- scorer variants ([InertiaKV] section 5.1) ------------------------------------
+
+@pytest.mark.parametrize("scorer", ["vnorm", "entropy", "vnorm+entropy"])
+def test_scorers_matrix_core_path(scorer):
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(1100,), budget=150,
+                                             scorer=scorer)
+    _gu().run_token_lockstep(w, 16)
+
+
+@pytest.mark.parametrize("scorer", ["vnorm", "entropy", "vnorm+entropy"])
+def test_scorers_fp32_vector_path(scorer):
+    st = _gu().run_token_lockstep(synth.workload("tiny").scaled(scorer=scorer), 24)
+    assert st.max_out_err <= 1e-5 and st.max_score_err <= 1e-5
+
+
+def test_scorers_with_lazy_refresh_and_group_7():
+    """Observations only every 4th step (the scorer outputs are skipped in
+    between) on a group of 7, batch of 2."""
+    w = synth.workload("lazy16x8k").scaled(n_layers=2, n_q_heads=28, n_kv_heads=4,
+                                           prefill_lens=(640, 515), budget=160,
+                                           refresh_interval=4, scorer="vnorm+entropy")
+    _gu().run_token_lockstep(w, 14)
+
+
+def test_scorers_fused_step():
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(900,), budget=100,
+                                             scorer="vnorm+entropy")
+    _gu().run_token_lockstep(w, 12, fused=True)
