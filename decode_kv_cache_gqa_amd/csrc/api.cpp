@@ -152,7 +152,6 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
       (f.scorer != 0 || f.granularity != KVEV_PER_KV_HEAD))
     return bad("scorer variants and granularity apply to the token policies only");
-  if (f.granularity != KVEV_PER_KV_HEAD) return bad("per-sequence granularity is not available");
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
   if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
@@ -201,10 +200,14 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.n_layers > 64) return bad("n_layers must be <= 64");
   {
     // the post kernel stages per-layer statistics and one layer's split
-    // weights in LDS: (3 L HG + HG S + 65 L) floats must fit 64 KiB
+    // weights in LDS: (3 L HG + HG S + 65 L) floats must fit 56 KiB (the
+    // rest of the 64 KiB is the kernels' static arrays, < 8 KiB)
     const int64_t S = (f.max_tokens + kAttnChunk - 1) / kAttnChunk;
     const int64_t lds = (3ll * f.n_layers * hg + hg * S + 65ll * f.n_layers) * 4;
-    if (!block && lds > 65536) return bad("max_tokens too large for this layer count and group size");
+    if (!block && lds > 57344) return bad("max_tokens too large for this layer count and group size");
+    if (f.granularity == KVEV_PER_SEQUENCE &&
+        pool_post_shm(f.n_layers, f.n_q_heads, f.n_kv_heads, S) * 4 > 57344)
+      return bad("per-sequence granularity: too many (layer, query head) pairs or max_tokens too large");
   }
 
   kvev_ctx* c = new (std::nothrow) kvev_ctx();
@@ -218,7 +221,9 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->maxpages = static_cast<int>((c->cap + c->PT - 1) / c->PT);
   c->P = static_cast<int64_t>(c->G) * c->maxpages;
   c->max_splits = static_cast<int>((c->cap + kAttnChunk - 1) / kAttnChunk);
-  c->max_post_blocks = std::max(static_cast<int>((c->cap + 63) / 64), f.n_layers);
+  c->pooled = f.granularity == KVEV_PER_SEQUENCE;
+  c->max_post_blocks = std::max(static_cast<int>((c->cap + 63) / 64),
+                                c->pooled ? f.n_layers * f.n_kv_heads : f.n_layers);
   c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
   c->count.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
@@ -773,6 +778,7 @@ kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return kvev_block_state(c, seq, dst, nullptr, nullptr, cap, n_written);
+  if (c->pooled) g = seq * c->cfg.n_kv_heads;  // the sequence's utilities
   const int64_t n = c->count[g];
   if (n_written) *n_written = n;
   if (!dst || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
@@ -788,6 +794,7 @@ kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* position
   if (c->tier_mode) return fail(c, KVEV_EINVAL, "tiered mode: use the kvev_tier_* calls");
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  if (c->pooled) g = seq * c->cfg.n_kv_heads;  // one retained set per sequence
   const int64_t n = c->count[g];
   if (n_out) *n_out = n;
   if (!positions || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
@@ -818,6 +825,7 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return fail(c, KVEV_EINVAL, "block mode: use kvev_import_blocks");
+  if (c->pooled) return fail(c, KVEV_EINVAL, "per-sequence granularity: groups cannot be imported one by one");
   if (!positions || !scores || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_ERANGE, "n out of range");
   int maxp = 0;

@@ -13,6 +13,7 @@
 namespace kvev {
 
 constexpr int kAttnChunk = 256;   // slots per attention split
+constexpr int kPostTokens = 64;   // slots per post-attention block
 constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies itself
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
 constexpr int kRegions = 8;       // region labels of the block-granular mode
@@ -129,6 +130,7 @@ struct kvev_ctx {
   hipStream_t stream = nullptr;
   int device = 0;
   int G = 0, HG = 0, PT = kvev::kPageTokens, maxpages = 0;
+  bool pooled = false;  // one retained set per sequence (KVEV_PER_SEQUENCE)
   int64_t cap = 0, P = 0;
   int64_t lstride = 0;  // slot stride of the logit scratch in the current step
   int max_splits = 0;
@@ -161,6 +163,12 @@ struct kvev_ctx {
 
 namespace kvev {
 
+// Dynamic LDS floats of the sequence-pooled post kernel: per (layer, query
+// head) statistics and entropies, one output's split weights, the slot
+// masses, the layer factors and the per (layer, KV head) norm factors.
+inline int64_t pool_post_shm(int L, int Hq, int Hkv, int64_t S) {
+  return 3ll * L * Hq + (Hq / Hkv) * S + static_cast<int64_t>(L) * (kPostTokens + 1) + static_cast<int64_t>(L) * Hkv;
+}
 // Calls fn(std::integral_constant<int, HG>) for a query group size 1..8.
 template <typename Fn>
 inline hipError_t with_group(int hg, Fn&& fn) {

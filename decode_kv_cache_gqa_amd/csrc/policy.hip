@@ -1,287 +1,8 @@
 // Probability pass + score fold, top-budget selection with compaction plan,
 // K/V moves, and the cache copy kernels.
-#include "common.h"
-#include "kvev_internal.h"
+#include "post_common.h"
 
 namespace kvev {
-
-// ---------------------------------------------------------------------------
-// Selection + compaction plan for one group, executed by one block of NT
-// threads.  Keep the protected tokens (positions < n_sink, or among the
-// n_recent newest) and evict the k = n - B lowest (score, position) keys of
-// the rest, i.e. keep the top (B - |protected|) ("What Matters ...", section
-// 3.1: evict the lowest utility when over budget; "MemDecay", section III-A
-// (1): forcing F then taking the best B is optimal).  The k-th smallest key
-// comes from an LDS radix select on order-preserving 32-bit score keys (four
-// 8-bit digits), plus a radix select on positions only when equal scores
-// straddle the cut; k == 1 is an argmin.  Plan: holes = unkept slots < B
-// ascending, movers = kept slots >= B ascending, mover j fills hole j.
-// Positions and utilities are moved here; returns the number of moves.
-// ---------------------------------------------------------------------------
-template <int NT>
-__device__ __forceinline__ void scan_256(const int* hist, int* excl_out, int* wsum, int tid) {
-  const int v = tid < 256 ? hist[tid] : 0;
-  int x = v;
-  const int lane = tid % kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (tid < 256 && lane == kWave - 1) wsum[tid / kWave] = x;
-  __syncthreads();
-  if (tid < 256) {
-    int off = 0;
-    for (int w = 0; w < tid / kWave; ++w) off += wsum[w];
-    excl_out[tid] = off + x - v;
-  }
-  __syncthreads();
-}
-
-// Loads of slot state.  COH: the values may have been written by other
-// blocks of the same kernel with write-through (device-scope) stores, so
-// read them with device-scope loads that bypass the CU and L2 copies.
-template <bool COH, typename T>
-__device__ __forceinline__ T ld_state(const T* p) {
-  if constexpr (COH)
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    return *p;
-}
-template <typename T>
-__device__ __forceinline__ void st_coherent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int NT, bool COH>
-__device__ int select_group(int n, int B, int newest, int n_sink, int n_recent,
-                            int* __restrict__ gp, float* __restrict__ gs, int* __restrict__ src,
-                            int* __restrict__ dst, int* __restrict__ errflag) {
-  static_assert(NT >= 256, "selection needs >= 256 threads");
-  __shared__ int hist[256];
-  __shared__ int excl[256];
-  __shared__ int wsum[4];
-  __shared__ int sel[3];
-  __shared__ unsigned long long wmin[NT / kWave];
-  __shared__ int wcnt[2][NT / kWave];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int k = n - B;
-  auto is_cand = [&](int p) { return !(p < n_sink || p > newest - n_recent); };
-
-  uint32_t thr = 0;
-  int pos_cut = 0x7fffffff;
-  if (k == 1) {
-    // argmin of (score key, position) over candidates, carrying the slot
-    unsigned long long best = ~0ull;
-    int slot = -1;
-    for (int base = 0; base < n; base += NT * 8) {
-      int pv[8];
-      float sv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * NT + tid;
-        pv[u] = i < n ? ld_state<COH>(gp + i) : -1;
-        sv[u] = i < n ? ld_state<COH>(gs + i) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * NT + tid;
-        if (i >= n || !is_cand(pv[u])) continue;
-        const unsigned long long kk =
-            (static_cast<unsigned long long>(float_key(sv[u])) << 32) | static_cast<uint32_t>(pv[u]);
-        if (kk < best) {
-          best = kk;
-          slot = i;
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long y = __shfl_xor(best, o, kWave);
-      const int ys = __shfl_xor(slot, o, kWave);
-      if (y < best) {
-        best = y;
-        slot = ys;
-      }
-    }
-    if (lane == 0) {
-      wmin[wave] = best;
-      wcnt[0][wave] = slot;
-    }
-    __syncthreads();
-    best = wmin[0];
-    int ev = wcnt[0][0];
-    for (int w = 1; w < NT / kWave; ++w)
-      if (wmin[w] < best) {
-        best = wmin[w];
-        ev = wcnt[0][w];
-      }
-    __syncthreads();
-    if (best == ~0ull || ev < 0) {  // no candidate: impossible when B >= |protected|
-      if (tid == 0) atomicOr(errflag, 2);
-      return 0;
-    }
-    if (ev >= B) return 0;  // the evicted token sits at slot B: nothing moves
-    if (tid == 0) {
-      src[0] = B;
-      dst[0] = ev;
-      gp[ev] = ld_state<COH>(gp + B);
-      gs[ev] = ld_state<COH>(gs + B);
-    }
-    __syncthreads();
-    return 1;
-  }
-
-  {
-    uint32_t prefix = 0, mask = 0;
-    int kk = k, eq = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += NT) {
-        if (!is_cand(ld_state<COH>(gp + i))) continue;
-        const uint32_t key = float_key(ld_state<COH>(gs + i));
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-      }
-      __syncthreads();
-      scan_256<NT>(hist, excl, wsum, tid);
-      if (tid < 256 && excl[tid] < kk && kk <= excl[tid] + hist[tid]) {
-        sel[0] = tid;
-        sel[1] = excl[tid];
-        sel[2] = hist[tid];
-      }
-      __syncthreads();
-      prefix |= static_cast<uint32_t>(sel[0]) << shift;
-      mask |= 255u << shift;
-      kk -= sel[1];
-      eq = sel[2];
-      __syncthreads();
-    }
-    thr = prefix;
-    if (kk < eq) {
-      uint32_t pprefix = 0, pmask = 0;
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-          const int p = ld_state<COH>(gp + i);
-          if (!is_cand(p) || float_key(ld_state<COH>(gs + i)) != thr) continue;
-          const uint32_t key = static_cast<uint32_t>(p);
-          if ((key & pmask) == pprefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-        }
-        __syncthreads();
-        scan_256<NT>(hist, excl, wsum, tid);
-        if (tid < 256 && excl[tid] < kk && kk <= excl[tid] + hist[tid]) {
-          sel[0] = tid;
-          sel[1] = excl[tid];
-        }
-        __syncthreads();
-        pprefix |= static_cast<uint32_t>(sel[0]) << shift;
-        pmask |= 255u << shift;
-        kk -= sel[1];
-        __syncthreads();
-      }
-      pos_cut = static_cast<int>(pprefix);
-    }
-  }
-
-  auto keep = [&](int i) {
-    const int p = ld_state<COH>(gp + i);
-    if (!is_cand(p)) return true;
-    const uint32_t key = float_key(ld_state<COH>(gs + i));
-    return key > thr || (key == thr && p > pos_cut);
-  };
-  int hole_base = 0, mover_base = 0;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int tile = 0; tile < n; tile += NT) {
-    const int i = tile + tid;
-    const bool in = i < n;
-    const bool kp = in && keep(i);
-    const bool hole = in && i < B && !kp;
-    const bool mover = in && i >= B && kp;
-    const unsigned long long bh = __ballot(hole), bm = __ballot(mover);
-    if (lane == 0) {
-      wcnt[0][wave] = __popcll(bh);
-      wcnt[1][wave] = __popcll(bm);
-    }
-    __syncthreads();
-    int oh = hole_base, om = mover_base, th = 0, tm = 0;
-    for (int w = 0; w < NT / kWave; ++w) {
-      if (w < wave) {
-        oh += wcnt[0][w];
-        om += wcnt[1][w];
-      }
-      th += wcnt[0][w];
-      tm += wcnt[1][w];
-    }
-    if (hole) dst[oh + __popcll(bh & lt)] = i;
-    if (mover) src[om + __popcll(bm & lt)] = i;
-    hole_base += th;
-    mover_base += tm;
-    __syncthreads();
-  }
-  // the two counts agree by construction; a disagreement is reported, never used
-  const int nm = hole_base < mover_base ? hole_base : mover_base;
-  if (tid == 0 && hole_base != mover_base) atomicOr(errflag, 1);
-  __syncthreads();
-  for (int j = tid; j < nm; j += NT) {
-    const int s = src[j], d = dst[j];
-    gp[d] = ld_state<COH>(gp + s);
-    gs[d] = ld_state<COH>(gs + s);
-  }
-  __syncthreads();
-  return nm;
-}
-
-// Copy `nm` planned moves of one group for every layer: the K row (16-byte
-// pieces of a token-major page) and the V column (D elements of a
-// channel-major page).  The page table is shared by all layers, so each
-// move's two pages are looked up once; all loads of a batch are issued
-// before its stores.
-template <typename T, int D, int NT>
-__device__ void copy_moves(T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ pt,
-                           const int* __restrict__ src, const int* __restrict__ dst, int nm, int L,
-                           int64_t P, int64_t cap) {
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int KB = 4;  // 16-byte K pieces per thread per batch
-  constexpr int VB = 8;  // V elements per thread per batch
-  for (int j = 0; j < nm; ++j) {
-    const int s = src[j], d = dst[j];
-    if (s < 0 || s >= cap || d < 0 || d >= cap) continue;
-    const int ps = pt[s / kPageTokens], pd = pt[d / kPageTokens];
-    const int rs = s % kPageTokens, rd = d % kPageTokens;
-    for (int base = 0; base < L * LPR; base += NT * KB) {
-      uint4 v[KB];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * LPR)
-          v[u] = *reinterpret_cast<const uint4*>(kpool + kidx(idx / LPR, ps, rs, (idx % LPR) * EPL, P, D));
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * LPR)
-          *reinterpret_cast<uint4*>(kpool + kidx(idx / LPR, pd, rd, (idx % LPR) * EPL, P, D)) = v[u];
-      }
-    }
-    for (int base = 0; base < L * D; base += NT * VB) {
-      T v[VB];
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * D) v[u] = vpool[vidx(idx / D, ps, rs, idx % D, P, D)];
-      }
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * D) vpool[vidx(idx / D, pd, rd, idx % D, P, D)] = v[u];
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Post-attention kernel, grid (blocks per group, groups); block c owns slots
 // [64c, 64c + 64) and, when c < L, the output of layer c.  Every block:
@@ -310,62 +31,6 @@ __device__ void copy_moves(T* __restrict__ kpool, T* __restrict__ vpool, const i
 // with device-scope loads; no agent-scope fence is used (on this GPU it
 // writes back the whole L2).
 // ---------------------------------------------------------------------------
-constexpr int kPostTok = 64;  // slots per post block (one wave's worth)
-constexpr int kMergeBatch = 16;
-
-struct PostArgs {
-  int* count;
-  int* pos;
-  float* score;
-  int* nextpos;
-  const float* logits;
-  const float* part_ml;
-  const float* part_o;
-  const float* part_u;   // entropy partials, or null
-  const float* vnorm;    // value-row norms, or null
-  const float* part_vn;  // per-split norm sums (with vnorm)
-  float* out;
-  unsigned* grpctr;
-  unsigned long long* blk_key;
-  int* blk_slot;
-  int* blk_page;
-  float* blk_sum;
-  int* mv_src;
-  int* mv_dst;
-  int* nmoves;
-  int* errflag;
-  void* kpool;
-  void* vpool;
-  const int* ptab;
-  const void* k_new;
-  const void* v_new;
-  int L, G, Hkv, Hq, S, CT, maxpages, max_blk;
-  int64_t cap, P, lstride;
-  float a;
-  int cumulative, refresh, do_select, B, n_sink, n_recent, inline_moves, nblk;
-};
-
-// HG consecutive fp32 logits (one slot of one layer)
-template <int HG>
-__device__ __forceinline__ void load_heads(const float* p, float* x) {
-  if constexpr (HG % 4 == 0) {
-#pragma unroll
-    for (int h = 0; h < HG; h += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(p + h);
-      x[h] = v.x; x[h + 1] = v.y; x[h + 2] = v.z; x[h + 3] = v.w;
-    }
-  } else if constexpr (HG % 2 == 0) {
-#pragma unroll
-    for (int h = 0; h < HG; h += 2) {
-      const float2 v = *reinterpret_cast<const float2*>(p + h);
-      x[h] = v.x; x[h + 1] = v.y;
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < HG; ++h) x[h] = p[h];
-  }
-}
-
 template <typename T, int D, int HG, int NT, bool SC>
 __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   static_assert(NT % kPostTok == 0 && NT >= 256, "block shape");
@@ -747,17 +412,21 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   write_output();
 }
 
-// Standalone selection (kvev_evict): one block per group.
+// Standalone selection (kvev_evict): one block per group, or, in the
+// sequence-pooled mode (pool = Hkv > 0), one block per sequence working on
+// its first group's state, whose plan every KV head's moves then follow.
 constexpr int kSelNT = 1024;
 __global__ __launch_bounds__(kSelNT) void select_kernel(
     int* __restrict__ count, int* __restrict__ pos, float* __restrict__ score,
     const int* __restrict__ nextpos, int* __restrict__ mv_src, int* __restrict__ mv_dst,
     int* __restrict__ nmoves, int* __restrict__ errflag, int64_t cap, int B, int n_sink,
-    int n_recent) {
-  const int g = blockIdx.x;
+    int n_recent, int pool) {
+  const int g = pool ? blockIdx.x * pool : blockIdx.x;
+  const int ng = pool ? pool : 1;
   const int n = count[g];
   if (n <= B) {
-    if (threadIdx.x == 0) nmoves[g] = 0;
+    if (threadIdx.x == 0)
+      for (int h = 0; h < ng; ++h) nmoves[g + h] = 0;
     return;
   }
   const int nm = select_group<kSelNT, false>(n, B, nextpos[g] - 1, n_sink, n_recent,
@@ -766,8 +435,10 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(
                                       mv_src + static_cast<int64_t>(g) * cap,
                                       mv_dst + static_cast<int64_t>(g) * cap, errflag);
   if (threadIdx.x == 0) {
-    nmoves[g] = nm;
-    count[g] = B;
+    for (int h = 0; h < ng; ++h) {
+      nmoves[g + h] = nm;
+      count[g + h] = B;
+    }
   }
 }
 
@@ -778,16 +449,17 @@ __global__ __launch_bounds__(NT) void move_kernel(T* __restrict__ kpool, T* __re
                                                   const int* __restrict__ mv_src,
                                                   const int* __restrict__ mv_dst,
                                                   const int* __restrict__ nmoves, int64_t P,
-                                                  int maxpages, int64_t cap, int per_block) {
+                                                  int maxpages, int64_t cap, int per_block, int pool) {
   constexpr int EPL = Vec16<T>::N;
   constexpr int LPR = D / EPL;
   const int g = blockIdx.y, l = blockIdx.z;
+  const int gm = pool ? g / pool * pool : g;  // the group whose plan applies (pooled: the sequence's first)
   const int nm = nmoves[g];
   const int j0 = blockIdx.x * per_block;
   const int j1 = min(nm, j0 + per_block);
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
-  const int* ms = mv_src + static_cast<int64_t>(g) * cap;
-  const int* md = mv_dst + static_cast<int64_t>(g) * cap;
+  const int* ms = mv_src + static_cast<int64_t>(gm) * cap;
+  const int* md = mv_dst + static_cast<int64_t>(gm) * cap;
   for (int idx = threadIdx.x; idx < (j1 - j0) * LPR; idx += NT) {
     const int j = j0 + idx / LPR, sub = idx % LPR;
     const int s = ms[j], d = md[j];
@@ -945,6 +617,12 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.n_recent = cf.n_recent;
   A.inline_moves = inline_moves;
   const int tok_blocks = (n_max + kPostTok - 1) / kPostTok;
+  if (c->pooled) {
+    // one grid row per sequence; blocks cover the slots and the (layer, KV head) outputs
+    const int outs = cf.n_layers * cf.n_kv_heads;
+    A.nblk = tok_blocks > outs ? tok_blocks : outs;
+    return launch_pool_post<T, D>(c, A);
+  }
   A.nblk = tok_blocks > cf.n_layers ? tok_blocks : cf.n_layers;
   dim3 grid(A.nblk, c->G);
   const size_t shm = (static_cast<size_t>(cf.n_layers) * c->HG * 3 + static_cast<size_t>(c->HG) * A.S +
@@ -971,10 +649,10 @@ hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v
 
 hipError_t launch_select(kvev_ctx* c, int64_t budget) {
   const auto& cf = c->cfg;
-  select_kernel<<<c->G, kSelNT, 0, c->stream>>>(c->d.count, c->d.pos, c->d.score, c->d.nextpos,
-                                                c->d.mv_src, c->d.mv_dst, c->d.nmoves,
-                                                c->d.errflag, c->cap, static_cast<int>(budget),
-                                                cf.n_sink, cf.n_recent);
+  const int pool = c->pooled ? cf.n_kv_heads : 0;
+  select_kernel<<<pool ? cf.batch : c->G, kSelNT, 0, c->stream>>>(
+      c->d.count, c->d.pos, c->d.score, c->d.nextpos, c->d.mv_src, c->d.mv_dst, c->d.nmoves,
+      c->d.errflag, c->cap, static_cast<int>(budget), cf.n_sink, cf.n_recent, pool);
   return hipGetLastError();
 }
 
@@ -984,7 +662,7 @@ static hipError_t moves_impl(kvev_ctx* c, int max_moves) {
   dim3 grid((max_moves + PER - 1) / PER, c->G, c->cfg.n_layers);
   move_kernel<T, D, NT><<<grid, NT, 0, c->stream>>>(
       static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.mv_src,
-      c->d.mv_dst, c->d.nmoves, c->P, c->maxpages, c->cap, PER);
+      c->d.mv_dst, c->d.nmoves, c->P, c->maxpages, c->cap, PER, c->pooled ? c->cfg.n_kv_heads : 0);
   return hipGetLastError();
 }
 

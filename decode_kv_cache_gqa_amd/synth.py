@@ -357,13 +357,28 @@ def _lengths(seed, n, lo, hi):
 
 
 def workload(name: str) -> Workload:
-    """The five configured workloads, by short name."""
+    """The configured workloads, by short name: the five of the method's
+    configurations plus variants of the 32k one (pooled granularity, the
+    scorer variants, the Qwen2.5-7B group shape)."""
     if name == "tiny":
         return Workload("tiny_inertiakv_1L_8q2kv_d64_f32", 1, 8, 2, 64, "f32", (512,), 64,
                         seed=1001, alpha_new=0.05, budget=128, structured=False)
     if name == "llama8b_32k":
         return Workload("llama8b_32k_10pct", 32, 32, 8, 128, "bf16", (32768,), 256,
                         seed=1002, alpha_new=0.05, budget=3277, n_sink=4, n_recent=32)
+    if name == "llama8b_32k_pooled":
+        # one utility and one retained set per sequence ("What Matters ...", section 3.1 Eq.1)
+        return Workload("llama8b_32k_10pct_pooled", 32, 32, 8, 128, "bf16", (32768,), 256,
+                        seed=1002, alpha_new=0.05, budget=3277, n_sink=4, n_recent=32,
+                        granularity="sequence")
+    if name == "llama8b_32k_vnorm_entropy":
+        return Workload("llama8b_32k_10pct_vnorm_entropy", 32, 32, 8, 128, "bf16", (32768,), 256,
+                        seed=1002, alpha_new=0.05, budget=3277, n_sink=4, n_recent=32,
+                        scorer="vnorm+entropy")
+    if name == "qwen7b_32k":
+        # Qwen2.5-7B attention shape: 28 layers, 28 query and 4 KV heads (groups of 7)
+        return Workload("qwen2.5_7b_32k_10pct", 28, 28, 4, 128, "bf16", (32768,), 256,
+                        seed=1006, alpha_new=0.05, budget=3277, n_sink=4, n_recent=32)
     if name == "lazy16x8k":
         return Workload("batch16_8k_25pct_lazy8", 32, 32, 8, 128, "bf16", (8192,) * 16, 512,
                         seed=1003, alpha_new=0.05, budget=2048, refresh_interval=8)
@@ -384,4 +399,5 @@ def workload(name: str) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k")
+WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
+             "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k")

@@ -181,6 +181,129 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
 
 
 # ---------------------------------------------------------------------------
+# Sequence-pooled token mode
+# ---------------------------------------------------------------------------
+
+def run_pooled_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", fused=False,
+                        kv_every=4, budget=None):
+    """Run `steps` steps of a per-sequence (pooled) workload on the GPU and
+    the oracle.  Every KV head of a sequence must report the same retained
+    positions; an excused near-tie makes the oracle adopt the GPU's state."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    rtol = rtol if rtol is not None else (1e-5 if w.dtype == "f32" else 2e-3)
+    B = w.budget if budget is None else budget
+    sample = list(range(w.batch)) if sample_seqs is None else list(sample_seqs)
+    Hkv, Hg = w.n_kv_heads, w.group_size
+    log(f"[pooled] {w.name}: L={w.n_layers} Hq={w.n_q_heads} Hkv={Hkv} batch={w.batch} "
+        f"L0={w.prefill_lens[:4]} steps={steps} B={B} sample={sample} fused={fused} scorer={w.scorer}")
+    t_start = time.time()
+    ctx = kvev.context_for(w, max_steps=steps, budget=B)
+    o = orc.PooledTokenOracle(w.n_layers, w.n_q_heads, Hkv, w.head_dim, budget=B,
+                              alpha_new=w.alpha_new,
+                              policy=w.policy if w.policy == "cumulative" else "ema",
+                              refresh_interval=w.refresh_interval, score_free=w.score_free,
+                              n_sink=w.n_sink, n_recent=w.n_recent,
+                              capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=device)
+        ctx.prefill(b, K.contiguous(), V.contiguous())
+        del K, V
+        if b in sample:
+            Kc, Vc = w.prefill_kv(b, device="cpu")
+            o.prefill(b, Kc.float().numpy(), Vc.float().numpy())
+    torch.cuda.synchronize()
+    st = Stats()
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
+
+    def retained_all(b):
+        pos = [ctx.retained(b, h) for h in range(Hkv)]
+        for h in range(1, Hkv):
+            np.testing.assert_array_equal(pos[h], pos[0], err_msg=f"seq {b}: KV head {h} holds other slots")
+        return pos[0]
+
+    for t in range(1, steps + 1):
+        q, kn, vn = w.step_inputs(t, device=device)
+        if fused:
+            ctx.step(q, kn, vn, out, B)
+        else:
+            ctx.decode_step(q, kn, vn, out)
+        qc, knc, vnc = w.step_inputs(t, device="cpu", seqs=sample)
+        ref_out = o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(), sample)
+        gout = out.cpu().numpy()
+        for bi, b in enumerate(sample):
+            for h in range(Hkv):
+                for l in range(w.n_layers):
+                    st.max_out_err = max(st.max_out_err, check_out(
+                        gout[l, b, h * Hg:(h + 1) * Hg], ref_out[l, bi, h * Hg:(h + 1) * Hg], rtol,
+                        f"step {t} out l={l} b={b} kvh={h}"))
+        pre = {}
+        if not fused:
+            for b in sample:
+                gp = retained_all(b)
+                gs = ctx.scores(b, 0)
+                np.testing.assert_array_equal(gp, o.positions(b), err_msg=f"step {t} pre-evict slots b={b}")
+                st.max_score_err = max(st.max_score_err, check_scores(gs, o.scores(b), rtol,
+                                                                      f"step {t} scores b={b}"))
+                pre[b] = (gs, gp)
+            ctx.evict(B)
+        ref_pre = {b: (o.scores(b), o.positions(b)) for b in sample}
+        o.evict(B)
+        for b in sample:
+            got = retained_all(b)
+            if not fused:
+                gs, gp = pre[b]
+                exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
+                np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b}")
+                st.exact_selection_checks += 1
+            ref_pos = o.positions(b)
+            if not np.array_equal(got, ref_pos):
+                ms, pos_all = ref_pre[b]
+                keep_ref = np.isin(pos_all, ref_pos)
+                prot = (pos_all < w.n_sink) | (pos_all > pos_all.max() - w.n_recent)
+                kept = ms[keep_ref & ~prot]
+                theta = kept.min() if kept.size else 0.0
+                diff = set(got.tolist()) ^ set(ref_pos.tolist())
+                idx = {p: i for i, p in enumerate(pos_all.tolist())}
+                gaps = [abs(ms[idx[p]] - theta) for p in diff]
+                assert max(gaps) < 1e-5, (f"step {t} b={b}: retained sets differ by {len(diff)} positions "
+                                          f"with oracle score gap {max(gaps):.3e} >= 1e-5")
+                # the oracle adopts the GPU's retained set, utilities and cache
+                sst = o.seqs[b]
+                n = len(got)
+                sst.pos[:n] = got
+                sst.m[:n] = ctx.scores(b, 0).astype(np.float64)
+                for h in range(Hkv):
+                    gk, gv = ctx.export_kv(b, h)
+                    sst.K[:, h, :n] = gk.float().cpu().numpy()
+                    sst.V[:, h, :n] = gv.float().cpu().numpy()
+                sst.n = n
+                st.near_tie_resyncs += 1
+                st.notes.append(f"t={t} b={b} near-tie resync ({len(diff)} positions)")
+                continue
+            if fused:
+                st.max_score_err = max(st.max_score_err, check_scores(
+                    ctx.scores(b, 0), o.scores(b), rtol, f"step {t} post-evict scores b={b}"))
+            if kv_every and t % kv_every == 0:
+                sst = o.seqs[b]
+                for h in range(Hkv):
+                    gk, gv = ctx.export_kv(b, h)
+                    rk = torch.from_numpy(sst.K[:, h, :sst.n].copy()).to(w.torch_dtype)
+                    rv = torch.from_numpy(sst.V[:, h, :sst.n].copy()).to(w.torch_dtype)
+                    assert torch.equal(gk.cpu(), rk), f"step {t} compacted K differs b={b} kvh={h}"
+                    assert torch.equal(gv.cpu(), rv), f"step {t} compacted V differs b={b} kvh={h}"
+                    st.kv_checks += 1
+        st.steps = t
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[pooled] step {t}: out_err {st.max_out_err:.2e} score_err {st.max_score_err:.2e} "
+                f"resyncs {st.near_tie_resyncs} ({time.time() - t_start:.1f}s)")
+    ctx.sync()
+    ctx.close()
+    return st
+
+
+# ---------------------------------------------------------------------------
 # Block-granular LRFU mode
 # ---------------------------------------------------------------------------
 

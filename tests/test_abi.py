@@ -74,6 +74,8 @@ def _create(**kw):
     (dict(granularity=2), "granularity"),
     (dict(policy=kvev.LRFU_BLOCK, scorer=kvev.SCORE_VNORM), "token policies"),
     (dict(n_layers=64, n_q_heads=16, max_tokens=1 << 20), "max_tokens too large"),
+    (dict(n_layers=64, n_q_heads=64, n_kv_heads=8, granularity=kvev.PER_SEQUENCE, max_tokens=4096),
+     "per-sequence granularity"),
     (dict(budget=0), "budget"),
     (dict(n_sink=8, n_recent=4), "exceeds the budget"),
     (dict(page_tokens=32), "page_tokens"),
