@@ -39,7 +39,7 @@ void free_all(kvev_ctx* c) {
   auto& d = c->d;
   void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
-                  d.grpctr, d.blk_key, d.blk_slot, d.blk_page, d.blk_sum, d.btab, d.nres,
+                  d.grpctr, d.blk_key, d.blk_slot, d.blk_sum, d.btab, d.nres,
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
                   d.rd_ids, d.part_u, d.vnorm, d.part_vn};
   for (void* p : ptrs)
@@ -222,8 +222,9 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->P = static_cast<int64_t>(c->G) * c->maxpages;
   c->max_splits = static_cast<int>((c->cap + kAttnChunk - 1) / kAttnChunk);
   c->pooled = f.granularity == KVEV_PER_SEQUENCE;
-  c->max_post_blocks = std::max(static_cast<int>((c->cap + 63) / 64),
-                                c->pooled ? f.n_layers * f.n_kv_heads : f.n_layers);
+  c->max_post_blocks = c->pooled ? std::max(static_cast<int>((c->cap + kPoolTokens - 1) / kPoolTokens),
+                                            f.n_layers * f.n_kv_heads)
+                                 : std::max(static_cast<int>((c->cap + 63) / 64), f.n_layers);
   c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
   c->count.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
@@ -275,7 +276,6 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.grpctr, G));
   A(dalloc(&d.blk_key, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_slot, static_cast<size_t>(G) * c->max_post_blocks));
-  A(dalloc(&d.blk_page, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_sum, static_cast<size_t>(G) * c->max_post_blocks));
   if (block) {
     const size_t Bs = f.batch;
@@ -593,13 +593,14 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
     ProfScope p(c, "attn");
     KVEV_HIP(c, launch_attention(c, q, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0));
   }
-  const bool inline_moves = max_moves <= kInlineMoves;
   {
     ProfScope p(c, "post");
     KVEV_HIP(c, launch_post(c, out, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0,
-                            do_select ? 1 : 0, B, inline_moves ? 1 : 0));
+                            do_select ? 1 : 0, B));
   }
-  if (do_select && !inline_moves) {
+  // the post kernel plans the compaction; the move kernel copies the rows
+  // (its blocks spread the scattered stores of the channel-major V columns)
+  if (do_select && max_moves > 0) {
     ProfScope p(c, "move");
     KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
   }

@@ -14,7 +14,7 @@ namespace kvev {
 
 constexpr int kAttnChunk = 256;   // slots per attention split
 constexpr int kPostTokens = 64;   // slots per post-attention block
-constexpr int kInlineMoves = 8;   // compaction moves the post kernel copies itself
+constexpr int kPoolTokens = 16;   // slots per block of the sequence-pooled post kernel
 constexpr int kMaxGroupSize = 8;  // query heads per KV head supported
 constexpr int kRegions = 8;       // region labels of the block-granular mode
 constexpr int kMaxBlockEntries = 4096;  // block-table entries per sequence (block mode)
@@ -49,7 +49,6 @@ struct DevState {
   unsigned* grpctr = nullptr;  // [G] arrival counters of the post kernel (0 between launches)
   unsigned long long* blk_key = nullptr;  // [G][max_post_blocks] per-block minimum eviction key
   int* blk_slot = nullptr;                // [G][max_post_blocks] its slot
-  int* blk_page = nullptr;                // [G][max_post_blocks] that slot's page
   float* blk_sum = nullptr;               // [G][max_post_blocks] per-block utility sum
   // block-granular mode
   int* btab = nullptr;      // [batch][maxpages] logical block of each table entry
@@ -164,10 +163,12 @@ struct kvev_ctx {
 namespace kvev {
 
 // Dynamic LDS floats of the sequence-pooled post kernel: per (layer, query
-// head) statistics and entropies, one output's split weights, the slot
-// masses, the layer factors and the per (layer, KV head) norm factors.
+// head) statistics and entropies, one output's split weights, the per
+// (layer, KV head) and per layer slot masses, the layer factors and the per
+// (layer, KV head) norm factors.
 inline int64_t pool_post_shm(int L, int Hq, int Hkv, int64_t S) {
-  return 3ll * L * Hq + (Hq / Hkv) * S + static_cast<int64_t>(L) * (kPostTokens + 1) + static_cast<int64_t>(L) * Hkv;
+  return 3ll * L * Hq + (Hq / Hkv) * S + static_cast<int64_t>(L) * Hkv * (kPoolTokens + 1) +
+         static_cast<int64_t>(L) * (kPoolTokens + 1);
 }
 // Calls fn(std::integral_constant<int, HG>) for a query group size 1..8.
 template <typename Fn>
@@ -192,7 +193,7 @@ hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
 hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                             int n_max, int write_logits);
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                       int refresh, int do_select, int64_t budget, int inline_moves);
+                       int refresh, int do_select, int64_t budget);
 hipError_t launch_select(kvev_ctx* c, int64_t budget);
 hipError_t launch_moves(kvev_ctx* c, int max_moves);
 hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);

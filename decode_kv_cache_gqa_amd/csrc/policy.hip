@@ -6,7 +6,8 @@ namespace kvev {
 // ---------------------------------------------------------------------------
 // Post-attention kernel, grid (blocks per group, groups); block c owns slots
 // [64c, 64c + 64) and, when c < L, the output of layer c.  Every block:
-//  * merges the splits' (max, sum) of all layers of its group;
+//  * merges the splits' (max, sum) of all layers of its group (a block that
+//    does not fold: only those of its output layer);
 //  * block c < L writes the attention output of layer c,
 //    out = sum_s e^{m_s - M} o_s / Z;
 //  * on an observation step, folds its slots' probability mass layer by
@@ -24,9 +25,10 @@ namespace kvev {
 // last block to finish (arrival counter, no waiting) gives the new token the
 // mean utility on a non-observation step (appendix E "New token insertion"),
 // records its position, commits the count and, when asked, selects and
-// compacts: with one token over budget the eviction is the minimum of the
-// published keys and the new token's key, and the only move copies the new
-// token (slot B) into the hole; otherwise a full radix select runs.
+// plans the compaction: with one token over budget the eviction is the
+// minimum of the published keys and the new token's key, and the only move
+// takes the new token (slot B) into the hole; otherwise a full radix select
+// runs.  The move kernel copies the planned K/V rows afterwards.
 // Data handed between blocks is written through to device scope and read
 // with device-scope loads; no agent-scope fence is used (on this GPU it
 // writes back the whole L2).
@@ -46,7 +48,6 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   __shared__ float red[NT / kWave];
   __shared__ unsigned long long s_key[NT / kWave];
   __shared__ int s_slot[NT / kWave];
-  __shared__ int s_page[NT / kWave];
   __shared__ int s_last;
   const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
   const int n = A.count[g] + 1;
@@ -77,17 +78,20 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
   }
   float prior = 0.f;
-  int mypos = 0, mypage = 0;
+  int mypos = 0;
   if (tid < kPostTok && t < n - 1) {
     prior = gs[t];
     mypos = gp[t];
-    mypage = A.ptab[static_cast<int64_t>(g) * A.maxpages + t / kPageTokens];
   }
+  // statistics merged: every layer's for a folding block, else only those
+  // of the block's output layer
+  const int m0 = fold ? 0 : c * HG;
+  const int m1 = fold ? L * HG : (c < L ? m0 + HG : 0);
   float2 pm[kMergeBatch];
-  const int ml_l = tid / HG, ml_h = tid % HG;
+  const int ml_l = (m0 + tid) / HG, ml_h = (m0 + tid) % HG;
   const float2* pmb = reinterpret_cast<const float2*>(A.part_ml) +
                       (static_cast<int64_t>(ml_l) * A.G + g) * A.S * HG + ml_h;
-  if (tid < L * HG) {
+  if (m0 + tid < m1) {
 #pragma unroll
     for (int k = 0; k < kMergeBatch; ++k) pm[k] = k < ns ? pmb[k * HG] : make_float2(-INFINITY, 0.f);
   }
@@ -103,13 +107,13 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
   }
 
-  // ---- merge every layer's split statistics: (M, Z) per (layer, head) ------
-  for (int i = tid; i < L * HG; i += NT) {
+  // ---- merge the split statistics: (M, Z) per (layer, head) ----------------
+  for (int i = m0 + tid; i < m1; i += NT) {
     float M = -INFINITY, Z = 0.f, U = 0.f;
     const int64_t sb = (static_cast<int64_t>(i / HG) * A.G + g) * A.S * HG + i % HG;
     for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
       float2 v[kMergeBatch];
-      if (i == tid && s0 == 0) {
+      if (i == m0 + tid && s0 == 0) {
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) v[k] = pm[k];
       } else {
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 
   // ---- attention output of layer c (after the block's arrival: the
   // selection does not wait on it) ------------------------------------------------
-  auto write_output = [&]() {
+  auto write_output = [&]() __attribute__((always_inline)) {
     if (c >= L) return;
     const int l = c;
     const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * A.S * HG;
@@ -232,17 +236,14 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       key = (static_cast<unsigned long long>(float_key(myscore)) << 32) | static_cast<uint32_t>(mypos);
       slot = t;
     }
-    int page = mypage;
     float sum = mine ? myscore : 0.f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const unsigned long long y = __shfl_xor(key, o, kWave);
       const int ys = __shfl_xor(slot, o, kWave);
-      const int yp = __shfl_xor(page, o, kWave);
       if (y < key) {
         key = y;
         slot = ys;
-        page = yp;
       }
     }
     sum = wave_sum(sum);
@@ -250,7 +251,6 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       const int64_t bi = static_cast<int64_t>(g) * A.max_blk + c;
       st_coherent(A.blk_key + bi, key);
       st_coherent(A.blk_slot + bi, slot);
-      st_coherent(A.blk_page + bi, page);
       st_coherent(A.blk_sum + bi, sum);
     }
   }
@@ -270,40 +270,21 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
 
   // ---- the group's last block ------------------------------------------------
-  // Everything it may need is loaded in one batch: the block summaries, the
-  // new token's utility (observation step) and page, and, for the move of
-  // the new token into a hole, its K/V rows from the step inputs.
+  // It loads the block summaries and the new token's utility (observation
+  // step) in one batch.
   const bool one_over = A.do_select && n == A.B + 1;
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int NCH = (64 * LPR + NT - 1) / NT;  // 16-byte row pieces per thread (L <= 64)
-  uint4 kpre[NCH], vpre[NCH];
-  if (one_over) {
-    // unconditional loads (index clamped into the rows): a conditionally
-    // written array would be placed in scratch and its loads serialised
-#pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int idx = min(u * NT + tid, L * LPR - 1);
-      const int64_t in = (static_cast<int64_t>((idx / LPR) * Bsz + b) * A.Hkv + kvh) * D + (idx % LPR) * EPL;
-      kpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.k_new) + in);
-      vpre[u] = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.v_new) + in);
-    }
-  }
-  const int newpage = A.ptab[static_cast<int64_t>(g) * A.maxpages + (n - 1) / kPageTokens];
   const float newscore_obs = A.refresh ? ld_state<true>(gs + (n - 1)) : 0.f;
   float part = 0.f;
   unsigned long long bkey = ~0ull;
-  int bslot = -1, bpage = 0;
+  int bslot = -1;
   for (int i = tid; i < A.nblk; i += NT) {
     const int64_t bi = static_cast<int64_t>(g) * A.max_blk + i;
     part += ld_state<true>(A.blk_sum + bi);
     const unsigned long long k2 = ld_state<true>(A.blk_key + bi);
     const int s2 = ld_state<true>(A.blk_slot + bi);
-    const int p2 = ld_state<true>(A.blk_page + bi);
     if (k2 < bkey) {
       bkey = k2;
       bslot = s2;
-      bpage = p2;
     }
   }
   part = wave_sum(part);
@@ -311,30 +292,25 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long y = __shfl_xor(bkey, o, kWave);
     const int ys = __shfl_xor(bslot, o, kWave);
-    const int yp = __shfl_xor(bpage, o, kWave);
     if (y < bkey) {
       bkey = y;
       bslot = ys;
-      bpage = yp;
     }
   }
   if (lane == 0) {
     red[tid / kWave] = part;
     s_key[tid / kWave] = bkey;
     s_slot[tid / kWave] = bslot;
-    s_page[tid / kWave] = bpage;
   }
   __syncthreads();
   float total = 0.f;
   bkey = s_key[0];
   bslot = s_slot[0];
-  bpage = s_page[0];
   for (int w = 0; w < NT / kWave; ++w) {
     total += red[w];
     if (s_key[w] < bkey) {
       bkey = s_key[w];
       bslot = s_slot[w];
-      bpage = s_page[w];
     }
   }
   float newscore = newscore_obs;
@@ -362,48 +338,28 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       if (kn < bkey) {
         bkey = kn;
         bslot = n - 1;
-        bpage = newpage;
       }
     }
     final_n = A.B;
     if (bslot < 0) {
       if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
     } else if (bslot < A.B) {
-      // the new token (slot B) fills the hole: state, then its K/V rows
-      const int ev = bslot, rd = ev % kPageTokens;
+      // the new token (slot B) fills the hole: state here, the K/V rows by
+      // the move kernel (its blocks spread the V column's scattered stores)
+      const int ev = bslot;
       if (tid == 0) {
         gp[ev] = newest;
         gs[ev] = newscore;
+        A.mv_src[static_cast<int64_t>(g) * A.cap] = A.B;
+        A.mv_dst[static_cast<int64_t>(g) * A.cap] = ev;
       }
-      T* kp = static_cast<T*>(A.kpool);
-      T* vp = static_cast<T*>(A.vpool);
-#pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        const int idx = u * NT + tid;
-        if (idx >= L * LPR) continue;
-        const int l = idx / LPR, c0 = (idx % LPR) * EPL;
-        *reinterpret_cast<uint4*>(kp + kidx(l, bpage, rd, c0, A.P, D)) = kpre[u];
-        const uint32_t vw[4] = {vpre[u].x, vpre[u].y, vpre[u].z, vpre[u].w};
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          // element e of the 16-byte piece (bf16: half words; fp32: words)
-          const uint32_t bits = EPL == 8 ? (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu : vw[e & 3];
-          T x;
-          __builtin_memcpy(&x, &bits, sizeof(T));
-          vp[vidx(l, bpage, rd, c0 + e, A.P, D)] = x;
-        }
-      }
+      nm = 1;
     }
   } else if (A.do_select && n > A.B) {
     int* src = A.mv_src + static_cast<int64_t>(g) * A.cap;
     int* dst = A.mv_dst + static_cast<int64_t>(g) * A.cap;
     nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag);
     final_n = A.B;
-    if (A.inline_moves) {
-      copy_moves<T, D, NT>(static_cast<T*>(A.kpool), static_cast<T*>(A.vpool),
-                           A.ptab + static_cast<int64_t>(g) * A.maxpages, src, dst, nm, L, A.P, A.cap);
-      nm = 0;
-    }
   }
   if (tid == 0) {
     A.count[g] = final_n;
@@ -568,7 +524,7 @@ hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd) {
 
 template <typename T, int D>
 static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                            int refresh, int do_select, int64_t budget, int inline_moves) {
+                            int refresh, int do_select, int64_t budget) {
   constexpr int NT = 256;
   const auto& cf = c->cfg;
   PostArgs A;
@@ -586,7 +542,6 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.grpctr = c->d.grpctr;
   A.blk_key = c->d.blk_key;
   A.blk_slot = c->d.blk_slot;
-  A.blk_page = c->d.blk_page;
   A.blk_sum = c->d.blk_sum;
   A.max_blk = c->max_post_blocks;
   A.k_new = k_new;
@@ -615,12 +570,12 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.B = static_cast<int>(budget);
   A.n_sink = cf.n_sink;
   A.n_recent = cf.n_recent;
-  A.inline_moves = inline_moves;
   const int tok_blocks = (n_max + kPostTok - 1) / kPostTok;
   if (c->pooled) {
     // one grid row per sequence; blocks cover the slots and the (layer, KV head) outputs
     const int outs = cf.n_layers * cf.n_kv_heads;
-    A.nblk = tok_blocks > outs ? tok_blocks : outs;
+    const int slot_blocks = (n_max + kPoolTokens - 1) / kPoolTokens;
+    A.nblk = slot_blocks > outs ? slot_blocks : outs;
     return launch_pool_post<T, D>(c, A);
   }
   A.nblk = tok_blocks > cf.n_layers ? tok_blocks : cf.n_layers;
@@ -638,13 +593,13 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
 }
 
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                       int refresh, int do_select, int64_t budget, int inline_moves) {
+                       int refresh, int do_select, int64_t budget) {
   const int D = c->cfg.head_dim;
   if (c->cfg.dtype == KVEV_BF16)
-    return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves)
-                    : post_impl<bf16_t, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves);
-  return D == 128 ? post_impl<float, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves)
-                  : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, inline_moves);
+    return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget)
+                    : post_impl<bf16_t, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget);
+  return D == 128 ? post_impl<float, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget)
+                  : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget);
 }
 
 hipError_t launch_select(kvev_ctx* c, int64_t budget) {

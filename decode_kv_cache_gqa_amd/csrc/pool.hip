@@ -12,34 +12,43 @@ namespace kvev {
 // head group of a sequence holds the same slots; the sequence's first group
 // (g0 = b * Hkv) carries the positions and utilities.  Grid (blocks per
 // sequence, sequences), kPoolNT threads.  Block c:
-//  * merges the split statistics of every (layer, query head) of the
-//    sequence;
+//  * when it folds (observation step, slots [16c, 16c + 16) exist), merges
+//    the split statistics of every (layer, query head) of the sequence;
+//    otherwise only those of its output;
 //  * when c < L * Hkv, writes the output of layer c % L, KV head c / L;
-//  * folds its 64 slots' pooled mass layer by layer:
+//  * folds its slots' pooled mass layer by layer:
 //    mass_l[t] = (1/Hq) sum over KV heads of (sum over the group's heads of
 //    p), with the scorer variants' factors (VNorm per KV head; entropy: the
-//    mean over all Hq heads);
+//    mean over all Hq heads).  The 64 lanes of a slot each take (layer, KV
+//    head) pairs, every logit row of a lane loaded at once; the per-pair
+//    masses are summed over KV heads in a fixed order;
 //  * publishes its minimum eviction key and utility sum.
-// The sequence's last block selects once and applies the result to every
-// KV head's pages: the new token into the hole (one over budget) or the
-// full selection's moves.  Same hand-off rules as post_kernel.
+// The sequence's last block selects once (one over budget: the minimum of
+// the published keys and the new token's; otherwise the radix select) and
+// plans the compaction in its first group's move lists; the move kernel then
+// copies every KV head's rows.  Same hand-off rules as post_kernel.
 // ---------------------------------------------------------------------------
-constexpr int kPoolNT = 1024;
-constexpr int kPoolKvBatch = 8;  // KV heads whose logit rows are loaded together
+constexpr int kPoolNT = 512;
+constexpr int kPoolTok = kPoolTokens;             // slots per block
+constexpr int kPoolLanes = kPoolNT / kPoolTok;    // lanes per slot
+constexpr int kPoolPairs = 8;                     // (layer, KV head) rows per lane and batch (<= 4 heads)
+static_assert(kPoolTok <= kWave, "a block's slots fit one wave");
 
 template <typename T, int D, int HG, bool SC>
 __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   constexpr int NT = kPoolNT;
-  constexpr int LG = NT / kPostTok;  // layer lanes per slot
-  static_assert(HG * D <= NT, "one output element per thread");
+  constexpr int EO = (HG * D + NT - 1) / NT;  // output elements per thread
+  constexpr int PP = HG <= 4 ? kPoolPairs : kPoolPairs / 2;  // rows per lane and batch
   extern __shared__ float dyn[];
   const int L = A.L, Hkv = A.Hkv, Hq = A.Hq;
-  float* s_ml = dyn;                     // [L][Hq][2]
-  float* s_w = s_ml + L * Hq * 2;        // [HG][S] split weights of this block's output
-  float* s_mass = s_w + HG * A.S;        // [L][kPostTok]
-  float* s_ent = s_mass + L * kPostTok;  // [L][Hq] normalised entropies (entropy scorer)
-  float* s_lw = s_ent + L * Hq;          // [L] layer factor: 1/Hq, times the entropy mean
-  float* s_vw = s_lw + L;                // [L][Hkv] n / sum of the value norms (VNorm)
+  const int LK = L * Hkv;
+  float* s_ml = dyn;                      // [L][Hq][2]
+  float* s_w = s_ml + L * Hq * 2;         // [HG][S] split weights of this block's output
+  float* s_part = s_w + HG * A.S;         // [L * Hkv][kPoolTok] per (layer, KV head) masses
+  float* s_mass = s_part + LK * kPoolTok; // [L][kPoolTok]
+  float* s_ent = s_mass + L * kPoolTok;   // [L][Hq] normalised entropies (entropy scorer)
+  float* s_lw = s_ent + L * Hq;           // [L] layer factor: 1/Hq, times the entropy mean
+  float* s_vw = s_lw + L;                 // [L][Hkv] n / sum of the value norms (VNorm)
   __shared__ float red[NT / kWave];
   __shared__ unsigned long long s_key[NT / kWave];
   __shared__ int s_slot[NT / kWave];
@@ -50,33 +59,54 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   const int newest = A.nextpos[g0];
   const int ns = (n + A.CT - 1) / A.CT;
   const int Bsz = A.G / Hkv;
-  const int tbase = c * kPostTok;
+  const int tbase = c * kPoolTok;
   int* gp = A.pos + static_cast<int64_t>(g0) * A.cap;
   float* gs = A.score + static_cast<int64_t>(g0) * A.cap;
   auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
   const bool ent = SC && A.part_u != nullptr, vn = SC && A.vnorm != nullptr;
-  const int tl = tid % kPostTok, lg = tid / kPostTok;
-  const int t = tbase + tl;
   const bool fold = A.refresh && tbase < n;
+  // mass phase: slot ts of the block, lane j of the slot's kPoolLanes
+  const int ts = tid % kPoolTok, j = tid / kPoolTok;
+  const int t = tbase + ts;
 
   float prior = 0.f;
   int mypos = 0;
-  if (tid < kPostTok && t < n - 1) {
+  if (tid < kPoolTok && t < n - 1) {
     prior = gs[t];
     mypos = gp[t];
   }
-  // this block's output: layer c % L, KV head c / L (loaded before the merges)
-  const bool outb = c < L * Hkv;
+  // the first batch of this lane's logit rows (pairs j, j + kPoolLanes, ...)
+  float x[PP][HG], vx[PP];
+  auto load_pairs = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PP; ++u) {
+      const int pr = min(j + (k0 + u) * kPoolLanes, LK - 1);
+      const int l = pr / Hkv, kv = pr % Hkv;
+      const int64_t r = (static_cast<int64_t>(g0 + kv) * L + l) * A.lstride + min(t, n - 1);
+      load_heads<HG>(A.logits + r * HG, x[u]);
+      vx[u] = vn ? A.vnorm[r] : 1.f;
+    }
+  };
+  if (fold) load_pairs(0);
+  // this block's output: layer c % L, KV head c / L
+  const bool outb = c < LK;
   const int ol = c % L, okv = c / L;
-  float po[kMergeBatch];
+  float po[EO][kMergeBatch];
   const float* pob = A.part_o + (static_cast<int64_t>(ol) * A.G + g0 + (outb ? okv : 0)) * A.S * HG * D;
   if (outb) {
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) po[k] = (tid < HG * D && k < ns) ? pob[k * HG * D + tid] : 0.f;
+    for (int e = 0; e < EO; ++e) {
+      const int idx = tid + e * NT;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) po[e][k] = (idx < HG * D && k < ns) ? pob[k * HG * D + idx] : 0.f;
+    }
   }
 
-  // ---- (M, Z) of every (layer, query head) of the sequence -------------------
-  for (int i = tid; i < L * Hq; i += NT) {
+  // ---- (M, Z) per (layer, query head): every one for a folding block, else
+  // only those of the block's output -----------------------------------------------
+  const int m0 = fold ? 0 : ol * Hq + okv * HG;
+  const int m1 = fold ? L * Hq : (outb ? m0 + HG : 0);
+  for (int i = m0 + tid; i < m1; i += NT) {
     const int l = i / Hq, hq = i % Hq;
     const int64_t sb = (static_cast<int64_t>(l) * A.G + g0 + hq / HG) * A.S * HG + hq % HG;
     const float2* pb = reinterpret_cast<const float2*>(A.part_ml) + sb;
@@ -109,7 +139,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     if (ent) s_ent[i] = n > 1 ? (__logf(Z) + U / Z) / __logf(static_cast<float>(n)) : 1.f;
   }
   if (vn && fold) {
-    for (int i = tid; i < L * Hkv; i += NT) {
+    for (int i = tid; i < LK; i += NT) {
       const float* pv = A.part_vn + (static_cast<int64_t>(i / Hkv) * A.G + g0 + i % Hkv) * A.S;
       float sum = 0.f;
       for (int s = 0; s < ns; ++s) sum += pv[s];
@@ -117,6 +147,32 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     }
   }
   __syncthreads();
+
+  auto write_output = [&]() __attribute__((always_inline)) {
+    if (!outb) return;
+    const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(ol) * A.G + g0 + okv) * A.S * HG;
+    const float* ml = &s_ml[(ol * Hq + okv * HG) * 2];
+    for (int i = tid; i < HG * ns; i += NT) {
+      const int h = i / ns, s = i % ns;
+      const float ms = pml[s * HG + h].x;
+      s_w[h * A.S + s] = ms == -INFINITY ? 0.f : __expf(ms - ml[2 * h]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EO; ++e) {
+      const int idx = tid + e * NT;
+      if (idx >= HG * D) continue;
+      const int h = idx / D, cc = idx % D;
+      float o = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) o += k < ns ? s_w[h * A.S + k] * po[e][k] : 0.f;
+      for (int s = kMergeBatch; s < ns; ++s) o += s_w[h * A.S + s] * pob[s * HG * D + idx];
+      A.out[(static_cast<int64_t>(ol * Bsz + b) * Hq + okv * HG + h) * D + cc] = o / ml[2 * h + 1];
+    }
+  };
+
+  // ---- pooled mass per (layer, slot), then the layer-ordered fold ------------
+  float myscore = prior;
   if (fold) {
     for (int l = tid; l < L; l += NT) {
       float e = 1.f;
@@ -127,68 +183,37 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
       }
       s_lw[l] = e / static_cast<float>(Hq);
     }
-  }
-
-  auto write_output = [&]() {
-    if (!outb) return;
-    const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(ol) * A.G + g0 + okv) * A.S * HG;
-    const float* ml = &s_ml[(ol * Hq + okv * HG) * 2];
-    for (int i = tid; i < HG * ns; i += NT) {
-      const int h = i / ns, s = i % ns;
-      const float ms = pml[s * HG + h].x;
-      s_w[h * A.S + s] = ms == -INFINITY ? 0.f : __expf(ms - ml[2 * h]);
-    }
-    __syncthreads();
-    if (tid < HG * D) {
-      const int h = tid / D, cc = tid % D;
-      float o = 0.f;
+    for (int k0 = 0; j + k0 * kPoolLanes < LK; k0 += PP) {
+      if (k0 > 0) load_pairs(k0);
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) o += k < ns ? s_w[h * A.S + k] * po[k] : 0.f;
-      for (int s = kMergeBatch; s < ns; ++s) o += s_w[h * A.S + s] * pob[s * HG * D + tid];
-      A.out[(static_cast<int64_t>(ol * Bsz + b) * Hq + okv * HG + h) * D + cc] = o / ml[2 * h + 1];
-    }
-  };
-
-  // ---- pooled mass per (layer, slot), then the layer-ordered fold ------------
-  float myscore = prior;
-  if (fold) {
-    __syncthreads();  // s_lw
-    if (t < n) {
-      for (int l = lg; l < L; l += LG) {
-        float acc = 0.f;
-        for (int k0 = 0; k0 < Hkv; k0 += kPoolKvBatch) {
-          float x[kPoolKvBatch][HG], v[kPoolKvBatch];
+      for (int u = 0; u < PP; ++u) {
+        const int pr = j + (k0 + u) * kPoolLanes;
+        if (pr >= LK) continue;
+        const int l = pr / Hkv, kv = pr % Hkv;
+        const float* ml = &s_ml[(l * Hq + kv * HG) * 2];
+        float m = 0.f;
 #pragma unroll
-          for (int u = 0; u < kPoolKvBatch; ++u) {
-            const int kv = min(k0 + u, Hkv - 1);
-            const int64_t r = (static_cast<int64_t>(g0 + kv) * L + l) * A.lstride + t;
-            load_heads<HG>(A.logits + r * HG, x[u]);
-            v[u] = vn ? A.vnorm[r] : 1.f;
-          }
-#pragma unroll
-          for (int u = 0; u < kPoolKvBatch; ++u) {
-            const int kv = k0 + u;
-            if (kv >= Hkv) continue;
-            const float* ml = &s_ml[(l * Hq + kv * HG) * 2];
-            float m = 0.f;
-#pragma unroll
-            for (int h = 0; h < HG; ++h) m += __expf(x[u][h] - ml[2 * h]) / ml[2 * h + 1];
-            if (vn) {
-              const float w = s_vw[l * Hkv + kv];
-              m *= w > 0.f ? v[u] * w : 1.f;
-            }
-            acc += m;
-          }
+        for (int h = 0; h < HG; ++h) m += __expf(x[u][h] - ml[2 * h]) / ml[2 * h + 1];
+        if (vn) {
+          const float w = s_vw[pr];
+          m *= w > 0.f ? vx[u] * w : 1.f;
         }
-        s_mass[l * kPostTok + tl] = acc * s_lw[l];
+        s_part[pr * kPoolTok + ts] = m;
       }
     }
     __syncthreads();
-    if (tid < kPostTok && t < n) {
+    for (int i = tid; i < L * kPoolTok; i += NT) {
+      const int l = i / kPoolTok, sl = i % kPoolTok;
+      float acc = 0.f;
+      for (int kv = 0; kv < Hkv; ++kv) acc += s_part[(l * Hkv + kv) * kPoolTok + sl];
+      s_mass[i] = acc * s_lw[l];
+    }
+    __syncthreads();
+    if (tid < kPoolTok && t < n) {
       float m = (t == n - 1) ? 0.f : prior;
       const float keep = 1.0f - A.a;
       for (int l = 0; l < L; ++l) {
-        const float mass = s_mass[l * kPostTok + tl];
+        const float mass = s_mass[l * kPoolTok + tid];
         m = A.cumulative ? m + mass : A.a * mass + keep * m;
       }
       st_coherent(gs + t, m);
@@ -196,9 +221,9 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     }
   }
 
-  // ---- block summary over slots other than the new token's -------------------
-  if (tid < kPostTok) {
-    const bool mine = t < n - 1;
+  // ---- block summary over slots other than the new token's (wave 0) ---------------
+  if (tid < kWave) {
+    const bool mine = tid < kPoolTok && t < n - 1;
     unsigned long long key = ~0ull;
     int slot = -1;
     if (mine && is_cand(mypos)) {
@@ -309,45 +334,23 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     if (bslot < 0) {
       if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
     } else if (bslot < A.B) {
-      // the new token (slot B) fills the hole in every KV head's pages
-      const int ev = bslot, rd = ev % kPageTokens;
+      // the new token (slot B) fills the hole: the move is planned here and
+      // copied for every KV head and layer by the move kernel, whose blocks
+      // spread the scattered stores of the channel-major V column
+      const int ev = bslot;
       if (tid == 0) {
         gp[ev] = newest;
         gs[ev] = newscore;
+        A.mv_src[static_cast<int64_t>(g0) * A.cap] = A.B;
+        A.mv_dst[static_cast<int64_t>(g0) * A.cap] = ev;
       }
-      constexpr int EPL = Vec16<T>::N;
-      constexpr int LPR = D / EPL;
-      T* kp = static_cast<T*>(A.kpool);
-      T* vp = static_cast<T*>(A.vpool);
-      for (int idx = tid; idx < L * Hkv * LPR; idx += NT) {
-        const int l = idx / (Hkv * LPR), kv = (idx / LPR) % Hkv, c0 = (idx % LPR) * EPL;
-        const int page = A.ptab[static_cast<int64_t>(g0 + kv) * A.maxpages + ev / kPageTokens];
-        const int64_t in = (static_cast<int64_t>(l * Bsz + b) * Hkv + kv) * D + c0;
-        const uint4 kr = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.k_new) + in);
-        const uint4 vr = *reinterpret_cast<const uint4*>(static_cast<const T*>(A.v_new) + in);
-        *reinterpret_cast<uint4*>(kp + kidx(l, page, rd, c0, A.P, D)) = kr;
-        const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const uint32_t bits = EPL == 8 ? (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu : vw[e & 3];
-          T x;
-          __builtin_memcpy(&x, &bits, sizeof(T));
-          vp[vidx(l, page, rd, c0 + e, A.P, D)] = x;
-        }
-      }
+      nm = 1;
     }
   } else if (A.do_select && n > A.B) {
     int* src = A.mv_src + static_cast<int64_t>(g0) * A.cap;
     int* dst = A.mv_dst + static_cast<int64_t>(g0) * A.cap;
     nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag);
     final_n = A.B;
-    if (A.inline_moves) {
-      for (int kv = 0; kv < Hkv; ++kv)
-        copy_moves<T, D, NT>(static_cast<T*>(A.kpool), static_cast<T*>(A.vpool),
-                             A.ptab + static_cast<int64_t>(g0 + kv) * A.maxpages, src, dst, nm, L, A.P,
-                             A.cap);
-      nm = 0;
-    }
   }
   if (tid == 0) {
     for (int h = 0; h < Hkv; ++h) {
@@ -365,15 +368,11 @@ hipError_t launch_pool_post(kvev_ctx* c, const PostArgs& A) {
   const size_t shm = pool_post_shm(cf.n_layers, cf.n_q_heads, cf.n_kv_heads, A.S) * sizeof(float);
   return with_group(c->HG, [&](auto hg) -> hipError_t {
     constexpr int HG = decltype(hg)::value;
-    if constexpr (HG * D <= kPoolNT) {
-      if (A.part_u || A.vnorm)
-        pool_post_kernel<T, D, HG, true><<<grid, kPoolNT, shm, c->stream>>>(A);
-      else
-        pool_post_kernel<T, D, HG, false><<<grid, kPoolNT, shm, c->stream>>>(A);
-      return hipGetLastError();
-    } else {
-      return hipErrorInvalidValue;
-    }
+    if (A.part_u || A.vnorm)
+      pool_post_kernel<T, D, HG, true><<<grid, kPoolNT, shm, c->stream>>>(A);
+    else
+      pool_post_kernel<T, D, HG, false><<<grid, kPoolNT, shm, c->stream>>>(A);
+    return hipGetLastError();
   });
 }
 

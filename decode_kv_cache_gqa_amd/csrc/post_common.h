@@ -1,6 +1,6 @@
 // Device helpers shared by the post-attention kernels: the top-budget
-// selection with its compaction plan, the K/V move copies, slot-state
-// access across blocks, and the kernels' argument block.
+// selection with its compaction plan, slot-state access across blocks, and
+// the kernels' argument block.
 #pragma once
 #include "common.h"
 #include "kvev_internal.h"
@@ -235,55 +235,6 @@ __device__ int select_group(int n, int B, int newest, int n_sink, int n_recent,
   return nm;
 }
 
-// Copy `nm` planned moves of one group for every layer: the K row (16-byte
-// pieces of a token-major page) and the V column (D elements of a
-// channel-major page).  The page table is shared by all layers, so each
-// move's two pages are looked up once; all loads of a batch are issued
-// before its stores.
-template <typename T, int D, int NT>
-__device__ void copy_moves(T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ pt,
-                           const int* __restrict__ src, const int* __restrict__ dst, int nm, int L,
-                           int64_t P, int64_t cap) {
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int KB = 4;  // 16-byte K pieces per thread per batch
-  constexpr int VB = 8;  // V elements per thread per batch
-  for (int j = 0; j < nm; ++j) {
-    const int s = src[j], d = dst[j];
-    if (s < 0 || s >= cap || d < 0 || d >= cap) continue;
-    const int ps = pt[s / kPageTokens], pd = pt[d / kPageTokens];
-    const int rs = s % kPageTokens, rd = d % kPageTokens;
-    for (int base = 0; base < L * LPR; base += NT * KB) {
-      uint4 v[KB];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * LPR)
-          v[u] = *reinterpret_cast<const uint4*>(kpool + kidx(idx / LPR, ps, rs, (idx % LPR) * EPL, P, D));
-      }
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * LPR)
-          *reinterpret_cast<uint4*>(kpool + kidx(idx / LPR, pd, rd, (idx % LPR) * EPL, P, D)) = v[u];
-      }
-    }
-    for (int base = 0; base < L * D; base += NT * VB) {
-      T v[VB];
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * D) v[u] = vpool[vidx(idx / D, ps, rs, idx % D, P, D)];
-      }
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int idx = base + u * NT + threadIdx.x;
-        if (idx < L * D) vpool[vidx(idx / D, pd, rd, idx % D, P, D)] = v[u];
-      }
-    }
-  }
-}
-
 constexpr int kPostTok = kPostTokens;  // slots per post block (one wave's worth)
 constexpr int kMergeBatch = 16;
 
@@ -302,7 +253,6 @@ struct PostArgs {
   unsigned* grpctr;
   unsigned long long* blk_key;
   int* blk_slot;
-  int* blk_page;
   float* blk_sum;
   int* mv_src;
   int* mv_dst;
@@ -316,7 +266,7 @@ struct PostArgs {
   int L, G, Hkv, Hq, S, CT, maxpages, max_blk;
   int64_t cap, P, lstride;
   float a;
-  int cumulative, refresh, do_select, B, n_sink, n_recent, inline_moves, nblk;
+  int cumulative, refresh, do_select, B, n_sink, n_recent, nblk;
 };
 
 // HG consecutive fp32 logits (one slot of one layer)
