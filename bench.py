@@ -104,9 +104,10 @@ def measured_traffic(profile=TRAFFIC_PROFILE, sources=ATTN_SOURCES):
 
 
 def cpu_baseline(w, steps=300):
-    """Time the CPU oracle on a bounded sample: steady steps of ONE (sequence,
-    KV head) group at the workload's real shape (32 layers, budget+1 tokens,
-    4 query heads, d=128), scaled to the whole step (8 groups)."""
+    """Time the CPU oracle on a bounded sample: steady steps of ONE selection
+    group at the workload's real shape (all layers, budget+1 tokens), scaled
+    to the whole step.  A group is one (sequence, KV head), or one sequence
+    with all its KV heads in the per-sequence mode."""
     import numpy as np
     import oracle as orc
     try:
@@ -115,11 +116,22 @@ def cpu_baseline(w, steps=300):
     except Exception:
         cores = 1
     B = w.budget
-    o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=B,
-                            alpha_new=w.alpha_new, n_sink=w.n_sink, n_recent=w.n_recent,
-                            capacity=B + steps + 2)
-    K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0, heads=[0])
-    o.prefill(0, K.float().numpy(), V.float().numpy(), heads=[0])
+    pooled = w.granularity == "sequence"
+    kw = dict(budget=B, alpha_new=w.alpha_new, n_sink=w.n_sink, n_recent=w.n_recent,
+              capacity=B + steps + 2, scorer=w.scorer,
+              policy="cumulative" if w.policy == "cumulative" else "ema",
+              refresh_interval=w.refresh_interval, score_free=w.score_free)
+    if pooled:
+        steps = max(steps // w.n_kv_heads, 8)
+        o = orc.PooledTokenOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, **kw)
+        K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0)
+        o.prefill(0, K.float().numpy(), V.float().numpy())
+        groups = w.batch
+    else:
+        o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, **kw)
+        K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0, heads=[0])
+        o.prefill(0, K.float().numpy(), V.float().numpy(), heads=[0])
+        groups = w.n_kv_heads * w.batch
     ins = [w.step_inputs(t, seqs=[0]) for t in range(1, steps + 2)]
     ins = [tuple(x.float().numpy() for x in s) for s in ins]
     o.decode_step(1, *ins[0], [0])
@@ -129,11 +141,11 @@ def cpu_baseline(w, steps=300):
         o.decode_step(t, *ins[t - 1], [0])
         o.evict()
     dt = time.perf_counter() - t0
-    per_group = dt / steps
-    full_step = per_group * w.n_kv_heads * w.batch
+    full_step = dt / steps * groups
+    unit = "sequence" if pooled else "(sequence, KV head)"
     return {"value": 1.0 / full_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} steady steps of 1 of {w.n_kv_heads * w.batch} (sequence, KV head) "
-                      f"groups at {w.n_layers} layers x {B + 1} tokens, scaled x{w.n_kv_heads * w.batch}"}
+            "sample": f"{steps} steady steps of 1 of {groups} {unit} groups at {w.n_layers} layers x "
+                      f"{B + 1} tokens, scaled x{groups}"}
 
 
 def tier_bytes(w, n_fp_tokens, n_q):
@@ -405,7 +417,8 @@ def main():
         "config": {"workload": w.name, "layers": w.n_layers, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "batch": w.batch,
                    "prefill": w.prefill_lens[0], "budget": w.budget, "n_sink": w.n_sink,
-                   "n_recent": w.n_recent, "alpha_new": w.alpha_new},
+                   "n_recent": w.n_recent, "alpha_new": w.alpha_new, "scorer": w.scorer,
+                   "granularity": w.granularity},
         "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
         "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,
@@ -417,8 +430,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": measured_traffic(),
-            "kernel": "attn_mfma_kernel",
+            # the committed counters were taken on the 32k workload only
+            "traffic": measured_traffic() if args.workload == "llama8b_32k" else None,
+            "kernel": "attn_mfma_kernel" if w.dtype == "bf16" and w.head_dim == 128 else "attn_valu_kernel",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
