@@ -1022,9 +1022,17 @@ class TieredOracle:
     n_sink: int = 0
     n_recent: int = 0
     capacity: int = 0
+    route_interval: int = 1
     layers: dict = field(default_factory=dict)
     npos: int = 0
     last_mass: dict = field(default_factory=dict)
+
+    def routes_after(self, t):
+        """Routing events follow the decode steps t with t = 0 mod Omega
+        ([QEvict] §4.2 Eq.1, "every Omega generated tokens"; the scores
+        accumulate every step, Eq.1's sum over the interval).  Omega <= 1:
+        every step."""
+        return t % max(self.route_interval, 1) == 0
 
     @property
     def group_size(self):

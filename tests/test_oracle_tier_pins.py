@@ -263,3 +263,61 @@ def test_int2_windows_change_the_output_by_the_reconstruction_only():
         _, tiers_now, ledger_now = o.window_state(0)
         promoted |= set(np.flatnonzero((tiers_now == 0) & ledger_now).tolist())
     assert promoted, "some window should be promoted back from the INT2 tier"
+
+
+def test_no_routing_event_within_the_interval_is_full_attention():
+    """With an interval beyond the run no routing event happens ([QEvict]
+    §4.2 Eq.1: events only at t = 0 mod Omega), so even with tight
+    capacities every step is softmax attention over the whole cache and
+    every window stays full precision."""
+    rng = np.random.default_rng(25)
+    L, Hq, Hkv, d, n, T = 1, 4, 2, 32, 60, 10
+    K, V, q, kn, vn = _inputs(rng, L, Hq, Hkv, d, n, T)
+    o = orc.TieredOracle(L, Hq, Hkv, d, k_f=1, k_q=1, window=8, n_sink=2, n_recent=4,
+                         route_interval=T + 1)
+    o.prefill(K, V)
+    Kall, Vall = K.astype(np.float64), V.astype(np.float64)
+    for t in range(1, T + 1):
+        out = o.decode_step(t, q[t - 1], kn[t - 1], vn[t - 1])
+        Kall = np.concatenate([Kall, kn[t - 1][:, :, None].astype(np.float64)], 2)
+        Vall = np.concatenate([Vall, vn[t - 1][:, :, None].astype(np.float64)], 2)
+        qq = torch.from_numpy(q[t - 1, 0].astype(np.float64)).reshape(Hkv, Hq // Hkv, d)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, torch.from_numpy(Kall[0]), torch.from_numpy(Vall[0])).reshape(Hq, d).numpy()
+        np.testing.assert_allclose(out[0], ref, rtol=0, atol=1e-12)
+        assert not o.routes_after(t)
+        _, tiers, ledger = o.window_state(0)
+        assert (tiers == 0).all() and not ledger.any()
+
+
+def test_routing_every_omega_steps():
+    """Omega = 4: tiers change only after steps 4, 8, ...; at each event the
+    candidates are the windows kept by the previous event plus those aged
+    since (Eq.4), ranked by the score accumulated over every step (Eq.1,
+    Eq.5); attention mass is conserved throughout."""
+    rng = np.random.default_rng(26)
+    L, Hq, Hkv, d, n, T, omega = 1, 4, 2, 32, 90, 24, 4
+    K, V, q, kn, vn = _inputs(rng, L, Hq, Hkv, d, n, T, heavy=6.0)
+    o = orc.TieredOracle(L, Hq, Hkv, d, k_f=2, k_q=3, window=8, n_sink=3, n_recent=8,
+                         route_interval=omega)
+    o.prefill(K, V)
+    prev = o.window_state(0)[1].copy()
+    for t in range(1, T + 1):
+        o.decode_step(t, q[t - 1], kn[t - 1], vn[t - 1])
+        S, tiers, _ = o.window_state(0)
+        assert abs(S.sum() - t) < 1e-10
+        if not o.routes_after(t):
+            np.testing.assert_array_equal(tiers[:len(prev)], prev)
+            assert (tiers[len(prev):] == 0).all()  # windows opened since stay full precision
+            prev = tiers.copy()
+            continue
+        cand = [w for w in range(o.n_windows()) if o.is_aged(w) and tiers[w] != 2]
+        F, Q, E = orc.route_tiers(S, cand, 2, 3)
+        o.route()
+        S2, tiers2, _ = o.window_state(0)
+        np.testing.assert_array_equal(S2, S)
+        assert sorted(np.flatnonzero(tiers2 == 1).tolist()) == Q
+        routed_f = [w for w in np.flatnonzero(tiers2 == 0).tolist() if w in cand]
+        assert routed_f == F
+        assert all(tiers2[w] == 2 for w in E)
+        prev = tiers2.copy()
