@@ -31,7 +31,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 # stream (the per-kernel averages and the roofline come from those launches).
 # An event record costs about 3.7 us of GPU time, so profiling every step
 # would inflate the step time by about 12% on the 32k workload.
-PROF_EVERY = 8
+PROF_EVERY = 7  # coprime with the tiered routing interval 8, so routing steps are sampled too
 
 
 def timed_steps(ctx, inputs, out, first, total):
@@ -172,7 +172,8 @@ def tier_cpu_baseline(w, steps=3):
         cores = 1
     o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                          k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
-                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 2)
+                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 2,
+                         route_interval=w.route_interval)
     K, V = w.prefill_kv(0, layers=[0])
     o.prefill(K.float().numpy(), V.float().numpy(), layers=[0])
     del K, V
@@ -182,7 +183,8 @@ def tier_cpu_baseline(w, steps=3):
     t0 = time.perf_counter()
     for t in range(2, steps + 2):
         o.decode_step(t, *ins[t - 1])
-        o.route()
+        if o.routes_after(t):
+            o.route()
     per_layer = (time.perf_counter() - t0) / steps
     return {"value": 1.0 / (per_layer * w.n_layers), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{steps} steady steps of layer 0 of {w.n_layers} after the first routing event "

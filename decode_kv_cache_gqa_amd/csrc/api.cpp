@@ -147,6 +147,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) && hg != 4)
     return bad("block and tiered modes: query group size must be 4");
   if (f.scorer & ~(KVEV_SCORE_VNORM | KVEV_SCORE_ENTROPY)) return bad("unknown scorer bits");
+  if (f.route_interval < 0) return bad("route_interval must be >= 0");
   if (f.granularity != KVEV_PER_KV_HEAD && f.granularity != KVEV_PER_SEQUENCE)
     return bad("unknown granularity");
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
@@ -635,7 +636,8 @@ kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void*
   if (c->block_mode) return block_step(c, q, k_new, v_new, out, true, budget);
   if (c->tier_mode) {
     if (kvev_status s = tier_decode(c, q, k_new, v_new, out)) return s;
-    return tier_route(c);
+    const int omega = c->cfg.route_interval > 1 ? c->cfg.route_interval : 1;
+    return c->t % omega == 0 ? tier_route(c) : KVEV_OK;  // routing events at t = 0 mod Omega
   }
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -268,3 +269,17 @@ kvev_status kvev_tier_import(kvev_ctx* c, int32_t layer, int64_t n_windows, cons
 }
 
 }  // extern "C"
+
+kvev_status kvev_tier_capacities(double b_hist, double q, double m_f, double m_q, int32_t* k_f,
+                                 int32_t* k_q) {
+  if (!k_f || !k_q) return KVEV_EINVAL;
+  if (!std::isfinite(b_hist) || !std::isfinite(q) || !std::isfinite(m_f) || !std::isfinite(m_q))
+    return KVEV_EINVAL;
+  if (q < 0.0 || q > 1.0 || b_hist < 0.0 || !(m_f > 0.0) || !(m_q > 0.0)) return KVEV_EINVAL;
+  const double f = std::floor((1.0 - q) * b_hist / m_f);
+  const double g = std::floor(q * b_hist / m_q);
+  if (f > 2147483647.0 || g > 2147483647.0) return KVEV_EINVAL;
+  *k_f = static_cast<int32_t>(f);
+  *k_q = static_cast<int32_t>(g);
+  return KVEV_OK;
+}

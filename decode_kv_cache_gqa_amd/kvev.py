@@ -49,6 +49,7 @@ class Config(ctypes.Structure):
         ("window_tokens", ctypes.c_int32), ("fp_windows", ctypes.c_int32),
         ("int2_windows", ctypes.c_int32),
         ("scorer", ctypes.c_int32), ("granularity", ctypes.c_int32),
+        ("route_interval", ctypes.c_int32),
     ]
 
 
@@ -87,6 +88,7 @@ _SIGS = {
                          + [ctypes.c_void_p] * 6),
     "kvev_tier_import": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
+    "kvev_tier_capacities": (ctypes.c_int, [ctypes.c_double] * 4 + [ctypes.POINTER(ctypes.c_int32)] * 2),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
     "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
@@ -353,6 +355,17 @@ class Context:
         return ms.value, n.value
 
 
+def tier_capacities(b_hist, q, m_f, m_q):
+    """(K_f, K_q) of the two-tier mode from a byte budget (the library's
+    kvev_tier_capacities; host arithmetic)."""
+    kf, kq = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().kvev_tier_capacities(float(b_hist), float(q), float(m_f), float(m_q), ctypes.byref(kf),
+                                    ctypes.byref(kq))
+    if st != OK:
+        raise KvevError(st, "invalid tier capacity arguments")
+    return kf.value, kq.value
+
+
 def context_for(w, max_steps=None, budget=None, stream=None):
     """A context configured for a synth.Workload."""
     steps = w.steps if max_steps is None else max_steps
@@ -374,7 +387,7 @@ def context_for(w, max_steps=None, budget=None, stream=None):
             head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,
             max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=TIERED_INT2,
             n_sink=w.n_sink, n_recent=w.n_recent, budget=1, window_tokens=w.window_tokens,
-            fp_windows=w.fp_windows, int2_windows=w.int2_windows)
+            fp_windows=w.fp_windows, int2_windows=w.int2_windows, route_interval=w.route_interval)
         return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

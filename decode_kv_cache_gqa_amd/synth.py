@@ -135,6 +135,7 @@ class Workload:
     decode_region: int = 4
     scorer: str = "attention"       # attention | vnorm | entropy | vnorm+entropy
     granularity: str = "kv_head"    # kv_head | sequence
+    route_interval: int = 1         # tiered mode: routing events every route_interval steps
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -396,8 +397,11 @@ def workload(name: str) -> Workload:
         return Workload("qevict_131k_fp5_int2_20", 32, 32, 8, 128, "bf16", (131072,), 128,
                         seed=1005, policy="tiered_int2", n_sink=5, n_recent=32, n_epochs=4,
                         epoch_steps=32, window_tokens=32, fp_windows=205, int2_windows=819)
+    if name == "qevict131k_omega8":
+        # the review's routing interval: one routing event every 8 steps (section 4.2 Eq.1)
+        return replace(workload("qevict131k"), name="qevict_131k_fp5_int2_20_omega8", route_interval=8)
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
-             "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k")
+             "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8")

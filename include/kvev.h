@@ -158,6 +158,12 @@ typedef struct {
   /* KVEV_EMA and KVEV_CUMULATIVE only (0 in the other modes). */
   int32_t scorer;                             /* kvev_scorer bit mask; 0: attention */
   int32_t granularity;                        /* kvev_granularity */
+  /* KVEV_TIERED_INT2 only: the routing interval Omega.  kvev_step runs a
+   * routing event after the decode steps t (counted from 1) with
+   * t % Omega == 0; the window scores accumulate every step in between
+   * ("QEvict" review, section 4.2 Eq.1; the review's default is 8).  0 or 1:
+   * every step.  kvev_evict is always one routing event. */
+  int32_t route_interval;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -293,6 +299,20 @@ kvev_status kvev_block_state(kvev_ctx* ctx, int32_t seq, float* score, int32_t* 
 kvev_status kvev_import_blocks(kvev_ctx* ctx, int32_t seq, int64_t n_blocks, const float* score,
                                const int32_t* tref, const uint8_t* resident, int64_t n_tokens,
                                const void* k, const void* v);
+
+/* Tier capacities from a byte budget ("QEvict" review, section 4.3 Eq.3):
+ * *k_f = floor((1 - q) * b_hist / m_f) and *k_q = floor(q * b_hist / m_q),
+ * evaluated in double precision.  b_hist: the bytes left for routed windows
+ * after the sink and local windows (B_total - B_sink - B_local); q: the
+ * quantized-tier fraction in [0, 1] (the review uses 0.70); m_f, m_q: the
+ * bytes of one window in full precision and as an INT2 record, over the
+ * layers and KV heads the budget covers (this library's records: 32 tokens
+ * x 512 B and 3,072 B per layer and KV head).  Host arithmetic only: no
+ * context and no device work.  Errors: KVEV_EINVAL (null outputs, q outside
+ * [0, 1], b_hist < 0, m_f or m_q <= 0, non-finite arguments, a capacity
+ * above INT32_MAX). */
+kvev_status kvev_tier_capacities(double b_hist, double q, double m_f, double m_q, int32_t* k_f,
+                                 int32_t* k_q);
 
 /* ---- KVEV_TIERED_INT2 mode ---------------------------------------------
  * In this mode kvev_prefill takes seq 0; kvev_decode_step appends, attends

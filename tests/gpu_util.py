@@ -481,7 +481,8 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     ctx = kvev.context_for(w, max_steps=steps)
     o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                          k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
-                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1)
+                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1,
+                         route_interval=w.route_interval)
     K, V = w.prefill_kv(0, device=device)
     ctx.prefill(0, K.contiguous(), V.contiguous())
     del K, V
@@ -493,6 +494,7 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     st = Stats()
     st.ledger_checks = 0
     st.promotions = 0
+    st.routing_events = 0
     Hg = w.group_size
     out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
     for t in range(1, steps + 1):
@@ -510,6 +512,7 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
                 st.max_out_err = max(st.max_out_err, check_out(
                     gout[l, 0, h * Hg:(h + 1) * Hg], ref_out[j, h * Hg:(h + 1) * Hg], rtol,
                     f"step {t} out l={l} kvh={h}"))
+        routes = o.routes_after(t)
         if not fused:
             for l in layers:
                 gs, _, _ = ctx.tier_state(l)
@@ -517,10 +520,13 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
                 live = ot != 2
                 st.max_score_err = max(st.max_score_err, check_scores(
                     gs[live], os_[live], rtol, f"step {t} pre-route scores l={l}"))
-            ctx.evict()
+            if routes:
+                ctx.evict()
         prev = {l: o.window_state(l)[1] for l in layers}
         nw_pre = o.n_windows()
-        o.route()
+        if routes:
+            o.route()
+            st.routing_events += 1
         for l in layers:
             gs, gt, gl = ctx.tier_state(l)
             os_, ot, ol = o.window_state(l)

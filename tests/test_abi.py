@@ -5,6 +5,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 from decode_kv_cache_gqa_amd import kvev
@@ -142,3 +143,21 @@ def test_block_entry_points_reject_null_context():
     assert L.kvev_readmit(None, 0, 1, None, None, None) == kvev.EINVAL
     assert L.kvev_block_state(None, 0, None, None, None, 0, None) == kvev.EINVAL
     assert L.kvev_import_blocks(None, 0, 1, None, None, None, 0, None, None) == kvev.EINVAL
+
+
+def test_tier_capacities_match_the_worked_example_and_the_oracle():
+    """kvev_tier_capacities is host arithmetic ("QEvict" review, section 4.3
+    Eq.3): the review's worked example (B_hist = 100 MB, q = 0.70, 1 MB and
+    0.131 MB windows give 30 and 534) and the oracle's function agree."""
+    import oracle as orc
+    MB = 1024 * 1024
+    assert kvev.tier_capacities(100 * MB, 0.70, MB, 0.131 * MB) == (30, 534)
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        b, q = float(rng.uniform(0, 1e10)), float(rng.uniform(0, 1))
+        mf, mq = float(rng.uniform(1e3, 1e7)), float(rng.uniform(1e2, 1e6))
+        assert kvev.tier_capacities(b, q, mf, mq) == orc.tier_capacities(b, q, mf, mq)
+    for bad in [(1.0, 1.5, 1.0, 1.0), (1.0, -0.1, 1.0, 1.0), (-1.0, 0.5, 1.0, 1.0),
+                (1.0, 0.5, 0.0, 1.0), (1.0, 0.5, 1.0, float("nan")), (1e12, 0.5, 1.0, 1.0)]:
+        with pytest.raises(kvev.KvevError):
+            kvev.tier_capacities(*bad)

@@ -78,3 +78,14 @@ def test_tier_max_capacity_sampled():
     w = synth.workload("qevict131k").scaled(n_layers=4, prefill_lens=(196600,))
     st = _gu().run_tier_lockstep(w, 7, sample_layers=[3], kv_every=7, ledger_every=7)
     assert st.steps == 7
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_tier_route_interval_8(fused):
+    """Routing every 8 steps (the review's Omega): window scores accumulate
+    every step, windows aged between events stay full precision until the
+    next event, and tiers change only at t = 0 mod 8."""
+    w = synth.workload("qevict131k_omega8").scaled(n_layers=2, prefill_lens=(700,), fp_windows=5,
+                                                   int2_windows=7, epoch_steps=12, n_epochs=3)
+    st = _gu().run_tier_lockstep(w, 36, fused=fused)
+    assert st.routing_events == 4
