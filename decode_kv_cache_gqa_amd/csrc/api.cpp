@@ -41,7 +41,7 @@ void free_all(kvev_ctx* c) {
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
                   d.grpctr, d.blk_key, d.blk_slot, d.blk_sum, d.btab, d.nres,
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
-                  d.rd_ids, d.part_u, d.vnorm, d.part_vn};
+                  d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -97,6 +97,7 @@ static kvev_status tier_create(const kvev_config& f, void* hip_stream, kvev_ctx*
   c->cap = f.max_tokens;
   c->elem = 2;
   c->count.assign(c->G, 0);
+  c->hole_in.assign(c->G, 0);
   c->prefilled.assign(1, 0);
   c->tier_mode = true;
   c->tw.NW = static_cast<int>((c->cap + kTierWin - 1) / kTierWin);
@@ -228,6 +229,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
                                  : std::max(static_cast<int>((c->cap + 63) / 64), f.n_layers);
   c->elem = f.dtype == KVEV_BF16 ? 2 : 4;
   c->count.assign(c->G, 0);
+  c->hole_in.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
   c->block_mode = block;
   if (block) {
@@ -258,6 +260,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.pos, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.score, static_cast<size_t>(G) * c->cap));
   A(dalloc(&d.count, G));
+  if (!block) A(dalloc(&d.hole, G));  // token modes: the free slot the next token takes
   A(dalloc(&d.nextpos, G));
   // the logit stride is the step's slot count rounded up to 16, which can
   // exceed a capacity that is not a multiple of 16
@@ -305,6 +308,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(hipMemsetAsync(d.score, 0, sizeof(float) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.pos, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.count, 0, sizeof(int) * G, c->stream));
+  if (d.hole) A(hipMemsetAsync(d.hole, 0, sizeof(int) * G, c->stream));
   A(hipMemsetAsync(d.nextpos, 0, sizeof(int) * G, c->stream));
   A(hipMemsetAsync(d.nmoves, 0, sizeof(int) * G, c->stream));
   A(hipMemsetAsync(d.errflag, 0, sizeof(int), c->stream));
@@ -472,6 +476,7 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
                                sizeof(float) * n, c->stream));
     const int cnt = static_cast<int>(n);
     KVEV_HIP(c, hipMemcpyAsync(c->d.count + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
+    KVEV_HIP(c, hipMemcpyAsync(c->d.hole + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
     KVEV_HIP(c, hipMemcpyAsync(c->d.nextpos + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
     KVEV_HIP(c, hipStreamSynchronize(c->stream));  // host buffers above are stack-local
     c->count[g] = n;
@@ -584,7 +589,8 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
   for (int g = 0; g < c->G; ++g) {
     if (c->count[g] + 1 > c->cap) return fail(c, KVEV_ESTATE, "slot capacity exhausted");
     n_max = std::max(n_max, c->count[g] + 1);
-    if (c->count[g] + 1 > B) max_moves = std::max(max_moves, std::min(B, c->count[g] + 1 - B));
+    // one token over budget frees a slot (no move); more plan a hole fill
+    if (c->count[g] + 1 > B + 1) max_moves = std::max(max_moves, std::min(B, c->count[g] + 1 - B));
   }
   for (int g = 0; g < c->G; ++g)
     if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
@@ -607,8 +613,11 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
   }
   for (int g = 0; g < c->G; ++g) {
     c->count[g] += 1;
+    // a single-token eviction leaves its slot free inside the cache
+    c->hole_in[g] = do_select && c->count[g] == B + 1;
     if (do_select && c->count[g] > B) c->count[g] = B;
-    if (do_select) release_pages(c, g, c->count[g]);
+    // the cache spans count + 1 slots (the free slot may lie inside)
+    if (do_select) release_pages(c, g, c->count[g] + 1);
   }
   c->t = t;
   return KVEV_OK;
@@ -651,26 +660,64 @@ kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   int64_t max_moves = 0;
-  bool any = false;
+  bool any = false, inner = false;
   for (int g = 0; g < c->G; ++g) {
     if (c->count[g] > B) {
       any = true;
-      max_moves = std::max(max_moves, std::min(B, c->count[g] - B));
+      inner = inner || c->hole_in[g];
+      // one token over budget frees a slot (no move); more plan a hole fill
+      if (c->count[g] > B + 1) max_moves = std::max(max_moves, std::min(B, c->count[g] - B));
     }
   }
   if (!any) return KVEV_OK;
+  if (inner) {
+    // a free slot inside the cache: the last token moves into it first
+    ProfScope p(c, "move");
+    KVEV_HIP(c, launch_close_holes(c, B));
+    KVEV_HIP(c, launch_moves(c, 1));
+  }
   {
     ProfScope p(c, "select");
     KVEV_HIP(c, launch_select(c, B));
   }
-  {
+  if (max_moves > 0) {
     ProfScope p(c, "move");
     KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
   }
   for (int g = 0; g < c->G; ++g) {
-    if (c->count[g] > B) c->count[g] = B;
-    release_pages(c, g, c->count[g]);
+    if (c->count[g] > B) {
+      c->hole_in[g] = c->count[g] == B + 1;
+      c->count[g] = B;
+    }
+    release_pages(c, g, c->count[g] + 1);
   }
+  return KVEV_OK;
+}
+
+// The free slot of group g (token modes; block mode: count, the end).
+// Synchronises.
+static kvev_status read_hole(kvev_ctx* c, int g, int* hole) {
+  *hole = static_cast<int>(c->count[g]);
+  if (!c->d.hole) return KVEV_OK;
+  KVEV_HIP(c, hipMemcpyAsync(hole, c->d.hole + g, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  if (*hole < 0 || *hole > c->count[g]) return fail(c, KVEV_ESTATE, "inconsistent free slot");
+  return KVEV_OK;
+}
+
+// Copy the count[g] live entries (elem bytes each) of a per-slot array
+// (slots [0, count], the free slot skipped) to host memory.
+static kvev_status copy_live(kvev_ctx* c, int g, const void* base, size_t elem, void* dst) {
+  int h;
+  if (kvev_status s = read_hole(c, g, &h)) return s;
+  const int64_t n = c->count[g];
+  const char* src = static_cast<const char*>(base) + static_cast<int64_t>(g) * c->cap * elem;
+  char* out = static_cast<char*>(dst);
+  if (h > 0) KVEV_HIP(c, hipMemcpyAsync(out, src, elem * h, hipMemcpyDeviceToHost, c->stream));
+  if (n > h)
+    KVEV_HIP(c, hipMemcpyAsync(out + elem * h, src + elem * (h + 1), elem * (n - h), hipMemcpyDeviceToHost,
+                               c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
   return KVEV_OK;
 }
 
@@ -785,10 +832,7 @@ kvev_status kvev_scores(kvev_ctx* c, int32_t seq, int32_t h, float* dst, int64_t
   const int64_t n = c->count[g];
   if (n_written) *n_written = n;
   if (!dst || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
-  KVEV_HIP(c, hipMemcpyAsync(dst, c->d.score + static_cast<int64_t>(g) * c->cap, sizeof(float) * n,
-                             hipMemcpyDeviceToHost, c->stream));
-  KVEV_HIP(c, hipStreamSynchronize(c->stream));
-  return KVEV_OK;
+  return copy_live(c, g, c->d.score, sizeof(float), dst);
 }
 
 kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* positions, int64_t cap,
@@ -801,10 +845,7 @@ kvev_status kvev_retained(kvev_ctx* c, int32_t seq, int32_t h, int32_t* position
   const int64_t n = c->count[g];
   if (n_out) *n_out = n;
   if (!positions || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
-  KVEV_HIP(c, hipMemcpyAsync(positions, c->d.pos + static_cast<int64_t>(g) * c->cap,
-                             sizeof(int) * n, hipMemcpyDeviceToHost, c->stream));
-  KVEV_HIP(c, hipStreamSynchronize(c->stream));
-  return KVEV_OK;
+  return copy_live(c, g, c->d.pos, sizeof(int), positions);
 }
 
 kvev_status kvev_export_kv(kvev_ctx* c, int32_t seq, int32_t h, void* k_out, void* v_out,
@@ -816,7 +857,9 @@ kvev_status kvev_export_kv(kvev_ctx* c, int32_t seq, int32_t h, void* k_out, voi
   const int64_t n = c->count[g];
   if (n_out) *n_out = n;
   if (!k_out || !v_out || cap < n) return fail(c, KVEV_ERANGE, "destination too small");
-  KVEV_HIP(c, launch_export(c, g, k_out, v_out, n, cap));
+  int hole;
+  if (kvev_status s = read_hole(c, g, &hole)) return s;
+  KVEV_HIP(c, launch_export(c, g, k_out, v_out, n, cap, hole));
   return KVEV_OK;
 }
 
@@ -843,9 +886,11 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
                              sizeof(float) * n, hipMemcpyHostToDevice, c->stream));
   const int cnt = static_cast<int>(n);
   KVEV_HIP(c, hipMemcpyAsync(c->d.count + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(c->d.hole + g, &cnt, sizeof(int), hipMemcpyHostToDevice, c->stream));
   KVEV_HIP(c, hipStreamSynchronize(c->stream));
-  release_pages(c, g, n);
+  release_pages(c, g, n + 1);
   c->count[g] = n;
+  c->hole_in[g] = 0;
   return KVEV_OK;
 }
 

@@ -8,9 +8,11 @@
 //   m[h] = max_t s, l[h] = sum_t exp(s - m), o[h][:] = sum_t exp(s - m) v_t
 // The logits are stored (fp32) for the probability pass, which normalises
 // them once every split's (m, l) is merged; the post kernel does the merge.
-// The group's cache holds count[g] tokens in slots [0, count); the new
-// token is slot count[g]: it is read from k_new / v_new and written into its
-// page by the lanes that hold it.
+// The group's cache holds count[g] tokens in slots [0, count] minus one free
+// slot, hole[g] (count[g] itself unless the last eviction removed a single
+// token and left its slot free); the new token takes the free slot: it is
+// read from k_new / v_new and written into its page by the lanes that hold
+// it.  Without a hole array (block mode) the free slot is count[g].
 #include "common.h"
 #include "kvev_internal.h"
 
@@ -63,10 +65,10 @@ template <int NW, int HG, bool SC>
 __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
-    const int* __restrict__ ptab, const int* __restrict__ count, float* __restrict__ logits,
-    float* __restrict__ part_ml, float* __restrict__ part_o, float* __restrict__ part_u,
-    float* __restrict__ vnorm, float* __restrict__ part_vn, int L, int G, int Hkv, int Hq,
-    int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits) {
+    const int* __restrict__ ptab, const int* __restrict__ count, const int* __restrict__ hole,
+    float* __restrict__ logits, float* __restrict__ part_ml, float* __restrict__ part_o,
+    float* __restrict__ part_u, float* __restrict__ vnorm, float* __restrict__ part_vn, int L, int G,
+    int Hkv, int Hq, int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits) {
   static_assert(HG >= 1 && HG <= 8, "group size");
   constexpr int D = 128, NG = 4, WT = NG * 16;
   __shared__ __align__(16) float p_lds[NW][HG][WT];
@@ -87,9 +89,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
 #pragma unroll
   for (int j = 0; j < NG; ++j) pages[j] = pt[min((wt0 + 16 * j) / kPageTokens, maxpages - 1)];
   const int n = count[g] + 1;  // slots including the new token
+  const int tnew = hole ? hole[g] : n - 1;
   if (t0 >= n) return;
   const int B = G / Hkv, b = g / Hkv, kvh = g % Hkv;
-  const int tnew = n - 1;
   const int64_t new_off = (static_cast<int64_t>(l * B + b) * Hkv + kvh) * D;
   // SC: compiled with the scorer variants' outputs (present when non-null)
   const bool ent = SC && part_u != nullptr, vn = SC && vnorm != nullptr;
@@ -326,8 +328,9 @@ template <typename T, int D, int HG, int NT, int CT, bool SC>
 __global__ __launch_bounds__(NT) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k_new, const T* __restrict__ v_new,
     T* __restrict__ kpool, T* __restrict__ vpool, const int* __restrict__ ptab,
-    const int* __restrict__ count, float* __restrict__ logits, float* __restrict__ part_ml,
-    float* __restrict__ part_o, float* __restrict__ part_u, float* __restrict__ vnorm,
+    const int* __restrict__ count, const int* __restrict__ hole, float* __restrict__ logits,
+    float* __restrict__ part_ml, float* __restrict__ part_o, float* __restrict__ part_u,
+    float* __restrict__ vnorm,
     float* __restrict__ part_vn, int L, int G, int Hkv, int Hq, int64_t P, int maxpages,
     int64_t lstride, int S, float scale, int write_logits) {
   constexpr int EPL = Vec16<T>::N;
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(NT) void attn_valu_kernel(
   const int B = G / Hkv, b = g / Hkv, kvh = g % Hkv;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int sub = lane % LPT, tslot = lane / LPT;
-  const int tnew = n - 1;
+  const int tnew = hole ? hole[g] : n - 1;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
   const int64_t new_off = (static_cast<int64_t>(l * B + b) * Hkv + kvh) * D + sub * EPL;
 
@@ -562,7 +565,7 @@ static hipError_t attention_valu(kvev_ctx* c, const void* q, const void* k_new, 
   auto launch = [&](auto kern) {
     kern<<<grid, NT, 0, c->stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k_new), static_cast<const T*>(v_new),
-        static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.count,
+        static_cast<T*>(c->d.kpool), static_cast<T*>(c->d.vpool), c->d.ptab, c->d.count, c->d.hole,
         c->d.logits, c->d.part_ml, c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads,
         cf.n_q_heads, c->P, c->maxpages, c->lstride, splits, 1.0f / sqrtf(static_cast<float>(D)),
         write_logits);
@@ -590,7 +593,7 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
         kern<<<grid, kMfmaNW * kWave, 0, c->stream>>>(
             static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
             static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
-            static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.logits, c->d.part_ml,
+            static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.hole, c->d.logits, c->d.part_ml,
             c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
             c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f), write_logits);
       };

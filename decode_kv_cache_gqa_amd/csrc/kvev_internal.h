@@ -34,6 +34,8 @@ struct DevState {
   int* pos = nullptr;      // [G][cap] position of each slot
   float* score = nullptr;  // [G][cap] utility of each slot
   int* count = nullptr;    // [G] tokens in the group
+  int* hole = nullptr;     // [G] the free slot the next token takes (token modes): count, or the
+                           // slot a single-token eviction freed (the cache then spans count + 1 slots)
   int* nextpos = nullptr;  // [G] position the next appended token takes
   float* logits = nullptr; // [G][L][lstride][HG] fp32 logits of the current step
   float* part_ml = nullptr;// [L][G][S][HG][2] per-split (max, sum), S = splits of the step
@@ -138,6 +140,8 @@ struct kvev_ctx {
   kvev::DevState d;
   // host mirrors (kept exact: every count change is deterministic)
   std::vector<int64_t> count;
+  std::vector<uint8_t> hole_in;             // token modes: the free slot may lie inside (after a
+                                            // single-token eviction; an append fills it)
   std::vector<int> prefilled;               // per sequence
   std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
   std::vector<int> free_pages;
@@ -195,8 +199,11 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
                        int refresh, int do_select, int64_t budget);
 hipError_t launch_select(kvev_ctx* c, int64_t budget);
+// plans the move of each over-budget group's last token into its inner free slot
+hipError_t launch_close_holes(kvev_ctx* c, int64_t budget);
 hipError_t launch_moves(kvev_ctx* c, int max_moves);
-hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap);
+// the n rows of slots [0, n] other than slot `skip` (n + 1 > skip: the free slot)
+hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap, int64_t skip);
 hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n);
 // block-granular mode (block.hip)
 hipError_t launch_block_open(kvev_ctx* c, int n_max, int t);

@@ -24,11 +24,11 @@ namespace kvev {
 // All loads a block needs are issued before the first use.  The group's
 // last block to finish (arrival counter, no waiting) gives the new token the
 // mean utility on a non-observation step (appendix E "New token insertion"),
-// records its position, commits the count and, when asked, selects and
-// plans the compaction: with one token over budget the eviction is the
-// minimum of the published keys and the new token's key, and the only move
-// takes the new token (slot B) into the hole; otherwise a full radix select
-// runs.  The move kernel copies the planned K/V rows afterwards.
+// records its position, commits the count and, when asked, selects: with one
+// token over budget the eviction is the minimum of the published keys and
+// the new token's key, and the evicted slot becomes the group's free slot,
+// which the next token takes (nothing moves); otherwise a full radix select
+// plans the hole fill, and the move kernel copies the planned K/V rows.
 // Data handed between blocks is written through to device scope and read
 // with device-scope loads; no agent-scope fence is used (on this GPU it
 // writes back the whole L2).
@@ -50,7 +50,8 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   __shared__ int s_slot[NT / kWave];
   __shared__ int s_last;
   const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
-  const int n = A.count[g] + 1;
+  const int n = A.count[g] + 1;  // slots spanned, the new token's included
+  const int hn = A.hole[g];       // the new token's slot
   const int newest = A.nextpos[g];
   const int ns = (n + A.CT - 1) / A.CT;
   const int Bsz = A.G / A.Hkv, b = g / A.Hkv, kvh = g % A.Hkv;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   float prior = 0.f;
   int mypos = 0;
-  if (tid < kPostTok && t < n - 1) {
+  if (tid < kPostTok && t < n && t != hn) {
     prior = gs[t];
     mypos = gp[t];
   }
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
     __syncthreads();
     if (tid < kPostTok && t < n) {
-      float m = (t == n - 1) ? 0.f : prior;
+      float m = (t == hn) ? 0.f : prior;
       const float keep = 1.0f - A.a;
       for (int l = 0; l < L; ++l) {
         const float mass = s_mass[l * kPostTok + tl];
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 
   // ---- block summary over slots other than the new token's -------------------
   if (tid < kPostTok) {
-    const bool mine = t < n - 1;
+    const bool mine = t < n && t != hn;
     unsigned long long key = ~0ull;
     int slot = -1;
     if (mine && is_cand(mypos)) {
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   // It loads the block summaries and the new token's utility (observation
   // step) in one batch.
   const bool one_over = A.do_select && n == A.B + 1;
-  const float newscore_obs = A.refresh ? ld_state<true>(gs + (n - 1)) : 0.f;
+  const float newscore_obs = A.refresh ? ld_state<true>(gs + hn) : 0.f;
   float part = 0.f;
   unsigned long long bkey = ~0ull;
   int bslot = -1;
@@ -316,10 +317,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   float newscore = newscore_obs;
   if (!A.refresh) {
     newscore = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
-    if (tid == 0) st_coherent(gs + (n - 1), newscore);
+    if (tid == 0) st_coherent(gs + hn, newscore);
   }
   if (tid == 0) {
-    st_coherent(gp + (n - 1), newest);
+    st_coherent(gp + hn, newest);
     A.nextpos[g] = newest + 1;
     A.grpctr[g] = 0u;
   }
@@ -329,40 +330,37 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     __syncthreads();
   }
 
-  int final_n = n, nm = 0;
+  // every slot of [0, n) now holds a token; new_hole is the slot the next
+  // token takes
+  int final_n = n, nm = 0, new_hole = n;
   if (one_over) {
-    // one over budget: evict the smallest key, the new token included
+    // one over budget: evict the smallest key, the new token included; the
+    // evicted slot stays free for the next token, so nothing moves
     if (is_cand(newest)) {
       const unsigned long long kn =
           (static_cast<unsigned long long>(float_key(newscore)) << 32) | static_cast<uint32_t>(newest);
       if (kn < bkey) {
         bkey = kn;
-        bslot = n - 1;
+        bslot = hn;
       }
     }
     final_n = A.B;
     if (bslot < 0) {
       if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
-    } else if (bslot < A.B) {
-      // the new token (slot B) fills the hole: state here, the K/V rows by
-      // the move kernel (its blocks spread the V column's scattered stores)
-      const int ev = bslot;
-      if (tid == 0) {
-        gp[ev] = newest;
-        gs[ev] = newscore;
-        A.mv_src[static_cast<int64_t>(g) * A.cap] = A.B;
-        A.mv_dst[static_cast<int64_t>(g) * A.cap] = ev;
-      }
-      nm = 1;
+      new_hole = hn;
+    } else {
+      new_hole = bslot;
     }
   } else if (A.do_select && n > A.B) {
     int* src = A.mv_src + static_cast<int64_t>(g) * A.cap;
     int* dst = A.mv_dst + static_cast<int64_t>(g) * A.cap;
-    nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag);
+    nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag,
+                                new_hole);
     final_n = A.B;
   }
   if (tid == 0) {
     A.count[g] = final_n;
+    A.hole[g] = new_hole;
     A.nmoves[g] = nm;
   }
   write_output();
@@ -373,7 +371,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 // its first group's state, whose plan every KV head's moves then follow.
 constexpr int kSelNT = 1024;
 __global__ __launch_bounds__(kSelNT) void select_kernel(
-    int* __restrict__ count, int* __restrict__ pos, float* __restrict__ score,
+    int* __restrict__ count, int* __restrict__ hole, int* __restrict__ pos, float* __restrict__ score,
     const int* __restrict__ nextpos, int* __restrict__ mv_src, int* __restrict__ mv_dst,
     int* __restrict__ nmoves, int* __restrict__ errflag, int64_t cap, int B, int n_sink,
     int n_recent, int pool) {
@@ -385,17 +383,48 @@ __global__ __launch_bounds__(kSelNT) void select_kernel(
       for (int h = 0; h < ng; ++h) nmoves[g + h] = 0;
     return;
   }
+  int new_hole = B;
   const int nm = select_group<kSelNT, false>(n, B, nextpos[g] - 1, n_sink, n_recent,
                                       pos + static_cast<int64_t>(g) * cap,
                                       score + static_cast<int64_t>(g) * cap,
                                       mv_src + static_cast<int64_t>(g) * cap,
-                                      mv_dst + static_cast<int64_t>(g) * cap, errflag);
+                                      mv_dst + static_cast<int64_t>(g) * cap, errflag, new_hole);
   if (threadIdx.x == 0) {
     for (int h = 0; h < ng; ++h) {
       nmoves[g + h] = nm;
       count[g + h] = B;
+      hole[g + h] = new_hole;
     }
   }
+}
+
+// Before a standalone selection: a group whose free slot lies inside its
+// cache (count tokens spread over slots [0, count] after a single-token
+// eviction) gets its last token (slot count) planned into the free slot, so
+// that the selection sees its tokens in slots [0, count).  One thread per
+// group; in the sequence-pooled mode (pool = Hkv) the state and the plan are
+// the sequence's first group's, and every group of the sequence follows it.
+__global__ void close_hole_kernel(const int* __restrict__ count, int* __restrict__ hole,
+                                  int* __restrict__ pos, float* __restrict__ score,
+                                  int* __restrict__ mv_src, int* __restrict__ mv_dst,
+                                  int* __restrict__ nmoves, int64_t cap, int G, int B, int pool) {
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= G) return;
+  const int n = count[g], h = hole[g];
+  int nm = 0;
+  if (n > B && h < n) {
+    const int gc = pool ? g / pool * pool : g;
+    if (g == gc) {
+      const int64_t o = static_cast<int64_t>(gc) * cap;
+      pos[o + h] = pos[o + n];
+      score[o + h] = score[o + n];
+      mv_src[o] = n;
+      mv_dst[o] = h;
+    }
+    hole[g] = n;
+    nm = 1;
+  }
+  nmoves[g] = nm;
 }
 
 // K/V moves of the compaction plan: block (chunk of moves, group, layer).
@@ -473,15 +502,16 @@ __global__ __launch_bounds__(NT) void group_copy_kernel(T* __restrict__ kd, T* _
                                                         T* __restrict__ kpool, T* __restrict__ vpool,
                                                         const int* __restrict__ ptab, int g,
                                                         int64_t n, int64_t ld, int64_t P,
-                                                        int maxpages, int dir) {
+                                                        int maxpages, int dir, int64_t skip) {
   const int l = blockIdx.y;
   const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
   for (int64_t idx = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; idx < n * D;
        idx += static_cast<int64_t>(gridDim.x) * NT) {
-    const int64_t t = idx / D;
+    const int64_t i = idx / D;             // dense row
+    const int64_t t = i + (i >= skip);     // its slot (the free slot is skipped)
     const int c = static_cast<int>(idx % D);
     const int page = pt[t / kPageTokens], r = static_cast<int>(t % kPageTokens);
-    const int64_t dense = (static_cast<int64_t>(l) * ld + t) * D + c;
+    const int64_t dense = (static_cast<int64_t>(l) * ld + i) * D + c;
     if (dir == 0) {
       kd[dense] = kpool[kidx(l, page, r, c, P, D)];
       vd[dense] = vpool[vidx(l, page, r, c, P, D)];
@@ -529,6 +559,7 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   const auto& cf = c->cfg;
   PostArgs A;
   A.count = c->d.count;
+  A.hole = c->d.hole;
   A.pos = c->d.pos;
   A.score = c->d.score;
   A.nextpos = c->d.nextpos;
@@ -602,12 +633,20 @@ hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v
                   : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget);
 }
 
+hipError_t launch_close_holes(kvev_ctx* c, int64_t budget) {
+  constexpr int NT = 256;
+  close_hole_kernel<<<(c->G + NT - 1) / NT, NT, 0, c->stream>>>(
+      c->d.count, c->d.hole, c->d.pos, c->d.score, c->d.mv_src, c->d.mv_dst, c->d.nmoves, c->cap, c->G,
+      static_cast<int>(budget), c->pooled ? c->cfg.n_kv_heads : 0);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(kvev_ctx* c, int64_t budget) {
   const auto& cf = c->cfg;
   const int pool = c->pooled ? cf.n_kv_heads : 0;
   select_kernel<<<pool ? cf.batch : c->G, kSelNT, 0, c->stream>>>(
-      c->d.count, c->d.pos, c->d.score, c->d.nextpos, c->d.mv_src, c->d.mv_dst, c->d.nmoves,
-      c->d.errflag, c->cap, static_cast<int>(budget), cf.n_sink, cf.n_recent, pool);
+      c->d.count, c->d.hole, c->d.pos, c->d.score, c->d.nextpos, c->d.mv_src, c->d.mv_dst,
+      c->d.nmoves, c->d.errflag, c->cap, static_cast<int>(budget), cf.n_sink, cf.n_recent, pool);
   return hipGetLastError();
 }
 
@@ -654,7 +693,7 @@ hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const voi
 
 template <typename T, int D>
 static hipError_t group_copy_impl(kvev_ctx* c, int g, void* k, void* v, int64_t n, int64_t ld,
-                                  int dir) {
+                                  int dir, int64_t skip) {
   constexpr int NT = 256;
   int64_t bx = (n * D + NT - 1) / NT;
   if (bx < 1) return hipSuccess;
@@ -662,24 +701,27 @@ static hipError_t group_copy_impl(kvev_ctx* c, int g, void* k, void* v, int64_t 
   dim3 grid(static_cast<unsigned>(bx), c->cfg.n_layers);
   group_copy_kernel<T, D, NT><<<grid, NT, 0, c->stream>>>(
       static_cast<T*>(k), static_cast<T*>(v), static_cast<T*>(c->d.kpool),
-      static_cast<T*>(c->d.vpool), c->d.ptab, g, n, ld, c->P, c->maxpages, dir);
+      static_cast<T*>(c->d.vpool), c->d.ptab, g, n, ld, c->P, c->maxpages, dir, skip);
   return hipGetLastError();
 }
 
-static hipError_t group_copy(kvev_ctx* c, int g, void* k, void* v, int64_t n, int64_t ld, int dir) {
+static hipError_t group_copy(kvev_ctx* c, int g, void* k, void* v, int64_t n, int64_t ld, int dir,
+                             int64_t skip) {
   const int D = c->cfg.head_dim;
-  if (c->cfg.dtype == KVEV_BF16) return D == 128 ? group_copy_impl<bf16_t, 128>(c, g, k, v, n, ld, dir)
-                                                 : group_copy_impl<bf16_t, 64>(c, g, k, v, n, ld, dir);
-  return D == 128 ? group_copy_impl<float, 128>(c, g, k, v, n, ld, dir)
-                  : group_copy_impl<float, 64>(c, g, k, v, n, ld, dir);
+  if (c->cfg.dtype == KVEV_BF16)
+    return D == 128 ? group_copy_impl<bf16_t, 128>(c, g, k, v, n, ld, dir, skip)
+                    : group_copy_impl<bf16_t, 64>(c, g, k, v, n, ld, dir, skip);
+  return D == 128 ? group_copy_impl<float, 128>(c, g, k, v, n, ld, dir, skip)
+                  : group_copy_impl<float, 64>(c, g, k, v, n, ld, dir, skip);
 }
 
-hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap) {
-  return group_copy(c, g, k_out, v_out, n, cap, 0);
+hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap,
+                         int64_t skip) {
+  return group_copy(c, g, k_out, v_out, n, cap, 0, skip);
 }
 
 hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n) {
-  return group_copy(c, g, const_cast<void*>(k), const_cast<void*>(v), n, n, 1);
+  return group_copy(c, g, const_cast<void*>(k), const_cast<void*>(v), n, n, 1, n);
 }
 
 }  // namespace kvev

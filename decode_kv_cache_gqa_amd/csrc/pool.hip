@@ -23,10 +23,11 @@ namespace kvev {
 //    head) pairs, every logit row of a lane loaded at once; the per-pair
 //    masses are summed over KV heads in a fixed order;
 //  * publishes its minimum eviction key and utility sum.
-// The sequence's last block selects once (one over budget: the minimum of
-// the published keys and the new token's; otherwise the radix select) and
-// plans the compaction in its first group's move lists; the move kernel then
-// copies every KV head's rows.  Same hand-off rules as post_kernel.
+// The sequence's last block selects once: one over budget, the minimum of
+// the published keys and the new token's, whose slot becomes every KV
+// head's free slot (nothing moves); otherwise the radix select plans the
+// hole fill in its first group's move lists, and the move kernel copies
+// every KV head's rows.  Same hand-off rules as post_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kPoolNT = 512;
 constexpr int kPoolTok = kPoolTokens;             // slots per block
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   __shared__ int s_last;
   const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
   const int g0 = b * Hkv;
-  const int n = A.count[g0] + 1;
+  const int n = A.count[g0] + 1;  // slots spanned, the new token's included
+  const int hn = A.hole[g0];       // the new token's slot
   const int newest = A.nextpos[g0];
   const int ns = (n + A.CT - 1) / A.CT;
   const int Bsz = A.G / Hkv;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
 
   float prior = 0.f;
   int mypos = 0;
-  if (tid < kPoolTok && t < n - 1) {
+  if (tid < kPoolTok && t < n && t != hn) {
     prior = gs[t];
     mypos = gp[t];
   }
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     }
     __syncthreads();
     if (tid < kPoolTok && t < n) {
-      float m = (t == n - 1) ? 0.f : prior;
+      float m = (t == hn) ? 0.f : prior;
       const float keep = 1.0f - A.a;
       for (int l = 0; l < L; ++l) {
         const float mass = s_mass[l * kPoolTok + tid];
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
 
   // ---- block summary over slots other than the new token's (wave 0) ---------------
   if (tid < kWave) {
-    const bool mine = tid < kPoolTok && t < n - 1;
+    const bool mine = tid < kPoolTok && t < n && t != hn;
     unsigned long long key = ~0ull;
     int slot = -1;
     if (mine && is_cand(mypos)) {
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
 
   // ---- the sequence's last block ------------------------------------------------
   const bool one_over = A.do_select && n == A.B + 1;
-  const float newscore_obs = A.refresh ? ld_state<true>(gs + (n - 1)) : 0.f;
+  const float newscore_obs = A.refresh ? ld_state<true>(gs + hn) : 0.f;
   float part = 0.f;
   unsigned long long bkey = ~0ull;
   int bslot = -1;
@@ -308,10 +310,10 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   float newscore = newscore_obs;
   if (!A.refresh) {
     newscore = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
-    if (tid == 0) st_coherent(gs + (n - 1), newscore);
+    if (tid == 0) st_coherent(gs + hn, newscore);
   }
   if (tid == 0) {
-    st_coherent(gp + (n - 1), newest);
+    st_coherent(gp + hn, newest);
     for (int h = 0; h < Hkv; ++h) A.nextpos[g0 + h] = newest + 1;
     A.grpctr[g0] = 0u;
   }
@@ -320,41 +322,37 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     __syncthreads();
   }
 
-  int final_n = n, nm = 0;
+  // every slot of [0, n) now holds a token; new_hole is the slot the next
+  // token takes in every KV head's pages
+  int final_n = n, nm = 0, new_hole = n;
   if (one_over) {
+    // one over budget: the evicted slot stays free for the next token
     if (is_cand(newest)) {
       const unsigned long long kn =
           (static_cast<unsigned long long>(float_key(newscore)) << 32) | static_cast<uint32_t>(newest);
       if (kn < bkey) {
         bkey = kn;
-        bslot = n - 1;
+        bslot = hn;
       }
     }
     final_n = A.B;
     if (bslot < 0) {
       if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
-    } else if (bslot < A.B) {
-      // the new token (slot B) fills the hole: the move is planned here and
-      // copied for every KV head and layer by the move kernel, whose blocks
-      // spread the scattered stores of the channel-major V column
-      const int ev = bslot;
-      if (tid == 0) {
-        gp[ev] = newest;
-        gs[ev] = newscore;
-        A.mv_src[static_cast<int64_t>(g0) * A.cap] = A.B;
-        A.mv_dst[static_cast<int64_t>(g0) * A.cap] = ev;
-      }
-      nm = 1;
+      new_hole = hn;
+    } else {
+      new_hole = bslot;
     }
   } else if (A.do_select && n > A.B) {
     int* src = A.mv_src + static_cast<int64_t>(g0) * A.cap;
     int* dst = A.mv_dst + static_cast<int64_t>(g0) * A.cap;
-    nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag);
+    nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag,
+                                new_hole);
     final_n = A.B;
   }
   if (tid == 0) {
     for (int h = 0; h < Hkv; ++h) {
       A.count[g0 + h] = final_n;
+      A.hole[g0 + h] = new_hole;
       A.nmoves[g0 + h] = nm;
     }
   }

@@ -16,9 +16,13 @@ namespace kvev {
 // (1): forcing F then taking the best B is optimal).  The k-th smallest key
 // comes from an LDS radix select on order-preserving 32-bit score keys (four
 // 8-bit digits), plus a radix select on positions only when equal scores
-// straddle the cut; k == 1 is an argmin.  Plan: holes = unkept slots < B
-// ascending, movers = kept slots >= B ascending, mover j fills hole j.
-// Positions and utilities are moved here; returns the number of moves.
+// straddle the cut; k == 1 is an argmin.  With k == 1 nothing moves: the
+// evicted slot becomes the group's free slot, which the next token takes
+// (*new_hole = that slot; the cache then spans B + 1 slots).  Otherwise the
+// plan is the hole fill: holes = unkept slots < B ascending, movers = kept
+// slots >= B ascending, mover j fills hole j (*new_hole = B).  All n slots
+// hold tokens on entry.  Positions and utilities are moved here; returns the
+// number of moves.
 // ---------------------------------------------------------------------------
 template <int NT>
 __device__ __forceinline__ void scan_256(const int* hist, int* excl_out, int* wsum, int tid) {
@@ -58,7 +62,7 @@ __device__ __forceinline__ void st_coherent(T* p, T v) {
 template <int NT, bool COH>
 __device__ int select_group(int n, int B, int newest, int n_sink, int n_recent,
                             int* __restrict__ gp, float* __restrict__ gs, int* __restrict__ src,
-                            int* __restrict__ dst, int* __restrict__ errflag) {
+                            int* __restrict__ dst, int* __restrict__ errflag, int& new_hole) {
   static_assert(NT >= 256, "selection needs >= 256 threads");
   __shared__ int hist[256];
   __shared__ int excl[256];
@@ -121,18 +125,13 @@ __device__ int select_group(int n, int B, int newest, int n_sink, int n_recent,
     __syncthreads();
     if (best == ~0ull || ev < 0) {  // no candidate: impossible when B >= |protected|
       if (tid == 0) atomicOr(errflag, 2);
+      new_hole = B;
       return 0;
     }
-    if (ev >= B) return 0;  // the evicted token sits at slot B: nothing moves
-    if (tid == 0) {
-      src[0] = B;
-      dst[0] = ev;
-      gp[ev] = ld_state<COH>(gp + B);
-      gs[ev] = ld_state<COH>(gs + B);
-    }
-    __syncthreads();
-    return 1;
+    new_hole = ev;  // the evicted slot is the next token's
+    return 0;
   }
+  new_hole = B;
 
   {
     uint32_t prefix = 0, mask = 0;
@@ -240,6 +239,7 @@ constexpr int kMergeBatch = 16;
 
 struct PostArgs {
   int* count;
+  int* hole;
   int* pos;
   float* score;
   int* nextpos;

@@ -55,14 +55,26 @@ def check_out(gpu, ref, rtol, what):
 
 
 def expected_after_evict(scores, pos_pre, B, n_sink, n_recent):
-    """The oracle's selection + hole-fill applied to the GPU's own pre-evict
-    scores and slot layout (fp32 widened to fp64 exactly)."""
+    """The positions the oracle's selection keeps from the GPU's own
+    pre-evict scores (fp32 widened to fp64 exactly), sorted."""
     keep = orc.select_keep(np.asarray(scores, np.float64), pos_pre, B, n_sink, n_recent)
-    moves = orc.hole_fill_moves(keep, B)
-    post = np.array(pos_pre, copy=True)
-    for s, d in moves:
-        post[d] = post[s]
-    return post[: min(B, len(post))]
+    return np.sort(np.asarray(pos_pre)[keep])
+
+
+def by_position(pos, *arrays):
+    """Positions and per-slot arrays sorted by position.  The library keeps
+    its own slot order (a single-token eviction leaves its slot free for the
+    next token; larger evictions fill holes), so parity is checked position
+    by position."""
+    o = np.argsort(np.asarray(pos), kind="stable")
+    return (np.asarray(pos)[o],) + tuple(np.asarray(a)[o] for a in arrays)
+
+
+def rows_by_position(K, pos_ref, pos_want):
+    """Rows (axis 1 of K [L, n, d]) of the positions pos_want, taken from an
+    array laid out by pos_ref."""
+    idx = {p: j for j, p in enumerate(np.asarray(pos_ref).tolist())}
+    return K[:, [idx[p] for p in np.asarray(pos_want).tolist()]]
 
 
 def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=None,
@@ -120,9 +132,11 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                     continue
                 gs = ctx.scores(b, h)
                 gp = ctx.retained(b, h)
-                np.testing.assert_array_equal(gp, o.positions(b, h), err_msg=f"step {t} pre-evict slots")
+                gps, gss = by_position(gp, gs)
+                ops, oss = by_position(o.positions(b, h), o.scores(b, h))
+                np.testing.assert_array_equal(gps, ops, err_msg=f"step {t} pre-evict positions")
                 st.max_score_err = max(st.max_score_err, check_scores(
-                    gs, o.scores(b, h), rtol, f"step {t} scores b={b} kvh={h}"))
+                    gss, oss, rtol, f"step {t} scores b={b} kvh={h}"))
                 pre[(b, h)] = (gs, gp)
         if not fused:
             ctx.evict(B)
@@ -131,16 +145,18 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
         ref_pre_pos = {k: o.positions(*k) for k in keys}
         o.evict(B)
         for (b, h) in keys:
-            got = ctx.retained(b, h)
+            got_slots = ctx.retained(b, h)
+            got = np.sort(got_slots)
+            assert len(np.unique(got)) == len(got), f"step {t} b={b} kvh={h}: a position held twice"
             if not fused:
                 gs, gp = pre[(b, h)]
-                # selection + compaction on the GPU's own scores: bit-exact
+                # selection on the GPU's own scores: bit-exact
                 exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
                 np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b} kvh={h}")
                 st.exact_selection_checks += 1
             else:
                 gp = ref_pre_pos[(b, h)]
-            ref_pos = o.positions(b, h)
+            ref_pos = np.sort(o.positions(b, h))
             if not np.array_equal(got, ref_pos):
                 # near-tie exemption: every differing position within 1e-5 of the boundary
                 ms = ref_pre_scores[(b, h)]
@@ -162,13 +178,15 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                 st.notes.append(f"t={t} b={b} h={h} near-tie resync ({len(diff)} positions)")
                 continue
             if fused:
+                _, gss = by_position(got_slots, ctx.scores(b, h))
+                _, oss = by_position(o.positions(b, h), o.scores(b, h))
                 st.max_score_err = max(st.max_score_err, check_scores(
-                    ctx.scores(b, h), o.scores(b, h), rtol, f"step {t} post-evict scores b={b} kvh={h}"))
+                    gss, oss, rtol, f"step {t} post-evict scores b={b} kvh={h}"))
             if kv_every and t % kv_every == 0:
-                gk, gv = ctx.export_kv(b, h)
+                gk, gv = ctx.export_kv(b, h)  # rows in the order of ctx.retained
                 g = o.groups[(b, h)]
-                rk = torch.from_numpy(g.K[:, :g.n].copy()).to(w.torch_dtype)
-                rv = torch.from_numpy(g.V[:, :g.n].copy()).to(w.torch_dtype)
+                rk = torch.from_numpy(rows_by_position(g.K, g.pos[:g.n], got_slots).copy()).to(w.torch_dtype)
+                rv = torch.from_numpy(rows_by_position(g.V, g.pos[:g.n], got_slots).copy()).to(w.torch_dtype)
                 assert torch.equal(gk.cpu(), rk), f"step {t} compacted K differs b={b} kvh={h}"
                 assert torch.equal(gv.cpu(), rv), f"step {t} compacted V differs b={b} kvh={h}"
                 st.kv_checks += 1
@@ -243,21 +261,25 @@ def run_pooled_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda",
             for b in sample:
                 gp = retained_all(b)
                 gs = ctx.scores(b, 0)
-                np.testing.assert_array_equal(gp, o.positions(b), err_msg=f"step {t} pre-evict slots b={b}")
-                st.max_score_err = max(st.max_score_err, check_scores(gs, o.scores(b), rtol,
+                gps, gss = by_position(gp, gs)
+                ops, oss = by_position(o.positions(b), o.scores(b))
+                np.testing.assert_array_equal(gps, ops, err_msg=f"step {t} pre-evict positions b={b}")
+                st.max_score_err = max(st.max_score_err, check_scores(gss, oss, rtol,
                                                                       f"step {t} scores b={b}"))
                 pre[b] = (gs, gp)
             ctx.evict(B)
         ref_pre = {b: (o.scores(b), o.positions(b)) for b in sample}
         o.evict(B)
         for b in sample:
-            got = retained_all(b)
+            got_slots = retained_all(b)
+            got = np.sort(got_slots)
+            assert len(np.unique(got)) == len(got), f"step {t} b={b}: a position held twice"
             if not fused:
                 gs, gp = pre[b]
                 exp = expected_after_evict(gs, gp, B, w.n_sink, w.n_recent)
                 np.testing.assert_array_equal(got, exp, err_msg=f"step {t} selection on GPU scores b={b}")
                 st.exact_selection_checks += 1
-            ref_pos = o.positions(b)
+            ref_pos = np.sort(o.positions(b))
             if not np.array_equal(got, ref_pos):
                 ms, pos_all = ref_pre[b]
                 keep_ref = np.isin(pos_all, ref_pos)
@@ -271,8 +293,8 @@ def run_pooled_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda",
                                           f"with oracle score gap {max(gaps):.3e} >= 1e-5")
                 # the oracle adopts the GPU's retained set, utilities and cache
                 sst = o.seqs[b]
-                n = len(got)
-                sst.pos[:n] = got
+                n = len(got_slots)
+                sst.pos[:n] = got_slots
                 sst.m[:n] = ctx.scores(b, 0).astype(np.float64)
                 for h in range(Hkv):
                     gk, gv = ctx.export_kv(b, h)
@@ -283,14 +305,18 @@ def run_pooled_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda",
                 st.notes.append(f"t={t} b={b} near-tie resync ({len(diff)} positions)")
                 continue
             if fused:
+                _, gss = by_position(got_slots, ctx.scores(b, 0))
+                _, oss = by_position(o.positions(b), o.scores(b))
                 st.max_score_err = max(st.max_score_err, check_scores(
-                    ctx.scores(b, 0), o.scores(b), rtol, f"step {t} post-evict scores b={b}"))
+                    gss, oss, rtol, f"step {t} post-evict scores b={b}"))
             if kv_every and t % kv_every == 0:
                 sst = o.seqs[b]
                 for h in range(Hkv):
                     gk, gv = ctx.export_kv(b, h)
-                    rk = torch.from_numpy(sst.K[:, h, :sst.n].copy()).to(w.torch_dtype)
-                    rv = torch.from_numpy(sst.V[:, h, :sst.n].copy()).to(w.torch_dtype)
+                    rk = torch.from_numpy(rows_by_position(sst.K[:, h], sst.pos[:sst.n], got_slots).copy()
+                                          ).to(w.torch_dtype)
+                    rv = torch.from_numpy(rows_by_position(sst.V[:, h], sst.pos[:sst.n], got_slots).copy()
+                                          ).to(w.torch_dtype)
                     assert torch.equal(gk.cpu(), rk), f"step {t} compacted K differs b={b} kvh={h}"
                     assert torch.equal(gv.cpu(), rv), f"step {t} compacted V differs b={b} kvh={h}"
                     st.kv_checks += 1
