@@ -51,3 +51,50 @@ def test_pooled_single_kv_head_and_cumulative():
     w = _w(n_layers=2, n_q_heads=8, n_kv_heads=1, prefill_lens=(600,), budget=90,
            policy="cumulative")
     _gu().run_pooled_lockstep(w, 12)
+
+
+def test_pooled_smaller_budget_after_single_token_evictions():
+    """The per-sequence free slot (left by single-token evictions of the
+    fused step) is filled from the last slot of every KV head before a
+    kvev_evict with a smaller budget selects."""
+    import numpy as np
+    import torch
+    import oracle as orc
+    from decode_kv_cache_gqa_amd import kvev
+    gu = _gu()
+    w = _w(n_layers=2, prefill_lens=(400,), budget=90, n_sink=2, n_recent=5)
+    ctx = kvev.context_for(w, max_steps=16)
+    o = orc.PooledTokenOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=90,
+                              alpha_new=w.alpha_new, n_sink=2, n_recent=5, capacity=420)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    Kc, Vc = w.prefill_kv(0, device="cpu")
+    o.prefill(0, Kc.float().numpy(), Vc.float().numpy())
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def compare(what):
+        gp0 = ctx.retained(0, 0)
+        gps, gss = gu.by_position(gp0, ctx.scores(0, 0))
+        ops, oss = gu.by_position(o.positions(0), o.scores(0))
+        np.testing.assert_array_equal(gps, ops, err_msg=f"{what} positions")
+        gu.check_scores(gss, oss, 2e-3, f"{what} scores")
+        st = o.seqs[0]
+        for h in range(w.n_kv_heads):
+            np.testing.assert_array_equal(ctx.retained(0, h), gp0)
+            gk, gv = ctx.export_kv(0, h)
+            rk = torch.from_numpy(gu.rows_by_position(st.K[:, h], st.pos[:st.n], gp0).copy()).to(torch.bfloat16)
+            rv = torch.from_numpy(gu.rows_by_position(st.V[:, h], st.pos[:st.n], gp0).copy()).to(torch.bfloat16)
+            assert torch.equal(gk.cpu(), rk) and torch.equal(gv.cpu(), rv), f"{what} kvh={h} K/V"
+
+    for t in range(1, 7):
+        q, kn, vn = w.step_inputs(t, device="cuda")
+        ctx.step(q, kn, vn, out, 90)
+        qc, knc, vnc = w.step_inputs(t, device="cpu")
+        o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(), [0])
+        o.evict(90)
+    compare("after single-token evictions")
+    ctx.evict(75)
+    o.evict(75)
+    compare("after the smaller budget")
+    ctx.sync()
+    ctx.close()

@@ -249,3 +249,61 @@ def test_scorers_fused_step():
     w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(900,), budget=100,
                                              scorer="vnorm+entropy")
     _gu().run_token_lockstep(w, 12, fused=True)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_smaller_budget_after_single_token_evictions(fused):
+    """A single-token eviction leaves its slot free inside the cache (the
+    next token takes it).  A later kvev_evict with a smaller budget first
+    moves the last token into that slot, then selects; the result must match
+    the oracle by position (retained set, utilities, K/V rows)."""
+    import torch
+    import oracle as orc
+    from decode_kv_cache_gqa_amd import kvev
+    gu = _gu()
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(500,), budget=120,
+                                             n_sink=2, n_recent=6)
+    ctx = kvev.context_for(w, max_steps=16)
+    o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=120,
+                            alpha_new=w.alpha_new, n_sink=2, n_recent=6, capacity=520)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    Kc, Vc = w.prefill_kv(0, device="cpu")
+    o.prefill(0, Kc.float().numpy(), Vc.float().numpy())
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+
+    def step(t, B):
+        q, kn, vn = w.step_inputs(t, device="cuda")
+        if fused:
+            ctx.step(q, kn, vn, out, B)
+        else:
+            ctx.decode_step(q, kn, vn, out)
+            ctx.evict(B)
+        qc, knc, vnc = w.step_inputs(t, device="cpu")
+        o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(), [0])
+        o.evict(B)
+
+    def compare(what):
+        for h in range(w.n_kv_heads):
+            gp = ctx.retained(0, h)
+            gps, gss = gu.by_position(gp, ctx.scores(0, h))
+            ops, oss = gu.by_position(o.positions(0, h), o.scores(0, h))
+            np.testing.assert_array_equal(gps, ops, err_msg=f"{what} kvh={h} positions")
+            gu.check_scores(gss, oss, 2e-3, f"{what} kvh={h} scores")
+            gk, gv = ctx.export_kv(0, h)
+            g = o.groups[(0, h)]
+            rk = torch.from_numpy(gu.rows_by_position(g.K, g.pos[:g.n], gp).copy()).to(torch.bfloat16)
+            rv = torch.from_numpy(gu.rows_by_position(g.V, g.pos[:g.n], gp).copy()).to(torch.bfloat16)
+            assert torch.equal(gk.cpu(), rk) and torch.equal(gv.cpu(), rv), f"{what} kvh={h} K/V"
+
+    for t in range(1, 7):
+        step(t, 120)  # t = 1 compacts 501 -> 120, then single-token evictions
+    compare("after single-token evictions")
+    ctx.evict(100)
+    o.evict(100)
+    compare("after the smaller budget")
+    for t in range(7, 12):
+        step(t, 100)
+    compare("after further steps")
+    ctx.sync()
+    ctx.close()
