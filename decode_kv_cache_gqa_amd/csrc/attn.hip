@@ -107,6 +107,18 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     }
   }
 
+  // the new token's rows, loaded first by the wave whose slots hold it (the
+  // free slot may lie in any split, where this latency would otherwise
+  // extend the block)
+  const bool app = tnew >= wt0 && tnew < wt0 + WT;  // wave-uniform
+  uint4 knew[4];
+  uint32_t vnew[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    knew[s] = app ? *reinterpret_cast<const uint4*>(k_new + new_off + 32 * s + 8 * q4) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) vnew[ct] = app ? v_new[new_off + 16 * ct + r16] : 0u;
+
   uint4 kr[NG][4];
   uint4 vr[2][8];
 #pragma unroll
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
 
   // append: the new token replaces the stale slot contents in registers
   // and is written into its page
-  if (tnew >= wt0 && tnew < wt0 + WT) {
+  if (app) {
     const int jn = (tnew - wt0) >> 4, rn = (tnew - wt0) & 15;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -137,9 +149,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
       uint16_t* kd = kpool + kidx(l, pages[j], rn, 8 * q4, P, D);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint4 v = *reinterpret_cast<const uint4*>(k_new + new_off + 32 * s + 8 * q4);
-        kr[j][s] = v;
-        *reinterpret_cast<uint4*>(kd + 32 * s) = v;
+        kr[j][s] = knew[s];
+        *reinterpret_cast<uint4*>(kd + 32 * s) = knew[s];
       }
     }
 #pragma unroll
@@ -147,7 +158,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
       if (k != (jn >> 1) || (q4 >> 1) != (jn & 1) || (q4 & 1) != (rn >> 3)) continue;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const uint16_t x = v_new[new_off + 16 * ct + r16];
+        const uint16_t x = static_cast<uint16_t>(vnew[ct]);
         put16(vr[k][ct], rn & 7, x);
         vpool[vidx(l, pages[jn], rn, 16 * ct + r16, P, D)] = x;
       }
