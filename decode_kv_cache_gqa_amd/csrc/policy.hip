@@ -4,12 +4,14 @@
 
 namespace kvev {
 // ---------------------------------------------------------------------------
-// Post-attention kernel, grid (blocks per group, groups); block c owns slots
-// [64c, 64c + 64) and, when c < L, the output of layer c.  Every block:
-//  * merges the splits' (max, sum) of all layers of its group (a block that
-//    does not fold: only those of its output layer);
-//  * block c < L writes the attention output of layer c,
-//    out = sum_s e^{m_s - M} o_s / Z;
+// Post-attention kernel, grid (slot blocks + L output blocks, groups).  Slot
+// block c < nblk owns slots [64c, 64c + 64); output block nblk + l writes
+// the attention output of layer l, out = sum_s e^{m_s - M} o_s / Z, from its
+// own merge of that layer's split statistics, and leaves (it takes no part
+// in the arrival, so the group's last block ends with the selection).
+// Every slot block:
+//  * merges the splits' (max, sum) of all layers of its group (on an
+//    observation step);
 //  * on an observation step, folds its slots' probability mass layer by
 //    layer: mass_l[t] = sum_{h in group} exp(s_l[h][t] - M_l[h]) / Z_l[h],
 //    m <- a*mass + (1-a)*m (EMA) or m <- m + mass (cumulative), l = 0..L-1
@@ -50,6 +52,8 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   __shared__ int s_slot[NT / kWave];
   __shared__ int s_last;
   const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
+  const bool outb = c >= A.nblk;  // an output block, for layer ol
+  const int ol = c - A.nblk;
   const int n = A.count[g] + 1;  // slots spanned, the new token's included
   const int hn = A.hole[g];       // the new token's slot
   const int newest = A.nextpos[g];
@@ -65,7 +69,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   // ---- issue every load of the block ---------------------------------------
   const int tl = tid % kPostTok, lg = tid / kPostTok;
   const int t = tbase + tl;
-  const bool fold = A.refresh && tbase < n;
+  const bool fold = !outb && A.refresh && tbase < n;
   float sx[8][HG];
   float vx[8];
   if (fold) {
@@ -80,14 +84,14 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   float prior = 0.f;
   int mypos = 0;
-  if (tid < kPostTok && t < n && t != hn) {
+  if (!outb && tid < kPostTok && t < n && t != hn) {
     prior = gs[t];
     mypos = gp[t];
   }
-  // statistics merged: every layer's for a folding block, else only those
-  // of the block's output layer
-  const int m0 = fold ? 0 : c * HG;
-  const int m1 = fold ? L * HG : (c < L ? m0 + HG : 0);
+  // statistics merged: every layer's for a folding block, its layer's for an
+  // output block, none otherwise
+  const int m0 = outb ? ol * HG : 0;  // (ol is negative for a slot block)
+  const int m1 = fold ? L * HG : (outb ? m0 + HG : 0);
   float2 pm[kMergeBatch];
   const int ml_l = (m0 + tid) / HG, ml_h = (m0 + tid) % HG;
   const float2* pmb = reinterpret_cast<const float2*>(A.part_ml) +
@@ -97,8 +101,8 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     for (int k = 0; k < kMergeBatch; ++k) pm[k] = k < ns ? pmb[k * HG] : make_float2(-INFINITY, 0.f);
   }
   float po[EO][kMergeBatch];
-  const float* pob = A.part_o + (static_cast<int64_t>(c) * A.G + g) * A.S * HG * D;
-  if (c < L) {
+  const float* pob = A.part_o + (static_cast<int64_t>(outb ? ol : 0) * A.G + g) * A.S * HG * D;
+  if (outb) {
 #pragma unroll
     for (int e = 0; e < EO; ++e) {
       const int idx = tid + e * NT;
@@ -160,8 +164,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   // ---- attention output of layer c (after the block's arrival: the
   // selection does not wait on it) ------------------------------------------------
   auto write_output = [&]() __attribute__((always_inline)) {
-    if (c >= L) return;
-    const int l = c;
+    const int l = ol;
     const float2* pml = reinterpret_cast<const float2*>(A.part_ml) + (static_cast<int64_t>(l) * A.G + g) * A.S * HG;
     for (int i = tid; i < HG * ns; i += NT) {
       const int h = i / ns, s = i % ns;
@@ -228,6 +231,11 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     }
   }
 
+  if (outb) {
+    write_output();
+    return;
+  }
+
   // ---- block summary over slots other than the new token's -------------------
   if (tid < kPostTok) {
     const bool mine = t < n && t != hn;
@@ -265,10 +273,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     s_last = (old == static_cast<unsigned>(A.nblk - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!s_last) {
-    write_output();
-    return;
-  }
+  if (!s_last) return;
 
   // ---- the group's last block ------------------------------------------------
   // It loads the block summaries and the new token's utility (observation
@@ -363,7 +368,6 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     A.hole[g] = new_hole;
     A.nmoves[g] = nm;
   }
-  write_output();
 }
 
 // Standalone selection (kvev_evict): one block per group, or, in the
@@ -609,8 +613,8 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
     A.nblk = slot_blocks > outs ? slot_blocks : outs;
     return launch_pool_post<T, D>(c, A);
   }
-  A.nblk = tok_blocks > cf.n_layers ? tok_blocks : cf.n_layers;
-  dim3 grid(A.nblk, c->G);
+  A.nblk = tok_blocks;  // slot blocks; the L output blocks follow them
+  dim3 grid(A.nblk + cf.n_layers, c->G);
   const size_t shm = (static_cast<size_t>(cf.n_layers) * c->HG * 3 + static_cast<size_t>(c->HG) * A.S +
                       static_cast<size_t>(cf.n_layers) * (kPostTok + 1)) * sizeof(float);
   return with_group(c->HG, [&](auto hg) -> hipError_t {
