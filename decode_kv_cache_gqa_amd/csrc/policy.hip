@@ -607,10 +607,8 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.n_recent = cf.n_recent;
   const int tok_blocks = (n_max + kPostTok - 1) / kPostTok;
   if (c->pooled) {
-    // one grid row per sequence; blocks cover the slots and the (layer, KV head) outputs
-    const int outs = cf.n_layers * cf.n_kv_heads;
-    const int slot_blocks = (n_max + kPoolTokens - 1) / kPoolTokens;
-    A.nblk = slot_blocks > outs ? slot_blocks : outs;
+    // one grid row per sequence: the slot blocks, then one block per (layer, KV head) output
+    A.nblk = (n_max + kPoolTokens - 1) / kPoolTokens;
     return launch_pool_post<T, D>(c, A);
   }
   A.nblk = tok_blocks;  // slot blocks; the L output blocks follow them

@@ -14,8 +14,9 @@ namespace kvev {
 // sequence, sequences), kPoolNT threads.  Block c:
 //  * when it folds (observation step, slots [16c, 16c + 16) exist), merges
 //    the split statistics of every (layer, query head) of the sequence;
-//    otherwise only those of its output;
-//  * when c < L * Hkv, writes the output of layer c % L, KV head c / L;
+//  * output block nblk + o (o < L * Hkv) instead merges the statistics of
+//    layer o % L, KV head o / L, writes that output and leaves: the
+//    sequence's last block ends with its selection;
 //  * folds its slots' pooled mass layer by layer:
 //    mass_l[t] = (1/Hq) sum over KV heads of (sum over the group's heads of
 //    p), with the scorer variants' factors (VNorm per KV head; entropy: the
@@ -66,14 +67,17 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   float* gs = A.score + static_cast<int64_t>(g0) * A.cap;
   auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
   const bool ent = SC && A.part_u != nullptr, vn = SC && A.vnorm != nullptr;
-  const bool fold = A.refresh && tbase < n;
+  // blocks c >= nblk write outputs only (and take no part in the arrival)
+  const bool outb = c >= A.nblk;
+  const int oc = c - A.nblk;
+  const bool fold = !outb && A.refresh && tbase < n;
   // mass phase: slot ts of the block, lane j of the slot's kPoolLanes
   const int ts = tid % kPoolTok, j = tid / kPoolTok;
   const int t = tbase + ts;
 
   float prior = 0.f;
   int mypos = 0;
-  if (tid < kPoolTok && t < n && t != hn) {
+  if (!outb && tid < kPoolTok && t < n && t != hn) {
     prior = gs[t];
     mypos = gp[t];
   }
@@ -90,9 +94,8 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     }
   };
   if (fold) load_pairs(0);
-  // this block's output: layer c % L, KV head c / L
-  const bool outb = c < LK;
-  const int ol = c % L, okv = c / L;
+  // an output block's output: layer oc % L, KV head oc / L
+  const int ol = outb ? oc % L : 0, okv = outb ? oc / L : 0;
   float po[EO][kMergeBatch];
   const float* pob = A.part_o + (static_cast<int64_t>(ol) * A.G + g0 + (outb ? okv : 0)) * A.S * HG * D;
   if (outb) {
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
 
   // ---- (M, Z) per (layer, query head): every one for a folding block, else
   // only those of the block's output -----------------------------------------------
-  const int m0 = fold ? 0 : ol * Hq + okv * HG;
+  const int m0 = outb ? ol * Hq + okv * HG : 0;
   const int m1 = fold ? L * Hq : (outb ? m0 + HG : 0);
   for (int i = m0 + tid; i < m1; i += NT) {
     const int l = i / Hq, hq = i % Hq;
@@ -223,6 +226,11 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     }
   }
 
+  if (outb) {
+    write_output();
+    return;
+  }
+
   // ---- block summary over slots other than the new token's (wave 0) ---------------
   if (tid < kWave) {
     const bool mine = tid < kPoolTok && t < n && t != hn;
@@ -260,10 +268,7 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
     s_last = (old == static_cast<unsigned>(A.nblk - 1)) ? 1 : 0;
   }
   __syncthreads();
-  if (!s_last) {
-    write_output();
-    return;
-  }
+  if (!s_last) return;
 
   // ---- the sequence's last block ------------------------------------------------
   const bool one_over = A.do_select && n == A.B + 1;
@@ -356,13 +361,12 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
       A.nmoves[g0 + h] = nm;
     }
   }
-  write_output();
 }
 
 template <typename T, int D>
 hipError_t launch_pool_post(kvev_ctx* c, const PostArgs& A) {
   const auto& cf = c->cfg;
-  dim3 grid(A.nblk, cf.batch);
+  dim3 grid(A.nblk + cf.n_layers * cf.n_kv_heads, cf.batch);  // slot blocks, then output blocks
   const size_t shm = pool_post_shm(cf.n_layers, cf.n_q_heads, cf.n_kv_heads, A.S) * sizeof(float);
   return with_group(c->HG, [&](auto hg) -> hipError_t {
     constexpr int HG = decltype(hg)::value;
