@@ -392,7 +392,19 @@ def main():
     for t in range(args.warmup):
         ctx.step(*inputs[t], out)
     dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total)
-    prof = {k: ctx.profile_read(k) for k in ("attn", "post", "move")}
+    prof = {k: ctx.profile_read(k) for k in ("attn", "post", "move", "diag")}
+    diag = None
+    if w.diag_topk > 0:
+        import numpy as np
+        # rank-trace statistics over the whole run, averaged over the groups
+        gs = ctx.diag_read()
+        mean = lambda key, den: float(np.mean([g[key] / max(g[den], 1) for g in gs]))
+        diag = {"k": w.diag_topk, "steps": gs[0]["steps"],
+                "raw_churn": mean("sum_raw_churn", "pairs"),
+                "util_churn": mean("sum_util_churn", "pairs"),
+                "raw_util_jaccard": mean("sum_raw_util_jaccard", "steps"),
+                "raw_top_evicted": mean("sum_raw_top_evicted", "steps"),
+                "selection_churn": mean("sum_selection_churn", "pairs")}
     ctx.close()
 
     n_tok = w.budget + 1
@@ -402,7 +414,7 @@ def main():
     attn_ms, attn_n = prof["attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
-    policy_ms = sum(prof[k][0] for k in ("post", "move")) / n_prof
+    policy_ms = sum(prof[k][0] for k in ("post", "move", "diag")) / n_prof
     result = {
         "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
         "value": round(steps_s, 2),
@@ -420,7 +432,7 @@ def main():
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "batch": w.batch,
                    "prefill": w.prefill_lens[0], "budget": w.budget, "n_sink": w.n_sink,
                    "n_recent": w.n_recent, "alpha_new": w.alpha_new, "scorer": w.scorer,
-                   "granularity": w.granularity},
+                   "granularity": w.granularity, "diag_topk": w.diag_topk},
         "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
         "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,
@@ -438,6 +450,8 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    if diag is not None:
+        result["diagnostics"] = diag
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result))

@@ -41,7 +41,8 @@ void free_all(kvev_ctx* c) {
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
                   d.grpctr, d.blk_key, d.blk_slot, d.blk_sum, d.btab, d.nres,
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
-                  d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole};
+                  d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole, d.dg_n, d.dg_pos, d.dg_raw,
+                  d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc};
   for (void* p : ptrs)
     if (p) hipFree(p);
   d = DevState{};
@@ -154,6 +155,11 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
       (f.scorer != 0 || f.granularity != KVEV_PER_KV_HEAD))
     return bad("scorer variants and granularity apply to the token policies only");
+  if (f.diag_topk < 0) return bad("diag_topk must be >= 0");
+  if (f.diag_topk > 0 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
+    return bad("diagnostics apply to the token policies only");
+  if (f.diag_topk > 0 && (f.granularity != KVEV_PER_KV_HEAD || f.refresh_interval != 1 || f.score_free != 0))
+    return bad("diagnostics need per-KV-head granularity, refresh_interval 1 and score_free 0");
   if (f.head_dim != 64 && f.head_dim != 128) return bad("head_dim must be 64 or 128");
   if (f.dtype != KVEV_F32 && f.dtype != KVEV_BF16) return bad("dtype must be KVEV_F32 or KVEV_BF16");
   if (f.page_tokens != kPageTokens) return bad("page_tokens must be 16");
@@ -231,6 +237,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->count.assign(c->G, 0);
   c->hole_in.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
+  c->seq_next.assign(f.batch, 0);
   c->block_mode = block;
   if (block) {
     c->maxblk = c->maxpages;
@@ -281,6 +288,21 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.blk_key, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_slot, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_sum, static_cast<size_t>(G) * c->max_post_blocks));
+  const bool diag = f.diag_topk > 0;
+  const size_t npos = static_cast<size_t>(G) * f.max_tokens;  // per-position stamps
+  if (diag) {
+    A(dalloc(&d.dg_n, G));
+    A(dalloc(&d.dg_pos, static_cast<size_t>(G) * c->cap));
+    A(dalloc(&d.dg_raw, static_cast<size_t>(G) * c->cap));
+    A(dalloc(&d.dg_util, static_cast<size_t>(G) * c->cap));
+    A(dalloc(&d.st_raw, npos));
+    A(dalloc(&d.st_util, npos));
+    A(dalloc(&d.st_kept, npos));
+    A(dalloc(&d.ev_step, npos));
+    A(dalloc(&d.dprev, static_cast<size_t>(G) * 4));
+    A(dalloc(&d.dcnt, static_cast<size_t>(G) * kDiagCounts));
+    A(dalloc(&d.dacc, static_cast<size_t>(G) * kDiagAcc));
+  }
   if (block) {
     const size_t Bs = f.batch;
     A(dalloc(&d.btab, Bs * c->maxpages));
@@ -315,6 +337,16 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(hipMemsetAsync(d.grpctr, 0, sizeof(unsigned) * G, c->stream));
   A(hipMemsetAsync(d.mv_src, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.mv_dst, 0, sizeof(int) * G * c->cap, c->stream));
+  if (diag) {
+    A(hipMemsetAsync(d.dg_n, 0, sizeof(int) * G, c->stream));
+    A(hipMemsetAsync(d.st_raw, 0, sizeof(int) * npos, c->stream));
+    A(hipMemsetAsync(d.st_util, 0, sizeof(int) * npos, c->stream));
+    A(hipMemsetAsync(d.st_kept, 0, sizeof(int) * npos, c->stream));
+    A(hipMemsetAsync(d.ev_step, 0, sizeof(int) * npos, c->stream));
+    A(hipMemsetAsync(d.dprev, 0, sizeof(int) * G * 4, c->stream));
+    A(hipMemsetAsync(d.dcnt, 0, sizeof(int) * G * kDiagCounts, c->stream));
+    A(hipMemsetAsync(d.dacc, 0, sizeof(double) * G * kDiagAcc, c->stream));
+  }
   if (block) {
     const size_t Bs = f.batch;
     A(hipMemsetAsync(d.btab, 0, sizeof(int) * Bs * c->maxpages, c->stream));
@@ -482,6 +514,7 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
     c->count[g] = n;
   }
   c->prefilled[seq] = 1;
+  c->seq_next[seq] = n;
   return KVEV_OK;
 }
 
@@ -583,6 +616,11 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
     if (!c->prefilled[b]) return fail(c, KVEV_ESTATE, "a sequence has no prefill");
   const int64_t t = c->t + 1;
   const bool refresh = c->cfg.score_free ? (t == 1) : ((t - 1) % c->cfg.refresh_interval == 0);
+  const bool diag = c->cfg.diag_topk > 0;
+  if (diag)  // the diagnostics stamp positions below max_tokens
+    for (int b = 0; b < c->cfg.batch; ++b)
+      if (c->seq_next[b] >= c->cfg.max_tokens)
+        return fail(c, KVEV_ESTATE, "diagnostics: positions would reach max_tokens");
   auto& upd = c->ptab_upd;
   upd.clear();
   int64_t n_max = 0, max_moves = 0;
@@ -611,6 +649,11 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
     ProfScope p(c, "move");
     KVEV_HIP(c, launch_moves(c, static_cast<int>(max_moves)));
   }
+  if (diag && refresh) {
+    ProfScope p(c, "diag");
+    KVEV_HIP(c, launch_diag(c, static_cast<int>(t)));
+  }
+  for (int b = 0; b < c->cfg.batch; ++b) c->seq_next[b] += 1;
   for (int g = 0; g < c->G; ++g) {
     c->count[g] += 1;
     // a single-token eviction leaves its slot free inside the cache
@@ -636,6 +679,7 @@ kvev_status kvev_decode_step(kvev_ctx* c, const void* q, const void* k_new, cons
   KVEV_LIVE(c);
   if (c->block_mode) return block_step(c, q, k_new, v_new, out, false, 0);
   if (c->tier_mode) return tier_decode(c, q, k_new, v_new, out);
+  if (c->cfg.diag_topk > 0) return fail(c, KVEV_ESTATE, "diagnostics on: use kvev_step");
   return run_step(c, q, k_new, v_new, out, false, c->cfg.budget);
 }
 
@@ -657,6 +701,7 @@ kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   KVEV_LIVE(c);
   if (c->block_mode) return block_evict(c, budget);
   if (c->tier_mode) return tier_route(c);
+  if (c->cfg.diag_topk > 0) return fail(c, KVEV_ESTATE, "diagnostics on: use kvev_step");
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
   int64_t max_moves = 0;
@@ -872,6 +917,7 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return fail(c, KVEV_EINVAL, "block mode: use kvev_import_blocks");
   if (c->pooled) return fail(c, KVEV_EINVAL, "per-sequence granularity: groups cannot be imported one by one");
+  if (c->cfg.diag_topk > 0) return fail(c, KVEV_ESTATE, "diagnostics on: the state changes only by kvev_step");
   if (!positions || !scores || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_ERANGE, "n out of range");
   int maxp = 0;
@@ -891,6 +937,95 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   release_pages(c, g, n + 1);
   c->count[g] = n;
   c->hole_in[g] = 0;
+  return KVEV_OK;
+}
+
+kvev_status kvev_diag_read(kvev_ctx* c, kvev_diag_group* out, int32_t n_groups) {
+  KVEV_LIVE(c);
+  if (c->cfg.diag_topk <= 0 || !c->d.dcnt) return fail(c, KVEV_ESTATE, "diagnostics are off");
+  if (!out || n_groups < 1 || n_groups > c->G) return fail(c, KVEV_ERANGE, "n_groups out of range");
+  std::vector<int> cnt(static_cast<size_t>(n_groups) * kDiagCounts);
+  std::vector<double> acc(static_cast<size_t>(n_groups) * kDiagAcc);
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  KVEV_HIP(c, hipMemcpy(cnt.data(), c->d.dcnt, sizeof(int) * cnt.size(), hipMemcpyDeviceToHost));
+  KVEV_HIP(c, hipMemcpy(acc.data(), c->d.dacc, sizeof(double) * acc.size(), hipMemcpyDeviceToHost));
+  for (int g = 0; g < n_groups; ++g) {
+    const int* k = &cnt[static_cast<size_t>(g) * kDiagCounts];
+    const double* a = &acc[static_cast<size_t>(g) * kDiagAcc];
+    kvev_diag_group& o = out[g];
+    o.n = k[0];
+    o.k = k[1];
+    o.raw_overlap = k[2];
+    o.raw_prev = k[3];
+    o.util_overlap = k[4];
+    o.util_prev = k[5];
+    o.raw_util_overlap = k[6];
+    o.raw_top_evicted = k[7];
+    o.evicted = k[8];
+    o.retained = k[9];
+    o.retained_overlap = k[10];
+    o.retained_prev = k[11];
+    o.steps = static_cast<int64_t>(a[0]);
+    o.pairs = static_cast<int64_t>(a[1]);
+    o.sum_raw_churn = a[2];
+    o.sum_util_churn = a[3];
+    o.sum_raw_util_jaccard = a[4];
+    o.sum_raw_top_evicted = a[5];
+    o.sum_selection_churn = a[6];
+  }
+  return KVEV_OK;
+}
+
+kvev_status kvev_diag_trace(kvev_ctx* c, int32_t seq, int32_t h, int32_t* positions, float* raw,
+                            float* util, int64_t cap, int64_t* n) {
+  KVEV_LIVE(c);
+  if (c->cfg.diag_topk <= 0 || !c->d.dg_n) return fail(c, KVEV_ESTATE, "diagnostics are off");
+  int g;
+  if (kvev_status s = group_index(c, seq, h, &g)) return s;
+  int cnt = 0;
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  KVEV_HIP(c, hipMemcpy(&cnt, c->d.dg_n + g, sizeof(int), hipMemcpyDeviceToHost));
+  if (n) *n = cnt;
+  if (cnt > cap && (positions || raw || util)) return fail(c, KVEV_ERANGE, "cap too small");
+  const int64_t off = static_cast<int64_t>(g) * c->cap;
+  if (positions && cnt > 0)
+    KVEV_HIP(c, hipMemcpy(positions, c->d.dg_pos + off, sizeof(int) * cnt, hipMemcpyDeviceToHost));
+  if (raw && cnt > 0)
+    KVEV_HIP(c, hipMemcpy(raw, c->d.dg_raw + off, sizeof(float) * cnt, hipMemcpyDeviceToHost));
+  if (util && cnt > 0)
+    KVEV_HIP(c, hipMemcpy(util, c->d.dg_util + off, sizeof(float) * cnt, hipMemcpyDeviceToHost));
+  return KVEV_OK;
+}
+
+kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm) {
+  KVEV_LIVE(full);
+  KVEV_LIVE(comp);
+  if (!fmm || full == comp) return fail(comp, KVEV_EINVAL, "null output or the same context twice");
+  if (full->cfg.diag_topk <= 0 || comp->cfg.diag_topk <= 0)
+    return fail(comp, KVEV_ESTATE, "diagnostics are off");
+  const kvev_config &a = full->cfg, &b = comp->cfg;
+  if (a.n_layers != b.n_layers || a.n_q_heads != b.n_q_heads || a.n_kv_heads != b.n_kv_heads ||
+      a.batch != b.batch || a.head_dim != b.head_dim || a.max_tokens != b.max_tokens)
+    return fail(comp, KVEV_EINVAL, "contexts of different shapes");
+  if (a.budget < a.max_tokens || a.scorer != 0)
+    return fail(comp, KVEV_EINVAL, "the full context must never evict and use the attention scorer");
+  if (full->t != comp->t) return fail(comp, KVEV_EINVAL, "contexts at different steps");
+  if (comp->t < 1) return fail(comp, KVEV_ESTATE, "no step yet");
+  for (int s = 0; s < a.batch; ++s)
+    if (full->seq_next[s] != comp->seq_next[s]) return fail(comp, KVEV_EINVAL, "different prefill lengths");
+  double* dev = nullptr;
+  KVEV_HIP(comp, hipMalloc(&dev, sizeof(double) * comp->G));
+  hipEvent_t ev = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(ev, full->stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(comp->stream, ev, 0);
+  if (e == hipSuccess) e = launch_fmm(full, comp, dev);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(fmm, dev, sizeof(double) * comp->G, hipMemcpyDeviceToHost, comp->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(comp->stream);
+  if (ev) hipEventDestroy(ev);
+  hipFree(dev);
+  if (e != hipSuccess) return hip_fail(comp, e, "kvev_diag_fmm");
   return KVEV_OK;
 }
 

@@ -24,6 +24,9 @@ constexpr int kTierD = 128;             // head dim of the tiered mode
 constexpr int kTierLedgerBytes = 3072;  // INT2 record per (layer, KV head, window)
 constexpr int kTierMaxWin = 6144;       // windows per sequence (196608 positions)
 constexpr int kTierXferBlocks = 64;     // blocks per layer of the transition kernel
+// rank-trace diagnostics
+constexpr int kDiagCounts = 12;  // the int32 counts of kvev_diag_group, in order
+constexpr int kDiagAcc = 7;      // steps, pairs and the five sums
 
 // Device buffers of one context.  Groups are (sequence, KV head) pairs,
 // g = seq * Hkv + kv_head; slots of a group are its cached tokens in order.
@@ -52,6 +55,18 @@ struct DevState {
   unsigned long long* blk_key = nullptr;  // [G][max_post_blocks] per-block minimum eviction key
   int* blk_slot = nullptr;                // [G][max_post_blocks] its slot
   float* blk_sum = nullptr;               // [G][max_post_blocks] per-block utility sum
+  // rank-trace diagnostics (cfg.diag_topk > 0)
+  int* dg_n = nullptr;      // [G] tokens the last step attended
+  int* dg_pos = nullptr;    // [G][cap] their positions, in the step's slot order
+  float* dg_raw = nullptr;  // [G][cap] the step's observation summed over layers
+  float* dg_util = nullptr; // [G][cap] the utility after the step's fold
+  int* st_raw = nullptr;    // [G][max_tokens] last step whose raw top-k held the position
+  int* st_util = nullptr;   // [G][max_tokens] ... utility top-k
+  int* st_kept = nullptr;   // [G][max_tokens] last step after which the position was kept
+  int* ev_step = nullptr;   // [G][max_tokens] step that evicted the position (0: never)
+  int* dprev = nullptr;     // [G][4] last recorded step, its k, its retained count
+  int* dcnt = nullptr;      // [G][kDiagCounts] the last step's counts
+  double* dacc = nullptr;   // [G][kDiagAcc] sums over the recorded steps
   // block-granular mode
   int* btab = nullptr;      // [batch][maxpages] logical block of each table entry
   int* nres = nullptr;      // [batch] table entries (resident blocks)
@@ -143,6 +158,7 @@ struct kvev_ctx {
   std::vector<uint8_t> hole_in;             // token modes: the free slot may lie inside (after a
                                             // single-token eviction; an append fills it)
   std::vector<int> prefilled;               // per sequence
+  std::vector<int64_t> seq_next;            // per sequence: the next position (token modes)
   std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
   std::vector<int> free_pages;
   int64_t t = 0;
@@ -205,6 +221,10 @@ hipError_t launch_moves(kvev_ctx* c, int max_moves);
 // the n rows of slots [0, n] other than slot `skip` (n + 1 > skip: the free slot)
 hipError_t launch_export(kvev_ctx* c, int g, void* k_out, void* v_out, int64_t n, int64_t cap, int64_t skip);
 hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64_t n);
+// rank-trace diagnostics (diag.hip): after a step's post kernel, at step t
+hipError_t launch_diag(kvev_ctx* c, int t);
+// missed mass of `comp` against `full`, into device fmm[G]
+hipError_t launch_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm_dev);
 // block-granular mode (block.hip)
 hipError_t launch_block_open(kvev_ctx* c, int n_max, int t);
 hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max);

@@ -221,13 +221,22 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     __syncthreads();
     if (tid < kPostTok && t < n) {
       float m = (t == hn) ? 0.f : prior;
+      float raw = 0.f;
       const float keep = 1.0f - A.a;
       for (int l = 0; l < L; ++l) {
         const float mass = s_mass[l * kPostTok + tl];
+        raw += mass;
         m = A.cumulative ? m + mass : A.a * mass + keep * m;
       }
       st_coherent(gs + t, m);
       myscore = m;
+      if (A.dg_raw) {  // rank-trace diagnostics: the step's inputs per slot
+        const int64_t r = static_cast<int64_t>(g) * A.cap + t;
+        A.dg_pos[r] = t == hn ? newest : mypos;
+        A.dg_raw[r] = raw;
+        A.dg_util[r] = m;
+        if (t == 0) A.dg_n[g] = n;
+      }
     }
   }
 
@@ -585,6 +594,12 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.mv_dst = c->d.mv_dst;
   A.nmoves = c->d.nmoves;
   A.errflag = c->d.errflag;
+  // the diagnostics' inputs (recorded on observation steps)
+  const bool dg = refresh && c->d.dg_raw != nullptr;
+  A.dg_n = dg ? c->d.dg_n : nullptr;
+  A.dg_pos = dg ? c->d.dg_pos : nullptr;
+  A.dg_raw = dg ? c->d.dg_raw : nullptr;
+  A.dg_util = dg ? c->d.dg_util : nullptr;
   A.kpool = c->d.kpool;
   A.vpool = c->d.vpool;
   A.ptab = c->d.ptab;

@@ -258,6 +258,10 @@ struct PostArgs {
   int* mv_dst;
   int* nmoves;
   int* errflag;
+  int* dg_n;       // rank-trace diagnostics, or null: per slot of the step
+  int* dg_pos;     // its position,
+  float* dg_raw;   // the observation summed over layers,
+  float* dg_util;  // the utility after the fold
   void* kpool;
   void* vpool;
   const int* ptab;

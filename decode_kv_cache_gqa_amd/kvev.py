@@ -50,7 +50,22 @@ class Config(ctypes.Structure):
         ("int2_windows", ctypes.c_int32),
         ("scorer", ctypes.c_int32), ("granularity", ctypes.c_int32),
         ("route_interval", ctypes.c_int32),
+        ("diag_topk", ctypes.c_int32),
     ]
+
+
+class DiagGroup(ctypes.Structure):
+    """kvev_diag_group: one (sequence, KV head) group's rank-trace statistics."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "k", "raw_overlap", "raw_prev", "util_overlap", "util_prev", "raw_util_overlap",
+        "raw_top_evicted", "evicted", "retained", "retained_overlap", "retained_prev")] + [
+        ("steps", ctypes.c_int64), ("pairs", ctypes.c_int64),
+        ("sum_raw_churn", ctypes.c_double), ("sum_util_churn", ctypes.c_double),
+        ("sum_raw_util_jaccard", ctypes.c_double), ("sum_raw_top_evicted", ctypes.c_double),
+        ("sum_selection_churn", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 _lib = None
@@ -89,6 +104,11 @@ _SIGS = {
     "kvev_tier_import": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
     "kvev_tier_capacities": (ctypes.c_int, [ctypes.c_double] * 4 + [ctypes.POINTER(ctypes.c_int32)] * 2),
+    "kvev_diag_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(DiagGroup), ctypes.c_int32]),
+    "kvev_diag_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.POINTER(ctypes.c_int64)]),
+    "kvev_diag_fmm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
     "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
@@ -339,6 +359,26 @@ class Context:
         self._check(lib().kvev_tier_import(self._h, layer, score.shape[0], score.ctypes.data_as(ctypes.c_void_p),
                                            tier.ctypes.data_as(ctypes.c_void_p)))
 
+    def diag_read(self):
+        """Rank-trace statistics of every group (g = seq * n_kv_heads + kv_head)."""
+        G = self.cfg.batch * self.cfg.n_kv_heads
+        arr = (DiagGroup * G)()
+        self._check(lib().kvev_diag_read(self._h, arr, G))
+        return [a.as_dict() for a in arr]
+
+    def diag_trace(self, seq, kv_head):
+        """The last step's (positions, raw, util) of group (seq, kv_head), slot order."""
+        n = ctypes.c_int64()
+        cap = self.cfg.max_tokens
+        pos = np.zeros(cap, np.int32)
+        raw = np.zeros(cap, np.float32)
+        util = np.zeros(cap, np.float32)
+        self._check(lib().kvev_diag_trace(
+            self._h, seq, kv_head, pos.ctypes.data_as(ctypes.c_void_p), raw.ctypes.data_as(ctypes.c_void_p),
+            util.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)))
+        m = n.value
+        return pos[:m].copy(), raw[:m].copy(), util[:m].copy()
+
     def sync(self):
         self._check(lib().kvev_sync(self._h))
 
@@ -355,6 +395,15 @@ class Context:
         return ms.value, n.value
 
 
+def diag_fmm(full, compressed):
+    """Future missed mass of `compressed` against the never-evicting `full`
+    context, per group (the library's kvev_diag_fmm)."""
+    G = compressed.cfg.batch * compressed.cfg.n_kv_heads
+    out = (ctypes.c_double * G)()
+    compressed._check(lib().kvev_diag_fmm(full._h, compressed._h, out))
+    return np.array(list(out), dtype=np.float64)
+
+
 def tier_capacities(b_hist, q, m_f, m_q):
     """(K_f, K_q) of the two-tier mode from a byte budget (the library's
     kvev_tier_capacities; host arithmetic)."""
@@ -366,8 +415,9 @@ def tier_capacities(b_hist, q, m_f, m_q):
     return kf.value, kq.value
 
 
-def context_for(w, max_steps=None, budget=None, stream=None):
-    """A context configured for a synth.Workload."""
+def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None):
+    """A context configured for a synth.Workload (diag_topk: rank-trace
+    diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
     if w.policy == "lrfu_block":
         cfg = make_config(
@@ -396,5 +446,6 @@ def context_for(w, max_steps=None, budget=None, stream=None):
         policy=CUMULATIVE if w.policy == "cumulative" else EMA, alpha_new=w.alpha_new,
         refresh_interval=w.refresh_interval, score_free=1 if w.score_free else 0,
         n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget,
-        scorer=_SCORER_BITS[w.scorer], granularity=_GRANULARITY[w.granularity])
+        scorer=_SCORER_BITS[w.scorer], granularity=_GRANULARITY[w.granularity],
+        diag_topk=w.diag_topk if diag_topk is None else diag_topk)
     return Context(cfg, stream=stream)

@@ -136,6 +136,7 @@ class Workload:
     scorer: str = "attention"       # attention | vnorm | entropy | vnorm+entropy
     granularity: str = "kv_head"    # kv_head | sequence
     route_interval: int = 1         # tiered mode: routing events every route_interval steps
+    diag_topk: int = 0              # token modes: rank-trace diagnostics over the top-k (0: off)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -397,6 +398,9 @@ def workload(name: str) -> Workload:
         return Workload("qevict_131k_fp5_int2_20", 32, 32, 8, 128, "bf16", (131072,), 128,
                         seed=1005, policy="tiered_int2", n_sink=5, n_recent=32, n_epochs=4,
                         epoch_steps=32, window_tokens=32, fp_windows=205, int2_windows=819)
+    if name == "llama8b_32k_diag":
+        # rank-trace diagnostics at k = the budget ("What Matters ...", appendix I)
+        return replace(workload("llama8b_32k"), name="llama8b_32k_10pct_diag", diag_topk=3277)
     if name == "qevict131k_omega8":
         # the review's routing interval: one routing event every 8 steps (section 4.2 Eq.1)
         return replace(workload("qevict131k"), name="qevict_131k_fp5_int2_20_omega8", route_interval=8)
@@ -404,4 +408,5 @@ def workload(name: str) -> Workload:
 
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
-             "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8")
+             "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8",
+             "llama8b_32k_diag")

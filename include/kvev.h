@@ -164,6 +164,14 @@ typedef struct {
    * ("QEvict" review, section 4.2 Eq.1; the review's default is 8).  0 or 1:
    * every step.  kvev_evict is always one routing event. */
   int32_t route_interval;
+  /* Rank-trace diagnostics (KVEV_EMA and KVEV_CUMULATIVE, PER_KV_HEAD,
+   * refresh_interval 1, score_free 0; 0 in the other modes).  0: off.
+   * k >= 1: every kvev_step also records, per (sequence, KV head) group,
+   * the statistics of kvev_diag_group over the top-k sets (k = min(k, the
+   * step's token count)); kvev_step is then the only call that changes the
+   * state (kvev_decode_step, kvev_evict and kvev_import_group return
+   * KVEV_ESTATE).  Appendix I of "What Matters ..." takes k = the budget. */
+  int32_t diag_topk;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -262,6 +270,70 @@ kvev_status kvev_export_kv(kvev_ctx* ctx, int32_t seq, int32_t kv_head, void* k_
 kvev_status kvev_import_group(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int64_t n,
                               const int32_t* positions, const float* scores,
                               const void* k, const void* v);
+
+/* ---- Rank-trace diagnostics (cfg.diag_topk > 0) ------------------------
+ * After each kvev_step, for every (sequence, KV head) group, over the n
+ * tokens the step attended (the new one included, before the eviction):
+ *   raw_t(i)  = the step's observation of token i summed over the layers
+ *               (the per-layer group mass, times the scorer factors);
+ *   util_t(i) = its utility after the step's fold;
+ *   R_t, E_t  = the k tokens with the largest (raw_t, position) and
+ *               (util_t, position) keys, k = min(cfg.diag_topk, n);
+ *   Ev_t      = the tokens the step evicted; S_t = the tokens kept.
+ * Churn of a set is one minus the Jaccard index |X_t & X_t'| / |X_t | X_t'|
+ * against the previous step t' ("What Matters ...", appendix I, Table 13:
+ * raw and EMA top-k churn, raw / EMA Jaccard overlap, the share of the raw
+ * top-k evicted; the "QEvict" review, section 3: selection churn of the
+ * retained set between consecutive selections). */
+typedef struct {
+  /* the last step's counts */
+  int32_t n;                /* tokens the step attended */
+  int32_t k;                /* |R_t| = |E_t| */
+  int32_t raw_overlap;      /* |R_t & R_t-1| */
+  int32_t raw_prev;         /* |R_t-1| (0 at the first recorded step) */
+  int32_t util_overlap;     /* |E_t & E_t-1| */
+  int32_t util_prev;        /* |E_t-1| */
+  int32_t raw_util_overlap; /* |R_t & E_t| */
+  int32_t raw_top_evicted;  /* |R_t & Ev_t| */
+  int32_t evicted;          /* |Ev_t| */
+  int32_t retained;         /* |S_t| */
+  int32_t retained_overlap; /* |S_t & S_t-1| */
+  int32_t retained_prev;    /* |S_t-1| */
+  /* sums over the recorded steps (churns over the steps with a previous one) */
+  int64_t steps;
+  int64_t pairs;
+  double sum_raw_churn;     /* 1 - J(R_t, R_t-1) */
+  double sum_util_churn;    /* 1 - J(E_t, E_t-1) */
+  double sum_raw_util_jaccard;  /* J(R_t, E_t) */
+  double sum_raw_top_evicted;   /* |R_t & Ev_t| / k */
+  double sum_selection_churn;   /* 1 - J(S_t, S_t-1) */
+} kvev_diag_group;
+
+/* Copy the diagnostics of groups 0..n_groups-1 (g = seq * n_kv_heads +
+ * kv_head) to host `out`.  Synchronises.  Errors: KVEV_ESTATE (diagnostics
+ * off), KVEV_ERANGE (n_groups outside 1..batch * n_kv_heads). */
+kvev_status kvev_diag_read(kvev_ctx* ctx, kvev_diag_group* out, int32_t n_groups);
+
+/* Copy the last step's per-token inputs of the diagnostics of group
+ * (seq, kv_head), in the step's slot order, to host buffers (any may be
+ * NULL): positions, raw_t, util_t; *n = the step's token count (0 before
+ * the first step).  Synchronises.  Errors: KVEV_ESTATE (diagnostics off),
+ * KVEV_ERANGE (cap too small / bad indices). */
+kvev_status kvev_diag_trace(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int32_t* positions,
+                            float* raw, float* util, int64_t cap, int64_t* n);
+
+/* Future missed mass ("QEvict" review, section 3): for every group, the
+ * share of the full cache's attention at the last step that lands on
+ * positions the compressed cache evicted at an earlier step,
+ *   fmm[g] = sum_{i evicted before step t} raw_full(i) / sum_i raw_full(i),
+ * raw_full = the full context's per-token group mass summed over layers.
+ * `full` must never evict (budget >= max_tokens), use the attention scorer
+ * and have been stepped with the same prefill and inputs as `compressed`
+ * (same shape, same step count, both with diagnostics on).  Waits for
+ * `full`'s stream on `compressed`'s stream, then synchronises; fmm: host
+ * [batch * n_kv_heads].  Errors: KVEV_EINVAL (mismatched contexts),
+ * KVEV_ESTATE (diagnostics off, no step yet). */
+kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* compressed, double* fmm);
 
 /* ---- KVEV_LRFU_BLOCK mode ---------------------------------------------- */
 

@@ -40,7 +40,8 @@ __all__ = [
     "TokenModeOracle", "region_decay_rates", "block_survival", "block_priority",
     "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
     "vnorm_weights", "normalized_entropy", "scored_mass", "SCORERS",
-    "PooledTokenOracle",
+    "PooledTokenOracle", "jaccard", "top_k_positions", "RankTraceDiagnostics",
+    "future_missed_mass",
 ]
 
 
@@ -395,6 +396,123 @@ def int2_dequantize(codes, scales, zeros, axis_groups):
 # Token-granular eviction step (InertiaKV, InertiaKV-Lazy, Score-Free)
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Rank-trace diagnostics
+# ---------------------------------------------------------------------------
+
+def jaccard(a, b):
+    """Jaccard index |a & b| / |a | b| of two sets of positions.
+
+    [InertiaKV] App. I (raw / EMA Jaccard overlap, churn as its complement)
+    and [QEvict] §3 (selection churn, the Jaccard distance).  Reading: two
+    empty sets have index 1.
+    """
+    a, b = set(a), set(b)
+    u = len(a | b)
+    return 1.0 if u == 0 else len(a & b) / u
+
+
+def top_k_positions(values, positions, k):
+    """The positions of the k largest (value, position) keys.
+
+    [InertiaKV] App. I traces top-k token sets by score.  Reading: the order
+    is the selection's (``select_keep``): on equal values the larger
+    (more recent) position ranks higher; k larger than the token count takes
+    every token.
+    """
+    values = np.asarray(values, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    k = min(int(k), values.shape[0])
+    if k <= 0:
+        return set()
+    order = np.lexsort((positions, values))  # ascending by (value, position)
+    return set(positions[order[values.shape[0] - k:]].tolist())
+
+
+class RankTraceDiagnostics:
+    """Per-step rank-trace statistics of one selection group.
+
+    [InertiaKV] App. I, Table 13: raw top-k churn, EMA (utility) top-k churn,
+    the raw / EMA Jaccard overlap and the share of the raw top-k that is
+    evicted; [QEvict] §3: selection churn, the Jaccard distance between the
+    retained sets of consecutive selections.  Churn is one minus the Jaccard
+    index against the previous observed step.
+
+    Feed ``observe`` once per step, after the fold and before the eviction
+    takes effect, with the step's tokens (positions), their raw observation
+    and their utility, and the positions kept after the eviction.
+
+    Readings: the raw score of a step is its observation summed over the
+    layers (one raw value per token; the sum ranks like the mean); k is the
+    caller's (App. I measures at k = the budget); the evicted set of a step
+    is the step's tokens that are not kept.
+    """
+
+    COUNTS = ("n", "k", "raw_overlap", "raw_prev", "util_overlap", "util_prev",
+              "raw_util_overlap", "raw_top_evicted", "evicted", "retained",
+              "retained_overlap", "retained_prev")
+
+    def __init__(self, k):
+        self.k = int(k)
+        self.prev = None  # (R, E, S) of the previous step
+        self.step = 0
+        self.evicted_at = {}  # position -> step that evicted it
+        self.sums = {"steps": 0, "pairs": 0, "sum_raw_churn": 0.0, "sum_util_churn": 0.0,
+                     "sum_raw_util_jaccard": 0.0, "sum_raw_top_evicted": 0.0,
+                     "sum_selection_churn": 0.0}
+
+    def observe(self, positions, raw, util, kept_positions):
+        positions = np.asarray(positions, dtype=np.int64)
+        self.step += 1
+        R = top_k_positions(raw, positions, self.k)
+        E = top_k_positions(util, positions, self.k)
+        S = set(np.asarray(kept_positions, dtype=np.int64).tolist())
+        Ev = set(positions.tolist()) - S
+        for p in Ev:
+            self.evicted_at[p] = self.step
+        k = len(R)
+        c = {"n": int(positions.shape[0]), "k": k, "raw_util_overlap": len(R & E),
+             "raw_top_evicted": len(R & Ev), "evicted": len(Ev), "retained": len(S)}
+        sm = self.sums
+        sm["steps"] += 1
+        sm["sum_raw_util_jaccard"] += jaccard(R, E)
+        sm["sum_raw_top_evicted"] += len(R & Ev) / k
+        if self.prev is None:
+            c.update(raw_overlap=0, raw_prev=0, util_overlap=0, util_prev=0, retained_overlap=0,
+                     retained_prev=0)
+        else:
+            Rp, Ep, Sp = self.prev
+            c.update(raw_overlap=len(R & Rp), raw_prev=len(Rp), util_overlap=len(E & Ep),
+                     util_prev=len(Ep), retained_overlap=len(S & Sp), retained_prev=len(Sp))
+            sm["pairs"] += 1
+            sm["sum_raw_churn"] += 1.0 - jaccard(R, Rp)
+            sm["sum_util_churn"] += 1.0 - jaccard(E, Ep)
+            sm["sum_selection_churn"] += 1.0 - jaccard(S, Sp)
+        self.prev = (R, E, S)
+        return c
+
+    def evicted_before(self, step):
+        """Positions evicted at a step earlier than ``step`` (1-based)."""
+        return {p for p, e in self.evicted_at.items() if e < step}
+
+
+def future_missed_mass(full_positions, full_raw, evicted):
+    """Share of a full cache's attention mass on evicted positions.
+
+    [QEvict] §3 (Future Missed Mass): the uncompressed model's attention
+    distribution over its whole cache at a step, and the fraction of it that
+    lands on tokens the compressed policy has already discarded.  Reading:
+    the distribution of a (sequence, KV head) group is its observation
+    summed over the layers and the group's query heads (a uniform scale of
+    L * group size, which the ratio removes); ``evicted`` holds the
+    positions discarded at earlier steps.
+    """
+    w = np.asarray(full_raw, dtype=np.float64)
+    mask = np.isin(np.asarray(full_positions, dtype=np.int64), np.fromiter(evicted, dtype=np.int64))
+    tot = w.sum()
+    return float(w[mask].sum() / tot) if tot > 0 else 0.0
+
+
 @dataclass
 class _Group:
     """State of one (sequence, KV head) selection group, in slot order."""
@@ -547,6 +665,16 @@ class TokenModeOracle:
             g.n = B
 
     # -- views used by tests ------------------------------------------------
+    def step_observation(self, seq, h):
+        """After an observation step's ``decode_step`` and before ``evict``:
+        the group's (positions, raw, utility) in slot order, raw being the
+        step's observation summed over the layers (``RankTraceDiagnostics``)."""
+        g = self.groups[(seq, h)]
+        raw = np.zeros(g.n, dtype=np.float64)
+        for l in range(self.n_layers):
+            raw += self.last_G[(l, seq, h)]
+        return g.pos[:g.n].copy(), raw, g.m[:g.n].copy()
+
     def scores(self, seq, h):
         g = self.groups[(seq, h)]
         return g.m[:g.n].copy()

@@ -199,6 +199,135 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
 
 
 # ---------------------------------------------------------------------------
+# Rank-trace diagnostics
+# ---------------------------------------------------------------------------
+
+def run_diag_lockstep(w, steps, k, *, sample_seqs=None, sample_heads=None, rtol=None,
+                      check_values=True, fmm=False, device="cuda"):
+    """Step workload `w` with diagnostics over the top-k and check, every step
+    and for every sampled group:
+    * the library's counts equal the oracle's rank-trace statistics computed
+      from the library's own per-token inputs and retained set (the integer
+      decisions taken on the same fp32 values: exact), and its sums agree;
+    * (check_values) those inputs, position by position, equal the oracle's
+      raw observation and utility within rtol (on a near tie the oracle is
+      resynchronised to the library's retained set);
+    * (fmm) the missed mass against a never-evicting context equals the
+      oracle's formula on the library's full-cache inputs and evicted sets.
+    Returns the list of per-step diag_read() results of group 0."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    rtol = rtol if rtol is not None else (1e-5 if w.dtype == "f32" else 2e-3)
+    B = w.budget
+    Hkv = w.n_kv_heads
+    sample_seqs = list(range(w.batch)) if sample_seqs is None else list(sample_seqs)
+    sample_heads = list(range(Hkv)) if sample_heads is None else list(sample_heads)
+    keys = [(b, h) for b in sample_seqs for h in sample_heads]
+    log(f"[diag] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:4]} steps={steps} B={B} "
+        f"k={k} groups={keys} values={check_values} fmm={fmm}")
+    t_start = time.time()
+    ctx = kvev.context_for(w, max_steps=steps, diag_topk=k)
+    full = None
+    if fmm:
+        mt = max(w.prefill_lens) + steps + 1
+        full = kvev.context_for(w, max_steps=steps, budget=mt, diag_topk=1)
+    o = None
+    if check_values:
+        o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, Hkv, w.head_dim, budget=B,
+                                alpha_new=w.alpha_new,
+                                policy=w.policy if w.policy == "cumulative" else "ema",
+                                n_sink=w.n_sink, n_recent=w.n_recent,
+                                capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=device)
+        ctx.prefill(b, K.contiguous(), V.contiguous())
+        if full is not None:
+            full.prefill(b, K.contiguous(), V.contiguous())
+        del K, V
+        if o is not None and b in sample_seqs:
+            Kc, Vc = w.prefill_kv(b, device="cpu", heads=sample_heads)
+            o.prefill(b, Kc.float().numpy(), Vc.float().numpy(), heads=sample_heads)
+    torch.cuda.synchronize()
+    trackers = {key: orc.RankTraceDiagnostics(k) for key in keys}
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
+    out_full = torch.empty_like(out)
+    history, resyncs, max_err = [], 0, 0.0
+    for t in range(1, steps + 1):
+        q, kn, vn = w.step_inputs(t, device=device)
+        ctx.step(q, kn, vn, out, B)
+        if full is not None:
+            full.step(q, kn, vn, out_full, 0)
+        if o is not None:
+            qc, knc, vnc = w.step_inputs(t, device="cpu", seqs=sample_seqs)
+            o.decode_step(t, qc.float().numpy(), knc.float().numpy(), vnc.float().numpy(), sample_seqs)
+        gd = ctx.diag_read()
+        history.append(gd[0])
+        pre = {}
+        for (b, h) in keys:
+            g = b * Hkv + h
+            gpos, graw, gutil = ctx.diag_trace(b, h)
+            kept = ctx.retained(b, h)
+            exp = trackers[(b, h)].observe(gpos, graw.astype(np.float64), gutil.astype(np.float64), kept)
+            got = {name: gd[g][name] for name in orc.RankTraceDiagnostics.COUNTS}
+            assert got == exp, f"step {t} b={b} kvh={h}: counts {got} != oracle on the library's values {exp}"
+            for name, val in trackers[(b, h)].sums.items():
+                assert abs(gd[g][name] - val) <= 1e-12 * max(1.0, abs(val)), (
+                    f"step {t} b={b} kvh={h}: {name} {gd[g][name]!r} != {val!r}")
+            if o is not None:
+                opos, oraw, outil = o.step_observation(b, h)
+                gps, graw_s, gutil_s = by_position(gpos, graw, gutil)
+                ops, oraw_s, outil_s = by_position(opos, oraw, outil)
+                np.testing.assert_array_equal(gps, ops, err_msg=f"step {t} b={b} kvh={h}: step tokens")
+                max_err = max(max_err, check_scores(graw_s, oraw_s, rtol, f"step {t} raw b={b} kvh={h}"),
+                              check_scores(gutil_s, outil_s, rtol, f"step {t} util b={b} kvh={h}"))
+                grp = o.groups[(b, h)]
+                pre[(b, h)] = (grp.K[:, :grp.n].copy(), grp.V[:, :grp.n].copy(), grp.pos[:grp.n].copy(),
+                               kept, gps, gutil_s, ops, outil_s)
+        if o is not None:
+            o.evict(B)
+            for (b, h) in keys:
+                K0, V0, pos0, kept, gps, gutil_s, ops, outil_s = pre[(b, h)]
+                got = np.sort(kept)
+                ref = np.sort(o.positions(b, h))
+                if np.array_equal(got, ref):
+                    continue
+                # near tie: every differing position within 1e-5 of the kept minimum (oracle values)
+                prot = (ops < w.n_sink) | (ops > ops.max() - w.n_recent)
+                kept_ref = np.isin(ops, ref) & ~prot
+                theta = outil_s[kept_ref].min() if kept_ref.any() else 0.0
+                idx = {p: i for i, p in enumerate(ops.tolist())}
+                gaps = [abs(outil_s[idx[p]] - theta) for p in set(got.tolist()) ^ set(ref.tolist())]
+                assert max(gaps) < 1e-5, f"step {t} b={b} kvh={h}: retained sets differ (gap {max(gaps):.2e})"
+                # resynchronise the oracle to the library's retained set
+                sel = np.array([np.flatnonzero(pos0 == p)[0] for p in got.tolist()])
+                grp = o.groups[(b, h)]
+                n = len(sel)
+                grp.K[:, :n] = K0[:, sel]
+                grp.V[:, :n] = V0[:, sel]
+                grp.pos[:n] = pos0[sel]
+                grp.m[:n] = gutil_s[np.searchsorted(gps, pos0[sel])]
+                grp.n = n
+                resyncs += 1
+        if full is not None:
+            fm = kvev.diag_fmm(full, ctx)
+            for (b, h) in keys:
+                g = b * Hkv + h
+                fpos, fraw, _ = full.diag_trace(b, h)
+                assert len(fpos) == w.prefill_lens[b] + t, "the full context evicted"
+                want = orc.future_missed_mass(fpos, fraw.astype(np.float64),
+                                              trackers[(b, h)].evicted_before(t))
+                assert abs(fm[g] - want) <= 1e-9 * max(want, 1e-12) + 1e-15, (
+                    f"step {t} b={b} kvh={h}: fmm {fm[g]!r} != {want!r}")
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[diag] step {t}: value err {max_err:.2e} resyncs {resyncs} ({time.time() - t_start:.1f}s)")
+    ctx.close()
+    if full is not None:
+        full.close()
+    return history
+
+
+# ---------------------------------------------------------------------------
 # Sequence-pooled token mode
 # ---------------------------------------------------------------------------
 

@@ -103,12 +103,42 @@ def _create(**kw):
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, fp_windows=-1), "capacities"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, max_tokens=200000), "196608"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
+    (dict(diag_topk=-1), "diag_topk"),
+    (dict(diag_topk=4, policy=kvev.LRFU_BLOCK, n_q_heads=8), "token policies"),
+    (dict(diag_topk=4, policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, batch=1), "token policies"),
+    (dict(diag_topk=4, granularity=kvev.PER_SEQUENCE), "diagnostics need"),
+    (dict(diag_topk=4, refresh_interval=8), "diagnostics need"),
+    (dict(diag_topk=4, score_free=1), "diagnostics need"),
 ])
 def test_create_rejects_bad_config(bad, msg):
     st, err, h = _create(**bad)
     assert st == kvev.EINVAL
     assert msg in err
     assert not h.value
+
+
+def test_diag_group_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "diag_layout.c"
+    fields = [f for f, _ in kvev.DiagGroup._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(kvev_diag_group, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "kvev.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(kvev_diag_group));\n'
+                   f'  return 0;\n}}\n')
+    exe = tmp_path / "diag_layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(kvev.DiagGroup, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(kvev.DiagGroup)
+
+
+def test_diag_entry_points_reject_null_context():
+    L = kvev.lib()
+    assert L.kvev_diag_read(None, None, 1) == kvev.EINVAL
+    assert L.kvev_diag_trace(None, 0, 0, None, None, None, 0, None) == kvev.EINVAL
+    assert L.kvev_diag_fmm(None, None, None) == kvev.EINVAL
 
 
 def test_null_arguments():
