@@ -26,21 +26,35 @@ __device__ __forceinline__ unsigned long long diag_key(float v, int p) {
   return (static_cast<unsigned long long>(float_key(v)) << 32) | static_cast<uint32_t>(p);
 }
 
-__device__ __forceinline__ int block_sum_int(int v, int* red) {
+// Block sums of N counters, returned to thread 0.
+template <int N>
+__device__ __forceinline__ void block_sum_ints(int (&v)[N], int (*red)[N]) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  v = wave_sum_int(v);
+#pragma unroll
+  for (int j = 0; j < N; ++j) v[j] = wave_sum_int(v[j]);
+  if (lane == 0)
+#pragma unroll
+    for (int j = 0; j < N; ++j) red[wave][j] = v[j];
   __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  int t = 0;
-  for (int w = 0; w < static_cast<int>(blockDim.x) / kWave; ++w) t += red[w];
-  return t;
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      int t = 0;
+      for (int w = 0; w < static_cast<int>(blockDim.x) / kWave; ++w) t += red[w][j];
+      v[j] = t;
+    }
 }
 
+// Keys per thread held in registers; steps of more tokens read them again
+// from memory on every pass.
+constexpr int kDiagKPT = 8;
+
 // The k-th largest key of the raw (set 0) and utility (set 1) values over
-// slots [0, n), 1 <= k <= n.
+// slots [0, n), 1 <= k <= n.  cached: slot tid + u * kDiagNT's keys are
+// kr[u], ku[u] (n <= kDiagNT * kDiagKPT).
 __device__ void kth_largest_pair(int n, int k, const int* pos, const float* raw, const float* util,
-                                 unsigned long long* thr) {
+                                 bool cached, const unsigned long long* kr_c,
+                                 const unsigned long long* ku_c, unsigned long long* thr) {
   __shared__ int hist[2][256];
   __shared__ int excl[256];
   __shared__ int wsum[4];
@@ -53,12 +67,20 @@ __device__ void kth_largest_pair(int n, int k, const int* pos, const float* raw,
   for (int shift = 56; shift >= 0 && !(done[0] && done[1]); shift -= 8) {
     for (int i = tid; i < 512; i += kDiagNT) hist[i / 256][i % 256] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kDiagNT) {
-      const int p = pos[i];
-      const unsigned long long kr = diag_key(raw[i], p), ku = diag_key(util[i], p);
-      // bins in descending digit order, so the scan counts larger keys first
+    // bins in descending digit order, so the scan counts larger keys first
+    auto count = [&](unsigned long long kr, unsigned long long ku) {
       if (!done[0] && (kr & mask[0]) == pre[0]) atomicAdd(&hist[0][255 - ((kr >> shift) & 255u)], 1);
       if (!done[1] && (ku & mask[1]) == pre[1]) atomicAdd(&hist[1][255 - ((ku >> shift) & 255u)], 1);
+    };
+    if (cached) {
+#pragma unroll
+      for (int u = 0; u < kDiagKPT; ++u)
+        if (tid + u * kDiagNT < n) count(kr_c[u], ku_c[u]);
+    } else {
+      for (int i = tid; i < n; i += kDiagNT) {
+        const int p = pos[i];
+        count(diag_key(raw[i], p), diag_key(util[i], p));
+      }
     }
     __syncthreads();
     for (int s = 0; s < 2; ++s) {
@@ -82,11 +104,19 @@ __device__ void kth_largest_pair(int n, int k, const int* pos, const float* raw,
   }
   // a bucket of one key: that key is the threshold
   if (unique[0] || unique[1]) {
-    for (int i = tid; i < n; i += kDiagNT) {
-      const int p = pos[i];
-      const unsigned long long kr = diag_key(raw[i], p), ku = diag_key(util[i], p);
+    auto match = [&](unsigned long long kr, unsigned long long ku) {
       if (unique[0] && (kr & mask[0]) == pre[0]) found[0] = kr;
       if (unique[1] && (ku & mask[1]) == pre[1]) found[1] = ku;
+    };
+    if (cached) {
+#pragma unroll
+      for (int u = 0; u < kDiagKPT; ++u)
+        if (tid + u * kDiagNT < n) match(kr_c[u], ku_c[u]);
+    } else {
+      for (int i = tid; i < n; i += kDiagNT) {
+        const int p = pos[i];
+        match(diag_key(raw[i], p), diag_key(util[i], p));
+      }
     }
     __syncthreads();
     if (unique[0]) pre[0] = found[0];
@@ -118,7 +148,7 @@ struct DiagArgs {
 };
 
 __global__ __launch_bounds__(kDiagNT) void diag_kernel(DiagArgs A) {
-  __shared__ int red[kDiagNT / kWave];
+  __shared__ int red[kDiagNT / kWave][8];
   const int g = blockIdx.x, tid = threadIdx.x;
   const int64_t go = static_cast<int64_t>(g) * A.cap, so = static_cast<int64_t>(g) * A.maxpos;
   const int n = A.dg_n[g];
@@ -133,61 +163,122 @@ __global__ __launch_bounds__(kDiagNT) void diag_kernel(DiagArgs A) {
   const int tp = A.prev[g * 4 + 0];  // the previous recorded step (0: none)
   const int kprev = A.prev[g * 4 + 1], sprev = A.prev[g * 4 + 2];
   const int k = n < A.K ? n : A.K;
+  // the step's keys, held in registers when they fit (loads issued first)
+  const bool cached = n <= kDiagNT * kDiagKPT;
+  unsigned long long kr_c[kDiagKPT], ku_c[kDiagKPT];
+  int pos_c[kDiagKPT];
+  if (cached) {
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u) {
+      const int i = tid + u * kDiagNT;
+      const bool in = i < n;
+      pos_c[u] = in ? dpos[i] : -1;
+      const float r = in ? draw[i] : 0.f, v = in ? dutil[i] : 0.f;
+      kr_c[u] = diag_key(r, pos_c[u]);
+      ku_c[u] = diag_key(v, pos_c[u]);
+    }
+  }
 
   // ---- the retained set: slots [0, count] except the free slot ------------------
   const int cnt = A.count[g], hl = A.hole[g];
   int i_s = 0, n_s = 0, bad = 0;
-  for (int j = tid; j <= cnt; j += kDiagNT) {
-    if (j == hl || j >= A.cap) continue;
-    const int p = gp[j];
+  auto keep_slot = [&](int p, int old) {
     if (p < 0 || p >= A.maxpos) {
       bad = 1;
-      continue;
+      return;
     }
-    i_s += (tp > 0 && st_kept[p] == tp) ? 1 : 0;
+    i_s += (tp > 0 && old == tp) ? 1 : 0;
     st_kept[p] = A.t;
     ++n_s;
+  };
+  if (cnt + 1 <= kDiagNT * kDiagKPT) {
+    // every position load, then every stamp load, then the stores
+    int pk[kDiagKPT], old[kDiagKPT];
+    bool in[kDiagKPT];
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u) {
+      const int j = tid + u * kDiagNT;
+      in[u] = j <= cnt && j != hl && j < A.cap;
+      pk[u] = in[u] ? gp[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u)
+      old[u] = (in[u] && pk[u] >= 0 && pk[u] < A.maxpos) ? st_kept[pk[u]] : 0;
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u)
+      if (in[u]) keep_slot(pk[u], old[u]);
+  } else {
+    for (int j = tid; j <= cnt; j += kDiagNT) {
+      if (j == hl || j >= A.cap) continue;
+      const int p = gp[j];
+      keep_slot(p, (p >= 0 && p < A.maxpos) ? st_kept[p] : 0);
+    }
   }
 
   // ---- top-k thresholds --------------------------------------------------------
   unsigned long long thr[2];
-  kth_largest_pair(n, k, dpos, draw, dutil, thr);  // synchronises the block
+  kth_largest_pair(n, k, dpos, draw, dutil, cached, kr_c, ku_c, thr);  // synchronises the block
 
   // ---- membership, overlaps and evictions ------------------------------------------
   int i_r = 0, i_u = 0, i_ru = 0, i_rev = 0, n_ev = 0;
-  for (int i = tid; i < n; i += kDiagNT) {
-    const int p = dpos[i];
+  // the stamps of a step token p: kept after this step, in the previous raw
+  // and utility top-k
+  auto visit = [&](int p, unsigned long long kr, unsigned long long ku, int skept, int sraw, int sutil) {
     if (p < 0 || p >= A.maxpos) {
       bad = 1;
-      continue;
+      return;
     }
-    const bool inr = diag_key(draw[i], p) >= thr[0];
-    const bool inu = diag_key(dutil[i], p) >= thr[1];
-    const bool ev = st_kept[p] != A.t;
+    const bool inr = kr >= thr[0];
+    const bool inu = ku >= thr[1];
+    const bool ev = skept != A.t;
     if (ev) {
       ev_step[p] = A.t;
       ++n_ev;
     }
     if (inr) {
-      i_r += (tp > 0 && st_raw[p] == tp) ? 1 : 0;
+      i_r += (tp > 0 && sraw == tp) ? 1 : 0;
       st_raw[p] = A.t;
     }
     if (inu) {
-      i_u += (tp > 0 && st_util[p] == tp) ? 1 : 0;
+      i_u += (tp > 0 && sutil == tp) ? 1 : 0;
       st_util[p] = A.t;
     }
     i_ru += (inr && inu) ? 1 : 0;
     i_rev += (inr && ev) ? 1 : 0;
+  };
+  auto ok = [&](int p) { return p >= 0 && p < A.maxpos; };
+  if (cached) {
+    int sk[kDiagKPT], sr[kDiagKPT], su[kDiagKPT];
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u) {
+      const int p = pos_c[u];
+      const bool in = tid + u * kDiagNT < n && ok(p);
+      sk[u] = in ? st_kept[p] : 0;
+      sr[u] = in && kr_c[u] >= thr[0] ? st_raw[p] : 0;
+      su[u] = in && ku_c[u] >= thr[1] ? st_util[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kDiagKPT; ++u)
+      if (tid + u * kDiagNT < n) visit(pos_c[u], kr_c[u], ku_c[u], sk[u], sr[u], su[u]);
+  } else {
+    for (int i = tid; i < n; i += kDiagNT) {
+      const int p = dpos[i];
+      const bool in = ok(p);
+      visit(p, diag_key(draw[i], p), diag_key(dutil[i], p), in ? st_kept[p] : 0, in ? st_raw[p] : 0,
+            in ? st_util[p] : 0);
+    }
   }
-  i_s = block_sum_int(i_s, red);
-  n_s = block_sum_int(n_s, red);
-  bad = block_sum_int(bad, red);
-  i_r = block_sum_int(i_r, red);
-  i_u = block_sum_int(i_u, red);
-  i_ru = block_sum_int(i_ru, red);
-  i_rev = block_sum_int(i_rev, red);
-  n_ev = block_sum_int(n_ev, red);
+  int sums[8] = {i_s, n_s, bad, i_r, i_u, i_ru, i_rev, n_ev};
+  block_sum_ints(sums, red);
   if (tid != 0) return;
+  i_s = sums[0];
+  n_s = sums[1];
+  bad = sums[2];
+  i_r = sums[3];
+  i_u = sums[4];
+  i_ru = sums[5];
+  i_rev = sums[6];
+  n_ev = sums[7];
   if (bad) atomicOr(A.errflag, 64);
   const bool pair = tp > 0;
   int* c = A.cnt + static_cast<int64_t>(g) * kDiagCounts;
