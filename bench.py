@@ -243,7 +243,7 @@ def run_block(args, w):
     for t in range(args.warmup):
         ctx.step(*inputs[t], out)
     dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total)
-    names = ("open", "attn", "merge", "mass", "policy")
+    names = ("open", "attn", "merge", "mass", "policy", "offload")
     prof = {k: ctx.profile_read(k) for k in names}
     # resident tokens read by a steady step: every resident block is full
     # except the sequence's last one (the new token's)
@@ -260,7 +260,7 @@ def run_block(args, w):
     attn_ms, attn_n = prof["attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
-    policy_ms = sum(prof[k][0] for k in ("merge", "mass", "policy")) / n_prof
+    policy_ms = sum(prof[k][0] for k in ("merge", "mass", "policy", "offload")) / n_prof
     result = {
         "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
         "value": round(args.steps / dt, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -269,7 +269,8 @@ def run_block(args, w):
         "data": "synthetic (seeded generator: region labels, shared heavy blocks re-targeted per epoch)",
         "config": {"workload": w.name, "layers": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "batch": w.batch, "prefill": [min(w.prefill_lens), max(w.prefill_lens)],
-                   "block_budget_frac": w.budget_frac, "alpha_new": w.alpha_new, "beta": w.beta},
+                   "block_budget_frac": w.budget_frac, "alpha_new": w.alpha_new, "beta": w.beta,
+                   "offload_blocks": w.offload_blocks},
         "resident_tokens": n_tok,
         "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),

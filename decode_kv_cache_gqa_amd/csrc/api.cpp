@@ -42,9 +42,12 @@ void free_all(kvev_ctx* c) {
                   d.grpctr, d.blk_key, d.blk_slot, d.blk_sum, d.btab, d.nres,
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
                   d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole, d.dg_n, d.dg_pos, d.dg_raw,
-                  d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc};
+                  d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc,
+                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot};
   for (void* p : ptrs)
     if (p) hipFree(p);
+  if (c->hpool) hipHostFree(c->hpool);
+  c->hpool = c->hpool_dev = nullptr;
   d = DevState{};
   tier_free(c);
   for (auto& r : c->prof.pending) {
@@ -155,6 +158,8 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
       (f.scorer != 0 || f.granularity != KVEV_PER_KV_HEAD))
     return bad("scorer variants and granularity apply to the token policies only");
+  if (f.offload_blocks < 0) return bad("offload_blocks must be >= 0");
+  if (f.offload_blocks > 0 && f.policy != KVEV_LRFU_BLOCK) return bad("offload_blocks applies to the block mode only");
   if (f.diag_topk < 0) return bad("diag_topk must be >= 0");
   if (f.diag_topk > 0 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("diagnostics apply to the token policies only");
@@ -316,6 +321,19 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     A(dalloc(&d.bmass, Bs * c->maxpages));
     A(dalloc(&d.bbudget, Bs));
     A(dalloc(&d.rd_ids, c->maxpages));
+    if (f.offload_blocks > 0) {
+      A(dalloc(&d.ev_n, Bs));
+      A(dalloc(&d.ev_blk, Bs * c->maxpages));
+      A(dalloc(&d.ev_page, static_cast<size_t>(G) * c->maxpages));
+      A(dalloc(&d.hslot, Bs * c->maxblk));
+      A(dalloc(&d.sowner, static_cast<size_t>(f.offload_blocks)));
+      A(dalloc(&d.rd_slots, c->maxpages));
+      A(dalloc(&d.ev_slot, Bs * c->maxpages));
+      // K and V pages of every layer and KV head per slot
+      const size_t slot_bytes = 2ull * L * f.n_kv_heads * c->PT * D * c->elem;
+      A(hipHostMalloc(&c->hpool, slot_bytes * f.offload_blocks, hipHostMallocDefault));
+      if (c->hpool) A(hipHostGetDevicePointer(&c->hpool_dev, c->hpool, 0));
+    }
   }
   if (e != hipSuccess) {
     g_create_error = std::string("device allocation failed: ") + hipGetErrorString(e);
@@ -357,6 +375,15 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     A(hipMemsetAsync(d.bcnt, 0, Bs * c->maxblk * kRegions, c->stream));
     A(hipMemsetAsync(d.bmass, 0, sizeof(float) * Bs * c->maxpages, c->stream));
     A(hipMemsetAsync(d.rd_ids, 0, sizeof(int) * c->maxpages, c->stream));
+    if (f.offload_blocks > 0) {
+      A(hipMemsetAsync(d.ev_n, 0, sizeof(int) * Bs, c->stream));
+      A(hipMemsetAsync(d.ev_blk, 0, sizeof(int) * Bs * c->maxpages, c->stream));
+      A(hipMemsetAsync(d.ev_page, 0, sizeof(int) * G * c->maxpages, c->stream));
+      A(hipMemsetAsync(d.hslot, 0xff, sizeof(int) * Bs * c->maxblk, c->stream));  // -1
+      A(hipMemsetAsync(d.sowner, 0xff, sizeof(int) * f.offload_blocks, c->stream));
+      A(hipMemsetAsync(d.rd_slots, 0, sizeof(int) * c->maxpages, c->stream));
+      A(hipMemsetAsync(d.ev_slot, 0xff, sizeof(int) * Bs * c->maxpages, c->stream));
+    }
     std::vector<int> stack(static_cast<size_t>(G) * c->maxpages), top(G, c->maxpages);
     for (int64_t g = 0; g < G; ++g)
       for (int i = 0; i < c->maxpages; ++i)  // popped from the top: lowest page first
@@ -535,6 +562,23 @@ static int block_fill(const kvev_ctx* c, int64_t npos) {
 // Block mode step: open (slot and block of the new token), attention,
 // split merge, block mass, policy (score and clock update; selection and
 // table compaction when do_select).
+// Host-offload tier: after a selection that evicted ev[b] blocks of each
+// sequence, copy them into the pool's next ring slots (the last
+// offload_blocks of them when more were evicted).
+static hipError_t offload_evicted(kvev_ctx* c, const std::vector<int>& ev) {
+  int E = 0, kmax = 0;
+  for (int k : ev) {
+    E += k;
+    kmax = std::max(kmax, k);
+  }
+  if (E == 0) return hipSuccess;
+  ProfScope p(c, "offload");
+  const hipError_t e = launch_offload(c, kmax, E);
+  const int C = c->cfg.offload_blocks;
+  c->ring = (c->ring + std::min(C, E)) % C;
+  return e;
+}
+
 static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                               float* out, bool do_select, int64_t override_budget) {
   if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
@@ -574,6 +618,14 @@ static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, con
     KVEV_HIP(c, launch_block_policy(c, static_cast<int>(t), 1, do_select ? 1 : 0, 1,
                                     static_cast<int>(override_budget > 0 ? override_budget : 0)));
   }
+  if (c->cfg.offload_blocks > 0 && do_select) {
+    std::vector<int> ev(Bsz, 0);
+    for (int b = 0; b < Bsz; ++b) {
+      const int open = c->nres[b] + (c->npos[b] % c->PT == 0 ? 1 : 0);
+      ev[b] = std::max(0, open - Bs[b]);
+    }
+    KVEV_HIP(c, offload_evicted(c, ev));
+  }
   for (int b = 0; b < Bsz; ++b) {
     if (c->npos[b] % c->PT == 0) c->nres[b] += 1;
     c->npos[b] += 1;
@@ -598,6 +650,11 @@ static kvev_status block_evict(kvev_ctx* c, int64_t override_budget) {
     ProfScope p(c, "policy");
     KVEV_HIP(c, launch_block_policy(c, static_cast<int>(c->t), 0, 1, 0,
                                     static_cast<int>(override_budget > 0 ? override_budget : 0)));
+  }
+  if (c->cfg.offload_blocks > 0) {
+    std::vector<int> ev(Bsz, 0);
+    for (int b = 0; b < Bsz; ++b) ev[b] = std::max(0, c->nres[b] - Bs[b]);
+    KVEV_HIP(c, offload_evicted(c, ev));
   }
   for (int b = 0; b < Bsz; ++b) {
     if (c->nres[b] > Bs[b]) c->nres[b] = Bs[b];
@@ -842,11 +899,69 @@ kvev_status kvev_readmit(kvev_ctx* c, int32_t seq, int64_t n, const int64_t* ids
   return KVEV_OK;
 }
 
+kvev_status kvev_readmit_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const int64_t* ids) {
+  KVEV_LIVE(c);
+  if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (c->cfg.offload_blocks <= 0) return fail(c, KVEV_ESTATE, "the host-offload tier is off");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (!c->prefilled[seq]) return fail(c, KVEV_ESTATE, "sequence has no prefill");
+  if (n < 1 || !ids) return fail(c, KVEV_EINVAL, "null argument or n < 1");
+  if (c->nres[seq] + n > c->maxpages || c->count[seq * c->cfg.n_kv_heads] + c->PT * n + 1 > c->cap)
+    return fail(c, KVEV_ENOMEM, "block table full");
+  const int64_t tail = (c->npos[seq] - 1) / c->PT;
+  std::vector<int> res(tail + 1), slot(tail + 1);
+  const int64_t row = static_cast<int64_t>(seq) * c->maxblk;
+  KVEV_HIP(c, hipMemcpyAsync(res.data(), c->d.bres + row, sizeof(int) * (tail + 1), hipMemcpyDeviceToHost,
+                             c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(slot.data(), c->d.hslot + row, sizeof(int) * (tail + 1), hipMemcpyDeviceToHost,
+                             c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  std::vector<int> id32(n), sl(n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= tail) return fail(c, KVEV_EINVAL, "block id unknown or still being filled");
+    if (res[ids[i]]) return fail(c, KVEV_EINVAL, "block is resident (or listed twice)");
+    if (slot[ids[i]] < 0 || slot[ids[i]] >= c->cfg.offload_blocks)
+      return fail(c, KVEV_ESTATE, "block is not in the host pool");
+    res[ids[i]] = 1;
+    id32[i] = static_cast<int>(ids[i]);
+    sl[i] = slot[ids[i]];
+  }
+  const int e0 = c->nres[seq] - 1;
+  KVEV_HIP(c, hipMemcpyAsync(c->d.rd_ids, id32.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(c->d.rd_slots, sl.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
+  {
+    ProfScope p(c, "readmit");
+    KVEV_HIP(c, launch_block_readmit(c, seq, static_cast<int>(n), c->d.rd_ids, static_cast<int>(c->t)));
+    KVEV_HIP(c, launch_restore(c, seq, static_cast<int>(n), e0, c->d.rd_slots));
+  }
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));  // id32 and sl are local
+  c->nres[seq] += static_cast<int>(n);
+  for (int h = 0; h < c->cfg.n_kv_heads; ++h) c->count[seq * c->cfg.n_kv_heads + h] += c->PT * n;
+  return KVEV_OK;
+}
+
+kvev_status kvev_offload_state(kvev_ctx* c, int32_t seq, int32_t* slot, int64_t cap, int64_t* n_blocks) {
+  KVEV_LIVE(c);
+  if (!c->block_mode || c->cfg.offload_blocks <= 0) return fail(c, KVEV_ESTATE, "the host-offload tier is off");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_ERANGE, "sequence index out of range");
+  const int64_t nb = (c->npos[seq] + c->PT - 1) / c->PT;
+  if (n_blocks) *n_blocks = nb;
+  if (!slot) return KVEV_OK;
+  if (nb > cap) return fail(c, KVEV_ERANGE, "cap too small");
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  if (nb > 0)
+    KVEV_HIP(c, hipMemcpy(slot, c->d.hslot + static_cast<int64_t>(seq) * c->maxblk, sizeof(int) * nb,
+                          hipMemcpyDeviceToHost));
+  return KVEV_OK;
+}
+
 kvev_status kvev_import_blocks(kvev_ctx* c, int32_t seq, int64_t n_blocks, const float* score,
                                const int32_t* tref, const uint8_t* resident, int64_t n_tokens,
                                const void* k, const void* v) {
   KVEV_LIVE(c);
   if (!c->block_mode) return fail(c, KVEV_EINVAL, "not in block mode");
+  if (c->cfg.offload_blocks > 0)
+    return fail(c, KVEV_ESTATE, "host-offload tier on: the block state changes only by steps and readmissions");
   if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
   if (!c->prefilled[seq]) return fail(c, KVEV_ESTATE, "sequence has no prefill");
   if (!score || !tref || !resident || !k || !v) return fail(c, KVEV_EINVAL, "null argument");

@@ -41,6 +41,12 @@ struct BlockArgs {
   const float* part_ml;
   const float* part_o;
   float* out;
+  // host-offload tier (null when off)
+  int* ev_n;      // [batch] blocks the last selection evicted
+  int* ev_blk;    // [batch][maxpages] their block ids, in table order
+  int* ev_page;   // [G][maxpages] their pages, per KV head
+  int* hslot;     // [batch][maxblk] host-pool slot holding an evicted block, or -1
+  int* sowner;    // [offload_blocks] b * maxblk + block of each slot's block, or -1
   int L, G, Hkv, Hq, HG, D, maxpages, maxblk, S, batch;
   int64_t cap, lstride;
   float alpha, beta, tau;
@@ -305,6 +311,7 @@ __global__ __launch_bounds__(kPolNT) void blk_policy_kernel(BlockArgs A, int upd
   }
   if (!sel) {
     if (appended && tid < A.Hkv) A.count[g0 + tid] = cnt;
+    if (A.ev_n && tid == 0) A.ev_n[b] = 0;
     return;
   }
   __syncthreads();
@@ -338,8 +345,12 @@ __global__ __launch_bounds__(kPolNT) void blk_policy_kernel(BlockArgs A, int upd
   for (int e = tid; e < nres; e += kPolNT) {
     const int ni = s_new[e];
     const int j = A.btab[brow + e];
-    if (ni >= 0) s_btab[ni] = j;
-    else A.bres[bblk + j] = 0;
+    if (ni >= 0) {
+      s_btab[ni] = j;
+    } else {
+      A.bres[bblk + j] = 0;
+      if (A.ev_blk) A.ev_blk[brow + (-1 - ni)] = j;
+    }
   }
   __syncthreads();
   for (int e = tid; e < kept; e += kPolNT) A.btab[brow + e] = s_btab[e];
@@ -351,8 +362,12 @@ __global__ __launch_bounds__(kPolNT) void blk_policy_kernel(BlockArgs A, int upd
     __syncthreads();
     for (int e = tid; e < nres; e += kPolNT) {
       const int ni = s_new[e];
-      if (ni >= 0) A.ptab[grow + ni] = s_row[e];
-      else A.fstack[grow + top + (-1 - ni)] = s_row[e];
+      if (ni >= 0) {
+        A.ptab[grow + ni] = s_row[e];
+      } else {
+        A.fstack[grow + top + (-1 - ni)] = s_row[e];
+        if (A.ev_page) A.ev_page[grow + (-1 - ni)] = s_row[e];
+      }
     }
     __syncthreads();
     if (tid == 0) A.ftop[g] = top + (nres - kept);
@@ -365,6 +380,7 @@ __global__ __launch_bounds__(kPolNT) void blk_policy_kernel(BlockArgs A, int upd
   }
   if (tid < A.Hkv) A.count[g0 + tid] = new_cnt;
   if (tid == 0) A.nres[b] = kept;
+  if (A.ev_n && tid == 0) A.ev_n[b] = nres - kept;
 }
 
 // ---------------------------------------------------------------------------
@@ -409,6 +425,110 @@ __global__ void blk_readmit_kernel(BlockArgs A, int b, int n, const int* __restr
     }
     A.btab[brow + e_tail + n] = tail_j;
     A.nres[b] = e_tail + 1 + n;
+    // a resident block holds no host-pool slot
+    if (A.hslot)
+      for (int i = 0; i < n; ++i) {
+        const int sl = A.hslot[bblk + ids[i]];
+        if (sl >= 0) {
+          A.sowner[sl] = -1;
+          A.hslot[bblk + ids[i]] = -1;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-offload tier ("MemDecay" section III-E: pages offloaded to host memory
+// before they are dropped, recovered when they become relevant again; the
+// "Attention-Aware Block Eviction" page: a block's policy state survives its
+// eviction).  After a selection, every evicted block's pages (each layer and
+// KV head, K and V as stored) are copied into a slot of a pinned host pool
+// of C slots, written by the kernel through its device mapping.  Order: the
+// step's evictions are ranked by (sequence, block id); with E of them, the
+// last min(C, E) take consecutive ring slots from `ring` and the rest are
+// dropped.  A slot's previous block loses its copy.
+// offload_slot_kernel: one block per sequence ranks its evictions, assigns
+// the slots and updates the slot tables; offload_copy_kernel: one block per
+// (evicted block, layer) copies that layer's pages.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void offload_slot_kernel(BlockArgs A, int* __restrict__ ev_slot, int C,
+                                                           int ring, int e_host) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int kb = A.ev_n[b];
+  const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
+  // the step's evictions before this sequence's, and in all
+  int off = 0, E = 0;
+  for (int i = 0; i < A.batch; ++i) {
+    const int k = A.ev_n[i];
+    off += i < b ? k : 0;
+    E += k;
+  }
+  const int kept = E < C ? E : C;
+  for (int j = tid; j < kb; j += 256) {
+    if (E != e_host) {  // the host's count sizes the ring: never disagree silently
+      ev_slot[brow + j] = -1;
+      atomicOr(A.errflag, 128);
+      continue;
+    }
+    const int blk = A.ev_blk[brow + j];
+    int r = 0;  // rank of the block id among the sequence's evictions
+    for (int i = 0; i < kb; ++i) r += A.ev_blk[brow + i] < blk ? 1 : 0;
+    const int gidx = off + r - (E - kept);  // index among the offloaded ones
+    if (gidx < 0) {                         // dropped: a later eviction of this step takes its slot
+      ev_slot[brow + j] = -1;
+      continue;
+    }
+    const int slot = static_cast<int>((static_cast<int64_t>(ring) + gidx) % C);
+    ev_slot[brow + j] = slot;
+    const int key = b * A.maxblk + blk;
+    const int prev = A.sowner[slot];
+    if (prev >= 0 && A.hslot[prev] == slot) A.hslot[prev] = -1;
+    A.sowner[slot] = key;
+    A.hslot[key] = slot;
+  }
+}
+
+// pool slot layout: K pages then V pages, each [L][Hkv][page_vec] 16-byte vectors
+__global__ __launch_bounds__(256) void offload_copy_kernel(BlockArgs A, const int* __restrict__ ev_slot,
+                                                           uint4* __restrict__ pool,
+                                                           const uint4* __restrict__ kpool,
+                                                           const uint4* __restrict__ vpool, int64_t page_vec,
+                                                           int64_t P) {
+  const int j = blockIdx.x, b = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
+  if (j >= A.ev_n[b]) return;
+  const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
+  const int slot = ev_slot[brow + j];
+  if (slot < 0) return;
+  const int64_t per_half = static_cast<int64_t>(A.L) * A.Hkv * page_vec;
+  uint4* dst = pool + static_cast<int64_t>(slot) * 2 * per_half + static_cast<int64_t>(l) * A.Hkv * page_vec;
+  const int64_t n = static_cast<int64_t>(A.Hkv) * page_vec;
+  for (int64_t i = tid; i < n; i += 256) {
+    const int h = static_cast<int>(i / page_vec), x = static_cast<int>(i % page_vec);
+    const int page = A.ev_page[static_cast<int64_t>(b * A.Hkv + h) * A.maxpages + j];
+    const int64_t src = (static_cast<int64_t>(l) * P + page) * page_vec + x;
+    const uint4 kv = kpool[src], vv = vpool[src];
+    dst[i] = kv;
+    dst[per_half + i] = vv;
+  }
+}
+
+// Re-admission from the host pool: after blk_readmit_kernel gave the n blocks
+// table entries [e0, e0 + n), copy slot slots[i] into entry e0 + i's pages.
+// Grid (n, Hkv * L).
+__global__ __launch_bounds__(256) void restore_kernel(BlockArgs A, const uint4* __restrict__ pool,
+                                                      uint4* __restrict__ kpool, uint4* __restrict__ vpool,
+                                                      int64_t page_vec, int64_t P, int b, int e0,
+                                                      const int* __restrict__ slots) {
+  const int i = blockIdx.x, lh = blockIdx.y, tid = threadIdx.x;
+  const int l = lh / A.Hkv, h = lh % A.Hkv;
+  const int slot = slots[i];
+  const int page = A.ptab[static_cast<int64_t>(b * A.Hkv + h) * A.maxpages + e0 + i];
+  const int64_t per_half = static_cast<int64_t>(A.L) * A.Hkv * page_vec;
+  const uint4* src = pool + static_cast<int64_t>(slot) * 2 * per_half + static_cast<int64_t>(lh) * page_vec;
+  const int64_t dst = (static_cast<int64_t>(l) * P + page) * page_vec;
+  for (int x = tid; x < page_vec; x += 256) {
+    kpool[dst + x] = src[x];
+    vpool[dst + x] = src[per_half + x];
   }
 }
 
@@ -438,6 +558,11 @@ static BlockArgs block_args(kvev_ctx* c, float* out, int n_max) {
   A.part_ml = c->d.part_ml;
   A.part_o = c->d.part_o;
   A.out = out;
+  A.ev_n = c->d.ev_n;
+  A.ev_blk = c->d.ev_blk;
+  A.ev_page = c->d.ev_page;
+  A.hslot = c->d.hslot;
+  A.sowner = c->d.sowner;
   A.L = cf.n_layers;
   A.G = c->G;
   A.Hkv = cf.n_kv_heads;
@@ -490,6 +615,28 @@ hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, in
   const size_t shm = static_cast<size_t>(c->maxpages) * (8 + 4);
   blk_policy_kernel<<<c->cfg.batch, kPolNT, shm, c->stream>>>(A, update, do_select, appended,
                                                               budget_override);
+  return hipGetLastError();
+}
+
+hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host) {
+  BlockArgs A = block_args(c, nullptr, 1);
+  const int64_t page_vec = static_cast<int64_t>(c->PT) * c->cfg.head_dim * c->elem / 16;
+  offload_slot_kernel<<<c->cfg.batch, 256, 0, c->stream>>>(A, c->d.ev_slot, c->cfg.offload_blocks,
+                                                           static_cast<int>(c->ring), e_host);
+  dim3 grid(k_max, c->cfg.batch, c->cfg.n_layers);
+  offload_copy_kernel<<<grid, 256, 0, c->stream>>>(A, c->d.ev_slot, static_cast<uint4*>(c->hpool_dev),
+                                                   static_cast<const uint4*>(c->d.kpool),
+                                                   static_cast<const uint4*>(c->d.vpool), page_vec, c->P);
+  return hipGetLastError();
+}
+
+hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* slots_dev) {
+  BlockArgs A = block_args(c, nullptr, 1);
+  const int64_t page_vec = static_cast<int64_t>(c->PT) * c->cfg.head_dim * c->elem / 16;
+  dim3 grid(n, c->cfg.n_layers * c->cfg.n_kv_heads);
+  restore_kernel<<<grid, 256, 0, c->stream>>>(A, static_cast<const uint4*>(c->hpool_dev),
+                                              static_cast<uint4*>(c->d.kpool), static_cast<uint4*>(c->d.vpool),
+                                              page_vec, c->P, b, e0, slots_dev);
   return hipGetLastError();
 }
 

@@ -67,6 +67,14 @@ struct DevState {
   int* dprev = nullptr;     // [G][4] last recorded step, its k, its retained count
   int* dcnt = nullptr;      // [G][kDiagCounts] the last step's counts
   double* dacc = nullptr;   // [G][kDiagAcc] sums over the recorded steps
+  // host-offload tier (block mode, cfg.offload_blocks > 0)
+  int* ev_n = nullptr;      // [batch] blocks the last selection evicted
+  int* ev_blk = nullptr;    // [batch][maxpages] their ids
+  int* ev_page = nullptr;   // [G][maxpages] their pages
+  int* hslot = nullptr;     // [batch][maxblk] pool slot of an evicted block, or -1
+  int* sowner = nullptr;    // [offload_blocks] owner b * maxblk + block, or -1
+  int* rd_slots = nullptr;  // [maxpages] slots of a re-admission
+  int* ev_slot = nullptr;   // [batch][maxpages] pool slot of each evicted block, or -1 (dropped)
   // block-granular mode
   int* btab = nullptr;      // [batch][maxpages] logical block of each table entry
   int* nres = nullptr;      // [batch] table entries (resident blocks)
@@ -159,6 +167,9 @@ struct kvev_ctx {
                                             // single-token eviction; an append fills it)
   std::vector<int> prefilled;               // per sequence
   std::vector<int64_t> seq_next;            // per sequence: the next position (token modes)
+  void* hpool = nullptr;                    // pinned host pool of the offload tier
+  void* hpool_dev = nullptr;                // its device mapping
+  int64_t ring = 0;                         // next offload slot (mod offload_blocks)
   std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
   std::vector<int> free_pages;
   int64_t t = 0;
@@ -232,6 +243,10 @@ hipError_t launch_block_mass(kvev_ctx* c, int n_max);
 hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
                                int budget_override);
 hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, int t);
+// host-offload tier: copy the last selection's evicted blocks into the pool;
+// copy pool slots into the entries [e0, e0 + n) of sequence b
+hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host);
+hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* slots_dev);
 // two-tier window mode (tier.hip)
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n);
 hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new);

@@ -51,6 +51,7 @@ class Config(ctypes.Structure):
         ("scorer", ctypes.c_int32), ("granularity", ctypes.c_int32),
         ("route_interval", ctypes.c_int32),
         ("diag_topk", ctypes.c_int32),
+        ("offload_blocks", ctypes.c_int32),
     ]
 
 
@@ -90,6 +91,9 @@ _SIGS = {
     "kvev_set_budget": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64]),
     "kvev_readmit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]),
+    "kvev_readmit_offloaded": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    "kvev_offload_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.POINTER(ctypes.c_int64)]),
     "kvev_block_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
     "kvev_import_blocks": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
@@ -284,6 +288,19 @@ class Context:
         self._check(lib().kvev_readmit(self._h, seq, ids.shape[0], ids.ctypes.data_as(ctypes.c_void_p),
                                        _ptr(k, self.dtype, shape, "k"), _ptr(v, self.dtype, shape, "v")))
 
+    def readmit_offloaded(self, seq, block_ids):
+        """Re-admit evicted blocks of `seq` from the host-offload pool."""
+        ids = np.ascontiguousarray(block_ids, dtype=np.int64)
+        self._check(lib().kvev_readmit_offloaded(self._h, seq, ids.size, ids.ctypes.data_as(ctypes.c_void_p)))
+
+    def offload_state(self, seq):
+        """Pool slot of every block `seq` has had (-1: not in the pool)."""
+        n = ctypes.c_int64()
+        buf = np.zeros(self.cfg.max_tokens // 16 + 2, np.int32)
+        self._check(lib().kvev_offload_state(self._h, seq, buf.ctypes.data_as(ctypes.c_void_p), buf.size,
+                                             ctypes.byref(n)))
+        return buf[: n.value].copy()
+
     def block_state(self, seq):
         """(score float32, tref int32, resident bool) over every block seen."""
         cap = (self.cfg.max_tokens + 15) // 16
@@ -415,7 +432,7 @@ def tier_capacities(b_hist, q, m_f, m_q):
     return kf.value, kq.value
 
 
-def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None):
+def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None):
     """A context configured for a synth.Workload (diag_topk: rank-trace
     diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
@@ -427,7 +444,7 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None):
             alpha_new=w.alpha_new, budget=max(w.block_budget(b) for b in range(w.batch))
             if budget is None else budget, beta=w.beta,
             pinned_region_mask=sum(1 << r for r in w.pinned_regions), decode_region=w.decode_region,
-            access_tau_mult=2.0)
+            access_tau_mult=2.0, offload_blocks=w.offload_blocks if offload_blocks is None else offload_blocks)
         for r, hl in enumerate(w.region_half_lives):
             cfg.region_half_life[r] = hl
         return Context(cfg, stream=stream)

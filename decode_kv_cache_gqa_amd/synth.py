@@ -137,6 +137,7 @@ class Workload:
     granularity: str = "kv_head"    # kv_head | sequence
     route_interval: int = 1         # tiered mode: routing events every route_interval steps
     diag_topk: int = 0              # token modes: rank-trace diagnostics over the top-k (0: off)
+    offload_blocks: int = 0         # block mode: host-offload pool slots (0: off)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -401,6 +402,10 @@ def workload(name: str) -> Workload:
     if name == "llama8b_32k_diag":
         # rank-trace diagnostics at k = the budget ("What Matters ...", appendix I)
         return replace(workload("llama8b_32k"), name="llama8b_32k_10pct_diag", diag_topk=3277)
+    if name == "lrfu64_offload":
+        # evicted blocks kept in a pinned host pool of 1,024 blocks ("MemDecay" section III-E)
+        return replace(workload("lrfu64"), name="lrfu_64seq_4k16k_blocks20pct_offload1024",
+                       offload_blocks=1024)
     if name == "qevict131k_omega8":
         # the review's routing interval: one routing event every 8 steps (section 4.2 Eq.1)
         return replace(workload("qevict131k"), name="qevict_131k_fp5_int2_20_omega8", route_interval=8)
@@ -409,4 +414,4 @@ def workload(name: str) -> Workload:
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
              "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8",
-             "llama8b_32k_diag")
+             "llama8b_32k_diag", "lrfu64_offload")

@@ -172,6 +172,15 @@ typedef struct {
    * state (kvev_decode_step, kvev_evict and kvev_import_group return
    * KVEV_ESTATE).  Appendix I of "What Matters ..." takes k = the budget. */
   int32_t diag_topk;
+  /* KVEV_LRFU_BLOCK only: host-offload tier ("MemDecay" section III-E).  0:
+   * off.  C >= 1: a pinned host pool of C block slots (each block's K and V
+   * pages of every layer and KV head, as stored).  After every selection the
+   * evicted blocks are copied into it, ranked by (sequence, block id); when a
+   * selection evicts E > C blocks only the last C are kept.  Slots are reused
+   * in ring order, so the pool holds the latest C evictions that have not
+   * been re-admitted since; kvev_readmit_offloaded recovers them.
+   * kvev_import_blocks is then refused (KVEV_ESTATE). */
+  int32_t offload_blocks;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -354,6 +363,19 @@ kvev_status kvev_set_budget(kvev_ctx* ctx, int32_t seq, int64_t budget);
  * resident or unknown, duplicates), KVEV_ENOMEM (no free pages). */
 kvev_status kvev_readmit(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* block_ids,
                          const void* k, const void* v);
+
+/* Re-admit n evicted blocks of sequence `seq` from the host-offload pool
+ * (cfg.offload_blocks > 0): as kvev_readmit, with each block's K and V
+ * taken from its pool slot (bit-exact copies of its pages at eviction) and
+ * the slot released.  Synchronises.  Errors: as kvev_readmit, and
+ * KVEV_ESTATE (offload off, or a block no longer in the pool: never
+ * offloaded, or its slot reused by a later eviction). */
+kvev_status kvev_readmit_offloaded(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* block_ids);
+
+/* Host-pool slot of every block sequence `seq` has had (ids
+ * 0..*n_blocks-1): slot index, or -1 (resident, never evicted, or dropped).
+ * Synchronises.  Errors: KVEV_ESTATE (offload off), KVEV_ERANGE. */
+kvev_status kvev_offload_state(kvev_ctx* ctx, int32_t seq, int32_t* slot, int64_t cap, int64_t* n_blocks);
 
 /* Copy the state of every block sequence `seq` has had so far (ids
  * 0..*n_blocks-1) to host buffers: score, clock (step of the last access or

@@ -41,7 +41,7 @@ __all__ = [
     "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
     "vnorm_weights", "normalized_entropy", "scored_mass", "SCORERS",
     "PooledTokenOracle", "jaccard", "top_k_positions", "RankTraceDiagnostics",
-    "future_missed_mass",
+    "future_missed_mass", "HostOffloadPool",
 ]
 
 
@@ -1079,6 +1079,47 @@ class BlockLRFUOracle:
         tref = np.array([s.tref[j] for j in ids], dtype=np.int64)
         res = np.array([j in s.resident for j in ids], dtype=bool)
         return ids, score, tref, res
+
+
+class HostOffloadPool:
+    """Which evicted blocks a host pool of ``capacity`` slots still holds.
+
+    [MemDecay] §III-E: a tiered extension offloads pages to host memory
+    before dropping them and recovers them when later queries make them
+    relevant again; [LRFU-fig]: a block's policy state persists across its
+    eviction.  Readings: one slot holds one block (every layer and KV head);
+    slots are reused in ring order, so the pool keeps the latest evictions;
+    within one selection the evicted blocks are ordered by (sequence, block
+    id) and, when there are more than ``capacity`` of them, only the last
+    ``capacity`` are kept; a re-admitted block's slot is released (a
+    resident block holds no slot).
+    """
+
+    def __init__(self, capacity):
+        self.capacity = int(capacity)
+        self.slots = [None] * self.capacity
+        self.where = {}  # (seq, block) -> slot
+        self.ring = 0
+
+    def offload(self, evicted):
+        """Record one selection's evictions, an iterable of (seq, block)."""
+        order = sorted(evicted)
+        kept = min(self.capacity, len(order))
+        for i, key in enumerate(order[len(order) - kept:]):
+            s = (self.ring + i) % self.capacity
+            prev = self.slots[s]
+            if prev is not None and self.where.get(prev) == s:
+                del self.where[prev]
+            self.slots[s] = key
+            self.where[key] = s
+        self.ring = (self.ring + kept) % self.capacity
+
+    def readmit(self, key):
+        s = self.where.pop(key)
+        self.slots[s] = None
+
+    def slot(self, key):
+        return self.where.get(key, -1)
 
 
 # ---------------------------------------------------------------------------

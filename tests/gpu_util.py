@@ -612,6 +612,107 @@ def run_block_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", 
 
 
 # ---------------------------------------------------------------------------
+# Host-offload tier of the block mode
+# ---------------------------------------------------------------------------
+
+def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cuda"):
+    """Two block contexts on the same inputs: `plain` (no pool) re-admits each
+    epoch's heavy blocks with K/V regenerated from the seed, `off` (a host
+    pool of `capacity` blocks) re-admits the same blocks from its pool.  Every
+    step both must agree bit for bit (outputs, scores, clocks, residency,
+    retained positions, exported K/V), and the pool's slot of every block
+    must equal the oracle's HostOffloadPool fed with each selection's
+    evictions.  Blocks no longer in the pool are refused by the offload
+    re-admission and skipped by both."""
+    import pytest
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+
+    log(f"[offload] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:6]} steps={steps} "
+        f"capacity={capacity} fused={fused}")
+    ctxs = [kvev.context_for(w, max_steps=steps, offload_blocks=0),
+            kvev.context_for(w, max_steps=steps, offload_blocks=capacity)]
+    plain, off = ctxs
+    pool = orc.HostOffloadPool(capacity)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device=device)
+        lab = w.region_labels(b)
+        for c in ctxs:
+            c.prefill(b, K.contiguous(), V.contiguous(), lab)
+            c.set_budget(b, w.block_budget(b))
+        del K, V
+    torch.cuda.synchronize()
+    outs = [torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
+            for _ in ctxs]
+    stats = {"readmitted": 0, "refused": 0, "offloaded": 0, "dropped": 0}
+
+    def resident(c, b):
+        return np.asarray(c.block_state(b)[2], dtype=bool)
+
+    for t in range(1, steps + 1):
+        if _epoch_start(w, t):
+            e = w.epoch_of(t)
+            for b in range(w.batch):
+                res = set(np.flatnonzero(resident(plain, b)).tolist())
+                tail = (w.prefill_lens[b] + t - 2) // 16
+                cand = [j for j in w.heavy_blocks(b, e) if j not in res and j < tail]
+                ids = [j for j in cand if pool.slot((b, j)) >= 0]
+                for j in cand:
+                    if pool.slot((b, j)) < 0:
+                        # dropped from the pool (or never offloaded): refused, state untouched
+                        with pytest.raises(kvev.KvevError):
+                            off.readmit_offloaded(b, [j])
+                        stats["refused"] += 1
+                        break
+                if not ids:
+                    continue
+                Kr, Vr = block_rows(w, b, ids, device)
+                plain.readmit(b, ids, Kr, Vr)
+                off.readmit_offloaded(b, ids)
+                for j in ids:
+                    pool.readmit((b, j))
+                stats["readmitted"] += len(ids)
+        before = {b: resident(plain, b) for b in range(w.batch)}
+        q, kn, vn = w.step_inputs(t, device=device)
+        for c, o in zip(ctxs, outs):
+            if fused:
+                c.step(q, kn, vn, o)
+            else:
+                c.decode_step(q, kn, vn, o)
+                c.evict()
+        assert torch.equal(outs[0], outs[1]), f"step {t}: outputs differ"
+        evicted = []
+        for b in range(w.batch):
+            sp, so = plain.block_state(b), off.block_state(b)
+            for x, y, name in zip(sp, so, ("score", "clock", "resident")):
+                np.testing.assert_array_equal(x, y, err_msg=f"step {t} b={b}: {name}")
+            now = np.asarray(sp[2], dtype=bool)
+            was = np.zeros_like(now)
+            was[:len(before[b])] = before[b]
+            evicted += [(b, int(j)) for j in np.flatnonzero(was & ~now)]
+        pool.offload(evicted)
+        stats["offloaded"] += min(capacity, len(evicted))
+        stats["dropped"] += max(0, len(evicted) - capacity)
+        for b in range(w.batch):
+            got = off.offload_state(b)
+            want = np.array([pool.slot((b, j)) for j in range(len(got))], dtype=np.int32)
+            np.testing.assert_array_equal(got, want, err_msg=f"step {t} b={b}: pool slots")
+            if kv_every and (t % kv_every == 0 or t == steps):
+                for h in range(w.n_kv_heads):
+                    np.testing.assert_array_equal(plain.retained(b, h), off.retained(b, h),
+                                                  err_msg=f"step {t} b={b} kvh={h}: retained")
+                    kp, vp = plain.export_kv(b, h)
+                    ko, vo = off.export_kv(b, h)
+                    assert torch.equal(kp, ko) and torch.equal(vp, vo), f"step {t} b={b} kvh={h}: K/V differ"
+        if t == 1 or t % 16 == 0 or t == steps:
+            log(f"[offload] step {t}: {stats}")
+    for c in ctxs:
+        c.sync()
+        c.close()
+    return stats
+
+
+# ---------------------------------------------------------------------------
 # Two-tier window mode (full precision / INT2 / evicted per layer)
 # ---------------------------------------------------------------------------
 

@@ -104,6 +104,8 @@ def _create(**kw):
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, max_tokens=200000), "196608"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
     (dict(diag_topk=-1), "diag_topk"),
+    (dict(offload_blocks=-1), "offload_blocks"),
+    (dict(offload_blocks=8), "block mode only"),
     (dict(diag_topk=4, policy=kvev.LRFU_BLOCK, n_q_heads=8), "token policies"),
     (dict(diag_topk=4, policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, batch=1), "token policies"),
     (dict(diag_topk=4, granularity=kvev.PER_SEQUENCE), "diagnostics need"),
@@ -139,6 +141,8 @@ def test_diag_entry_points_reject_null_context():
     assert L.kvev_diag_read(None, None, 1) == kvev.EINVAL
     assert L.kvev_diag_trace(None, 0, 0, None, None, None, 0, None) == kvev.EINVAL
     assert L.kvev_diag_fmm(None, None, None) == kvev.EINVAL
+    assert L.kvev_readmit_offloaded(None, 0, 1, None) == kvev.EINVAL
+    assert L.kvev_offload_state(None, 0, None, 0, None) == kvev.EINVAL
 
 
 def test_null_arguments():
