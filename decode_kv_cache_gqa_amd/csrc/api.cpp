@@ -158,6 +158,8 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if ((f.policy == KVEV_LRFU_BLOCK || f.policy == KVEV_TIERED_INT2) &&
       (f.scorer != 0 || f.granularity != KVEV_PER_KV_HEAD))
     return bad("scorer variants and granularity apply to the token policies only");
+  if (f.revival_gap < 0) return bad("revival_gap must be >= 0");
+  if (f.revival_gap > 0 && f.policy != KVEV_TIERED_INT2) return bad("revival_gap applies to the tiered mode only");
   if (f.offload_blocks < 0) return bad("offload_blocks must be >= 0");
   if (f.offload_blocks > 0 && f.policy != KVEV_LRFU_BLOCK) return bad("offload_blocks applies to the block mode only");
   if (f.diag_topk < 0) return bad("diag_topk must be >= 0");

@@ -98,6 +98,12 @@ struct TierDev {
   uint8_t* hasled = nullptr; // [L][NW] 1 once the window has been quantized
   uint8_t* forced = nullptr; // [L][NW] tiers imported by kvev_tier_import
   float* S = nullptr;        // [L][NW] cumulative window score
+  // routing diagnostics (cfg.revival_gap > 0)
+  int* rd_fstamp = nullptr;  // [L][NW] last event that routed the window to full precision
+  int* rd_rstamp = nullptr;  // [L][NW] last event that kept it (full precision or INT2)
+  int* rd_run = nullptr;     // [L][NW] consecutive events outside full precision
+  int* rd_cnt = nullptr;     // [L][6] the last event's set sizes and overlaps
+  double* rd_acc = nullptr;  // [L][6] events, pairs, churn sums, sustained, revived
   int* fplist = nullptr;     // [L][NW] full-precision windows (pinned, local, routed)
   int* qlist = nullptr;      // [L][NW] INT2 windows
   int* jobs = nullptr;       // [L][NW] transition jobs: window << 2 | kind (1 quantize, 2 promote)
@@ -114,6 +120,7 @@ struct TierHost {
   int n_q = 0;       // INT2 windows listed
   int n_kept = 0;    // routed windows in F or Q after the last routing event
   int na_prev = 0;   // aged windows at the last routing event
+  int events = 0;    // routing events so far
 };
 
 // Kernel arguments of the tiered mode.
@@ -133,6 +140,12 @@ struct TierArgs {
   float* ml;       // [L][Hkv][4][2]
   float* emass;
   int* errflag;
+  int* rd_fstamp;  // routing diagnostics, or null
+  int* rd_rstamp;
+  int* rd_run;
+  int* rd_cnt;
+  double* rd_acc;
+  int rd_gap, rd_event;
   int L, Hkv, Hq, NW, maxch;
 };
 

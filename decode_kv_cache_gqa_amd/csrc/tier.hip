@@ -628,6 +628,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __shared__ uint8_t tl[kTierMaxWin];
   __shared__ uint8_t hl[kTierMaxWin];
   __shared__ int ncand, njobs, wsum[2][kRouteNT / kWave], base[2];
+  __shared__ int dsum[6][kRouteNT / kWave];
   const int l = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int64_t lw0 = static_cast<int64_t>(l) * A.NW;
   if (tid == 0) {
@@ -735,9 +736,74 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     base[0] = totF;
     base[1] = totQ;
   }
+  // routing diagnostics over this event's candidates (aged, not evicted
+  // before it): the stamps of the previous event give the overlaps, the run
+  // counters the sustained absences and revivals
+  const bool diag = A.rd_cnt != nullptr && forced == nullptr;
+  const int ev = A.rd_event;
+  int dF = 0, dFo = 0, dR = 0, dRo = 0, dS = 0, dV = 0;
   for (int w = tid; w < nw; w += kRouteNT) {
-    A.tier[lw0 + w] = tl[w];
-    A.hasled[lw0 + w] = hl[w];
+    const int64_t i = lw0 + w;
+    if (diag && aged(w) && A.tier[i] != 2) {
+      const bool inF = tl[w] == 0, inR = tl[w] != 2;
+      if (inF) {
+        ++dF;
+        dFo += (ev > 1 && A.rd_fstamp[i] == ev - 1) ? 1 : 0;  // stamps start at 0
+        A.rd_fstamp[i] = ev;
+      }
+      if (inR) {
+        ++dR;
+        dRo += (ev > 1 && A.rd_rstamp[i] == ev - 1) ? 1 : 0;
+        A.rd_rstamp[i] = ev;
+      }
+      int run = A.rd_run[i];
+      if (inF) {
+        dV += run >= A.rd_gap ? 1 : 0;
+        run = 0;
+      } else {
+        ++run;
+        dS += run == A.rd_gap ? 1 : 0;
+      }
+      A.rd_run[i] = run;
+    }
+    A.tier[i] = tl[w];
+    A.hasled[i] = hl[w];
+  }
+  if (diag) {
+    int v[6] = {dF, dFo, dR, dRo, dS, dV};
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      v[j] = wave_sum_int(v[j]);
+      if (lane == 0) dsum[j][wv] = v[j];
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int j = 0; j < 6; ++j) {
+        int t = 0;
+        for (int u = 0; u < kRouteNT / kWave; ++u) t += dsum[j][u];
+        v[j] = t;
+      }
+      int* cn = A.rd_cnt + l * 6;
+      double* ac = A.rd_acc + l * 6;
+      const int fp = cn[1], rp = cn[4];  // the previous event's sizes
+      const bool pair = ev > 1;
+      cn[0] = pair ? fp : 0;
+      cn[1] = v[0];
+      cn[2] = v[1];
+      cn[3] = pair ? rp : 0;
+      cn[4] = v[2];
+      cn[5] = v[3];
+      ac[0] += 1.0;
+      if (pair) {
+        const int uf = fp + v[0] - v[1], ur = rp + v[2] - v[3];
+        ac[1] += 1.0;
+        ac[2] += uf > 0 ? 1.0 - static_cast<double>(v[1]) / uf : 0.0;
+        ac[3] += ur > 0 ? 1.0 - static_cast<double>(v[3]) / ur : 0.0;
+      }
+      ac[4] += v[4];
+      ac[5] += v[5];
+    }
   }
   if (tid == 0) {
     A.njobs[l] = njobs;
@@ -948,6 +1014,13 @@ static TierArgs tier_args(kvev_ctx* c) {
   a.ml = c->d.ml;
   a.emass = c->td.emass;
   a.errflag = c->d.errflag;
+  a.rd_fstamp = c->td.rd_fstamp;
+  a.rd_rstamp = c->td.rd_rstamp;
+  a.rd_run = c->td.rd_run;
+  a.rd_cnt = c->td.rd_cnt;
+  a.rd_acc = c->td.rd_acc;
+  a.rd_gap = c->cfg.revival_gap;
+  a.rd_event = c->tw.events + 1;
   a.L = c->cfg.n_layers;
   a.Hkv = c->cfg.n_kv_heads;
   a.Hq = c->cfg.n_q_heads;

@@ -43,7 +43,8 @@ Counts tier_counts(const kvev_ctx* c) {
 void tier_free(kvev_ctx* c) {
   auto& t = c->td;
   void* ptrs[] = {t.kfp, t.vfp, t.ledger, t.tier, t.hasled, t.forced, t.S,
-                  t.fplist, t.qlist, t.jobs, t.njobs, t.emass};
+                  t.fplist, t.qlist, t.jobs, t.njobs, t.emass, t.rd_fstamp, t.rd_rstamp,
+                  t.rd_run, t.rd_cnt, t.rd_acc};
   for (void* p : ptrs)
     if (p) hipFree(p);
   t = TierDev{};
@@ -77,7 +78,21 @@ hipError_t tier_alloc(kvev_ctx* c) {
   A(dalloc(&d.part_o, parts * kTierD));
   A(dalloc(&d.ml, static_cast<size_t>(L) * H * 4 * 2));
   A(dalloc(&d.errflag, 1));
+  if (f.revival_gap > 0) {
+    A(dalloc(&t.rd_fstamp, lw));
+    A(dalloc(&t.rd_rstamp, lw));
+    A(dalloc(&t.rd_run, lw));
+    A(dalloc(&t.rd_cnt, static_cast<size_t>(L) * 6));
+    A(dalloc(&t.rd_acc, static_cast<size_t>(L) * 6));
+  }
   if (e != hipSuccess) return e;
+  if (f.revival_gap > 0) {
+    A(hipMemsetAsync(t.rd_fstamp, 0, lw * sizeof(int), c->stream));
+    A(hipMemsetAsync(t.rd_rstamp, 0, lw * sizeof(int), c->stream));
+    A(hipMemsetAsync(t.rd_run, 0, lw * sizeof(int), c->stream));
+    A(hipMemsetAsync(t.rd_cnt, 0, L * 6 * sizeof(int), c->stream));
+    A(hipMemsetAsync(t.rd_acc, 0, L * 6 * sizeof(double), c->stream));
+  }
   // zero the storage so that unwritten rows are finite
   A(hipMemsetAsync(t.kfp, 0, win * kTierWin * kTierD * 2, c->stream));
   A(hipMemsetAsync(t.vfp, 0, win * kTierWin * kTierD * 2, c->stream));
@@ -149,6 +164,7 @@ kvev_status tier_route(kvev_ctx* c) {
   tw.n_q = nQ;
   tw.n_kept = nF + nQ;
   tw.na_prev = k.na;
+  tw.events += 1;
   return KVEV_OK;
 }
 
@@ -161,6 +177,31 @@ kvev_status tier_scores(kvev_ctx* c, int layer, float* dst, int64_t cap, int64_t
 using namespace kvev;
 
 extern "C" {
+
+kvev_status kvev_tier_diag(kvev_ctx* c, int32_t layer, kvev_route_diag* out) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  if (c->cfg.revival_gap <= 0 || !c->td.rd_cnt) return fail(c, KVEV_ESTATE, "routing diagnostics are off");
+  if (layer < 0 || layer >= c->cfg.n_layers || !out) return fail(c, KVEV_ERANGE, "layer out of range or null output");
+  int cn[6];
+  double ac[6];
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  KVEV_HIP(c, hipMemcpy(cn, c->td.rd_cnt + layer * 6, sizeof(cn), hipMemcpyDeviceToHost));
+  KVEV_HIP(c, hipMemcpy(ac, c->td.rd_acc + layer * 6, sizeof(ac), hipMemcpyDeviceToHost));
+  out->f_prev = cn[0];
+  out->f_new = cn[1];
+  out->f_overlap = cn[2];
+  out->r_prev = cn[3];
+  out->r_new = cn[4];
+  out->r_overlap = cn[5];
+  out->events = static_cast<int64_t>(ac[0]);
+  out->pairs = static_cast<int64_t>(ac[1]);
+  out->sum_f_churn = ac[2];
+  out->sum_r_churn = ac[3];
+  out->sustained = static_cast<int64_t>(ac[4]);
+  out->revived = static_cast<int64_t>(ac[5]);
+  return KVEV_OK;
+}
 
 kvev_status kvev_tier_state(kvev_ctx* c, int32_t layer, float* score, uint8_t* tier, uint8_t* ledger,
                             int64_t cap, int64_t* n_windows) {

@@ -52,7 +52,19 @@ class Config(ctypes.Structure):
         ("route_interval", ctypes.c_int32),
         ("diag_topk", ctypes.c_int32),
         ("offload_blocks", ctypes.c_int32),
+        ("revival_gap", ctypes.c_int32),
     ]
+
+
+class RouteDiag(ctypes.Structure):
+    """kvev_route_diag: one layer's routing diagnostics."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "f_prev", "f_new", "f_overlap", "r_prev", "r_new", "r_overlap")] + [
+        ("events", ctypes.c_int64), ("pairs", ctypes.c_int64), ("sustained", ctypes.c_int64),
+        ("revived", ctypes.c_int64), ("sum_f_churn", ctypes.c_double), ("sum_r_churn", ctypes.c_double)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 class DiagGroup(ctypes.Structure):
@@ -113,6 +125,7 @@ _SIGS = {
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.POINTER(ctypes.c_int64)]),
     "kvev_diag_fmm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
+    "kvev_tier_diag": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(RouteDiag)]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
     "kvev_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
@@ -396,6 +409,12 @@ class Context:
         m = n.value
         return pos[:m].copy(), raw[:m].copy(), util[:m].copy()
 
+    def tier_diag(self, layer):
+        """Routing diagnostics of `layer` (tiered mode, revival_gap > 0)."""
+        d = RouteDiag()
+        self._check(lib().kvev_tier_diag(self._h, layer, ctypes.byref(d)))
+        return d.as_dict()
+
     def sync(self):
         self._check(lib().kvev_sync(self._h))
 
@@ -432,7 +451,8 @@ def tier_capacities(b_hist, q, m_f, m_q):
     return kf.value, kq.value
 
 
-def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None):
+def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None,
+                revival_gap=None):
     """A context configured for a synth.Workload (diag_topk: rank-trace
     diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
@@ -454,7 +474,8 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             head_dim=w.head_dim, batch=w.batch, dtype=F32 if w.dtype == "f32" else BF16,
             max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=TIERED_INT2,
             n_sink=w.n_sink, n_recent=w.n_recent, budget=1, window_tokens=w.window_tokens,
-            fp_windows=w.fp_windows, int2_windows=w.int2_windows, route_interval=w.route_interval)
+            fp_windows=w.fp_windows, int2_windows=w.int2_windows, route_interval=w.route_interval,
+            revival_gap=w.revival_gap if revival_gap is None else revival_gap)
         return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

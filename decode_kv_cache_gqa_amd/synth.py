@@ -138,6 +138,7 @@ class Workload:
     route_interval: int = 1         # tiered mode: routing events every route_interval steps
     diag_topk: int = 0              # token modes: rank-trace diagnostics over the top-k (0: off)
     offload_blocks: int = 0         # block mode: host-offload pool slots (0: off)
+    revival_gap: int = 0            # tiered mode: routing diagnostics, sustained-absence length (0: off)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property

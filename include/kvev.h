@@ -181,6 +181,15 @@ typedef struct {
    * been re-admitted since; kvev_readmit_offloaded recovers them.
    * kvev_import_blocks is then refused (KVEV_ESTATE). */
   int32_t offload_blocks;
+  /* KVEV_TIERED_INT2 only: routing diagnostics ("QEvict" review, section 3).
+   * 0: off.  g >= 1: every routing event records, per layer, the selection
+   * churn of the routed full-precision set and of the routed retained set
+   * (full precision or INT2) against the previous event, and Global LIR: a
+   * routed window's run of consecutive events outside the full-precision
+   * set counts as sustained when it reaches g events, and as revived when
+   * the window re-enters the full-precision set after such a run.  Tier
+   * imports (kvev_tier_import) are not routing events and record nothing. */
+  int32_t revival_gap;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -443,6 +452,25 @@ kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void
 kvev_status kvev_tier_ledger(kvev_ctx* ctx, int32_t layer, int32_t kv_head, int32_t window,
                              uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero);
+
+/* Routing diagnostics of one layer (cfg.revival_gap > 0).  Over the
+ * event's candidates (aged windows not evicted before it): F = those routed
+ * to full precision, R = those kept (full precision or INT2). */
+typedef struct {
+  int32_t f_prev, f_new, f_overlap;  /* |F_e-1|, |F_e|, |F_e & F_e-1| of the last event */
+  int32_t r_prev, r_new, r_overlap;  /* the same for R */
+  int64_t events;                    /* routing events so far */
+  int64_t pairs;                     /* events with a previous one */
+  int64_t sustained;                 /* runs outside F that reached revival_gap events */
+  int64_t revived;                   /* such runs ended by re-entering F */
+  double sum_f_churn;                /* 1 - J(F_e, F_e-1) over the pairs */
+  double sum_r_churn;                /* 1 - J(R_e, R_e-1) */
+} kvev_route_diag;
+
+/* Copy layer `layer`'s routing diagnostics to host *out.  Synchronises.
+ * Errors: KVEV_EINVAL (not tiered mode), KVEV_ESTATE (diagnostics off),
+ * KVEV_ERANGE (layer). */
+kvev_status kvev_tier_diag(kvev_ctx* ctx, int32_t layer, kvev_route_diag* out);
 
 /* Replace the window state of `layer`: host score and tier (as in
  * kvev_tier_state) for windows 0..n_windows-1 (n_windows must equal the

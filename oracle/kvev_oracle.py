@@ -41,7 +41,7 @@ __all__ = [
     "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
     "vnorm_weights", "normalized_entropy", "scored_mass", "SCORERS",
     "PooledTokenOracle", "jaccard", "top_k_positions", "RankTraceDiagnostics",
-    "future_missed_mass", "HostOffloadPool",
+    "future_missed_mass", "HostOffloadPool", "RoutingDiagnostics",
 ]
 
 
@@ -1079,6 +1079,56 @@ class BlockLRFUOracle:
         tref = np.array([s.tref[j] for j in ids], dtype=np.int64)
         res = np.array([j in s.resident for j in ids], dtype=bool)
         return ids, score, tref, res
+
+
+class RoutingDiagnostics:
+    """Selection churn and Global LIR of one layer's routing events.
+
+    [QEvict] §3: selection churn is the Jaccard distance between the retained
+    sets of consecutive routing events; Global LIR measures how often a
+    window that stayed out of the full-precision set for a sustained period
+    re-enters it.  Readings: the sets are taken over the event's candidates
+    (aged windows not evicted before it): F = those routed to full
+    precision, R = those kept (full precision or INT2); a window's run of
+    consecutive events outside F is sustained once it reaches ``gap`` events
+    (the review leaves the length open) and revived when the window then
+    re-enters F.  Feed ``observe`` with each event's candidates and the
+    tiers after it (0 full precision, 1 INT2, 2 evicted).
+    """
+
+    def __init__(self, gap):
+        self.gap = int(gap)
+        self.prev = None  # (F, R) of the previous event
+        self.run = {}
+        self.sums = {"events": 0, "pairs": 0, "sum_f_churn": 0.0, "sum_r_churn": 0.0,
+                     "sustained": 0, "revived": 0}
+
+    def observe(self, candidates, tiers):
+        F = {int(w) for w in candidates if tiers[w] == 0}
+        R = {int(w) for w in candidates if tiers[w] != 2}
+        sm = self.sums
+        sm["events"] += 1
+        c = {"f_new": len(F), "r_new": len(R)}
+        if self.prev is None:
+            c.update(f_prev=0, f_overlap=0, r_prev=0, r_overlap=0)
+        else:
+            Fp, Rp = self.prev
+            c.update(f_prev=len(Fp), f_overlap=len(F & Fp), r_prev=len(Rp), r_overlap=len(R & Rp))
+            sm["pairs"] += 1
+            sm["sum_f_churn"] += 1.0 - jaccard(F, Fp)
+            sm["sum_r_churn"] += 1.0 - jaccard(R, Rp)
+        for w in candidates:
+            w = int(w)
+            run = self.run.get(w, 0)
+            if tiers[w] == 0:
+                sm["revived"] += 1 if run >= self.gap else 0
+                run = 0
+            else:
+                run += 1
+                sm["sustained"] += 1 if run == self.gap else 0
+            self.run[w] = run
+        self.prev = (F, R)
+        return c
 
 
 class HostOffloadPool:

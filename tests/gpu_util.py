@@ -724,9 +724,12 @@ def _tier_boundaries(S, tiers, cand):
 
 
 def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda", fused=True,
-                      kv_every=4, ledger_every=4):
+                      kv_every=4, ledger_every=4, revival_gap=0):
     """Run `steps` decode + routing steps of tiered workload `w` on the GPU and
-    the oracle (the oracle holds `sample_layers`)."""
+    the oracle (the oracle holds `sample_layers`).  revival_gap > 0: after
+    every routing event each sampled layer's routing diagnostics must equal
+    the oracle's, computed from the event's candidates and the library's own
+    tiers (exact)."""
     import torch
     from decode_kv_cache_gqa_amd import kvev
 
@@ -734,7 +737,8 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     log(f"[tier] {w.name}: L={w.n_layers} L0={w.prefill_lens[0]} steps={steps} K_f={w.fp_windows} "
         f"K_q={w.int2_windows} sink={w.n_sink} recent={w.n_recent} layers={layers} fused={fused}")
     t_start = time.time()
-    ctx = kvev.context_for(w, max_steps=steps)
+    ctx = kvev.context_for(w, max_steps=steps, revival_gap=revival_gap)
+    rdiag = {l: orc.RoutingDiagnostics(revival_gap) for l in layers} if revival_gap else None
     o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                          k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
                          n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1,
@@ -754,6 +758,8 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     Hg = w.group_size
     out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
     for t in range(1, steps + 1):
+        # the library's tiers before this step's routing event
+        gprev = {l: ctx.tier_state(l)[1] for l in layers} if rdiag else None
         q, kn, vn = w.step_inputs(t, device=device)
         if fused:
             ctx.step(q, kn, vn, out)
@@ -787,6 +793,16 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
             gs, gt, gl = ctx.tier_state(l)
             os_, ot, ol = o.window_state(l)
             assert len(gt) == len(ot), f"step {t} l={l}: {len(gt)} windows on the GPU, {len(ot)} in the oracle"
+            if rdiag and routes:
+                was = lambda x: gprev[l][x] if x < len(gprev[l]) else 0
+                cand = [x for x in range(nw_pre) if o.is_aged(x) and was(x) != 2]
+                exp = rdiag[l].observe(cand, gt)
+                got = ctx.tier_diag(l)
+                for k, v in exp.items():
+                    assert got[k] == v, f"step {t} l={l}: routing diagnostic {k} {got[k]} != {v}"
+                for k, v in rdiag[l].sums.items():
+                    assert abs(got[k] - v) <= 1e-12 * max(1.0, abs(v)), f"step {t} l={l}: {k} {got[k]!r} != {v!r}"
+                st.route_diag_checks = getattr(st, "route_diag_checks", 0) + 1
             st.promotions += int(((prev[l] == 1) & (ot == 0)).sum())
             if not np.array_equal(gt, ot) or not np.array_equal(gl, ol):
                 cand = [x for x in range(nw_pre) if o.is_aged(x) and prev[l][x] != 2]

@@ -105,6 +105,8 @@ def _create(**kw):
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
     (dict(diag_topk=-1), "diag_topk"),
     (dict(offload_blocks=-1), "offload_blocks"),
+    (dict(revival_gap=-1), "revival_gap"),
+    (dict(revival_gap=4), "tiered mode only"),
     (dict(offload_blocks=8), "block mode only"),
     (dict(diag_topk=4, policy=kvev.LRFU_BLOCK, n_q_heads=8), "token policies"),
     (dict(diag_topk=4, policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, batch=1), "token policies"),
@@ -136,6 +138,23 @@ def test_diag_group_struct_layout_matches_c(tmp_path):
     assert int(got["size"]) == ctypes.sizeof(kvev.DiagGroup)
 
 
+def test_route_diag_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "route_layout.c"
+    fields = [f for f, _ in kvev.RouteDiag._fields_]
+    body = "\n".join(f'  printf("{f} %zu\\n", offsetof(kvev_route_diag, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "kvev.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("size %zu\\n", sizeof(kvev_route_diag));\n'
+                   f'  return 0;\n}}\n')
+    exe = tmp_path / "route_layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                       check=True).stdout.splitlines())
+    for f in fields:
+        assert int(got[f]) == getattr(kvev.RouteDiag, f).offset, f
+    assert int(got["size"]) == ctypes.sizeof(kvev.RouteDiag)
+
+
 def test_diag_entry_points_reject_null_context():
     L = kvev.lib()
     assert L.kvev_diag_read(None, None, 1) == kvev.EINVAL
@@ -143,6 +162,7 @@ def test_diag_entry_points_reject_null_context():
     assert L.kvev_diag_fmm(None, None, None) == kvev.EINVAL
     assert L.kvev_readmit_offloaded(None, 0, 1, None) == kvev.EINVAL
     assert L.kvev_offload_state(None, 0, None, 0, None) == kvev.EINVAL
+    assert L.kvev_tier_diag(None, 0, None) == kvev.EINVAL
 
 
 def test_null_arguments():

@@ -89,3 +89,20 @@ def test_tier_route_interval_8(fused):
                                                    int2_windows=7, epoch_steps=12, n_epochs=3)
     st = _gu().run_tier_lockstep(w, 36, fused=fused)
     assert st.routing_events == 4
+
+
+@pytest.mark.parametrize("gap", [1, 4])
+def test_tier_routing_diagnostics(gap):
+    """Selection churn and Global LIR ("QEvict" review, section 3) recorded by
+    the routing kernel, against the oracle's on the event's candidates and
+    the library's tiers, over re-targeted heavy-key epochs (windows leave
+    and re-enter the full-precision set)."""
+    st = _gu().run_tier_lockstep(_scaled(), 48, revival_gap=gap)
+    assert st.route_diag_checks == 2 * 48
+
+
+def test_tier_routing_diagnostics_interval_8_separate_calls():
+    w = synth.workload("qevict131k_omega8").scaled(n_layers=2, prefill_lens=(700,), fp_windows=5,
+                                                   int2_windows=7, epoch_steps=12, n_epochs=3)
+    st = _gu().run_tier_lockstep(w, 36, fused=False, revival_gap=2)
+    assert st.route_diag_checks == 2 * 4
