@@ -91,3 +91,42 @@ def test_offload_refusals():
     off.sync()
     off.close()
     plain.close()
+
+
+def test_readmit_with_caller_kv_releases_the_slot():
+    """kvev_readmit (K/V from the caller) on an offload context also releases
+    the block's pool slot (a resident block holds none), so a later eviction
+    of the block takes a fresh slot and the pool follows the oracle's model."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    import gpu_util
+    import oracle as orc
+    w = _scaled(prefill_lens=(640,), n_epochs=1, epoch_steps=0)
+    ctx = kvev.context_for(w, max_steps=40, offload_blocks=64)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K.contiguous(), V.contiguous(), w.region_labels(0))
+    ctx.set_budget(0, w.block_budget(0))
+    pool = orc.HostOffloadPool(64)
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    readmitted = False
+    for t in range(1, 41):
+        before = np.asarray(ctx.block_state(0)[2], dtype=bool)
+        q, kn, vn = w.step_inputs(t, device="cuda")
+        ctx.step(q, kn, vn, out)
+        now = np.asarray(ctx.block_state(0)[2], dtype=bool)
+        was = np.zeros_like(now)
+        was[:len(before)] = before
+        pool.offload([(0, int(j)) for j in np.flatnonzero(was & ~now)])
+        slots = ctx.offload_state(0)
+        np.testing.assert_array_equal(slots, [pool.slot((0, j)) for j in range(len(slots))],
+                                      err_msg=f"step {t}: pool slots")
+        if t == 3:
+            j = int(np.flatnonzero(slots >= 0)[0])
+            Kr, Vr = gpu_util.block_rows(w, 0, [j], "cuda")
+            ctx.readmit(0, [j], Kr, Vr)
+            pool.readmit((0, j))
+            assert ctx.offload_state(0)[j] == -1
+            readmitted = True
+    assert readmitted
+    ctx.sync()
+    ctx.close()
