@@ -37,6 +37,15 @@ void prof_drain(kvev_ctx* c) {
 
 void free_all(kvev_ctx* c) {
   auto& d = c->d;
+  if (c->pf_stream) {  // copies may still read the pinned pool
+    hipStreamSynchronize(c->pf_stream);
+    hipStreamDestroy(c->pf_stream);
+    c->pf_stream = nullptr;
+  }
+  if (c->pf_done) hipEventDestroy(c->pf_done);
+  c->pf_done = nullptr;
+  if (c->dstage) hipFree(c->dstage);
+  c->dstage = nullptr;
   void* ptrs[] = {d.kpool, d.vpool, d.ptab, d.pos, d.score, d.count, d.nextpos, d.logits,
                   d.part_ml, d.part_o, d.ml, d.mv_src, d.mv_dst, d.nmoves, d.errflag,
                   d.grpctr, d.blk_key, d.blk_slot, d.blk_sum, d.btab, d.nres,
@@ -162,6 +171,8 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.revival_gap > 0 && f.policy != KVEV_TIERED_INT2) return bad("revival_gap applies to the tiered mode only");
   if (f.offload_blocks < 0) return bad("offload_blocks must be >= 0");
   if (f.offload_blocks > 0 && f.policy != KVEV_LRFU_BLOCK) return bad("offload_blocks applies to the block mode only");
+  if (f.prefetch_blocks < 0) return bad("prefetch_blocks must be >= 0");
+  if (f.prefetch_blocks > 0 && f.offload_blocks <= 0) return bad("prefetch_blocks needs the host-offload tier");
   if (f.diag_topk < 0) return bad("diag_topk must be >= 0");
   if (f.diag_topk > 0 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("diagnostics apply to the token policies only");
@@ -335,6 +346,13 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
       const size_t slot_bytes = 2ull * L * f.n_kv_heads * c->PT * D * c->elem;
       A(hipHostMalloc(&c->hpool, slot_bytes * f.offload_blocks, hipHostMallocDefault));
       if (c->hpool) A(hipHostGetDevicePointer(&c->hpool_dev, c->hpool, 0));
+      if (f.prefetch_blocks > 0) {
+        A(hipMalloc(&c->dstage, slot_bytes * f.prefetch_blocks));
+        A(hipStreamCreateWithFlags(&c->pf_stream, hipStreamNonBlocking));
+        A(hipEventCreateWithFlags(&c->pf_done, hipEventDisableTiming));
+        c->pf_of_slot.assign(f.offload_blocks, -1);
+        c->pf_slot.assign(f.prefetch_blocks, -1);
+      }
     }
   }
   if (e != hipSuccess) {
@@ -574,10 +592,21 @@ static hipError_t offload_evicted(kvev_ctx* c, const std::vector<int>& ev) {
     kmax = std::max(kmax, k);
   }
   if (E == 0) return hipSuccess;
+  const int C = c->cfg.offload_blocks;
+  const int kept = std::min(C, E);
+  if (c->pf_pending) {  // prefetch copies still read the slots about to be written
+    if (hipError_t w = hipStreamWaitEvent(c->stream, c->pf_done, 0)) return w;
+    c->pf_pending = false;
+  }
+  if (!c->pf_of_slot.empty())
+    for (int i = 0; i < kept; ++i) {
+      const int s = static_cast<int>((c->ring + i) % C);
+      if (c->pf_of_slot[s] >= 0) c->pf_slot[c->pf_of_slot[s]] = -1;
+      c->pf_of_slot[s] = -1;
+    }
   ProfScope p(c, "offload");
   const hipError_t e = launch_offload(c, kmax, E);
-  const int C = c->cfg.offload_blocks;
-  c->ring = (c->ring + std::min(C, E)) % C;
+  c->ring = (c->ring + kept) % C;
   return e;
 }
 
@@ -926,8 +955,20 @@ kvev_status kvev_readmit_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const in
       return fail(c, KVEV_ESTATE, "block is not in the host pool");
     res[ids[i]] = 1;
     id32[i] = static_cast<int>(ids[i]);
-    sl[i] = slot[ids[i]];
+    // a prefetched copy in device staging, else the pool slot (encoded -1 - slot)
+    const int s = slot[ids[i]];
+    const int st = c->pf_of_slot.empty() ? -1 : c->pf_of_slot[s];
+    sl[i] = st >= 0 ? st : -1 - s;
   }
+  if (c->pf_pending) {
+    KVEV_HIP(c, hipStreamWaitEvent(c->stream, c->pf_done, 0));
+    c->pf_pending = false;
+  }
+  for (int64_t i = 0; i < n; ++i)  // consumed: the slots are released below
+    if (sl[i] >= 0) {
+      c->pf_of_slot[c->pf_slot[sl[i]]] = -1;
+      c->pf_slot[sl[i]] = -1;
+    }
   const int e0 = c->nres[seq] - 1;
   KVEV_HIP(c, hipMemcpyAsync(c->d.rd_ids, id32.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
   KVEV_HIP(c, hipMemcpyAsync(c->d.rd_slots, sl.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
@@ -939,6 +980,40 @@ kvev_status kvev_readmit_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const in
   KVEV_HIP(c, hipStreamSynchronize(c->stream));  // id32 and sl are local
   c->nres[seq] += static_cast<int>(n);
   for (int h = 0; h < c->cfg.n_kv_heads; ++h) c->count[seq * c->cfg.n_kv_heads + h] += c->PT * n;
+  return KVEV_OK;
+}
+
+kvev_status kvev_prefetch_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const int64_t* ids) {
+  KVEV_LIVE(c);
+  if (!c->block_mode || c->cfg.prefetch_blocks <= 0 || !c->pf_stream)
+    return fail(c, KVEV_ESTATE, "prefetch is off");
+  if (seq < 0 || seq >= c->cfg.batch) return fail(c, KVEV_EINVAL, "sequence index out of range");
+  if (n < 1 || !ids || n > c->cfg.prefetch_blocks) return fail(c, KVEV_EINVAL, "n outside 1..prefetch_blocks");
+  const int64_t tail = (c->npos[seq] - 1) / c->PT;
+  std::vector<int> slot(tail + 1);
+  // the stream's earlier work (restores from staging, offloads into the pool) completes here
+  KVEV_HIP(c, hipMemcpyAsync(slot.data(), c->d.hslot + static_cast<int64_t>(seq) * c->maxblk,
+                             sizeof(int) * (tail + 1), hipMemcpyDeviceToHost, c->stream));
+  KVEV_HIP(c, hipStreamSynchronize(c->stream));
+  for (int64_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= tail) return fail(c, KVEV_EINVAL, "block id unknown or still being filled");
+    if (slot[ids[i]] < 0 || slot[ids[i]] >= c->cfg.offload_blocks)
+      return fail(c, KVEV_ESTATE, "block is not in the host pool");
+  }
+  const size_t sb = 2ull * c->cfg.n_layers * c->cfg.n_kv_heads * c->PT * c->cfg.head_dim * c->elem;
+  for (int64_t i = 0; i < n; ++i) {
+    const int s = slot[ids[i]];
+    if (c->pf_of_slot[s] >= 0) continue;  // already staged
+    const int st = c->pf_next;
+    c->pf_next = (c->pf_next + 1) % c->cfg.prefetch_blocks;
+    if (c->pf_slot[st] >= 0) c->pf_of_slot[c->pf_slot[st]] = -1;
+    KVEV_HIP(c, hipMemcpyAsync(static_cast<char*>(c->dstage) + sb * st, static_cast<char*>(c->hpool) + sb * s, sb,
+                               hipMemcpyHostToDevice, c->pf_stream));
+    c->pf_slot[st] = s;
+    c->pf_of_slot[s] = st;
+  }
+  KVEV_HIP(c, hipEventRecord(c->pf_done, c->pf_stream));
+  c->pf_pending = true;
   return KVEV_OK;
 }
 

@@ -513,18 +513,22 @@ __global__ __launch_bounds__(256) void offload_copy_kernel(BlockArgs A, const in
 }
 
 // Re-admission from the host pool: after blk_readmit_kernel gave the n blocks
-// table entries [e0, e0 + n), copy slot slots[i] into entry e0 + i's pages.
-// Grid (n, Hkv * L).
+// table entries [e0, e0 + n), copy block i's slot into entry e0 + i's pages;
+// src[i] >= 0 is a device staging slot (a prefetched copy), -1 - s pool
+// slot s.  Grid (n, Hkv * L).
 __global__ __launch_bounds__(256) void restore_kernel(BlockArgs A, const uint4* __restrict__ pool,
+                                                      const uint4* __restrict__ stage,
                                                       uint4* __restrict__ kpool, uint4* __restrict__ vpool,
                                                       int64_t page_vec, int64_t P, int b, int e0,
                                                       const int* __restrict__ slots) {
   const int i = blockIdx.x, lh = blockIdx.y, tid = threadIdx.x;
   const int l = lh / A.Hkv, h = lh % A.Hkv;
-  const int slot = slots[i];
+  const int v = slots[i];
   const int page = A.ptab[static_cast<int64_t>(b * A.Hkv + h) * A.maxpages + e0 + i];
   const int64_t per_half = static_cast<int64_t>(A.L) * A.Hkv * page_vec;
-  const uint4* src = pool + static_cast<int64_t>(slot) * 2 * per_half + static_cast<int64_t>(lh) * page_vec;
+  const uint4* base = v >= 0 ? stage : pool;
+  const int slot = v >= 0 ? v : -1 - v;
+  const uint4* src = base + static_cast<int64_t>(slot) * 2 * per_half + static_cast<int64_t>(lh) * page_vec;
   const int64_t dst = (static_cast<int64_t>(l) * P + page) * page_vec;
   for (int x = tid; x < page_vec; x += 256) {
     kpool[dst + x] = src[x];
@@ -630,13 +634,14 @@ hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host) {
   return hipGetLastError();
 }
 
-hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* slots_dev) {
+hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* src_dev) {
   BlockArgs A = block_args(c, nullptr, 1);
   const int64_t page_vec = static_cast<int64_t>(c->PT) * c->cfg.head_dim * c->elem / 16;
   dim3 grid(n, c->cfg.n_layers * c->cfg.n_kv_heads);
   restore_kernel<<<grid, 256, 0, c->stream>>>(A, static_cast<const uint4*>(c->hpool_dev),
+                                              static_cast<const uint4*>(c->dstage),
                                               static_cast<uint4*>(c->d.kpool), static_cast<uint4*>(c->d.vpool),
-                                              page_vec, c->P, b, e0, slots_dev);
+                                              page_vec, c->P, b, e0, src_dev);
   return hipGetLastError();
 }
 

@@ -183,6 +183,14 @@ struct kvev_ctx {
   void* hpool = nullptr;                    // pinned host pool of the offload tier
   void* hpool_dev = nullptr;                // its device mapping
   int64_t ring = 0;                         // next offload slot (mod offload_blocks)
+  // background prefetch of pool blocks into device staging
+  hipStream_t pf_stream = nullptr;          // the copies' stream (default priority)
+  hipEvent_t pf_done = nullptr;             // recorded after each batch of copies
+  bool pf_pending = false;                  // the context's stream has not waited for pf_done yet
+  void* dstage = nullptr;                   // [prefetch_blocks] device copies of pool slots
+  std::vector<int> pf_of_slot;              // pool slot -> staging slot, or -1
+  std::vector<int> pf_slot;                 // staging slot -> pool slot, or -1
+  int pf_next = 0;                          // next staging slot
   std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
   std::vector<int> free_pages;
   int64_t t = 0;
@@ -259,7 +267,8 @@ hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, i
 // host-offload tier: copy the last selection's evicted blocks into the pool;
 // copy pool slots into the entries [e0, e0 + n) of sequence b
 hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host);
-hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* slots_dev);
+// src_dev[i] >= 0: staging slot; -1 - s: pool slot s
+hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* src_dev);
 // two-tier window mode (tier.hip)
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n);
 hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new);

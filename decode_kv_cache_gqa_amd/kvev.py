@@ -53,6 +53,7 @@ class Config(ctypes.Structure):
         ("diag_topk", ctypes.c_int32),
         ("offload_blocks", ctypes.c_int32),
         ("revival_gap", ctypes.c_int32),
+        ("prefetch_blocks", ctypes.c_int32),
     ]
 
 
@@ -104,6 +105,7 @@ _SIGS = {
     "kvev_readmit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]),
     "kvev_readmit_offloaded": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
+    "kvev_prefetch_offloaded": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]),
     "kvev_offload_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
                                           ctypes.POINTER(ctypes.c_int64)]),
     "kvev_block_state": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -306,6 +308,11 @@ class Context:
         ids = np.ascontiguousarray(block_ids, dtype=np.int64)
         self._check(lib().kvev_readmit_offloaded(self._h, seq, ids.size, ids.ctypes.data_as(ctypes.c_void_p)))
 
+    def prefetch_offloaded(self, seq, block_ids):
+        """Start copying evicted blocks of `seq` from the host pool into device staging."""
+        ids = np.ascontiguousarray(block_ids, dtype=np.int64)
+        self._check(lib().kvev_prefetch_offloaded(self._h, seq, ids.size, ids.ctypes.data_as(ctypes.c_void_p)))
+
     def offload_state(self, seq):
         """Pool slot of every block `seq` has had (-1: not in the pool)."""
         n = ctypes.c_int64()
@@ -452,7 +459,7 @@ def tier_capacities(b_hist, q, m_f, m_q):
 
 
 def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None,
-                revival_gap=None):
+                revival_gap=None, prefetch_blocks=0):
     """A context configured for a synth.Workload (diag_topk: rank-trace
     diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
@@ -464,7 +471,8 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             alpha_new=w.alpha_new, budget=max(w.block_budget(b) for b in range(w.batch))
             if budget is None else budget, beta=w.beta,
             pinned_region_mask=sum(1 << r for r in w.pinned_regions), decode_region=w.decode_region,
-            access_tau_mult=2.0, offload_blocks=w.offload_blocks if offload_blocks is None else offload_blocks)
+            access_tau_mult=2.0, offload_blocks=w.offload_blocks if offload_blocks is None else offload_blocks,
+            prefetch_blocks=prefetch_blocks)
         for r, hl in enumerate(w.region_half_lives):
             cfg.region_half_life[r] = hl
         return Context(cfg, stream=stream)

@@ -190,6 +190,9 @@ typedef struct {
    * the window re-enters the full-precision set after such a run.  Tier
    * imports (kvev_tier_import) are not routing events and record nothing. */
   int32_t revival_gap;
+  /* KVEV_LRFU_BLOCK with offload_blocks > 0: device staging slots for
+   * kvev_prefetch_offloaded (0: no prefetch). */
+  int32_t prefetch_blocks;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
@@ -380,6 +383,18 @@ kvev_status kvev_readmit(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* b
  * KVEV_ESTATE (offload off, or a block no longer in the pool: never
  * offloaded, or its slot reused by a later eviction). */
 kvev_status kvev_readmit_offloaded(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* block_ids);
+
+/* Background prefetch ("MemDecay" section III-E): start copying n evicted
+ * blocks of sequence `seq` from the host pool into device staging slots
+ * (cfg.prefetch_blocks, reused in ring order) on a stream of the context's
+ * own, so that the copy overlaps later work on the context's stream.  A later
+ * kvev_readmit_offloaded of such a block restores it from the device copy.
+ * The context's stream waits for the copies before it next writes into the
+ * pool or restores from staging; a staging entry is dropped when its pool
+ * slot is reused.  Synchronises the context's stream first (to read the
+ * blocks' slots).  Errors: KVEV_ESTATE (prefetch off, a block not in the
+ * pool), KVEV_EINVAL (bad indices, n > prefetch_blocks). */
+kvev_status kvev_prefetch_offloaded(kvev_ctx* ctx, int32_t seq, int64_t n, const int64_t* block_ids);
 
 /* Host-pool slot of every block sequence `seq` has had (ids
  * 0..*n_blocks-1): slot index, or -1 (resident, never evicted, or dropped).

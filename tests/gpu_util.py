@@ -615,7 +615,7 @@ def run_block_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", 
 # Host-offload tier of the block mode
 # ---------------------------------------------------------------------------
 
-def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cuda"):
+def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cuda", prefetch=0):
     """Two block contexts on the same inputs: `plain` (no pool) re-admits each
     epoch's heavy blocks with K/V regenerated from the seed, `off` (a host
     pool of `capacity` blocks) re-admits the same blocks from its pool.  Every
@@ -623,7 +623,9 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     retained positions, exported K/V), and the pool's slot of every block
     must equal the oracle's HostOffloadPool fed with each selection's
     evictions.  Blocks no longer in the pool are refused by the offload
-    re-admission and skipped by both."""
+    re-admission and skipped by both.  prefetch > 0: `off` has that many
+    device staging slots and, one step before each epoch starts, prefetches
+    the heavy blocks it will re-admit (restored from the staged copies)."""
     import pytest
     import torch
     from decode_kv_cache_gqa_amd import kvev
@@ -631,7 +633,7 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     log(f"[offload] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:6]} steps={steps} "
         f"capacity={capacity} fused={fused}")
     ctxs = [kvev.context_for(w, max_steps=steps, offload_blocks=0),
-            kvev.context_for(w, max_steps=steps, offload_blocks=capacity)]
+            kvev.context_for(w, max_steps=steps, offload_blocks=capacity, prefetch_blocks=prefetch)]
     plain, off = ctxs
     pool = orc.HostOffloadPool(capacity)
     for b in range(w.batch):
@@ -644,12 +646,22 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     torch.cuda.synchronize()
     outs = [torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
             for _ in ctxs]
-    stats = {"readmitted": 0, "refused": 0, "offloaded": 0, "dropped": 0}
+    stats = {"readmitted": 0, "refused": 0, "offloaded": 0, "dropped": 0, "prefetched": 0}
 
     def resident(c, b):
         return np.asarray(c.block_state(b)[2], dtype=bool)
 
     for t in range(1, steps + 1):
+        if prefetch and t + 1 <= steps and _epoch_start(w, t + 1):
+            # background copies of the next epoch's heavy blocks, overlapping this step
+            e = w.epoch_of(t + 1)
+            for b in range(w.batch):
+                res = set(np.flatnonzero(resident(off, b)).tolist())
+                tail = (w.prefill_lens[b] + t - 2) // 16
+                ids = [j for j in w.heavy_blocks(b, e) if j not in res and j < tail and pool.slot((b, j)) >= 0]
+                if ids:
+                    off.prefetch_offloaded(b, ids[:prefetch])
+                    stats["prefetched"] += len(ids[:prefetch])
         if _epoch_start(w, t):
             e = w.epoch_of(t)
             for b in range(w.batch):

@@ -106,6 +106,8 @@ def _create(**kw):
     (dict(diag_topk=-1), "diag_topk"),
     (dict(offload_blocks=-1), "offload_blocks"),
     (dict(revival_gap=-1), "revival_gap"),
+    (dict(prefetch_blocks=-1), "prefetch_blocks"),
+    (dict(policy=kvev.LRFU_BLOCK, prefetch_blocks=4), "needs the host-offload tier"),
     (dict(revival_gap=4), "tiered mode only"),
     (dict(offload_blocks=8), "block mode only"),
     (dict(diag_topk=4, policy=kvev.LRFU_BLOCK, n_q_heads=8), "token policies"),
@@ -163,6 +165,7 @@ def test_diag_entry_points_reject_null_context():
     assert L.kvev_readmit_offloaded(None, 0, 1, None) == kvev.EINVAL
     assert L.kvev_offload_state(None, 0, None, 0, None) == kvev.EINVAL
     assert L.kvev_tier_diag(None, 0, None) == kvev.EINVAL
+    assert L.kvev_prefetch_offloaded(None, 0, 1, None) == kvev.EINVAL
 
 
 def test_null_arguments():

@@ -41,6 +41,16 @@ def test_offload_pool_overflow_and_ring_reuse():
     assert st["dropped"] > 0 and st["readmitted"] > 0 and st["refused"] > 0
 
 
+def test_offload_with_background_prefetch():
+    """Blocks prefetched into device staging one step before their
+    re-admission (the copy overlaps that step) come back bit-exact; a pool
+    smaller than the first selection keeps some prefetch targets out."""
+    st = _gu().run_offload_twins(_scaled(), 48, 512, prefetch=64)
+    assert st["prefetched"] > 0 and st["readmitted"] > 0
+    st = _gu().run_offload_twins(_scaled(), 48, 24, prefetch=4)
+    assert st["prefetched"] > 0
+
+
 def test_offload_separate_calls_fp32():
     """kvev_decode_step + kvev_evict (the standalone selection offloads too),
     fp32, d = 64, one layer."""
