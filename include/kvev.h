@@ -20,7 +20,9 @@
  *     runtime failure returns KVEV_EHIP and makes the context sticky: every
  *     later call except kvev_last_error / kvev_destroy returns KVEV_ESTATE.
  *     kvev_last_error() describes the last failure.
- *   - A context is bound to one HIP stream and is not thread safe.
+ *   - A context is bound to one HIP stream and is not thread safe.  (With
+ *     cfg.prefetch_blocks > 0 it also owns one copy stream of its own, at
+ *     default priority, ordered against the context's stream by events.)
  *   - Element dtype of q / k / v inputs is cfg.dtype (fp32 or bf16, dense,
  *     row-major, head_dim innermost); attention outputs are always fp32.
  */
