@@ -52,7 +52,7 @@ void free_all(kvev_ctx* c) {
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
                   d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole, d.dg_n, d.dg_pos, d.dg_raw,
                   d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc,
-                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot};
+                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot, d.oring};
   for (void* p : ptrs)
     if (p) hipFree(p);
   if (c->hpool) hipHostFree(c->hpool);
@@ -173,6 +173,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.offload_blocks > 0 && f.policy != KVEV_LRFU_BLOCK) return bad("offload_blocks applies to the block mode only");
   if (f.prefetch_blocks < 0) return bad("prefetch_blocks must be >= 0");
   if (f.prefetch_blocks > 0 && f.offload_blocks <= 0) return bad("prefetch_blocks needs the host-offload tier");
+  if (!std::isfinite(f.offload_min_score)) return bad("offload_min_score must be finite");
   if (f.diag_topk < 0) return bad("diag_topk must be >= 0");
   if (f.diag_topk > 0 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("diagnostics apply to the token policies only");
@@ -342,6 +343,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
       A(dalloc(&d.sowner, static_cast<size_t>(f.offload_blocks)));
       A(dalloc(&d.rd_slots, c->maxpages));
       A(dalloc(&d.ev_slot, Bs * c->maxpages));
+      A(dalloc(&d.oring, 2));
       // K and V pages of every layer and KV head per slot
       const size_t slot_bytes = 2ull * L * f.n_kv_heads * c->PT * D * c->elem;
       A(hipHostMalloc(&c->hpool, slot_bytes * f.offload_blocks, hipHostMallocDefault));
@@ -350,8 +352,8 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
         A(hipMalloc(&c->dstage, slot_bytes * f.prefetch_blocks));
         A(hipStreamCreateWithFlags(&c->pf_stream, hipStreamNonBlocking));
         A(hipEventCreateWithFlags(&c->pf_done, hipEventDisableTiming));
-        c->pf_of_slot.assign(f.offload_blocks, -1);
-        c->pf_slot.assign(f.prefetch_blocks, -1);
+        c->pf_key.assign(f.prefetch_blocks, -1);
+        c->pf_src.assign(f.prefetch_blocks, -1);
       }
     }
   }
@@ -403,6 +405,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
       A(hipMemsetAsync(d.sowner, 0xff, sizeof(int) * f.offload_blocks, c->stream));
       A(hipMemsetAsync(d.rd_slots, 0, sizeof(int) * c->maxpages, c->stream));
       A(hipMemsetAsync(d.ev_slot, 0xff, sizeof(int) * Bs * c->maxpages, c->stream));
+      A(hipMemsetAsync(d.oring, 0, sizeof(int) * 2, c->stream));
     }
     std::vector<int> stack(static_cast<size_t>(G) * c->maxpages), top(G, c->maxpages);
     for (int64_t g = 0; g < G; ++g)
@@ -592,22 +595,12 @@ static hipError_t offload_evicted(kvev_ctx* c, const std::vector<int>& ev) {
     kmax = std::max(kmax, k);
   }
   if (E == 0) return hipSuccess;
-  const int C = c->cfg.offload_blocks;
-  const int kept = std::min(C, E);
   if (c->pf_pending) {  // prefetch copies still read the slots about to be written
     if (hipError_t w = hipStreamWaitEvent(c->stream, c->pf_done, 0)) return w;
     c->pf_pending = false;
   }
-  if (!c->pf_of_slot.empty())
-    for (int i = 0; i < kept; ++i) {
-      const int s = static_cast<int>((c->ring + i) % C);
-      if (c->pf_of_slot[s] >= 0) c->pf_slot[c->pf_of_slot[s]] = -1;
-      c->pf_of_slot[s] = -1;
-    }
   ProfScope p(c, "offload");
-  const hipError_t e = launch_offload(c, kmax, E);
-  c->ring = (c->ring + kept) % C;
-  return e;
+  return launch_offload(c, kmax, E);
 }
 
 static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
@@ -955,20 +948,21 @@ kvev_status kvev_readmit_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const in
       return fail(c, KVEV_ESTATE, "block is not in the host pool");
     res[ids[i]] = 1;
     id32[i] = static_cast<int>(ids[i]);
-    // a prefetched copy in device staging, else the pool slot (encoded -1 - slot)
+    // a prefetched copy in device staging (valid while the block still owns
+    // the pool slot it was copied from), else the pool slot (encoded -1 - slot)
     const int s = slot[ids[i]];
-    const int st = c->pf_of_slot.empty() ? -1 : c->pf_of_slot[s];
+    const int key = static_cast<int>(seq * c->maxblk + ids[i]);
+    int st = -1;
+    for (int x = 0; x < static_cast<int>(c->pf_key.size()); ++x)
+      if (c->pf_key[x] == key && c->pf_src[x] == s) st = x;
     sl[i] = st >= 0 ? st : -1 - s;
   }
   if (c->pf_pending) {
     KVEV_HIP(c, hipStreamWaitEvent(c->stream, c->pf_done, 0));
     c->pf_pending = false;
   }
-  for (int64_t i = 0; i < n; ++i)  // consumed: the slots are released below
-    if (sl[i] >= 0) {
-      c->pf_of_slot[c->pf_slot[sl[i]]] = -1;
-      c->pf_slot[sl[i]] = -1;
-    }
+  for (int64_t i = 0; i < n; ++i)  // consumed
+    if (sl[i] >= 0) c->pf_key[sl[i]] = -1;
   const int e0 = c->nres[seq] - 1;
   KVEV_HIP(c, hipMemcpyAsync(c->d.rd_ids, id32.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
   KVEV_HIP(c, hipMemcpyAsync(c->d.rd_slots, sl.data(), sizeof(int) * n, hipMemcpyHostToDevice, c->stream));
@@ -1003,14 +997,17 @@ kvev_status kvev_prefetch_offloaded(kvev_ctx* c, int32_t seq, int64_t n, const i
   const size_t sb = 2ull * c->cfg.n_layers * c->cfg.n_kv_heads * c->PT * c->cfg.head_dim * c->elem;
   for (int64_t i = 0; i < n; ++i) {
     const int s = slot[ids[i]];
-    if (c->pf_of_slot[s] >= 0) continue;  // already staged
+    const int key = static_cast<int>(seq * c->maxblk + ids[i]);
+    bool staged = false;
+    for (int x = 0; x < static_cast<int>(c->pf_key.size()); ++x)
+      staged = staged || (c->pf_key[x] == key && c->pf_src[x] == s);
+    if (staged) continue;
     const int st = c->pf_next;
     c->pf_next = (c->pf_next + 1) % c->cfg.prefetch_blocks;
-    if (c->pf_slot[st] >= 0) c->pf_of_slot[c->pf_slot[st]] = -1;
     KVEV_HIP(c, hipMemcpyAsync(static_cast<char*>(c->dstage) + sb * st, static_cast<char*>(c->hpool) + sb * s, sb,
                                hipMemcpyHostToDevice, c->pf_stream));
-    c->pf_slot[st] = s;
-    c->pf_of_slot[s] = st;
+    c->pf_key[st] = key;
+    c->pf_src[st] = s;
   }
   KVEV_HIP(c, hipEventRecord(c->pf_done, c->pf_stream));
   c->pf_pending = true;

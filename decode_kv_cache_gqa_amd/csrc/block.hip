@@ -47,6 +47,8 @@ struct BlockArgs {
   int* ev_page;   // [G][maxpages] their pages, per KV head
   int* hslot;     // [batch][maxblk] host-pool slot holding an evicted block, or -1
   int* sowner;    // [offload_blocks] b * maxblk + block of each slot's block, or -1
+  int* oring;     // [2] next ring slot, and its value after this selection
+  float omin;     // evicted blocks scoring below omin are dropped, not offloaded
   int L, G, Hkv, Hq, HG, D, maxpages, maxblk, S, batch;
   int64_t cap, lstride;
   float alpha, beta, tau;
@@ -444,35 +446,56 @@ __global__ void blk_readmit_kernel(BlockArgs A, int b, int n, const int* __restr
 // eviction).  After a selection, every evicted block's pages (each layer and
 // KV head, K and V as stored) are copied into a slot of a pinned host pool
 // of C slots, written by the kernel through its device mapping.  Order: the
-// step's evictions are ranked by (sequence, block id); with E of them, the
-// last min(C, E) take consecutive ring slots from `ring` and the rest are
-// dropped.  A slot's previous block loses its copy.
+// step's evictions whose persisted score is at least omin are offloaded,
+// the others dropped; the offloaded ones are ranked by (sequence, block id)
+// and, with E of them, the last min(C, E) take consecutive ring slots from
+// oring[0] (the rest are dropped).  A slot's previous block loses its copy.
 // offload_slot_kernel: one block per sequence ranks its evictions, assigns
 // the slots and updates the slot tables; offload_copy_kernel: one block per
 // (evicted block, layer) copies that layer's pages.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void offload_slot_kernel(BlockArgs A, int* __restrict__ ev_slot, int C,
-                                                           int ring, int e_host) {
+                                                           int e_host) {
+  __shared__ int red[256 / kWave];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int kb = A.ev_n[b];
   const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
-  // the step's evictions before this sequence's, and in all
-  int off = 0, E = 0;
+  auto eligible = [&](int i, int j) {  // j-th eviction of sequence i is offloaded
+    const int64_t r = static_cast<int64_t>(i) * A.maxpages + j;
+    return A.bscore[static_cast<int64_t>(i) * A.maxblk + A.ev_blk[r]] >= A.omin;
+  };
+  // the step's evictions (a consistency check), and the offloaded ones
+  // before this sequence's and in all
+  int all = 0, off = 0, E = 0;
   for (int i = 0; i < A.batch; ++i) {
     const int k = A.ev_n[i];
-    off += i < b ? k : 0;
-    E += k;
+    all += k;
+    int e = 0;
+    for (int j = tid; j < k; j += 256) e += eligible(i, j) ? 1 : 0;
+    e = wave_sum_int(e);
+    __syncthreads();
+    if (tid % kWave == 0) red[tid / kWave] = e;
+    __syncthreads();
+    e = red[0] + red[1] + red[2] + red[3];
+    off += i < b ? e : 0;
+    E += e;
   }
   const int kept = E < C ? E : C;
+  const int ring = A.oring[0];
+  if (b == 0 && tid == 0) A.oring[1] = (ring + kept) % C;  // committed by the copy kernel
   for (int j = tid; j < kb; j += 256) {
-    if (E != e_host) {  // the host's count sizes the ring: never disagree silently
+    if (all != e_host) {  // the host's count sizes the launch: never disagree silently
       ev_slot[brow + j] = -1;
       atomicOr(A.errflag, 128);
       continue;
     }
+    if (!eligible(b, j)) {
+      ev_slot[brow + j] = -1;
+      continue;
+    }
     const int blk = A.ev_blk[brow + j];
-    int r = 0;  // rank of the block id among the sequence's evictions
-    for (int i = 0; i < kb; ++i) r += A.ev_blk[brow + i] < blk ? 1 : 0;
+    int r = 0;  // rank of the block id among the sequence's offloaded evictions
+    for (int i = 0; i < kb; ++i) r += (A.ev_blk[brow + i] < blk && eligible(b, i)) ? 1 : 0;
     const int gidx = off + r - (E - kept);  // index among the offloaded ones
     if (gidx < 0) {                         // dropped: a later eviction of this step takes its slot
       ev_slot[brow + j] = -1;
@@ -495,6 +518,7 @@ __global__ __launch_bounds__(256) void offload_copy_kernel(BlockArgs A, const in
                                                            const uint4* __restrict__ vpool, int64_t page_vec,
                                                            int64_t P) {
   const int j = blockIdx.x, b = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
+  if (j == 0 && b == 0 && l == 0 && tid == 0) A.oring[0] = A.oring[1];  // the slot kernel has read oring[0]
   if (j >= A.ev_n[b]) return;
   const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
   const int slot = ev_slot[brow + j];
@@ -567,6 +591,8 @@ static BlockArgs block_args(kvev_ctx* c, float* out, int n_max) {
   A.ev_page = c->d.ev_page;
   A.hslot = c->d.hslot;
   A.sowner = c->d.sowner;
+  A.oring = c->d.oring;
+  A.omin = cf.offload_min_score;
   A.L = cf.n_layers;
   A.G = c->G;
   A.Hkv = cf.n_kv_heads;
@@ -625,8 +651,7 @@ hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, in
 hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host) {
   BlockArgs A = block_args(c, nullptr, 1);
   const int64_t page_vec = static_cast<int64_t>(c->PT) * c->cfg.head_dim * c->elem / 16;
-  offload_slot_kernel<<<c->cfg.batch, 256, 0, c->stream>>>(A, c->d.ev_slot, c->cfg.offload_blocks,
-                                                           static_cast<int>(c->ring), e_host);
+  offload_slot_kernel<<<c->cfg.batch, 256, 0, c->stream>>>(A, c->d.ev_slot, c->cfg.offload_blocks, e_host);
   dim3 grid(k_max, c->cfg.batch, c->cfg.n_layers);
   offload_copy_kernel<<<grid, 256, 0, c->stream>>>(A, c->d.ev_slot, static_cast<uint4*>(c->hpool_dev),
                                                    static_cast<const uint4*>(c->d.kpool),

@@ -75,6 +75,7 @@ struct DevState {
   int* sowner = nullptr;    // [offload_blocks] owner b * maxblk + block, or -1
   int* rd_slots = nullptr;  // [maxpages] slots of a re-admission
   int* ev_slot = nullptr;   // [batch][maxpages] pool slot of each evicted block, or -1 (dropped)
+  int* oring = nullptr;     // [2] the pool's next ring slot, and its value after the current selection
   // block-granular mode
   int* btab = nullptr;      // [batch][maxpages] logical block of each table entry
   int* nres = nullptr;      // [batch] table entries (resident blocks)
@@ -182,14 +183,13 @@ struct kvev_ctx {
   std::vector<int64_t> seq_next;            // per sequence: the next position (token modes)
   void* hpool = nullptr;                    // pinned host pool of the offload tier
   void* hpool_dev = nullptr;                // its device mapping
-  int64_t ring = 0;                         // next offload slot (mod offload_blocks)
   // background prefetch of pool blocks into device staging
   hipStream_t pf_stream = nullptr;          // the copies' stream (default priority)
   hipEvent_t pf_done = nullptr;             // recorded after each batch of copies
   bool pf_pending = false;                  // the context's stream has not waited for pf_done yet
   void* dstage = nullptr;                   // [prefetch_blocks] device copies of pool slots
-  std::vector<int> pf_of_slot;              // pool slot -> staging slot, or -1
-  std::vector<int> pf_slot;                 // staging slot -> pool slot, or -1
+  std::vector<int> pf_key;                  // staging slot -> block key b * maxblk + block, or -1
+  std::vector<int> pf_src;                  // staging slot -> the pool slot it was copied from
   int pf_next = 0;                          // next staging slot
   std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
   std::vector<int> free_pages;

@@ -54,6 +54,7 @@ class Config(ctypes.Structure):
         ("offload_blocks", ctypes.c_int32),
         ("revival_gap", ctypes.c_int32),
         ("prefetch_blocks", ctypes.c_int32),
+        ("offload_min_score", ctypes.c_float),
     ]
 
 
@@ -459,7 +460,7 @@ def tier_capacities(b_hist, q, m_f, m_q):
 
 
 def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None,
-                revival_gap=None, prefetch_blocks=0):
+                revival_gap=None, prefetch_blocks=0, offload_min_score=0.0):
     """A context configured for a synth.Workload (diag_topk: rank-trace
     diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
@@ -472,7 +473,7 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             if budget is None else budget, beta=w.beta,
             pinned_region_mask=sum(1 << r for r in w.pinned_regions), decode_region=w.decode_region,
             access_tau_mult=2.0, offload_blocks=w.offload_blocks if offload_blocks is None else offload_blocks,
-            prefetch_blocks=prefetch_blocks)
+            prefetch_blocks=prefetch_blocks, offload_min_score=offload_min_score)
         for r, hl in enumerate(w.region_half_lives):
             cfg.region_half_life[r] = hl
         return Context(cfg, stream=stream)

@@ -195,6 +195,11 @@ typedef struct {
   /* KVEV_LRFU_BLOCK with offload_blocks > 0: device staging slots for
    * kvev_prefetch_offloaded (0: no prefetch). */
   int32_t prefetch_blocks;
+  /* KVEV_LRFU_BLOCK with offload_blocks > 0: an evicted block whose
+   * persisted score is below this value is dropped instead of offloaded
+   * (the graded offload / drop rule of "MemDecay" section III-E; 0: every
+   * evicted block is offloaded). */
+  float offload_min_score;
 } kvev_config;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,

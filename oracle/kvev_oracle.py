@@ -1142,7 +1142,9 @@ class HostOffloadPool:
     within one selection the evicted blocks are ordered by (sequence, block
     id) and, when there are more than ``capacity`` of them, only the last
     ``capacity`` are kept; a re-admitted block's slot is released (a
-    resident block holds no slot).
+    resident block holds no slot).  The graded rule of [MemDecay] §III-E
+    (offload above a threshold, drop below it) is the caller's filter:
+    ``offload`` receives only the evictions to keep.
     """
 
     def __init__(self, capacity):

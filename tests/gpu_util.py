@@ -615,7 +615,8 @@ def run_block_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda", 
 # Host-offload tier of the block mode
 # ---------------------------------------------------------------------------
 
-def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cuda", prefetch=0):
+def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cuda", prefetch=0,
+                      min_score=0.0):
     """Two block contexts on the same inputs: `plain` (no pool) re-admits each
     epoch's heavy blocks with K/V regenerated from the seed, `off` (a host
     pool of `capacity` blocks) re-admits the same blocks from its pool.  Every
@@ -625,7 +626,9 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     evictions.  Blocks no longer in the pool are refused by the offload
     re-admission and skipped by both.  prefetch > 0: `off` has that many
     device staging slots and, one step before each epoch starts, prefetches
-    the heavy blocks it will re-admit (restored from the staged copies)."""
+    the heavy blocks it will re-admit (restored from the staged copies).
+    min_score: evicted blocks scoring below it (the library's fp32 scores,
+    compared in fp32) are dropped instead of offloaded."""
     import pytest
     import torch
     from decode_kv_cache_gqa_amd import kvev
@@ -633,7 +636,8 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     log(f"[offload] {w.name}: L={w.n_layers} batch={w.batch} L0={w.prefill_lens[:6]} steps={steps} "
         f"capacity={capacity} fused={fused}")
     ctxs = [kvev.context_for(w, max_steps=steps, offload_blocks=0),
-            kvev.context_for(w, max_steps=steps, offload_blocks=capacity, prefetch_blocks=prefetch)]
+            kvev.context_for(w, max_steps=steps, offload_blocks=capacity, prefetch_blocks=prefetch,
+                             offload_min_score=min_score)]
     plain, off = ctxs
     pool = orc.HostOffloadPool(capacity)
     for b in range(w.batch):
@@ -646,7 +650,8 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
     torch.cuda.synchronize()
     outs = [torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device=device)
             for _ in ctxs]
-    stats = {"readmitted": 0, "refused": 0, "offloaded": 0, "dropped": 0, "prefetched": 0}
+    stats = {"readmitted": 0, "refused": 0, "offloaded": 0, "dropped": 0, "prefetched": 0,
+             "below_threshold": 0}
 
     def resident(c, b):
         return np.asarray(c.block_state(b)[2], dtype=bool)
@@ -701,7 +706,11 @@ def run_offload_twins(w, steps, capacity, *, fused=True, kv_every=4, device="cud
             now = np.asarray(sp[2], dtype=bool)
             was = np.zeros_like(now)
             was[:len(before[b])] = before[b]
-            evicted += [(b, int(j)) for j in np.flatnonzero(was & ~now)]
+            for j in np.flatnonzero(was & ~now):
+                if np.float32(so[0][j]) >= np.float32(min_score):
+                    evicted.append((b, int(j)))
+                else:
+                    stats["below_threshold"] += 1
         pool.offload(evicted)
         stats["offloaded"] += min(capacity, len(evicted))
         stats["dropped"] += max(0, len(evicted) - capacity)

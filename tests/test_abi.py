@@ -107,6 +107,7 @@ def _create(**kw):
     (dict(offload_blocks=-1), "offload_blocks"),
     (dict(revival_gap=-1), "revival_gap"),
     (dict(prefetch_blocks=-1), "prefetch_blocks"),
+    (dict(policy=kvev.LRFU_BLOCK, offload_blocks=4, offload_min_score=float("nan")), "offload_min_score"),
     (dict(policy=kvev.LRFU_BLOCK, prefetch_blocks=4), "needs the host-offload tier"),
     (dict(revival_gap=4), "tiered mode only"),
     (dict(offload_blocks=8), "block mode only"),

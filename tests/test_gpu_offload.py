@@ -51,6 +51,17 @@ def test_offload_with_background_prefetch():
     assert st["prefetched"] > 0
 
 
+@pytest.mark.parametrize("min_score", [0.01, 1e9])
+def test_offload_score_threshold(min_score):
+    """The graded rule: evicted blocks scoring below the threshold are
+    dropped, the rest offloaded (1e9: nothing reaches the pool, every
+    recovery is refused); the pool still matches the oracle's model."""
+    st = _gu().run_offload_twins(_scaled(), 40, 64, min_score=min_score, prefetch=8)
+    assert st["below_threshold"] > 0
+    if min_score > 1e8:
+        assert st["offloaded"] == 0 and st["readmitted"] == 0
+
+
 def test_offload_separate_calls_fp32():
     """kvev_decode_step + kvev_evict (the standalone selection offloads too),
     fp32, d = 64, one layer."""

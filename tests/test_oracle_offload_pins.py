@@ -61,3 +61,13 @@ def test_pool_holds_the_latest_evictions_not_readmitted():
         latest = log[-C:]
         want = {k for i, k in enumerate(latest) if k not in resident and k not in latest[i + 1:]}
         assert set(p.where) == want, step
+
+
+def test_dropped_evictions_do_not_advance_the_ring():
+    """Evictions below the score threshold are dropped before the pool sees
+    them: the ring advances only by the offloaded ones."""
+    p = orc.HostOffloadPool(4)
+    scores = {(0, 1): 0.5, (0, 2): 0.01, (1, 5): 0.3, (1, 6): 0.002}
+    keep = [k for k, v in scores.items() if v >= 0.1]
+    p.offload(keep)
+    assert p.where == {(0, 1): 0, (1, 5): 1} and p.ring == 2
