@@ -456,7 +456,6 @@ __global__ void blk_readmit_kernel(BlockArgs A, int b, int n, const int* __restr
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void offload_slot_kernel(BlockArgs A, int* __restrict__ ev_slot, int C,
                                                            int e_host) {
-  __shared__ int red[256 / kWave];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int kb = A.ev_n[b];
   const int64_t brow = static_cast<int64_t>(b) * A.maxpages;
@@ -465,20 +464,28 @@ __global__ __launch_bounds__(256) void offload_slot_kernel(BlockArgs A, int* __r
     return A.bscore[static_cast<int64_t>(i) * A.maxblk + A.ev_blk[r]] >= A.omin;
   };
   // the step's evictions (a consistency check), and the offloaded ones
-  // before this sequence's and in all
+  // before this sequence's and in all: each thread counts whole sequences
   int all = 0, off = 0, E = 0;
-  for (int i = 0; i < A.batch; ++i) {
+  for (int i = tid; i < A.batch; i += 256) {
     const int k = A.ev_n[i];
-    all += k;
     int e = 0;
-    for (int j = tid; j < k; j += 256) e += eligible(i, j) ? 1 : 0;
-    e = wave_sum_int(e);
-    __syncthreads();
-    if (tid % kWave == 0) red[tid / kWave] = e;
-    __syncthreads();
-    e = red[0] + red[1] + red[2] + red[3];
+    for (int j = 0; j < k; ++j) e += eligible(i, j) ? 1 : 0;
+    all += k;
     off += i < b ? e : 0;
     E += e;
+  }
+  {
+    int v[3] = {all, off, E};
+#pragma unroll
+    for (int x = 0; x < 3; ++x) v[x] = wave_sum_int(v[x]);
+    __shared__ int red3[3][256 / kWave];
+    if (tid % kWave == 0)
+#pragma unroll
+      for (int x = 0; x < 3; ++x) red3[x][tid / kWave] = v[x];
+    __syncthreads();
+    all = red3[0][0] + red3[0][1] + red3[0][2] + red3[0][3];
+    off = red3[1][0] + red3[1][1] + red3[1][2] + red3[1][3];
+    E = red3[2][0] + red3[2][1] + red3[2][2] + red3[2][3];
   }
   const int kept = E < C ? E : C;
   const int ring = A.oring[0];
