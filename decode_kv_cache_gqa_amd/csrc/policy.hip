@@ -59,7 +59,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   const int newest = A.nextpos[g];
   const int ns = (n + A.CT - 1) / A.CT;
   const int Bsz = A.G / A.Hkv, b = g / A.Hkv, kvh = g % A.Hkv;
-  const int tbase = c * kPostTok;
+  // slots per slot block: kPostTok on an observation step (the fold stages
+  // every layer's mass of its slots in LDS), one per thread otherwise
+  const int spb = A.refresh ? kPostTok : NT;
+  const int tbase = c * spb;
   int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
   float* gs = A.score + static_cast<int64_t>(g) * A.cap;
   auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
@@ -68,7 +71,8 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 
   // ---- issue every load of the block ---------------------------------------
   const int tl = tid % kPostTok, lg = tid / kPostTok;
-  const int t = tbase + tl;
+  const int t = A.refresh ? tbase + tl : tbase + tid;
+  const bool holder = A.refresh ? tid < kPostTok : true;  // the thread summarises slot t
   const bool fold = !outb && A.refresh && tbase < n;
   float sx[8][HG];
   float vx[8];
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
   float prior = 0.f;
   int mypos = 0;
-  if (!outb && tid < kPostTok && t < n && t != hn) {
+  if (!outb && holder && t < n && t != hn) {
     prior = gs[t];
     mypos = gp[t];
   }
@@ -246,7 +250,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   }
 
   // ---- block summary over slots other than the new token's -------------------
-  if (tid < kPostTok) {
+  unsigned long long skey = ~0ull;
+  int sslot = -1;
+  float ssum = 0.f;
+  if (holder) {
     const bool mine = t < n && t != hn;
     unsigned long long key = ~0ull;
     int slot = -1;
@@ -265,12 +272,32 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       }
     }
     sum = wave_sum(sum);
-    if (tid == 0) {
-      const int64_t bi = static_cast<int64_t>(g) * A.max_blk + c;
-      st_coherent(A.blk_key + bi, key);
-      st_coherent(A.blk_slot + bi, slot);
-      st_coherent(A.blk_sum + bi, sum);
+    skey = key;
+    sslot = slot;
+    ssum = sum;
+  }
+  if (!A.refresh) {  // the block's slots span every wave: combine them
+    if (lane == 0) {
+      s_key[tid / kWave] = skey;
+      s_slot[tid / kWave] = sslot;
+      red[tid / kWave] = ssum;
     }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < NT / kWave; ++w) {
+        ssum += red[w];
+        if (s_key[w] < skey) {
+          skey = s_key[w];
+          sslot = s_slot[w];
+        }
+      }
+    }
+  }
+  if (tid == 0) {
+    const int64_t bi = static_cast<int64_t>(g) * A.max_blk + c;
+    st_coherent(A.blk_key + bi, skey);
+    st_coherent(A.blk_slot + bi, sslot);
+    st_coherent(A.blk_sum + bi, ssum);
   }
 
   // ---- arrival ----------------------------------------------------------------------
@@ -620,7 +647,8 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.B = static_cast<int>(budget);
   A.n_sink = cf.n_sink;
   A.n_recent = cf.n_recent;
-  const int tok_blocks = (n_max + kPostTok - 1) / kPostTok;
+  const int spb = refresh ? kPostTok : NT;  // slots per slot block (see post_kernel)
+  const int tok_blocks = (n_max + spb - 1) / spb;
   if (c->pooled) {
     // one grid row per sequence: the slot blocks, then one block per (layer, KV head) output
     A.nblk = (n_max + kPoolTokens - 1) / kPoolTokens;
