@@ -52,7 +52,7 @@ void free_all(kvev_ctx* c) {
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
                   d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole, d.dg_n, d.dg_pos, d.dg_raw,
                   d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc,
-                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot, d.oring};
+                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot, d.oring, d.bpart};
   for (void* p : ptrs)
     if (p) hipFree(p);
   if (c->hpool) hipHostFree(c->hpool);
@@ -329,6 +329,9 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     A(dalloc(&d.bscore, Bs * c->maxblk));
     A(dalloc(&d.btref, Bs * c->maxblk));
     A(dalloc(&d.bres, Bs * c->maxblk));
+    // the matrix-core attention writes per-block sums instead of per-slot logits
+    if (f.dtype == KVEV_BF16 && f.head_dim == 128)
+      A(dalloc(&d.bpart, static_cast<size_t>(L) * G * c->maxpages * HG));
     A(dalloc(&d.bcnt, Bs * c->maxblk * kRegions));
     A(dalloc(&d.fstack, static_cast<size_t>(G) * c->maxpages));
     A(dalloc(&d.ftop, G));

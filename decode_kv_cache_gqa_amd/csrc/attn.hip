@@ -68,9 +68,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     const int* __restrict__ ptab, const int* __restrict__ count, const int* __restrict__ hole,
     float* __restrict__ logits, float* __restrict__ part_ml, float* __restrict__ part_o,
     float* __restrict__ part_u, float* __restrict__ vnorm, float* __restrict__ part_vn, int L, int G,
-    int Hkv, int Hq, int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits) {
+    int Hkv, int Hq, int64_t P, int maxpages, int64_t lstride, int S, float scale, int write_logits,
+    float* __restrict__ bpart) {
   static_assert(HG >= 1 && HG <= 8, "group size");
   constexpr int D = 128, NG = 4, WT = NG * 16;
+  // bpart (16-token block mode): instead of per-slot logits, the sum over
+  // each 16-slot block of exp(s - M_split) per head, [L][G][maxpages][HG]
+  __shared__ float bsum[NW][NG][HG];
   __shared__ __align__(16) float p_lds[NW][HG][WT];
   __shared__ __align__(16) float wstat[NW][HG][2];
   __shared__ float wstat_u[SC ? NW : 1][HG];
@@ -242,6 +246,15 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
     lh[i] = row16_sum(sum);
     uh[i] = ent ? row16_sum(u) : 0.f;
   }
+  if (bpart) {  // per-block sums relative to the wave's maximum (uniform branch)
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bs = row16_sum(sv[j][i]);
+        if (r16 == 0 && h0 + i < HG) bsum[wave][j][h0 + i] = bs;
+      }
+  }
   if (h0 < HG) {
 #pragma unroll
     for (int j = 0; j < NG; ++j)
@@ -326,6 +339,19 @@ __global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(
 #pragma unroll
     for (int w = 0; w < NW; ++w) t += wvn[w];
     part_vn[pbase] = t;
+  }
+  if (bpart) {  // rescale each block's sum to the split's maximum
+    for (int idx = tid; idx < NW * NG * HG; idx += NW * kWave) {
+      const int w = idx / (NG * HG), j = (idx / HG) % NG, h = idx % HG;
+      float M = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) M = fmaxf(M, wstat[x][h][0]);
+      const float mw = wstat[w][h][0];
+      const int e = split * (NW * NG) + w * NG + j;  // the block's table entry
+      if (16 * e < n)
+        bpart[((static_cast<int64_t>(l) * G + g) * maxpages + e) * HG + h] =
+            mw == -INFINITY ? 0.f : __expf(mw - M) * bsum[w][j][h];
+    }
   }
 }
 
@@ -600,13 +626,14 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
       float* pu = write_logits ? c->d.part_u : nullptr;
       float* vn = write_logits ? c->d.vnorm : nullptr;
       float* pvn = write_logits ? c->d.part_vn : nullptr;
+      float* bp = write_logits ? c->d.bpart : nullptr;  // block mode: block sums instead of logits
       auto launch = [&](auto kern) {
         kern<<<grid, kMfmaNW * kWave, 0, c->stream>>>(
             static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
             static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
             static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.hole, c->d.logits, c->d.part_ml,
             c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
-            c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f), write_logits);
+            c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f), bp ? 0 : write_logits, bp);
       };
       if (pu || vn)
         launch(attn_mfma_kernel<kMfmaNW, HG, true>);

@@ -225,6 +225,37 @@ __global__ __launch_bounds__(kMassNT) void blk_mass_kernel(BlockArgs A) {
   }
 }
 
+// Mass of each table entry from the attention's per-block sums (matrix-core
+// path): sum over (layer, KV head, head) of bpart * exp(m_split - M) / Z,
+// m_split the maximum of the entry's split (256 slots = 16 entries), M and
+// Z the merged statistics.  One wave per entry, four entries per block.
+__global__ __launch_bounds__(256) void blk_mass_part_kernel(BlockArgs A, const float* __restrict__ bpart) {
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
+  const int g0 = b * A.Hkv;
+  const int e = blockIdx.x * 4 + tid / kWave;
+  const int nres = A.nres[b];
+  float acc = 0.f;
+  if (e < nres) {
+    const int split = e / (kAttnChunk / kPageTokens);
+    const int np = A.L * A.Hkv;
+    for (int i = lane; i < np; i += kWave) {
+      const int l = i / A.Hkv, h = i % A.Hkv;
+      const int64_t lg = static_cast<int64_t>(l) * A.G + g0 + h;
+      const float4 x = *reinterpret_cast<const float4*>(bpart + (lg * A.maxpages + e) * 4);
+      const float* ml = A.ml + lg * 8;                                  // [4 heads][M, Z]
+      const float* pm = A.part_ml + (lg * A.S + split) * 8;            // the split's [4][m, l]
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const float ms = pm[2 * hh];
+        if (ms != -INFINITY) acc += xs[hh] * __expf(ms - ml[2 * hh]) / ml[2 * hh + 1];
+      }
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0 && e < nres) A.bmass[static_cast<int64_t>(b) * A.maxpages + e] = acc;
+}
+
 // Exclusive prefix sum of one int per thread over the block (NT threads).
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
@@ -639,6 +670,11 @@ hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max) {
 
 hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
   BlockArgs A = block_args(c, nullptr, n_max);
+  if (c->d.bpart) {  // the attention wrote per-block sums
+    dim3 grid((n_max + 4 * kPageTokens - 1) / (4 * kPageTokens), c->cfg.batch);
+    blk_mass_part_kernel<<<grid, 256, 0, c->stream>>>(A, c->d.bpart);
+    return hipGetLastError();
+  }
   dim3 grid((n_max + 63) / 64, c->cfg.batch);
   const size_t shm = (static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 8 + 256) * sizeof(float);
   blk_mass_kernel<<<grid, kMassNT, shm, c->stream>>>(A);

@@ -82,6 +82,7 @@ struct DevState {
   float* bscore = nullptr;  // [batch][maxblk] score of every logical block (kept when evicted)
   int* btref = nullptr;     // [batch][maxblk] step of the last access / insertion
   int* bres = nullptr;      // [batch][maxblk] 1 while resident
+  float* bpart = nullptr;   // [L][G][maxpages][HG] per-block sums of exp(s - M_split) (matrix-core path)
   uint8_t* bcnt = nullptr;  // [batch][maxblk][kRegions] tokens of each region in the block
   int* fstack = nullptr;    // [G][maxpages] free pages of each group
   int* ftop = nullptr;      // [G] free pages on the stack
