@@ -230,26 +230,34 @@ __global__ __launch_bounds__(kMassNT) void blk_mass_kernel(BlockArgs A) {
 // m_split the maximum of the entry's split (256 slots = 16 entries), M and
 // Z the merged statistics.  One wave per entry, four entries per block.
 __global__ __launch_bounds__(256) void blk_mass_part_kernel(BlockArgs A, const float* __restrict__ bpart) {
+  extern __shared__ float fac[];  // [L * Hkv][4] exp(m_split - M) / Z of the block's split
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
   const int g0 = b * A.Hkv;
-  const int e = blockIdx.x * 4 + tid / kWave;
+  const int e0 = blockIdx.x * 4, e = e0 + tid / kWave;
   const int nres = A.nres[b];
+  if (e0 >= nres) return;
+  const int split = e0 / (kAttnChunk / kPageTokens);  // the block's 4 entries share it
+  const int np = A.L * A.Hkv;
+  for (int i = tid; i < np; i += 256) {
+    const int l = i / A.Hkv, h = i % A.Hkv;
+    const int64_t lg = static_cast<int64_t>(l) * A.G + g0 + h;
+    const float* ml = A.ml + lg * 8;                        // [4 heads][M, Z]
+    const float* pm = A.part_ml + (lg * A.S + split) * 8;   // the split's [4][m, l]
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float ms = pm[2 * hh];
+      fac[i * 4 + hh] = ms == -INFINITY ? 0.f : __expf(ms - ml[2 * hh]) / ml[2 * hh + 1];
+    }
+  }
+  __syncthreads();
   float acc = 0.f;
   if (e < nres) {
-    const int split = e / (kAttnChunk / kPageTokens);
-    const int np = A.L * A.Hkv;
     for (int i = lane; i < np; i += kWave) {
       const int l = i / A.Hkv, h = i % A.Hkv;
       const int64_t lg = static_cast<int64_t>(l) * A.G + g0 + h;
       const float4 x = *reinterpret_cast<const float4*>(bpart + (lg * A.maxpages + e) * 4);
-      const float* ml = A.ml + lg * 8;                                  // [4 heads][M, Z]
-      const float* pm = A.part_ml + (lg * A.S + split) * 8;            // the split's [4][m, l]
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float ms = pm[2 * hh];
-        if (ms != -INFINITY) acc += xs[hh] * __expf(ms - ml[2 * hh]) / ml[2 * hh + 1];
-      }
+      const float4 f = *reinterpret_cast<const float4*>(&fac[i * 4]);
+      acc += x.x * f.x + x.y * f.y + x.z * f.z + x.w * f.w;
     }
   }
   acc = wave_sum(acc);
@@ -672,7 +680,8 @@ hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
   BlockArgs A = block_args(c, nullptr, n_max);
   if (c->d.bpart) {  // the attention wrote per-block sums
     dim3 grid((n_max + 4 * kPageTokens - 1) / (4 * kPageTokens), c->cfg.batch);
-    blk_mass_part_kernel<<<grid, 256, 0, c->stream>>>(A, c->d.bpart);
+    const size_t shm = static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 4 * sizeof(float);
+    blk_mass_part_kernel<<<grid, 256, shm, c->stream>>>(A, c->d.bpart);
     return hipGetLastError();
   }
   dim3 grid((n_max + 63) / 64, c->cfg.batch);
