@@ -3,8 +3,10 @@
 Workload: Llama-3.1-8B-shaped attention (32 layers, 32 query heads over 8 KV
 heads, head dim 128, bf16, batch 1), 32,768-token prefill, EMA alpha 0.05
 folded layer by layer, budget 3,277 tokens per KV head with 4 sinks and 32
-recent tokens protected.  One step = kvev_step: append + split attention over all layers, then
-split merge + probability pass + layer fold + radix select + compaction.  W warm-up steps (the first one evicts the
+recent tokens protected.  One step = kvev_step: append + attention over all
+layers (the whole-cache kernel: one workgroup per (KV head, layer), writing
+the outputs and each slot's group mass), then layer fold + selection +
+compaction.  W warm-up steps (the first one evicts the
 prefill down to the budget) run untimed, then exactly K steps are timed
 between two device synchronisations; inputs are resident in HBM before the
 timed region.
@@ -27,18 +29,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-# Every PROF_EVERY-th timed step is bracketed by HIP events on the library's
-# stream (the per-kernel averages and the roofline come from those launches).
-# An event record costs about 3.7 us of GPU time, so profiling every step
-# would inflate the step time by about 12% on the 32k workload.
-PROF_EVERY = 7  # coprime with the tiered routing interval 8, so routing steps are sampled too
+# Every PROF_EVERY-th timed step is profiled (the per-kernel averages and the
+# roofline come from those launches).  The token path's attention and post
+# launches record their own dispatch start and end into HIP events
+# (hipExtLaunchKernelGGL); the other kernels are bracketed by event records,
+# each costing about 3.7 us of GPU time.  Sampling keeps the step time within
+# about 0.5% of an unprofiled run on the 32k workload.
+PROF_EVERY = 15  # coprime with the tiered routing interval 8, so routing steps are sampled too
 
 
-def timed_steps(ctx, inputs, out, first, total):
+def timed_steps(ctx, inputs, out, first, total, prof_every=None):
     """Run steps first..total-1 between two device synchronisations, with
-    HIP-event profiling of every PROF_EVERY-th step.  Returns (seconds,
-    profiled steps)."""
+    HIP-event profiling of every prof_every-th step (default PROF_EVERY).
+    Returns (seconds, profiled steps)."""
     import torch
+    prof_every = prof_every or PROF_EVERY
     ctx.sync()
     ctx.profile(False)
     ctx.profile_reset()
@@ -46,7 +51,7 @@ def timed_steps(ctx, inputs, out, first, total):
     n_prof = 0
     t0 = time.perf_counter()
     for i, t in enumerate(range(first, total)):
-        sample = i % PROF_EVERY == 0
+        sample = i % prof_every == 0
         if sample:
             ctx.profile(True)
             n_prof += 1
@@ -81,8 +86,8 @@ def algorithmic_bytes(w, n_tokens):
 CSRC = os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_kernel_traffic_llama8b_32k.md")
 ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "common.h")]
-TIER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tier_attn_kernel_traffic_qevict131k.md")
-TIER_SOURCES = [os.path.join(CSRC, f) for f in ("tier.hip", "common.h")]
+SEQ_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_seq_kernel_traffic_llama8b_32k.md")
+SEQ_SOURCES = [os.path.join(CSRC, f) for f in ("attn_seq.hip", "common.h")]
 
 
 def measured_traffic(profile=TRAFFIC_PROFILE, sources=ATTN_SOURCES):
@@ -242,7 +247,7 @@ def run_block(args, w):
     torch.cuda.synchronize()
     for t in range(args.warmup):
         ctx.step(*inputs[t], out)
-    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total)
+    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
     names = ("open", "attn", "merge", "mass", "policy", "offload")
     prof = {k: ctx.profile_read(k) for k in names}
     # resident tokens read by a steady step: every resident block is full
@@ -303,7 +308,7 @@ def run_tier(args, w):
     torch.cuda.synchronize()
     for t in range(args.warmup):
         ctx.step(*inputs[t], out)
-    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total)
+    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
     prof = {k: ctx.profile_read(k) for k in ("append", "attn", "merge", "route")}
     _, tiers, _ = ctx.tier_state(0)
     npos = w.prefill_lens[0] + total
@@ -352,6 +357,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--prof-every", type=int, default=PROF_EVERY,
+                    help="profile every N-th timed step (HIP events around its launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -392,8 +399,8 @@ def main():
 
     for t in range(args.warmup):
         ctx.step(*inputs[t], out)
-    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total)
-    prof = {k: ctx.profile_read(k) for k in ("attn", "post", "move", "diag")}
+    dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
+    prof = {k: ctx.profile_read(k) for k in ("attn", "attn_whole", "post", "move", "diag")}
     diag = None
     if w.diag_topk > 0:
         import numpy as np
@@ -410,9 +417,15 @@ def main():
 
     n_tok = w.budget + 1
     kv_bytes, step_bytes = algorithmic_bytes(w, n_tok)
+    # the library names the attention launches by kernel: "attn_whole" for
+    # the whole-cache kernel, "attn" for the split kernel
+    whole = prof["attn_whole"][1] > 0
+    assert not (whole and prof["attn"][1] > 0), "both attention kernels ran in the timed steps"
+    attn_kernel = ("attn_seq_kernel" if whole else "attn_mfma_kernel") if w.dtype == "bf16" and w.head_dim == 128 \
+        else "attn_valu_kernel"
     ms_step = dt * 1e3 / args.steps
     steps_s = args.steps / dt
-    attn_ms, attn_n = prof["attn"]
+    attn_ms, attn_n = prof["attn_whole" if whole else "attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
     policy_ms = sum(prof[k][0] for k in ("post", "move", "diag")) / n_prof
@@ -446,8 +459,9 @@ def main():
             "unit": "GB/s",
             "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
             # the committed counters were taken on the 32k workload only
-            "traffic": measured_traffic() if args.workload == "llama8b_32k" else None,
-            "kernel": "attn_mfma_kernel" if w.dtype == "bf16" and w.head_dim == 128 else "attn_valu_kernel",
+            "traffic": (measured_traffic(*((SEQ_TRAFFIC_PROFILE, SEQ_SOURCES) if whole else ()))
+                        if args.workload == "llama8b_32k" else None),
+            "kernel": attn_kernel,
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }

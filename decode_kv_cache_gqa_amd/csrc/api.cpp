@@ -52,7 +52,8 @@ void free_all(kvev_ctx* c) {
                   d.bscore, d.btref, d.bres, d.bcnt, d.fstack, d.ftop, d.bmass, d.bbudget,
                   d.rd_ids, d.part_u, d.vnorm, d.part_vn, d.hole, d.dg_n, d.dg_pos, d.dg_raw,
                   d.dg_util, d.st_raw, d.st_util, d.st_kept, d.ev_step, d.dprev, d.dcnt, d.dacc,
-                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot, d.oring, d.bpart};
+                  d.ev_n, d.ev_blk, d.ev_page, d.hslot, d.sowner, d.rd_slots, d.ev_slot, d.oring, d.bpart,
+                  d.gnew};
   for (void* p : ptrs)
     if (p) hipFree(p);
   if (c->hpool) hipHostFree(c->hpool);
@@ -68,28 +69,21 @@ void free_all(kvev_ctx* c) {
   c->prof.pool.clear();
 }
 
-// Allocate pages so that group g can hold `n_slots` slots; collects ptab updates.
+// Token modes: group g's logical page i is the pool page g * maxpages + i,
+// a fixed contiguous region per group (the page table holds this mapping
+// from kvev_create on), so a step streams each group's pages in address
+// order.  The pool holds maxpages pages for every group; a group fits
+// `n_slots` slots when they need at most maxpages pages.
 bool ensure_pages(kvev_ctx* c, int g, int64_t n_slots, std::vector<int>& upd) {
-  const int need = static_cast<int>((n_slots + c->PT - 1) / c->PT);
-  auto& pg = c->pages[g];
-  while (static_cast<int>(pg.size()) < need) {
-    if (c->free_pages.empty()) return false;
-    const int p = c->free_pages.back();
-    c->free_pages.pop_back();
-    upd.push_back(g * c->maxpages + static_cast<int>(pg.size()));
-    upd.push_back(p);
-    pg.push_back(p);
-  }
-  return true;
+  (void)g;
+  (void)upd;
+  return (n_slots + c->PT - 1) / c->PT <= c->maxpages;
 }
 
 void release_pages(kvev_ctx* c, int g, int64_t n_slots) {
-  const int keep = static_cast<int>((n_slots + c->PT - 1) / c->PT);
-  auto& pg = c->pages[g];
-  while (static_cast<int>(pg.size()) > keep) {
-    c->free_pages.push_back(pg.back());
-    pg.pop_back();
-  }
+  (void)c;
+  (void)g;
+  (void)n_slots;
 }
 
 }  // namespace
@@ -174,6 +168,11 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.prefetch_blocks < 0) return bad("prefetch_blocks must be >= 0");
   if (f.prefetch_blocks > 0 && f.offload_blocks <= 0) return bad("prefetch_blocks needs the host-offload tier");
   if (!std::isfinite(f.offload_min_score)) return bad("offload_min_score must be finite");
+  if (f.attn_path < KVEV_ATTN_AUTO || f.attn_path > KVEV_ATTN_WHOLE) return bad("unknown attn_path");
+  if (f.evict_interval < 0) return bad("evict_interval must be >= 0");
+  if (f.evict_interval > 1 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
+    return bad("evict_interval applies to the token policies only");
+  if (f.evict_interval > 1 && f.diag_topk > 0) return bad("diagnostics need evict_interval 0 or 1");
   if (f.diag_topk < 0) return bad("diag_topk must be >= 0");
   if (f.diag_topk > 0 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("diagnostics apply to the token policies only");
@@ -242,6 +241,8 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->cfg = f;
   c->stream = static_cast<hipStream_t>(hip_stream);
   hipGetDevice(&c->device);
+  if (hipDeviceGetAttribute(&c->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device) != hipSuccess)
+    c->max_lds = 65536;
   c->G = f.batch * f.n_kv_heads;
   c->HG = f.n_q_heads / f.n_kv_heads;
   c->cap = f.max_tokens;
@@ -257,6 +258,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   c->hole_in.assign(c->G, 0);
   c->prefilled.assign(f.batch, 0);
   c->seq_next.assign(f.batch, 0);
+  if (c->pooled) c->pool_import.assign(f.batch, {});
   c->block_mode = block;
   if (block) {
     c->maxblk = c->maxpages;
@@ -269,9 +271,6 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     c->bbudget.assign(f.batch, static_cast<int>(f.budget));
     c->npinned.assign(f.batch, 0);
   }
-  c->pages.assign(c->G, {});
-  c->free_pages.resize(c->P);  // popped from the back: lowest page first
-  for (int64_t i = 0; i < c->P; ++i) c->free_pages[i] = static_cast<int>(c->P - 1 - i);
 
   auto& d = c->d;
   const int64_t L = f.n_layers, D = f.head_dim, G = c->G, HG = c->HG;
@@ -289,8 +288,10 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (!block) A(dalloc(&d.hole, G));  // token modes: the free slot the next token takes
   A(dalloc(&d.nextpos, G));
   // the logit stride is the step's slot count rounded up to 16, which can
-  // exceed a capacity that is not a multiple of 16
-  A(dalloc(&d.logits, static_cast<size_t>(G) * L * ((c->cap + 15) / 16 * 16) * HG));
+  // exceed a capacity that is not a multiple of 16.  The block mode's
+  // matrix-core attention writes per-block sums (bpart) instead of logits.
+  const bool block_sums = block && f.dtype == KVEV_BF16 && f.head_dim == 128;
+  if (!block_sums) A(dalloc(&d.logits, static_cast<size_t>(G) * L * ((c->cap + 15) / 16 * 16) * HG));
   A(dalloc(&d.part_ml, static_cast<size_t>(L) * G * c->max_splits * HG * 2));
   A(dalloc(&d.part_o, static_cast<size_t>(L) * G * c->max_splits * HG * D));
   A(dalloc(&d.ml, static_cast<size_t>(L) * G * HG * 2));
@@ -307,6 +308,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   A(dalloc(&d.blk_key, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_slot, static_cast<size_t>(G) * c->max_post_blocks));
   A(dalloc(&d.blk_sum, static_cast<size_t>(G) * c->max_post_blocks));
+  A(dalloc(&d.gnew, G));
   const bool diag = f.diag_topk > 0;
   const size_t npos = static_cast<size_t>(G) * f.max_tokens;  // per-position stamps
   if (diag) {
@@ -330,8 +332,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
     A(dalloc(&d.btref, Bs * c->maxblk));
     A(dalloc(&d.bres, Bs * c->maxblk));
     // the matrix-core attention writes per-block sums instead of per-slot logits
-    if (f.dtype == KVEV_BF16 && f.head_dim == 128)
-      A(dalloc(&d.bpart, static_cast<size_t>(L) * G * c->maxpages * HG));
+    if (block_sums) A(dalloc(&d.bpart, static_cast<size_t>(L) * G * c->maxpages * HG));
     A(dalloc(&d.bcnt, Bs * c->maxblk * kRegions));
     A(dalloc(&d.fstack, static_cast<size_t>(G) * c->maxpages));
     A(dalloc(&d.ftop, G));
@@ -369,7 +370,14 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   // zero everything so unused slots hold finite values
   A(hipMemsetAsync(d.kpool, 0, pool_bytes, c->stream));
   A(hipMemsetAsync(d.vpool, 0, pool_bytes, c->stream));
-  A(hipMemsetAsync(d.ptab, 0, sizeof(int) * G * c->maxpages, c->stream));
+  if (block) {
+    A(hipMemsetAsync(d.ptab, 0, sizeof(int) * G * c->maxpages, c->stream));
+  } else {
+    // token modes: the fixed mapping of logical page i of group g to pool page g * maxpages + i
+    std::vector<int> idmap(static_cast<size_t>(G) * c->maxpages);
+    for (size_t i = 0; i < idmap.size(); ++i) idmap[i] = static_cast<int>(i);
+    A(hipMemcpy(d.ptab, idmap.data(), sizeof(int) * idmap.size(), hipMemcpyHostToDevice));
+  }
   A(hipMemsetAsync(d.score, 0, sizeof(float) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.pos, 0, sizeof(int) * G * c->cap, c->stream));
   A(hipMemsetAsync(d.count, 0, sizeof(int) * G, c->stream));
@@ -541,14 +549,8 @@ kvev_status kvev_prefill(kvev_ctx* c, int32_t seq, const void* k, const void* v,
     const int g = seq * Hkv + h;
     release_pages(c, g, 0);
   }
-  // page i of every KV head of the sequence is allocated before page i + 1,
-  // so the pages that survive compaction (the lowest) are adjacent in memory
-  const int64_t npages = (n + c->PT - 1) / c->PT;
-  for (int64_t i = 1; i <= npages; ++i)
-    for (int h = 0; h < Hkv; ++h)
-      if (!ensure_pages(c, seq * Hkv + h, std::min(n, i * c->PT), upd))
-        return fail(c, KVEV_ENOMEM, "page pool exhausted");
-  if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
+  for (int h = 0; h < Hkv; ++h)
+    if (!ensure_pages(c, seq * Hkv + h, n, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
   KVEV_HIP(c, launch_prefill_scatter(c, seq, k, v, n));
   // positions 0..n-1, utilities 0, count n, next position n
   std::vector<int> posv(n);
@@ -693,9 +695,31 @@ static kvev_status block_evict(kvev_ctx* c, int64_t override_budget) {
 
 // Shared by kvev_decode_step and kvev_step: pages for the new token, the
 // attention launch and the post launch.
+// Per-sequence granularity: a sequence whose KV heads were only partly
+// imported (kvev_import_group) holds inconsistent slots.
+static kvev_status check_pool_import(kvev_ctx* c) {
+  for (const auto& pi : c->pool_import)
+    if (!pi.done.empty())
+      return fail(c, KVEV_ESTATE, "per-sequence granularity: a sequence's KV heads were only partly imported");
+  return KVEV_OK;
+}
+
+// The whole-cache attention kernel applies to the token policies with bf16,
+// head_dim 128, the attention scorer and per-KV-head granularity, when the
+// step's slots fit its bound and its LDS (the logits of an observation
+// step, the per-wave outputs and about 1 KiB of fixed arrays).
+static bool whole_cache_attention(const kvev_ctx* c, int64_t n_max) {
+  const auto& f = c->cfg;
+  if (f.attn_path == KVEV_ATTN_SPLIT || c->block_mode || c->tier_mode || c->pooled) return false;
+  if (f.dtype != KVEV_BF16 || f.head_dim != 128 || f.scorer != 0) return false;
+  if (n_max > kSeqMaxSlots || seq_attn_lds_bytes(c->HG, n_max, true) + 1024 > c->max_lds) return false;
+  return f.attn_path == KVEV_ATTN_WHOLE || static_cast<int64_t>(c->G) * f.n_layers >= 224;
+}
+
 static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                             float* out, bool do_select, int64_t B) {
   if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
+  if (kvev_status s = check_pool_import(c)) return s;
   for (int b = 0; b < c->cfg.batch; ++b)
     if (!c->prefilled[b]) return fail(c, KVEV_ESTATE, "a sequence has no prefill");
   const int64_t t = c->t + 1;
@@ -718,14 +742,17 @@ static kvev_status run_step(kvev_ctx* c, const void* q, const void* k_new, const
     if (!ensure_pages(c, g, c->count[g] + 1, upd)) return fail(c, KVEV_ENOMEM, "page pool exhausted");
   if (!upd.empty()) KVEV_HIP(c, launch_set_pages(c, upd.data(), static_cast<int>(upd.size() / 2)));
   c->lstride = (n_max + 15) / 16 * 16;
-  {
-    ProfScope p(c, "attn");
-    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0));
-  }
-  {
-    ProfScope p(c, "post");
+  const bool whole = whole_cache_attention(c, n_max);
+  // the launches time themselves ("attn_whole", "attn", "post") when
+  // profiling; after the whole-cache attention the fold kernel folds,
+  // selects and commits each group's state
+  if (whole) {
+    KVEV_HIP(c, launch_attention_seq(c, q, k_new, v_new, out, static_cast<int>(n_max), refresh ? 1 : 0));
+    KVEV_HIP(c, launch_fold(c, static_cast<int>(n_max), refresh ? 1 : 0, do_select ? 1 : 0, B));
+  } else {
+    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0, "attn"));
     KVEV_HIP(c, launch_post(c, out, k_new, v_new, static_cast<int>(n_max), refresh ? 1 : 0,
-                            do_select ? 1 : 0, B));
+                            do_select ? 1 : 0, B, 0));
   }
   // the post kernel plans the compaction; the move kernel copies the rows
   // (its blocks spread the scattered stores of the channel-major V columns)
@@ -778,7 +805,9 @@ kvev_status kvev_step(kvev_ctx* c, const void* q, const void* k_new, const void*
   }
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
-  return run_step(c, q, k_new, v_new, out, true, B);
+  // selection only after the steps t with (t - 1) % evict_interval == 0
+  const int64_t ei = c->cfg.evict_interval > 1 ? c->cfg.evict_interval : 1;
+  return run_step(c, q, k_new, v_new, out, c->t % ei == 0, B);
 }
 
 kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
@@ -788,6 +817,7 @@ kvev_status kvev_evict(kvev_ctx* c, int64_t budget) {
   if (c->cfg.diag_topk > 0) return fail(c, KVEV_ESTATE, "diagnostics on: use kvev_step");
   int64_t B;
   if (kvev_status s = check_budget(c, budget, &B)) return s;
+  if (kvev_status s = check_pool_import(c)) return s;
   int64_t max_moves = 0;
   bool any = false, inner = false;
   for (int g = 0; g < c->G; ++g) {
@@ -1108,10 +1138,22 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   int g;
   if (kvev_status s = group_index(c, seq, h, &g)) return s;
   if (c->block_mode) return fail(c, KVEV_EINVAL, "block mode: use kvev_import_blocks");
-  if (c->pooled) return fail(c, KVEV_EINVAL, "per-sequence granularity: groups cannot be imported one by one");
   if (c->cfg.diag_topk > 0) return fail(c, KVEV_ESTATE, "diagnostics on: the state changes only by kvev_step");
   if (!positions || !scores || !k || !v) return fail(c, KVEV_EINVAL, "null argument");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_ERANGE, "n out of range");
+  if (c->pooled) {
+    // every KV head of a sequence holds the same slots: the sequence's
+    // import completes once each of its KV heads was imported with the same
+    // positions (in the same slot order); until then the step calls refuse
+    auto& pi = c->pool_import[seq];
+    if (pi.done.empty()) {
+      pi.done.assign(c->cfg.n_kv_heads, 0);
+      pi.pos.assign(positions, positions + n);
+    } else if (static_cast<int64_t>(pi.pos.size()) != n || !std::equal(pi.pos.begin(), pi.pos.end(), positions)) {
+      return fail(c, KVEV_EINVAL,
+                  "per-sequence granularity: every KV head of a sequence must be imported with the same positions");
+    }
+  }
   int maxp = 0;
   for (int64_t i = 0; i < n; ++i) maxp = std::max(maxp, positions[i]);
   std::vector<int> upd;
@@ -1129,6 +1171,14 @@ kvev_status kvev_import_group(kvev_ctx* c, int32_t seq, int32_t h, int64_t n,
   release_pages(c, g, n + 1);
   c->count[g] = n;
   c->hole_in[g] = 0;
+  if (c->pooled) {
+    auto& pi = c->pool_import[seq];
+    pi.done[h] = 1;
+    if (std::all_of(pi.done.begin(), pi.done.end(), [](uint8_t x) { return x != 0; })) {
+      pi.done.clear();
+      pi.pos.clear();
+    }
+  }
   return KVEV_OK;
 }
 
@@ -1189,9 +1239,11 @@ kvev_status kvev_diag_trace(kvev_ctx* c, int32_t seq, int32_t h, int32_t* positi
   return KVEV_OK;
 }
 
-kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm) {
-  KVEV_LIVE(full);
-  KVEV_LIVE(comp);
+}  // extern "C"
+
+namespace kvev {
+// The argument checks shared by the two missed-mass entry points.
+kvev_status fmm_check(kvev_ctx* full, kvev_ctx* comp, const double* fmm) {
   if (!fmm || full == comp) return fail(comp, KVEV_EINVAL, "null output or the same context twice");
   if (full->cfg.diag_topk <= 0 || comp->cfg.diag_topk <= 0)
     return fail(comp, KVEV_ESTATE, "diagnostics are off");
@@ -1205,6 +1257,16 @@ kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm) {
   if (comp->t < 1) return fail(comp, KVEV_ESTATE, "no step yet");
   for (int s = 0; s < a.batch; ++s)
     if (full->seq_next[s] != comp->seq_next[s]) return fail(comp, KVEV_EINVAL, "different prefill lengths");
+  return KVEV_OK;
+}
+}  // namespace kvev
+
+extern "C" {
+
+kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm) {
+  KVEV_LIVE(full);
+  KVEV_LIVE(comp);
+  if (kvev_status s = fmm_check(full, comp, fmm)) return s;
   double* dev = nullptr;
   KVEV_HIP(comp, hipMalloc(&dev, sizeof(double) * comp->G));
   hipEvent_t ev = nullptr;

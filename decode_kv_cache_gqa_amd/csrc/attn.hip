@@ -15,6 +15,7 @@
 // it.  Without a hole array (block mode) the free slot is count[g].
 #include "common.h"
 #include "kvev_internal.h"
+#include "host_util.h"
 
 namespace kvev {
 
@@ -615,7 +616,7 @@ static hipError_t attention_valu(kvev_ctx* c, const void* q, const void* k_new, 
 }
 
 hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
-                            int n_max, int write_logits) {
+                            int n_max, int write_logits, const char* prof) {
   const auto& cf = c->cfg;
   const int D = cf.head_dim;
   return with_group(c->HG, [&](auto hg) -> hipError_t {
@@ -628,19 +629,20 @@ hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const
       float* pvn = write_logits ? c->d.part_vn : nullptr;
       float* bp = write_logits ? c->d.bpart : nullptr;  // block mode: block sums instead of logits
       auto launch = [&](auto kern) {
-        kern<<<grid, kMfmaNW * kWave, 0, c->stream>>>(
-            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
-            static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
-            static_cast<uint16_t*>(c->d.vpool), c->d.ptab, c->d.count, c->d.hole, c->d.logits, c->d.part_ml,
-            c->d.part_o, pu, vn, pvn, cf.n_layers, c->G, cf.n_kv_heads, cf.n_q_heads, c->P,
-            c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f), bp ? 0 : write_logits, bp);
+        return timed_launch(
+            c, prof, kern, grid, dim3(kMfmaNW * kWave), 0, static_cast<const uint16_t*>(q),
+            static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+            static_cast<uint16_t*>(c->d.kpool), static_cast<uint16_t*>(c->d.vpool),
+            static_cast<const int*>(c->d.ptab), static_cast<const int*>(c->d.count),
+            static_cast<const int*>(c->d.hole), c->d.logits, c->d.part_ml, c->d.part_o, pu, vn, pvn,
+            static_cast<int>(cf.n_layers), c->G, static_cast<int>(cf.n_kv_heads),
+            static_cast<int>(cf.n_q_heads), c->P, c->maxpages, c->lstride, splits, 1.0f / sqrtf(128.0f),
+            bp ? 0 : write_logits, bp);
       };
-      if (pu || vn)
-        launch(attn_mfma_kernel<kMfmaNW, HG, true>);
-      else
-        launch(attn_mfma_kernel<kMfmaNW, HG, false>);
-      return hipGetLastError();
+      if (pu || vn) return launch(attn_mfma_kernel<kMfmaNW, HG, true>);
+      return launch(attn_mfma_kernel<kMfmaNW, HG, false>);
     }
+    ProfScope p(c, prof);  // the vector path is timed by events around it
     if (cf.dtype == KVEV_BF16) return attention_valu<bf16_t, 64, HG>(c, q, k_new, v_new, n_max, write_logits);
     if (D == 128) return attention_valu<float, 128, HG>(c, q, k_new, v_new, n_max, write_logits);
     return attention_valu<float, 64, HG>(c, q, k_new, v_new, n_max, write_logits);

@@ -1,0 +1,338 @@
+// Whole-cache GQA decode attention per (layer, group): one workgroup reads
+// every retained slot of one (sequence, KV head) group at one layer, so the
+// softmax statistics are final inside the workgroup.  It writes the
+// attention output and, on an observation step, the group's probability
+// mass per slot, G[t] = sum_{h in group} exp(s_h[t] - M_h) / Z_h
+// ("QEvict" review, section 4.1 (Attention): s = q.k / sqrt(d); "What
+// Matters ...", section 3.1 Eq.1 with appendix E's GQA sharing: the KV
+// head's query group pooled by summation).  No split partials and no
+// per-slot logits leave the chip: the logits stay in LDS until the
+// probability pass.  The step's new token is appended on the way (it takes
+// the group's free slot, hole[g]).
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16, 32 slots = two pages per
+// iteration):
+//   q.K^T  C[16 slots][16 heads] = K (A: lane (slot r16, k-group q4) holds
+//          channels 32s + 8q4 .. +8 of a token-major K page row) x Q^T (B:
+//          lane (head r16, q4) holds the same channels of query head r16;
+//          heads >= HG are zero).  Lane (head r16, q4) receives the logits
+//          of slots 4q4 .. 4q4+3 of the tile.
+//   p.V    C[16 channels][16 heads] = V^T x P^T over a k-block of 32 slots
+//          ordered sigma(8q4 + e) = 16 (e >> 2) + 4q4 + (e & 3): then the
+//          probabilities a lane holds after q.K^T of the two tiles are
+//          exactly its B operand, and its A operand is slots 4q4 .. 4q4+3 of
+//          one channel in each of the two channel-major V pages (8 bytes
+//          each).  P is split into bf16 high and low parts (two products),
+//          so its rounding is at most 2^-18 relative.
+// The online softmax keeps one running maximum and sum per lane (its head)
+// and rescales the accumulator, whose lanes hold the same head.  Each wave
+// streams a contiguous range of chunks with the next chunk's K and V loads
+// in flight while the current one is computed.
+#include "common.h"
+#include "kvev_internal.h"
+
+namespace kvev {
+
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef float f32x4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2s __attribute__((ext_vector_type(2)));
+
+// bit casts between same-size vector types (registers only)
+__device__ __forceinline__ bf16x8s to_bf16x8(u32x4s r) { return __builtin_bit_cast(bf16x8s, r); }
+
+// replace 16-bit element e (0..3) of an 8-byte register pair (values
+// selected, never an address: the pair stays in registers)
+__device__ __forceinline__ u32x2s put16x4(u32x2s r, int e, uint32_t x) {
+  const int sh = (e & 1) * 16;
+  const uint32_t m = ~(0xffffu << sh);
+  const uint32_t v = (x & 0xffffu) << sh;
+  const bool hi = (e >> 1) != 0;
+  u32x2s o;
+  o.x = hi ? r.x : ((r.x & m) | v);
+  o.y = hi ? ((r.y & m) | v) : r.y;
+  return o;
+}
+
+// The registers of one 32-slot chunk: K rows of its two pages (A operands
+// of q.K^T) and the V pieces of its two pages (A operands of p.V).
+struct SeqChunk {
+  u32x4s k[2][4];  // [page of the chunk][k-step]
+  u32x2s v[2][8];  // [page of the chunk][channel tile]
+};
+
+// Loads of chunk c from the group's pages (slots past the group's count are
+// masked, so their values never count).  The cache is read once per step:
+// non-temporal loads keep it from displacing reused lines.
+__device__ __forceinline__ void seq_load(SeqChunk& ch, const uint16_t* __restrict__ kpool,
+                                         const uint16_t* __restrict__ vpool, int page0, int maxpages, int c,
+                                         int l, int r16, int q4, int64_t P) {
+  constexpr int D = 128;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int page = page0 + min(2 * c + j, maxpages - 1);
+    const uint16_t* kb = kpool + kidx(l, page, r16, 8 * q4, P, D);
+    const uint16_t* vb = vpool + vidx(l, page, 4 * q4, r16, P, D);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ch.k[j][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4s*>(kb + 32 * s));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      ch.v[j][ct] = __builtin_nontemporal_load(reinterpret_cast<const u32x2s*>(vb + ct * 16 * kPageTokens));
+  }
+}
+
+// One chunk: append of the new token (when the chunk holds the free slot),
+// q.K^T, online softmax, p.V.
+template <int HG, bool OBS>
+__device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, int tnew, const u32x4s (&knew)[4],
+                                         const uint32_t (&vnew)[8], int page0,
+                                         uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, int l,
+                                         int r16, int q4, int64_t P, bool head, const bf16x8s (&qb)[4],
+                                         float scale, float* s_lg, int nstride, f32x4s (&oacc)[8],
+                                         float& m_run, float& l_run) {
+  constexpr int D = 128;
+  // append: the new token replaces the free slot's stale contents (per-lane
+  // selects with constant indices) and is written into its page
+  if (app && (tnew >> 5) == c) {  // wave-uniform
+    const int jn = (tnew >> 4) & 1, rn = tnew & 15;
+    const int page = page0 + 2 * c + jn;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool krow = j == jn && r16 == rn;
+      const bool vcol = j == jn && q4 == (rn >> 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ch.k[j][s] = krow ? knew[s] : ch.k[j][s];
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) ch.v[j][ct] = vcol ? put16x4(ch.v[j][ct], rn & 3, vnew[ct]) : ch.v[j][ct];
+    }
+    if (r16 == rn) {
+      uint16_t* kd = kpool + kidx(l, page, rn, 8 * q4, P, D);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4s*>(kd + 32 * s) = knew[s];
+    }
+    if (q4 == (rn >> 2)) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) vpool[vidx(l, page, rn, 16 * ct + r16, P, D)] = static_cast<uint16_t>(vnew[ct]);
+    }
+  }
+  // q.K^T of the two 16-slot tiles
+  float sv[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f32x4s acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(to_bf16x8(ch.k[j][s]), qb[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 32 * c + 16 * j + 4 * q4 + i;
+      sv[j][i] = (head && t < n) ? acc[i] * scale : -INFINITY;
+    }
+    if (OBS && head)
+      *reinterpret_cast<float4*>(&s_lg[r16 * nstride + 32 * c + 16 * j + 4 * q4]) =
+          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
+  }
+  // online softmax (the four lane quarters of a head hold its 32 slots)
+  float mc = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                   fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+  mc = fmaxf(mc, __shfl_xor(mc, 16, kWave));
+  mc = fmaxf(mc, __shfl_xor(mc, 32, kWave));
+  const float m_new = fmaxf(m_run, mc);
+  const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = sv[j][i] == -INFINITY ? 0.f : __expf(sv[j][i] - m_new);
+      sv[j][i] = p;
+      psum += p;
+    }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[ct][i] *= alpha;
+  // p.V: B = P^T in the sigma order, split into bf16 high and low parts
+  uint32_t h16[8], l16[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = sv[e >> 2][e & 3];
+    h16[e] = bf16_rne(x);
+    l16[e] = bf16_rne(x - __uint_as_float(h16[e] << 16));
+  }
+  const bf16x8s phi = to_bf16x8(u32x4s{h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16),
+                                        h16[4] | (h16[5] << 16), h16[6] | (h16[7] << 16)});
+  const bf16x8s plo = to_bf16x8(u32x4s{l16[0] | (l16[1] << 16), l16[2] | (l16[3] << 16),
+                                        l16[4] | (l16[5] << 16), l16[6] | (l16[7] << 16)});
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const bf16x8s va = to_bf16x8(u32x4s{ch.v[0][ct].x, ch.v[0][ct].y, ch.v[1][ct].x, ch.v[1][ct].y});
+    oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, oacc[ct], 0, 0, 0);
+    oacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, oacc[ct], 0, 0, 0);
+  }
+}
+
+template <int NW, int HG, bool OBS>
+__global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
+    const int* __restrict__ count, const int* __restrict__ hole, float* __restrict__ out,
+    float* __restrict__ gmass, int L, int G, int Hkv, int Hq, int64_t P, int maxpages, int64_t lstride,
+    int nstride, float scale, int nmax) {
+  static_assert(HG >= 1 && HG <= 8, "group size");
+  constexpr int D = 128, NT = NW * kWave;
+  extern __shared__ float dyn[];
+  float* s_lg = dyn;                                 // [HG][nstride] logits (observation steps)
+  float* o_m = dyn + (OBS ? HG * nstride : 0);       // [NW][HG][D] per-wave outputs
+  __shared__ float wm[NW][HG], wl[NW][HG];
+  __shared__ float sM[HG], sZ[HG];
+
+  const int g = blockIdx.x, l = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int Bsz = G / Hkv, b = g / Hkv, kvh = g % Hkv;
+  const int64_t new_off = (static_cast<int64_t>(l * Bsz + b) * Hkv + kvh) * D;
+  const bool head = r16 < HG;  // the lane's column is a real query head
+
+  // The chunk ranges come from the launch's slot bound nmax (>= every
+  // group's slot count), and a token-mode group's logical page i is the
+  // pool page g * maxpages + i, so the first page loads issue at once; slots
+  // past the group's count are masked.
+  const int nch = (nmax + 31) / 32;
+  const int cpw = (nch + NW - 1) / NW;
+  const int c0 = min(nch, wave * cpw), c1 = min(nch, c0 + cpw);
+  const int page0 = g * maxpages;  // the group's first page
+  const int n = count[g] + 1;  // slots including the new token
+  const int tnew = hole[g];
+
+  // B operand of q.K^T: query head r16, channels 32s + 8q4 .. +8
+  bf16x8s qb[4];
+  {
+    const uint16_t* qp = q + (static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + min(r16, HG - 1)) * D + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const u32x4s r = *reinterpret_cast<const u32x4s*>(qp + 32 * s);
+      qb[s] = to_bf16x8(head ? r : u32x4s{0u, 0u, 0u, 0u});
+    }
+  }
+
+  // the new token's K row piece and V column elements, loaded first by the
+  // wave whose range holds the free slot
+  const bool app = tnew >= 32 * c0 && tnew < 32 * c1;  // wave-uniform
+  u32x4s knew[4];
+  uint32_t vnew[8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    knew[s] = app ? *reinterpret_cast<const u32x4s*>(k_new + new_off + 32 * s + 8 * q4) : u32x4s{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) vnew[ct] = app ? v_new[new_off + 16 * ct + r16] : 0u;
+
+  f32x4s oacc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4s{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // two chunks per iteration, one per register buffer: the next chunk's
+  // loads are in flight while the current one is computed
+  SeqChunk cur, nxt;
+  if (c0 < c1) seq_load(cur, kpool, vpool, page0, maxpages, c0, l, r16, q4, P);
+#pragma unroll 1
+  for (int c = c0; c < c1; c += 2) {
+    if (c + 1 < c1) seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
+    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
+                      s_lg, nstride, oacc, m_run, l_run);
+    if (c + 1 < c1) {
+      if (c + 2 < c1) seq_load(cur, kpool, vpool, page0, maxpages, c + 2, l, r16, q4, P);
+      seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb,
+                        scale, s_lg, nstride, oacc, m_run, l_run);
+    }
+  }
+
+  // ---- merge the waves: (M, Z) per head and the output ----------------------
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (head) {
+    if (q4 == 0) {
+      wm[wave][r16] = m_run;
+      wl[wave][r16] = l_run;
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<float4*>(&o_m[(wave * HG + r16) * D + 16 * ct + 4 * q4]) =
+          make_float4(oacc[ct][0], oacc[ct][1], oacc[ct][2], oacc[ct][3]);
+  }
+  __syncthreads();
+  if (tid < HG) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][tid]);
+    float Z = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Z += wm[w][tid] == -INFINITY ? 0.f : wl[w][tid] * __expf(wm[w][tid] - M);
+    sM[tid] = M;
+    sZ[tid] = Z;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < HG * D; idx += NT) {
+    const int h = idx / D, cc = idx % D;
+    const float M = sM[h];
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      o += wm[w][h] == -INFINITY ? 0.f : __expf(wm[w][h] - M) * o_m[(w * HG + h) * D + cc];
+    out[(static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + h) * D + cc] = o / sZ[h];
+  }
+  if constexpr (OBS) {
+    // probability pass: the group's mass of every slot, from the logits in LDS
+    float Mh[HG], Zh[HG];
+#pragma unroll
+    for (int h = 0; h < HG; ++h) {
+      Mh[h] = sM[h];
+      Zh[h] = sZ[h];
+    }
+    float* gm = gmass + (static_cast<int64_t>(g) * L + l) * lstride;
+    for (int t = tid; t < n; t += NT) {
+      float m = 0.f;
+#pragma unroll
+      for (int h = 0; h < HG; ++h) m += __expf(s_lg[h * nstride + t] - Mh[h]) / Zh[h];
+      gm[t] = m;
+    }
+  }
+}
+
+// Grid (groups, layers), NW = 8 waves; dynamic LDS: the logits (observation
+// steps) and the per-wave outputs.
+constexpr int kSeqNW = 8;
+
+int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs) {
+  const int64_t nstride = (n_max + 31) / 32 * 32;
+  return ((obs ? hg * nstride : 0) + static_cast<int64_t>(kSeqNW) * hg * 128) * 4;
+}
+
+hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                                float* out, int n_max, int obs) {
+  const auto& cf = c->cfg;
+  const int nstride = (n_max + 31) / 32 * 32;
+  const size_t shm = static_cast<size_t>(seq_attn_lds_bytes(c->HG, n_max, obs != 0));
+  dim3 grid(c->G, cf.n_layers);
+  return with_group(c->HG, [&](auto hg) -> hipError_t {
+    constexpr int HG = decltype(hg)::value;
+    auto launch = [&](auto kern) -> hipError_t {
+      if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)))
+        return e;
+      return timed_launch(c, "attn_whole", kern, grid, dim3(kSeqNW * kWave), shm, static_cast<const uint16_t*>(q),
+                          static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                          static_cast<uint16_t*>(c->d.kpool), static_cast<uint16_t*>(c->d.vpool),
+                          static_cast<const int*>(c->d.count), static_cast<const int*>(c->d.hole), out,
+                          c->d.logits, static_cast<int>(cf.n_layers), c->G, static_cast<int>(cf.n_kv_heads),
+                          static_cast<int>(cf.n_q_heads), c->P, c->maxpages, c->lstride, nstride,
+                          1.0f / sqrtf(128.0f), n_max);
+    };
+    return obs ? launch(attn_seq_kernel<kSeqNW, HG, true>) : launch(attn_seq_kernel<kSeqNW, HG, false>);
+  });
+}
+
+}  // namespace kvev

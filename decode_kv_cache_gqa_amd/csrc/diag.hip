@@ -382,3 +382,4 @@ hipError_t launch_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm_dev) {
 }
 
 }  // namespace kvev
+

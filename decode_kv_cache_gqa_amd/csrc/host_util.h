@@ -45,7 +45,7 @@ struct ProfScope {
   const char* name;
   hipEvent_t a = nullptr;
   ProfScope(kvev_ctx* c_, const char* n) : c(c_), name(n) {
-    if (!c->prof.enabled) return;
+    if (!c->prof.enabled || !name) return;
     a = take_event();
     hipEventRecord(a, c->stream);
   }
@@ -60,7 +60,7 @@ struct ProfScope {
     return e;
   }
   ~ProfScope() {
-    if (!c->prof.enabled) return;
+    if (!c->prof.enabled || !name || !a) return;
     hipEvent_t b = take_event();
     hipEventRecord(b, c->stream);
     c->prof.pending.push_back({name, a, b});

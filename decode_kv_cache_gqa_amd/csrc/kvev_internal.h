@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <string>
 #include <type_traits>
@@ -55,6 +56,7 @@ struct DevState {
   unsigned long long* blk_key = nullptr;  // [G][max_post_blocks] per-block minimum eviction key
   int* blk_slot = nullptr;                // [G][max_post_blocks] its slot
   float* blk_sum = nullptr;               // [G][max_post_blocks] per-block utility sum
+  float* gnew = nullptr;                  // [G] the new token's folded utility (fold kernel)
   // rank-trace diagnostics (cfg.diag_topk > 0)
   int* dg_n = nullptr;      // [G] tokens the last step attended
   int* dg_pos = nullptr;    // [G][cap] their positions, in the step's slot order
@@ -153,6 +155,8 @@ struct TierArgs {
 
 struct Profiler {
   bool enabled = false;
+  // name under which the next timed_launch() records the kernel's own
+  // dispatch start and end (set by the caller around one launch)
   struct Rec {
     std::string name;
     hipEvent_t a, b;
@@ -169,6 +173,7 @@ struct kvev_ctx {
   hipStream_t stream = nullptr;
   int device = 0;
   int G = 0, HG = 0, PT = kvev::kPageTokens, maxpages = 0;
+  int max_lds = 65536;  // LDS bytes a workgroup may allocate on the device
   bool pooled = false;  // one retained set per sequence (KVEV_PER_SEQUENCE)
   int64_t cap = 0, P = 0;
   int64_t lstride = 0;  // slot stride of the logit scratch in the current step
@@ -182,6 +187,11 @@ struct kvev_ctx {
                                             // single-token eviction; an append fills it)
   std::vector<int> prefilled;               // per sequence
   std::vector<int64_t> seq_next;            // per sequence: the next position (token modes)
+  struct PoolImport {                       // per-sequence granularity: an import in progress
+    std::vector<uint8_t> done;              // KV heads imported so far (empty: none pending)
+    std::vector<int> pos;                   // the positions every KV head must take
+  };
+  std::vector<PoolImport> pool_import;      // per sequence
   void* hpool = nullptr;                    // pinned host pool of the offload tier
   void* hpool_dev = nullptr;                // its device mapping
   // background prefetch of pool blocks into device staging
@@ -192,8 +202,6 @@ struct kvev_ctx {
   std::vector<int> pf_key;                  // staging slot -> block key b * maxblk + block, or -1
   std::vector<int> pf_src;                  // staging slot -> the pool slot it was copied from
   int pf_next = 0;                          // next staging slot
-  std::vector<std::vector<int>> pages;      // per group: physical page of logical page i
-  std::vector<int> free_pages;
   int64_t t = 0;
   bool sticky = false;
   std::string err;
@@ -238,15 +246,38 @@ inline hipError_t with_group(int hg, Fn&& fn) {
     default: return hipErrorInvalidValue;
   }
 }
+// Pops a profiling event from the context's pool (or creates one).
+inline hipEvent_t prof_event(kvev_ctx* c);
+// Launch of `kern` on the context's stream.  With profiling on and a name,
+// the launch records its own dispatch start and end timestamps into an
+// event pair (hipExtLaunchKernelGGL: no separate event packets between the
+// step's kernels, so the durations are not inflated), accumulated under
+// `name`.
+template <typename F, typename... Args>
+hipError_t timed_launch(kvev_ctx* c, const char* name, F kern, dim3 grid, dim3 block, size_t shm,
+                        Args... args);
 // Launchers (defined in the .hip translation units).  All are stream-ordered.
 hipError_t launch_prefill_scatter(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n);
 // scatter into table entries [e0, e0 + ceil(n/16)) of every KV head of `seq`
 hipError_t launch_scatter_at(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n, int e0);
 hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd);
+// prof: the profiling name of the matrix-core launch (nullptr: the caller
+// times the launch itself)
 hipError_t launch_attention(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
-                            int n_max, int write_logits);
+                            int n_max, int write_logits, const char* prof = nullptr);
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                       int refresh, int do_select, int64_t budget);
+                       int refresh, int do_select, int64_t budget, int seq);
+// whole-cache attention: one workgroup per (group, layer) (attn_seq.hip);
+// writes out and, with obs, the per-slot group masses into d.logits
+// ([G][L][lstride]); token modes only (group g's logical page i is pool
+// page g * maxpages + i)
+hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                                float* out, int n_max, int obs);
+// after it: fold of the masses, the new token's state and the selection
+// (policy.hip)
+hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64_t budget);
+int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs);
+constexpr int kSeqMaxSlots = 8192;  // the whole-cache kernel's slot bound (64 pages per wave)
 hipError_t launch_select(kvev_ctx* c, int64_t budget);
 // plans the move of each over-budget group's last token into its inner free slot
 hipError_t launch_close_holes(kvev_ctx* c, int64_t budget);
@@ -258,6 +289,7 @@ hipError_t launch_import(kvev_ctx* c, int g, const void* k, const void* v, int64
 hipError_t launch_diag(kvev_ctx* c, int t);
 // missed mass of `comp` against `full`, into device fmm[G]
 hipError_t launch_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm_dev);
+kvev_status fmm_check(kvev_ctx* full, kvev_ctx* comp, const double* fmm);
 // block-granular mode (block.hip)
 hipError_t launch_block_open(kvev_ctx* c, int n_max, int t);
 hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max);
@@ -285,5 +317,29 @@ kvev_status tier_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int
 kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out);
 kvev_status tier_route(kvev_ctx* c);
 kvev_status tier_scores(kvev_ctx* c, int layer, float* dst, int64_t cap, int64_t* n);
+
+inline hipEvent_t prof_event(kvev_ctx* c) {
+  if (!c->prof.pool.empty()) {
+    hipEvent_t e = c->prof.pool.back();
+    c->prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  hipEventCreate(&e);
+  return e;
+}
+
+template <typename F, typename... Args>
+hipError_t timed_launch(kvev_ctx* c, const char* name, F kern, dim3 grid, dim3 block, size_t shm,
+                        Args... args) {
+  if (!c->prof.enabled || name == nullptr) {
+    kern<<<grid, block, shm, c->stream>>>(args...);
+    return hipGetLastError();
+  }
+  hipEvent_t a = prof_event(c), b = prof_event(c);
+  hipExtLaunchKernelGGL(kern, grid, block, static_cast<uint32_t>(shm), c->stream, a, b, 0, args...);
+  c->prof.pending.push_back({name, a, b});
+  return hipGetLastError();
+}
 
 }  // namespace kvev

@@ -1,6 +1,7 @@
 // Probability pass + score fold, top-budget selection with compaction plan,
 // K/V moves, and the cache copy kernels.
 #include "post_common.h"
+#include "host_util.h"
 
 namespace kvev {
 // ---------------------------------------------------------------------------
@@ -52,7 +53,11 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   __shared__ int s_slot[NT / kWave];
   __shared__ int s_last;
   const int c = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave;
-  const bool outb = c >= A.nblk;  // an output block, for layer ol
+  // seq: the whole-cache attention already wrote the outputs and, on an
+  // observation step, each slot's group mass per layer (A.logits then holds
+  // [G][L][lstride] masses): no statistics to merge and no output blocks
+  const bool seq = A.seq != 0;
+  const bool outb = !seq && c >= A.nblk;  // an output block, for layer ol
   const int ol = c - A.nblk;
   const int n = A.count[g] + 1;  // slots spanned, the new token's included
   const int hn = A.hole[g];       // the new token's slot
@@ -82,7 +87,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       const int l = lg + k * LG;
       const bool in = t < n && l < L;
       const int64_t r = (static_cast<int64_t>(g) * L + (in ? l : 0)) * A.lstride + (in ? t : 0);
-      load_heads<HG>(A.logits + r * HG, sx[k]);
+      if (seq)
+        sx[k][0] = A.logits[r];
+      else
+        load_heads<HG>(A.logits + r * HG, sx[k]);
       vx[k] = vn ? A.vnorm[r] : 1.f;
     }
   }
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   // statistics merged: every layer's for a folding block, its layer's for an
   // output block, none otherwise
   const int m0 = outb ? ol * HG : 0;  // (ol is negative for a slot block)
-  const int m1 = fold ? L * HG : (outb ? m0 + HG : 0);
+  const int m1 = (fold && !seq) ? L * HG : (outb ? m0 + HG : 0);
   float2 pm[kMergeBatch];
   const int ml_l = (m0 + tid) / HG, ml_h = (m0 + tid) % HG;
   const float2* pmb = reinterpret_cast<const float2*>(A.part_ml) +
@@ -213,10 +221,14 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       for (int k = 0; k < 8; ++k) {
         const int l = lg + k * LG;
         if (l >= L) continue;
-        s_mass[l * kPostTok + tl] = slot_mass(l, sx[k], vx[k]);
+        s_mass[l * kPostTok + tl] = seq ? sx[k][0] : slot_mass(l, sx[k], vx[k]);
       }
       for (int l = lg + 8 * LG; l < L; l += LG) {  // more than 8 * LG layers
         const int64_t r = (static_cast<int64_t>(g) * L + l) * A.lstride + t;
+        if (seq) {
+          s_mass[l * kPostTok + tl] = A.logits[r];
+          continue;
+        }
         float x[HG];
         load_heads<HG>(A.logits + r * HG, x);
         s_mass[l * kPostTok + tl] = slot_mass(l, x, vn ? A.vnorm[r] : 1.f);
@@ -404,6 +416,270 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
     A.hole[g] = new_hole;
     A.nmoves[g] = nm;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fold + selection after the whole-cache attention (which wrote the
+// outputs and, on an observation step, every slot's group mass per layer
+// into gmass [G][L][lstride]).  Grid (slot blocks of 256, groups), one slot
+// per thread.  Each thread's loads do not wait for the group's count (slots
+// past it are masked afterwards): the slot's utility and position and, on
+// an observation step, its masses of every layer, folded in ascending layer
+// order ("What Matters ...", section 3.1 Eq.3/Eq.4, appendix E "Layer
+// scoring"; the new token starts at 0).  Each block publishes the minimum
+// eviction key (order-preserving utility key, position) of its unprotected
+// slots, its slot and the utility sum (the new token excluded), and the
+// block holding the new token its folded utility; the group's last block
+// to arrive (no waiting) gives the new token its state (on a step without
+// an observation the mean of the others, appendix E "New token insertion")
+// and selects as post_kernel's last block does.  Data handed between blocks
+// is written through to device scope and read with device-scope loads.
+// ---------------------------------------------------------------------------
+constexpr int kFoldNT = 256;
+constexpr int kFoldLayers = 64;  // the library's layer bound
+
+struct FoldArgs {
+  int* count;
+  int* hole;
+  int* pos;
+  float* score;
+  int* nextpos;
+  const float* gmass;
+  unsigned* grpctr;
+  unsigned long long* blk_key;
+  int* blk_slot;
+  float* blk_sum;
+  float* gnew;  // [G] the new token's folded utility (observation steps)
+  int* mv_src;
+  int* mv_dst;
+  int* nmoves;
+  int* errflag;
+  int* dg_n;  // rank-trace diagnostics, or null
+  int* dg_pos;
+  float* dg_raw;
+  float* dg_util;
+  int L, max_blk, nblk;
+  int64_t cap, lstride;
+  float a;
+  int cumulative, refresh, do_select, B, n_sink, n_recent;
+};
+
+template <int NL>
+__global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
+  constexpr int NT = kFoldNT, NWV = NT / kWave;
+  __shared__ float red[NWV], s_new[NWV];
+  __shared__ unsigned long long s_key[NWV];
+  __shared__ int s_slot[NWV];
+  __shared__ int s_last;
+  const int blk = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int t = blk * NT + tid;
+  const bool valid = t < A.cap;
+  int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
+  float* gs = A.score + static_cast<int64_t>(g) * A.cap;
+  // loads that do not depend on the count
+  const float prior = valid ? gs[t] : 0.f;
+  const int mypos = valid ? gp[t] : 0;
+  float x[NL];
+  if (A.refresh) {
+    const float* gm = A.gmass + static_cast<int64_t>(g) * A.L * A.lstride + (t < A.lstride ? t : 0);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) x[l] = l < A.L ? gm[static_cast<int64_t>(l) * A.lstride] : 0.f;
+  }
+  const int n = A.count[g] + 1, hn = A.hole[g], newest = A.nextpos[g];
+  auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
+  const bool in = t < n;
+  float m = (in && t != hn) ? prior : 0.f;
+  if (A.refresh && in) {
+    float raw = 0.f;
+    const float keep = 1.0f - A.a;
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      if (l < A.L) {
+        raw += x[l];
+        m = A.cumulative ? m + x[l] : A.a * x[l] + keep * m;
+      }
+    }
+    st_coherent(gs + t, m);  // the selection of a larger eviction reads it back
+    if (A.dg_raw) {  // rank-trace diagnostics: the step's inputs per slot
+      const int64_t r = static_cast<int64_t>(g) * A.cap + t;
+      A.dg_pos[r] = t == hn ? newest : mypos;
+      A.dg_raw[r] = raw;
+      A.dg_util[r] = m;
+      if (t == 0) A.dg_n[g] = n;
+    }
+  }
+  // block summary over slots other than the new token's
+  const bool mine = in && t != hn;
+  unsigned long long key = ~0ull;
+  int slot = -1;
+  if (mine && is_cand(mypos)) {
+    key = (static_cast<unsigned long long>(float_key(m)) << 32) | static_cast<uint32_t>(mypos);
+    slot = t;
+  }
+  float sum = mine ? m : 0.f;
+  float mn = (A.refresh && in && t == hn) ? m : 0.f;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(key, o, kWave);
+    const int ys = __shfl_xor(slot, o, kWave);
+    if (y < key) {
+      key = y;
+      slot = ys;
+    }
+  }
+  sum = wave_sum(sum);
+  mn = wave_sum(mn);
+  if (lane == 0) {
+    s_key[wave] = key;
+    s_slot[wave] = slot;
+    red[wave] = sum;
+    s_new[wave] = mn;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < NWV; ++w) {
+      sum += red[w];
+      mn += s_new[w];
+      if (s_key[w] < key) {
+        key = s_key[w];
+        slot = s_slot[w];
+      }
+    }
+    const int64_t bi = static_cast<int64_t>(g) * A.max_blk + blk;
+    st_coherent(A.blk_key + bi, key);
+    st_coherent(A.blk_slot + bi, slot);
+    st_coherent(A.blk_sum + bi, sum);
+    if (A.refresh && hn / NT == blk) st_coherent(A.gnew + g, mn);
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned old = __hip_atomic_fetch_add(&A.grpctr[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == static_cast<unsigned>(A.nblk - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the group's last block ------------------------------------------------
+  float part = 0.f;
+  unsigned long long bkey = ~0ull;
+  int bslot = -1;
+  for (int i = tid; i < A.nblk; i += NT) {
+    const int64_t bi = static_cast<int64_t>(g) * A.max_blk + i;
+    part += ld_state<true>(A.blk_sum + bi);
+    const unsigned long long k2 = ld_state<true>(A.blk_key + bi);
+    const int s2 = ld_state<true>(A.blk_slot + bi);
+    if (k2 < bkey) {
+      bkey = k2;
+      bslot = s2;
+    }
+  }
+  const float newscore_obs = A.refresh ? ld_state<true>(A.gnew + g) : 0.f;
+  part = wave_sum(part);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long y = __shfl_xor(bkey, o, kWave);
+    const int ys = __shfl_xor(bslot, o, kWave);
+    if (y < bkey) {
+      bkey = y;
+      bslot = ys;
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+    red[wave] = part;
+    s_key[wave] = bkey;
+    s_slot[wave] = bslot;
+  }
+  __syncthreads();
+  float total = 0.f;
+  bkey = s_key[0];
+  bslot = s_slot[0];
+  for (int w = 0; w < NWV; ++w) {
+    total += red[w];
+    if (s_key[w] < bkey) {
+      bkey = s_key[w];
+      bslot = s_slot[w];
+    }
+  }
+  const float newscore = A.refresh ? newscore_obs : (n > 1 ? total / static_cast<float>(n - 1) : 0.f);
+  if (tid == 0) {
+    if (!A.refresh) st_coherent(gs + hn, newscore);
+    st_coherent(gp + hn, newest);
+    A.nextpos[g] = newest + 1;
+    A.grpctr[g] = 0u;
+  }
+  const bool one_over = A.do_select && n == A.B + 1;
+  int final_n = n, nm = 0, new_hole = n;
+  if (one_over) {
+    // one over budget: evict the smallest key, the new token included; the
+    // evicted slot stays free for the next token, so nothing moves
+    if (is_cand(newest)) {
+      const unsigned long long kn =
+          (static_cast<unsigned long long>(float_key(newscore)) << 32) | static_cast<uint32_t>(newest);
+      if (kn < bkey) {
+        bkey = kn;
+        bslot = hn;
+      }
+    }
+    final_n = A.B;
+    if (bslot < 0) {
+      if (tid == 0) atomicOr(A.errflag, 2);  // no candidate: impossible when B >= |protected|
+      new_hole = hn;
+    } else {
+      new_hole = bslot;
+    }
+  } else if (A.do_select && n > A.B) {
+    // the selection reads every slot's state back, the new token's included
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int* src = A.mv_src + static_cast<int64_t>(g) * A.cap;
+    int* dst = A.mv_dst + static_cast<int64_t>(g) * A.cap;
+    nm = select_group<NT, true>(n, A.B, newest, A.n_sink, A.n_recent, gp, gs, src, dst, A.errflag, new_hole);
+    final_n = A.B;
+  }
+  if (tid == 0) {
+    A.count[g] = final_n;
+    A.hole[g] = new_hole;
+    A.nmoves[g] = nm;
+  }
+}
+
+hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64_t budget) {
+  const auto& cf = c->cfg;
+  FoldArgs A;
+  A.count = c->d.count;
+  A.hole = c->d.hole;
+  A.pos = c->d.pos;
+  A.score = c->d.score;
+  A.nextpos = c->d.nextpos;
+  A.gmass = c->d.logits;
+  A.grpctr = c->d.grpctr;
+  A.blk_key = c->d.blk_key;
+  A.blk_slot = c->d.blk_slot;
+  A.blk_sum = c->d.blk_sum;
+  A.gnew = c->d.gnew;
+  A.mv_src = c->d.mv_src;
+  A.mv_dst = c->d.mv_dst;
+  A.nmoves = c->d.nmoves;
+  A.errflag = c->d.errflag;
+  const bool dg = refresh && c->d.dg_raw != nullptr;
+  A.dg_n = dg ? c->d.dg_n : nullptr;
+  A.dg_pos = dg ? c->d.dg_pos : nullptr;
+  A.dg_raw = dg ? c->d.dg_raw : nullptr;
+  A.dg_util = dg ? c->d.dg_util : nullptr;
+  A.L = cf.n_layers;
+  A.max_blk = c->max_post_blocks;
+  A.nblk = (n_max + kFoldNT - 1) / kFoldNT;
+  A.cap = c->cap;
+  A.lstride = c->lstride;
+  A.a = cf.alpha_new;
+  A.cumulative = cf.policy == KVEV_CUMULATIVE;
+  A.refresh = refresh;
+  A.do_select = do_select;
+  A.B = static_cast<int>(budget);
+  A.n_sink = cf.n_sink;
+  A.n_recent = cf.n_recent;
+  dim3 grid(A.nblk, c->G);
+  if (cf.n_layers <= 32) return timed_launch(c, "post", fold_kernel<32>, grid, dim3(kFoldNT), 0, A);
+  return timed_launch(c, "post", fold_kernel<kFoldLayers>, grid, dim3(kFoldNT), 0, A);
 }
 
 // Standalone selection (kvev_evict): one block per group, or, in the
@@ -594,7 +870,7 @@ hipError_t launch_set_pages(kvev_ctx* c, const int* upd, int n_upd) {
 
 template <typename T, int D>
 static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                            int refresh, int do_select, int64_t budget) {
+                            int refresh, int do_select, int64_t budget, int seq) {
   constexpr int NT = 256;
   const auto& cf = c->cfg;
   PostArgs A;
@@ -644,6 +920,7 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.cumulative = cf.policy == KVEV_CUMULATIVE;
   A.refresh = refresh;
   A.do_select = do_select;
+  A.seq = 0;
   A.B = static_cast<int>(budget);
   A.n_sink = cf.n_sink;
   A.n_recent = cf.n_recent;
@@ -652,30 +929,29 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   if (c->pooled) {
     // one grid row per sequence: the slot blocks, then one block per (layer, KV head) output
     A.nblk = (n_max + kPoolTokens - 1) / kPoolTokens;
+    ProfScope p(c, "post");
     return launch_pool_post<T, D>(c, A);
   }
-  A.nblk = tok_blocks;  // slot blocks; the L output blocks follow them
-  dim3 grid(A.nblk + cf.n_layers, c->G);
+  A.nblk = tok_blocks;  // slot blocks; the L output blocks follow them (split attention)
+  A.seq = seq;
+  dim3 grid(A.nblk + (seq ? 0 : cf.n_layers), c->G);
   const size_t shm = (static_cast<size_t>(cf.n_layers) * c->HG * 3 + static_cast<size_t>(c->HG) * A.S +
                       static_cast<size_t>(cf.n_layers) * (kPostTok + 1)) * sizeof(float);
   return with_group(c->HG, [&](auto hg) -> hipError_t {
     constexpr int HG = decltype(hg)::value;
-    if (A.part_u || A.vnorm)
-      post_kernel<T, D, HG, NT, true><<<grid, NT, shm, c->stream>>>(A);
-    else
-      post_kernel<T, D, HG, NT, false><<<grid, NT, shm, c->stream>>>(A);
-    return hipGetLastError();
+    if (A.part_u || A.vnorm) return timed_launch(c, "post", post_kernel<T, D, HG, NT, true>, grid, dim3(NT), shm, A);
+    return timed_launch(c, "post", post_kernel<T, D, HG, NT, false>, grid, dim3(NT), shm, A);
   });
 }
 
 hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v_new, int n_max,
-                       int refresh, int do_select, int64_t budget) {
+                       int refresh, int do_select, int64_t budget, int seq) {
   const int D = c->cfg.head_dim;
   if (c->cfg.dtype == KVEV_BF16)
-    return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget)
-                    : post_impl<bf16_t, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget);
-  return D == 128 ? post_impl<float, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget)
-                  : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget);
+    return D == 128 ? post_impl<bf16_t, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, seq)
+                    : post_impl<bf16_t, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, seq);
+  return D == 128 ? post_impl<float, 128>(c, out, k_new, v_new, n_max, refresh, do_select, budget, seq)
+                  : post_impl<float, 64>(c, out, k_new, v_new, n_max, refresh, do_select, budget, seq);
 }
 
 hipError_t launch_close_holes(kvev_ctx* c, int64_t budget) {

@@ -271,6 +271,7 @@ struct PostArgs {
   int64_t cap, P, lstride;
   float a;
   int cumulative, refresh, do_select, B, n_sink, n_recent, nblk;
+  int seq;  // the whole-cache attention wrote the outputs and the per-slot group masses
 };
 
 // HG consecutive fp32 logits (one slot of one layer)

@@ -16,6 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvev.so")
 
 OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
+ATTN_AUTO, ATTN_SPLIT, ATTN_WHOLE = 0, 1, 2
 F32, BF16 = 0, 1
 EMA, CUMULATIVE, LRFU_BLOCK, TIERED_INT2 = 0, 1, 2, 3
 SCORE_VNORM, SCORE_ENTROPY = 1, 2
@@ -55,6 +56,8 @@ class Config(ctypes.Structure):
         ("revival_gap", ctypes.c_int32),
         ("prefetch_blocks", ctypes.c_int32),
         ("offload_min_score", ctypes.c_float),
+        ("attn_path", ctypes.c_int32),
+        ("evict_interval", ctypes.c_int32),
     ]
 
 
@@ -460,7 +463,7 @@ def tier_capacities(b_hist, q, m_f, m_q):
 
 
 def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, offload_blocks=None,
-                revival_gap=None, prefetch_blocks=0, offload_min_score=0.0):
+                revival_gap=None, prefetch_blocks=0, offload_min_score=0.0, attn_path=None):
     """A context configured for a synth.Workload (diag_topk: rank-trace
     diagnostics, default the workload's)."""
     steps = w.steps if max_steps is None else max_steps
@@ -494,5 +497,6 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
         refresh_interval=w.refresh_interval, score_free=1 if w.score_free else 0,
         n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget,
         scorer=_SCORER_BITS[w.scorer], granularity=_GRANULARITY[w.granularity],
-        diag_topk=w.diag_topk if diag_topk is None else diag_topk)
+        diag_topk=w.diag_topk if diag_topk is None else diag_topk,
+        attn_path=w.attn_path if attn_path is None else attn_path, evict_interval=w.evict_interval)
     return Context(cfg, stream=stream)

@@ -60,6 +60,17 @@ def stream_key(*fields: int) -> int:
     return k
 
 
+def stream_keys(*fields) -> np.ndarray:
+    """stream_key over broadcast integer arrays of fields: the same 32-bit
+    chain evaluated elementwise in int64 (identical values)."""
+    arrs = np.broadcast_arrays(*[np.asarray(f, dtype=np.int64) for f in fields])
+    k = np.full(arrs[0].shape, 0x9E3779B9, dtype=np.int64)
+    for f in arrs:
+        k = _mix32_np(k ^ (f & _M32))
+        k = _mix32_np(k + 0x7F4A7C15)
+    return k
+
+
 def _mix32_np(x):
     x = x & _M32
     x = (((x >> 16) ^ x) * 0x45D9F3B) & _M32
@@ -97,6 +108,14 @@ def _rank_channels(key: int, n: int) -> np.ndarray:
     """A key-dependent permutation of range(n) (sorting hashed ids)."""
     h = _mix32_np(_mix32_np(np.arange(n, dtype=np.int64)) ^ key)
     return np.lexsort((np.arange(n), h))
+
+
+def _rank_channels_many(keys, n: int) -> np.ndarray:
+    """_rank_channels for every key of an integer array: [..., n]."""
+    keys = np.asarray(keys, dtype=np.int64)
+    h = _mix32_np(_mix32_np(np.arange(n, dtype=np.int64)) ^ keys[..., None])
+    ids = np.broadcast_to(np.arange(n, dtype=np.int64), h.shape)
+    return np.lexsort((ids, h), axis=-1)
 
 
 @dataclass(frozen=True)
@@ -139,6 +158,8 @@ class Workload:
     diag_topk: int = 0              # token modes: rank-trace diagnostics over the top-k (0: off)
     offload_blocks: int = 0         # block mode: host-offload pool slots (0: off)
     revival_gap: int = 0            # tiered mode: routing diagnostics, sustained-absence length (0: off)
+    attn_path: int = 0              # token modes: attention kernel (0 auto, 1 split, 2 whole-cache)
+    evict_interval: int = 1         # token modes: select only every evict_interval steps
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -180,6 +201,29 @@ class Workload:
         w[perm[half:]] = (signs[perm[half:]] / math.sqrt(half)).astype(np.float32)
         return u, w
 
+    def _structure_many(self, layers, seqs, heads):
+        """(ck, cq) of _structure for broadcast index arrays: [..., d]."""
+        d = self.head_dim
+        out = []
+        for meta in (_META_KOUT, _META_QOUT):
+            top = _rank_channels_many(stream_keys(self.seed, meta, layers, seqs, heads), d)[..., :4]
+            c = np.ones(top.shape[:-1] + (d,), np.float32)
+            np.put_along_axis(c, top, np.float32(8.0), axis=-1)
+            out.append(c)
+        return out[0], out[1]
+
+    def _u_many(self, layers, seqs, heads, epoch):
+        """The u of _directions for broadcast index arrays: [..., d]."""
+        d = self.head_dim
+        half = d // 2
+        perm = _rank_channels_many(stream_keys(self.seed, _META_U, layers, seqs, heads, epoch), d)
+        sk = stream_keys(self.seed, _META_U + 100, layers, seqs, heads, epoch)
+        signs = np.where(_mix32_np(np.arange(d, dtype=np.int64) ^ sk[..., None]) & 1, 1.0, -1.0)
+        vals = (np.take_along_axis(signs, perm[..., :half], axis=-1) / math.sqrt(half)).astype(np.float32)
+        u = np.zeros(perm.shape, np.float32)
+        np.put_along_axis(u, perm[..., :half], vals, axis=-1)
+        return u
+
     def _norm_c(self):
         return math.sqrt((self.head_dim - 4) + 4 * 64.0)
 
@@ -218,6 +262,23 @@ class Workload:
             u, w = self._directions(layer, seq, kvh, e)
             rows[e] = (np.float32(nc * 0.6) * u + np.float32(nc * 0.8) * w).astype(np.float32)
         return pos, np.stack([rows[owner[p]] for p in pos.tolist()])
+
+    def _heavy_rows_at(self, layer, seq, kvh, pos):
+        """(indices into pos, rows) of the requested positions that hold a
+        heavy key, each with the latest owning epoch's row: the rows of
+        _heavy_rows restricted to pos, with directions computed only for
+        the epochs that own one of them."""
+        pos = np.asarray(pos, dtype=np.int64)
+        owner = np.full(len(pos), -1, dtype=np.int64)
+        for e in range(self.n_epochs):
+            owner[np.isin(pos, self.heavy_positions(layer, seq, kvh, e))] = e
+        hit = np.flatnonzero(owner >= 0)
+        rows = np.zeros((len(hit), self.head_dim), np.float32)
+        nc = self._norm_c()
+        for e in np.unique(owner[hit]).tolist():
+            u, w = self._directions(layer, seq, kvh, e)
+            rows[owner[hit] == e] = (np.float32(nc * 0.6) * u + np.float32(nc * 0.8) * w).astype(np.float32)
+        return hit, rows
 
     def region_labels(self, seq):
         """uint8 region id of every prefill position (contiguous spans)."""
@@ -294,12 +355,9 @@ class Workload:
                 if self.structured:
                     ck, _ = self._structure(l, seq, h)
                     k = k * torch.from_numpy(ck).to(device)
-                    hp, rows = self._heavy_rows(l, seq, h)
-                    where = np.searchsorted(hp, pos)
-                    hit = np.flatnonzero((where < len(hp)) & (hp[np.minimum(where, len(hp) - 1)] == pos)) \
-                        if len(hp) else np.zeros(0, np.int64)
+                    hit, rows = self._heavy_rows_at(l, seq, h, pos)
                     if len(hit):
-                        k[torch.from_numpy(hit).to(device)] = torch.from_numpy(rows[where[hit]]).to(device)
+                        k[torch.from_numpy(hit).to(device)] = torch.from_numpy(rows).to(device)
                 kh.append(self._round(k))
                 vh.append(self._round(v))
             Ks.append(torch.stack(kh))
@@ -317,12 +375,11 @@ class Workload:
             mu_u = np.zeros((L, len(seqs), Hkv, d), np.float32)
             if self.structured:
                 mu = np.float32(self._norm_c() / 4.0)
-                for l in range(L):
-                    for bi, b in enumerate(seqs):
-                        for h in range(Hkv):
-                            ck[l, bi, h], cq[l, bi, h] = self._structure(l, b, h)
-                            u, _ = self._directions(l, b, h, epoch)
-                            mu_u[l, bi, h] = (mu * u).astype(np.float32)
+                lg = np.arange(L, dtype=np.int64)[:, None, None]
+                bg = np.asarray(seqs, dtype=np.int64)[None, :, None]
+                hg = np.arange(Hkv, dtype=np.int64)[None, None, :]
+                ck, cq = self._structure_many(lg, bg, hg)
+                mu_u = (mu * self._u_many(lg, bg, hg, epoch)).astype(np.float32)
             cache[key] = (ck, cq, mu_u)
         return cache[key]
 
@@ -333,10 +390,12 @@ class Workload:
         L, d, Hkv, Hg = self.n_layers, self.head_dim, self.n_kv_heads, self.group_size
         nb = len(seqs)
 
+        lg = np.arange(L, dtype=np.int64)[:, None, None]
+        bg = np.asarray(seqs, dtype=np.int64)[None, :, None]
+        hg = np.arange(Hkv, dtype=np.int64)[None, None, :]
+
         def keys(kind):
-            k = [[[stream_key(self.seed, kind, l, b, h, t) for h in range(Hkv)]
-                  for b in seqs] for l in range(L)]
-            return torch.tensor(k, dtype=torch.int64, device=device)
+            return torch.from_numpy(stream_keys(self.seed, kind, lg, bg, hg, t)).to(device)
 
         table = _normal_table(device)
         idx_kv = _mix32_t(torch.arange(d, dtype=torch.int64, device=device))
@@ -386,6 +445,10 @@ def workload(name: str) -> Workload:
     if name == "lazy16x8k":
         return Workload("batch16_8k_25pct_lazy8", 32, 32, 8, 128, "bf16", (8192,) * 16, 512,
                         seed=1003, alpha_new=0.05, budget=2048, refresh_interval=8)
+    if name == "lazy16x8k_evict8":
+        # the batched lazy workload's wording taken literally: scores recomputed and the cache
+        # evicted every 8 steps (it grows to the budget + 7 in between)
+        return replace(workload("lazy16x8k"), name="batch16_8k_25pct_lazy8_evict8", evict_interval=8)
     if name == "scorefree16x8k":
         return Workload("batch16_8k_25pct_scorefree", 32, 32, 8, 128, "bf16", (8192,) * 16, 512,
                         seed=1003, alpha_new=0.05, budget=2048, score_free=True, n_recent=32)
@@ -415,4 +478,4 @@ def workload(name: str) -> Workload:
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
              "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8",
-             "llama8b_32k_diag", "lrfu64_offload")
+             "llama8b_32k_diag", "lrfu64_offload", "lazy16x8k_evict8")

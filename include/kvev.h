@@ -200,7 +200,27 @@ typedef struct {
    * (the graded offload / drop rule of "MemDecay" section III-E; 0: every
    * evicted block is offloaded). */
   float offload_min_score;
+  /* Token policies, bf16 and head_dim 128: which attention kernel runs (a
+   * kvev_attn_path).  AUTO: the whole-cache kernel (one workgroup per (KV
+   * head group, layer) over every retained slot; it writes the outputs and
+   * each slot's group mass directly) when there are at least 224 (group,
+   * layer) pairs, the step's slot count fits its bound (8,192 slots and the
+   * logits in the workgroup's LDS) and neither a scorer variant nor
+   * per-sequence granularity is set; the split kernel otherwise.  SPLIT:
+   * always the split kernel.  WHOLE: the whole-cache kernel whenever it
+   * applies, whatever the pair count.  Results agree within the
+   * tolerances; each path is deterministic. */
+  int32_t attn_path;
+  /* Token policies: kvev_step selects only after the steps t (counted from
+   * 1) with (t - 1) % evict_interval == 0, and in between only appends, so
+   * the cache grows to budget + evict_interval - 1 tokens.  This is the
+   * literal reading of the batched lazy workload's "recompute scores and
+   * evict every 8 steps"; 0 or 1: every step ("What Matters ...", section
+   * 3.2 evicts every step).  kvev_evict always selects. */
+  int32_t evict_interval;
 } kvev_config;
+
+typedef enum { KVEV_ATTN_AUTO = 0, KVEV_ATTN_SPLIT = 1, KVEV_ATTN_WHOLE = 2 } kvev_attn_path;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
  * refresh_interval 1, no protection, window_tokens 32; shape fields zero. */
@@ -293,8 +313,14 @@ kvev_status kvev_export_kv(kvev_ctx* ctx, int32_t seq, int32_t kv_head, void* k_
 
 /* Replace the state of group (seq, kv_head): n tokens with host `positions`
  * and host `scores` (slot order), and device k, v [n_layers][n][head_dim].
- * Used to put both sides of a comparison on the same state.
- * Errors: KVEV_EINVAL / KVEV_ERANGE (n > capacity), KVEV_ENOMEM. */
+ * Used to put both sides of a comparison on the same state.  With
+ * granularity KVEV_PER_SEQUENCE every KV head of the sequence holds the same
+ * slots: the caller imports each of them with the same positions (and
+ * scores), and kvev_decode_step / kvev_step / kvev_evict return KVEV_ESTATE
+ * until the sequence's last KV head is imported.
+ * Errors: KVEV_EINVAL (different positions for another KV head of a
+ * per-sequence context) / KVEV_ERANGE (n > capacity), KVEV_ENOMEM,
+ * KVEV_ESTATE (diagnostics on). */
 kvev_status kvev_import_group(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int64_t n,
                               const int32_t* positions, const float* scores,
                               const void* k, const void* v);
@@ -513,9 +539,13 @@ int64_t kvev_step_index(const kvev_ctx* ctx);
 
 /* Kernel timing, measured with HIP events recorded on the context's stream
  * around every launch of the named kernel while enabled.  `kernel`:
- * "attn" (append + split attention), "post" (split merge, probability pass,
- * fold, and in kvev_step selection + compaction), "select" and "move"
- * (kvev_evict; "move" also in kvev_step when many slots move).  LRFU_BLOCK
+ * "attn" (append + split attention), "attn_whole" (append + whole-cache
+ * attention with the probability pass), "post" (split merge, probability
+ * pass, fold, and in kvev_step selection + compaction), "select" and "move"
+ * (kvev_evict; "move" also in kvev_step when many slots move).  The token
+ * policies' "attn", "attn_whole" and "post" launches record their own
+ * dispatch start and end (no event packets between the step's kernels);
+ * every other name is timed by events recorded around its launches.  LRFU_BLOCK
  * mode: "open" (slot and block of the new token), "attn", "merge" (split
  * merge and output), "mass" (block mass), "policy" (score, clock, priority,
  * selection, table compaction), "readmit".  TIERED_INT2 mode: "append",

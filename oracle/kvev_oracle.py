@@ -516,7 +516,7 @@ def future_missed_mass(full_positions, full_raw, evicted):
 @dataclass
 class _Group:
     """State of one (sequence, KV head) selection group, in slot order."""
-    K: np.ndarray          # [L, cap, d] float32 (exact copies of the inputs)
+    K: np.ndarray          # [L, cap, d] float64 (exact widenings of the inputs)
     V: np.ndarray          # [L, cap, d]
     pos: np.ndarray        # [cap] int64
     m: np.ndarray          # [cap] float64 utility
@@ -545,6 +545,10 @@ class TokenModeOracle:
     * Eviction happens once per step after all layers, whenever the group
       holds more than ``budget`` tokens, including non-refresh steps with
       the stale utility ([InertiaKV] App. E "Eviction on non-refresh steps").
+      ``evict_interval`` e > 1 takes the batched workload's wording "recompute
+      scores and evict every 8 steps" literally: the caller selects only on
+      the steps ``is_evict_step`` names, t in {1, 1 + e, 1 + 2e, ...}, and
+      the cache grows by one token per step in between.
     * ``scorer``: the observation folded per layer, see ``scored_mass``.
     """
     n_layers: int
@@ -560,6 +564,7 @@ class TokenModeOracle:
     n_recent: int = 0
     capacity: int = 0
     scorer: str = "attention"
+    evict_interval: int = 1
     groups: dict = field(default_factory=dict)
     prefill_len: dict = field(default_factory=dict)
     last_G: dict = field(default_factory=dict)
@@ -582,8 +587,8 @@ class TokenModeOracle:
         heads = list(range(nh)) if heads is None else list(heads)
         cap = max(self.capacity, n + 1)
         for j, h in enumerate(heads):
-            g = _Group(K=np.zeros((L, cap, d), np.float32),
-                       V=np.zeros((L, cap, d), np.float32),
+            g = _Group(K=np.zeros((L, cap, d), np.float64),
+                       V=np.zeros((L, cap, d), np.float64),
                        pos=np.zeros(cap, np.int64), m=np.zeros(cap, np.float64))
             g.K[:, :n] = K[:, j]
             g.V[:, :n] = V[:, j]
@@ -596,6 +601,10 @@ class TokenModeOracle:
         if self.score_free:
             return t == 1
         return (t - 1) % self.refresh_interval == 0
+
+    def is_evict_step(self, t):
+        """Whether step t selects (every step unless evict_interval > 1)."""
+        return (t - 1) % max(self.evict_interval, 1) == 0
 
     def _grow(self, g):
         if g.n < g.K.shape[1]:
@@ -688,8 +697,8 @@ class _SeqState:
     """State of one sequence in the pooled mode, in slot order."""
 
     def __init__(self, L, Hkv, cap, d):
-        self.K = np.zeros((L, Hkv, cap, d), np.float32)
-        self.V = np.zeros((L, Hkv, cap, d), np.float32)
+        self.K = np.zeros((L, Hkv, cap, d), np.float64)
+        self.V = np.zeros((L, Hkv, cap, d), np.float64)
         self.pos = np.zeros(cap, np.int64)
         self.m = np.zeros(cap, np.float64)
         self.n = 0
@@ -883,7 +892,7 @@ def select_blocks(ids, prio, pinned, budget):
 @dataclass
 class _BlockSeq:
     """One sequence of the block-granular mode, indexed by position."""
-    K: np.ndarray            # [L, Hkv, cap, d] float32 (exact copies of inputs)
+    K: np.ndarray            # [L, Hkv, cap, d] float64 (exact widenings of the inputs)
     V: np.ndarray
     labels: list             # region id of every position so far
     npos: int                # positions 0 .. npos-1 exist
@@ -953,7 +962,7 @@ class BlockLRFUOracle:
         V = np.asarray(V, dtype=np.float32)
         L, H, n, d = K.shape
         cap = max(self.capacity, n + 1)
-        s = _BlockSeq(K=np.zeros((L, H, cap, d), np.float32), V=np.zeros((L, H, cap, d), np.float32),
+        s = _BlockSeq(K=np.zeros((L, H, cap, d), np.float64), V=np.zeros((L, H, cap, d), np.float64),
                       labels=[int(x) for x in labels], npos=n, budget=int(budget))
         if len(s.labels) != n:
             raise ValueError("one region label per prefill token")
@@ -1190,7 +1199,8 @@ class _TierLayer:
     """One layer's windows: FP storage, ledger, tier and cumulative score."""
     K: np.ndarray            # [Hkv, cap, d] fp32: full-precision values by position
     V: np.ndarray
-    Keff: np.ndarray         # [Hkv, cap, d] fp32: what attention reads (FP or INT2 reconstruction)
+    Keff: np.ndarray         # [Hkv, cap, d] fp64 holding fp32 values: what attention reads
+                             # (full precision or the INT2 reconstruction)
     Veff: np.ndarray
     tier: dict = field(default_factory=dict)     # window -> "F" | "Q" | "E"
     S: dict = field(default_factory=dict)        # window -> cumulative score (fp64)
@@ -1268,7 +1278,7 @@ class TieredOracle:
         cap = max(self.capacity, n + 1)
         for j, l in enumerate(layers):
             st = _TierLayer(K=np.zeros((H, cap, d), np.float32), V=np.zeros((H, cap, d), np.float32),
-                            Keff=np.zeros((H, cap, d), np.float32), Veff=np.zeros((H, cap, d), np.float32))
+                            Keff=np.zeros((H, cap, d), np.float64), Veff=np.zeros((H, cap, d), np.float64))
             for arr in (st.K, st.Keff):
                 arr[:, :n] = K[j]
             for arr in (st.V, st.Veff):
@@ -1382,7 +1392,8 @@ class TieredOracle:
             for w in Q:
                 if w not in st.ledger:                   # first demotion: quantize once
                     self._quantize_window(st, w)
-                self._reconstruct(st, w)
+                if st.tier[w] != "Q":                    # entering INT2: attention reads the reconstruction
+                    self._reconstruct(st, w)
                 st.tier[w] = "Q"
             for w in F:
                 if st.tier[w] == "Q":                    # promotion: dequantize into bf16 storage

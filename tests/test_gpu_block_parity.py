@@ -114,17 +114,6 @@ def test_readmit_rejects_resident_and_unknown_blocks():
     ctx.close()
 
 
-def test_full_size_lrfu64_sampled():
-    """The full 64-sequence workload (lengths 4k-16k, 32 layers, 8 KV heads,
-    20% block budgets) in the benchmark's launch configuration; the oracle
-    follows the shortest sequence through the first steps, including the
-    first step's eviction of 80% of its blocks."""
-    w = synth.workload("lrfu64")
-    b = int(np.argmin(w.prefill_lens))
-    st = _gu().run_block_lockstep(w, 3, sample_seqs=[b], readmit=False, kv_every=3)
-    assert st.steps == 3
-
-
 def test_block_max_positions_sampled():
     """One sequence of 65,520 tokens (4,095 blocks, 20% budget of 819) stepped
     toward the mode's 65,536-position bound, 4 layers, oracle on the whole

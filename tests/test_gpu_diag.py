@@ -26,10 +26,17 @@ def test_diag_tiny_fp32_top_budget():
     assert last["k"] == w.budget and last["retained"] == w.budget
 
 
-def test_diag_llama_shape_topk_below_budget():
-    """Matrix-core path, 3 layers, protected sinks and recent tokens, k < B."""
-    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209)
+@pytest.mark.parametrize("path", [1, 2])
+def test_diag_llama_shape_topk_below_budget(path):
+    """Matrix-core path (split and whole-cache attention), 3 layers,
+    protected sinks and recent tokens, k < B."""
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209, attn_path=path)
     _gu().run_diag_lockstep(w, 24, 50)
+
+
+def test_diag_group7_whole_cache_attention():
+    w = synth.workload("qwen7b_32k").scaled(n_layers=2, prefill_lens=(700, 1300), budget=150, attn_path=2)
+    _gu().run_diag_lockstep(w, 16, 37)
 
 
 def test_diag_group7_ragged_batch():

@@ -59,17 +59,6 @@ def test_tier_large_int2_share():
     assert st.steps == 32
 
 
-def test_qevict131k_full_size_sampled():
-    """The full 32-layer, 131,072-token workload (205 full-precision and 819
-    INT2 windows per layer, 5 sinks, 32 recent) in the benchmark's launch
-    configuration; the oracle holds layers 0 and 31.  34 steps: the first
-    routing event over 4,094 candidates, the first aged-out window at step
-    32 and the first heavy-key re-targeting at step 33."""
-    w = synth.workload("qevict131k")
-    st = _gu().run_tier_lockstep(w, 34, sample_layers=[0, 31], kv_every=16, ledger_every=16)
-    assert st.steps == 34 and st.ledger_checks > 0
-
-
 def test_tier_max_capacity_sampled():
     """A 196,600-token prefill stepped to the mode's 196,608-position capacity
     (6,144 windows per layer, the routing kernel's LDS bound), 4 layers; the

@@ -41,23 +41,27 @@ def test_tiny_fp32_fused_step():
     assert st.steps == 64
 
 
-def test_llama_shape_fused_step():
-    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209)
+@pytest.mark.parametrize("path", [1, 2])
+def test_llama_shape_fused_step(path):
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209, attn_path=path)
     _gu().run_token_lockstep(w, 40, fused=True)
 
 
-def test_lazy_fused_step():
-    w = synth.workload("lazy16x8k").scaled(n_layers=2, prefill_lens=(1000, 1000, 1000), budget=250)
+@pytest.mark.parametrize("path", [1, 2])
+def test_lazy_fused_step(path):
+    w = synth.workload("lazy16x8k").scaled(n_layers=2, prefill_lens=(1000, 1000, 1000), budget=250,
+                                           attn_path=path)
     _gu().run_token_lockstep(w, 20, fused=True)
 
 
-def test_fused_step_bitwise_equals_separate_calls():
+@pytest.mark.parametrize("path", [1, 2])
+def test_fused_step_bitwise_equals_separate_calls(path):
     """kvev_step == kvev_decode_step + kvev_evict, bit for bit (outputs,
     utilities, slot layout and cached K/V), including the first step's
     large compaction and many single-eviction steps."""
     import torch
     from decode_kv_cache_gqa_amd import kvev
-    w = synth.workload("llama8b_32k").scaled(n_layers=4, prefill_lens=(5000,), budget=500)
+    w = synth.workload("llama8b_32k").scaled(n_layers=4, prefill_lens=(5000,), budget=500, attn_path=path)
     ctxs = [kvev.context_for(w, max_steps=24) for _ in range(2)]
     K, V = w.prefill_kv(0, device="cuda")
     for c in ctxs:
@@ -81,53 +85,63 @@ def test_fused_step_bitwise_equals_separate_calls():
         c.close()
 
 
-def test_llama_shape_scaled_ragged():
+@pytest.mark.parametrize("path", [1, 2])
+def test_llama_shape_scaled_ragged(path):
     """Llama-8B head shape, bf16, 3 layers, ragged prefill, 4 sinks + 32 recent."""
-    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209)
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(2083,), budget=209,
+                                             attn_path=path)
     st = _gu().run_token_lockstep(w, 40)
     assert st.steps == 40
 
 
-def test_cumulative_policy():
+@pytest.mark.parametrize("path", [1, 2])
+def test_cumulative_policy(path):
     w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(700,), budget=100,
-                                             policy="cumulative")
+                                             policy="cumulative", attn_path=path)
     _gu().run_token_lockstep(w, 12)
 
 
-def test_lazy_refresh_batch():
+@pytest.mark.parametrize("path", [1, 2])
+def test_lazy_refresh_batch(path):
     """Batched lazy refresh (r=8), no protection, 3 sequences of a ragged length."""
-    w = synth.workload("lazy16x8k").scaled(n_layers=2, prefill_lens=(1000, 1000, 1000), budget=250)
+    w = synth.workload("lazy16x8k").scaled(n_layers=2, prefill_lens=(1000, 1000, 1000), budget=250,
+                                           attn_path=path)
     _gu().run_token_lockstep(w, 20, sample_seqs=[0, 2])
 
 
-def test_score_free_batch():
-    w = synth.workload("scorefree16x8k").scaled(n_layers=2, prefill_lens=(900, 900), budget=240)
+@pytest.mark.parametrize("path", [1, 2])
+def test_score_free_batch(path):
+    w = synth.workload("scorefree16x8k").scaled(n_layers=2, prefill_lens=(900, 900), budget=240,
+                                                attn_path=path)
     _gu().run_token_lockstep(w, 20)
 
 
-def test_edge_budget_not_binding_and_tiny_prefill():
+@pytest.mark.parametrize("path", [1, 2])
+def test_edge_budget_not_binding_and_tiny_prefill(path):
     # prefill of 1 token, budget larger than the cache: evict is a no-op
     w = synth.workload("llama8b_32k").scaled(n_layers=1, prefill_lens=(1, 17), budget=40,
-                                             n_sink=1, n_recent=2)
+                                             n_sink=1, n_recent=2, attn_path=path)
     _gu().run_token_lockstep(w, 30)
 
 
-def test_capacity_not_multiple_of_16_filled():
+@pytest.mark.parametrize("path", [1, 2])
+def test_capacity_not_multiple_of_16_filled(path):
     """The budget never binds and the slot capacity (prefill + steps + 1 = 45)
     is not a multiple of 16: on the last steps the logit rows, whose stride is
     the slot count rounded up to 16 (48), must stay inside their buffer."""
     w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(20,), budget=100,
-                                             n_sink=1, n_recent=2)
+                                             n_sink=1, n_recent=2, attn_path=path)
     _gu().run_token_lockstep(w, 24)
 
 
-def test_equal_scores_resolved_by_position():
+@pytest.mark.parametrize("path", [1, 2])
+def test_equal_scores_resolved_by_position(path):
     """All-zero keys give every token the same logits, so utilities tie
     exactly; the cut must fall by position (more recent kept)."""
     import torch
     from decode_kv_cache_gqa_amd import kvev
     w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(300,), budget=50,
-                                             n_sink=0, n_recent=0)
+                                             n_sink=0, n_recent=0, attn_path=path)
     ctx = kvev.context_for(w, max_steps=4)
     K, V = w.prefill_kv(0, device="cuda")
     ctx.prefill(0, torch.zeros_like(K), V.contiguous())
@@ -143,10 +157,12 @@ def test_equal_scores_resolved_by_position():
     ctx.close()
 
 
-def test_determinism_bitwise():
+@pytest.mark.parametrize("path", [1, 2])
+def test_determinism_bitwise(path):
     import torch
     from decode_kv_cache_gqa_amd import kvev
-    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(1500,), budget=150)
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(1500,), budget=150,
+                                             attn_path=path)
     runs = []
     for _ in range(2):
         ctx = kvev.context_for(w, max_steps=6)
@@ -168,49 +184,15 @@ def test_determinism_bitwise():
         np.testing.assert_array_equal(a, b)
 
 
-def test_llama8b_32k_full_size_sampled():
-    """The full 32-layer, 32,768-token workload in the benchmark's launch
-    configuration; the oracle follows two sampled KV-head groups."""
-    w = synth.workload("llama8b_32k")
-    st = _gu().run_token_lockstep(w, 6, sample_heads=[0, 5], kv_every=3, ctx_steps=w.steps)
-    assert st.steps == 6
-
-
-def test_lazy16x8k_full_size_sampled():
-    """The full batched lazy workload (16 sequences, 8,192-token prefill, 32
-    layers, budget 2,048, observations at t = 1, 9, 17, ...) in the
-    benchmark's launch configuration; the oracle follows two sequences' first
-    and last KV heads through the first eviction, the unobserved steps and
-    the observation at t = 9."""
-    w = synth.workload("lazy16x8k")
-    st = _gu().run_token_lockstep(w, 10, sample_seqs=[0, 15], sample_heads=[0, 7], kv_every=5,
-                                  ctx_steps=w.steps, fused=True)
-    assert st.steps == 10
-
-
-def test_scorefree16x8k_full_size_sampled():
-    """The full batched score-free workload (scores observed at t = 1 only,
-    new tokens take the mean) in the benchmark's launch configuration."""
-    w = synth.workload("scorefree16x8k")
-    st = _gu().run_token_lockstep(w, 6, sample_seqs=[7], sample_heads=[3], kv_every=3, ctx_steps=w.steps,
-                                  fused=True)
-    assert st.steps == 6
-
-
-def test_llama8b_32k_full_size_fused_sampled():
-    w = synth.workload("llama8b_32k")
-    st = _gu().run_token_lockstep(w, 6, sample_heads=[3], kv_every=3, ctx_steps=w.steps, fused=True)
-    assert st.steps == 6
-
-
 # --- query group sizes other than 4 ----------------------------------------------
 
+@pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 8), (20, 4), (30, 5), (28, 4), (32, 4)])
-def test_group_sizes_matrix_core_path(hq, hkv):
+def test_group_sizes_matrix_core_path(hq, hkv, path):
     """bf16, head_dim 128 (matrix-core kernel) with 1..8 query heads per KV
     head; (28, 4) is the Qwen2.5-7B attention shape."""
     w = synth.workload("llama8b_32k").scaled(n_layers=2, n_q_heads=hq, n_kv_heads=hkv,
-                                             prefill_lens=(700, 433), budget=120)
+                                             prefill_lens=(700, 433), budget=120, attn_path=path)
     _gu().run_token_lockstep(w, 12)
 
 
@@ -251,8 +233,9 @@ def test_scorers_fused_step():
     _gu().run_token_lockstep(w, 12, fused=True)
 
 
+@pytest.mark.parametrize("path", [1, 2])
 @pytest.mark.parametrize("fused", [True, False])
-def test_smaller_budget_after_single_token_evictions(fused):
+def test_smaller_budget_after_single_token_evictions(fused, path):
     """A single-token eviction leaves its slot free inside the cache (the
     next token takes it).  A later kvev_evict with a smaller budget first
     moves the last token into that slot, then selects; the result must match
@@ -262,7 +245,7 @@ def test_smaller_budget_after_single_token_evictions(fused):
     from decode_kv_cache_gqa_amd import kvev
     gu = _gu()
     w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(500,), budget=120,
-                                             n_sink=2, n_recent=6)
+                                             n_sink=2, n_recent=6, attn_path=path)
     ctx = kvev.context_for(w, max_steps=16)
     o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=120,
                             alpha_new=w.alpha_new, n_sink=2, n_recent=6, capacity=520)
@@ -305,5 +288,47 @@ def test_smaller_budget_after_single_token_evictions(fused):
     for t in range(7, 12):
         step(t, 100)
     compare("after further steps")
+    ctx.sync()
+    ctx.close()
+
+
+def test_single_step_rule_alpha_one():
+    """alpha_new = 1, the single-step rule ("What Matters ...", section 3.1
+    Eq.2): every observation replaces the utility, so after a step's
+    layer-sequential fold a token's utility is the last layer's group mass
+    and the retained set is the top budget of that mass.  Checked in
+    lockstep with the oracle over 12 steps, and on the library's own values:
+    the utilities of the first step equal the oracle's last-layer group mass
+    and the selection keeps the top budget of them."""
+    import torch
+    import oracle as orc
+    from decode_kv_cache_gqa_amd import kvev
+    gu = _gu()
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(1200,), budget=150, alpha_new=1.0)
+    gu.run_token_lockstep(w, 12)
+    gu.run_token_lockstep(w, 12, fused=True)
+    ctx = kvev.context_for(w, max_steps=2)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    o = orc.TokenModeOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=w.budget,
+                            alpha_new=1.0, n_sink=w.n_sink, n_recent=w.n_recent, capacity=1300)
+    o.prefill(0, K.float().cpu().numpy(), V.float().cpu().numpy())
+    q, kn, vn = w.step_inputs(1, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ctx.decode_step(q, kn, vn, out)
+    o.decode_step(1, q.float().cpu().numpy(), kn.float().cpu().numpy(), vn.float().cpu().numpy(), [0])
+    pre = {}
+    for h in range(w.n_kv_heads):
+        gp, gs = ctx.retained(0, h), ctx.scores(0, h)
+        gps, gss = gu.by_position(gp, gs)
+        last = o.last_G[(w.n_layers - 1, 0, h)]  # oracle slot order = position order before any eviction
+        np.testing.assert_array_equal(gps, o.positions(0, h))
+        gu.check_scores(gss, last, 2e-3, f"kvh={h}: utility vs the last layer's mass")
+        pre[h] = (gs, gp)
+    ctx.evict()
+    for h in range(w.n_kv_heads):
+        gs, gp = pre[h]
+        np.testing.assert_array_equal(np.sort(ctx.retained(0, h)),
+                                      gu.expected_after_evict(gs, gp, w.budget, w.n_sink, w.n_recent))
     ctx.sync()
     ctx.close()
