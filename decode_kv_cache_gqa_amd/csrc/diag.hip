@@ -17,6 +17,9 @@
 // Every per-position stamp array has one entry per position a sequence can
 // reach, so nothing is cleared between steps.
 #include "post_common.h"
+#include "host_util.h"
+
+#include <mutex>
 
 namespace kvev {
 
@@ -381,5 +384,57 @@ hipError_t launch_fmm(kvev_ctx* full, kvev_ctx* comp, double* fmm_dev) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Missed mass without any allocation, for callers that cannot allocate
+// (graph capture, serving loops): the per-group results are staged in a
+// file-scope device array of kFmmScratchGroups doubles (32 KiB), which each
+// GPU holds until the process ends.  Host code never passes the array's name
+// to a kernel or a copy: it uses the device address that hipGetSymbolAddress
+// returns, fetched once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr int kFmmScratchGroups = 4096;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) double scratch[kFmmScratchGroups];
+
+static std::mutex g_scratch_mu;
+static double* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `device` (the current device).
+static hipError_t scratch_address(int device, double** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[device] = static_cast<double*>(p);
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
 }  // namespace kvev
 
+using namespace kvev;
+
+extern "C" kvev_status kvev_diag_fmm_noalloc(kvev_ctx* full, kvev_ctx* comp, double* fmm) {
+  KVEV_LIVE(full);
+  KVEV_LIVE(comp);
+  if (kvev_status s = fmm_check(full, comp, fmm)) return s;
+  if (comp->G > kFmmScratchGroups)
+    return fail(comp, KVEV_ERANGE, "more groups than the missed-mass scratch holds (4096)");
+  int cur = -1;
+  KVEV_HIP(comp, hipGetDevice(&cur));
+  if (cur != comp->device || cur != full->device)
+    return fail(comp, KVEV_EINVAL, "call with the contexts' device current");
+  double* dev = nullptr;
+  KVEV_HIP(comp, scratch_address(cur, &dev));
+  // the full context's step must be complete before its per-token values
+  // are read on the compressed context's stream (no event: nothing allocated)
+  KVEV_HIP(comp, hipStreamSynchronize(full->stream));
+  // every group's entry g < G is written by its own block: nothing to clear
+  KVEV_HIP(comp, launch_fmm(full, comp, dev));
+  KVEV_HIP(comp, hipMemcpyAsync(fmm, dev, sizeof(double) * comp->G, hipMemcpyDeviceToHost, comp->stream));
+  KVEV_HIP(comp, hipStreamSynchronize(comp->stream));
+  return KVEV_OK;
+}

@@ -131,6 +131,7 @@ _SIGS = {
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.POINTER(ctypes.c_int64)]),
     "kvev_diag_fmm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
+    "kvev_diag_fmm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
     "kvev_tier_diag": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(RouteDiag)]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
@@ -448,6 +449,15 @@ def diag_fmm(full, compressed):
     G = compressed.cfg.batch * compressed.cfg.n_kv_heads
     out = (ctypes.c_double * G)()
     compressed._check(lib().kvev_diag_fmm(full._h, compressed._h, out))
+    return np.array(list(out), dtype=np.float64)
+
+
+def diag_fmm_noalloc(full, compressed):
+    """As diag_fmm, through the library's allocation-free entry point
+    kvev_diag_fmm_noalloc (its staging buffer is a fixed device array)."""
+    G = compressed.cfg.batch * compressed.cfg.n_kv_heads
+    out = (ctypes.c_double * G)()
+    compressed._check(lib().kvev_diag_fmm_noalloc(full._h, compressed._h, out))
     return np.array(list(out), dtype=np.float64)
 
 

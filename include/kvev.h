@@ -389,6 +389,18 @@ kvev_status kvev_diag_trace(kvev_ctx* ctx, int32_t seq, int32_t kv_head, int32_t
  * KVEV_ESTATE (diagnostics off, no step yet). */
 kvev_status kvev_diag_fmm(kvev_ctx* full, kvev_ctx* compressed, double* fmm);
 
+/* kvev_diag_fmm for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): same
+ * arguments, checks and result, but nothing is allocated.  The per-group
+ * results are staged in a fixed device array of 4,096 doubles (32 KiB) that
+ * each GPU the library runs on holds until the process ends; instead of an
+ * event, the call synchronises `full`'s stream before launching on
+ * `compressed`'s.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (from several threads) race.  The current device
+ * must be the contexts' device.  Errors: as kvev_diag_fmm, and KVEV_ERANGE
+ * (more than 4,096 groups), KVEV_EINVAL (another device current). */
+kvev_status kvev_diag_fmm_noalloc(kvev_ctx* full, kvev_ctx* compressed, double* fmm);
+
 /* ---- KVEV_LRFU_BLOCK mode ---------------------------------------------- */
 
 /* Set the retained-block budget of sequence `seq` (used by kvev_step and
