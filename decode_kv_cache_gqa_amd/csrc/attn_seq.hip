@@ -88,7 +88,7 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
                                          const uint32_t (&vnew)[8], int page0,
                                          uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, int l,
                                          int r16, int q4, int64_t P, bool head, const bf16x8s (&qb)[4],
-                                         float scale, float* s_lg, int nstride, f32x4s (&oacc)[8],
+                                         float scale, float* s_lg, float* s_mc, int nstride, f32x4s (&oacc)[8],
                                          float& m_run, float& l_run) {
   constexpr int D = 128;
   // append: the new token replaces the free slot's stale contents (per-lane
@@ -127,9 +127,6 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
       const int t = 32 * c + 16 * j + 4 * q4 + i;
       sv[j][i] = (head && t < n) ? acc[i] * scale : -INFINITY;
     }
-    if (OBS && head)
-      *reinterpret_cast<float4*>(&s_lg[r16 * nstride + 32 * c + 16 * j + 4 * q4]) =
-          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
   }
   // online softmax (the four lane quarters of a head hold its 32 slots)
   float mc = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
@@ -149,6 +146,15 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
     }
   l_run = l_run * alpha + psum;
   m_run = m_new;
+  if (OBS && head) {
+    // the chunk's probabilities relative to its running maximum, and that
+    // maximum: the probability pass rescales them once M and Z are known
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<float4*>(&s_lg[r16 * nstride + 32 * c + 16 * j + 4 * q4]) =
+          make_float4(sv[j][0], sv[j][1], sv[j][2], sv[j][3]);
+    if (q4 == 0) s_mc[c * HG + r16] = m_new;
+  }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -173,6 +179,18 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
   }
 }
 
+// A head's overall maximum M and normaliser Z from the waves' (m, l).
+template <int NW, int HG>
+__device__ __forceinline__ void head_stats(const float (&wm)[NW][HG], const float (&wl)[NW][HG], int h, float& M,
+                                           float& Z) {
+  M = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) M = fmaxf(M, wm[x][h]);
+  Z = 0.f;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) Z += wm[x][h] == -INFINITY ? 0.f : wl[x][h] * __expf(wm[x][h] - M);
+}
+
 template <int NW, int HG, bool OBS>
 __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
@@ -183,10 +201,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   static_assert(HG >= 1 && HG <= 8, "group size");
   constexpr int D = 128, NT = NW * kWave;
   extern __shared__ float dyn[];
-  float* s_lg = dyn;                                 // [HG][nstride] logits (observation steps)
-  float* o_m = dyn + (OBS ? HG * nstride : 0);       // [NW][HG][D] per-wave outputs
-  __shared__ float wm[NW][HG], wl[NW][HG];
-  __shared__ float sM[HG], sZ[HG];
+  // observation steps: [HG][nstride] probabilities and [nstride / 32][HG]
+  // chunk maxima; then [NW][HG][D] per-wave outputs
+  float* s_lg = dyn;
+  float* s_mc = dyn + (OBS ? HG * nstride : 0);
+  float* o_m = s_mc + (OBS ? HG * (nstride / 32) : 0);
+  __shared__ float wm[NW][HG], wl[NW][HG], sf[NW][HG];
 
   const int g = blockIdx.x, l = blockIdx.y;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -207,27 +227,27 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   const int n = count[g] + 1;  // slots including the new token
   const int tnew = hole[g];
 
-  // B operand of q.K^T: query head r16, channels 32s + 8q4 .. +8
+  // B operand of q.K^T: query head r16, channels 32s + 8q4 .. +8.  Lanes
+  // past the group's heads repeat its last head: their logits are masked
+  // to -inf, so their probabilities and outputs never count.
   bf16x8s qb[4];
   {
     const uint16_t* qp = q + (static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + min(r16, HG - 1)) * D + 8 * q4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const u32x4s r = *reinterpret_cast<const u32x4s*>(qp + 32 * s);
-      qb[s] = to_bf16x8(head ? r : u32x4s{0u, 0u, 0u, 0u});
-    }
+    for (int s = 0; s < 4; ++s) qb[s] = to_bf16x8(*reinterpret_cast<const u32x4s*>(qp + 32 * s));
   }
 
-  // the new token's K row piece and V column elements, loaded first by the
-  // wave whose range holds the free slot
+  // the new token's K row piece and V column elements, used by the wave
+  // whose range holds the free slot.  Every wave loads them: no load here
+  // or in the chunk loop sits on a branch, so each wait covers exactly the
+  // loads it needs.
   const bool app = tnew >= 32 * c0 && tnew < 32 * c1;  // wave-uniform
   u32x4s knew[4];
   uint32_t vnew[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    knew[s] = app ? *reinterpret_cast<const u32x4s*>(k_new + new_off + 32 * s + 8 * q4) : u32x4s{0u, 0u, 0u, 0u};
+  for (int s = 0; s < 4; ++s) knew[s] = *reinterpret_cast<const u32x4s*>(k_new + new_off + 32 * s + 8 * q4);
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) vnew[ct] = app ? v_new[new_off + 16 * ct + r16] : 0u;
+  for (int ct = 0; ct < 8; ++ct) vnew[ct] = v_new[new_off + 16 * ct + r16];
 
   f32x4s oacc[8];
 #pragma unroll
@@ -235,22 +255,38 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // two chunks per iteration, one per register buffer: the next chunk's
-  // loads are in flight while the current one is computed
+  // loads are in flight while the current one is computed.  Every load in
+  // the loop body is unconditional (the loop runs while two chunks remain
+  // after the current one), so the wait before each chunk covers that
+  // chunk's loads only; the last one or two chunks are peeled.
+  // (a wave without chunks loads one in bounds and leaves it unused).  The
+  // query and new-token loads stay ahead of the first chunk's, so that
+  // waiting for them never waits for the chunk.
   SeqChunk cur, nxt;
-  if (c0 < c1) seq_load(cur, kpool, vpool, page0, maxpages, c0, l, r16, q4, P);
+  int c = c0;
+  __builtin_amdgcn_sched_barrier(0);
+  seq_load(cur, kpool, vpool, page0, maxpages, c0, l, r16, q4, P);
 #pragma unroll 1
-  for (int c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
+  for (; c + 2 < c1; c += 2) {
+    seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
     seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, nstride, oacc, m_run, l_run);
-    if (c + 1 < c1) {
-      if (c + 2 < c1) seq_load(cur, kpool, vpool, page0, maxpages, c + 2, l, r16, q4, P);
-      seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb,
-                        scale, s_lg, nstride, oacc, m_run, l_run);
-    }
+                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_load(cur, kpool, vpool, page0, maxpages, c + 2, l, r16, q4, P);
+    seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
+                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+  }
+  if (c + 1 < c1) {
+    seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
+    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
+                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
+                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+  } else if (c < c1) {
+    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
+                      s_lg, s_mc, nstride, oacc, m_run, l_run);
   }
 
-  // ---- merge the waves: (M, Z) per head and the output ----------------------
+  // ---- merge the waves --------------------------------------------------------
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   if (head) {
@@ -264,39 +300,41 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
           make_float4(oacc[ct][0], oacc[ct][1], oacc[ct][2], oacc[ct][3]);
   }
   __syncthreads();
-  if (tid < HG) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w][tid]);
-    float Z = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) Z += wm[w][tid] == -INFINITY ? 0.f : wl[w][tid] * __expf(wm[w][tid] - M);
-    sM[tid] = M;
-    sZ[tid] = Z;
+  // per (wave, head) weight of the wave's output, exp(m_wave - M) / Z, and
+  // per (chunk, head) scale of the chunk's probabilities, exp(m_chunk - M) /
+  // Z, with the head's overall maximum M and normaliser Z (a wave or chunk
+  // without slots has m = -inf and weighs 0)
+  if (tid < NW * HG) {
+    const int w = tid / HG, h = tid % HG;
+    float M, Z;
+    head_stats<NW, HG>(wm, wl, h, M, Z);
+    sf[w][h] = wm[w][h] == -INFINITY ? 0.f : __expf(wm[w][h] - M) / Z;
+  }
+  if constexpr (OBS) {
+    const int nc = (n + 31) / 32;
+    for (int i = tid; i < nc * HG; i += NT) {
+      float M, Z;
+      head_stats<NW, HG>(wm, wl, i % HG, M, Z);
+      const float mc = s_mc[i];
+      s_mc[i] = mc == -INFINITY ? 0.f : __expf(mc - M) / Z;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < HG * D; idx += NT) {
     const int h = idx / D, cc = idx % D;
-    const float M = sM[h];
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-      o += wm[w][h] == -INFINITY ? 0.f : __expf(wm[w][h] - M) * o_m[(w * HG + h) * D + cc];
-    out[(static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + h) * D + cc] = o / sZ[h];
+    for (int w = 0; w < NW; ++w) o += sf[w][h] * o_m[(w * HG + h) * D + cc];
+    out[(static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + h) * D + cc] = o;
   }
   if constexpr (OBS) {
-    // probability pass: the group's mass of every slot, from the logits in LDS
-    float Mh[HG], Zh[HG];
-#pragma unroll
-    for (int h = 0; h < HG; ++h) {
-      Mh[h] = sM[h];
-      Zh[h] = sZ[h];
-    }
+    // probability pass: the group's mass of every slot
     float* gm = gmass + (static_cast<int64_t>(g) * L + l) * lstride;
     for (int t = tid; t < n; t += NT) {
+      const float* f = s_mc + (t >> 5) * HG;
       float m = 0.f;
 #pragma unroll
-      for (int h = 0; h < HG; ++h) m += __expf(s_lg[h * nstride + t] - Mh[h]) / Zh[h];
+      for (int h = 0; h < HG; ++h) m += s_lg[h * nstride + t] * f[h];
       gm[t] = m;
     }
   }
@@ -308,7 +346,7 @@ constexpr int kSeqNW = 8;
 
 int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs) {
   const int64_t nstride = (n_max + 31) / 32 * 32;
-  return ((obs ? hg * nstride : 0) + static_cast<int64_t>(kSeqNW) * hg * 128) * 4;
+  return ((obs ? hg * nstride + hg * (nstride / 32) : 0) + static_cast<int64_t>(kSeqNW) * hg * 128) * 4;
 }
 
 hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
