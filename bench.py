@@ -87,6 +87,8 @@ CSRC = os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_kernel_traffic_llama8b_32k.md")
 ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "common.h")]
 SEQ_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_seq_kernel_traffic_llama8b_32k.md")
+TIER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tier_attn_kernel_traffic_qevict131k.md")
+TIER_SOURCES = [os.path.join(CSRC, f) for f in ("tier.hip", "common.h")]
 SEQ_SOURCES = [os.path.join(CSRC, f) for f in ("attn_seq.hip", "common.h")]
 
 
