@@ -22,8 +22,8 @@
 //     [1024, 2048)  value codes, 16 B per lane
 //     [2048, 2304)  key scale per channel, fp16 [128]
 //     [2304, 2560)  key zero point per channel, fp16 [128]
-//     [2560, 2816)  value scale per (token, 32-channel group), fp16 [32][4]
-//     [2816, 3072)  value zero point, fp16 [32][4]
+//     [2560, 2816)  value scale per (32-channel group, token), fp16 [4][32]
+//     [2816, 3072)  value zero point, fp16 [4][32]
 // Full-precision storage is never released: a demoted window keeps it, so a
 // promotion only rewrites it and nothing moves when tiers change.
 //
@@ -51,6 +51,7 @@ constexpr int D = kTierD;  // head dim
 constexpr int HG = 4;      // query heads per KV head
 constexpr int W = kTierWin;
 constexpr int kRecK = 0, kRecV = 1024, kRecSK = 2048, kRecZK = 2304, kRecSV = 2560, kRecZV = 2816;
+constexpr int kFW = 2, kQW = 4;  // windows per wave of the attention: full-precision, INT2
 
 __device__ __forceinline__ bf16x8_t as_b8(const uint4& r) {
   bf16x8_t v;
@@ -118,6 +119,26 @@ __device__ __forceinline__ bf16x8_t split_rows(const float* x, int r16) {
   return as_b8(make_uint4(w[0], w[1], w[2], w[3]));
 }
 
+// The high and low bf16 parts of 8 fp32 values, packed two per word.
+__device__ __forceinline__ void split_hilo(const float* x, uint4& hi, uint4& lo) {
+  uint32_t h[4], w[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = pack_bf16(x[2 * p], x[2 * p + 1]);
+    w[p] = pack_bf16(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xffff0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Orders a wave's LDS stores and loads that exchange data between its lanes
+// (the LDS executes a wave's operations in order; this keeps the compiler
+// from moving them across each other).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -182,9 +203,9 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
 
 // ---------------------------------------------------------------------------
 // Attention over the accessible windows of (layer l, KV head h).  Block
-// (chunk, h, l) of 4 waves; a wave takes 2 consecutive windows of a list
-// (64 tokens), a chunk 8.  Chunks [0, nch_f) cover the full-precision list,
-// the rest the INT2 list.  Writes the chunk's (max, sum) and unnormalised
+// (chunk, h, l) of 4 waves; a wave takes kFW = 2 consecutive windows of the
+// full-precision list (a chunk 8) or kQW = 4 of the INT2 list (a chunk 16).
+// Chunks [0, nch_f) cover the full-precision list, the rest the INT2 list.  Writes the chunk's (max, sum) and unnormalised
 // output per head, and per window and head the sum of exp(s - chunk max)
 // over the window's tokens (its attention mass before normalisation).
 //   q.K: A = the 4 query rows, B = K^T (n-tiles of 16 tokens, k-steps of 32
@@ -199,26 +220,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     TierArgs A, const uint16_t* __restrict__ q,
                                                         int n_fp, int n_q, int nch_f, int npos,
                                                         float scale) {
-  __shared__ __align__(16) float p_lds[4][HG][64];
+  __shared__ __align__(16) float p_lds[4][HG][32 * kQW];
   __shared__ __align__(16) float o_lds[4][HG][D];
   __shared__ float wstat[4][HG][2];
-  __shared__ float e_lds[4][2][HG];
+  __shared__ float e_lds[4][kQW][HG];
+  __shared__ uint4 opnd[4][2][129];  // INT2 A operands staged per wave; [w][0][128] is zero
 
   const int chunk = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r16 = lane & 15, q4 = lane >> 4;
   const bool isq = chunk >= nch_f;
-  const int base = (isq ? chunk - nch_f : chunk) * 8;
+  const int wpw = isq ? kQW : kFW;  // windows per wave
+  const int base = isq ? (chunk - nch_f) * 4 * kQW : chunk * 4 * kFW;
   const int nlist = isq ? n_q : n_fp;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int* list = (isq ? A.qlist : A.fplist) + static_cast<int64_t>(l) * A.NW;
-  int win[2];
-  bool live[2];
+  int win[kQW];
+  bool live[kQW];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = base + 2 * wave + k;
-    live[k] = idx < nlist;
+  for (int k = 0; k < kQW; ++k) {
+    const int idx = base + wpw * wave + k;
+    live[k] = k < wpw && idx < nlist;
     win[k] = live[k] ? list[idx] : 0;
   }
 
@@ -230,11 +253,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qp + 32 * s);
   }
 
-  float sv[4][HG];      // logits of n-tile jj = 2k + j (lanes q4 == 0 hold them)
+  float sv[2 * kQW][HG];  // logits of n-tile jj = 2k + j (lanes q4 == 0 hold them)
   f32x4_t oacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float bz[4] = {0.f, 0.f, 0.f, 0.f};  // INT2: sum_t p_t z_tg per group (lanes r16 < 4)
+  float bzl = 0.f;  // INT2: sum_t p_t z_tg of (head, group) over the lane's tokens
 
   if (!isq) {
     // ---- full-precision windows -------------------------------------------
@@ -312,47 +335,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     }
   } else {
     // ---- INT2 windows -------------------------------------------------------
-    float qf[4][8];
+    // The scaled operands are formed once per (head, channel) and (head,
+    // token, group) by the wave's lanes and staged in LDS as matrix-core A
+    // operands (rows 0..3: high parts of heads 0..3, rows 4..7: low parts):
+    //   q.K: lane (head hs = lane / 16, channels 8 cs .. +8, cs = lane % 16)
+    //   p.V: lane (head hs, tokens 8 ts .. +8 of the window, ts = lane / 4 % 4,
+    //        32-channel group gs = lane % 4)
+    const int hs = lane >> 4, cs = lane & 15, ts = (lane >> 2) & 3, gs = lane & 3;
+    uint4* sk = opnd[wave][0];  // [k-step][row][k-group]
+    uint4* sp = opnd[wave][1];  // [group][row][k-group]
+    const uint4* zrow = &opnd[wave][0][128];  // the A rows 8..15 of every operand
+    if (lane == 0) opnd[wave][0][128] = make_uint4(0, 0, 0, 0);
+    float qx[8];
+    Vec16<bf16_t>::widen(
+        *reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(l) * A.Hq + h * HG + hs) * D + 8 * cs), qx);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float t[8];
-      Vec16<bf16_t>::widen(qraw[s], t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = t[e];
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kQW; ++k) {
       const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
-      uint4 kc = make_uint4(0, 0, 0, 0);
+      uint4 kc = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
       float bias = 0.f;
-      bf16x8_t a1[4];
-      if (live[k]) {
+      if (live[k]) {  // wave-uniform
         kc = *reinterpret_cast<const uint4*>(rec + kRecK + 16 * lane);
+        const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSK + 16 * cs);
+        const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZK + 16 * cs);
+        float x[8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSK + 2 * (32 * s + 8 * q4));
-          const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZK + 2 * (32 * s + 8 * q4));
-          const uint32_t sw[4] = {sr.x, sr.y, sr.z, sr.w}, zw[4] = {zr.x, zr.y, zr.z, zr.w};
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float sc = h2f(sw[e >> 1] >> (16 * (e & 1)));
-            const float zp = h2f(zw[e >> 1] >> (16 * (e & 1)));
-            x[e] = qf[s][e] * sc;
-            bias = fmaf(qf[s][e], zp, bias);
-          }
-          a1[s] = split_rows(x, r16);
+        for (int e = 0; e < 8; ++e) {
+          const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
+          const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
+          x[e] = qx[e] * sc;
+          bias = fmaf(qx[e], zp, bias);
         }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) a1[s] = as_b8(make_uint4(0, 0, 0, 0));
+        split_hilo(x, hi, lo);
       }
-      // full sum_c q_c z_c of head r16 & 3 (lanes r16 = 0..3 of every q4)
-      bias += __shfl_xor(bias, 16, kWave);
-      bias += __shfl_xor(bias, 32, kWave);
+      wave_lds_order();
+      sk[((cs >> 2) * 8 + hs) * 4 + (cs & 3)] = hi;
+      sk[((cs >> 2) * 8 + 4 + hs) * 4 + (cs & 3)] = lo;
+      wave_lds_order();
+      bf16x8_t a1[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a1[s] = as_b8(*(r16 < 8 ? &sk[(s * 8 + r16) * 4 + q4] : zrow));
+      // sum_c q_c z_c of each head (the 16 lanes of head hs hold its parts)
+      bias = row16_sum(bias);
       float bb[HG];
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) bb[hh] = __shfl(bias, hh, kWave);
+      for (int hh = 0; hh < HG; ++hh) bb[hh] = __shfl(bias, 16 * hh, kWave);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         f32x4_t acc = q4 == 0 ? f32x4_t{bb[0], bb[1], bb[2], bb[3]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -376,63 +403,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     float mh[HG];
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      float m = fmaxf(fmaxf(sv[0][hh], sv[1][hh]), fmaxf(sv[2][hh], sv[3][hh]));
+      float m = sv[0][hh];
+#pragma unroll
+      for (int jj = 1; jj < 2 * kQW; ++jj) m = fmaxf(m, sv[jj][hh]);
       mh[hh] = row16_max(m);
     }
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      float e0 = 0.f, e1 = 0.f;
+      float ew[kQW];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float pv = mh[hh] == -INFINITY ? 0.f : __expf(sv[jj][hh] - mh[hh]);
-        sv[jj][hh] = pv;
-        if (jj < 2) e0 += pv; else e1 += pv;
+      for (int k = 0; k < kQW; ++k) {
+        const float p0 = mh[hh] == -INFINITY ? 0.f : __expf(sv[2 * k][hh] - mh[hh]);
+        const float p1 = mh[hh] == -INFINITY ? 0.f : __expf(sv[2 * k + 1][hh] - mh[hh]);
+        sv[2 * k][hh] = p0;
+        sv[2 * k + 1][hh] = p1;
+        ew[k] = row16_sum(p0 + p1);
       }
-      e0 = row16_sum(e0);
-      e1 = row16_sum(e1);
       if (lane == 0) {
-        e_lds[wave][0][hh] = e0;
-        e_lds[wave][1][hh] = e1;
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < kQW; ++k) {
+          e_lds[wave][k][hh] = ew[k];
+          tot += ew[k];
+        }
         wstat[wave][hh][0] = mh[hh];
-        wstat[wave][hh][1] = e0 + e1;
+        wstat[wave][hh][1] = tot;
       }
     }
     if (q4 == 0) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 2 * kQW; ++jj)
 #pragma unroll
         for (int hh = 0; hh < HG; ++hh) p_lds[wave][hh][16 * jj + r16] = sv[jj][hh];
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kQW; ++k) {
       if (!live[k]) continue;  // wave-uniform
       const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
       const uint4 vc = *reinterpret_cast<const uint4*>(rec + kRecV + 16 * lane);
-      const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4]);
-      const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][r16 & 3][32 * k + 8 * q4 + 4]);
+      // scale and zero point of (group gs, tokens 8 ts .. +8), stored [group][token]
+      const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * gs + 8 * ts));
+      const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * gs + 8 * ts));
+      const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts]);
+      const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts + 4]);
       const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
-      // scale and zero point of tokens 8q4 .. +8, groups 0..3 ([token][group] fp16)
-      uint32_t sw[16], zw[16];
+      float x[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * q4 + 8 * u));
-        const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * q4 + 8 * u));
-        sw[4 * u] = sr.x; sw[4 * u + 1] = sr.y; sw[4 * u + 2] = sr.z; sw[4 * u + 3] = sr.w;
-        zw[4 * u] = zr.x; zw[4 * u + 1] = zr.y; zw[4 * u + 2] = zr.z; zw[4 * u + 3] = zr.w;
+      for (int e = 0; e < 8; ++e) {
+        const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
+        const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
+        x[e] = pv[e] * sc;
+        bzl = fmaf(pv[e], zp, bzl);
       }
+      uint4 hi, lo;
+      split_hilo(x, hi, lo);
+      wave_lds_order();
+      sp[(gs * 8 + hs) * 4 + ts] = hi;
+      sp[(gs * 8 + 4 + hs) * 4 + ts] = lo;
+      wave_lds_order();
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = 4 * e + g;  // fp16 index of (token 8q4 + e, group g)
-          const float sc = h2f(sw[idx >> 1] >> (16 * (idx & 1)));
-          const float zp = h2f(zw[idx >> 1] >> (16 * (idx & 1)));
-          x[e] = pv[e] * sc;
-          bz[g] = fmaf(pv[e], zp, bz[g]);
-        }
-        const bf16x8_t pa = split_rows(x, r16);
+        const bf16x8_t pa = as_b8(*(r16 < 8 ? &sp[(g * 8 + r16) * 4 + q4] : zrow));
         const uint32_t w0 = word_of(vc, g >> 1), w1 = word_of(vc, 2 + (g >> 1));
         // tiles ct = 2g, 2g + 1 sit at pairs 4 (ct % 4) .. of word ct / 4
         if ((g & 1) == 0) {
@@ -448,11 +480,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
         }
       }
     }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bz[g] += __shfl_xor(bz[g], 16, kWave);
-      bz[g] += __shfl_xor(bz[g], 32, kWave);
-    }
+    // sum_t p_t z_tg of each (head, group): over the lanes' token blocks
+    bzl += __shfl_xor(bzl, 4, kWave);
+    bzl += __shfl_xor(bzl, 8, kWave);
   }
 
   // the wave's output: high rows (q4 == 0) + low rows (q4 == 1) + zero-point terms
@@ -460,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) bzh[hh][g] = isq ? __shfl(bz[g], hh, kWave) : 0.f;
+    for (int g = 0; g < 4; ++g) bzh[hh][g] = isq ? __shfl(bzl, 16 * hh + g, kWave) : 0.f;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
 #pragma unroll
@@ -492,9 +522,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
       A.part_ml[(pb * HG + hh) * 2 + 1] = Z;
     }
   }
-  if (tid < 8 * HG) {
-    const int slot = tid / HG, hh = tid % HG;  // slot = 2 * wave + k
-    const int wv = slot >> 1, k = slot & 1;
+  if (tid < 4 * wpw * HG) {
+    const int slot = tid / HG, hh = tid % HG;  // slot = wpw * wave + k
+    const int wv = slot / wpw, k = slot % wpw;
     const int idx = base + slot;
     if (idx < nlist) {
       float M = -INFINITY;
@@ -579,7 +609,7 @@ __global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, in
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= n_fp + n_q) return;
   const bool isq = idx >= n_fp;
-  const int chunk = isq ? nch_f + (idx - n_fp) / 8 : idx / 8;
+  const int chunk = isq ? nch_f + (idx - n_fp) / (4 * kQW) : idx / (4 * kFW);
   const int w = isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
                     : A.fplist[static_cast<int64_t>(l) * A.NW + idx];
   float acc = 0.f;
@@ -897,8 +927,8 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         float sc, zp;
         uint16_t s16, z16;
         int2_group(&xv[r][32 * g], 32, 1, sc, zp, s16, z16);
-        rec16[kRecSV / 2 + 4 * r + g] = s16;
-        rec16[kRecZV / 2 + 4 * r + g] = z16;
+        rec16[kRecSV / 2 + 32 * g + r] = s16;
+        rec16[kRecZV / 2 + 32 * g + r] = z16;
         for (int c = 32 * g; c < 32 * g + 32; ++c) cv[r][c] = int2_code(xv[r][c], sc, zp);
       }
       __syncthreads();
@@ -958,7 +988,7 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
             const uint32_t w0 = recl[kRecV / 4 + 4 * ln + part], w1 = recl[kRecV / 4 + 4 * ln + 2 + part];
             const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
             const int g = c >> 5;
-            const float sc = h2f(rl16[kRecSV / 2 + 4 * r + g]), zp = h2f(rl16[kRecZV / 2 + 4 * r + g]);
+            const float sc = h2f(rl16[kRecSV / 2 + 32 * g + r]), zp = h2f(rl16[kRecZV / 2 + 32 * g + r]);
             vb = bf16_rne(__fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp));
           }
           if (e & 1) {
@@ -1046,7 +1076,7 @@ hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new)
 }
 
 hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
-  const int nch_f = (c->tw.n_fp + 7) / 8, nch_q = (c->tw.n_q + 7) / 8;
+  const int nch_f = (c->tw.n_fp + 4 * kFW - 1) / (4 * kFW), nch_q = (c->tw.n_q + 4 * kQW - 1) / (4 * kQW);
   const int npos = static_cast<int>(c->tw.npos);
   TierArgs a = tier_args(c);
   dim3 grid(nch_f + nch_q, c->cfg.n_kv_heads, c->cfg.n_layers);
@@ -1056,7 +1086,7 @@ hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
 }
 
 hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
-  const int nch_f = (c->tw.n_fp + 7) / 8, nch_q = (c->tw.n_q + 7) / 8;
+  const int nch_f = (c->tw.n_fp + 4 * kFW - 1) / (4 * kFW), nch_q = (c->tw.n_q + 4 * kQW - 1) / (4 * kQW);
   TierArgs a = tier_args(c);
   hipError_t e;
   dim3 gm(HG, c->cfg.n_kv_heads, c->cfg.n_layers);

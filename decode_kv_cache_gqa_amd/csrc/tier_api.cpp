@@ -275,8 +275,15 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
     }
   std::memcpy(k_scale, rec.data() + 2048, 256);
   std::memcpy(k_zero, rec.data() + 2304, 256);
-  std::memcpy(v_scale, rec.data() + 2560, 256);
-  std::memcpy(v_zero, rec.data() + 2816, 256);
+  // value scales and zero points are stored [group][token]; the export is [token][group]
+  uint16_t vs[4][kTierWin], vz[4][kTierWin];
+  std::memcpy(vs, rec.data() + 2560, 256);
+  std::memcpy(vz, rec.data() + 2816, 256);
+  for (int r = 0; r < kTierWin; ++r)
+    for (int g = 0; g < 4; ++g) {
+      v_scale[r * 4 + g] = vs[g][r];
+      v_zero[r * 4 + g] = vz[g][r];
+    }
   return KVEV_OK;
 }
 
