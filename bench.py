@@ -110,26 +110,50 @@ def measured_traffic(profile=TRAFFIC_PROFILE, sources=ATTN_SOURCES):
     return int(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w, steps=300):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _timed_two_ways(segment):
+    """segment(k) runs and times the k-th timed segment (k = 0, 1) of an
+    oracle sample and returns its seconds per scaled step.  Segment 0 runs
+    with the BLAS pools limited to one thread, segment 1 with the default
+    pools.  Returns (seconds all threads, seconds one thread, threads)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=1):
+        one = segment(0)
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return segment(1), one, cores
+
+
+def _baseline_record(sec_all, sec_one, cores, sample):
+    return {"value": 1.0 / sec_all, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "value_1thread": 1.0 / sec_one, "cpu_model": _cpu_model(), "sample": sample}
+
+
+def cpu_baseline(w, steps=150):
     """Time the CPU oracle on a bounded sample: steady steps of ONE selection
     group at the workload's real shape (all layers, budget+1 tokens), scaled
     to the whole step.  A group is one (sequence, KV head), or one sequence
-    with all its KV heads in the per-sequence mode."""
-    import numpy as np
+    with all its KV heads in the per-sequence mode.  Two segments of `steps`
+    steps: one with one BLAS thread, one with the default threads."""
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
     B = w.budget
     pooled = w.granularity == "sequence"
+    if pooled:
+        steps = max(steps // w.n_kv_heads, 8)
     kw = dict(budget=B, alpha_new=w.alpha_new, n_sink=w.n_sink, n_recent=w.n_recent,
-              capacity=B + steps + 2, scorer=w.scorer,
+              capacity=B + 2 * steps + 2, scorer=w.scorer,
               policy="cumulative" if w.policy == "cumulative" else "ema",
               refresh_interval=w.refresh_interval, score_free=w.score_free)
     if pooled:
-        steps = max(steps // w.n_kv_heads, 8)
         o = orc.PooledTokenOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, **kw)
         K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0)
         o.prefill(0, K.float().numpy(), V.float().numpy())
@@ -139,20 +163,23 @@ def cpu_baseline(w, steps=300):
         K, V = w.scaled(prefill_lens=(B,)).prefill_kv(0, heads=[0])
         o.prefill(0, K.float().numpy(), V.float().numpy(), heads=[0])
         groups = w.n_kv_heads * w.batch
-    ins = [w.step_inputs(t, seqs=[0]) for t in range(1, steps + 2)]
+    ins = [w.step_inputs(t, seqs=[0]) for t in range(1, 2 * steps + 2)]
     ins = [tuple(x.float().numpy() for x in s) for s in ins]
     o.decode_step(1, *ins[0], [0])
     o.evict()
-    t0 = time.perf_counter()
-    for t in range(2, steps + 2):
-        o.decode_step(t, *ins[t - 1], [0])
-        o.evict()
-    dt = time.perf_counter() - t0
-    full_step = dt / steps * groups
+
+    def segment(k):
+        t0 = time.perf_counter()
+        for t in range(2 + k * steps, 2 + (k + 1) * steps):
+            o.decode_step(t, *ins[t - 1], [0])
+            o.evict()
+        return (time.perf_counter() - t0) / steps * groups
+
+    sec_all, sec_one, cores = _timed_two_ways(segment)
     unit = "sequence" if pooled else "(sequence, KV head)"
-    return {"value": 1.0 / full_step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} steady steps of 1 of {groups} {unit} groups at {w.n_layers} layers x "
-                      f"{B + 1} tokens, scaled x{groups}"}
+    return _baseline_record(sec_all, sec_one, cores,
+                            f"2 x {steps} steady steps of 1 of {groups} {unit} groups at {w.n_layers} layers x "
+                            f"{B + 1} tokens, scaled x{groups}")
 
 
 def tier_bytes(w, n_fp_tokens, n_q):
@@ -169,65 +196,64 @@ def tier_bytes(w, n_fp_tokens, n_q):
 
 def tier_cpu_baseline(w, steps=3):
     """The CPU oracle on one layer of the tiered workload: the first routing
-    event untimed, then `steps` steady steps timed and scaled to all layers."""
-    import numpy as np
+    event untimed, then two segments of `steps` steady steps (one BLAS
+    thread, default threads), each scaled to all layers."""
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
     o = orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                          k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
-                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 2,
+                         n_recent=w.n_recent, capacity=w.prefill_lens[0] + 2 * steps + 2,
                          route_interval=w.route_interval)
     K, V = w.prefill_kv(0, layers=[0])
     o.prefill(K.float().numpy(), V.float().numpy(), layers=[0])
     del K, V
-    ins = [tuple(x[:1, 0].float().numpy() for x in w.step_inputs(t, seqs=[0])) for t in range(1, steps + 2)]
+    ins = [tuple(x[:1, 0].float().numpy() for x in w.step_inputs(t, seqs=[0])) for t in range(1, 2 * steps + 2)]
     o.decode_step(1, *ins[0])
     o.route()
-    t0 = time.perf_counter()
-    for t in range(2, steps + 2):
-        o.decode_step(t, *ins[t - 1])
-        if o.routes_after(t):
-            o.route()
-    per_layer = (time.perf_counter() - t0) / steps
-    return {"value": 1.0 / (per_layer * w.n_layers), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} steady steps of layer 0 of {w.n_layers} after the first routing event "
-                      f"({w.prefill_lens[0]}-token prefill), scaled x{w.n_layers}"}
+
+    def segment(k):
+        t0 = time.perf_counter()
+        for t in range(2 + k * steps, 2 + (k + 1) * steps):
+            o.decode_step(t, *ins[t - 1])
+            if o.routes_after(t):
+                o.route()
+        return (time.perf_counter() - t0) / steps * w.n_layers
+
+    sec_all, sec_one, cores = _timed_two_ways(segment)
+    return _baseline_record(sec_all, sec_one, cores,
+                            f"2 x {steps} steady steps of layer 0 of {w.n_layers} after the first routing event "
+                            f"({w.prefill_lens[0]}-token prefill), scaled x{w.n_layers}")
 
 
-def block_cpu_baseline(w, steps=40):
+def block_cpu_baseline(w, steps=20):
     """The CPU oracle on the median-length sequence of the block workload:
-    its prefill and first eviction untimed, then `steps` steady steps timed
-    and scaled to every sequence."""
+    its prefill and first eviction untimed, then two segments of `steps`
+    steady steps (one BLAS thread, default threads), each scaled to every
+    sequence."""
     import numpy as np
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
     b = int(np.argsort(w.prefill_lens)[len(w.prefill_lens) // 2])
     o = orc.BlockLRFUOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, alpha_new=w.alpha_new,
                             beta=w.beta, half_lives=tuple(w.region_half_lives),
                             pinned_regions=tuple(w.pinned_regions), decode_region=w.decode_region,
-                            capacity=w.prefill_lens[b] + steps + 2)
+                            capacity=w.prefill_lens[b] + 2 * steps + 2)
     K, V = w.prefill_kv(b)
     o.prefill(b, K.float().numpy(), V.float().numpy(), w.region_labels(b), w.block_budget(b))
     del K, V
-    ins = [tuple(x.float().numpy() for x in w.step_inputs(t, seqs=[b])) for t in range(1, steps + 2)]
+    ins = [tuple(x.float().numpy() for x in w.step_inputs(t, seqs=[b])) for t in range(1, 2 * steps + 2)]
     o.decode_step(1, *ins[0], [b])
     o.evict(1, seqs=[b])
-    t0 = time.perf_counter()
-    for t in range(2, steps + 2):
-        o.decode_step(t, *ins[t - 1], [b])
-        o.evict(t, seqs=[b])
-    per_seq = (time.perf_counter() - t0) / steps
-    return {"value": 1.0 / (per_seq * w.batch), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{steps} steady steps of sequence {b} ({w.prefill_lens[b]}-token prefill, the median) "
-                      f"of {w.batch} after its first eviction, scaled x{w.batch}"}
+
+    def segment(k):
+        t0 = time.perf_counter()
+        for t in range(2 + k * steps, 2 + (k + 1) * steps):
+            o.decode_step(t, *ins[t - 1], [b])
+            o.evict(t, seqs=[b])
+        return (time.perf_counter() - t0) / steps * w.batch
+
+    sec_all, sec_one, cores = _timed_two_ways(segment)
+    return _baseline_record(sec_all, sec_one, cores,
+                            f"2 x {steps} steady steps of sequence {b} ({w.prefill_lens[b]}-token prefill, the "
+                            f"median) of {w.batch} after its first eviction, scaled x{w.batch}")
 
 
 def run_block(args, w):
@@ -343,13 +369,44 @@ def run_tier(args, w):
         "roofline": {
             "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": measured_traffic(TIER_TRAFFIC_PROFILE, TIER_SOURCES), "kernel": "tier_attn_kernel",
+            "traffic": (measured_traffic(TIER_TRAFFIC_PROFILE, TIER_SOURCES)
+                        if args.workload == "qevict131k" else None), "kernel": "tier_attn_kernel",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = tier_cpu_baseline(w)
     print(json.dumps(result))
+
+
+def calibrate_stream(n_bytes=2 << 30, reps=10):
+    """The HBM streaming-read ceiling: kvev_calibrate_read over a 2 GiB
+    buffer (8x the last-level cache), plain and non-temporal loads, 2-16
+    workgroups of 256 threads per compute unit, each configuration timed
+    over `reps` launches with events on torch's stream."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.ones(n_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(16 * cus, dtype=torch.int32, device="cuda")
+    rows = []
+    for nt in (0, 1):
+        for bpc in (2, 4, 8, 16):
+            blocks = bpc * cus
+            for _ in range(2):
+                kvev.calibrate_read(buf, nt, blocks, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                kvev.calibrate_read(buf, nt, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / reps
+            rows.append({"nontemporal": nt, "blocks_per_cu": bpc, "us": round(us, 2),
+                         "TBps": round(n_bytes / us / 1e6, 3)})
+    best = max(rows, key=lambda r: r["TBps"])
+    print(json.dumps({"calibration": "stream_read", "bytes": n_bytes, "cus": cus, "reps": reps,
+                      "results": rows, "best": best}))
 
 
 def main():
@@ -363,6 +420,8 @@ def main():
                     help="profile every N-th timed step (HIP events around its launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--calibrate-stream", action="store_true",
+                    help="only time the library's streaming read of a 2 GiB buffer (the HBM read ceiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported",
@@ -381,6 +440,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 4}))
         return
+
+    if args.calibrate_stream:
+        return calibrate_stream()
 
     w = synth.workload(args.workload)
     if w.policy == "tiered_int2":

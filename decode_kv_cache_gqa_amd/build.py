@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvev.so")
-SOURCES = ["api.cpp", "tier_api.cpp", "attn.hip", "attn_seq.hip", "policy.hip", "pool.hip", "block.hip", "tier.hip", "diag.hip"]
+SOURCES = ["api.cpp", "tier_api.cpp", "attn.hip", "attn_seq.hip", "policy.hip", "pool.hip", "block.hip", "tier.hip", "diag.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -132,6 +132,8 @@ _SIGS = {
                                        ctypes.POINTER(ctypes.c_int64)]),
     "kvev_diag_fmm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
     "kvev_diag_fmm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double)]),
+    "kvev_calibrate_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p]),
     "kvev_tier_diag": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(RouteDiag)]),
     "kvev_sync": (ctypes.c_int, [ctypes.c_void_p]),
     "kvev_step_index": (ctypes.c_int64, [ctypes.c_void_p]),
@@ -459,6 +461,24 @@ def diag_fmm_noalloc(full, compressed):
     out = (ctypes.c_double * G)()
     compressed._check(lib().kvev_diag_fmm_noalloc(full._h, compressed._h, out))
     return np.array(list(out), dtype=np.float64)
+
+
+def calibrate_read(buf, nontemporal, blocks, sink, stream=None):
+    """kvev_calibrate_read: one streaming read of the device tensor `buf`
+    (16-byte aligned, a multiple of 16 bytes) on `stream` (default: torch's
+    current stream); `sink` is a device uint32/int32 tensor of >= blocks
+    words."""
+    import torch
+    if not (buf.is_cuda and sink.is_cuda):
+        raise ValueError("device tensors required")
+    if sink.numel() * sink.element_size() < 4 * blocks:
+        raise ValueError("sink too small")
+    s = torch.cuda.current_stream() if stream is None else stream
+    st = lib().kvev_calibrate_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                   1 if nontemporal else 0, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(s.cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"kvev_calibrate_read failed with status {st}")
 
 
 def tier_capacities(b_hist, q, m_f, m_q):

@@ -473,9 +473,15 @@ def workload(name: str) -> Workload:
     if name == "qevict131k_omega8":
         # the review's routing interval: one routing event every 8 steps (section 4.2 Eq.1)
         return replace(workload("qevict131k"), name="qevict_131k_fp5_int2_20_omega8", route_interval=8)
+    if name == "qevict131k_allfp":
+        # calibration: every routed window full precision (the tier split of the attention)
+        return replace(workload("qevict131k"), name="qevict_131k_allfp", fp_windows=1024, int2_windows=0)
+    if name == "qevict131k_allint2":
+        # calibration: every routed window INT2
+        return replace(workload("qevict131k"), name="qevict_131k_allint2", fp_windows=0, int2_windows=1024)
     raise KeyError(name)
 
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
              "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8",
-             "llama8b_32k_diag", "lrfu64_offload", "lazy16x8k_evict8")
+             "llama8b_32k_diag", "lrfu64_offload", "lazy16x8k_evict8", "qevict131k_allfp", "qevict131k_allint2")

@@ -574,6 +574,22 @@ kvev_status kvev_profile_read(kvev_ctx* ctx, const char* kernel, double* total_m
  * (then: the last kvev_create failure). */
 const char* kvev_last_error(const kvev_ctx* ctx);
 
+/* ---- Measurement utility (not part of the decode step) --------------------
+ * The HBM streaming-read ceiling that the attention kernels' achieved
+ * bandwidth is compared with ("What Matters ...", appendix J, and the
+ * "QEvict" review, section 4.1: decode attention is bound by reading the
+ * cache).  Launches one grid-stride read of `bytes` bytes at device pointer
+ * `buf` on HIP stream `stream` (a hipStream_t; NULL: the null stream):
+ * `blocks` workgroups of 256 threads, eight independent 16-byte loads per
+ * thread and iteration, non-temporal when `nontemporal` != 0.  Each block
+ * writes one XOR word of what it read to sink[block] (device, >= `blocks`
+ * words), so no load is dead.  Asynchronous: time it with events on
+ * `stream`.  Errors: KVEV_EINVAL (null pointer, bytes <= 0 or not a multiple
+ * of 16, buf not 16-byte aligned, blocks <= 0), KVEV_EHIP (launch failure).
+ * No context and no allocation. */
+kvev_status kvev_calibrate_read(const void* buf, int64_t bytes, int32_t nontemporal, int32_t blocks,
+                                uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
