@@ -41,7 +41,7 @@ __all__ = [
     "select_blocks", "BlockLRFUOracle", "bf16_round", "TieredOracle",
     "vnorm_weights", "normalized_entropy", "scored_mass", "SCORERS",
     "PooledTokenOracle", "jaccard", "top_k_positions", "RankTraceDiagnostics",
-    "future_missed_mass", "HostOffloadPool", "RoutingDiagnostics",
+    "future_missed_mass", "HostOffloadPool", "RoutingDiagnostics", "rope",
 ]
 
 
@@ -390,6 +390,27 @@ def int2_dequantize(codes, scales, zeros, axis_groups):
         raise ValueError(axis_groups)
     prod = (codes * s).astype(np.float32)
     return (prod + z).astype(np.float32)
+
+
+def rope(x, positions, theta):
+    """Rotary position embedding of the rows of ``x`` [n, d] at their
+    absolute ``positions`` [n], in fp64.
+
+    [QEvict] §4.4, "Positional handling for promoted keys": keys are
+    quantized before the rotation, with their original absolute positions,
+    and the rotation is applied again at those positions when a window is
+    promoted.  Reading (the pages give no formula): the rotary embedding of
+    the named Llama shape, which turns channel pair (i, i + d/2) by the
+    angle ``position * theta**(-2i/d)``, i < d/2.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    h = d // 2
+    freq = float(theta) ** (-2.0 * np.arange(h, dtype=np.float64) / d)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * freq[None, :]
+    c, sn = np.cos(ang), np.sin(ang)
+    a, b = x[:, :h], x[:, h:]
+    return np.concatenate([a * c - b * sn, b * c + a * sn], axis=1)
 
 
 # ---------------------------------------------------------------------------
@@ -1199,6 +1220,7 @@ class _TierLayer:
     """One layer's windows: FP storage, ledger, tier and cumulative score."""
     K: np.ndarray            # [Hkv, cap, d] fp32: full-precision values by position
     V: np.ndarray
+    Kpre: np.ndarray         # [Hkv, cap, d] fp32: the keys before the rotation (rotary mode), else empty
     Keff: np.ndarray         # [Hkv, cap, d] fp64 holding fp32 values: what attention reads
                              # (full precision or the INT2 reconstruction)
     Veff: np.ndarray
@@ -1235,11 +1257,24 @@ class TieredOracle:
       are quantized per channel over the window's tokens, values per token
       in 32-channel groups ([QEvict] §4.4 Algorithm 1; ``int2_quantize``).
     * A window promoted from Q to F gets its dequantized values rounded to
-      bf16 as its full-precision storage (reading: the synthetic keys carry
-      no rotary embedding, so there is none to re-apply).
+      bf16 as its full-precision storage.
+    * Rotary mode (``rope_theta`` > 0; [QEvict] §4.4, "Positional handling
+      for promoted keys"): prefill keys, appended keys and queries arrive
+      before the rotation.  Full-precision storage holds the rotated keys
+      rounded to bf16, ``bf16(rope(k, position))``; queries enter
+      attention as ``bf16(rope(q, p))`` at the new token's position p (a
+      bf16 model's rotated query).  Keys are quantized from the keys before
+      the rotation; the reconstruction of a key is ``rope(code*scale +
+      zero, original position)``, and a promotion stores it rounded to
+      bf16.  Without rotary mode the keys carry no rotation and there is
+      none to re-apply.
     * Attention reads full-precision windows from storage and INT2 windows
-      through their fp32 reconstruction ``code*scale + zero``
-      ([QEvict] §4.1, the accessible keys and values).
+      through their reconstruction ([QEvict] §4.1, the accessible keys and
+      values): exact (fp32 ``code*scale + zero``, rotated in fp64) by
+      default, or rounded to bf16 when ``reconstruct_bf16`` is set.  With
+      ``reconstruct_bf16`` the reconstruction also replaces the window's
+      full-precision storage when it enters the INT2 tier, so that storage
+      already holds what a later promotion writes.
 
     Layers are independent, so the object may hold any subset of them.
     """
@@ -1254,6 +1289,8 @@ class TieredOracle:
     n_recent: int = 0
     capacity: int = 0
     route_interval: int = 1
+    rope_theta: float = 0.0
+    reconstruct_bf16: bool = False
     layers: dict = field(default_factory=dict)
     npos: int = 0
     last_mass: dict = field(default_factory=dict)
@@ -1276,11 +1313,17 @@ class TieredOracle:
         nl, H, n, d = K.shape
         layers = list(range(nl)) if layers is None else list(layers)
         cap = max(self.capacity, n + 1)
+        rot = self.rope_theta > 0
         for j, l in enumerate(layers):
             st = _TierLayer(K=np.zeros((H, cap, d), np.float32), V=np.zeros((H, cap, d), np.float32),
+                            Kpre=np.zeros((H, cap if rot else 0, d), np.float32),
                             Keff=np.zeros((H, cap, d), np.float64), Veff=np.zeros((H, cap, d), np.float64))
+            kj = K[j]
+            if rot:
+                st.Kpre[:, :n] = K[j]
+                kj = np.stack([bf16_round(rope(K[j, h], np.arange(n), self.rope_theta)) for h in range(H)])
             for arr in (st.K, st.Keff):
-                arr[:, :n] = K[j]
+                arr[:, :n] = kj
             for arr in (st.V, st.Veff):
                 arr[:, :n] = V[j]
             for w in range(self.n_windows(n)):
@@ -1315,7 +1358,7 @@ class TieredOracle:
         if self.npos < st.K.shape[1]:
             return
         extra = max(64, st.K.shape[1] // 4)
-        for name in ("K", "V", "Keff", "Veff"):
+        for name in ("K", "V", "Keff", "Veff") + (("Kpre",) if self.rope_theta > 0 else ()):
             a = getattr(st, name)
             setattr(st, name, np.concatenate([a, np.zeros((a.shape[0], extra, a.shape[2]), a.dtype)], 1))
 
@@ -1331,11 +1374,19 @@ class TieredOracle:
         v_new = np.asarray(v_new, dtype=np.float32)
         held = sorted(self.layers)
         p = self.npos
+        rot = self.rope_theta > 0
+        if rot:                                      # the query at the new token's position
+            q = np.stack([bf16_round(rope(q[j], np.full(q.shape[1], p), self.rope_theta))
+                          for j in range(q.shape[0])])
         for j, l in enumerate(held):
             st = self.layers[l]
             self._grow(st)
+            kj = k_new[j]
+            if rot:
+                st.Kpre[:, p] = k_new[j]
+                kj = bf16_round(rope(k_new[j], np.full(k_new.shape[1], p), self.rope_theta))
             for arr in (st.K, st.Keff):
-                arr[:, p] = k_new[j]
+                arr[:, p] = kj
             for arr in (st.V, st.Veff):
                 arr[:, p] = v_new[j]
             w = p // self.window
@@ -1367,18 +1418,26 @@ class TieredOracle:
 
     def _quantize_window(self, st, w):
         sl = slice(w * self.window, (w + 1) * self.window)
+        src = st.Kpre if self.rope_theta > 0 else st.K     # keys before the rotation
         entry = []
         for h in range(self.n_kv_heads):
-            kc, ks, kz = int2_quantize(st.K[h, sl], "channel")
+            kc, ks, kz = int2_quantize(src[h, sl], "channel")
             vc, vs, vz = int2_quantize(st.V[h, sl], "token32")
             entry.append((kc, ks, kz, vc, vs, vz))
         st.ledger[w] = entry
 
     def _reconstruct(self, st, w):
         sl = slice(w * self.window, (w + 1) * self.window)
+        pos = np.arange(w * self.window, (w + 1) * self.window)
         for h, (kc, ks, kz, vc, vs, vz) in enumerate(st.ledger[w]):
-            st.Keff[h, sl] = int2_dequantize(kc, ks, kz, "channel")
-            st.Veff[h, sl] = int2_dequantize(vc, vs, vz, "token32")
+            k = int2_dequantize(kc, ks, kz, "channel").astype(np.float64)
+            if self.rope_theta > 0:                  # re-rotated at the original positions
+                k = rope(k, pos, self.rope_theta)
+            v = int2_dequantize(vc, vs, vz, "token32")
+            if self.reconstruct_bf16:
+                k, v = bf16_round(k), bf16_round(v)
+            st.Keff[h, sl] = k
+            st.Veff[h, sl] = v
 
     def route(self):
         """One routing event in every held layer (after the step's attention)."""
@@ -1394,6 +1453,9 @@ class TieredOracle:
                     self._quantize_window(st, w)
                 if st.tier[w] != "Q":                    # entering INT2: attention reads the reconstruction
                     self._reconstruct(st, w)
+                    if self.reconstruct_bf16:            # which also becomes the stored full precision
+                        st.K[:, sl(w)] = st.Keff[:, sl(w)]
+                        st.V[:, sl(w)] = st.Veff[:, sl(w)]
                 st.tier[w] = "Q"
             for w in F:
                 if st.tier[w] == "Q":                    # promotion: dequantize into bf16 storage
