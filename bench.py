@@ -184,13 +184,18 @@ def cpu_baseline(w, steps=150):
 
 def tier_bytes(w, n_fp_tokens, n_q):
     """Bytes of a steady tiered step: the full-precision tokens' K/V (512 B per
-    token and KV head) and the INT2 windows' records (3,072 B: 2-bit codes of
-    32 x 128 keys and values, fp16 scale and zero per key channel and per
-    value token-group) in every layer, plus q, the fp32 output, the appended
-    token and the window scores read and written."""
+    token and KV head) and the INT2 windows in every layer, plus q, the fp32
+    output, the appended token and the window scores read and written.  An
+    INT2 window of the fused path (32-token windows, no rotation) is read as
+    its 3,072-byte record (2-bit codes of 32 x 128 keys and values, fp16
+    scale and zero per key channel and per value token-group); with 8-token
+    windows or the rotary mode it is read as its bf16 reconstruction
+    (512 B per token and KV head)."""
     L, Hkv, Hq, d = w.n_layers, w.n_kv_heads, w.n_q_heads, w.head_dim
-    kv = L * Hkv * (n_fp_tokens * 2 * d * 2 + n_q * 3072)
-    extra = L * Hq * d * 2 + L * Hq * d * 4 + L * Hkv * 2 * d * 2 + L * (n_fp_tokens // 32 + n_q) * 4 * 2
+    W = w.window_tokens
+    q_win = W * 2 * d * 2 if (W == 8 or w.rope_theta > 0) else 3072
+    kv = L * Hkv * (n_fp_tokens * 2 * d * 2 + n_q * q_win)
+    extra = L * Hq * d * 2 + L * Hq * d * 4 + L * Hkv * 2 * d * 2 + L * (n_fp_tokens // W + n_q) * 4 * 2
     return kv, kv + extra
 
 
@@ -343,7 +348,8 @@ def run_tier(args, w):
     ctx.close()
     n_fp_win = int((tiers == 0).sum())
     n_q = int((tiers == 1).sum())
-    n_fp_tokens = n_fp_win * 32 - (-npos % 32)
+    W = w.window_tokens
+    n_fp_tokens = n_fp_win * W - (-npos % W)
     kv_bytes, step_bytes = tier_bytes(w, n_fp_tokens, n_q)
     ms_step = dt * 1e3 / args.steps
     attn_ms, attn_n = prof["attn"]

@@ -107,7 +107,10 @@ static kvev_status tier_create(const kvev_config& f, void* hip_stream, kvev_ctx*
   c->hole_in.assign(c->G, 0);
   c->prefilled.assign(1, 0);
   c->tier_mode = true;
-  c->tw.NW = static_cast<int>((c->cap + kTierWin - 1) / kTierWin);
+  c->tw.W = f.window_tokens;
+  c->tw.rope = f.rope_theta > 0.f;
+  c->tw.mat = c->tw.W == 8 || c->tw.rope;
+  c->tw.NW = static_cast<int>((c->cap + c->tw.W - 1) / c->tw.W);
   c->tw.maxch = 2 * ((c->tw.NW + 7) / 8);
   const hipError_t e = tier_alloc(c);
   if (e != hipSuccess) {
@@ -134,6 +137,7 @@ void kvev_config_init(kvev_config* cfg) {
   cfg->decode_region = 4;
   cfg->access_tau_mult = 2.0f;
   cfg->window_tokens = kTierWin;
+  cfg->rope_theta = 0.f;
 }
 
 kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out) {
@@ -169,6 +173,7 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.prefetch_blocks > 0 && f.offload_blocks <= 0) return bad("prefetch_blocks needs the host-offload tier");
   if (!std::isfinite(f.offload_min_score)) return bad("offload_min_score must be finite");
   if (f.attn_path < KVEV_ATTN_AUTO || f.attn_path > KVEV_ATTN_WHOLE) return bad("unknown attn_path");
+  if (f.rope_theta != 0.f && f.policy != KVEV_TIERED_INT2) return bad("rope_theta applies to the tiered mode only");
   if (f.evict_interval < 0) return bad("evict_interval must be >= 0");
   if (f.evict_interval > 1 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("evict_interval applies to the token policies only");
@@ -188,10 +193,11 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (tiered) {
     if (f.dtype != KVEV_BF16 || f.head_dim != kTierD) return bad("tiered mode: bf16 and head_dim 128 only");
     if (f.batch != 1) return bad("tiered mode: batch must be 1");
-    if (f.window_tokens != kTierWin) return bad("tiered mode: window_tokens must be 32");
+    if (f.window_tokens != 8 && f.window_tokens != 32) return bad("tiered mode: window_tokens must be 8 or 32");
     if (f.fp_windows < 0 || f.int2_windows < 0) return bad("tiered mode: tier capacities must be >= 0");
-    if (f.max_tokens > static_cast<int64_t>(kTierMaxWin) * kTierWin)
-      return bad("tiered mode: max_tokens must be <= 196608");
+    if (f.max_tokens > static_cast<int64_t>(kTierMaxWin) * f.window_tokens)
+      return bad("tiered mode: max_tokens must be <= 12288 windows");
+    if (!(f.rope_theta >= 0.f) || !std::isfinite(f.rope_theta)) return bad("rope_theta must be finite and >= 0");
     if (f.refresh_interval != 1 || f.score_free != 0)
       return bad("tiered mode: refresh_interval must be 1 and score_free 0");
     if (f.n_sink < 0 || f.n_recent < 0) return bad("n_sink and n_recent must be >= 0");

@@ -23,7 +23,9 @@ constexpr int kMaxBlockEntries = 4096;  // block-table entries per sequence (blo
 constexpr int kTierWin = 32;            // tokens per routing window
 constexpr int kTierD = 128;             // head dim of the tiered mode
 constexpr int kTierLedgerBytes = 3072;  // INT2 record per (layer, KV head, window)
-constexpr int kTierMaxWin = 6144;       // windows per sequence (196608 positions)
+constexpr int kTierMaxWin = 12288;      // windows per sequence (393216 positions at 32 tokens a window)
+constexpr int kTierLedgerBytes8 = 1152; // INT2 record of an 8-token window
+inline int tier_rec_bytes(int w) { return w == 8 ? kTierLedgerBytes8 : kTierLedgerBytes; }
 constexpr int kTierXferBlocks = 64;     // blocks per layer of the transition kernel
 // rank-trace diagnostics
 constexpr int kDiagCounts = 12;  // the int32 counts of kvev_diag_group, in order
@@ -95,9 +97,12 @@ struct DevState {
 
 // Device buffers of the two-tier window mode ([L][Hkv][NW] windows).
 struct TierDev {
-  uint16_t* kfp = nullptr;   // [L][Hkv][NW][32][128] bf16 keys, token-major
-  uint16_t* vfp = nullptr;   // [L][Hkv][NW][128][32] bf16 values, channel-major
-  uint8_t* ledger = nullptr; // [L][Hkv][NW][3072] INT2 codes and parameters
+  uint16_t* kfp = nullptr;   // [L][Hkv][NW][W][128] bf16 keys, token-major (rotated in rotary mode)
+  uint16_t* vfp = nullptr;   // [L][Hkv][NW][128][W] bf16 values, channel-major
+  uint8_t* ledger = nullptr; // [L][Hkv][NW][record bytes] INT2 codes and parameters
+  uint16_t* kpre = nullptr;  // rotary mode: [L][Hkv][NW][W][128] bf16 keys before the rotation
+  double* rcs = nullptr;     // rotary mode: [max_tokens][64][2] cos and sin of position * frequency
+  double* ifreq = nullptr;   // rotary mode: [64] frequencies theta^(-2i/128)
   uint8_t* tier = nullptr;   // [L][NW] 0 full precision, 1 INT2, 2 evicted
   uint8_t* hasled = nullptr; // [L][NW] 1 once the window has been quantized
   uint8_t* forced = nullptr; // [L][NW] tiers imported by kvev_tier_import
@@ -119,6 +124,10 @@ struct TierDev {
 // layer: every layer routes the same number of candidates).
 struct TierHost {
   int NW = 0, maxch = 0;
+  int W = 32;          // tokens per window
+  bool rope = false;   // rotary mode (cfg.rope_theta > 0)
+  bool mat = false;    // INT2 windows are attended through their bf16 reconstruction, kept in the
+                       // full-precision storage (8-token windows or rotary mode)
   int64_t npos = 0;  // positions 0 .. npos-1 exist
   int n_fp = 0;      // full-precision windows listed (pinned + local + routed F)
   int n_q = 0;       // INT2 windows listed
@@ -151,6 +160,10 @@ struct TierArgs {
   double* rd_acc;
   int rd_gap, rd_event;
   int L, Hkv, Hq, NW, maxch;
+  int W, rope, mat, recb;  // window tokens, rotary mode, bf16 reconstruction, record bytes
+  uint16_t* kpre;
+  double* rcs;
+  const double* ifreq;
 };
 
 struct Profiler {
@@ -304,6 +317,7 @@ hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host);
 hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* src_dev);
 // two-tier window mode (tier.hip)
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n);
+hipError_t launch_tier_rope_table(kvev_ctx* c, int64_t p0, int64_t n);
 hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new);
 hipError_t launch_tier_attention(kvev_ctx* c, const void* q);
 hipError_t launch_tier_merge(kvev_ctx* c, float* out);

@@ -49,9 +49,13 @@ namespace {
 
 constexpr int D = kTierD;  // head dim
 constexpr int HG = 4;      // query heads per KV head
-constexpr int W = kTierWin;
+constexpr int W = kTierWin;  // the fused INT2 path's window (32 tokens)
 constexpr int kRecK = 0, kRecV = 1024, kRecSK = 2048, kRecZK = 2304, kRecSV = 2560, kRecZV = 2816;
-constexpr int kFW = 2, kQW = 4;  // windows per wave of the attention: full-precision, INT2
+constexpr int kQW = 4;  // INT2 windows per wave of the fused INT2 path
+// 8-token record: key codes [8][128] and value codes [8][128] at 2 bits
+// (element e at byte e / 4, bits 2 (e % 4)), key scale and zero [128], value
+// scale and zero [4][8] (fp16)
+constexpr int kRec8K = 0, kRec8V = 256, kRec8SK = 512, kRec8ZK = 768, kRec8SV = 1024, kRec8ZV = 1088;
 
 __device__ __forceinline__ bf16x8_t as_b8(const uint4& r) {
   bf16x8_t v;
@@ -139,6 +143,18 @@ __device__ __forceinline__ void wave_lds_order() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Rotary embedding of channel c of a key or query: x its value, y the value
+// of its partner channel c ^ 64, rc the (cos, sin) row of its position.  The
+// products and the sum are separately rounded fp64 operations (no fused
+// multiply-add), the result rounded to fp32.
+__device__ __forceinline__ float rope_elem(float x, float y, int c, const double* __restrict__ rc) {
+  const double cs = rc[2 * (c & 63)], sn = rc[2 * (c & 63) + 1];
+  const double a = __dmul_rn(static_cast<double>(x), cs), b = __dmul_rn(static_cast<double>(y), sn);
+  return static_cast<float>(c < 64 ? __dsub_rn(a, b) : __dadd_rn(a, b));
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float((b & 0xffffu) << 16); }
+
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -154,20 +170,29 @@ __global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uin
                                                            const uint16_t* __restrict__ v, int n) {
   __shared__ uint16_t vt[W][D + 2];
   const int w = blockIdx.x, h = blockIdx.y, l = blockIdx.z, tid = threadIdx.x;
+  const int Wn = A.W;  // tokens per window (8 or 32)
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int64_t src0 = lh * n;
-  uint16_t* kd = A.kfp + (lh * A.NW + w) * W * D;
-  uint16_t* vd = A.vfp + (lh * A.NW + w) * W * D;
-  for (int i = tid; i < W * D; i += 256) {
+  uint16_t* kd = A.kfp + (lh * A.NW + w) * Wn * D;
+  uint16_t* vd = A.vfp + (lh * A.NW + w) * Wn * D;
+  for (int i = tid; i < Wn * D; i += 256) {
     const int r = i / D, c = i % D;
-    const int p = w * W + r;
+    const int p = w * Wn + r;
     const bool in = p < n;
-    kd[i] = in ? k[(src0 + p) * D + c] : 0;
+    const uint16_t kv = in ? k[(src0 + p) * D + c] : 0;
+    if (A.rope) {  // rotary mode: keep the key as given, store it rotated at its position
+      A.kpre[(lh * A.NW + w) * Wn * D + i] = kv;
+      const uint16_t kp = in ? k[(src0 + p) * D + (c ^ 64)] : 0;
+      kd[i] = in ? static_cast<uint16_t>(bf16_rne(rope_elem(bf2f(kv), bf2f(kp), c, A.rcs + static_cast<int64_t>(p) * 128)))
+                 : 0;
+    } else {
+      kd[i] = kv;
+    }
     vt[r][c] = in ? v[(src0 + p) * D + c] : 0;
   }
   __syncthreads();
-  for (int i = tid; i < W * D; i += 256) {
-    const int c = i / W, r = i % W;
+  for (int i = tid; i < Wn * D; i += 256) {
+    const int c = i / Wn, r = i % Wn;
     vd[i] = vt[r][c];
   }
   if (h == 0 && tid == 0) {
@@ -180,6 +205,21 @@ __global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uin
 }
 
 // ---------------------------------------------------------------------------
+// Rotary mode: (cos, sin) of position * frequency_i for positions
+// [p0, p0 + n) and i < 64, in fp64.  One thread per (position, i).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tier_rope_table_kernel(TierArgs A, int64_t p0, int64_t n) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n * 64) return;
+  const int64_t p = p0 + idx / 64;
+  const int i = static_cast<int>(idx % 64);
+  double sn, cs;
+  sincos(__dmul_rn(static_cast<double>(p), A.ifreq[i]), &sn, &cs);
+  A.rcs[(p * 64 + i) * 2] = cs;
+  A.rcs[(p * 64 + i) * 2 + 1] = sn;
+}
+
+// ---------------------------------------------------------------------------
 // Append: the new token (position npos) into its window's storage.  When it
 // opens a window, that window starts full precision with score 0 and joins
 // the full-precision list at index n_fp.  Block (h, l), 128 threads.
@@ -188,10 +228,18 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
                                                           const uint16_t* __restrict__ v_new, int npos,
                                                           int n_fp) {
   const int h = blockIdx.x, l = blockIdx.y, c = threadIdx.x;
+  const int Wn = A.W;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
-  const int w = npos / W, r = npos % W;
-  A.kfp[((lh * A.NW + w) * W + r) * D + c] = k_new[lh * D + c];
-  A.vfp[(lh * A.NW + w) * W * D + c * W + r] = v_new[lh * D + c];
+  const int w = npos / Wn, r = npos % Wn;
+  const int64_t ki = ((lh * A.NW + w) * Wn + r) * D + c;
+  if (A.rope) {
+    A.kpre[ki] = k_new[lh * D + c];
+    A.kfp[ki] = static_cast<uint16_t>(bf16_rne(rope_elem(bf2f(k_new[lh * D + c]), bf2f(k_new[lh * D + (c ^ 64)]), c,
+                                                         A.rcs + static_cast<int64_t>(npos) * 128)));
+  } else {
+    A.kfp[ki] = k_new[lh * D + c];
+  }
+  A.vfp[(lh * A.NW + w) * Wn * D + c * Wn + r] = v_new[lh * D + c];
   if (r == 0 && h == 0 && c == 0) {
     const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
     A.fplist[static_cast<int64_t>(l) * A.NW + n_fp] = w;
@@ -203,8 +251,9 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
 
 // ---------------------------------------------------------------------------
 // Attention over the accessible windows of (layer l, KV head h).  Block
-// (chunk, h, l) of 4 waves; a wave takes kFW = 2 consecutive windows of the
-// full-precision list (a chunk 8) or kQW = 4 of the INT2 list (a chunk 16).
+// (chunk, h, l) of 4 waves; a wave takes 64 tokens of the full-precision
+// list (2 windows of 32 or 8 of 8) or kQW = 4 windows of the INT2 list
+// (the fused INT2 path: a chunk 16).
 // Chunks [0, nch_f) cover the full-precision list, the rest the INT2 list.  Writes the chunk's (max, sum) and unnormalised
 // output per head, and per window and head the sum of exp(s - chunk max)
 // over the window's tokens (its attention mass before normalisation).
@@ -216,14 +265,20 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
 // ---------------------------------------------------------------------------
 // Three waves per SIMD: the INT2 windows are bound by vector arithmetic and
 // memory latency, and the register cap this sets (168) costs no spills.
+// WT: tokens per window (32 or 8).  MAT: INT2 windows are read from their
+// bf16 reconstruction in the full-precision storage (8-token windows,
+// rotary mode), so every window takes the full-precision path; in rotary
+// mode the queries are rotated at the new token's position npos - 1.
+template <int WT, bool MAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tier_attn_kernel(
-    TierArgs A, const uint16_t* __restrict__ q,
-                                                        int n_fp, int n_q, int nch_f, int npos,
-                                                        float scale) {
+    TierArgs A, const uint16_t* __restrict__ q, int n_fp, int n_q, int nch_f, int npos, float scale) {
+  constexpr int FW = 64 / WT;                    // full-precision-path windows per wave
+  constexpr int NWIN = FW > kQW ? FW : kQW;
+  static_assert(WT == 32 || (WT == 8 && MAT), "8-token windows are read through the full-precision path");
   __shared__ __align__(16) float p_lds[4][HG][32 * kQW];
   __shared__ __align__(16) float o_lds[4][HG][D];
   __shared__ float wstat[4][HG][2];
-  __shared__ float e_lds[4][kQW][HG];
+  __shared__ float e_lds[4][NWIN][HG];
   __shared__ uint4 opnd[4][2][129];  // INT2 A operands staged per wave; [w][0][128] is zero
 
   const int chunk = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
@@ -231,15 +286,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r16 = lane & 15, q4 = lane >> 4;
   const bool isq = chunk >= nch_f;
-  const int wpw = isq ? kQW : kFW;  // windows per wave
-  const int base = isq ? (chunk - nch_f) * 4 * kQW : chunk * 4 * kFW;
+  const bool fused = isq && !MAT;  // the fused INT2 path
+  const int wpw = fused ? kQW : FW;  // windows per wave
+  const int base = isq ? (chunk - nch_f) * 4 * wpw : chunk * 4 * FW;
   const int nlist = isq ? n_q : n_fp;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int* list = (isq ? A.qlist : A.fplist) + static_cast<int64_t>(l) * A.NW;
-  int win[kQW];
-  bool live[kQW];
+  int win[NWIN];
+  bool live[NWIN];
 #pragma unroll
-  for (int k = 0; k < kQW; ++k) {
+  for (int k = 0; k < NWIN; ++k) {
     const int idx = base + wpw * wave + k;
     live[k] = k < wpw && idx < nlist;
     win[k] = live[k] ? list[idx] : 0;
@@ -252,46 +308,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
     for (int s = 0; s < 4; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qp + 32 * s);
   }
+  if constexpr (MAT) {
+    if (A.rope) {  // channel 32s + 8q4 + e (s < 2) pairs with the same element of k-step s + 2
+      const double* rc = A.rcs + static_cast<int64_t>(npos - 1) * 128;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t a = word_of(qraw[s], u), b = word_of(qraw[s + 2], u);
+          uint32_t ra = 0, rb = 0;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int c = 32 * s + 8 * q4 + 2 * u + half;
+            const float x = bf2f(a >> (16 * half)), y = bf2f(b >> (16 * half));
+            ra |= bf16_rne(rope_elem(x, y, c, rc)) << (16 * half);
+            rb |= bf16_rne(rope_elem(y, x, c + 64, rc)) << (16 * half);
+          }
+          lo[u] = ra;
+          hi[u] = rb;
+        }
+        qraw[s] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        qraw[s + 2] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    }
+  }
 
-  float sv[2 * kQW][HG];  // logits of n-tile jj = 2k + j (lanes q4 == 0 hold them)
+  float sv[2 * kQW][HG];  // logits of n-tile jj (lanes q4 == 0 hold them)
   f32x4_t oacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float bzl = 0.f;  // INT2: sum_t p_t z_tg of (head, group) over the lane's tokens
 
-  if (!isq) {
-    // ---- full-precision windows -------------------------------------------
+  if (!fused) {
+    // ---- windows read from full-precision storage ---------------------------
+    // A wave reads 64 tokens: 2 windows of 32, or 8 of 8.  K tile jj is
+    // tokens 16jj .. 16jj+15 of the wave (token r16 of the tile in window
+    // slot (16jj + r16) / WT); p.V k-step k is tokens 32k .. 32k+31 (the
+    // lane's 8 tokens 8q4 .. +8 in slot (32k + 8q4) / WT).
     bf16x8_t qa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[s] = as_b8(r16 < HG ? qraw[s] : make_uint4(0, 0, 0, 0));
     uint4 kr[4][4], vr[2][8];
+    int kpos[4];
+    bool klive[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int k = jj >> 1;
-      const uint16_t* kb = A.kfp + ((lh * A.NW + win[k]) * W + 16 * (jj & 1) + r16) * D + 8 * q4;
+      int wk, rk;
+      if constexpr (WT == 32) {
+        wk = win[jj >> 1];
+        klive[jj] = live[jj >> 1];
+        rk = 16 * (jj & 1) + r16;
+      } else {
+        const bool up = r16 >= 8;
+        wk = up ? win[2 * jj + 1] : win[2 * jj];
+        klive[jj] = up ? live[2 * jj + 1] : live[2 * jj];
+        rk = r16 & 7;
+      }
+      kpos[jj] = wk * WT + rk;
+      const uint16_t* kb = A.kfp + ((lh * A.NW + wk) * WT + rk) * D + 8 * q4;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        kr[jj][s] = live[k] ? *reinterpret_cast<const uint4*>(kb + 32 * s) : make_uint4(0, 0, 0, 0);
+        kr[jj][s] = klive[jj] ? *reinterpret_cast<const uint4*>(kb + 32 * s) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint16_t* vb = A.vfp + (lh * A.NW + win[k]) * W * D + r16 * W + 8 * q4;
+      int wv, r0;
+      bool lv;
+      if constexpr (WT == 32) {
+        wv = win[k];
+        lv = live[k];
+        r0 = 8 * q4;
+      } else {
+        const int a = 4 * k;
+        wv = q4 == 0 ? win[a] : (q4 == 1 ? win[a + 1] : (q4 == 2 ? win[a + 2] : win[a + 3]));
+        lv = q4 == 0 ? live[a] : (q4 == 1 ? live[a + 1] : (q4 == 2 ? live[a + 2] : live[a + 3]));
+        r0 = 0;
+      }
+      const uint16_t* vb = A.vfp + (lh * A.NW + wv) * WT * D + r16 * WT + r0;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
-        vr[k][ct] = live[k] ? *reinterpret_cast<const uint4*>(vb + 16 * ct * W) : make_uint4(0, 0, 0, 0);
+        vr[k][ct] = lv ? *reinterpret_cast<const uint4*>(vb + 16 * ct * WT) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) acc = mfma(qa[s], as_b8(kr[jj][s]), acc);
-      const int k = jj >> 1;
-      const int p = win[k] * W + 16 * (jj & 1) + r16;
-      const bool valid = q4 == 0 && live[k] && p < npos;
+      const bool valid = q4 == 0 && klive[jj] && kpos[jj] < npos;
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) sv[jj][hh] = valid ? acc[hh] * scale : -INFINITY;
     }
-    // softmax statistics of the wave, probabilities to LDS
+    // softmax statistics of the wave, per-window masses, probabilities to LDS
     float mh[HG];
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
@@ -300,20 +408,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     }
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
-      float e0 = 0.f, e1 = 0.f;
+      float tile[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const float pv = mh[hh] == -INFINITY ? 0.f : __expf(sv[jj][hh] - mh[hh]);
         sv[jj][hh] = pv;
-        if (jj < 2) e0 += pv; else e1 += pv;
+        tile[jj] = pv;
       }
-      e0 = row16_sum(e0);
-      e1 = row16_sum(e1);
+      float tot = 0.f;
+      if constexpr (WT == 32) {
+        const float e0 = row16_sum(tile[0] + tile[1]), e1 = row16_sum(tile[2] + tile[3]);
+        if (lane == 0) {
+          e_lds[wave][0][hh] = e0;
+          e_lds[wave][1][hh] = e1;
+        }
+        tot = e0 + e1;
+      } else {
+        // a tile holds two windows: lanes 0..7 and 8..15 of the row
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float e = tile[jj];
+          e += __shfl_xor(e, 1, kWave);
+          e += __shfl_xor(e, 2, kWave);
+          e += __shfl_xor(e, 4, kWave);
+          if (lane == 0) e_lds[wave][2 * jj][hh] = e;
+          if (lane == 8) e_lds[wave][2 * jj + 1][hh] = e;
+          tot += e + __shfl_xor(e, 8, kWave);
+        }
+      }
       if (lane == 0) {
-        e_lds[wave][0][hh] = e0;
-        e_lds[wave][1][hh] = e1;
         wstat[wave][hh][0] = mh[hh];
-        wstat[wave][hh][1] = e0 + e1;
+        wstat[wave][hh][1] = tot;
       }
     }
     if (q4 == 0) {
@@ -333,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) oacc[ct] = mfma(pa, as_b8(vr[k][ct]), oacc[ct]);
     }
-  } else {
+  } else if constexpr (!MAT) {
     // ---- INT2 windows -------------------------------------------------------
     // The scaled operands are formed once per (head, channel) and (head,
     // token, group) by the wave's lanes and staged in LDS as matrix-core A
@@ -490,7 +615,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
   for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) bzh[hh][g] = isq ? __shfl(bzl, 16 * hh + g, kWave) : 0.f;
+    for (int g = 0; g < 4; ++g) bzh[hh][g] = fused ? __shfl(bzl, 16 * hh + g, kWave) : 0.f;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
 #pragma unroll
@@ -604,12 +729,13 @@ __global__ __launch_bounds__(256) void tier_merge_kernel(TierArgs A, float* __re
 // (1/Hq) sum over KV heads and their query heads of the window's
 // probability mass.  Block (x, l), 256 threads, one window per thread.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, int n_q, int nch_f) {
+__global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, int n_q, int nch_f, int cw_f,
+                                                        int cw_q) {
   const int l = blockIdx.y;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= n_fp + n_q) return;
   const bool isq = idx >= n_fp;
-  const int chunk = isq ? nch_f + (idx - n_fp) / (4 * kQW) : idx / (4 * kFW);
+  const int chunk = isq ? nch_f + (idx - n_fp) / cw_q : idx / cw_f;  // cw_*: windows per chunk
   const int w = isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
                     : A.fplist[static_cast<int64_t>(l) * A.NW + idx];
   float acc = 0.f;
@@ -670,7 +796,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     hl[w] = A.hasled[lw0 + w];
   }
   __syncthreads();
-  auto aged = [&](int w) { return w >= np && (w + 1) * W <= recent_lo; };
+  auto aged = [&](int w) { return w >= np && (w + 1) * A.W <= recent_lo; };
   if (!forced) {
     for (int w = tid; w < nw; w += kRouteNT) {
       if (aged(w) && tl[w] != 2) {
@@ -876,17 +1002,21 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
   __shared__ uint8_t ck[W][D];
   __shared__ uint8_t cv[W][D];
   __shared__ uint32_t recl[kTierLedgerBytes / 4];
+  __shared__ float ksc[D], kzp[D], vsc[W][4], vzp[W][4];  // the window's parameters as fp32
   const int l = blockIdx.y, tid = threadIdx.x;
   const int nj = A.njobs[l];
+  const int Wn = A.W;  // tokens per window (8 or 32)
   // the layer's (job, KV head) pairs, strided over the blocks of the layer
   for (int p = blockIdx.x; p < nj * A.Hkv; p += gridDim.x) {
     const int j = p / A.Hkv, h = p % A.Hkv;
     const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
     const int job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
     const int w = job >> 2, kind = job & 3;
-    uint16_t* kd = A.kfp + (lh * A.NW + w) * W * D;
-    uint16_t* vd = A.vfp + (lh * A.NW + w) * W * D;
-    uint8_t* rec = A.ledger + (lh * A.NW + w) * static_cast<int64_t>(kTierLedgerBytes);
+    uint16_t* kd = A.kfp + (lh * A.NW + w) * Wn * D;
+    uint16_t* vd = A.vfp + (lh * A.NW + w) * Wn * D;
+    // keys are quantized before the rotation in rotary mode
+    const uint16_t* ks = A.rope ? A.kpre + (lh * A.NW + w) * Wn * D : kd;
+    uint8_t* rec = A.ledger + (lh * A.NW + w) * static_cast<int64_t>(A.recb);
     uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
     uint32_t* rec32 = reinterpret_cast<uint32_t*>(rec);
     if (kind == 1) {
@@ -897,12 +1027,14 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i0 = 8 * (tid + 256 * u);
-        kr[u] = *reinterpret_cast<const uint4*>(kd + i0);
-        vr[u] = *reinterpret_cast<const uint4*>(vd + i0);
+        const bool in = i0 < Wn * D;
+        kr[u] = in ? *reinterpret_cast<const uint4*>(ks + i0) : make_uint4(0, 0, 0, 0);
+        vr[u] = in ? *reinterpret_cast<const uint4*>(vd + i0) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i0 = 8 * (tid + 256 * u);
+        if (i0 >= Wn * D) continue;
         const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
         const uint32_t vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
@@ -910,7 +1042,7 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
           const uint32_t kb = (kw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
           const uint32_t vb = (vw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
           xk[(i0 + e) / D][(i0 + e) % D] = __uint_as_float(kb << 16);
-          xv[(i0 + e) % W][(i0 + e) / W] = __uint_as_float(vb << 16);
+          xv[(i0 + e) % Wn][(i0 + e) / Wn] = __uint_as_float(vb << 16);
         }
       }
       __syncthreads();
@@ -918,21 +1050,36 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         const int c = tid;
         float sc, zp;
         uint16_t s16, z16;
-        int2_group(&xk[0][c], W, D + 1, sc, zp, s16, z16);
-        rec16[kRecSK / 2 + c] = s16;
-        rec16[kRecZK / 2 + c] = z16;
-        for (int r = 0; r < W; ++r) ck[r][c] = int2_code(xk[r][c], sc, zp);
-      } else {  // values: one token's 32-channel group
+        int2_group(&xk[0][c], Wn, D + 1, sc, zp, s16, z16);
+        rec16[(Wn == 8 ? kRec8SK : kRecSK) / 2 + c] = s16;
+        rec16[(Wn == 8 ? kRec8ZK : kRecZK) / 2 + c] = z16;
+        ksc[c] = sc;
+        kzp[c] = zp;
+        for (int r = 0; r < Wn; ++r) ck[r][c] = int2_code(xk[r][c], sc, zp);
+      } else if ((tid - D) / 4 < Wn) {  // values: one token's 32-channel group
         const int r = (tid - D) / 4, g = (tid - D) % 4;
         float sc, zp;
         uint16_t s16, z16;
         int2_group(&xv[r][32 * g], 32, 1, sc, zp, s16, z16);
-        rec16[kRecSV / 2 + 32 * g + r] = s16;
-        rec16[kRecZV / 2 + 32 * g + r] = z16;
+        rec16[(Wn == 8 ? kRec8SV / 2 + 8 * g : kRecSV / 2 + 32 * g) + r] = s16;
+        rec16[(Wn == 8 ? kRec8ZV / 2 + 8 * g : kRecZV / 2 + 32 * g) + r] = z16;
+        vsc[r][g] = sc;
+        vzp[r][g] = zp;
         for (int c = 32 * g; c < 32 * g + 32; ++c) cv[r][c] = int2_code(xv[r][c], sc, zp);
       }
       __syncthreads();
-      {
+      if (Wn == 8) {
+        // 8-token record: four codes a byte, element order (token, channel)
+        const int e = 4 * tid;  // 256 threads cover the 1,024 elements
+        uint32_t kb = 0, vb = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          kb |= static_cast<uint32_t>(ck[(e + u) / D][(e + u) % D]) << (2 * u);
+          vb |= static_cast<uint32_t>(cv[(e + u) / D][(e + u) % D]) << (2 * u);
+        }
+        rec[kRec8K + tid] = static_cast<uint8_t>(kb);
+        rec[kRec8V + tid] = static_cast<uint8_t>(vb);
+      } else {
         // thread = (lane, word): lane = tid / 4, word = tid % 4 (plane word / 2, part word % 2)
         const int ln = tid >> 2, wd = tid & 3, r16 = ln & 15, q4 = ln >> 4;
         const int plane = wd >> 1, part = wd & 1;
@@ -953,8 +1100,38 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         rec32[(kRecK / 4) + 4 * ln + 2 * plane + part] = kw;
         rec32[(kRecV / 4) + 4 * ln + 2 * plane + part] = vw;
       }
+      if (A.mat) {
+        // the reconstruction, rounded to bf16, replaces the full-precision
+        // storage: code * scale + zero (separate fp32 multiply and add),
+        // keys rotated at their original positions in rotary mode
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i0 = 8 * (tid + 256 * u);
+          if (i0 >= Wn * D) continue;
+          uint32_t ko[4] = {0, 0, 0, 0}, vo[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int i = i0 + e;
+            const int r = i / D, c = i % D;  // key element (token r, channel c)
+            float kx = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][c]), ksc[c]), kzp[c]);
+            if (A.rope) {
+              const int cp = c ^ 64;
+              const float ky = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][cp]), ksc[cp]), kzp[cp]);
+              kx = rope_elem(kx, ky, c, A.rcs + static_cast<int64_t>(w * Wn + r) * 128);
+            }
+            const int vc = i / Wn, vr_ = i % Wn;  // value element (channel vc, token vr_)
+            const float vx = __fadd_rn(__fmul_rn(static_cast<float>(cv[vr_][vc]), vsc[vr_][vc >> 5]), vzp[vr_][vc >> 5]);
+            ko[e >> 1] |= bf16_rne(kx) << (16 * (e & 1));
+            vo[e >> 1] |= bf16_rne(vx) << (16 * (e & 1));
+          }
+          *reinterpret_cast<uint4*>(kd + i0) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+          *reinterpret_cast<uint4*>(vd + i0) = make_uint4(vo[0], vo[1], vo[2], vo[3]);
+        }
+      }
       __syncthreads();
-    } else if (kind == 2) {
+    } else if (kind == 2 && !A.mat) {
+      // (with bf16 reconstruction the storage already holds what a
+      // promotion would write)
       // the record into LDS (3,072 B, three words per thread), then 8
       // consecutive elements of K (one token) and of V (one channel) per
       // thread and 16-byte store
@@ -1015,12 +1192,13 @@ __global__ __launch_bounds__(256) void tier_export_kernel(TierArgs A, int l, int
                                                           uint16_t* __restrict__ v_out) {
   const int w = blockIdx.x, tid = threadIdx.x;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
-  const uint16_t* ks = A.kfp + (lh * A.NW + w) * W * D;
-  const uint16_t* vs = A.vfp + (lh * A.NW + w) * W * D;
-  for (int i = tid; i < W * D; i += 256) {
+  const int Wn = A.W;
+  const uint16_t* ks = A.kfp + (lh * A.NW + w) * Wn * D;
+  const uint16_t* vs = A.vfp + (lh * A.NW + w) * Wn * D;
+  for (int i = tid; i < Wn * D; i += 256) {
     const int r = i / D, c = i % D;
-    k_out[static_cast<int64_t>(w) * W * D + i] = ks[i];
-    v_out[static_cast<int64_t>(w) * W * D + i] = vs[c * W + r];
+    k_out[static_cast<int64_t>(w) * Wn * D + i] = ks[i];
+    v_out[static_cast<int64_t>(w) * Wn * D + i] = vs[c * Wn + r];
   }
 }
 
@@ -1056,11 +1234,30 @@ static TierArgs tier_args(kvev_ctx* c) {
   a.Hq = c->cfg.n_q_heads;
   a.NW = c->tw.NW;
   a.maxch = c->tw.maxch;
+  a.W = c->tw.W;
+  a.rope = c->tw.rope ? 1 : 0;
+  a.mat = c->tw.mat ? 1 : 0;
+  a.recb = tier_rec_bytes(c->tw.W);
+  a.kpre = c->td.kpre;
+  a.rcs = c->td.rcs;
+  a.ifreq = c->td.ifreq;
   return a;
 }
 
+// windows per attention chunk: (full-precision list, INT2 list)
+static void tier_chunk_windows(const kvev_ctx* c, int& cw_f, int& cw_q) {
+  cw_f = 4 * (64 / c->tw.W);
+  cw_q = c->tw.mat ? cw_f : 4 * kQW;
+}
+
+hipError_t launch_tier_rope_table(kvev_ctx* c, int64_t p0, int64_t n) {
+  const int64_t threads = n * 64;
+  tier_rope_table_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, c->stream>>>(tier_args(c), p0, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n) {
-  const int nwin = static_cast<int>((n + W - 1) / W);
+  const int nwin = static_cast<int>((n + c->tw.W - 1) / c->tw.W);
   dim3 grid(nwin, c->cfg.n_kv_heads, c->cfg.n_layers);
   tier_prefill_kernel<<<grid, 256, 0, c->stream>>>(tier_args(c), static_cast<const uint16_t*>(k),
                                                    static_cast<const uint16_t*>(v), static_cast<int>(n));
@@ -1076,17 +1273,27 @@ hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new)
 }
 
 hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
-  const int nch_f = (c->tw.n_fp + 4 * kFW - 1) / (4 * kFW), nch_q = (c->tw.n_q + 4 * kQW - 1) / (4 * kQW);
+  int cw_f, cw_q;
+  tier_chunk_windows(c, cw_f, cw_q);
+  const int nch_f = (c->tw.n_fp + cw_f - 1) / cw_f, nch_q = (c->tw.n_q + cw_q - 1) / cw_q;
   const int npos = static_cast<int>(c->tw.npos);
   TierArgs a = tier_args(c);
   dim3 grid(nch_f + nch_q, c->cfg.n_kv_heads, c->cfg.n_layers);
-  tier_attn_kernel<<<grid, 256, 0, c->stream>>>(a, static_cast<const uint16_t*>(q), c->tw.n_fp, c->tw.n_q,
-                                                nch_f, npos, 1.0f / sqrtf(static_cast<float>(D)));
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const float scale = 1.0f / sqrtf(static_cast<float>(D));
+  if (c->tw.W == 8)
+    tier_attn_kernel<8, true><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
+  else if (c->tw.mat)
+    tier_attn_kernel<32, true><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
+  else
+    tier_attn_kernel<32, false><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
-  const int nch_f = (c->tw.n_fp + 4 * kFW - 1) / (4 * kFW), nch_q = (c->tw.n_q + 4 * kQW - 1) / (4 * kQW);
+  int cw_f, cw_q;
+  tier_chunk_windows(c, cw_f, cw_q);
+  const int nch_f = (c->tw.n_fp + cw_f - 1) / cw_f, nch_q = (c->tw.n_q + cw_q - 1) / cw_q;
   TierArgs a = tier_args(c);
   hipError_t e;
   dim3 gm(HG, c->cfg.n_kv_heads, c->cfg.n_layers);
@@ -1096,7 +1303,7 @@ hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
   if (e != hipSuccess) return e;
   const int ntot = c->tw.n_fp + c->tw.n_q;
   dim3 gs((ntot + 255) / 256, c->cfg.n_layers);
-  tier_mass_kernel<<<gs, 256, 0, c->stream>>>(a, c->tw.n_fp, c->tw.n_q, nch_f);
+  tier_mass_kernel<<<gs, 256, 0, c->stream>>>(a, c->tw.n_fp, c->tw.n_q, nch_f, cw_f, cw_q);
   return hipGetLastError();
 }
 

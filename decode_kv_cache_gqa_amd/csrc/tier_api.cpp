@@ -29,11 +29,12 @@ struct Counts {
 Counts tier_counts(const kvev_ctx* c) {
   Counts k;
   const int64_t npos = c->tw.npos;
-  k.nw = static_cast<int>((npos + kTierWin - 1) / kTierWin);
-  k.np = c->cfg.n_sink > 0 ? std::min(k.nw, (c->cfg.n_sink + kTierWin - 1) / kTierWin) : 0;
+  const int W = c->tw.W;
+  k.nw = static_cast<int>((npos + W - 1) / W);
+  k.np = c->cfg.n_sink > 0 ? std::min(k.nw, (c->cfg.n_sink + W - 1) / W) : 0;
   const int64_t rl = npos - c->cfg.n_recent;
   k.recent_lo = static_cast<int>(std::max<int64_t>(rl, -1));
-  const int64_t full = rl >= 0 ? rl / kTierWin : 0;
+  const int64_t full = rl >= 0 ? rl / W : 0;
   k.na = static_cast<int>(std::max<int64_t>(0, full - k.np));
   return k;
 }
@@ -44,7 +45,7 @@ void tier_free(kvev_ctx* c) {
   auto& t = c->td;
   void* ptrs[] = {t.kfp, t.vfp, t.ledger, t.tier, t.hasled, t.forced, t.S,
                   t.fplist, t.qlist, t.jobs, t.njobs, t.emass, t.rd_fstamp, t.rd_rstamp,
-                  t.rd_run, t.rd_cnt, t.rd_acc};
+                  t.rd_run, t.rd_cnt, t.rd_acc, t.kpre, t.rcs, t.ifreq};
   for (void* p : ptrs)
     if (p) hipFree(p);
   t = TierDev{};
@@ -61,9 +62,15 @@ hipError_t tier_alloc(kvev_ctx* c) {
   auto A = [&](hipError_t r) {
     if (e == hipSuccess && r != hipSuccess) e = r;
   };
-  A(dalloc(&t.kfp, win * kTierWin * kTierD));
-  A(dalloc(&t.vfp, win * kTierWin * kTierD));
-  A(dalloc(&t.ledger, win * kTierLedgerBytes));
+  const size_t W = c->tw.W, recb = tier_rec_bytes(c->tw.W);
+  A(dalloc(&t.kfp, win * W * kTierD));
+  A(dalloc(&t.vfp, win * W * kTierD));
+  A(dalloc(&t.ledger, win * recb));
+  if (c->tw.rope) {
+    A(dalloc(&t.kpre, win * W * kTierD));
+    A(dalloc(&t.rcs, static_cast<size_t>(c->cap) * 64 * 2));
+    A(dalloc(&t.ifreq, 64));
+  }
   A(dalloc(&t.tier, lw));
   A(dalloc(&t.hasled, lw));
   A(dalloc(&t.forced, lw));
@@ -94,9 +101,16 @@ hipError_t tier_alloc(kvev_ctx* c) {
     A(hipMemsetAsync(t.rd_acc, 0, L * 6 * sizeof(double), c->stream));
   }
   // zero the storage so that unwritten rows are finite
-  A(hipMemsetAsync(t.kfp, 0, win * kTierWin * kTierD * 2, c->stream));
-  A(hipMemsetAsync(t.vfp, 0, win * kTierWin * kTierD * 2, c->stream));
-  A(hipMemsetAsync(t.ledger, 0, win * kTierLedgerBytes, c->stream));
+  A(hipMemsetAsync(t.kfp, 0, win * W * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.vfp, 0, win * W * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.ledger, 0, win * recb, c->stream));
+  if (c->tw.rope) {
+    // the rotary frequencies theta^(-2i/128), i < 64, in fp64 on the host
+    double fr[64];
+    for (int i = 0; i < 64; ++i) fr[i] = std::pow(static_cast<double>(f.rope_theta), -2.0 * i / 128.0);
+    A(hipMemsetAsync(t.kpre, 0, win * W * kTierD * 2, c->stream));
+    A(hipMemcpyAsync(t.ifreq, fr, sizeof(fr), hipMemcpyHostToDevice, c->stream));
+  }
   A(hipMemsetAsync(t.tier, 0, lw, c->stream));
   A(hipMemsetAsync(t.hasled, 0, lw, c->stream));
   A(hipMemsetAsync(t.S, 0, lw * sizeof(float), c->stream));
@@ -113,10 +127,11 @@ hipError_t tier_alloc(kvev_ctx* c) {
 kvev_status tier_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
   if (seq != 0) return fail(c, KVEV_EINVAL, "tiered mode: the only sequence is 0");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
+  if (c->tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, 0, n));
   KVEV_HIP(c, launch_tier_prefill(c, k, v, n));
   auto& tw = c->tw;
   tw.npos = n;
-  tw.n_fp = static_cast<int>((n + kTierWin - 1) / kTierWin);
+  tw.n_fp = static_cast<int>((n + tw.W - 1) / tw.W);
   tw.n_q = 0;
   tw.n_kept = 0;
   tw.na_prev = 0;
@@ -129,9 +144,10 @@ kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const voi
   if (!c->prefilled[0]) return fail(c, KVEV_ESTATE, "the sequence has no prefill");
   auto& tw = c->tw;
   if (tw.npos + 1 > c->cap) return fail(c, KVEV_ESTATE, "position capacity exhausted");
-  const bool opens = tw.npos % kTierWin == 0;
+  const bool opens = tw.npos % tw.W == 0;
   {
     ProfScope p(c, "append");
+    if (tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, tw.npos, 1));
     KVEV_HIP(c, launch_tier_append(c, k_new, v_new));
   }
   if (opens) tw.n_fp += 1;
@@ -208,7 +224,7 @@ kvev_status kvev_tier_state(kvev_ctx* c, int32_t layer, float* score, uint8_t* t
   KVEV_LIVE(c);
   if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
   if (layer < 0 || layer >= c->cfg.n_layers) return fail(c, KVEV_EINVAL, "layer out of range");
-  const int64_t nw = (c->tw.npos + kTierWin - 1) / kTierWin;
+  const int64_t nw = (c->tw.npos + c->tw.W - 1) / c->tw.W;
   if (n_windows) *n_windows = nw;
   if (cap < nw) return fail(c, KVEV_ERANGE, "destination too small");
   const int64_t off = static_cast<int64_t>(layer) * c->tw.NW;
@@ -227,8 +243,8 @@ kvev_status kvev_tier_export(kvev_ctx* c, int32_t layer, int32_t h, void* k_out,
   if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
   if (layer < 0 || layer >= c->cfg.n_layers || h < 0 || h >= c->cfg.n_kv_heads)
     return fail(c, KVEV_EINVAL, "layer or KV head out of range");
-  const int nw = static_cast<int>((c->tw.npos + kTierWin - 1) / kTierWin);
-  const int64_t rows = static_cast<int64_t>(nw) * kTierWin;
+  const int nw = static_cast<int>((c->tw.npos + c->tw.W - 1) / c->tw.W);
+  const int64_t rows = static_cast<int64_t>(nw) * c->tw.W;
   if (n_rows) *n_rows = rows;
   if (!k_out || !v_out || cap < rows) return fail(c, KVEV_ERANGE, "destination too small");
   if (nw > 0) KVEV_HIP(c, launch_tier_export(c, layer, h, k_out, v_out, nw));
@@ -240,20 +256,41 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
                              uint16_t* v_zero) {
   KVEV_LIVE(c);
   if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
-  const int nw = static_cast<int>((c->tw.npos + kTierWin - 1) / kTierWin);
+  const int W = c->tw.W, recb = tier_rec_bytes(W);
+  const int nw = static_cast<int>((c->tw.npos + W - 1) / W);
   if (layer < 0 || layer >= c->cfg.n_layers || h < 0 || h >= c->cfg.n_kv_heads || w < 0 || w >= nw)
     return fail(c, KVEV_EINVAL, "layer, KV head or window out of range");
   if (!k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero)
     return fail(c, KVEV_EINVAL, "null argument");
   uint8_t flag = 0;
   const int64_t lw = static_cast<int64_t>(layer) * c->tw.NW + w;
-  std::vector<uint8_t> rec(kTierLedgerBytes);
-  const int64_t roff = ((static_cast<int64_t>(layer) * c->cfg.n_kv_heads + h) * c->tw.NW + w) * kTierLedgerBytes;
+  std::vector<uint8_t> rec(recb);
+  const int64_t roff = ((static_cast<int64_t>(layer) * c->cfg.n_kv_heads + h) * c->tw.NW + w) * recb;
   KVEV_HIP(c, hipMemcpyAsync(&flag, c->td.hasled + lw, 1, hipMemcpyDeviceToHost, c->stream));
-  KVEV_HIP(c, hipMemcpyAsync(rec.data(), c->td.ledger + roff, kTierLedgerBytes, hipMemcpyDeviceToHost,
+  KVEV_HIP(c, hipMemcpyAsync(rec.data(), c->td.ledger + roff, recb, hipMemcpyDeviceToHost,
                              c->stream));
   KVEV_HIP(c, hipStreamSynchronize(c->stream));
   if (!flag) return fail(c, KVEV_EINVAL, "window has never been quantized");
+  if (W == 8) {
+    // 8-token record: key / value codes [8][128] at 2 bits (element e at
+    // byte e / 4, bits 2 (e % 4)), key scale / zero [128], value scale /
+    // zero [4][8] (fp16)
+    for (int e = 0; e < 8 * kTierD; ++e) {
+      k_codes[e] = static_cast<uint8_t>((rec[e / 4] >> (2 * (e % 4))) & 3);
+      v_codes[e] = static_cast<uint8_t>((rec[256 + e / 4] >> (2 * (e % 4))) & 3);
+    }
+    std::memcpy(k_scale, rec.data() + 512, 256);
+    std::memcpy(k_zero, rec.data() + 768, 256);
+    uint16_t vs8[4][8], vz8[4][8];
+    std::memcpy(vs8, rec.data() + 1024, 64);
+    std::memcpy(vz8, rec.data() + 1088, 64);
+    for (int r = 0; r < 8; ++r)
+      for (int g = 0; g < 4; ++g) {
+        v_scale[r * 4 + g] = vs8[g][r];
+        v_zero[r * 4 + g] = vz8[g][r];
+      }
+    return KVEV_OK;
+  }
   uint32_t words[2][256];
   std::memcpy(words[0], rec.data(), 1024);
   std::memcpy(words[1], rec.data() + 1024, 1024);
@@ -301,7 +338,7 @@ kvev_status kvev_tier_import(kvev_ctx* c, int32_t layer, int64_t n_windows, cons
     if (tier[w] > 2) return fail(c, KVEV_EINVAL, "tier code out of range");
     nf += tier[w] == 0;
     nq += tier[w] == 1;
-    const bool aged = w >= k.np && (w + 1) * kTierWin <= k.recent_lo;
+    const bool aged = w >= k.np && (w + 1) * c->tw.W <= k.recent_lo;
     if (!aged && tier[w] != 0) return fail(c, KVEV_EINVAL, "pinned and local windows must be full precision");
   }
   if (nf != c->tw.n_fp || nq != c->tw.n_q)

@@ -58,6 +58,7 @@ class Config(ctypes.Structure):
         ("offload_min_score", ctypes.c_float),
         ("attn_path", ctypes.c_int32),
         ("evict_interval", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
     ]
 
 
@@ -359,7 +360,8 @@ class Context:
     # -- two-tier window mode -----------------------------------------------------
     def tier_state(self, layer):
         """(score float32, tier uint8 (0 FP, 1 INT2, 2 evicted), ledger bool) by window."""
-        cap = (self.cfg.max_tokens + 31) // 32
+        W = self.cfg.window_tokens
+        cap = (self.cfg.max_tokens + W - 1) // W
         sc = np.zeros(cap, np.float32)
         tr = np.zeros(cap, np.uint8)
         lg = np.zeros(cap, np.uint8)
@@ -371,10 +373,11 @@ class Context:
         return sc[:m].copy(), tr[:m].copy(), lg[:m].astype(bool)
 
     def tier_export(self, layer, kv_head):
-        """Full-precision storage of (layer, KV head) by position: k, v [32 * windows, d]."""
+        """Full-precision storage of (layer, KV head) by position: k, v [W * windows, d]."""
         import torch
         c = self.cfg
-        cap = ((c.max_tokens + 31) // 32) * 32
+        W = c.window_tokens
+        cap = ((c.max_tokens + W - 1) // W) * W
         k = torch.empty((cap, c.head_dim), dtype=self.dtype, device="cuda")
         v = torch.empty_like(k)
         n = ctypes.c_int64()
@@ -383,14 +386,15 @@ class Context:
         return k[: n.value].clone(), v[: n.value].clone()
 
     def tier_ledger(self, layer, kv_head, window):
-        """INT2 record: (k_codes [32,128], k_scale [128], k_zero [128], v_codes [32,128],
-        v_scale [32,4], v_zero [32,4]); parameters as float16."""
-        kc = np.zeros((32, self.cfg.head_dim), np.uint8)
+        """INT2 record: (k_codes [W,128], k_scale [128], k_zero [128], v_codes [W,128],
+        v_scale [W,4], v_zero [W,4]); parameters as float16."""
+        W = self.cfg.window_tokens
+        kc = np.zeros((W, self.cfg.head_dim), np.uint8)
         vc = np.zeros_like(kc)
         ks = np.zeros(128, np.uint16)
         kz = np.zeros(128, np.uint16)
-        vs = np.zeros((32, 4), np.uint16)
-        vz = np.zeros((32, 4), np.uint16)
+        vs = np.zeros((W, 4), np.uint16)
+        vz = np.zeros((W, 4), np.uint16)
         args = [a.ctypes.data_as(ctypes.c_void_p) for a in (kc, ks, kz, vc, vs, vz)]
         self._check(lib().kvev_tier_ledger(self._h, layer, kv_head, window, *args))
         return kc, ks.view(np.float16), kz.view(np.float16), vc, vs.view(np.float16), vz.view(np.float16)
@@ -517,7 +521,7 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=TIERED_INT2,
             n_sink=w.n_sink, n_recent=w.n_recent, budget=1, window_tokens=w.window_tokens,
             fp_windows=w.fp_windows, int2_windows=w.int2_windows, route_interval=w.route_interval,
-            revival_gap=w.revival_gap if revival_gap is None else revival_gap)
+            revival_gap=w.revival_gap if revival_gap is None else revival_gap, rope_theta=w.rope_theta)
         return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

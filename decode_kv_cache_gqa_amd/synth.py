@@ -160,6 +160,7 @@ class Workload:
     revival_gap: int = 0            # tiered mode: routing diagnostics, sustained-absence length (0: off)
     attn_path: int = 0              # token modes: attention kernel (0 auto, 1 split, 2 whole-cache)
     evict_interval: int = 1         # token modes: select only every evict_interval steps
+    rope_theta: float = 0.0         # tiered mode: keys and queries arrive before the rotary embedding
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -473,6 +474,19 @@ def workload(name: str) -> Workload:
     if name == "qevict131k_omega8":
         # the review's routing interval: one routing event every 8 steps (section 4.2 Eq.1)
         return replace(workload("qevict131k"), name="qevict_131k_fp5_int2_20_omega8", route_interval=8)
+    if name == "qevict65k_w8_rope":
+        # the review's own defaults: 8-token windows, routing every 8 steps, keys quantized before
+        # the rotary embedding and rotated again on promotion (section 4.4), tier capacities from
+        # the byte budget with q = 0.70 (section 4.3 Eq.3): B_hist = 10% of the prefill's
+        # full-precision bytes, M_f = 8 tokens x 4,096 B and M_q = 8 KV heads x the 1,152-byte
+        # record, per window and layer
+        n = 65536
+        m_f, m_q = 8 * 4096, 8 * 1152
+        b_hist = 0.1 * (n // 8) * m_f
+        return Workload("qevict_65k_w8_rope", 32, 32, 8, 128, "bf16", (n,), 128, seed=1006,
+                        policy="tiered_int2", n_sink=5, n_recent=32, n_epochs=4, epoch_steps=32,
+                        window_tokens=8, fp_windows=int(0.3 * b_hist // m_f),
+                        int2_windows=int(0.7 * b_hist // m_q), route_interval=8, rope_theta=500000.0)
     if name == "qevict131k_allfp":
         # calibration: every routed window full precision (the tier split of the attention)
         return replace(workload("qevict131k"), name="qevict_131k_allfp", fp_windows=1024, int2_windows=0)
@@ -484,4 +498,5 @@ def workload(name: str) -> Workload:
 
 WORKLOADS = ("tiny", "llama8b_32k", "lazy16x8k", "scorefree16x8k", "lrfu64", "qevict131k",
              "llama8b_32k_pooled", "llama8b_32k_vnorm_entropy", "qwen7b_32k", "qevict131k_omega8",
-             "llama8b_32k_diag", "lrfu64_offload", "lazy16x8k_evict8", "qevict131k_allfp", "qevict131k_allint2")
+             "llama8b_32k_diag", "lrfu64_offload", "lazy16x8k_evict8", "qevict131k_allfp", "qevict131k_allint2",
+             "qevict65k_w8_rope")

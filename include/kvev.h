@@ -150,11 +150,12 @@ typedef struct {
                                                  is >= access_tau_mult / (resident tokens);
                                                  "MemDecay" section IV-A uses 2 */
   /* KVEV_TIERED_INT2 only: dtype bf16, head_dim 128, 4 query heads per KV
-   * head, batch 1, max_tokens <= 196608, refresh_interval 1, score_free 0;
+   * head, batch 1, max_tokens <= 12288 windows, refresh_interval 1, score_free 0;
    * budget is ignored (the tier capacities replace it).  n_sink positions
    * (their windows) and the n_recent newest positions (their windows) stay
    * full precision and are never routed. */
-  int32_t window_tokens;                      /* tokens per window; must be 32 */
+  int32_t window_tokens;                      /* tokens per window: 32, or 8 ("QEvict" review,
+                                                 section 5: the review's default) */
   int32_t fp_windows;                         /* K_f: routed windows kept in full precision */
   int32_t int2_windows;                       /* K_q: routed windows kept in INT2 */
   /* KVEV_EMA and KVEV_CUMULATIVE only (0 in the other modes). */
@@ -218,12 +219,27 @@ typedef struct {
    * evict every 8 steps"; 0 or 1: every step ("What Matters ...", section
    * 3.2 evicts every step).  kvev_evict always selects. */
   int32_t evict_interval;
+  /* KVEV_TIERED_INT2 only (0 otherwise): rotary mode ("QEvict" review,
+   * section 4.4, "Positional handling for promoted keys").  0: off, keys
+   * carry no rotation.  theta > 0: q, k_new and the prefill keys arrive
+   * before the rotary embedding; the library rotates channel pair (i, i+64)
+   * of a key at position p by p * theta^(-2i/128) (angles and rotation in
+   * fp64, rounded to fp32 then bf16) and stores the rotated keys as full
+   * precision; keys are quantized from their values before the rotation
+   * (kept until the first demotion), and a reconstruction is rotated again
+   * at the window's original positions.  The query of a step is rotated at
+   * the new token's position.  With rotary mode or 8-token windows, an INT2
+   * window is attended through its reconstruction rounded to bf16, which is
+   * written into its full-precision storage at its first demotion (so a
+   * promotion leaves that storage as it is). */
+  float rope_theta;
 } kvev_config;
 
 typedef enum { KVEV_ATTN_AUTO = 0, KVEV_ATTN_SPLIT = 1, KVEV_ATTN_WHOLE = 2 } kvev_attn_path;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
- * refresh_interval 1, no protection, window_tokens 32; shape fields zero. */
+ * refresh_interval 1, no protection, window_tokens 32, rope_theta 0; shape
+ * fields zero. */
 void kvev_config_init(kvev_config* cfg);
 
 /* Validate *cfg, allocate the page pool and all per-step state on the
@@ -488,7 +504,7 @@ kvev_status kvev_tier_capacities(double b_hist, double q, double m_f, double m_q
  * calls below). */
 
 /* Copy the window state of `layer` (windows 0..*n_windows-1, window w =
- * positions [32w, 32w+32)) to host buffers: score, tier (0 full precision,
+ * positions [W w, W w + W), W = window_tokens) to host buffers: score, tier (0 full precision,
  * 1 INT2, 2 evicted), ledger flag (1 once quantized).  Any may be NULL.
  * Synchronises.  Errors: KVEV_EINVAL (not tiered mode, bad layer),
  * KVEV_ERANGE (cap too small). */
@@ -496,18 +512,19 @@ kvev_status kvev_tier_state(kvev_ctx* ctx, int32_t layer, float* score, uint8_t*
                             uint8_t* ledger, int64_t cap, int64_t* n_windows);
 
 /* Copy the full-precision storage of (layer, kv_head) for windows
- * 0..nw-1 into device k_out, v_out, each [32 * nw][128] bf16 by position
- * (rows of evicted windows and of INT2 windows hold whatever the storage
- * holds: the original values, or the last promotion's).  cap = rows the
- * buffers hold; *n_rows = 32 * nw.  Stream-ordered.  Errors: KVEV_EINVAL,
+ * 0..nw-1 into device k_out, v_out, each [W * nw][128] bf16 by position
+ * (keys rotated in rotary mode; rows of evicted windows and of INT2 windows
+ * hold whatever the storage holds: the original values, the last
+ * promotion's, or, with bf16 reconstruction, the reconstruction).  cap =
+ * rows the buffers hold; *n_rows = W * nw.  Stream-ordered.  Errors: KVEV_EINVAL,
  * KVEV_ERANGE. */
 kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void* k_out,
                              void* v_out, int64_t cap, int64_t* n_rows);
 
 /* Copy and unpack the INT2 record of (layer, kv_head, window) to host
- * buffers: k_codes [32][128] (token, channel), k_scale / k_zero [128] fp16
- * bits, v_codes [32][128], v_scale / v_zero [32][4] fp16 bits (token,
- * 32-channel group).  Synchronises.  Errors: KVEV_EINVAL (not tiered mode,
+ * buffers: k_codes [W][128] (token, channel; keys before the rotation in
+ * rotary mode), k_scale / k_zero [128] fp16 bits, v_codes [W][128],
+ * v_scale / v_zero [W][4] fp16 bits (token, 32-channel group).  Synchronises.  Errors: KVEV_EINVAL (not tiered mode,
  * bad indices, window never quantized). */
 kvev_status kvev_tier_ledger(kvev_ctx* ctx, int32_t layer, int32_t kv_head, int32_t window,
                              uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,

@@ -897,10 +897,15 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     t_start = time.time()
     ctx = kvev.context_for(w, max_steps=steps, revival_gap=revival_gap)
     rdiag = {l: orc.RoutingDiagnostics(revival_gap) for l in layers} if revival_gap else None
+    # 8-token windows and the rotary mode read INT2 windows through their bf16
+    # reconstruction, kept in the full-precision storage
+    mat = w.window_tokens == 8 or w.rope_theta > 0
     orcs = {l: orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                                 k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
                                 n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1,
-                                route_interval=w.route_interval) for l in layers}
+                                route_interval=w.route_interval, rope_theta=w.rope_theta,
+                                reconstruct_bf16=mat) for l in layers}
+    W = w.window_tokens
     K, V = w.prefill_kv(0, device=device)
     ctx.prefill(0, K.contiguous(), V.contiguous())
     for l in layers:
@@ -987,13 +992,26 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
                 st.exact_selection_checks += 1
                 if kv_every and (t % kv_every == 0 or t == 1 or t == steps):
                     lay = o.layers[l]
-                    rows = np.concatenate([np.arange(32 * x, min(32 * x + 32, o.npos)) for x in np.flatnonzero(ot == 0)])
+                    # full-precision windows (and, with bf16 reconstruction, INT2 windows, whose
+                    # storage holds the reconstruction)
+                    held = np.flatnonzero((ot == 0) | ((ot == 1) & mat))
+                    rows = np.concatenate([np.arange(W * x, min(W * x + W, o.npos)) for x in held])
                     for h in range(w.n_kv_heads):
                         gk, gv = ctx.tier_export(l, h)
                         idx = torch.from_numpy(rows)
                         rk = torch.from_numpy(lay.K[h, rows].copy()).to(w.torch_dtype)
                         rv = torch.from_numpy(lay.V[h, rows].copy()).to(w.torch_dtype)
-                        assert torch.equal(gk.cpu()[idx], rk), f"step {t} l={l} kvh={h}: full-precision K differs"
+                        gkr = gk.cpu()[idx]
+                        if w.rope_theta > 0 and not torch.equal(gkr, rk):
+                            # rotated keys: the device's and numpy's fp64 sin / cos may differ in the
+                            # last bit, which can move a bf16 rounding by one unit, rarely
+                            d = (gkr.view(torch.int16).int() - rk.view(torch.int16).int()).abs()
+                            nbad = int((d != 0).sum())
+                            assert int(d.max()) == 1 and nbad <= max(2, rk.numel() // 100000), (
+                                f"step {t} l={l} kvh={h}: rotated K differs in {nbad} elements (max {int(d.max())} ulp)")
+                            st.rope_ulp = getattr(st, "rope_ulp", 0) + nbad
+                        else:
+                            assert torch.equal(gkr, rk), f"step {t} l={l} kvh={h}: full-precision K differs"
                         assert torch.equal(gv.cpu()[idx], rv), f"step {t} l={l} kvh={h}: full-precision V differs"
                         st.kv_checks += 1
                 if ledger_every and (t % ledger_every == 0 or t == 1):

@@ -101,7 +101,12 @@ def _create(**kw):
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, batch=2), "batch"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, window_tokens=16), "window_tokens"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, fp_windows=-1), "capacities"),
-    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, max_tokens=200000), "196608"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, max_tokens=400000), "12288 windows"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, window_tokens=8, max_tokens=100000),
+     "12288 windows"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, rope_theta=-1.0), "rope_theta"),
+    (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, rope_theta=float("inf")), "rope_theta"),
+    (dict(rope_theta=10000.0), "rope_theta applies to the tiered mode only"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
     (dict(diag_topk=-1), "diag_topk"),
     (dict(offload_blocks=-1), "offload_blocks"),
@@ -184,7 +189,7 @@ def test_config_defaults():
     assert abs(c.alpha_new - 0.05) < 1e-7
     assert abs(c.beta - 0.001) < 1e-9 and c.decode_region == 4 and c.access_tau_mult == 2.0
     assert c.pinned_region_mask == 0 and list(c.region_half_life) == [0.0] * 8
-    assert c.window_tokens == 32 and c.fp_windows == 0 and c.int2_windows == 0
+    assert c.window_tokens == 32 and c.fp_windows == 0 and c.int2_windows == 0 and c.rope_theta == 0.0
 
 
 def test_tier_entry_points_reject_null_context():

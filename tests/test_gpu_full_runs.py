@@ -76,3 +76,13 @@ def test_qevict131k_full_run():
     w = synth.workload("qevict131k")
     st = _gu().run_tier_lockstep(w, w.steps, sample_layers=[0, 31], kv_every=32, ledger_every=32)
     assert st.steps == 128 and st.routing_events == 128 and st.ledger_checks > 0
+
+
+def test_qevict65k_w8_rope_full_run():
+    """The review's defaults at full size: 65,536-token prefill in 8,192
+    windows of 8 per layer, rotary keys and queries, routing every 8 steps,
+    byte-budget capacities (245 full-precision and 2,038 INT2 windows), 128
+    steps over 4 heavy-key epochs; the oracle holds layers 0 and 31."""
+    w = synth.workload("qevict65k_w8_rope")
+    st = _gu().run_tier_lockstep(w, w.steps, sample_layers=[0, 31], kv_every=32, ledger_every=32)
+    assert st.steps == 128 and st.routing_events == 16 and st.ledger_checks > 0

@@ -60,10 +60,10 @@ def test_tier_large_int2_share():
 
 
 def test_tier_max_capacity_sampled():
-    """A 196,600-token prefill stepped to the mode's 196,608-position capacity
-    (6,144 windows per layer, the routing kernel's LDS bound), 4 layers; the
-    oracle holds layer 3 through the first routing event over about 6,140
-    candidates and every step up to the last position."""
+    """A 196,600-token prefill stepped to 196,608 positions (6,144 windows
+    per layer), 4 layers; the oracle holds layer 3 through the first routing
+    event over about 6,140 candidates and every step up to the last
+    position."""
     w = synth.workload("qevict131k").scaled(n_layers=4, prefill_lens=(196600,))
     st = _gu().run_tier_lockstep(w, 7, sample_layers=[3], kv_every=7, ledger_every=7)
     assert st.steps == 7
