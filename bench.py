@@ -331,6 +331,11 @@ def run_tier(args, w):
     import torch
     from decode_kv_cache_gqa_amd import kvev
 
+    if args.warmup < max(w.route_interval, 1):
+        # the steps before the first routing event attend every prefill window in full precision
+        print(f"warmup raised to the routing interval ({w.route_interval}) so that the timed steps are "
+              "steady", file=sys.stderr)
+        args.warmup = w.route_interval
     total = args.warmup + args.steps
     ctx = kvev.context_for(w, max_steps=total)
     K, V = w.prefill_kv(0, device="cuda")

@@ -1,31 +1,42 @@
-// Two-tier window mode: per-layer routing of 32-token windows between a
-// full-precision tier, a recoverable INT2 tier and permanent eviction.
+// Two-tier window mode: per-layer routing of windows of W = 32 or 8 tokens
+// between a full-precision tier, a recoverable INT2 tier and permanent
+// eviction.
 //
 // Source: the technical review of "QEvict: Recoverable Quantized KV Eviction
 // for Attention-Drift-Robust Long-Context Decoding", section 4: the
 // accessible keys and values are the full-precision windows plus the
 // reconstructions of the INT2 windows (section 4.1, (Attention)); each
 // window's score accumulates its attention mass averaged over the layer's
-// query heads (section 4.2, Eq.1); at each routing event the candidates are
-// ranked, the best K_f stay in full precision, the next K_q go to the INT2
-// tier and the rest are evicted for good (section 4.4, Eq.4-6); a window is
-// quantized once, at its first demotion, keys per channel and values per
-// token, and its codes are reused by every later demotion and promotion
-// (section 4.4, Algorithm 1).  The routing interval here is one step.
+// query heads, over the steps of a routing interval (section 4.2, Eq.1); at
+// each routing event the candidates are ranked, the best K_f stay in full
+// precision, the next K_q go to the INT2 tier and the rest are evicted for
+// good (section 4.4, Eq.4-6); a window is quantized once, at its first
+// demotion, keys per channel and values per token, and its codes are reused
+// by every later demotion and promotion (section 4.4, Algorithm 1).  In the
+// rotary mode keys are quantized before the rotary embedding and rotated
+// again at their original positions when reconstructed (section 4.4,
+// positional handling for promoted keys).
 //
-// Layout, per (layer l, KV head h) and window w (positions [32w, 32w+32)):
-//   kfp    [L][Hkv][NW][32][128] bf16  keys, token-major
-//   vfp    [L][Hkv][NW][128][32] bf16  values, channel-major (a channel's 32
-//          tokens are 64 contiguous bytes: the p.V operand of the matrix cores)
-//   ledger [L][Hkv][NW][3072 B]   INT2 record:
+// Layout, per (layer l, KV head h) and window w (positions [Ww, Ww+W)):
+//   kfp    [L][Hkv][NW][W][128] bf16  keys, token-major (rotated in the
+//          rotary mode)
+//   vfp    [L][Hkv][NW][128][W] bf16  values, channel-major (a channel's W
+//          tokens are contiguous: the p.V operand of the matrix cores)
+//   kpre   [L][Hkv][NW][W][128] bf16  rotary mode only: the keys as given,
+//          read by a window's first quantization
+//   ledger [L][Hkv][NW][record]  INT2 record; for W = 32 (3,072 B):
 //     [0, 1024)     key codes, 16 B per lane of a wave (see below)
 //     [1024, 2048)  value codes, 16 B per lane
 //     [2048, 2304)  key scale per channel, fp16 [128]
 //     [2304, 2560)  key zero point per channel, fp16 [128]
 //     [2560, 2816)  value scale per (32-channel group, token), fp16 [4][32]
 //     [2816, 3072)  value zero point, fp16 [4][32]
+//   and for W = 8 (1,152 B) the kRec8* offsets below.
 // Full-precision storage is never released: a demoted window keeps it, so a
-// promotion only rewrites it and nothing moves when tiers change.
+// promotion only rewrites it and nothing moves when tiers change.  With
+// W = 8 or the rotary mode an INT2 window's storage holds its reconstruction
+// rounded to bf16 (written at its first demotion), and the attention reads
+// every listed window from full-precision storage.
 //
 // Code records.  A 2-bit code c = b0 + 2 b1 is stored as two bit planes.  In
 // the matrix-core products plane 0 is a B operand of 8 bf16 values in {0,1}
