@@ -38,23 +38,22 @@
 // rounded to bf16 (written at its first demotion), and the attention reads
 // every listed window from full-precision storage.
 //
-// Code records.  A 2-bit code c = b0 + 2 b1 is stored as two bit planes.  In
-// the matrix-core products plane 0 is a B operand of 8 bf16 values in {0,1}
-// and plane 1 one in {0,2} (made from the bits with one AND and one 24-bit
-// multiply per pair), so the two products with the same A operand sum
-// code * operand exactly.  Lane (r16, q4) = lane r16 + 16 q4 of a wave owns
-// four 32-bit words: plane 0 / plane 1, two words each; bit pi (low half)
-// and bit 16 + pi (high half) of a word are the two codes of pair pi.
-//   keys:   word (plane b, n-tile j) pair pi = 4s + p holds tokens 16j + r16,
-//           channels 32s + 8q4 + 2p (+1 in the high half), s = k-step 0..3
-//   values: word (plane b, half) pair pi = 4(ct % 4) + p, ct = 4 half + ..,
-//           holds channel 16ct + r16, tokens 8q4 + 2p (+1 in the high half)
+// Code records (32-token windows).  The attention multiplies the 2-bit
+// codes as int8 B operands of v_mfma_i32_16x16x64_i8; a 32-bit word holds
+// the 16 codes of one lane's operand, element k at bits 8 (k % 4) + 2 (k / 4),
+// so that (w >> 2d) & 0x03030303 is the operand's word d.
+//   keys:   lane (r16, q4) = lane r16 + 16 q4 owns four words (n-tile j,
+//           k-step ks) at word 4 lane + 2 j + ks: token 16 j + r16, channels
+//           64 ks + 16 q4 .. +16
+//   values: word (hf 16 + r16) 8 + ct holds channel 16 ct + r16, tokens
+//           16 hf .. +16 (hf = 0, 1)
 #include "kvev_internal.h"
 
 namespace kvev {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -88,22 +87,54 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return b;
 }
 
-// Pair pi (0..15) of a bit-plane word as two bf16 values in {0, v}: v = 1
-// for plane 0 and v = 2 for plane 1, so a product with the plane sums
-// code * operand exactly (c = b0 + 2 b1).
-template <int PI, int PLANE>
-__device__ __forceinline__ uint32_t plane_pair(uint32_t w) {
-  constexpr int sh = PI & 7;
-  constexpr uint32_t v = PLANE ? 0x4000u : 0x3F80u;  // bf16 2.0 / 1.0 (low bits zero, so v >> sh is exact)
-  const uint32_t x = PI < 8 ? w : (w >> 8);
-  return __umul24(x & (0x00010001u << sh), v >> sh);
+// 16 two-bit codes of a spread word as the 16 int8 elements of a matrix-core
+// operand: byte j of word d is the code at bits 8j + 2d (element 4d + j).
+__device__ __forceinline__ uint4 spread_codes(uint32_t w) {
+  constexpr uint32_t m = 0x03030303u;
+  return make_uint4(w & m, (w >> 2) & m, (w >> 4) & m, (w >> 6) & m);
 }
 
-// B operand (4 pairs) of pairs 4p0 .. 4p0+3 of one plane word.
-template <int P0, int PLANE>
-__device__ __forceinline__ bf16x8_t plane_operand(uint32_t w) {
-  return as_b8(make_uint4(plane_pair<4 * P0 + 0, PLANE>(w), plane_pair<4 * P0 + 1, PLANE>(w),
-                          plane_pair<4 * P0 + 2, PLANE>(w), plane_pair<4 * P0 + 3, PLANE>(w)));
+// Bit position of element k (0..15) in a spread word.
+__host__ __device__ constexpr int spread_bit(int k) { return 8 * (k & 3) + 2 * (k >> 2); }
+
+// Fixed-point digits of four integers |x| <= 2^22 as int8 operand bytes
+// (element e in byte e): x = 65536 d2 + 256 (d1 + 128) + (d0 + 128).  The
+// two low bytes are offset by 128 (a byte u read as u ^ 0x80 is u - 128),
+// the third byte is the signed top digit.
+__device__ __forceinline__ void digits4(const int* x, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+  const uint32_t t01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+  const uint32_t t23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  d0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
+  d1 = __builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u;
+  const uint32_t u01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+  const uint32_t u23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  d2 = __builtin_amdgcn_perm(u23, u01, 0x05040100u);
+}
+
+// The product of a digit A operand (rows 4 hd + 0..2 the digits of head hd,
+// row 4 hd + 3 all ones) with codes, summed back into sum_k x_k code_k: the
+// four accumulator rows of the lane are (d0, d1, d2, sum of codes).  Exact
+// in int32 while the true sum fits.
+__device__ __forceinline__ int digit_sum(const i32x4_t& r) {
+  const uint32_t t = static_cast<uint32_t>(r[0]) + (static_cast<uint32_t>(r[1]) << 8) +
+                     (static_cast<uint32_t>(r[2]) << 16) + 32896u * static_cast<uint32_t>(r[3]);
+  return static_cast<int>(t);
+}
+
+__device__ __forceinline__ i32x4_t mfma_i8(const uint4& a, const uint4& b, const i32x4_t& c) {
+  const i32x4_t av = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w)};
+  const i32x4_t bv = {static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+}
+
+// Exponent F that puts the largest magnitude m of a set just under 2^22:
+// |v| * 2^F <= 2^22 for every |v| <= m (0 when m is 0).
+__device__ __forceinline__ int fixed_exp(float m) { return m > 0.f ? 22 - __builtin_amdgcn_frexp_expf(m) : 0; }
+
+// rint(v * 2^F) for eight values.
+__device__ __forceinline__ void to_fixed(const float* v, int F, int* x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<int>(__builtin_rintf(__builtin_amdgcn_ldexpf(v[e], F)));
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& r, int i) {
@@ -132,18 +163,6 @@ __device__ __forceinline__ bf16x8_t split_rows(const float* x, int r16) {
     w[p] = r16 < 4 ? hi : (r16 < 8 ? lo : 0u);
   }
   return as_b8(make_uint4(w[0], w[1], w[2], w[3]));
-}
-
-// The high and low bf16 parts of 8 fp32 values, packed two per word.
-__device__ __forceinline__ void split_hilo(const float* x, uint4& hi, uint4& lo) {
-  uint32_t h[4], w[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    h[p] = pack_bf16(x[2 * p], x[2 * p + 1]);
-    w[p] = pack_bf16(x[2 * p] - __uint_as_float(h[p] << 16), x[2 * p + 1] - __uint_as_float(h[p] & 0xffff0000u));
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Orders a wave's LDS stores and loads that exchange data between its lanes
@@ -290,7 +309,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
   __shared__ __align__(16) float o_lds[4][HG][D];
   __shared__ float wstat[4][HG][2];
   __shared__ float e_lds[4][NWIN][HG];
-  __shared__ uint4 opnd[4][2][129];  // INT2 A operands staged per wave; [w][0][128] is zero
+  __shared__ uint4 opk[4][2 * 16 * 4];  // INT2 q.K digit operands, per wave
+  __shared__ uint4 opv[4][4 * 16 * 4];  // INT2 p.V digit operands, per wave
 
   const int chunk = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -345,13 +365,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     }
   }
 
-  float sv[2 * kQW][HG];  // logits of n-tile jj (lanes q4 == 0 hold them)
-  f32x4_t oacc[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float bzl = 0.f;  // INT2: sum_t p_t z_tg of (head, group) over the lane's tokens
-
   if (!fused) {
+    float sv[4][HG];  // logits of n-tile jj (lanes q4 == 0 hold them)
+    f32x4_t oacc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) oacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // ---- windows read from full-precision storage ---------------------------
     // A wave reads 64 tokens: 2 windows of 32, or 8 of 8.  K tile jj is
     // tokens 16jj .. 16jj+15 of the wave (token r16 of the tile in window
@@ -469,171 +487,189 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) oacc[ct] = mfma(pa, as_b8(vr[k][ct]), oacc[ct]);
     }
+    // the wave's output: high rows (q4 == 0) + low rows (q4 == 1)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        const float o = oacc[ct][hh] + __shfl_xor(oacc[ct][hh], 16, kWave);
+        if (q4 == 0) o_lds[wave][hh][16 * ct + r16] = o;
+      }
+    }
   } else if constexpr (!MAT) {
-    // ---- INT2 windows -------------------------------------------------------
-    // The scaled operands are formed once per (head, channel) and (head,
-    // token, group) by the wave's lanes and staged in LDS as matrix-core A
-    // operands (rows 0..3: high parts of heads 0..3, rows 4..7: low parts):
-    //   q.K: lane (head hs = lane / 16, channels 8 cs .. +8, cs = lane % 16)
-    //   p.V: lane (head hs, tokens 8 ts .. +8 of the window, ts = lane / 4 % 4,
-    //        32-channel group gs = lane % 4)
+    // ---- INT2 windows: int8 matrix-core products -----------------------------
+    // Each product runs on the codes as int8 B operands and on fixed-point
+    // digits of the scaled operands as the A operand: rows 4 hd + 0..2 hold
+    // the three digits of head hd, row 4 hd + 3 is all ones (the sum of the
+    // codes, which undoes the digits' offset).  The scaled operands are
+    // formed once per (head, channel) and (head, token, group) and staged in
+    // LDS by the lanes that form them:
+    //   q.K: lane (head hs = lane / 16, channels 8 cs .. +8, cs = lane % 16);
+    //        exponent per (head, window) from the largest |q_c s_c|
+    //   p.V: lane (head hs, tokens 8 ts .. +8, ts = lane / 4 % 4, 32-channel
+    //        group gs = lane % 4), two windows (64 tokens) per k range;
+    //        exponent per (head, group, window pair) from the largest p_t s_tg
+    // A lane (r16, q4) of a product's result holds head q4 (= hs of the lane
+    // that formed its operand): token or channel r16, accumulator rows
+    // (d0, d1, d2, sum of codes).
     const int hs = lane >> 4, cs = lane & 15, ts = (lane >> 2) & 3, gs = lane & 3;
-    uint4* sk = opnd[wave][0];  // [k-step][row][k-group]
-    uint4* sp = opnd[wave][1];  // [group][row][k-group]
-    const uint4* zrow = &opnd[wave][0][128];  // the A rows 8..15 of every operand
-    if (lane == 0) opnd[wave][0][128] = make_uint4(0, 0, 0, 0);
+    uint4* ka = opk[wave];  // [k-step 2][row 16][k-group 4]
+    uint4* va = opv[wave];  // [group 4][row 16][k-group 4]
+    // the ones rows: 32 entries of ka, 64 of va
+    if (lane < 32) ka[((lane >> 4) * 16 + 4 * ((lane >> 2) & 3) + 3) * 4 + (lane & 3)] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+    va[((lane >> 4) * 16 + 4 * ((lane >> 2) & 3) + 3) * 4 + (lane & 3)] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
     float qx[8];
     Vec16<bf16_t>::widen(
         *reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(l) * A.Hq + h * HG + hs) * D + 8 * cs), qx);
+    float lgt[2 * kQW];  // logits of head q4, token r16 of n-tile jj
+    // where the lane's 8 digit bytes of a k-step go: k-step cs / 8, k-group
+    // (cs % 8) / 2, half cs % 2 of the 16-byte row entry
+    uint2* kdst = reinterpret_cast<uint2*>(ka) + (((cs >> 3) * 16 + 4 * hs) * 4 + ((cs & 7) >> 1)) * 2 + (cs & 1);
 #pragma unroll
     for (int k = 0; k < kQW; ++k) {
       const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
-      uint4 kc = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
-      float bias = 0.f;
+      uint4 kc = make_uint4(0, 0, 0, 0);
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float bias = 0.f, amax = 0.f;
       if (live[k]) {  // wave-uniform
         kc = *reinterpret_cast<const uint4*>(rec + kRecK + 16 * lane);
         const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSK + 16 * cs);
         const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZK + 16 * cs);
-        float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
           const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
-          x[e] = qx[e] * sc;
+          a[e] = qx[e] * sc;
           bias = fmaf(qx[e], zp, bias);
+          amax = fmaxf(amax, fabsf(a[e]));
         }
-        split_hilo(x, hi, lo);
       }
-      wave_lds_order();
-      sk[((cs >> 2) * 8 + hs) * 4 + (cs & 3)] = hi;
-      sk[((cs >> 2) * 8 + 4 + hs) * 4 + (cs & 3)] = lo;
-      wave_lds_order();
-      bf16x8_t a1[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a1[s] = as_b8(*(r16 < 8 ? &sk[(s * 8 + r16) * 4 + q4] : zrow));
-      // sum_c q_c z_c of each head (the 16 lanes of head hs hold its parts)
+      // per head: the exponent and sum_c q_c z_c (the 16 lanes of head hs)
+      const int F = fixed_exp(row16_max(amax));
       bias = row16_sum(bias);
-      float bb[HG];
+      int x[8];
+      to_fixed(a, F, x);
+      uint32_t dg[3][2];
+      digits4(x, dg[0][0], dg[1][0], dg[2][0]);
+      digits4(x + 4, dg[0][1], dg[1][1], dg[2][1]);
+      wave_lds_order();
 #pragma unroll
-      for (int hh = 0; hh < HG; ++hh) bb[hh] = __shfl(bias, 16 * hh, kWave);
+      for (int d = 0; d < 3; ++d) kdst[d * 4 * 2] = make_uint2(dg[d][0], dg[d][1]);
+      wave_lds_order();
+      const uint4 a0 = ka[(0 * 16 + r16) * 4 + q4], a1 = ka[(1 * 16 + r16) * 4 + q4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        f32x4_t acc = q4 == 0 ? f32x4_t{bb[0], bb[1], bb[2], bb[3]} : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint32_t w0 = word_of(kc, j), w1 = word_of(kc, 2 + j);
-        acc = mfma(a1[0], plane_operand<0, 0>(w0), acc);
-        acc = mfma(a1[0], plane_operand<0, 1>(w1), acc);
-        acc = mfma(a1[1], plane_operand<1, 0>(w0), acc);
-        acc = mfma(a1[1], plane_operand<1, 1>(w1), acc);
-        acc = mfma(a1[2], plane_operand<2, 0>(w0), acc);
-        acc = mfma(a1[2], plane_operand<2, 1>(w1), acc);
-        acc = mfma(a1[3], plane_operand<3, 0>(w0), acc);
-        acc = mfma(a1[3], plane_operand<3, 1>(w1), acc);
-        const bool valid = q4 == 0 && live[k];
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-          const float lg = acc[hh] + __shfl_xor(acc[hh], 16, kWave);
-          sv[2 * k + j][hh] = valid ? lg * scale : -INFINITY;
-        }
+        i32x4_t acc = {0, 0, 0, 0};
+        acc = mfma_i8(a0, spread_codes(word_of(kc, 2 * j)), acc);
+        acc = mfma_i8(a1, spread_codes(word_of(kc, 2 * j + 1)), acc);
+        const float lg = __builtin_amdgcn_ldexpf(static_cast<float>(digit_sum(acc)), -F) + bias;
+        lgt[2 * k + j] = live[k] ? lg * scale : -INFINITY;
       }
     }
-    float mh[HG];
+    // softmax statistics of head q4 over the wave's windows
+    float m = lgt[0];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      float m = sv[0][hh];
-#pragma unroll
-      for (int jj = 1; jj < 2 * kQW; ++jj) m = fmaxf(m, sv[jj][hh]);
-      mh[hh] = row16_max(m);
-    }
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      float ew[kQW];
-#pragma unroll
-      for (int k = 0; k < kQW; ++k) {
-        const float p0 = mh[hh] == -INFINITY ? 0.f : __expf(sv[2 * k][hh] - mh[hh]);
-        const float p1 = mh[hh] == -INFINITY ? 0.f : __expf(sv[2 * k + 1][hh] - mh[hh]);
-        sv[2 * k][hh] = p0;
-        sv[2 * k + 1][hh] = p1;
-        ew[k] = row16_sum(p0 + p1);
-      }
-      if (lane == 0) {
-        float tot = 0.f;
-#pragma unroll
-        for (int k = 0; k < kQW; ++k) {
-          e_lds[wave][k][hh] = ew[k];
-          tot += ew[k];
-        }
-        wstat[wave][hh][0] = mh[hh];
-        wstat[wave][hh][1] = tot;
-      }
-    }
-    if (q4 == 0) {
-#pragma unroll
-      for (int jj = 0; jj < 2 * kQW; ++jj)
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) p_lds[wave][hh][16 * jj + r16] = sv[jj][hh];
-    }
-    __syncthreads();
+    for (int jj = 1; jj < 2 * kQW; ++jj) m = fmaxf(m, lgt[jj]);
+    m = row16_max(m);
+    float tot = 0.f;
 #pragma unroll
     for (int k = 0; k < kQW; ++k) {
-      if (!live[k]) continue;  // wave-uniform
-      const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
-      const uint4 vc = *reinterpret_cast<const uint4*>(rec + kRecV + 16 * lane);
-      // scale and zero point of (group gs, tokens 8 ts .. +8), stored [group][token]
-      const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * gs + 8 * ts));
-      const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * gs + 8 * ts));
-      const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts]);
-      const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts + 4]);
-      const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
-      float x[8];
+      const float p0 = m == -INFINITY ? 0.f : __expf(lgt[2 * k] - m);
+      const float p1 = m == -INFINITY ? 0.f : __expf(lgt[2 * k + 1] - m);
+      lgt[2 * k] = p0;
+      lgt[2 * k + 1] = p1;
+      const float e = row16_sum(p0 + p1);
+      if (r16 == 0) e_lds[wave][k][q4] = e;
+      tot += e;
+    }
+    if (r16 == 0) {
+      wstat[wave][q4][0] = m;
+      wstat[wave][q4][1] = tot;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
-        const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
-        x[e] = pv[e] * sc;
-        bzl = fmaf(pv[e], zp, bzl);
+    for (int jj = 0; jj < 2 * kQW; ++jj) p_lds[wave][q4][16 * jj + r16] = lgt[jj];
+    wave_lds_order();
+    // p.V over window pairs
+    float ov[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // head q4, channel 16 ct + r16
+    float bzl = 0.f;  // sum_t p_t z_tg of (head hs, group gs) over the lane's tokens
+#pragma unroll
+    for (int pr = 0; pr < kQW / 2; ++pr) {
+      float y[2][8];
+      float ymax = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int k = 2 * pr + kk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[kk][e] = 0.f;
+        if (live[k]) {  // wave-uniform
+          const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
+          // scale and zero point of (group gs, tokens 8 ts .. +8), stored [group][token]
+          const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * gs + 8 * ts));
+          const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * gs + 8 * ts));
+          const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts]);
+          const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts + 4]);
+          const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
+            const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
+            y[kk][e] = pv[e] * sc;
+            bzl = fmaf(pv[e], zp, bzl);
+            ymax = fmaxf(ymax, y[kk][e]);
+          }
+        }
       }
-      uint4 hi, lo;
-      split_hilo(x, hi, lo);
+      // exponent of (head hs, group gs): the lanes of its 4 token blocks
+      ymax = fmaxf(ymax, __shfl_xor(ymax, 4, kWave));
+      ymax = fmaxf(ymax, __shfl_xor(ymax, 8, kWave));
+      const int Fv = fixed_exp(ymax);
+      uint32_t dg[2][3][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        int x[8];
+        to_fixed(y[kk], Fv, x);
+        digits4(x, dg[kk][0][0], dg[kk][1][0], dg[kk][2][0]);
+        digits4(x + 4, dg[kk][0][1], dg[kk][1][1], dg[kk][2][1]);
+      }
+      // the codes of the lane's B operands: window 2 pr + q4 / 2, tokens
+      // 16 (q4 % 2) .. +16, channel 16 ct + r16 for ct = 0..7
+      const int kc_ = 2 * pr + (q4 >> 1);
+      const bool lc = kc_ == 2 * pr ? live[2 * pr] : live[2 * pr + 1];
+      const int wc = kc_ == 2 * pr ? win[2 * pr] : win[2 * pr + 1];
+      const uint8_t* recc = A.ledger + (lh * A.NW + wc) * static_cast<int64_t>(kTierLedgerBytes) + kRecV +
+                            32 * ((q4 & 1) * 16 + r16);
+      const uint4 vc0 = lc ? *reinterpret_cast<const uint4*>(recc) : make_uint4(0, 0, 0, 0);
+      const uint4 vc1 = lc ? *reinterpret_cast<const uint4*>(recc + 16) : make_uint4(0, 0, 0, 0);
+      int Fg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) Fg[g] = __shfl(Fv, 16 * q4 + g, kWave);
       wave_lds_order();
-      sp[(gs * 8 + hs) * 4 + ts] = hi;
-      sp[(gs * 8 + 4 + hs) * 4 + ts] = lo;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int d = 0; d < 3; ++d)
+          reinterpret_cast<uint2*>(va)[((gs * 16 + 4 * hs + d) * 4 + 2 * kk + (ts >> 1)) * 2 + (ts & 1)] =
+              make_uint2(dg[kk][d][0], dg[kk][d][1]);
       wave_lds_order();
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const bf16x8_t pa = as_b8(*(r16 < 8 ? &sp[(g * 8 + r16) * 4 + q4] : zrow));
-        const uint32_t w0 = word_of(vc, g >> 1), w1 = word_of(vc, 2 + (g >> 1));
-        // tiles ct = 2g, 2g + 1 sit at pairs 4 (ct % 4) .. of word ct / 4
-        if ((g & 1) == 0) {
-          oacc[2 * g] = mfma(pa, plane_operand<0, 0>(w0), oacc[2 * g]);
-          oacc[2 * g] = mfma(pa, plane_operand<0, 1>(w1), oacc[2 * g]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<1, 0>(w0), oacc[2 * g + 1]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<1, 1>(w1), oacc[2 * g + 1]);
-        } else {
-          oacc[2 * g] = mfma(pa, plane_operand<2, 0>(w0), oacc[2 * g]);
-          oacc[2 * g] = mfma(pa, plane_operand<2, 1>(w1), oacc[2 * g]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<3, 0>(w0), oacc[2 * g + 1]);
-          oacc[2 * g + 1] = mfma(pa, plane_operand<3, 1>(w1), oacc[2 * g + 1]);
+        const uint4 ag = va[(g * 16 + r16) * 4 + q4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int ct = 2 * g + t;
+          const i32x4_t acc = mfma_i8(ag, spread_codes(word_of(ct < 4 ? vc0 : vc1, ct & 3)), i32x4_t{0, 0, 0, 0});
+          ov[ct] += __builtin_amdgcn_ldexpf(static_cast<float>(digit_sum(acc)), -Fg[g]);
         }
       }
     }
     // sum_t p_t z_tg of each (head, group): over the lanes' token blocks
     bzl += __shfl_xor(bzl, 4, kWave);
     bzl += __shfl_xor(bzl, 8, kWave);
-  }
-
-  // the wave's output: high rows (q4 == 0) + low rows (q4 == 1) + zero-point terms
-  float bzh[HG][4];
+    float bz[4];
 #pragma unroll
-  for (int hh = 0; hh < HG; ++hh)
+    for (int g = 0; g < 4; ++g) bz[g] = __shfl(bzl, 16 * q4 + g, kWave);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) bzh[hh][g] = fused ? __shfl(bzl, 16 * hh + g, kWave) : 0.f;
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-      const float o = oacc[ct][hh] + __shfl_xor(oacc[ct][hh], 16, kWave) + bzh[hh][ct >> 1];
-      if (q4 == 0) o_lds[wave][hh][16 * ct + r16] = o;
-    }
+    for (int ct = 0; ct < 8; ++ct) o_lds[wave][q4][16 * ct + r16] = ov[ct] + bz[ct >> 1];
   }
   __syncthreads();
 
@@ -1091,25 +1127,20 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         rec[kRec8K + tid] = static_cast<uint8_t>(kb);
         rec[kRec8V + tid] = static_cast<uint8_t>(vb);
       } else {
-        // thread = (lane, word): lane = tid / 4, word = tid % 4 (plane word / 2, part word % 2)
-        const int ln = tid >> 2, wd = tid & 3, r16 = ln & 15, q4 = ln >> 4;
-        const int plane = wd >> 1, part = wd & 1;
+        // keys: thread = (lane ln, n-tile j, k-step ks) of the attention's
+        // int8 product, 16 channels 64 ks + 16 q4 .. +16 of token 16 j + r16;
+        // values: thread = (half hf, r16, tile ct), 16 tokens 16 hf .. +16 of
+        // channel 16 ct + r16 (element k of a word at bits spread_bit(k))
+        const int ln = tid >> 2, jt = (tid >> 1) & 1, ks = tid & 1, r16 = ln & 15, q4 = ln >> 4;
+        const int hf = tid >> 7, vr16 = (tid >> 3) & 15, ct = tid & 7;
         uint32_t kw = 0, vw = 0;
 #pragma unroll
-        for (int pi = 0; pi < 16; ++pi)
-#pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const int p = pi & 3, e = 2 * p + hi;
-            // keys: n-tile part, k-step pi / 4
-            const int tk = 16 * part + r16, ckk = 32 * (pi >> 2) + 8 * q4 + e;
-            kw |= static_cast<uint32_t>((ck[tk][ckk] >> plane) & 1) << (pi + 16 * hi);
-            // values: tile 4 part + pi / 4
-            const int ct = 4 * part + (pi >> 2);
-            const int cvc = 16 * ct + r16, tv = 8 * q4 + e;
-            vw |= static_cast<uint32_t>((cv[tv][cvc] >> plane) & 1) << (pi + 16 * hi);
-          }
-        rec32[(kRecK / 4) + 4 * ln + 2 * plane + part] = kw;
-        rec32[(kRecV / 4) + 4 * ln + 2 * plane + part] = vw;
+        for (int e = 0; e < 16; ++e) {
+          kw |= static_cast<uint32_t>(ck[16 * jt + r16][64 * ks + 16 * q4 + e]) << spread_bit(e);
+          vw |= static_cast<uint32_t>(cv[16 * hf + e][16 * ct + vr16]) << spread_bit(e);
+        }
+        rec32[kRecK / 4 + 4 * ln + 2 * jt + ks] = kw;
+        rec32[kRecV / 4 + (hf * 16 + vr16) * 8 + ct] = vw;
       }
       if (A.mat) {
         // the reconstruction, rounded to bf16, replaces the full-precision
@@ -1162,19 +1193,14 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
           uint32_t kb, vb;
           {  // key element (token r, channel c)
             const int i = i0 + e, r = i / D, c = i % D;
-            const int r16 = r & 15, part = r >> 4, s4 = c >> 5, q4 = (c & 31) >> 3, ee = c & 7;
-            const int ln = q4 * 16 + r16, pi = 4 * s4 + (ee >> 1), bit = pi + 16 * (ee & 1);
-            const uint32_t w0 = recl[kRecK / 4 + 4 * ln + part], w1 = recl[kRecK / 4 + 4 * ln + 2 + part];
-            const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+            const int ln = ((c >> 4) & 3) * 16 + (r & 15);
+            const uint32_t code = (recl[kRecK / 4 + 4 * ln + 2 * (r >> 4) + (c >> 6)] >> spread_bit(c & 15)) & 3u;
             const float sc = h2f(rl16[kRecSK / 2 + c]), zp = h2f(rl16[kRecZK / 2 + c]);
             kb = bf16_rne(__fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp));
           }
           {  // value element (channel c, token r): channel-major index
             const int i = i0 + e, c = i / W, r = i % W;
-            const int r16 = c & 15, ct = c >> 4, q4 = r >> 3, ee = r & 7;
-            const int ln = q4 * 16 + r16, part = ct >> 2, pi = 4 * (ct & 3) + (ee >> 1), bit = pi + 16 * (ee & 1);
-            const uint32_t w0 = recl[kRecV / 4 + 4 * ln + part], w1 = recl[kRecV / 4 + 4 * ln + 2 + part];
-            const uint32_t code = ((w0 >> bit) & 1u) | (((w1 >> bit) & 1u) << 1);
+            const uint32_t code = (recl[kRecV / 4 + ((r >> 4) * 16 + (c & 15)) * 8 + (c >> 4)] >> spread_bit(r & 15)) & 3u;
             const int g = c >> 5;
             const float sc = h2f(rl16[kRecSV / 2 + 32 * g + r]), zp = h2f(rl16[kRecZV / 2 + 32 * g + r]);
             vb = bf16_rne(__fadd_rn(__fmul_rn(static_cast<float>(code), sc), zp));

@@ -294,21 +294,18 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
   uint32_t words[2][256];
   std::memcpy(words[0], rec.data(), 1024);
   std::memcpy(words[1], rec.data() + 1024, 1024);
-  // lane (r16, q4) owns words 4*lane + 2*plane + part (layout in tier.hip)
+  // element k of a 16-code word sits at bits 8 (k % 4) + 2 (k / 4); key word
+  // 4 lane + 2 j + ks of lane (r16, q4) holds token 16 j + r16, channels
+  // 64 ks + 16 q4 .. +16; value word (hf 16 + r16) 8 + ct holds channel
+  // 16 ct + r16, tokens 16 hf .. +16 (layout in tier.hip)
+  auto bit = [](int k) { return 8 * (k & 3) + 2 * (k >> 2); };
   for (int r = 0; r < kTierWin; ++r)
     for (int ch = 0; ch < kTierD; ++ch) {
-      {  // key (token r, channel ch)
-        const int r16 = r & 15, part = r >> 4, s = ch >> 5, q4 = (ch & 31) >> 3, e = ch & 7;
-        const int ln = q4 * 16 + r16, bit = 4 * s + (e >> 1) + 16 * (e & 1);
-        const uint32_t b0 = (words[0][4 * ln + part] >> bit) & 1u, b1 = (words[0][4 * ln + 2 + part] >> bit) & 1u;
-        k_codes[r * kTierD + ch] = static_cast<uint8_t>(b0 | (b1 << 1));
-      }
-      {  // value (token r, channel ch)
-        const int r16 = ch & 15, ct = ch >> 4, q4 = r >> 3, e = r & 7;
-        const int ln = q4 * 16 + r16, part = ct >> 2, bit = 4 * (ct & 3) + (e >> 1) + 16 * (e & 1);
-        const uint32_t b0 = (words[1][4 * ln + part] >> bit) & 1u, b1 = (words[1][4 * ln + 2 + part] >> bit) & 1u;
-        v_codes[r * kTierD + ch] = static_cast<uint8_t>(b0 | (b1 << 1));
-      }
+      const int ln = ((ch >> 4) & 3) * 16 + (r & 15);
+      k_codes[r * kTierD + ch] =
+          static_cast<uint8_t>((words[0][4 * ln + 2 * (r >> 4) + (ch >> 6)] >> bit(ch & 15)) & 3u);
+      v_codes[r * kTierD + ch] =
+          static_cast<uint8_t>((words[1][((r >> 4) * 16 + (ch & 15)) * 8 + (ch >> 4)] >> bit(r & 15)) & 3u);
     }
   std::memcpy(k_scale, rec.data() + 2048, 256);
   std::memcpy(k_zero, rec.data() + 2304, 256);
