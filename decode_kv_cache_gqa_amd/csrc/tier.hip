@@ -97,11 +97,13 @@ __device__ __forceinline__ uint4 spread_codes(uint32_t w) {
 // Bit position of element k (0..15) in a spread word.
 __host__ __device__ constexpr int spread_bit(int k) { return 8 * (k & 3) + 2 * (k >> 2); }
 
-// Fixed-point digits of four integers |x| <= 2^22 as int8 operand bytes
-// (element e in byte e): x = 65536 d2 + 256 (d1 + 128) + (d0 + 128).  The
-// two low bytes are offset by 128 (a byte u read as u ^ 0x80 is u - 128),
-// the third byte is the signed top digit.
-__device__ __forceinline__ void digits4(const int* x, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
+// Fixed-point digits as int8 operand bytes.  A value t = v * 2^F with
+// |t| < 2^21 is rounded to the integer x = rint(t) by one fused multiply-add,
+// f = v * 2^F + 1.5 * 2^23, whose bits are 0x4B000000 + 2^22 + x: bytes 0
+// and 1 of f are those of x and byte 2 is 64 + (x >> 16).  The operand takes
+// bytes 0 and 1 offset by 128 (u ^ 0x80 is u - 128 as int8) and byte 2 as
+// it is, so x = 65536 (b2 - 64) + 256 (b1' + 128) + (b0' + 128).
+__device__ __forceinline__ void digits4(const uint32_t* x, uint32_t& d0, uint32_t& d1, uint32_t& d2) {
   const uint32_t t01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
   const uint32_t t23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
   d0 = __builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u;
@@ -113,11 +115,12 @@ __device__ __forceinline__ void digits4(const int* x, uint32_t& d0, uint32_t& d1
 
 // The product of a digit A operand (rows 4 hd + 0..2 the digits of head hd,
 // row 4 hd + 3 all ones) with codes, summed back into sum_k x_k code_k: the
-// four accumulator rows of the lane are (d0, d1, d2, sum of codes).  Exact
-// in int32 while the true sum fits.
+// lane's four accumulator rows are (d0, d1, d2, sum of codes), and
+// sum x code = R0 + 256 R1 + 65536 R2 + (128 + 32768 - 64 * 65536) S.
+// Exact (modulo 2^32 on the way) while the true sum fits in int32.
 __device__ __forceinline__ int digit_sum(const i32x4_t& r) {
   const uint32_t t = static_cast<uint32_t>(r[0]) + (static_cast<uint32_t>(r[1]) << 8) +
-                     (static_cast<uint32_t>(r[2]) << 16) + 32896u * static_cast<uint32_t>(r[3]);
+                     (static_cast<uint32_t>(r[2]) << 16) - 4161408u * static_cast<uint32_t>(r[3]);
   return static_cast<int>(t);
 }
 
@@ -127,14 +130,28 @@ __device__ __forceinline__ i32x4_t mfma_i8(const uint4& a, const uint4& b, const
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
 }
 
-// Exponent F that puts the largest magnitude m of a set just under 2^22:
-// |v| * 2^F <= 2^22 for every |v| <= m (0 when m is 0).
-__device__ __forceinline__ int fixed_exp(float m) { return m > 0.f ? 22 - __builtin_amdgcn_frexp_expf(m) : 0; }
+// Exponent F that puts the largest magnitude m of a set under 2^21:
+// |v| * 2^F < 2^21 for every |v| <= m (0 when m is 0; at most 127).
+__device__ __forceinline__ int fixed_exp(float m) {
+  return m > 0.f ? min(21 - __builtin_amdgcn_frexp_expf(m), 127) : 0;
+}
 
-// rint(v * 2^F) for eight values.
-__device__ __forceinline__ void to_fixed(const float* v, int F, int* x) {
+// The float bits of v * 2^F + 1.5 * 2^23 (rint(v * 2^F) in the low bits) for
+// eight values; p2 = 2^F.
+__device__ __forceinline__ void to_fixed(const float* v, float p2, uint32_t* x) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = static_cast<int>(__builtin_rintf(__builtin_amdgcn_ldexpf(v[e], F)));
+  for (int e = 0; e < 8; ++e) x[e] = __float_as_uint(fmaf(v[e], p2, 12582912.0f));
+}
+
+// DPP within the 16 lanes of a row: rotate by 4 / 8, or take lane 4k + g of
+// each quad.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& r, int i) {
@@ -515,40 +532,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     const int hs = lane >> 4, cs = lane & 15, ts = (lane >> 2) & 3, gs = lane & 3;
     uint4* ka = opk[wave];  // [k-step 2][row 16][k-group 4]
     uint4* va = opv[wave];  // [group 4][row 16][k-group 4]
-    // the ones rows: 32 entries of ka, 64 of va
-    if (lane < 32) ka[((lane >> 4) * 16 + 4 * ((lane >> 2) & 3) + 3) * 4 + (lane & 3)] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
-    va[((lane >> 4) * 16 + 4 * ((lane >> 2) & 3) + 3) * 4 + (lane & 3)] = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+    // Every record load is issued up front and unconditionally (a window
+    // past the list reads window 0 of the layer, whose results are masked:
+    // its logits are -inf, so its probabilities and p.V digits are 0).
+    const uint8_t* recs[kQW];
+#pragma unroll
+    for (int k = 0; k < kQW; ++k) recs[k] = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
+    uint4 kc[kQW], ksr[kQW], kzr[kQW];
+#pragma unroll
+    for (int k = 0; k < kQW; ++k) {
+      kc[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecK + 16 * lane);
+      ksr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecSK + 16 * cs);
+      kzr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecZK + 16 * cs);
+    }
     float qx[8];
     Vec16<bf16_t>::widen(
         *reinterpret_cast<const uint4*>(q + (static_cast<int64_t>(l) * A.Hq + h * HG + hs) * D + 8 * cs), qx);
+    // the ones rows: 32 entries of ka, 64 of va
+    {
+      const uint4 ones = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+      const int ent = (4 * ((lane >> 2) & 3) + 3) * 4 + (lane & 3);
+      if (lane < 32) ka[(lane >> 4) * 64 + ent] = ones;
+      va[(lane >> 4) * 64 + ent] = ones;
+    }
     float lgt[2 * kQW];  // logits of head q4, token r16 of n-tile jj
     // where the lane's 8 digit bytes of a k-step go: k-step cs / 8, k-group
     // (cs % 8) / 2, half cs % 2 of the 16-byte row entry
     uint2* kdst = reinterpret_cast<uint2*>(ka) + (((cs >> 3) * 16 + 4 * hs) * 4 + ((cs & 7) >> 1)) * 2 + (cs & 1);
 #pragma unroll
     for (int k = 0; k < kQW; ++k) {
-      const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
-      uint4 kc = make_uint4(0, 0, 0, 0);
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float a[8];
       float bias = 0.f, amax = 0.f;
-      if (live[k]) {  // wave-uniform
-        kc = *reinterpret_cast<const uint4*>(rec + kRecK + 16 * lane);
-        const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSK + 16 * cs);
-        const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZK + 16 * cs);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
-          const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
-          a[e] = qx[e] * sc;
-          bias = fmaf(qx[e], zp, bias);
-          amax = fmaxf(amax, fabsf(a[e]));
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float sc = h2f(word_of(ksr[k], e >> 1) >> (16 * (e & 1)));
+        const float zp = h2f(word_of(kzr[k], e >> 1) >> (16 * (e & 1)));
+        a[e] = qx[e] * sc;
+        bias = fmaf(qx[e], zp, bias);
+        amax = fmaxf(amax, fabsf(a[e]));
       }
       // per head: the exponent and sum_c q_c z_c (the 16 lanes of head hs)
       const int F = fixed_exp(row16_max(amax));
       bias = row16_sum(bias);
-      int x[8];
-      to_fixed(a, F, x);
+      uint32_t x[8];
+      to_fixed(a, __builtin_amdgcn_ldexpf(1.0f, F), x);
       uint32_t dg[3][2];
       digits4(x, dg[0][0], dg[1][0], dg[2][0]);
       digits4(x + 4, dg[0][1], dg[1][1], dg[2][1]);
@@ -560,11 +587,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         i32x4_t acc = {0, 0, 0, 0};
-        acc = mfma_i8(a0, spread_codes(word_of(kc, 2 * j)), acc);
-        acc = mfma_i8(a1, spread_codes(word_of(kc, 2 * j + 1)), acc);
+        acc = mfma_i8(a0, spread_codes(word_of(kc[k], 2 * j)), acc);
+        acc = mfma_i8(a1, spread_codes(word_of(kc[k], 2 * j + 1)), acc);
         const float lg = __builtin_amdgcn_ldexpf(static_cast<float>(digit_sum(acc)), -F) + bias;
         lgt[2 * k + j] = live[k] ? lg * scale : -INFINITY;
       }
+    }
+    // p.V records: scale and zero point of (group gs, tokens 8 ts .. +8),
+    // stored [group][token], and the codes of the lane's B operands: window
+    // 2 pr + q4 / 2, tokens 16 (q4 % 2) .. +16, channel 16 ct + r16
+    uint4 vsr[kQW], vzr[kQW], vc[kQW / 2][2];
+#pragma unroll
+    for (int k = 0; k < kQW; ++k) {
+      vsr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecSV + 2 * (32 * gs + 8 * ts));
+      vzr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecZV + 2 * (32 * gs + 8 * ts));
+    }
+#pragma unroll
+    for (int pr = 0; pr < kQW / 2; ++pr) {
+      const uint8_t* rc = (q4 >> 1) ? recs[2 * pr + 1] : recs[2 * pr];
+      const uint8_t* b = rc + kRecV + 32 * ((q4 & 1) * 16 + r16);
+      vc[pr][0] = *reinterpret_cast<const uint4*>(b);
+      vc[pr][1] = *reinterpret_cast<const uint4*>(b + 16);
     }
     // softmax statistics of head q4 over the wave's windows
     float m = lgt[0];
@@ -599,50 +642,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int k = 2 * pr + kk;
+        const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts]);
+        const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts + 4]);
+        const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[kk][e] = 0.f;
-        if (live[k]) {  // wave-uniform
-          const uint8_t* rec = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
-          // scale and zero point of (group gs, tokens 8 ts .. +8), stored [group][token]
-          const uint4 sr = *reinterpret_cast<const uint4*>(rec + kRecSV + 2 * (32 * gs + 8 * ts));
-          const uint4 zr = *reinterpret_cast<const uint4*>(rec + kRecZV + 2 * (32 * gs + 8 * ts));
-          const float4 pa4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts]);
-          const float4 pb4 = *reinterpret_cast<const float4*>(&p_lds[wave][hs][32 * k + 8 * ts + 4]);
-          const float pv[8] = {pa4.x, pa4.y, pa4.z, pa4.w, pb4.x, pb4.y, pb4.z, pb4.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float sc = h2f(word_of(sr, e >> 1) >> (16 * (e & 1)));
-            const float zp = h2f(word_of(zr, e >> 1) >> (16 * (e & 1)));
-            y[kk][e] = pv[e] * sc;
-            bzl = fmaf(pv[e], zp, bzl);
-            ymax = fmaxf(ymax, y[kk][e]);
-          }
+        for (int e = 0; e < 8; ++e) {
+          const float sc = h2f(word_of(vsr[k], e >> 1) >> (16 * (e & 1)));
+          const float zp = h2f(word_of(vzr[k], e >> 1) >> (16 * (e & 1)));
+          y[kk][e] = pv[e] * sc;
+          bzl = fmaf(pv[e], zp, bzl);
+          ymax = fmaxf(ymax, y[kk][e]);
         }
       }
       // exponent of (head hs, group gs): the lanes of its 4 token blocks
-      ymax = fmaxf(ymax, __shfl_xor(ymax, 4, kWave));
-      ymax = fmaxf(ymax, __shfl_xor(ymax, 8, kWave));
+      // (lanes 4k + gs of the row)
+      ymax = fmaxf(ymax, dpp_row<0x124>(ymax));
+      ymax = fmaxf(ymax, dpp_row<0x128>(ymax));
       const int Fv = fixed_exp(ymax);
+      const float p2 = __builtin_amdgcn_ldexpf(1.0f, Fv);
       uint32_t dg[2][3][2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        int x[8];
-        to_fixed(y[kk], Fv, x);
+        uint32_t x[8];
+        to_fixed(y[kk], p2, x);
         digits4(x, dg[kk][0][0], dg[kk][1][0], dg[kk][2][0]);
         digits4(x + 4, dg[kk][0][1], dg[kk][1][1], dg[kk][2][1]);
       }
-      // the codes of the lane's B operands: window 2 pr + q4 / 2, tokens
-      // 16 (q4 % 2) .. +16, channel 16 ct + r16 for ct = 0..7
-      const int kc_ = 2 * pr + (q4 >> 1);
-      const bool lc = kc_ == 2 * pr ? live[2 * pr] : live[2 * pr + 1];
-      const int wc = kc_ == 2 * pr ? win[2 * pr] : win[2 * pr + 1];
-      const uint8_t* recc = A.ledger + (lh * A.NW + wc) * static_cast<int64_t>(kTierLedgerBytes) + kRecV +
-                            32 * ((q4 & 1) * 16 + r16);
-      const uint4 vc0 = lc ? *reinterpret_cast<const uint4*>(recc) : make_uint4(0, 0, 0, 0);
-      const uint4 vc1 = lc ? *reinterpret_cast<const uint4*>(recc + 16) : make_uint4(0, 0, 0, 0);
-      int Fg[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) Fg[g] = __shfl(Fv, 16 * q4 + g, kWave);
+      // the exponent of (head q4, group g): lane g of any quad of row q4
+      const int Fg[4] = {dpp_row_i<0x00>(Fv), dpp_row_i<0x55>(Fv), dpp_row_i<0xAA>(Fv), dpp_row_i<0xFF>(Fv)};
       wave_lds_order();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -657,17 +684,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int ct = 2 * g + t;
-          const i32x4_t acc = mfma_i8(ag, spread_codes(word_of(ct < 4 ? vc0 : vc1, ct & 3)), i32x4_t{0, 0, 0, 0});
+          const i32x4_t acc = mfma_i8(ag, spread_codes(word_of(vc[pr][ct >> 2], ct & 3)), i32x4_t{0, 0, 0, 0});
           ov[ct] += __builtin_amdgcn_ldexpf(static_cast<float>(digit_sum(acc)), -Fg[g]);
         }
       }
     }
-    // sum_t p_t z_tg of each (head, group): over the lanes' token blocks
-    bzl += __shfl_xor(bzl, 4, kWave);
-    bzl += __shfl_xor(bzl, 8, kWave);
-    float bz[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) bz[g] = __shfl(bzl, 16 * q4 + g, kWave);
+    // sum_t p_t z_tg of each (head, group): over the lanes' token blocks,
+    // then lane g of a quad of row q4 holds group g
+    bzl += dpp_row<0x124>(bzl);
+    bzl += dpp_row<0x128>(bzl);
+    const float bz[4] = {dpp_row<0x00>(bzl), dpp_row<0x55>(bzl), dpp_row<0xAA>(bzl), dpp_row<0xFF>(bzl)};
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) o_lds[wave][q4][16 * ct + r16] = ov[ct] + bz[ct >> 1];
   }
