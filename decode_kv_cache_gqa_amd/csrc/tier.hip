@@ -154,6 +154,13 @@ __device__ __forceinline__ int dpp_row_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
 
+// A 16-byte load that streams past the caches (each byte is read once).
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  const u32x4v r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+
 __device__ __forceinline__ uint32_t word_of(const uint4& r, int i) {
   return i == 0 ? r.x : (i == 1 ? r.y : (i == 2 ? r.z : r.w));
 }
@@ -395,6 +402,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     bf16x8_t qa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[s] = as_b8(r16 < HG ? qraw[s] : make_uint4(0, 0, 0, 0));
+    // Loads are unconditional: a window past the list reads window 0 of the
+    // layer, and its logits are masked (-inf), so its values meet p = 0.
     uint4 kr[4][4], vr[2][8];
     int kpos[4];
     bool klive[4];
@@ -415,26 +424,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
       const uint16_t* kb = A.kfp + ((lh * A.NW + wk) * WT + rk) * D + 8 * q4;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        kr[jj][s] = klive[jj] ? *reinterpret_cast<const uint4*>(kb + 32 * s) : make_uint4(0, 0, 0, 0);
+        kr[jj][s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       int wv, r0;
-      bool lv;
       if constexpr (WT == 32) {
         wv = win[k];
-        lv = live[k];
         r0 = 8 * q4;
       } else {
         const int a = 4 * k;
         wv = q4 == 0 ? win[a] : (q4 == 1 ? win[a + 1] : (q4 == 2 ? win[a + 2] : win[a + 3]));
-        lv = q4 == 0 ? live[a] : (q4 == 1 ? live[a + 1] : (q4 == 2 ? live[a + 2] : live[a + 3]));
         r0 = 0;
       }
       const uint16_t* vb = A.vfp + (lh * A.NW + wv) * WT * D + r16 * WT + r0;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
-        vr[k][ct] = lv ? *reinterpret_cast<const uint4*>(vb + 16 * ct * WT) : make_uint4(0, 0, 0, 0);
+        vr[k][ct] = *reinterpret_cast<const uint4*>(vb + 16 * ct * WT);
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     uint4 kc[kQW], ksr[kQW], kzr[kQW];
 #pragma unroll
     for (int k = 0; k < kQW; ++k) {
-      kc[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecK + 16 * lane);
+      kc[k] = ld_nt(recs[k] + kRecK + 16 * lane);
       ksr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecSK + 16 * cs);
       kzr[k] = *reinterpret_cast<const uint4*>(recs[k] + kRecZK + 16 * cs);
     }
@@ -606,8 +612,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     for (int pr = 0; pr < kQW / 2; ++pr) {
       const uint8_t* rc = (q4 >> 1) ? recs[2 * pr + 1] : recs[2 * pr];
       const uint8_t* b = rc + kRecV + 32 * ((q4 & 1) * 16 + r16);
-      vc[pr][0] = *reinterpret_cast<const uint4*>(b);
-      vc[pr][1] = *reinterpret_cast<const uint4*>(b + 16);
+      vc[pr][0] = ld_nt(b);
+      vc[pr][1] = ld_nt(b + 16);
     }
     // softmax statistics of head q4 over the wave's windows
     float m = lgt[0];
