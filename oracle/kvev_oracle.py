@@ -1465,8 +1465,9 @@ class TieredOracle:
                 st.Keff[:, sl(w)] = st.K[:, sl(w)]
                 st.Veff[:, sl(w)] = st.V[:, sl(w)]
                 st.tier[w] = "F"
-            for w in E:
+            for w in E:                                  # evicted for good: the record is freed too
                 st.tier[w] = "E"
+                st.ledger.pop(w, None)
 
     # -- views used by tests ------------------------------------------------
     def window_state(self, l):

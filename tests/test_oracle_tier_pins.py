@@ -321,3 +321,36 @@ def test_routing_every_omega_steps():
         assert routed_f == F
         assert all(tiers2[w] == 2 for w in E)
         prev = tiers2.copy()
+
+
+def test_held_memory_stays_within_the_byte_budget():
+    """§4.1 (Budget) and §4.3 Eq.3: an evicted window holds nothing, not
+    even its INT2 record; after every routing event the full-precision
+    windows are the pinned and local ones plus at most K_f routed ones, and
+    the records held are those of the F and Q windows that were ever
+    quantized, at most K_f + K_q."""
+    rng = np.random.default_rng(27)
+    L, Hq, Hkv, d, n, T = 1, 8, 2, 64, 320, 64
+    K, V, q, kn, vn = _inputs(rng, L, Hq, Hkv, d, n, T, heavy=8.0)
+    W, k_f, k_q, n_sink, n_recent = 8, 4, 12, 5, 8
+    o = orc.TieredOracle(L, Hq, Hkv, d, k_f=k_f, k_q=k_q, window=W, n_sink=n_sink, n_recent=n_recent)
+    o.prefill(K, V)
+    ever = set()
+    dropped = []
+
+    def check(t):
+        _, tiers, ledger = o.window_state(0)
+        nw = len(tiers)
+        routed = [w for w in range(nw) if o.is_aged(w)]
+        assert not (ledger & (tiers == 2)).any(), f"step {t}: an evicted window holds a record"
+        assert int(((tiers == 0) & np.isin(np.arange(nw), routed)).sum()) <= k_f
+        assert int(ledger.sum()) <= k_f + k_q
+        held = set(np.flatnonzero(ledger).tolist())
+        dropped.extend(w for w in ever - held if tiers[w] == 2)
+        ever.update(held)
+        for w in range(nw):
+            if w not in routed:
+                assert tiers[w] == 0        # pinned and local windows stay full precision
+
+    _run(o, q, kn, vn, check)
+    assert dropped, "some quantized window should be evicted (and lose its record)"
