@@ -199,6 +199,20 @@ def tier_bytes(w, n_fp_tokens, n_q):
     return kv, kv + extra
 
 
+def tier_footprint_record(w, fp):
+    """The context's window memory against the byte budget of the review's
+    section 4.3 Eq.3, B_hist = K_f M_f + K_q M_q over all layers (M_f: a
+    window's full-precision K/V, M_q: its INT2 record, per KV head)."""
+    W, d = w.window_tokens, w.head_dim
+    rec = 1152 if W == 8 else 3072
+    lh = w.n_layers * w.n_kv_heads
+    m_f, m_q = W * 2 * d * 2, rec
+    return {"fp_pool_bytes": fp["fp_pool"], "record_pool_bytes": fp["record_pool"],
+            "staging_bytes": fp["staging"], "fp_slots": fp["fp_slots"], "record_slots": fp["record_slots"],
+            "eq3_b_hist_bytes": lh * (w.fp_windows * m_f + w.int2_windows * m_q),
+            "all_full_precision_bytes": lh * (-(-(w.prefill_lens[0]) // W)) * m_f}
+
+
 def tier_cpu_baseline(w, steps=3):
     """The CPU oracle on one layer of the tiered workload: the first routing
     event untimed, then two segments of `steps` steady steps (one BLAS
@@ -331,11 +345,12 @@ def run_tier(args, w):
     import torch
     from decode_kv_cache_gqa_amd import kvev
 
-    if args.warmup < max(w.route_interval, 1):
-        # the steps before the first routing event attend every prefill window in full precision
-        print(f"warmup raised to the routing interval ({w.route_interval}) so that the timed steps are "
-              "steady", file=sys.stderr)
-        args.warmup = w.route_interval
+    if args.warmup < max(w.route_interval, 1) + 1:
+        # the steps before the first routing event attend every prefill window in full precision,
+        # and the step after it releases the prefill staging buffers
+        print(f"warmup raised to the routing interval + 1 ({w.route_interval + 1}) so that the timed "
+              "steps are steady", file=sys.stderr)
+        args.warmup = max(w.route_interval, 1) + 1
     total = args.warmup + args.steps
     ctx = kvev.context_for(w, max_steps=total)
     K, V = w.prefill_kv(0, device="cuda")
@@ -349,6 +364,7 @@ def run_tier(args, w):
     dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
     prof = {k: ctx.profile_read(k) for k in ("append", "attn", "merge", "route")}
     _, tiers, _ = ctx.tier_state(0)
+    fp = ctx.tier_footprint()
     npos = w.prefill_lens[0] + total
     ctx.close()
     n_fp_win = int((tiers == 0).sum())
@@ -372,6 +388,7 @@ def run_tier(args, w):
                    "fp_windows": w.fp_windows, "int2_windows": w.int2_windows, "n_sink": w.n_sink,
                    "n_recent": w.n_recent},
         "listed_windows": {"full_precision": n_fp_win, "int2": n_q},
+        "device_footprint": tier_footprint_record(w, fp),
         "kv_read_GBps": round(step_bytes / (dt / args.steps) / 1e9, 1),
         "pct_hbm_peak": round(100.0 * step_bytes / (dt / args.steps) / 1e9 / HBM_PEAK_GBPS, 2),
         "score_topk_compaction_share": round(policy_ms / ms_step, 4) if ms_step > 0 else None,

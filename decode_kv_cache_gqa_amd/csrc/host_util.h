@@ -47,7 +47,7 @@ struct ProfScope {
   ProfScope(kvev_ctx* c_, const char* n) : c(c_), name(n) {
     if (!c->prof.enabled || !name) return;
     a = take_event();
-    hipEventRecord(a, c->stream);
+    if (a) hipEventRecord(a, c->stream);
   }
   hipEvent_t take_event() {
     if (!c->prof.pool.empty()) {
@@ -55,13 +55,14 @@ struct ProfScope {
       c->prof.pool.pop_back();
       return e;
     }
-    hipEvent_t e;
-    hipEventCreate(&e);
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
   }
   ~ProfScope() {
     if (!c->prof.enabled || !name || !a) return;
     hipEvent_t b = take_event();
+    if (!b) return;
     hipEventRecord(b, c->stream);
     c->prof.pending.push_back({name, a, b});
   }

@@ -27,6 +27,7 @@ constexpr int kTierMaxWin = 12288;      // windows per sequence (393216 position
 constexpr int kTierLedgerBytes8 = 1152; // INT2 record of an 8-token window
 inline int tier_rec_bytes(int w) { return w == 8 ? kTierLedgerBytes8 : kTierLedgerBytes; }
 constexpr int kTierXferBlocks = 64;     // blocks per layer of the transition kernel
+constexpr int kTierWinBits = 14;        // a list entry is slot << kTierWinBits | window
 // rank-trace diagnostics
 constexpr int kDiagCounts = 12;  // the int32 counts of kvev_diag_group, in order
 constexpr int kDiagAcc = 7;      // steps, pairs and the five sums
@@ -97,10 +98,20 @@ struct DevState {
 
 // Device buffers of the two-tier window mode ([L][Hkv][NW] windows).
 struct TierDev {
-  uint16_t* kfp = nullptr;   // [L][Hkv][NW][W][128] bf16 keys, token-major (rotated in rotary mode)
-  uint16_t* vfp = nullptr;   // [L][Hkv][NW][128][W] bf16 values, channel-major
-  uint8_t* ledger = nullptr; // [L][Hkv][NW][record bytes] INT2 codes and parameters
-  uint16_t* kpre = nullptr;  // rotary mode: [L][Hkv][NW][W][128] bf16 keys before the rotation
+  // full-precision slot pool: SF window slots per (layer, KV head)
+  uint16_t* kfp = nullptr;   // [L][Hkv][SF][W][128] bf16 keys, token-major (rotated in rotary mode)
+  uint16_t* vfp = nullptr;   // [L][Hkv][SF][128][W] bf16 values, channel-major
+  uint16_t* kpre = nullptr;  // rotary mode: [L][Hkv][SF][W][128] bf16 keys before the rotation
+  // INT2 record pool: SQ records per (layer, KV head)
+  uint8_t* ledger = nullptr; // [L][Hkv][SQ][record bytes] INT2 codes and parameters
+  // prefill staging (until the first routing event has placed every prefill
+  // window): NWS windows in the layout of the pool; slot SF + w is window w
+  uint16_t* kst = nullptr;
+  uint16_t* vst = nullptr;
+  uint16_t* kpst = nullptr;
+  int* fslot = nullptr;      // [L][NW] full-precision slot of each window (-1: none)
+  int* lslot = nullptr;      // [L][NW] record slot of each window (-1: none)
+  int* ffree = nullptr;      // [L][SF] the free full-precision slots after the last routing event, ascending
   double* rcs = nullptr;     // rotary mode: [max_tokens][64][2] cos and sin of position * frequency
   double* ifreq = nullptr;   // rotary mode: [64] frequencies theta^(-2i/128)
   uint8_t* tier = nullptr;   // [L][NW] 0 full precision, 1 INT2, 2 evicted
@@ -115,7 +126,7 @@ struct TierDev {
   double* rd_acc = nullptr;  // [L][6] events, pairs, churn sums, sustained, revived
   int* fplist = nullptr;     // [L][NW] full-precision windows (pinned, local, routed)
   int* qlist = nullptr;      // [L][NW] INT2 windows
-  int* jobs = nullptr;       // [L][NW] transition jobs: window << 2 | kind (1 quantize, 2 promote)
+  int4* jobs = nullptr;      // [L][NW] transition jobs: (window << 2 | kind, source slot, slot, record slot)
   int* njobs = nullptr;      // [L]
   float* emass = nullptr;    // [L][Hkv][NW][4] per listed window and head: sum exp(s - chunk max)
 };
@@ -124,6 +135,11 @@ struct TierDev {
 // layer: every layer routes the same number of candidates).
 struct TierHost {
   int NW = 0, maxch = 0;
+  int SF = 0, SQ = 0;  // full-precision and record slots per (layer, KV head)
+  int NWS = 0;         // prefill windows in the staging buffers (0: none allocated)
+  bool stage_done = false;  // every prefill window placed: the staging buffers may be freed
+  int held = 0;        // full-precision slots held after the last routing event
+  int opened = 0;      // windows opened since then (each took the next free slot)
   int W = 32;          // tokens per window
   bool rope = false;   // rotary mode (cfg.rope_theta > 0)
   bool mat = false;    // INT2 windows are attended through their bf16 reconstruction, kept in the
@@ -146,7 +162,7 @@ struct TierArgs {
   float* S;
   int* fplist;
   int* qlist;
-  int* jobs;
+  int4* jobs;
   int* njobs;
   float* part_ml;  // [L][Hkv][maxch][4][2]
   float* part_o;   // [L][Hkv][maxch][4][128]
@@ -164,6 +180,13 @@ struct TierArgs {
   uint16_t* kpre;
   double* rcs;
   const double* ifreq;
+  uint16_t* kst;
+  uint16_t* vst;
+  uint16_t* kpst;
+  int* fslot;
+  int* lslot;
+  int* ffree;
+  int SF, SQ, NWS;
 };
 
 struct Profiler {
@@ -318,11 +341,11 @@ hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* src_dev)
 // two-tier window mode (tier.hip)
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n);
 hipError_t launch_tier_rope_table(kvev_ctx* c, int64_t p0, int64_t n);
-hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new);
+hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new, int kslot);
 hipError_t launch_tier_attention(kvev_ctx* c, const void* q);
 hipError_t launch_tier_merge(kvev_ctx* c, float* out);
 hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp_fp, int exp_q,
-                             const uint8_t* forced_dev);
+                             const uint8_t* forced_dev, int layer);  // layer < 0: every layer
 hipError_t launch_tier_export(kvev_ctx* c, int l, int h, void* k_out, void* v_out, int nwin);
 // host side of the tiered mode (tier_api.cpp)
 hipError_t tier_alloc(kvev_ctx* c);
@@ -339,7 +362,7 @@ inline hipEvent_t prof_event(kvev_ctx* c) {
     return e;
   }
   hipEvent_t e = nullptr;
-  hipEventCreate(&e);
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -351,6 +374,10 @@ hipError_t timed_launch(kvev_ctx* c, const char* name, F kern, dim3 grid, dim3 b
     return hipGetLastError();
   }
   hipEvent_t a = prof_event(c), b = prof_event(c);
+  if (!a || !b) {  // no events to be had: launch untimed
+    kern<<<grid, block, shm, c->stream>>>(args...);
+    return hipGetLastError();
+  }
   hipExtLaunchKernelGGL(kern, grid, block, static_cast<uint32_t>(shm), c->stream, a, b, 0, args...);
   c->prof.pending.push_back({name, a, b});
   return hipGetLastError();

@@ -209,6 +209,25 @@ __device__ __forceinline__ float rope_elem(float x, float y, int c, const double
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float((b & 0xffffu) << 16); }
 
+// Full-precision storage of slot s of (layer, KV head) lh: the pool below
+// SF, the prefill staging (window s - SF) above.
+__device__ __forceinline__ uint16_t* kfp_at(const TierArgs& A, int64_t lh, int s, int Wn) {
+  return s < A.SF ? A.kfp + (lh * A.SF + s) * Wn * kTierD : A.kst + (lh * A.NWS + (s - A.SF)) * Wn * kTierD;
+}
+__device__ __forceinline__ uint16_t* vfp_at(const TierArgs& A, int64_t lh, int s, int Wn) {
+  return s < A.SF ? A.vfp + (lh * A.SF + s) * Wn * kTierD : A.vst + (lh * A.NWS + (s - A.SF)) * Wn * kTierD;
+}
+__device__ __forceinline__ uint16_t* kpre_at(const TierArgs& A, int64_t lh, int s, int Wn) {
+  return s < A.SF ? A.kpre + (lh * A.SF + s) * Wn * kTierD : A.kpst + (lh * A.NWS + (s - A.SF)) * Wn * kTierD;
+}
+__device__ __forceinline__ uint8_t* rec_at(const TierArgs& A, int64_t lh, int s, int bytes) {
+  return A.ledger + (lh * A.SQ + s) * static_cast<int64_t>(bytes);
+}
+// list entry: slot << kTierWinBits | window
+__device__ __forceinline__ int ent_win(int e) { return e & ((1 << kTierWinBits) - 1); }
+__device__ __forceinline__ int ent_slot(int e) { return e >> kTierWinBits; }
+__device__ __forceinline__ int make_ent(int slot, int w) { return (slot << kTierWinBits) | w; }
+
 __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -217,8 +236,9 @@ __device__ __forceinline__ f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, co
 
 // ---------------------------------------------------------------------------
 // Prefill: windows [0, nwin) of every (layer, KV head) from k, v
-// [L][Hkv][n][128]; tokens past n are zero.  Block (w, h, l), 256 threads.
-// Also resets the window state of layer l (h == 0).
+// [L][Hkv][n][128] into the staging buffers; tokens past n are zero.  Block
+// (w, h, l), 256 threads.  Also resets the window state of layer l (h == 0):
+// window w holds staging slot SF + w.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v, int n) {
@@ -227,15 +247,15 @@ __global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uin
   const int Wn = A.W;  // tokens per window (8 or 32)
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int64_t src0 = lh * n;
-  uint16_t* kd = A.kfp + (lh * A.NW + w) * Wn * D;
-  uint16_t* vd = A.vfp + (lh * A.NW + w) * Wn * D;
+  uint16_t* kd = kfp_at(A, lh, A.SF + w, Wn);
+  uint16_t* vd = vfp_at(A, lh, A.SF + w, Wn);
   for (int i = tid; i < Wn * D; i += 256) {
     const int r = i / D, c = i % D;
     const int p = w * Wn + r;
     const bool in = p < n;
     const uint16_t kv = in ? k[(src0 + p) * D + c] : 0;
     if (A.rope) {  // rotary mode: keep the key as given, store it rotated at its position
-      A.kpre[(lh * A.NW + w) * Wn * D + i] = kv;
+      kpre_at(A, lh, A.SF + w, Wn)[i] = kv;
       const uint16_t kp = in ? k[(src0 + p) * D + (c ^ 64)] : 0;
       kd[i] = in ? static_cast<uint16_t>(bf16_rne(rope_elem(bf2f(kv), bf2f(kp), c, A.rcs + static_cast<int64_t>(p) * 128)))
                  : 0;
@@ -251,7 +271,9 @@ __global__ __launch_bounds__(256) void tier_prefill_kernel(TierArgs A, const uin
   }
   if (h == 0 && tid == 0) {
     const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
-    A.fplist[lw] = w;
+    A.fplist[lw] = make_ent(A.SF + w, w);
+    A.fslot[lw] = A.SF + w;
+    A.lslot[lw] = -1;
     A.tier[lw] = 0;
     A.hasled[lw] = 0;
     A.S[lw] = 0.f;
@@ -275,28 +297,33 @@ __global__ __launch_bounds__(256) void tier_rope_table_kernel(TierArgs A, int64_
 
 // ---------------------------------------------------------------------------
 // Append: the new token (position npos) into its window's storage.  When it
-// opens a window, that window starts full precision with score 0 and joins
-// the full-precision list at index n_fp.  Block (h, l), 128 threads.
+// opens a window, that window takes free slot kslot of its layer (the
+// kslot-th window opened since the last routing event), starts full
+// precision with score 0 and joins the full-precision list at index n_fp.
+// Block (h, l), 128 threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint16_t* __restrict__ k_new,
                                                           const uint16_t* __restrict__ v_new, int npos,
-                                                          int n_fp) {
+                                                          int n_fp, int kslot) {
   const int h = blockIdx.x, l = blockIdx.y, c = threadIdx.x;
   const int Wn = A.W;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int w = npos / Wn, r = npos % Wn;
-  const int64_t ki = ((lh * A.NW + w) * Wn + r) * D + c;
+  const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
+  const int slot = max(r == 0 ? A.ffree[static_cast<int64_t>(l) * A.SF + kslot] : A.fslot[lw], 0);
+  const int64_t ki = static_cast<int64_t>(r) * D + c;
   if (A.rope) {
-    A.kpre[ki] = k_new[lh * D + c];
-    A.kfp[ki] = static_cast<uint16_t>(bf16_rne(rope_elem(bf2f(k_new[lh * D + c]), bf2f(k_new[lh * D + (c ^ 64)]), c,
-                                                         A.rcs + static_cast<int64_t>(npos) * 128)));
+    kpre_at(A, lh, slot, Wn)[ki] = k_new[lh * D + c];
+    kfp_at(A, lh, slot, Wn)[ki] = static_cast<uint16_t>(bf16_rne(
+        rope_elem(bf2f(k_new[lh * D + c]), bf2f(k_new[lh * D + (c ^ 64)]), c, A.rcs + static_cast<int64_t>(npos) * 128)));
   } else {
-    A.kfp[ki] = k_new[lh * D + c];
+    kfp_at(A, lh, slot, Wn)[ki] = k_new[lh * D + c];
   }
-  A.vfp[(lh * A.NW + w) * Wn * D + c * Wn + r] = v_new[lh * D + c];
+  vfp_at(A, lh, slot, Wn)[c * Wn + r] = v_new[lh * D + c];
   if (r == 0 && h == 0 && c == 0) {
-    const int64_t lw = static_cast<int64_t>(l) * A.NW + w;
-    A.fplist[static_cast<int64_t>(l) * A.NW + n_fp] = w;
+    A.fplist[static_cast<int64_t>(l) * A.NW + n_fp] = make_ent(slot, w);
+    A.fslot[lw] = slot;
+    A.lslot[lw] = -1;
     A.tier[lw] = 0;
     A.hasled[lw] = 0;
     A.S[lw] = 0.f;
@@ -347,13 +374,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
   const int nlist = isq ? n_q : n_fp;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int* list = (isq ? A.qlist : A.fplist) + static_cast<int64_t>(l) * A.NW;
-  int win[NWIN];
+  int win[NWIN], slot[NWIN];  // window and its storage slot (full precision, or its record)
   bool live[NWIN];
 #pragma unroll
   for (int k = 0; k < NWIN; ++k) {
     const int idx = base + wpw * wave + k;
     live[k] = k < wpw && idx < nlist;
-    win[k] = live[k] ? list[idx] : 0;
+    const int e = live[k] ? list[idx] : 0;
+    win[k] = ent_win(e);
+    slot[k] = ent_slot(e);
   }
 
   // the lane's query row (head r16 & 3) on channels 32s + 8q4 .. +8
@@ -409,35 +438,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     bool klive[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      int wk, rk;
+      int wk, sk, rk;
       if constexpr (WT == 32) {
         wk = win[jj >> 1];
+        sk = slot[jj >> 1];
         klive[jj] = live[jj >> 1];
         rk = 16 * (jj & 1) + r16;
       } else {
         const bool up = r16 >= 8;
         wk = up ? win[2 * jj + 1] : win[2 * jj];
+        sk = up ? slot[2 * jj + 1] : slot[2 * jj];
         klive[jj] = up ? live[2 * jj + 1] : live[2 * jj];
         rk = r16 & 7;
       }
       kpos[jj] = wk * WT + rk;
-      const uint16_t* kb = A.kfp + ((lh * A.NW + wk) * WT + rk) * D + 8 * q4;
+      const uint16_t* kb = kfp_at(A, lh, sk, WT) + rk * D + 8 * q4;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         kr[jj][s] = *reinterpret_cast<const uint4*>(kb + 32 * s);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      int wv, r0;
+      int sv, r0;
       if constexpr (WT == 32) {
-        wv = win[k];
+        sv = slot[k];
         r0 = 8 * q4;
       } else {
         const int a = 4 * k;
-        wv = q4 == 0 ? win[a] : (q4 == 1 ? win[a + 1] : (q4 == 2 ? win[a + 2] : win[a + 3]));
+        sv = q4 == 0 ? slot[a] : (q4 == 1 ? slot[a + 1] : (q4 == 2 ? slot[a + 2] : slot[a + 3]));
         r0 = 0;
       }
-      const uint16_t* vb = A.vfp + (lh * A.NW + wv) * WT * D + r16 * WT + r0;
+      const uint16_t* vb = vfp_at(A, lh, sv, WT) + r16 * WT + r0;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
         vr[k][ct] = *reinterpret_cast<const uint4*>(vb + 16 * ct * WT);
@@ -543,7 +574,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
     // its logits are -inf, so its probabilities and p.V digits are 0).
     const uint8_t* recs[kQW];
 #pragma unroll
-    for (int k = 0; k < kQW; ++k) recs[k] = A.ledger + (lh * A.NW + win[k]) * static_cast<int64_t>(kTierLedgerBytes);
+    for (int k = 0; k < kQW; ++k) recs[k] = rec_at(A, lh, slot[k], kTierLedgerBytes);
     uint4 kc[kQW], ksr[kQW], kzr[kQW];
 #pragma unroll
     for (int k = 0; k < kQW; ++k) {
@@ -815,8 +846,8 @@ __global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, in
   if (idx >= n_fp + n_q) return;
   const bool isq = idx >= n_fp;
   const int chunk = isq ? nch_f + (idx - n_fp) / cw_q : idx / cw_f;  // cw_*: windows per chunk
-  const int w = isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
-                    : A.fplist[static_cast<int64_t>(l) * A.NW + idx];
+  const int w = ent_win(isq ? A.qlist[static_cast<int64_t>(l) * A.NW + idx - n_fp]
+                            : A.fplist[static_cast<int64_t>(l) * A.NW + idx]);
   float acc = 0.f;
   // the KV heads in batches of 8, every load of a batch issued before use
   for (int h0 = 0; h0 < A.Hkv; h0 += 8) {
@@ -845,26 +876,82 @@ __global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, in
 }
 
 // ---------------------------------------------------------------------------
-// Routing event of layer l (one block of 1024 threads per layer).
-// Candidates are the aged windows (w >= np, 32(w+1) <= recent_lo) not yet
-// evicted; each is ranked by (score, window) descending; rank < k_f stays /
-// becomes full precision, rank < k_f + k_q INT2, the rest evicted.  With
-// `forced` the tiers of every window are taken from it instead (state
-// import).  Emits the quantize (first demotion) and promote jobs, then
-// rebuilds the full-precision and INT2 lists in window order.  The counts
-// must equal the host's (exp_fp, exp_q); otherwise errflag bit 32.
+// Routing event of layer l0 + blockIdx.x (one block of 1024 threads per
+// layer).  Candidates are the aged windows (w >= np, W(w+1) <= recent_lo)
+// not yet evicted; each is ranked by (score, window) descending; rank < k_f
+// stays / becomes full precision, rank < k_f + k_q INT2, the rest evicted.
+// With `forced` the tiers of every window are taken from it instead (state
+// import).  Then the storage follows the tiers:
+//   * a window keeps its full-precision slot while it stays full precision
+//     (with bf16 reconstructions: also while INT2); a prefill window moves
+//     from the staging buffers into a slot of the pool (adopt job); a
+//     promoted window takes a new slot (promote job); a demoted or evicted
+//     window releases its slot;
+//   * a first demotion takes a record slot (quantize job, which also writes
+//     the bf16 reconstruction where INT2 windows are read through it); an
+//     evicted window releases its record.
+// New slots are the lowest free ones, given in window order; a slot released
+// by this event may be taken by it (the quantize jobs, which read released
+// slots, run before the promote and adopt jobs, which write new ones).  The
+// lists are rebuilt in window order with each entry's slot.  Errors (flag
+// bits): the list sizes differ from the host's (exp_fp, exp_q): 32; an
+// evicted window would be kept (its storage is gone): 64; a pool is
+// exhausted: 128.
 // ---------------------------------------------------------------------------
 constexpr int kRouteNT = 1024;
+constexpr int kSlotWords = kTierMaxWin / 32;  // bitmap words of a slot pool
+
+// Stable rank of the calling thread's first item among the items of the
+// block (thread tid owning a consecutive run of cnt items): an exclusive
+// block-wide prefix sum.  `ws` holds kRouteNT / 64 ints of scratch; returns
+// the total in `tot`.
+__device__ __forceinline__ int block_excl_scan(int cnt, int* ws, int& tot) {
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  int x = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) ws[wv] = x;
+  __syncthreads();
+  int off = x - cnt;
+  tot = 0;
+  for (int u = 0; u < kRouteNT / kWave; ++u) {
+    if (u < wv) off += ws[u];
+    tot += ws[u];
+  }
+  return off;
+}
+
+// The r-th set bit (0-based) of a bitmap of nw words whose exclusive prefix
+// popcounts are pre[]; -1 when there are not that many.
+__device__ __forceinline__ int nth_bit(const uint32_t* bits, const int* pre, int nw, int total, int r) {
+  if (r >= total) return -1;
+  int lo = 0, hi = nw - 1;  // the last word with pre <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  uint32_t b = bits[lo];
+  for (int k = r - pre[lo]; k > 0; --k) b &= b - 1;
+  return 32 * lo + __builtin_ctz(b);
+}
 
 __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw, int np, int recent_lo,
                                                               int k_f, int k_q, int exp_fp, int exp_q,
-                                                              const uint8_t* __restrict__ forced) {
-  __shared__ unsigned long long keys[kTierMaxWin];
-  __shared__ uint8_t tl[kTierMaxWin];
-  __shared__ uint8_t hl[kTierMaxWin];
-  __shared__ int ncand, njobs, wsum[2][kRouteNT / kWave], base[2];
+                                                              const uint8_t* __restrict__ forced, int l0) {
+  __shared__ unsigned long long keys[kTierMaxWin];  // the ranking; then the two slot arrays
+  __shared__ uint8_t tl[kTierMaxWin];               // tier after the event
+  __shared__ uint8_t hl[kTierMaxWin];               // record held after the event
+  __shared__ uint8_t act[kTierMaxWin];              // bit 0 new full-precision slot, bit 1 new record, bits 2.. job
+  __shared__ uint32_t freeF[kSlotWords], freeQ[kSlotWords];
+  __shared__ int preF[kSlotWords], preQ[kSlotWords];
+  __shared__ int ncand, njobs, wsum[kRouteNT / kWave], tots[4];
   __shared__ int dsum[6][kRouteNT / kWave];
-  const int l = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int l = l0 + blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int64_t lw0 = static_cast<int64_t>(l) * A.NW;
   if (tid == 0) {
     ncand = 0;
@@ -901,34 +988,130 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
 #pragma unroll
       for (int u = 0; u < 8; ++u) rank += part[u];
       const int w = static_cast<int>(ki & 0xffffffffu);
-      const uint8_t nt = rank < k_f ? 0 : (rank < k_f + k_q ? 1 : 2);
-      const uint8_t ot = tl[w];
-      if (nt == 1 && !hl[w]) {
-        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 1;
-        hl[w] = 1;
-      } else if (nt == 0 && ot == 1) {
-        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 2;
-      }
-      tl[w] = nt;
+      tl[w] = rank < k_f ? 0 : (rank < k_f + k_q ? 1 : 2);
     }
   } else {
-    for (int w = tid; w < nw; w += kRouteNT) {
-      const uint8_t nt = forced[lw0 + w];
-      const uint8_t ot = tl[w];
-      if (nt == 1 && !hl[w]) {
-        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 1;
-        hl[w] = 1;
-      } else if (nt == 0 && ot == 1) {
-        A.jobs[lw0 + atomicAdd(&njobs, 1)] = (w << 2) | 2;
+    for (int w = tid; w < nw; w += kRouteNT) tl[w] = forced[lw0 + w];
+  }
+  __syncthreads();
+  // ---- storage of the new tiers --------------------------------------------
+  int* fs = reinterpret_cast<int*>(keys);  // [nw] full-precision slot
+  int* qs = fs + kTierMaxWin;              // [nw] record slot
+  for (int i = tid; i < kSlotWords; i += kRouteNT) {
+    freeF[i] = 0xffffffffu;
+    freeQ[i] = 0xffffffffu;
+  }
+  for (int w = tid; w < nw; w += kRouteNT) {
+    fs[w] = A.fslot[lw0 + w];
+    qs[w] = A.lslot[lw0 + w];
+  }
+  __syncthreads();
+  int err = 0;
+  for (int w = tid; w < nw; w += kRouteNT) {
+    const int o = A.tier[lw0 + w];
+    int t = tl[w];
+    if (o == 2 && t != 2) {  // an evicted window's storage is gone
+      err |= 64;
+      t = 2;
+      tl[w] = 2;
+    }
+    const bool h0 = hl[w] != 0;
+    const int f = fs[w], q = qs[w];
+    const bool needF = t == 0 || (A.mat && t == 1);
+    const bool quant = t == 1 && !h0;  // first demotion
+    const bool needQ = t != 2 && (h0 || quant);
+    const bool keepF = needF && f >= 0 && f < A.SF;
+    const bool keepQ = needQ && q >= 0;
+    uint8_t a = 0;
+    if (needF && !keepF) a |= 1;
+    if (needQ && !keepQ) a |= 2;
+    if (quant) a |= 1 << 2;                                    // quantize (from slot f)
+    else if (!A.mat && o == 1 && t == 0) a |= 2 << 2;         // promote (record q into a new slot)
+    else if (needF && f >= A.SF) a |= 3 << 2;                 // adopt (staging into a new slot)
+    act[w] = a;
+    hl[w] = needQ ? 1 : 0;
+    if (keepF) atomicAnd(&freeF[f >> 5], ~(1u << (f & 31)));
+    if (keepQ) atomicAnd(&freeQ[q >> 5], ~(1u << (q & 31)));
+    if (!keepF) fs[w] = -1;  // a new slot is given below when act bit 0 is set
+    if (!keepQ) qs[w] = -1;
+  }
+  if (err) atomicOr(A.errflag, err);
+  __syncthreads();
+  // free slots: prefix popcounts of the bitmaps (slots past the pool are not free)
+  const int nwf = (A.SF + 31) / 32, nwq = (A.SQ + 31) / 32;
+  for (int i = tid; i < kSlotWords; i += kRouteNT) {
+    const int bf = A.SF - 32 * i, bq = A.SQ - 32 * i;
+    freeF[i] &= bf >= 32 ? 0xffffffffu : (bf <= 0 ? 0u : (1u << bf) - 1u);
+    freeQ[i] &= bq >= 32 ? 0xffffffffu : (bq <= 0 ? 0u : (1u << bq) - 1u);
+  }
+  __syncthreads();
+  if (tid < kWave) {  // one wave scans both bitmaps
+    int cf = 0, cq = 0;
+    for (int i0 = 0; i0 < kSlotWords; i0 += kWave) {
+      const int i = i0 + lane;
+      int xf = __popc(freeF[i]), xq = __popc(freeQ[i]);
+      const int yf0 = xf, yq0 = xq;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int yf = __shfl_up(xf, o, kWave), yq = __shfl_up(xq, o, kWave);
+        if (lane >= o) {
+          xf += yf;
+          xq += yq;
+        }
       }
-      tl[w] = nt;
+      preF[i] = cf + xf - yf0;
+      preQ[i] = cq + xq - yq0;
+      cf += __shfl(xf, kWave - 1, kWave);
+      cq += __shfl(xq, kWave - 1, kWave);
+    }
+    if (lane == 0) {
+      tots[0] = cf;
+      tots[1] = cq;
     }
   }
   __syncthreads();
-  // stable compaction of the two lists: thread tid owns the consecutive
-  // windows [tid * E, tid * E + E); one block-wide exclusive scan of the
-  // per-thread counts gives each thread its offsets in both lists
+  // requests in window order: thread tid owns windows [tid * E, tid * E + E)
   const int E = (nw + kRouteNT - 1) / kRouteNT;
+  int rf = 0, rq = 0;
+  for (int e = 0; e < E; ++e) {
+    const int w = tid * E + e;
+    if (w < nw) {
+      rf += act[w] & 1;
+      rq += (act[w] >> 1) & 1;
+    }
+  }
+  int totF, totQ;
+  int offF = block_excl_scan(rf, wsum, totF);
+  int offQ = block_excl_scan(rq, wsum, totQ);
+  int err2 = 0;
+  for (int e = 0; e < E; ++e) {
+    const int w = tid * E + e;
+    if (w >= nw) continue;
+    const uint8_t a = act[w];
+    const int fold = A.fslot[lw0 + w];
+    int fnew = fs[w], qnew = qs[w];
+    if (a & 1) {
+      fnew = nth_bit(freeF, preF, nwf, tots[0], offF++);
+      if (fnew < 0) err2 |= 128;
+    }
+    if (a & 2) {
+      qnew = nth_bit(freeQ, preQ, nwq, tots[1], offQ++);
+      if (qnew < 0) err2 |= 128;
+    }
+    const int kind = a >> 2;
+    if (kind && !(err2 & 128)) {
+      // (window << 2 | kind, source full-precision slot, full-precision slot
+      // after the event, record slot)
+      A.jobs[lw0 + atomicAdd(&njobs, 1)] = make_int4((w << 2) | kind, fold, fnew, qnew);
+    }
+    fs[w] = fnew;
+    qs[w] = qnew;
+  }
+  if (err2) atomicOr(A.errflag, err2);
+  __syncthreads();
+  // stable compaction of the two lists (entries carry the slot the
+  // attention reads: the full-precision one, or the record for INT2 windows
+  // read from their codes)
   int cF = 0, cQ = 0;
   for (int e = 0; e < E; ++e) {
     const int w = tid * E + e;
@@ -937,39 +1120,44 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
       cQ += tl[w] == 1;
     }
   }
-  int xF = cF, xQ = cQ;  // inclusive scan within the wave
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int yF = __shfl_up(xF, o, kWave), yQ = __shfl_up(xQ, o, kWave);
-    if (lane >= o) {
-      xF += yF;
-      xQ += yQ;
-    }
-  }
-  if (lane == kWave - 1) {
-    wsum[0][wv] = xF;
-    wsum[1][wv] = xQ;
-  }
-  __syncthreads();
-  int offF = xF - cF, offQ = xQ - cQ, totF = 0, totQ = 0;
-  for (int u = 0; u < kRouteNT / kWave; ++u) {
-    if (u < wv) {
-      offF += wsum[0][u];
-      offQ += wsum[1][u];
-    }
-    totF += wsum[0][u];
-    totQ += wsum[1][u];
-  }
+  int totLF, totLQ;
+  int oF = block_excl_scan(cF, wsum, totLF);
+  int oQ = block_excl_scan(cQ, wsum, totLQ);
   for (int e = 0; e < E; ++e) {
     const int w = tid * E + e;
     if (w < nw) {
-      if (tl[w] == 0) A.fplist[lw0 + offF++] = w;
-      else if (tl[w] == 1) A.qlist[lw0 + offQ++] = w;
+      // (a slot that could not be given (flag 128) reads as slot 0: in
+      // bounds, and the step fails at the next check)
+      if (tl[w] == 0) A.fplist[lw0 + oF++] = make_ent(max(fs[w], 0), w);
+      else if (tl[w] == 1) A.qlist[lw0 + oQ++] = make_ent(max(A.mat ? fs[w] : qs[w], 0), w);
     }
   }
-  if (tid == 0) {
-    base[0] = totF;
-    base[1] = totQ;
+  // the free full-precision slots after the event, ascending (new windows
+  // take them in order until the next event)
+  __syncthreads();
+  for (int w = tid; w < nw; w += kRouteNT) {
+    const int f = fs[w];
+    if (f >= 0 && f < A.SF) atomicAnd(&freeF[f >> 5], ~(1u << (f & 31)));
+  }
+  __syncthreads();
+  {
+    int c = 0;
+    const int EW = (kSlotWords + kRouteNT - 1) / kRouteNT;
+    for (int e = 0; e < EW; ++e) {
+      const int i = tid * EW + e;
+      if (i < nwf) c += __popc(freeF[i]);
+    }
+    int tf;
+    int off = block_excl_scan(c, wsum, tf);
+    for (int e = 0; e < EW; ++e) {
+      const int i = tid * EW + e;
+      if (i >= nwf) continue;
+      uint32_t b = freeF[i];
+      while (b) {
+        A.ffree[static_cast<int64_t>(l) * A.SF + off++] = 32 * i + __builtin_ctz(b);
+        b &= b - 1;
+      }
+    }
   }
   // routing diagnostics over this event's candidates (aged, not evicted
   // before it): the stamps of the previous event give the overlaps, the run
@@ -1003,6 +1191,8 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     }
     A.tier[i] = tl[w];
     A.hasled[i] = hl[w];
+    A.fslot[i] = fs[w];
+    A.lslot[i] = qs[w];
   }
   if (diag) {
     int v[6] = {dF, dFo, dR, dRo, dS, dV};
@@ -1042,7 +1232,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   }
   if (tid == 0) {
     A.njobs[l] = njobs;
-    if (base[0] != exp_fp || base[1] != exp_q) atomicOr(A.errflag, 32);
+    if (totLF != exp_fp || totLQ != exp_q) atomicOr(A.errflag, 32);
   }
 }
 
@@ -1075,30 +1265,52 @@ __device__ __forceinline__ uint8_t int2_code(float x, float sc, float zp) {
   return static_cast<uint8_t>(fminf(fmaxf(r, 0.f), 3.f));
 }
 
-__global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
+__global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, int l0) {
   __shared__ float xk[W][D + 1];
   __shared__ float xv[W][D + 1];
   __shared__ uint8_t ck[W][D];
   __shared__ uint8_t cv[W][D];
   __shared__ uint32_t recl[kTierLedgerBytes / 4];
   __shared__ float ksc[D], kzp[D], vsc[W][4], vzp[W][4];  // the window's parameters as fp32
-  const int l = blockIdx.y, tid = threadIdx.x;
+  const int l = l0 + blockIdx.y, tid = threadIdx.x;
   const int nj = A.njobs[l];
   const int Wn = A.W;  // tokens per window (8 or 32)
-  // the layer's (job, KV head) pairs, strided over the blocks of the layer
+  // the layer's (job, KV head) pairs, strided over the blocks of the layer;
+  // phase 1 runs the quantize jobs, phase 2 the promote and adopt jobs
   for (int p = blockIdx.x; p < nj * A.Hkv; p += gridDim.x) {
     const int j = p / A.Hkv, h = p % A.Hkv;
     const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
-    const int job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
-    const int w = job >> 2, kind = job & 3;
-    uint16_t* kd = A.kfp + (lh * A.NW + w) * Wn * D;
-    uint16_t* vd = A.vfp + (lh * A.NW + w) * Wn * D;
+    const int4 job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
+    const int w = job.x >> 2, kind = job.x & 3;
+    if ((kind == 1) != (phase == 1)) continue;  // block-uniform
+    // every slot the job uses was given (the routing flags it otherwise)
+    const bool ok = kind == 1 ? (job.y >= 0 && job.w >= 0 && (!A.mat || job.z >= 0))
+                              : (kind == 2 ? (job.z >= 0 && job.w >= 0) : (job.y >= A.SF && job.z >= 0));
+    if (!ok) continue;
+    // source storage (quantize, adopt), the window's storage after the
+    // event (promote, adopt, the bf16 reconstruction of a quantize) and its
+    // record
+    const uint16_t* ksrc = job.y >= 0 ? kfp_at(A, lh, job.y, Wn) : nullptr;
+    const uint16_t* vsrc = job.y >= 0 ? vfp_at(A, lh, job.y, Wn) : nullptr;
+    uint16_t* kd = job.z >= 0 ? kfp_at(A, lh, job.z, Wn) : nullptr;
+    uint16_t* vd = job.z >= 0 ? vfp_at(A, lh, job.z, Wn) : nullptr;
     // keys are quantized before the rotation in rotary mode
-    const uint16_t* ks = A.rope ? A.kpre + (lh * A.NW + w) * Wn * D : kd;
-    uint8_t* rec = A.ledger + (lh * A.NW + w) * static_cast<int64_t>(A.recb);
+    const uint16_t* ks = A.rope && job.y >= 0 ? kpre_at(A, lh, job.y, Wn) : ksrc;
+    uint8_t* rec = job.w >= 0 ? rec_at(A, lh, job.w, A.recb) : nullptr;
     uint16_t* rec16 = reinterpret_cast<uint16_t*>(rec);
     uint32_t* rec32 = reinterpret_cast<uint32_t*>(rec);
-    if (kind == 1) {
+    if (kind == 3) {
+      // adopt: a prefill window from the staging buffers into its slot
+      for (int i0 = 8 * tid; i0 < Wn * D; i0 += 8 * 256) {
+        const uint4 kx = *reinterpret_cast<const uint4*>(ksrc + i0);
+        const uint4 vx = *reinterpret_cast<const uint4*>(vsrc + i0);
+        uint4 px = make_uint4(0, 0, 0, 0);
+        if (A.rope) px = *reinterpret_cast<const uint4*>(ks + i0);
+        *reinterpret_cast<uint4*>(kd + i0) = kx;
+        *reinterpret_cast<uint4*>(vd + i0) = vx;
+        if (A.rope) *reinterpret_cast<uint4*>(kpre_at(A, lh, job.z, Wn) + i0) = px;
+      }
+    } else if (kind == 1) {
       // stage the window in LDS as fp32: 8 consecutive elements of K
       // (token-major) and of V (channel-major) per 16-byte load, all loads
       // of the thread issued before the first store
@@ -1108,7 +1320,7 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         const int i0 = 8 * (tid + 256 * u);
         const bool in = i0 < Wn * D;
         kr[u] = in ? *reinterpret_cast<const uint4*>(ks + i0) : make_uint4(0, 0, 0, 0);
-        vr[u] = in ? *reinterpret_cast<const uint4*>(vd + i0) : make_uint4(0, 0, 0, 0);
+        vr[u] = in ? *reinterpret_cast<const uint4*>(vsrc + i0) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -1163,15 +1375,15 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
         // int8 product, 16 channels 64 ks + 16 q4 .. +16 of token 16 j + r16;
         // values: thread = (half hf, r16, tile ct), 16 tokens 16 hf .. +16 of
         // channel 16 ct + r16 (element k of a word at bits spread_bit(k))
-        const int ln = tid >> 2, jt = (tid >> 1) & 1, ks = tid & 1, r16 = ln & 15, q4 = ln >> 4;
+        const int ln = tid >> 2, jt = (tid >> 1) & 1, kx = tid & 1, r16 = ln & 15, q4 = ln >> 4;
         const int hf = tid >> 7, vr16 = (tid >> 3) & 15, ct = tid & 7;
         uint32_t kw = 0, vw = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          kw |= static_cast<uint32_t>(ck[16 * jt + r16][64 * ks + 16 * q4 + e]) << spread_bit(e);
+          kw |= static_cast<uint32_t>(ck[16 * jt + r16][64 * kx + 16 * q4 + e]) << spread_bit(e);
           vw |= static_cast<uint32_t>(cv[16 * hf + e][16 * ct + vr16]) << spread_bit(e);
         }
-        rec32[kRecK / 4 + 4 * ln + 2 * jt + ks] = kw;
+        rec32[kRecK / 4 + 4 * ln + 2 * jt + kx] = kw;
         rec32[kRecV / 4 + (hf * 16 + vr16) * 8 + ct] = vw;
       }
       if (A.mat) {
@@ -1255,19 +1467,21 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A) {
 
 // ---------------------------------------------------------------------------
 // Export of the full-precision storage of (layer l, KV head h), windows
-// [0, nwin), token-major: k_out, v_out [nwin * 32][128].
+// [0, nwin), token-major: k_out, v_out [nwin * W][128]; a window that holds
+// no full-precision storage exports zeros.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void tier_export_kernel(TierArgs A, int l, int h, uint16_t* __restrict__ k_out,
                                                           uint16_t* __restrict__ v_out) {
   const int w = blockIdx.x, tid = threadIdx.x;
   const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
   const int Wn = A.W;
-  const uint16_t* ks = A.kfp + (lh * A.NW + w) * Wn * D;
-  const uint16_t* vs = A.vfp + (lh * A.NW + w) * Wn * D;
+  const int s = A.fslot[static_cast<int64_t>(l) * A.NW + w];
+  const uint16_t* ks = s >= 0 ? kfp_at(A, lh, s, Wn) : nullptr;
+  const uint16_t* vs = s >= 0 ? vfp_at(A, lh, s, Wn) : nullptr;
   for (int i = tid; i < Wn * D; i += 256) {
     const int r = i / D, c = i % D;
-    k_out[static_cast<int64_t>(w) * Wn * D + i] = ks[i];
-    v_out[static_cast<int64_t>(w) * Wn * D + i] = vs[c * Wn + r];
+    k_out[static_cast<int64_t>(w) * Wn * D + i] = s >= 0 ? ks[i] : 0;
+    v_out[static_cast<int64_t>(w) * Wn * D + i] = s >= 0 ? vs[c * Wn + r] : 0;
   }
 }
 
@@ -1310,6 +1524,15 @@ static TierArgs tier_args(kvev_ctx* c) {
   a.kpre = c->td.kpre;
   a.rcs = c->td.rcs;
   a.ifreq = c->td.ifreq;
+  a.kst = c->td.kst;
+  a.vst = c->td.vst;
+  a.kpst = c->td.kpst;
+  a.fslot = c->td.fslot;
+  a.lslot = c->td.lslot;
+  a.ffree = c->td.ffree;
+  a.SF = c->tw.SF;
+  a.SQ = c->tw.SQ;
+  a.NWS = c->tw.NWS;
   return a;
 }
 
@@ -1333,11 +1556,11 @@ hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new) {
+hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new, int kslot) {
   dim3 grid(c->cfg.n_kv_heads, c->cfg.n_layers);
   tier_append_kernel<<<grid, D, 0, c->stream>>>(tier_args(c), static_cast<const uint16_t*>(k_new),
                                                 static_cast<const uint16_t*>(v_new),
-                                                static_cast<int>(c->tw.npos), c->tw.n_fp);
+                                                static_cast<int>(c->tw.npos), c->tw.n_fp, kslot);
   return hipGetLastError();
 }
 
@@ -1377,14 +1600,18 @@ hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
 }
 
 hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp_fp, int exp_q,
-                             const uint8_t* forced_dev) {
+                             const uint8_t* forced_dev, int layer) {
   TierArgs a = tier_args(c);
-  tier_route_kernel<<<c->cfg.n_layers, kRouteNT, 0, c->stream>>>(
-      a, nw, np, recent_lo, c->cfg.fp_windows, c->cfg.int2_windows, exp_fp, exp_q, forced_dev);
+  const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? c->cfg.n_layers : 1;
+  tier_route_kernel<<<nl, kRouteNT, 0, c->stream>>>(a, nw, np, recent_lo, c->cfg.fp_windows,
+                                                   c->cfg.int2_windows, exp_fp, exp_q, forced_dev, l0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 gx(kTierXferBlocks, c->cfg.n_layers);
-  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a);
+  dim3 gx(kTierXferBlocks, nl);
+  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a, 1, l0);  // quantize (reads released slots)
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a, 2, l0);  // promote and adopt (write new slots)
   return hipGetLastError();
 }
 

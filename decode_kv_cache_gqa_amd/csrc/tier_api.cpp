@@ -45,11 +45,50 @@ void tier_free(kvev_ctx* c) {
   auto& t = c->td;
   void* ptrs[] = {t.kfp, t.vfp, t.ledger, t.tier, t.hasled, t.forced, t.S,
                   t.fplist, t.qlist, t.jobs, t.njobs, t.emass, t.rd_fstamp, t.rd_rstamp,
-                  t.rd_run, t.rd_cnt, t.rd_acc, t.kpre, t.rcs, t.ifreq};
+                  t.rd_run, t.rd_cnt, t.rd_acc, t.kpre, t.rcs, t.ifreq, t.kst, t.vst, t.kpst,
+                  t.fslot, t.lslot, t.ffree};
   for (void* p : ptrs)
     if (p) hipFree(p);
   t = TierDev{};
 }
+
+namespace {
+
+// Releases the prefill staging buffers (every prefill window has been placed
+// by the first routing event).  Synchronises once.
+hipError_t tier_release_staging(kvev_ctx* c) {
+  auto& t = c->td;
+  if (!t.kst) return hipSuccess;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return e;
+  for (uint16_t** p : {&t.kst, &t.vst, &t.kpst})
+    if (*p) {
+      hipFree(*p);
+      *p = nullptr;
+    }
+  c->tw.NWS = 0;
+  c->tw.stage_done = false;
+  return hipSuccess;
+}
+
+// The free full-precision slots 0 .. SF-1 of every layer, ascending, and
+// no window holding a slot or a record.
+hipError_t tier_reset_slots(kvev_ctx* c) {
+  auto& t = c->td;
+  const size_t L = c->cfg.n_layers, lw = L * c->tw.NW, SF = c->tw.SF;
+  std::vector<int> fr(L * SF);
+  for (size_t l = 0; l < L; ++l)
+    for (size_t i = 0; i < SF; ++i) fr[l * SF + i] = static_cast<int>(i);
+  hipError_t e = hipMemcpyAsync(t.ffree, fr.data(), fr.size() * sizeof(int), hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(t.fslot, 0xff, lw * sizeof(int), c->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(t.lslot, 0xff, lw * sizeof(int), c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);  // fr is a host buffer
+  c->tw.held = 0;
+  c->tw.opened = 0;
+  return e;
+}
+
+}  // namespace
 
 hipError_t tier_alloc(kvev_ctx* c) {
   const auto& f = c->cfg;
@@ -63,11 +102,31 @@ hipError_t tier_alloc(kvev_ctx* c) {
     if (e == hipSuccess && r != hipSuccess) e = r;
   };
   const size_t W = c->tw.W, recb = tier_rec_bytes(c->tw.W);
-  A(dalloc(&t.kfp, win * W * kTierD));
-  A(dalloc(&t.vfp, win * W * kTierD));
-  A(dalloc(&t.ledger, win * recb));
+  // Slot pools ("QEvict" review, section 4.1 (Budget), section 4.3 Eq.3):
+  // full-precision slots for the pinned windows, the local and not yet
+  // routed ones (the n_recent newest positions plus a routing interval of
+  // new tokens) and K_f routed windows (and the K_q INT2 windows when they
+  // are read through bf16 reconstructions); records for the K_f + K_q routed
+  // windows kept (a promoted window keeps its record for its next demotion).
+  {
+    const int Wi = c->tw.W, nwi = c->tw.NW;
+    const int np = f.n_sink > 0 ? (f.n_sink + Wi - 1) / Wi : 0;
+    const int omega = std::max(f.route_interval, 1);
+    const int64_t reserve = (static_cast<int64_t>(f.n_recent) + omega + Wi - 1) / Wi + 4;
+    const int64_t sf = np + reserve + f.fp_windows + (c->tw.mat ? static_cast<int64_t>(f.int2_windows) : 0);
+    const int64_t sq = static_cast<int64_t>(f.fp_windows) + f.int2_windows;
+    c->tw.SF = static_cast<int>(std::min<int64_t>(nwi, sf));
+    c->tw.SQ = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(nwi, sq)));
+  }
+  const size_t fpw = static_cast<size_t>(L) * H * c->tw.SF, qw = static_cast<size_t>(L) * H * c->tw.SQ;
+  A(dalloc(&t.kfp, fpw * W * kTierD));
+  A(dalloc(&t.vfp, fpw * W * kTierD));
+  A(dalloc(&t.ledger, qw * recb));
+  A(dalloc(&t.fslot, lw));
+  A(dalloc(&t.lslot, lw));
+  A(dalloc(&t.ffree, static_cast<size_t>(L) * c->tw.SF));
   if (c->tw.rope) {
-    A(dalloc(&t.kpre, win * W * kTierD));
+    A(dalloc(&t.kpre, fpw * W * kTierD));
     A(dalloc(&t.rcs, static_cast<size_t>(c->cap) * 64 * 2));
     A(dalloc(&t.ifreq, 64));
   }
@@ -101,14 +160,14 @@ hipError_t tier_alloc(kvev_ctx* c) {
     A(hipMemsetAsync(t.rd_acc, 0, L * 6 * sizeof(double), c->stream));
   }
   // zero the storage so that unwritten rows are finite
-  A(hipMemsetAsync(t.kfp, 0, win * W * kTierD * 2, c->stream));
-  A(hipMemsetAsync(t.vfp, 0, win * W * kTierD * 2, c->stream));
-  A(hipMemsetAsync(t.ledger, 0, win * recb, c->stream));
+  A(hipMemsetAsync(t.kfp, 0, fpw * W * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.vfp, 0, fpw * W * kTierD * 2, c->stream));
+  A(hipMemsetAsync(t.ledger, 0, qw * recb, c->stream));
   if (c->tw.rope) {
     // the rotary frequencies theta^(-2i/128), i < 64, in fp64 on the host
     double fr[64];
     for (int i = 0; i < 64; ++i) fr[i] = std::pow(static_cast<double>(f.rope_theta), -2.0 * i / 128.0);
-    A(hipMemsetAsync(t.kpre, 0, win * W * kTierD * 2, c->stream));
+    A(hipMemsetAsync(t.kpre, 0, fpw * W * kTierD * 2, c->stream));
     A(hipMemcpyAsync(t.ifreq, fr, sizeof(fr), hipMemcpyHostToDevice, c->stream));
   }
   A(hipMemsetAsync(t.tier, 0, lw, c->stream));
@@ -118,18 +177,35 @@ hipError_t tier_alloc(kvev_ctx* c) {
   // list entries past the live lengths stay valid window ids (0)
   A(hipMemsetAsync(t.fplist, 0, lw * sizeof(int), c->stream));
   A(hipMemsetAsync(t.qlist, 0, lw * sizeof(int), c->stream));
-  A(hipMemsetAsync(t.jobs, 0, lw * sizeof(int), c->stream));
+  A(hipMemsetAsync(t.jobs, 0, lw * sizeof(int4), c->stream));
   A(hipMemsetAsync(d.errflag, 0, sizeof(int), c->stream));
   A(hipStreamSynchronize(c->stream));
+  if (e == hipSuccess) e = tier_reset_slots(c);
   return e;
 }
 
 kvev_status tier_prefill(kvev_ctx* c, int seq, const void* k, const void* v, int64_t n) {
   if (seq != 0) return fail(c, KVEV_EINVAL, "tiered mode: the only sequence is 0");
   if (n < 1 || n + 1 > c->cap) return fail(c, KVEV_EINVAL, "n_tokens out of range for max_tokens");
+  auto& tw = c->tw;
+  // the prefill windows go to staging buffers until the first routing event
+  // places them (full precision into the pool, INT2 into records, or evicted)
+  KVEV_HIP(c, tier_release_staging(c));
+  KVEV_HIP(c, tier_reset_slots(c));
+  {
+    const int nwin = static_cast<int>((n + tw.W - 1) / tw.W);
+    const size_t sw = static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * nwin * tw.W * kTierD;
+    hipError_t e = dalloc(&c->td.kst, sw);
+    if (e == hipSuccess) e = dalloc(&c->td.vst, sw);
+    if (e == hipSuccess && tw.rope) e = dalloc(&c->td.kpst, sw);
+    if (e != hipSuccess) {
+      (void)tier_release_staging(c);
+      return fail(c, KVEV_ENOMEM, "out of device memory for the prefill staging buffers");
+    }
+    tw.NWS = nwin;
+  }
   if (c->tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, 0, n));
   KVEV_HIP(c, launch_tier_prefill(c, k, v, n));
-  auto& tw = c->tw;
   tw.npos = n;
   tw.n_fp = static_cast<int>((n + tw.W - 1) / tw.W);
   tw.n_q = 0;
@@ -145,12 +221,18 @@ kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const voi
   auto& tw = c->tw;
   if (tw.npos + 1 > c->cap) return fail(c, KVEV_ESTATE, "position capacity exhausted");
   const bool opens = tw.npos % tw.W == 0;
+  if (opens && tw.opened >= tw.SF - tw.held)
+    return fail(c, KVEV_ESTATE, "full-precision slot pool exhausted: route at least every route_interval steps");
+  if (tw.stage_done) KVEV_HIP(c, tier_release_staging(c));
   {
     ProfScope p(c, "append");
     if (tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, tw.npos, 1));
-    KVEV_HIP(c, launch_tier_append(c, k_new, v_new));
+    KVEV_HIP(c, launch_tier_append(c, k_new, v_new, opens ? tw.opened : 0));
   }
-  if (opens) tw.n_fp += 1;
+  if (opens) {
+    tw.n_fp += 1;
+    tw.opened += 1;
+  }
   tw.npos += 1;
   {
     ProfScope p(c, "attn");
@@ -174,10 +256,13 @@ kvev_status tier_route(kvev_ctx* c) {
   const int exp_fp = k.np + (k.nw - k.np - k.na) + nF;
   {
     ProfScope p(c, "route");
-    KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, exp_fp, nQ, nullptr));
+    KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, exp_fp, nQ, nullptr, -1));
   }
   tw.n_fp = exp_fp;
   tw.n_q = nQ;
+  tw.held = exp_fp + (tw.mat ? nQ : 0);
+  tw.opened = 0;
+  if (tw.NWS) tw.stage_done = true;
   tw.n_kept = nF + nQ;
   tw.na_prev = k.na;
   tw.events += 1;
@@ -263,14 +348,15 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
   if (!k_codes || !k_scale || !k_zero || !v_codes || !v_scale || !v_zero)
     return fail(c, KVEV_EINVAL, "null argument");
   uint8_t flag = 0;
+  int slot = -1;
   const int64_t lw = static_cast<int64_t>(layer) * c->tw.NW + w;
   std::vector<uint8_t> rec(recb);
-  const int64_t roff = ((static_cast<int64_t>(layer) * c->cfg.n_kv_heads + h) * c->tw.NW + w) * recb;
   KVEV_HIP(c, hipMemcpyAsync(&flag, c->td.hasled + lw, 1, hipMemcpyDeviceToHost, c->stream));
-  KVEV_HIP(c, hipMemcpyAsync(rec.data(), c->td.ledger + roff, recb, hipMemcpyDeviceToHost,
-                             c->stream));
+  KVEV_HIP(c, hipMemcpyAsync(&slot, c->td.lslot + lw, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   KVEV_HIP(c, hipStreamSynchronize(c->stream));
-  if (!flag) return fail(c, KVEV_EINVAL, "window has never been quantized");
+  if (!flag || slot < 0) return fail(c, KVEV_EINVAL, "window holds no INT2 record");
+  const int64_t roff = ((static_cast<int64_t>(layer) * c->cfg.n_kv_heads + h) * c->tw.SQ + slot) * recb;
+  KVEV_HIP(c, hipMemcpy(rec.data(), c->td.ledger + roff, recb, hipMemcpyDeviceToHost));
   if (W == 8) {
     // 8-token record: key / value codes [8][128] at 2 bits (element e at
     // byte e / 4, bits 2 (e % 4)), key scale / zero [128], value scale /
@@ -345,12 +431,33 @@ kvev_status kvev_tier_import(kvev_ctx* c, int32_t layer, int64_t n_windows, cons
   KVEV_HIP(c, hipMemcpyAsync(c->td.forced, c->td.tier, lw, hipMemcpyDeviceToDevice, c->stream));
   KVEV_HIP(c, hipMemcpyAsync(c->td.forced + off, tier, k.nw, hipMemcpyHostToDevice, c->stream));
   KVEV_HIP(c, hipMemcpyAsync(c->td.S + off, score, sizeof(float) * k.nw, hipMemcpyHostToDevice, c->stream));
-  KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, c->tw.n_fp, c->tw.n_q, c->td.forced));
+  KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, c->tw.n_fp, c->tw.n_q, c->td.forced, -1));
   KVEV_HIP(c, hipStreamSynchronize(c->stream));  // host buffers are the caller's
+  c->tw.held = c->tw.n_fp + (c->tw.mat ? c->tw.n_q : 0);
+  c->tw.opened = 0;
+  if (c->tw.NWS) c->tw.stage_done = true;
+  int flag = 0;
+  KVEV_HIP(c, hipMemcpy(&flag, c->d.errflag, sizeof(int), hipMemcpyDeviceToHost));
+  if (flag & 64) return fail(c, KVEV_ESTATE, "an evicted window cannot be kept: its storage is released");
   return KVEV_OK;
 }
 
 }  // extern "C"
+
+kvev_status kvev_tier_footprint(kvev_ctx* c, int64_t* fp_pool, int64_t* record_pool, int64_t* staging,
+                                int32_t* fp_slots, int32_t* record_slots) {
+  KVEV_LIVE(c);
+  if (!c->tier_mode) return fail(c, KVEV_EINVAL, "not in tiered mode");
+  const int64_t lh = static_cast<int64_t>(c->cfg.n_layers) * c->cfg.n_kv_heads;
+  const int64_t win = static_cast<int64_t>(c->tw.W) * kTierD * 2;  // bytes of one window's keys (or values)
+  const int64_t per = (c->tw.rope ? 3 : 2) * win;                 // keys, values, keys before the rotation
+  if (fp_pool) *fp_pool = lh * c->tw.SF * per;
+  if (record_pool) *record_pool = lh * c->tw.SQ * tier_rec_bytes(c->tw.W);
+  if (staging) *staging = lh * c->tw.NWS * per;
+  if (fp_slots) *fp_slots = c->tw.SF;
+  if (record_slots) *record_slots = c->tw.SQ;
+  return KVEV_OK;
+}
 
 kvev_status kvev_tier_capacities(double b_hist, double q, double m_f, double m_q, int32_t* k_f,
                                  int32_t* k_q) {

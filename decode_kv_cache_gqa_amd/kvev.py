@@ -127,6 +127,8 @@ _SIGS = {
     "kvev_tier_import": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                         ctypes.c_void_p]),
     "kvev_tier_capacities": (ctypes.c_int, [ctypes.c_double] * 4 + [ctypes.POINTER(ctypes.c_int32)] * 2),
+    "kvev_tier_footprint": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.POINTER(ctypes.c_int64)] * 3
+                            + [ctypes.POINTER(ctypes.c_int32)] * 2),
     "kvev_diag_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(DiagGroup), ctypes.c_int32]),
     "kvev_diag_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
@@ -398,6 +400,16 @@ class Context:
         args = [a.ctypes.data_as(ctypes.c_void_p) for a in (kc, ks, kz, vc, vs, vz)]
         self._check(lib().kvev_tier_ledger(self._h, layer, kv_head, window, *args))
         return kc, ks.view(np.float16), kz.view(np.float16), vc, vs.view(np.float16), vz.view(np.float16)
+
+    def tier_footprint(self):
+        """Device bytes held for windows: dict with fp_pool, record_pool,
+        staging (bytes) and fp_slots, record_slots (per layer and KV head)."""
+        a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        f, r = ctypes.c_int32(), ctypes.c_int32()
+        self._check(lib().kvev_tier_footprint(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                              ctypes.byref(f), ctypes.byref(r)))
+        return {"fp_pool": a.value, "record_pool": b.value, "staging": c.value,
+                "fp_slots": f.value, "record_slots": r.value}
 
     def tier_import(self, layer, score, tier):
         score = np.ascontiguousarray(score, dtype=np.float32)

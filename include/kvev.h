@@ -505,7 +505,8 @@ kvev_status kvev_tier_capacities(double b_hist, double q, double m_f, double m_q
 
 /* Copy the window state of `layer` (windows 0..*n_windows-1, window w =
  * positions [W w, W w + W), W = window_tokens) to host buffers: score, tier (0 full precision,
- * 1 INT2, 2 evicted), ledger flag (1 once quantized).  Any may be NULL.
+ * 1 INT2, 2 evicted), ledger flag (1 while the window holds an INT2 record:
+ * from its first demotion until its eviction).  Any may be NULL.
  * Synchronises.  Errors: KVEV_EINVAL (not tiered mode, bad layer),
  * KVEV_ERANGE (cap too small). */
 kvev_status kvev_tier_state(kvev_ctx* ctx, int32_t layer, float* score, uint8_t* tier,
@@ -513,9 +514,9 @@ kvev_status kvev_tier_state(kvev_ctx* ctx, int32_t layer, float* score, uint8_t*
 
 /* Copy the full-precision storage of (layer, kv_head) for windows
  * 0..nw-1 into device k_out, v_out, each [W * nw][128] bf16 by position
- * (keys rotated in rotary mode; rows of evicted windows and of INT2 windows
- * hold whatever the storage holds: the original values, the last
- * promotion's, or, with bf16 reconstruction, the reconstruction).  cap =
+ * (keys rotated in rotary mode; a window that holds no full-precision slot,
+ * evicted or INT2 without bf16 reconstruction, exports zeros; with bf16
+ * reconstruction an INT2 window exports its reconstruction).  cap =
  * rows the buffers hold; *n_rows = W * nw.  Stream-ordered.  Errors: KVEV_EINVAL,
  * KVEV_ERANGE. */
 kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void* k_out,
@@ -525,7 +526,7 @@ kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void
  * buffers: k_codes [W][128] (token, channel; keys before the rotation in
  * rotary mode), k_scale / k_zero [128] fp16 bits, v_codes [W][128],
  * v_scale / v_zero [W][4] fp16 bits (token, 32-channel group).  Synchronises.  Errors: KVEV_EINVAL (not tiered mode,
- * bad indices, window never quantized). */
+ * bad indices, the window holds no record). */
 kvev_status kvev_tier_ledger(kvev_ctx* ctx, int32_t layer, int32_t kv_head, int32_t window,
                              uint8_t* k_codes, uint16_t* k_scale, uint16_t* k_zero,
                              uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero);
@@ -555,10 +556,31 @@ kvev_status kvev_tier_diag(kvev_ctx* ctx, int32_t layer, kvev_route_diag* out);
  * event would apply it (quantize a window entering INT2 without a record,
  * write the reconstruction of a window promoted from INT2).  The tier
  * counts must equal the context's (pinned and local windows full
- * precision).  Used to put both sides of a comparison on the same state.
- * Errors: KVEV_EINVAL. */
+ * precision).  An evicted window has released its storage and stays
+ * evicted.  Used to put both sides of a comparison on the same state.
+ * Synchronises.  Errors: KVEV_EINVAL; KVEV_ESTATE (a tier would keep an
+ * evicted window). */
 kvev_status kvev_tier_import(kvev_ctx* ctx, int32_t layer, int64_t n_windows, const float* score,
                              const uint8_t* tier);
+
+/* Device memory a tiered context holds for windows ("QEvict" review,
+ * section 4.1 (Budget) and section 4.3 Eq.3), in bytes over all layers and
+ * KV heads: *fp_pool, the full-precision slot pool (keys and values, and
+ * the keys before the rotation in the rotary mode); *record_pool, the INT2
+ * record pool; *staging, the prefill staging buffers (the prefill windows
+ * until the first routing event places them; released by the next decode
+ * step).  Per (layer, KV head) the pool has *fp_slots window slots: the
+ * pinned windows, the windows not yet routed (the n_recent newest
+ * positions plus route_interval new tokens, plus four windows of slack),
+ * K_f routed ones, and with 8-token windows or the rotary mode also K_q
+ * (INT2 windows are then read through their bf16 reconstructions); and
+ * *record_slots records: K_f + K_q (a promoted window keeps its record for
+ * its next demotion).  A window releases its full-precision slot when it
+ * leaves full precision (INT2 without reconstruction, or evicted) and its
+ * record when it is evicted.  Any output may be null.  Errors: KVEV_EINVAL
+ * (not tiered mode). */
+kvev_status kvev_tier_footprint(kvev_ctx* ctx, int64_t* fp_pool, int64_t* record_pool, int64_t* staging,
+                                int32_t* fp_slots, int32_t* record_slots);
 
 /* Wait for all work queued on the context's stream; report a HIP error. */
 kvev_status kvev_sync(kvev_ctx* ctx);

@@ -198,6 +198,7 @@ def test_tier_entry_points_reject_null_context():
     assert L.kvev_tier_export(None, 0, 0, None, None, 0, None) == kvev.EINVAL
     assert L.kvev_tier_ledger(None, 0, 0, 0, None, None, None, None, None, None) == kvev.EINVAL
     assert L.kvev_tier_import(None, 0, 0, None, None) == kvev.EINVAL
+    assert L.kvev_tier_footprint(None, None, None, None, None, None) == kvev.EINVAL
 
 
 def test_block_entry_points_reject_null_context():

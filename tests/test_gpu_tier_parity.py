@@ -95,3 +95,47 @@ def test_tier_routing_diagnostics_interval_8_separate_calls():
                                                    int2_windows=7, epoch_steps=12, n_epochs=3)
     st = _gu().run_tier_lockstep(w, 36, fused=False, revival_gap=2)
     assert st.route_diag_checks == 2 * 4
+
+
+@pytest.mark.parametrize("name,W,rope", [("qevict131k", 32, False), ("qevict65k_w8_rope", 8, True)])
+def test_slot_pools_follow_the_byte_budget(name, W, rope):
+    """"QEvict" review, section 4.1 (Budget) and section 4.3 Eq.3: the
+    context's window memory is a full-precision pool of pinned + not yet
+    routed + K_f (+ K_q when INT2 windows are read through bf16
+    reconstructions) window slots and a pool of K_f + K_q records per
+    (layer, KV head); the prefill waits in staging buffers until the first
+    routing event places it, and the step after it releases them.  Checked
+    on the sizes the context reports, against the arithmetic, and in
+    lockstep with the oracle (the pools are reused: windows leave and enter
+    them every event)."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    gu = _gu()
+    w = synth.workload(name).scaled(n_layers=2, n_q_heads=8, n_kv_heads=2, prefill_lens=(2000,),
+                                    fp_windows=6, int2_windows=20, n_epochs=3, epoch_steps=12)
+    st = gu.run_tier_lockstep(w, 36)
+    assert st.steps == 36 and st.ledger_checks > 0
+    ctx = kvev.context_for(w, max_steps=12)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    fp = ctx.tier_footprint()
+    lh, d = w.n_layers * w.n_kv_heads, w.head_dim
+    nwin = -(-w.prefill_lens[0] // W)
+    per = (3 if rope else 2) * W * d * 2
+    np_ = -(-w.n_sink // W) if w.n_sink else 0
+    reserve = -(-(w.n_recent + max(w.route_interval, 1)) // W) + 4
+    mat = W == 8 or rope
+    sf = min(-(-(w.prefill_lens[0] + 13) // W), np_ + reserve + w.fp_windows + (w.int2_windows if mat else 0))
+    sq = max(1, w.fp_windows + w.int2_windows)
+    rec = 1152 if W == 8 else 3072
+    assert fp["fp_slots"] == sf and fp["record_slots"] == sq
+    assert fp["fp_pool"] == lh * sf * per and fp["record_pool"] == lh * sq * rec
+    assert fp["staging"] == lh * nwin * per
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, d), dtype=torch.float32, device="cuda")
+    for t in range(1, max(w.route_interval, 1) + 2):
+        ctx.step(*w.step_inputs(t, device="cuda"), out)
+    ctx.sync()
+    assert ctx.tier_footprint()["staging"] == 0
+    # far below holding every window in full precision
+    assert fp["fp_pool"] + fp["record_pool"] < lh * nwin * per / 2
+    ctx.close()
