@@ -959,6 +959,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   }
   for (int w = tid; w < nw; w += kRouteNT) {
     tl[w] = A.tier[lw0 + w];
+    act[w] = tl[w];  // the tier before the event, until the storage pass
     hl[w] = A.hasled[lw0 + w];
   }
   __syncthreads();
@@ -1008,7 +1009,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __syncthreads();
   int err = 0;
   for (int w = tid; w < nw; w += kRouteNT) {
-    const int o = A.tier[lw0 + w];
+    const int o = act[w];
     int t = tl[w];
     if (o == 2 && t != 2) {  // an evicted window's storage is gone
       err |= 64;
@@ -1088,7 +1089,8 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     const int w = tid * E + e;
     if (w >= nw) continue;
     const uint8_t a = act[w];
-    const int fold = A.fslot[lw0 + w];
+    const int kind = a >> 2;
+    const int fold = kind ? A.fslot[lw0 + w] : -1;  // the slot before the event (a job's source)
     int fnew = fs[w], qnew = qs[w];
     if (a & 1) {
       fnew = nth_bit(freeF, preF, nwf, tots[0], offF++);
@@ -1098,7 +1100,6 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
       qnew = nth_bit(freeQ, preQ, nwq, tots[1], offQ++);
       if (qnew < 0) err2 |= 128;
     }
-    const int kind = a >> 2;
     if (kind && !(err2 & 128)) {
       // (window << 2 | kind, source full-precision slot, full-precision slot
       // after the event, record slot)
