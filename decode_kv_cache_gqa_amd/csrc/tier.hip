@@ -950,6 +950,8 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __shared__ uint32_t freeF[kSlotWords], freeQ[kSlotWords];
   __shared__ int preF[kSlotWords], preQ[kSlotWords];
   __shared__ int ncand, njobs, wsum[kRouteNT / kWave], tots[4];
+  __shared__ int hist[2][256], rsel[2];  // the two threshold searches
+  __shared__ unsigned long long psel[2];
   __shared__ int dsum[6][kRouteNT / kWave];
   const int l = l0 + blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int64_t lw0 = static_cast<int64_t>(l) * A.NW;
@@ -973,23 +975,66 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     }
     __syncthreads();
     const int nc = ncand;
-    // exact rank of each candidate; keys are distinct (window ids).  Every
-    // lane of a wave reads the same key (an LDS broadcast); eight
-    // independent partial counts keep eight reads in flight.
-    for (int i = tid; i < nc; i += kRouteNT) {
-      const unsigned long long ki = keys[i];
-      int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      int j = 0;
-      for (; j + 8 <= nc; j += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) part[u] += keys[j + u] > ki;
+    // F: the k_f largest keys, Q: the next k_q, E: the rest.  The keys are
+    // distinct (window ids), so the two thresholds are the keys of rank
+    // k_f - 1 and k_f + k_q - 1 (from the top), found together by 8-bit
+    // radix passes from the top byte: each pass counts the keys that share
+    // the prefix found so far by their next byte, and one wave per
+    // threshold takes the byte whose bucket holds the rank.
+    const int nsel0 = k_f, nsel1 = k_f + k_q;
+    const bool act0 = nsel0 > 0 && nsel0 < nc, act1 = nsel1 > 0 && nsel1 < nc;
+    if (tid == 0) {
+      psel[0] = psel[1] = 0ull;
+      rsel[0] = nsel0 - 1;
+      rsel[1] = nsel1 - 1;
+    }
+    for (int pass = 0; pass < 8; ++pass) {
+      const int sh = 56 - 8 * pass;
+      for (int i = tid; i < 512; i += kRouteNT) (&hist[0][0])[i] = 0;
+      __syncthreads();
+      const unsigned long long hm = pass == 0 ? 0ull : (~0ull << (sh + 8));
+      const unsigned long long p0 = psel[0] & hm, p1 = psel[1] & hm;
+      for (int i = tid; i < nc; i += kRouteNT) {
+        const unsigned long long key = keys[i];
+        const int b = static_cast<int>((key >> sh) & 255u);
+        if (act0 && (key & hm) == p0) atomicAdd(&hist[0][b], 1);
+        if (act1 && (key & hm) == p1) atomicAdd(&hist[1][b], 1);
       }
-      for (; j < nc; ++j) part[0] += keys[j] > ki;
-      int rank = 0;
+      __syncthreads();
+      if (wv < 2 && (wv == 0 ? act0 : act1)) {
+        const int sx = wv;
+        int c[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) rank += part[u];
-      const int w = static_cast<int>(ki & 0xffffffffu);
-      tl[w] = rank < k_f ? 0 : (rank < k_f + k_q ? 1 : 2);
+        for (int u = 0; u < 4; ++u) c[u] = hist[sx][4 * lane + u];
+        const int tot = c[0] + c[1] + c[2] + c[3];
+        int x = tot;  // keys in buckets >= 4 lane (a suffix sum over the lanes)
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int y = __shfl_down(x, o, kWave);
+          if (lane + o < kWave) x += y;
+        }
+        const int r = rsel[sx];
+        int acc = x - tot;  // keys in buckets above the lane's four
+        if (acc <= r && r < x) {
+          for (int u = 3; u >= 0; --u) {
+            if (r < acc + c[u]) {
+              psel[sx] |= static_cast<unsigned long long>(4 * lane + u) << sh;
+              rsel[sx] = r - acc;
+              break;
+            }
+            acc += c[u];
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const unsigned long long t0 = psel[0], t1 = psel[1];
+    for (int i = tid; i < nc; i += kRouteNT) {
+      const unsigned long long key = keys[i];
+      const int w = static_cast<int>(key & 0xffffffffu);
+      const bool inF = nsel0 >= nc ? true : (nsel0 <= 0 ? false : key >= t0);
+      const bool inR = nsel1 >= nc ? true : (nsel1 <= 0 ? false : key >= t1);
+      tl[w] = inF ? 0 : (inR ? 1 : 2);
     }
   } else {
     for (int w = tid; w < nw; w += kRouteNT) tl[w] = forced[lw0 + w];
