@@ -26,7 +26,7 @@ constexpr int kTierLedgerBytes = 3072;  // INT2 record per (layer, KV head, wind
 constexpr int kTierMaxWin = 12288;      // windows per sequence (393216 positions at 32 tokens a window)
 constexpr int kTierLedgerBytes8 = 1152; // INT2 record of an 8-token window
 inline int tier_rec_bytes(int w) { return w == 8 ? kTierLedgerBytes8 : kTierLedgerBytes; }
-constexpr int kTierXferBlocks = 64;     // blocks per layer of the transition kernel
+constexpr int kTierXferBlocks = 512;    // blocks of the transition kernel (all layers)
 constexpr int kTierWinBits = 14;        // a list entry is slot << kTierWinBits | window
 // rank-trace diagnostics
 constexpr int kDiagCounts = 12;  // the int32 counts of kvev_diag_group, in order

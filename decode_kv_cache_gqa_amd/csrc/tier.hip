@@ -890,13 +890,14 @@ __global__ __launch_bounds__(256) void tier_mass_kernel(TierArgs A, int n_fp, in
 //   * a first demotion takes a record slot (quantize job, which also writes
 //     the bf16 reconstruction where INT2 windows are read through it); an
 //     evicted window releases its record.
-// New slots are the lowest free ones, given in window order; a slot released
-// by this event may be taken by it (the quantize jobs, which read released
-// slots, run before the promote and adopt jobs, which write new ones).  The
-// lists are rebuilt in window order with each entry's slot.  Errors (flag
-// bits): the list sizes differ from the host's (exp_fp, exp_q): 32; an
-// evicted window would be kept (its storage is gone): 64; a pool is
-// exhausted: 128.
+// New slots are given in window order: first the lowest slots free before
+// the event, then the lowest ones it released.  The transitions run in two
+// launches: phase 1 the quantize jobs (which read released slots) and the
+// jobs into slots free before the event, phase 2 the jobs into released
+// slots.  The lists are rebuilt in window order with each entry's slot.
+// Errors (flag bits): the list sizes differ from the host's (exp_fp,
+// exp_q): 32; an evicted window would be kept (its storage is gone): 64; a
+// pool is exhausted: 128.
 // ---------------------------------------------------------------------------
 constexpr int kRouteNT = 1024;
 constexpr int kSlotWords = kTierMaxWin / 32;  // bitmap words of a slot pool
@@ -947,8 +948,8 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __shared__ uint8_t tl[kTierMaxWin];               // tier after the event
   __shared__ uint8_t hl[kTierMaxWin];               // record held after the event
   __shared__ uint8_t act[kTierMaxWin];              // bit 0 new full-precision slot, bit 1 new record, bits 2.. job
-  __shared__ uint32_t freeF[kSlotWords], freeQ[kSlotWords];
-  __shared__ int preF[kSlotWords], preQ[kSlotWords];
+  __shared__ uint32_t freeF[kSlotWords], freeQ[kSlotWords], freshF[kSlotWords];
+  __shared__ int preF[kSlotWords], preQ[kSlotWords], preN[kSlotWords];
   __shared__ int ncand, njobs, wsum[kRouteNT / kWave], tots[4];
   __shared__ int hist[2][256], rsel[2];  // the two threshold searches
   __shared__ unsigned long long psel[2];
@@ -1046,10 +1047,14 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   for (int i = tid; i < kSlotWords; i += kRouteNT) {
     freeF[i] = 0xffffffffu;
     freeQ[i] = 0xffffffffu;
+    freshF[i] = 0xffffffffu;  // slots no window held before the event
   }
+  __syncthreads();
   for (int w = tid; w < nw; w += kRouteNT) {
-    fs[w] = A.fslot[lw0 + w];
+    const int f = A.fslot[lw0 + w];
+    fs[w] = f;
     qs[w] = A.lslot[lw0 + w];
+    if (f >= 0 && f < A.SF) atomicAnd(&freshF[f >> 5], ~(1u << (f & 31)));
   }
   __syncthreads();
   int err = 0;
@@ -1085,34 +1090,44 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __syncthreads();
   // free slots: prefix popcounts of the bitmaps (slots past the pool are not free)
   const int nwf = (A.SF + 31) / 32, nwq = (A.SQ + 31) / 32;
+  // free full-precision slots: fresh ones (free before the event) in freshF,
+  // the ones released by it in freeF; new slots come from the fresh ones
+  // first, so that their jobs need not wait for the reads of released slots
   for (int i = tid; i < kSlotWords; i += kRouteNT) {
     const int bf = A.SF - 32 * i, bq = A.SQ - 32 * i;
-    freeF[i] &= bf >= 32 ? 0xffffffffu : (bf <= 0 ? 0u : (1u << bf) - 1u);
+    const uint32_t mf = bf >= 32 ? 0xffffffffu : (bf <= 0 ? 0u : (1u << bf) - 1u);
+    const uint32_t fr = freeF[i] & mf;
+    freshF[i] &= fr;
+    freeF[i] = fr & ~freshF[i];
     freeQ[i] &= bq >= 32 ? 0xffffffffu : (bq <= 0 ? 0u : (1u << bq) - 1u);
   }
   __syncthreads();
-  if (tid < kWave) {  // one wave scans both bitmaps
-    int cf = 0, cq = 0;
+  if (tid < kWave) {  // one wave scans the three bitmaps
+    int cf = 0, cq = 0, cn = 0;
     for (int i0 = 0; i0 < kSlotWords; i0 += kWave) {
       const int i = i0 + lane;
-      int xf = __popc(freeF[i]), xq = __popc(freeQ[i]);
-      const int yf0 = xf, yq0 = xq;
+      int xf = __popc(freeF[i]), xq = __popc(freeQ[i]), xn = __popc(freshF[i]);
+      const int yf0 = xf, yq0 = xq, yn0 = xn;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
-        const int yf = __shfl_up(xf, o, kWave), yq = __shfl_up(xq, o, kWave);
+        const int yf = __shfl_up(xf, o, kWave), yq = __shfl_up(xq, o, kWave), yn = __shfl_up(xn, o, kWave);
         if (lane >= o) {
           xf += yf;
           xq += yq;
+          xn += yn;
         }
       }
       preF[i] = cf + xf - yf0;
       preQ[i] = cq + xq - yq0;
+      preN[i] = cn + xn - yn0;
       cf += __shfl(xf, kWave - 1, kWave);
       cq += __shfl(xq, kWave - 1, kWave);
+      cn += __shfl(xn, kWave - 1, kWave);
     }
     if (lane == 0) {
       tots[0] = cf;
       tots[1] = cq;
+      tots[2] = cn;
     }
   }
   __syncthreads();
@@ -1137,8 +1152,15 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
     const int kind = a >> 2;
     const int fold = kind ? A.fslot[lw0 + w] : -1;  // the slot before the event (a job's source)
     int fnew = fs[w], qnew = qs[w];
+    bool fresh = true;  // the job writes no slot released by this event
     if (a & 1) {
-      fnew = nth_bit(freeF, preF, nwf, tots[0], offF++);
+      const int r = offF++;
+      if (r < tots[2]) {
+        fnew = nth_bit(freshF, preN, nwf, tots[2], r);
+      } else {
+        fnew = nth_bit(freeF, preF, nwf, tots[0], r - tots[2]);
+        fresh = false;
+      }
       if (fnew < 0) err2 |= 128;
     }
     if (a & 2) {
@@ -1146,9 +1168,11 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
       if (qnew < 0) err2 |= 128;
     }
     if (kind && !(err2 & 128)) {
-      // (window << 2 | kind, source full-precision slot, full-precision slot
-      // after the event, record slot)
-      A.jobs[lw0 + atomicAdd(&njobs, 1)] = make_int4((w << 2) | kind, fold, fnew, qnew);
+      // (window << 3 | phase 2 << 2 | kind, source full-precision slot,
+      // full-precision slot after the event, record slot); a promote or
+      // adopt job into a released slot waits for phase 2
+      const int late = (kind != 1 && !fresh) ? 1 : 0;
+      A.jobs[lw0 + atomicAdd(&njobs, 1)] = make_int4((w << 3) | (late << 2) | kind, fold, fnew, qnew);
     }
     fs[w] = fnew;
     qs[w] = qnew;
@@ -1180,6 +1204,8 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   }
   // the free full-precision slots after the event, ascending (new windows
   // take them in order until the next event)
+  __syncthreads();
+  for (int i = tid; i < kSlotWords; i += kRouteNT) freeF[i] |= freshF[i];
   __syncthreads();
   for (int w = tid; w < nw; w += kRouteNT) {
     const int f = fs[w];
@@ -1311,24 +1337,48 @@ __device__ __forceinline__ uint8_t int2_code(float x, float sc, float zp) {
   return static_cast<uint8_t>(fminf(fmaxf(r, 0.f), 3.f));
 }
 
-__global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, int l0) {
+constexpr int kXferMaxLayers = 64;  // the library's layer bound
+
+__global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, int l0, int nl) {
   __shared__ float xk[W][D + 1];
   __shared__ float xv[W][D + 1];
   __shared__ uint8_t ck[W][D];
   __shared__ uint8_t cv[W][D];
   __shared__ uint32_t recl[kTierLedgerBytes / 4];
   __shared__ float ksc[D], kzp[D], vsc[W][4], vzp[W][4];  // the window's parameters as fp32
-  const int l = l0 + blockIdx.y, tid = threadIdx.x;
-  const int nj = A.njobs[l];
+  __shared__ int jpre[kXferMaxLayers + 1];  // (job, KV head) pairs of the layers before
+  const int tid = threadIdx.x;
   const int Wn = A.W;  // tokens per window (8 or 32)
-  // the layer's (job, KV head) pairs, strided over the blocks of the layer;
-  // phase 1 runs the quantize jobs, phase 2 the promote and adopt jobs
-  for (int p = blockIdx.x; p < nj * A.Hkv; p += gridDim.x) {
-    const int j = p / A.Hkv, h = p % A.Hkv;
+  if (tid < kWave) {  // exclusive prefix of the layers' pair counts
+    int c = tid < nl ? A.njobs[l0 + tid] * A.Hkv : 0;
+    const int c0 = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(c, o, kWave);
+      if (tid >= o) c += y;
+    }
+    jpre[tid] = c - c0;
+    if (tid == kWave - 1) jpre[kWave] = c;
+  }
+  __syncthreads();
+  const int total = jpre[nl];
+  // the (layer, job, KV head) triples of every layer, strided over the
+  // blocks; phase 1 runs the quantize jobs and the promote / adopt jobs into
+  // slots that were free before the event, phase 2 those into slots the
+  // event released (after phase 1 has read them)
+  for (int p = blockIdx.x; p < total; p += gridDim.x) {
+    int lo = 0, hi = nl - 1;  // the last layer whose pairs start at or before p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (jpre[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const int l = l0 + lo, pq = p - jpre[lo];
+    const int j = pq / A.Hkv, h = pq % A.Hkv;
     const int64_t lh = static_cast<int64_t>(l) * A.Hkv + h;
     const int4 job = A.jobs[static_cast<int64_t>(l) * A.NW + j];
-    const int w = job.x >> 2, kind = job.x & 3;
-    if ((kind == 1) != (phase == 1)) continue;  // block-uniform
+    const int w = job.x >> 3, kind = job.x & 3, late = (job.x >> 2) & 1;
+    if ((late ? 2 : 1) != phase) continue;  // block-uniform
     // every slot the job uses was given (the routing flags it otherwise)
     const bool ok = kind == 1 ? (job.y >= 0 && job.w >= 0 && (!A.mat || job.z >= 0))
                               : (kind == 2 ? (job.z >= 0 && job.w >= 0) : (job.y >= A.SF && job.z >= 0));
@@ -1653,11 +1703,11 @@ hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp
                                                    c->cfg.int2_windows, exp_fp, exp_q, forced_dev, l0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 gx(kTierXferBlocks, nl);
-  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a, 1, l0);  // quantize (reads released slots)
+  // one residency round of blocks over every layer's jobs
+  tier_xfer_kernel<<<kTierXferBlocks, 256, 0, c->stream>>>(a, 1, l0, nl);  // quantize, jobs into fresh slots
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  tier_xfer_kernel<<<gx, 256, 0, c->stream>>>(a, 2, l0);  // promote and adopt (write new slots)
+  tier_xfer_kernel<<<kTierXferBlocks, 256, 0, c->stream>>>(a, 2, l0, nl);  // jobs into released slots
   return hipGetLastError();
 }
 
