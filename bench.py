@@ -31,11 +31,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 # Every PROF_EVERY-th timed step is profiled (the per-kernel averages and the
-# roofline come from those launches).  The token path's attention and post
-# launches record their own dispatch start and end into HIP events
-# (hipExtLaunchKernelGGL); the other kernels are bracketed by event records,
-# each costing about 3.7 us of GPU time.  Sampling keeps the step time within
-# about 0.5% of an unprofiled run on the 32k workload.
+# roofline come from those launches).  The step's launches record their own
+# dispatch start and end into HIP events (hipExtLaunchKernelGGL), so no event
+# record runs between kernels; the vector attention of the fp32 / d = 64
+# path and the move, select and diagnostics launches are bracketed by event
+# records instead (each about 3.7 us of GPU time).  Sampling keeps the step
+# time within about 0.5% of an unprofiled run on the 32k workload.
 PROF_EVERY = 15  # coprime with the tiered routing interval 8, so routing steps are sampled too
 
 
@@ -377,7 +378,7 @@ def run_tier(args, w):
     torch.cuda.synchronize()
     first_ms = warm_up(ctx, inputs, out, args.warmup)
     dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
-    prof = {k: ctx.profile_read(k) for k in ("append", "attn", "merge", "route")}
+    prof = {k: ctx.profile_read(k) for k in ("rope", "append", "attn", "merge", "mass", "route", "xfer")}
     _, tiers, _ = ctx.tier_state(0)
     fp = ctx.tier_footprint()
     npos = w.prefill_lens[0] + total
@@ -391,7 +392,7 @@ def run_tier(args, w):
     attn_ms, attn_n = prof["attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
-    policy_ms = sum(prof[k][0] for k in ("merge", "route")) / n_prof
+    policy_ms = sum(prof[k][0] for k in ("merge", "mass", "route", "xfer")) / n_prof
     result = {
         "metric": "decode steps/s + KV-read GB/s (% HBM peak), incl. EMA/top-k/compaction",
         "value": round(args.steps / dt, 2), "unit": "steps/s", "n_gpus": 1, "steps": args.steps,

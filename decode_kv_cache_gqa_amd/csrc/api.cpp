@@ -610,7 +610,6 @@ static hipError_t offload_evicted(kvev_ctx* c, const std::vector<int>& ev) {
     if (hipError_t w = hipStreamWaitEvent(c->stream, c->pf_done, 0)) return w;
     c->pf_pending = false;
   }
-  ProfScope p(c, "offload");
   return launch_offload(c, kmax, E);
 }
 
@@ -632,27 +631,13 @@ static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, con
   const int64_t t = c->t + 1;
   c->lstride = (n_max + 15) / 16 * 16;
   const int nm = static_cast<int>(n_max);
-  {
-    ProfScope p(c, "open");
-    KVEV_HIP(c, launch_block_open(c, nm, static_cast<int>(t)));
-  }
-  {
-    ProfScope p(c, "attn");
-    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, nm, 1));
-  }
-  {
-    ProfScope p(c, "merge");
-    KVEV_HIP(c, launch_block_merge(c, out, nm));
-  }
-  {
-    ProfScope p(c, "mass");
-    KVEV_HIP(c, launch_block_mass(c, nm));
-  }
-  {
-    ProfScope p(c, "policy");
-    KVEV_HIP(c, launch_block_policy(c, static_cast<int>(t), 1, do_select ? 1 : 0, 1,
-                                    static_cast<int>(override_budget > 0 ? override_budget : 0)));
-  }
+  // every launch of the step times itself from its own dispatch (kvev_profile_*)
+  KVEV_HIP(c, launch_block_open(c, nm, static_cast<int>(t)));
+  KVEV_HIP(c, launch_attention(c, q, k_new, v_new, nm, 1, "attn"));
+  KVEV_HIP(c, launch_block_merge(c, out, nm));
+  KVEV_HIP(c, launch_block_mass(c, nm));
+  KVEV_HIP(c, launch_block_policy(c, static_cast<int>(t), 1, do_select ? 1 : 0, 1,
+                                  static_cast<int>(override_budget > 0 ? override_budget : 0)));
   if (c->cfg.offload_blocks > 0 && do_select) {
     std::vector<int> ev(Bsz, 0);
     for (int b = 0; b < Bsz; ++b) {
@@ -681,11 +666,8 @@ static kvev_status block_evict(kvev_ctx* c, int64_t override_budget) {
     any = any || c->nres[b] > Bs[b];
   }
   if (!any) return KVEV_OK;
-  {
-    ProfScope p(c, "policy");
-    KVEV_HIP(c, launch_block_policy(c, static_cast<int>(c->t), 0, 1, 0,
-                                    static_cast<int>(override_budget > 0 ? override_budget : 0)));
-  }
+  KVEV_HIP(c, launch_block_policy(c, static_cast<int>(c->t), 0, 1, 0,
+                                  static_cast<int>(override_budget > 0 ? override_budget : 0)));
   if (c->cfg.offload_blocks > 0) {
     std::vector<int> ev(Bsz, 0);
     for (int b = 0; b < Bsz; ++b) ev[b] = std::max(0, c->nres[b] - Bs[b]);

@@ -664,16 +664,14 @@ static BlockArgs block_args(kvev_ctx* c, float* out, int n_max) {
 hipError_t launch_block_open(kvev_ctx* c, int n_max, int t) {
   BlockArgs A = block_args(c, nullptr, n_max);
   A.t = t;
-  blk_open_kernel<<<c->cfg.batch, 64, 0, c->stream>>>(A, n_max);
-  return hipGetLastError();
+  return timed_launch(c, "open", blk_open_kernel, dim3(c->cfg.batch), dim3(64), 0, A, n_max);
 }
 
 hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max) {
   BlockArgs A = block_args(c, out, n_max);
   dim3 grid(c->cfg.n_layers, c->G);
   const size_t shm = (static_cast<size_t>(c->HG) * A.S * 3 + c->HG * 2) * sizeof(float);
-  blk_merge_kernel<256><<<grid, 256, shm, c->stream>>>(A);
-  return hipGetLastError();
+  return timed_launch(c, "merge", blk_merge_kernel<256>, grid, dim3(256), shm, A);
 }
 
 hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
@@ -681,13 +679,12 @@ hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
   if (c->d.bpart) {  // the attention wrote per-block sums
     dim3 grid((n_max + 4 * kPageTokens - 1) / (4 * kPageTokens), c->cfg.batch);
     const size_t shm = static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 4 * sizeof(float);
-    blk_mass_part_kernel<<<grid, 256, shm, c->stream>>>(A, c->d.bpart);
-    return hipGetLastError();
+    return timed_launch(c, "mass", blk_mass_part_kernel, grid, dim3(256), shm, A,
+                        static_cast<const float*>(c->d.bpart));
   }
   dim3 grid((n_max + 63) / 64, c->cfg.batch);
   const size_t shm = (static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 8 + 256) * sizeof(float);
-  blk_mass_kernel<<<grid, kMassNT, shm, c->stream>>>(A);
-  return hipGetLastError();
+  return timed_launch(c, "mass", blk_mass_kernel, grid, dim3(kMassNT), shm, A);
 }
 
 hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
@@ -695,20 +692,20 @@ hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, in
   BlockArgs A = block_args(c, nullptr, 1);
   A.t = t;
   const size_t shm = static_cast<size_t>(c->maxpages) * (8 + 4);
-  blk_policy_kernel<<<c->cfg.batch, kPolNT, shm, c->stream>>>(A, update, do_select, appended,
-                                                              budget_override);
-  return hipGetLastError();
+  return timed_launch(c, "policy", blk_policy_kernel, dim3(c->cfg.batch), dim3(kPolNT), shm, A, update, do_select,
+                      appended, budget_override);
 }
 
 hipError_t launch_offload(kvev_ctx* c, int k_max, int e_host) {
   BlockArgs A = block_args(c, nullptr, 1);
   const int64_t page_vec = static_cast<int64_t>(c->PT) * c->cfg.head_dim * c->elem / 16;
-  offload_slot_kernel<<<c->cfg.batch, 256, 0, c->stream>>>(A, c->d.ev_slot, c->cfg.offload_blocks, e_host);
+  hipError_t e = timed_launch(c, "offload", offload_slot_kernel, dim3(c->cfg.batch), dim3(256), 0, A, c->d.ev_slot,
+                              static_cast<int>(c->cfg.offload_blocks), e_host);
+  if (e != hipSuccess) return e;
   dim3 grid(k_max, c->cfg.batch, c->cfg.n_layers);
-  offload_copy_kernel<<<grid, 256, 0, c->stream>>>(A, c->d.ev_slot, static_cast<uint4*>(c->hpool_dev),
-                                                   static_cast<const uint4*>(c->d.kpool),
-                                                   static_cast<const uint4*>(c->d.vpool), page_vec, c->P);
-  return hipGetLastError();
+  return timed_launch(c, "offload", offload_copy_kernel, grid, dim3(256), 0, A, c->d.ev_slot,
+                      static_cast<uint4*>(c->hpool_dev), static_cast<const uint4*>(c->d.kpool),
+                      static_cast<const uint4*>(c->d.vpool), page_vec, c->P);
 }
 
 hipError_t launch_restore(kvev_ctx* c, int b, int n, int e0, const int* src_dev) {

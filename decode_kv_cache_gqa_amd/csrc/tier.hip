@@ -1640,8 +1640,9 @@ static void tier_chunk_windows(const kvev_ctx* c, int& cw_f, int& cw_q) {
 
 hipError_t launch_tier_rope_table(kvev_ctx* c, int64_t p0, int64_t n) {
   const int64_t threads = n * 64;
-  tier_rope_table_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, c->stream>>>(tier_args(c), p0, n);
-  return hipGetLastError();
+  // timed as "rope" on decode steps (one new position), untimed at prefill
+  return timed_launch(c, n == 1 ? "rope" : nullptr, tier_rope_table_kernel,
+                      dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, tier_args(c), p0, n);
 }
 
 hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_t n) {
@@ -1654,10 +1655,9 @@ hipError_t launch_tier_prefill(kvev_ctx* c, const void* k, const void* v, int64_
 
 hipError_t launch_tier_append(kvev_ctx* c, const void* k_new, const void* v_new, int kslot) {
   dim3 grid(c->cfg.n_kv_heads, c->cfg.n_layers);
-  tier_append_kernel<<<grid, D, 0, c->stream>>>(tier_args(c), static_cast<const uint16_t*>(k_new),
-                                                static_cast<const uint16_t*>(v_new),
-                                                static_cast<int>(c->tw.npos), c->tw.n_fp, kslot);
-  return hipGetLastError();
+  return timed_launch(c, "append", tier_append_kernel, grid, dim3(D), 0, tier_args(c),
+                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                      static_cast<int>(c->tw.npos), c->tw.n_fp, kslot);
 }
 
 hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
@@ -1669,13 +1669,9 @@ hipError_t launch_tier_attention(kvev_ctx* c, const void* q) {
   dim3 grid(nch_f + nch_q, c->cfg.n_kv_heads, c->cfg.n_layers);
   const auto* qq = static_cast<const uint16_t*>(q);
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
-  if (c->tw.W == 8)
-    tier_attn_kernel<8, true><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
-  else if (c->tw.mat)
-    tier_attn_kernel<32, true><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
-  else
-    tier_attn_kernel<32, false><<<grid, 256, 0, c->stream>>>(a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
-  return hipGetLastError();
+  auto kern = c->tw.W == 8 ? tier_attn_kernel<8, true>
+                            : (c->tw.mat ? tier_attn_kernel<32, true> : tier_attn_kernel<32, false>);
+  return timed_launch(c, "attn", kern, grid, dim3(256), 0, a, qq, c->tw.n_fp, c->tw.n_q, nch_f, npos, scale);
 }
 
 hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
@@ -1686,29 +1682,27 @@ hipError_t launch_tier_merge(kvev_ctx* c, float* out) {
   hipError_t e;
   dim3 gm(HG, c->cfg.n_kv_heads, c->cfg.n_layers);
   const size_t shm = sizeof(float) * 2 * static_cast<size_t>(nch_f + nch_q);
-  tier_merge_kernel<<<gm, 256, shm, c->stream>>>(a, out, nch_f + nch_q);
-  e = hipGetLastError();
+  e = timed_launch(c, "merge", tier_merge_kernel, gm, dim3(256), shm, a, out, nch_f + nch_q);
   if (e != hipSuccess) return e;
   const int ntot = c->tw.n_fp + c->tw.n_q;
   dim3 gs((ntot + 255) / 256, c->cfg.n_layers);
-  tier_mass_kernel<<<gs, 256, 0, c->stream>>>(a, c->tw.n_fp, c->tw.n_q, nch_f, cw_f, cw_q);
-  return hipGetLastError();
+  return timed_launch(c, "mass", tier_mass_kernel, gs, dim3(256), 0, a, c->tw.n_fp, c->tw.n_q, nch_f, cw_f, cw_q);
 }
 
 hipError_t launch_tier_route(kvev_ctx* c, int nw, int np, int recent_lo, int exp_fp, int exp_q,
                              const uint8_t* forced_dev, int layer) {
   TierArgs a = tier_args(c);
   const int l0 = layer < 0 ? 0 : layer, nl = layer < 0 ? c->cfg.n_layers : 1;
-  tier_route_kernel<<<nl, kRouteNT, 0, c->stream>>>(a, nw, np, recent_lo, c->cfg.fp_windows,
-                                                   c->cfg.int2_windows, exp_fp, exp_q, forced_dev, l0);
-  hipError_t e = hipGetLastError();
+  hipError_t e = timed_launch(c, "route", tier_route_kernel, dim3(nl), dim3(kRouteNT), 0, a, nw, np, recent_lo,
+                              static_cast<int>(c->cfg.fp_windows), static_cast<int>(c->cfg.int2_windows), exp_fp,
+                              exp_q, forced_dev, l0);
   if (e != hipSuccess) return e;
   // one residency round of blocks over every layer's jobs
-  tier_xfer_kernel<<<kTierXferBlocks, 256, 0, c->stream>>>(a, 1, l0, nl);  // quantize, jobs into fresh slots
-  e = hipGetLastError();
+  e = timed_launch(c, "xfer", tier_xfer_kernel, dim3(kTierXferBlocks), dim3(256), 0, a, 1, l0,
+                   nl);  // quantize, jobs into fresh slots
   if (e != hipSuccess) return e;
-  tier_xfer_kernel<<<kTierXferBlocks, 256, 0, c->stream>>>(a, 2, l0, nl);  // jobs into released slots
-  return hipGetLastError();
+  return timed_launch(c, "xfer", tier_xfer_kernel, dim3(kTierXferBlocks), dim3(256), 0, a, 2, l0,
+                      nl);  // jobs into released slots
 }
 
 hipError_t launch_tier_export(kvev_ctx* c, int l, int h, void* k_out, void* v_out, int nwin) {

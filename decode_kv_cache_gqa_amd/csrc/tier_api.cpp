@@ -224,24 +224,16 @@ kvev_status tier_decode(kvev_ctx* c, const void* q, const void* k_new, const voi
   if (opens && tw.opened >= tw.SF - tw.held)
     return fail(c, KVEV_ESTATE, "full-precision slot pool exhausted: route at least every route_interval steps");
   if (tw.stage_done) KVEV_HIP(c, tier_release_staging(c));
-  {
-    ProfScope p(c, "append");
-    if (tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, tw.npos, 1));
-    KVEV_HIP(c, launch_tier_append(c, k_new, v_new, opens ? tw.opened : 0));
-  }
+  // every launch of the step times itself from its own dispatch (kvev_profile_*)
+  if (tw.rope) KVEV_HIP(c, launch_tier_rope_table(c, tw.npos, 1));
+  KVEV_HIP(c, launch_tier_append(c, k_new, v_new, opens ? tw.opened : 0));
   if (opens) {
     tw.n_fp += 1;
     tw.opened += 1;
   }
   tw.npos += 1;
-  {
-    ProfScope p(c, "attn");
-    KVEV_HIP(c, launch_tier_attention(c, q));
-  }
-  {
-    ProfScope p(c, "merge");
-    KVEV_HIP(c, launch_tier_merge(c, out));
-  }
+  KVEV_HIP(c, launch_tier_attention(c, q));
+  KVEV_HIP(c, launch_tier_merge(c, out));
   c->t += 1;
   return KVEV_OK;
 }
@@ -254,10 +246,7 @@ kvev_status tier_route(kvev_ctx* c) {
   const int nF = std::min(c->cfg.fp_windows, cand);
   const int nQ = std::min(c->cfg.int2_windows, cand - nF);
   const int exp_fp = k.np + (k.nw - k.np - k.na) + nF;
-  {
-    ProfScope p(c, "route");
-    KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, exp_fp, nQ, nullptr, -1));
-  }
+  KVEV_HIP(c, launch_tier_route(c, k.nw, k.np, k.recent_lo, exp_fp, nQ, nullptr, -1));
   tw.n_fp = exp_fp;
   tw.n_q = nQ;
   tw.held = exp_fp + (tw.mat ? nQ : 0);
