@@ -1256,6 +1256,9 @@ class TieredOracle:
       (its first demotion); otherwise the stored codes are reused.  Keys
       are quantized per channel over the window's tokens, values per token
       in 32-channel groups ([QEvict] §4.4 Algorithm 1; ``int2_quantize``).
+      With ``key_groups="token32"`` the keys are grouped like the values,
+      per token and 32-channel group (the 131k workload's wording read
+      literally: a "per-32-channel-group" scale and zero for both).
     * A window promoted from Q to F gets its dequantized values rounded to
       bf16 as its full-precision storage.
     * Rotary mode (``rope_theta`` > 0; [QEvict] §4.4, "Positional handling
@@ -1291,6 +1294,7 @@ class TieredOracle:
     route_interval: int = 1
     rope_theta: float = 0.0
     reconstruct_bf16: bool = False
+    key_groups: str = "channel"
     layers: dict = field(default_factory=dict)
     npos: int = 0
     last_mass: dict = field(default_factory=dict)
@@ -1421,7 +1425,7 @@ class TieredOracle:
         src = st.Kpre if self.rope_theta > 0 else st.K     # keys before the rotation
         entry = []
         for h in range(self.n_kv_heads):
-            kc, ks, kz = int2_quantize(src[h, sl], "channel")
+            kc, ks, kz = int2_quantize(src[h, sl], self.key_groups)
             vc, vs, vz = int2_quantize(st.V[h, sl], "token32")
             entry.append((kc, ks, kz, vc, vs, vz))
         st.ledger[w] = entry
@@ -1430,7 +1434,7 @@ class TieredOracle:
         sl = slice(w * self.window, (w + 1) * self.window)
         pos = np.arange(w * self.window, (w + 1) * self.window)
         for h, (kc, ks, kz, vc, vs, vz) in enumerate(st.ledger[w]):
-            k = int2_dequantize(kc, ks, kz, "channel").astype(np.float64)
+            k = int2_dequantize(kc, ks, kz, self.key_groups).astype(np.float64)
             if self.rope_theta > 0:                  # re-rotated at the original positions
                 k = rope(k, pos, self.rope_theta)
             v = int2_dequantize(vc, vs, vz, "token32")

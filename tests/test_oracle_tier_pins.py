@@ -354,3 +354,47 @@ def test_held_memory_stays_within_the_byte_budget():
 
     _run(o, q, kn, vn, check)
     assert dropped, "some quantized window should be evicted (and lose its record)"
+
+
+def test_key_groups_per_token_and_32_channels():
+    """The literal reading of the 131k workload's "per-32-channel-group"
+    scale and zero for keys as well (key_groups="token32"): a quantized
+    window's key parameters are one (scale, zero) per (token, 32-channel
+    group), and keys that each such group represents exactly (every row
+    of a group holds z + j*s, j in 0..3 with 0 and 3 present, z and s
+    dyadic) come back exactly from the reconstruction, while a per-channel
+    grouping of the same keys does not."""
+    rng = np.random.default_rng(29)
+    L, Hq, Hkv, d, W, n, T = 1, 8, 2, 64, 8, 160, 12
+    K = np.zeros((L, Hkv, n, d), np.float32)
+    for h in range(Hkv):
+        for t in range(n):
+            for g in range(d // 32):
+                z = rng.integers(-16, 16) / 8.0
+                s = rng.integers(1, 8) / 16.0
+                j = rng.integers(0, 4, 32)
+                j[0], j[1] = 0, 3
+                K[0, h, t, 32 * g:32 * g + 32] = z + j * s
+    V = rng.standard_normal((L, Hkv, n, d)).astype(np.float32)
+    q = rng.standard_normal((T, L, Hq, d)).astype(np.float32)
+    kn = rng.standard_normal((T, L, Hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((T, L, Hkv, d)).astype(np.float32)
+    o = orc.TieredOracle(L, Hq, Hkv, d, k_f=2, k_q=8, window=W, n_sink=2, n_recent=8, key_groups="token32")
+    o.prefill(K, V)
+    _run(o, q, kn, vn)
+    st = o.layers[0]
+    assert st.ledger
+    for w, entry in st.ledger.items():
+        sl = slice(w * W, (w + 1) * W)
+        for h, (kc, ks, kz, vc, vs, vz) in enumerate(entry):
+            assert np.shape(ks) == (W, d // 32) and np.shape(kz) == (W, d // 32)
+            # the reconstruction written out: code * scale + zero of the (token, group)
+            khat = np.empty((W, d), np.float32)
+            for t in range(W):
+                for c in range(d):
+                    khat[t, c] = np.float32(np.float32(kc[t, c]) * np.float32(ks[t, c // 32])) + np.float32(kz[t, c // 32])
+            if w * W + W <= n:  # a prefill window: the grid keys come back exactly
+                np.testing.assert_array_equal(khat, K[0, h, sl])
+                c2, s2, z2 = orc.int2_quantize(K[0, h, sl], "channel")
+                per_channel = orc.int2_dequantize(c2, s2, z2, "channel")
+                assert not np.array_equal(per_channel, K[0, h, sl])
