@@ -109,7 +109,8 @@ static kvev_status tier_create(const kvev_config& f, void* hip_stream, kvev_ctx*
   c->tier_mode = true;
   c->tw.W = f.window_tokens;
   c->tw.rope = f.rope_theta > 0.f;
-  c->tw.mat = c->tw.W == 8 || c->tw.rope;
+  c->tw.kgroups = f.int2_key_groups == 1;
+  c->tw.mat = c->tw.W == 8 || c->tw.rope || c->tw.kgroups;
   c->tw.NW = static_cast<int>((c->cap + c->tw.W - 1) / c->tw.W);
   c->tw.maxch = 2 * ((c->tw.NW + 7) / 8);
   const hipError_t e = tier_alloc(c);
@@ -174,6 +175,9 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (!std::isfinite(f.offload_min_score)) return bad("offload_min_score must be finite");
   if (f.attn_path < KVEV_ATTN_AUTO || f.attn_path > KVEV_ATTN_WHOLE) return bad("unknown attn_path");
   if (f.rope_theta != 0.f && f.policy != KVEV_TIERED_INT2) return bad("rope_theta applies to the tiered mode only");
+  if (f.int2_key_groups != 0 && f.policy != KVEV_TIERED_INT2)
+    return bad("int2_key_groups applies to the tiered mode only");
+  if (f.int2_key_groups != 0 && f.int2_key_groups != 1) return bad("int2_key_groups must be 0 or 1");
   if (f.evict_interval < 0) return bad("evict_interval must be >= 0");
   if (f.evict_interval > 1 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("evict_interval applies to the token policies only");

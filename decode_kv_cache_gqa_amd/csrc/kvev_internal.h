@@ -143,7 +143,8 @@ struct TierHost {
   int W = 32;          // tokens per window
   bool rope = false;   // rotary mode (cfg.rope_theta > 0)
   bool mat = false;    // INT2 windows are attended through their bf16 reconstruction, kept in the
-                       // full-precision storage (8-token windows or rotary mode)
+                       // full-precision storage (8-token windows, rotary mode or key groups)
+  bool kgroups = false;  // keys quantized per token and 32-channel group
   int64_t npos = 0;  // positions 0 .. npos-1 exist
   int n_fp = 0;      // full-precision windows listed (pinned + local + routed F)
   int n_q = 0;       // INT2 windows listed
@@ -187,6 +188,7 @@ struct TierArgs {
   int* lslot;
   int* ffree;
   int SF, SQ, NWS;
+  int kgroups;  // keys quantized per token and 32-channel group (else per channel)
 };
 
 struct Profiler {

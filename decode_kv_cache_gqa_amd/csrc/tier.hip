@@ -1433,7 +1433,7 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, i
         }
       }
       __syncthreads();
-      if (tid < D) {  // keys: one channel over the window's tokens
+      if (tid < D && !A.kgroups) {  // keys: one channel over the window's tokens
         const int c = tid;
         float sc, zp;
         uint16_t s16, z16;
@@ -1443,6 +1443,20 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, i
         ksc[c] = sc;
         kzp[c] = zp;
         for (int r = 0; r < Wn; ++r) ck[r][c] = int2_code(xk[r][c], sc, zp);
+      } else if (tid < D) {
+        // keys grouped like the values: one token's 32-channel group,
+        // parameters stored [group][token] and kept as ksc[token * 4 + group]
+        if (tid / 4 < Wn) {
+          const int r = tid / 4, g = tid % 4;
+          float sc, zp;
+          uint16_t s16, z16;
+          int2_group(&xk[r][32 * g], 32, 1, sc, zp, s16, z16);
+          rec16[(Wn == 8 ? kRec8SK / 2 + 8 * g : kRecSK / 2 + 32 * g) + r] = s16;
+          rec16[(Wn == 8 ? kRec8ZK / 2 + 8 * g : kRecZK / 2 + 32 * g) + r] = z16;
+          ksc[4 * r + g] = sc;
+          kzp[4 * r + g] = zp;
+          for (int c = 32 * g; c < 32 * g + 32; ++c) ck[r][c] = int2_code(xk[r][c], sc, zp);
+        }
       } else if ((tid - D) / 4 < Wn) {  // values: one token's 32-channel group
         const int r = (tid - D) / 4, g = (tid - D) % 4;
         float sc, zp;
@@ -1495,10 +1509,11 @@ __global__ __launch_bounds__(256) void tier_xfer_kernel(TierArgs A, int phase, i
           for (int e = 0; e < 8; ++e) {
             const int i = i0 + e;
             const int r = i / D, c = i % D;  // key element (token r, channel c)
-            float kx = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][c]), ksc[c]), kzp[c]);
+            const int pk = A.kgroups ? 4 * r + (c >> 5) : c;  // the key element's parameters
+            float kx = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][c]), ksc[pk]), kzp[pk]);
             if (A.rope) {
-              const int cp = c ^ 64;
-              const float ky = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][cp]), ksc[cp]), kzp[cp]);
+              const int cp = c ^ 64, pp = A.kgroups ? 4 * r + (cp >> 5) : cp;
+              const float ky = __fadd_rn(__fmul_rn(static_cast<float>(ck[r][cp]), ksc[pp]), kzp[pp]);
               kx = rope_elem(kx, ky, c, A.rcs + static_cast<int64_t>(w * Wn + r) * 128);
             }
             const int vc = i / Wn, vr_ = i % Wn;  // value element (channel vc, token vr_)
@@ -1629,6 +1644,7 @@ static TierArgs tier_args(kvev_ctx* c) {
   a.SF = c->tw.SF;
   a.SQ = c->tw.SQ;
   a.NWS = c->tw.NWS;
+  a.kgroups = c->tw.kgroups ? 1 : 0;
   return a;
 }
 

@@ -325,6 +325,25 @@ kvev_status kvev_tier_export(kvev_ctx* c, int32_t layer, int32_t h, void* k_out,
   return KVEV_OK;
 }
 
+// The key parameters of a record: per channel [128], or with key groups
+// stored [group][W] and exported [W][group].
+static void tier_key_params(const kvev_ctx* c, const uint8_t* s_src, const uint8_t* z_src, int W,
+                            uint16_t* k_scale, uint16_t* k_zero) {
+  if (!c->tw.kgroups) {
+    std::memcpy(k_scale, s_src, 256);
+    std::memcpy(k_zero, z_src, 256);
+    return;
+  }
+  uint16_t s[4 * kTierWin], z[4 * kTierWin];
+  std::memcpy(s, s_src, 8 * W);
+  std::memcpy(z, z_src, 8 * W);
+  for (int r = 0; r < W; ++r)
+    for (int g = 0; g < 4; ++g) {
+      k_scale[r * 4 + g] = s[g * W + r];
+      k_zero[r * 4 + g] = z[g * W + r];
+    }
+}
+
 kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, uint8_t* k_codes,
                              uint16_t* k_scale, uint16_t* k_zero, uint8_t* v_codes, uint16_t* v_scale,
                              uint16_t* v_zero) {
@@ -354,8 +373,7 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
       k_codes[e] = static_cast<uint8_t>((rec[e / 4] >> (2 * (e % 4))) & 3);
       v_codes[e] = static_cast<uint8_t>((rec[256 + e / 4] >> (2 * (e % 4))) & 3);
     }
-    std::memcpy(k_scale, rec.data() + 512, 256);
-    std::memcpy(k_zero, rec.data() + 768, 256);
+    tier_key_params(c, rec.data() + 512, rec.data() + 768, 8, k_scale, k_zero);
     uint16_t vs8[4][8], vz8[4][8];
     std::memcpy(vs8, rec.data() + 1024, 64);
     std::memcpy(vz8, rec.data() + 1088, 64);
@@ -382,8 +400,7 @@ kvev_status kvev_tier_ledger(kvev_ctx* c, int32_t layer, int32_t h, int32_t w, u
       v_codes[r * kTierD + ch] =
           static_cast<uint8_t>((words[1][((r >> 4) * 16 + (ch & 15)) * 8 + (ch >> 4)] >> bit(r & 15)) & 3u);
     }
-  std::memcpy(k_scale, rec.data() + 2048, 256);
-  std::memcpy(k_zero, rec.data() + 2304, 256);
+  tier_key_params(c, rec.data() + 2048, rec.data() + 2304, kTierWin, k_scale, k_zero);
   // value scales and zero points are stored [group][token]; the export is [token][group]
   uint16_t vs[4][kTierWin], vz[4][kTierWin];
   std::memcpy(vs, rec.data() + 2560, 256);

@@ -59,6 +59,7 @@ class Config(ctypes.Structure):
         ("attn_path", ctypes.c_int32),
         ("evict_interval", ctypes.c_int32),
         ("rope_theta", ctypes.c_float),
+        ("int2_key_groups", ctypes.c_int32),
     ]
 
 
@@ -389,16 +390,20 @@ class Context:
 
     def tier_ledger(self, layer, kv_head, window):
         """INT2 record: (k_codes [W,128], k_scale [128], k_zero [128], v_codes [W,128],
-        v_scale [W,4], v_zero [W,4]); parameters as float16."""
+        v_scale [W,4], v_zero [W,4]); parameters as float16.  With key groups
+        the key parameters are [W,4] like the values'."""
         W = self.cfg.window_tokens
         kc = np.zeros((W, self.cfg.head_dim), np.uint8)
         vc = np.zeros_like(kc)
-        ks = np.zeros(128, np.uint16)
+        kshape = (W, 4) if self.cfg.int2_key_groups else (128,)
+        ks = np.zeros(128, np.uint16)  # the C call writes at most 128 parameters
         kz = np.zeros(128, np.uint16)
         vs = np.zeros((W, 4), np.uint16)
         vz = np.zeros((W, 4), np.uint16)
         args = [a.ctypes.data_as(ctypes.c_void_p) for a in (kc, ks, kz, vc, vs, vz)]
         self._check(lib().kvev_tier_ledger(self._h, layer, kv_head, window, *args))
+        n = int(np.prod(kshape))
+        ks, kz = ks[:n].reshape(kshape), kz[:n].reshape(kshape)
         return kc, ks.view(np.float16), kz.view(np.float16), vc, vs.view(np.float16), vz.view(np.float16)
 
     def tier_footprint(self):
@@ -533,7 +538,8 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             max_tokens=max(w.prefill_lens) + steps + 1, page_tokens=16, policy=TIERED_INT2,
             n_sink=w.n_sink, n_recent=w.n_recent, budget=1, window_tokens=w.window_tokens,
             fp_windows=w.fp_windows, int2_windows=w.int2_windows, route_interval=w.route_interval,
-            revival_gap=w.revival_gap if revival_gap is None else revival_gap, rope_theta=w.rope_theta)
+            revival_gap=w.revival_gap if revival_gap is None else revival_gap, rope_theta=w.rope_theta,
+            int2_key_groups=w.int2_key_groups)
         return Context(cfg, stream=stream)
     cfg = make_config(
         n_layers=w.n_layers, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,

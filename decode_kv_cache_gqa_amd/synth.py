@@ -161,6 +161,7 @@ class Workload:
     attn_path: int = 0              # token modes: attention kernel (0 auto, 1 split, 2 whole-cache)
     evict_interval: int = 1         # token modes: select only every evict_interval steps
     rope_theta: float = 0.0         # tiered mode: keys and queries arrive before the rotary embedding
+    int2_key_groups: int = 0        # tiered mode: 1 = keys quantized per token and 32-channel group
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property

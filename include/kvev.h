@@ -233,6 +233,15 @@ typedef struct {
    * written into its full-precision storage at its first demotion (so a
    * promotion leaves that storage as it is). */
   float rope_theta;
+  /* KVEV_TIERED_INT2 only (0 otherwise): how the INT2 quantizer groups the
+   * keys.  0: one scale and zero per channel over the window's tokens (the
+   * "QEvict" review, section 4.4 Algorithm 1).  1: one per token and
+   * 32-channel group, like the values (the 131k workload's
+   * "per-32-channel-group" wording read for keys too).  With 1 an INT2
+   * window is attended through its reconstruction rounded to bf16, kept in
+   * its full-precision slot (as with rope_theta > 0), and kvev_tier_ledger
+   * returns the key parameters as [W][4] (token, group). */
+  int32_t int2_key_groups;
 } kvev_config;
 
 typedef enum { KVEV_ATTN_AUTO = 0, KVEV_ATTN_SPLIT = 1, KVEV_ATTN_WHOLE = 2 } kvev_attn_path;
@@ -524,7 +533,8 @@ kvev_status kvev_tier_export(kvev_ctx* ctx, int32_t layer, int32_t kv_head, void
 
 /* Copy and unpack the INT2 record of (layer, kv_head, window) to host
  * buffers: k_codes [W][128] (token, channel; keys before the rotation in
- * rotary mode), k_scale / k_zero [128] fp16 bits, v_codes [W][128],
+ * rotary mode), k_scale / k_zero [128] fp16 bits (with int2_key_groups:
+ * [W][4], token and 32-channel group), v_codes [W][128],
  * v_scale / v_zero [W][4] fp16 bits (token, 32-channel group).  Synchronises.  Errors: KVEV_EINVAL (not tiered mode,
  * bad indices, the window holds no record). */
 kvev_status kvev_tier_ledger(kvev_ctx* ctx, int32_t layer, int32_t kv_head, int32_t window,

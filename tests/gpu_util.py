@@ -897,14 +897,17 @@ def run_tier_lockstep(w, steps, *, sample_layers=None, rtol=2e-3, device="cuda",
     t_start = time.time()
     ctx = kvev.context_for(w, max_steps=steps, revival_gap=revival_gap)
     rdiag = {l: orc.RoutingDiagnostics(revival_gap) for l in layers} if revival_gap else None
-    # 8-token windows and the rotary mode read INT2 windows through their bf16
-    # reconstruction, kept in the full-precision storage
-    mat = w.window_tokens == 8 or w.rope_theta > 0
+    # 8-token windows, the rotary mode and per-token key groups read INT2
+    # windows through their bf16 reconstruction, kept in the full-precision
+    # storage
+    mat = w.window_tokens == 8 or w.rope_theta > 0 or w.int2_key_groups == 1
     orcs = {l: orc.TieredOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, k_f=w.fp_windows,
                                 k_q=w.int2_windows, window=w.window_tokens, n_sink=w.n_sink,
                                 n_recent=w.n_recent, capacity=w.prefill_lens[0] + steps + 1,
                                 route_interval=w.route_interval, rope_theta=w.rope_theta,
-                                reconstruct_bf16=mat) for l in layers}
+                                reconstruct_bf16=mat,
+                                key_groups="token32" if w.int2_key_groups == 1 else "channel")
+            for l in layers}
     W = w.window_tokens
     K, V = w.prefill_kv(0, device=device)
     ctx.prefill(0, K.contiguous(), V.contiguous())

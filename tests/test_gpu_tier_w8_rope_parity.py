@@ -69,3 +69,15 @@ def test_w8_rope_max_windows_sampled():
     w = _scaled(prefill_lens=(98290,), fp_windows=300, int2_windows=2000)
     st = _gu().run_tier_lockstep(w, 4, sample_layers=[1], kv_every=4, ledger_every=4)
     assert st.steps == 4
+
+
+@pytest.mark.parametrize("W,theta", [(32, 0.0), (8, 500000.0)])
+def test_keys_grouped_per_token(W, theta):
+    """int2_key_groups = 1: keys quantized per token and 32-channel group
+    (the 131k workload's wording read for keys too), with 32-token windows
+    and with the rotary 8-token mode: ledger records (key parameters [W,4]),
+    bf16 reconstructions, tiers, scores and outputs in lockstep."""
+    w = _scaled(n_layers=2, prefill_lens=(1200,), window_tokens=W, rope_theta=theta, int2_key_groups=1,
+                fp_windows=5 if W == 32 else 20, int2_windows=12 if W == 32 else 48, route_interval=1)
+    st = _gu().run_tier_lockstep(w, 24, ledger_every=4)
+    assert st.steps == 24 and st.ledger_checks > 0
