@@ -17,26 +17,32 @@
 // again at their original positions when reconstructed (section 4.4,
 // positional handling for promoted keys).
 //
-// Layout, per (layer l, KV head h) and window w (positions [Ww, Ww+W)):
-//   kfp    [L][Hkv][NW][W][128] bf16  keys, token-major (rotated in the
-//          rotary mode)
-//   vfp    [L][Hkv][NW][128][W] bf16  values, channel-major (a channel's W
+// Storage, per (layer l, KV head h), in two slot pools sized from the byte
+// budget (section 4.1 (Budget), section 4.3 Eq.3): a window holds only the
+// slots its tier needs, and the per-layer slot maps fslot / lslot name them.
+//   kfp    [L][Hkv][SF][W][128] bf16  full-precision keys, token-major
+//          (rotated in the rotary mode)
+//   vfp    [L][Hkv][SF][128][W] bf16  values, channel-major (a channel's W
 //          tokens are contiguous: the p.V operand of the matrix cores)
-//   kpre   [L][Hkv][NW][W][128] bf16  rotary mode only: the keys as given,
+//   kpre   [L][Hkv][SF][W][128] bf16  rotary mode only: the keys as given,
 //          read by a window's first quantization
-//   ledger [L][Hkv][NW][record]  INT2 record; for W = 32 (3,072 B):
+//   ledger [L][Hkv][SQ][record]  INT2 records; for W = 32 (3,072 B):
 //     [0, 1024)     key codes, 16 B per lane of a wave (see below)
 //     [1024, 2048)  value codes, 16 B per lane
-//     [2048, 2304)  key scale per channel, fp16 [128]
-//     [2304, 2560)  key zero point per channel, fp16 [128]
+//     [2048, 2304)  key scale per channel, fp16 [128] (with key groups:
+//                   per (32-channel group, token), [4][W])
+//     [2304, 2560)  key zero point, laid out as the scales
 //     [2560, 2816)  value scale per (32-channel group, token), fp16 [4][32]
 //     [2816, 3072)  value zero point, fp16 [4][32]
 //   and for W = 8 (1,152 B) the kRec8* offsets below.
-// Full-precision storage is never released: a demoted window keeps it, so a
-// promotion only rewrites it and nothing moves when tiers change.  With
-// W = 8 or the rotary mode an INT2 window's storage holds its reconstruction
-// rounded to bf16 (written at its first demotion), and the attention reads
-// every listed window from full-precision storage.
+// SF covers the pinned windows, the windows not yet routed and K_f routed
+// ones (and the K_q INT2 windows where they are read through bf16
+// reconstructions: 8-token windows, the rotary mode or key groups); SQ =
+// K_f + K_q.  A window releases its full-precision slot when it leaves full
+// precision and its record when it is evicted; a promotion takes a new slot
+// and writes the reconstruction into it.  The prefill windows wait in
+// staging buffers of the same layout (slot SF + w) until the first routing
+// event places them.
 //
 // Code records (32-token windows).  The attention multiplies the 2-bit
 // codes as int8 B operands of v_mfma_i32_16x16x64_i8; a 32-bit word holds
@@ -333,23 +339,25 @@ __global__ __launch_bounds__(128) void tier_append_kernel(TierArgs A, const uint
 // ---------------------------------------------------------------------------
 // Attention over the accessible windows of (layer l, KV head h).  Block
 // (chunk, h, l) of 4 waves; a wave takes 64 tokens of the full-precision
-// list (2 windows of 32 or 8 of 8) or kQW = 4 windows of the INT2 list
-// (the fused INT2 path: a chunk 16).
-// Chunks [0, nch_f) cover the full-precision list, the rest the INT2 list.  Writes the chunk's (max, sum) and unnormalised
-// output per head, and per window and head the sum of exp(s - chunk max)
-// over the window's tokens (its attention mass before normalisation).
-//   q.K: A = the 4 query rows, B = K^T (n-tiles of 16 tokens, k-steps of 32
-//     channels).  INT2: logit = sum_c (q_c s_c) code_c + sum_c q_c z_c, with
-//     q s split into bf16 high (rows 0..3) and low (rows 4..7) parts.
-//   p.V: A = P (high / low rows), B = V (a k-step is one window).  INT2:
-//     out_c = sum_t (p_t s_tg) code_tc + sum_t p_t z_tg, g = c / 32.
+// list (2 windows of 32 or 8 of 8) or kQW = 4 windows of the INT2 list (the
+// INT2 path: 16 windows a chunk).  Chunks [0, nch_f) cover the
+// full-precision list, the rest the INT2 list; each list entry names the
+// window and the slot its storage is read from.  Writes the chunk's (max,
+// sum) and unnormalised output per head, and per window and head the sum of
+// exp(s - chunk max) over the window's tokens (its attention mass before
+// normalisation).
+//   Full precision, bf16 matrix cores: q.K with A = the 4 query rows, B = K^T
+//     (n-tiles of 16 tokens, k-steps of 32 channels); p.V with A = P (bf16
+//     high / low rows), B = V (a k-step is 32 tokens).
+//   INT2, int8 matrix cores: logit = sum_c (q_c s_c) code_c + sum_c q_c z_c
+//     and out_c = sum_t (p_t s_tg) code_tc + sum_t p_t z_tg (g = c / 32),
+//     the scaled operands as fixed-point digit rows, the codes as B.
 // ---------------------------------------------------------------------------
-// Three waves per SIMD: the INT2 windows are bound by vector arithmetic and
-// memory latency, and the register cap this sets (168) costs no spills.
+// Three waves per SIMD: the register cap this sets (168) costs no spills.
 // WT: tokens per window (32 or 8).  MAT: INT2 windows are read from their
-// bf16 reconstruction in the full-precision storage (8-token windows,
-// rotary mode), so every window takes the full-precision path; in rotary
-// mode the queries are rotated at the new token's position npos - 1.
+// bf16 reconstruction in the full-precision pool (8-token windows, rotary
+// mode, key groups), so every window takes the full-precision path; in
+// rotary mode the queries are rotated at the new token's position npos - 1.
 template <int WT, bool MAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void tier_attn_kernel(
     TierArgs A, const uint16_t* __restrict__ q, int n_fp, int n_q, int nch_f, int npos, float scale) {
