@@ -311,8 +311,12 @@ def run_block(args, w):
     torch.cuda.synchronize()
     first_ms = warm_up(ctx, inputs, out, args.warmup)
     dt, n_prof = timed_steps(ctx, inputs, out, args.warmup, total, args.prof_every)
-    names = ("open", "attn", "merge", "mass", "policy", "offload")
+    names = ("open", "attn", "attn_whole", "merge", "mass", "policy", "offload")
     prof = {k: ctx.profile_read(k) for k in names}
+    # "attn_whole": the whole-cache kernel over the block tables (its steps
+    # need no merge), "attn": the split kernel
+    whole = prof["attn_whole"][1] > 0
+    assert not (whole and prof["attn"][1] > 0), "both attention kernels ran in the timed steps"
     # resident tokens read by a steady step: every resident block is full
     # except the sequence's last one (the new token's)
     n_tok = 0
@@ -325,7 +329,7 @@ def run_block(args, w):
     kv_bytes = L * Hkv * n_tok * 2 * d * 2
     step_bytes = kv_bytes + w.batch * (L * Hq * d * 2 + L * Hq * d * 4 + L * Hkv * 2 * d * 2)
     ms_step = dt * 1e3 / args.steps
-    attn_ms, attn_n = prof["attn"]
+    attn_ms, attn_n = prof["attn_whole" if whole else "attn"]
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     attn_gbps = kv_bytes / attn_avg_s / 1e9 if attn_avg_s > 0 else None
     policy_ms = sum(prof[k][0] for k in ("merge", "mass", "policy", "offload")) / n_prof
@@ -349,7 +353,8 @@ def run_block(args, w):
         "roofline": {
             "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": None, "kernel": "attn_mfma_kernel", "algorithmic_bytes_per_launch": kv_bytes,
+            "traffic": None, "kernel": "attn_seq_kernel" if whole else "attn_mfma_kernel",
+            "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
     if not args.no_cpu_baseline:

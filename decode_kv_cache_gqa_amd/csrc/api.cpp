@@ -617,6 +617,17 @@ static hipError_t offload_evicted(kvev_ctx* c, const std::vector<int>& ev) {
   return launch_offload(c, kmax, E);
 }
 
+// The whole-cache attention over the block tables (bf16, head_dim 128; the
+// block mode has no scorer variants): under the same rule as the token
+// modes' (at least 224 (group, layer) pairs unless attn_path asks for it,
+// the step's slots within its bound and its LDS).
+static bool block_whole_attention(const kvev_ctx* c, int64_t n_max) {
+  const auto& f = c->cfg;
+  if (f.attn_path == KVEV_ATTN_SPLIT || !c->d.bpart || f.scorer != 0) return false;
+  if (n_max > kSeqMaxSlots || seq_attn_lds_bytes(c->HG, n_max, true, true) + 1024 > c->max_lds) return false;
+  return f.attn_path == KVEV_ATTN_WHOLE || static_cast<int64_t>(c->G) * f.n_layers >= 224;
+}
+
 static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                               float* out, bool do_select, int64_t override_budget) {
   if (!q || !k_new || !v_new || !out) return fail(c, KVEV_EINVAL, "null argument");
@@ -637,9 +648,15 @@ static kvev_status block_step(kvev_ctx* c, const void* q, const void* k_new, con
   const int nm = static_cast<int>(n_max);
   // every launch of the step times itself from its own dispatch (kvev_profile_*)
   KVEV_HIP(c, launch_block_open(c, nm, static_cast<int>(t)));
-  KVEV_HIP(c, launch_attention(c, q, k_new, v_new, nm, 1, "attn"));
-  KVEV_HIP(c, launch_block_merge(c, out, nm));
-  KVEV_HIP(c, launch_block_mass(c, nm));
+  if (block_whole_attention(c, n_max)) {
+    // one workgroup per (group, layer): outputs and entry masses directly
+    KVEV_HIP(c, launch_attention_seq_blocks(c, q, k_new, v_new, out, nm));
+    KVEV_HIP(c, launch_block_entry_mass(c, nm));
+  } else {
+    KVEV_HIP(c, launch_attention(c, q, k_new, v_new, nm, 1, "attn"));
+    KVEV_HIP(c, launch_block_merge(c, out, nm));
+    KVEV_HIP(c, launch_block_mass(c, nm));
+  }
   KVEV_HIP(c, launch_block_policy(c, static_cast<int>(t), 1, do_select ? 1 : 0, 1,
                                   static_cast<int>(override_budget > 0 ? override_budget : 0)));
   if (c->cfg.offload_blocks > 0 && do_select) {
@@ -704,7 +721,7 @@ static bool whole_cache_attention(const kvev_ctx* c, int64_t n_max) {
   const auto& f = c->cfg;
   if (f.attn_path == KVEV_ATTN_SPLIT || c->block_mode || c->tier_mode || c->pooled) return false;
   if (f.dtype != KVEV_BF16 || f.head_dim != 128 || f.scorer != 0) return false;
-  if (n_max > kSeqMaxSlots || seq_attn_lds_bytes(c->HG, n_max, true) + 1024 > c->max_lds) return false;
+  if (n_max > kSeqMaxSlots || seq_attn_lds_bytes(c->HG, n_max, true, false) + 1024 > c->max_lds) return false;
   return f.attn_path == KVEV_ATTN_WHOLE || static_cast<int64_t>(c->G) * f.n_layers >= 224;
 }
 

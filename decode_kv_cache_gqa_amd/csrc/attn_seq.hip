@@ -64,13 +64,14 @@ struct SeqChunk {
 // Loads of chunk c from the group's pages (slots past the group's count are
 // masked, so their values never count).  The cache is read once per step:
 // non-temporal loads keep it from displacing reused lines.
+template <bool PG>
 __device__ __forceinline__ void seq_load(SeqChunk& ch, const uint16_t* __restrict__ kpool,
-                                         const uint16_t* __restrict__ vpool, int page0, int maxpages, int c,
-                                         int l, int r16, int q4, int64_t P) {
+                                         const uint16_t* __restrict__ vpool, int page0, const int* s_pt,
+                                         int maxpages, int c, int l, int r16, int q4, int64_t P) {
   constexpr int D = 128;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int page = page0 + min(2 * c + j, maxpages - 1);
+    const int page = PG ? s_pt[2 * c + j] : page0 + min(2 * c + j, maxpages - 1);
     const uint16_t* kb = kpool + kidx(l, page, r16, 8 * q4, P, D);
     const uint16_t* vb = vpool + vidx(l, page, 4 * q4, r16, P, D);
 #pragma unroll
@@ -83,9 +84,9 @@ __device__ __forceinline__ void seq_load(SeqChunk& ch, const uint16_t* __restric
 
 // One chunk: append of the new token (when the chunk holds the free slot),
 // q.K^T, online softmax, p.V.
-template <int HG, bool OBS>
+template <int HG, bool OBS, bool PG>
 __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, int tnew, const u32x4s (&knew)[4],
-                                         const uint32_t (&vnew)[8], int page0,
+                                         const uint32_t (&vnew)[8], int page0, const int* s_pt,
                                          uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool, int l,
                                          int r16, int q4, int64_t P, bool head, const bf16x8s (&qb)[4],
                                          float scale, float* s_lg, float* s_mc, int nstride, f32x4s (&oacc)[8],
@@ -95,7 +96,7 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
   // selects with constant indices) and is written into its page
   if (app && (tnew >> 5) == c) {  // wave-uniform
     const int jn = (tnew >> 4) & 1, rn = tnew & 15;
-    const int page = page0 + 2 * c + jn;
+    const int page = PG ? s_pt[2 * c + jn] : page0 + 2 * c + jn;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bool krow = j == jn && r16 == rn;
@@ -146,7 +147,23 @@ __device__ __forceinline__ void seq_step(SeqChunk& ch, int c, int n, bool app, i
     }
   l_run = l_run * alpha + psum;
   m_run = m_new;
-  if (OBS && head) {
+  if constexpr (OBS && PG) {
+    // block table: the chunk's two 16-slot tiles are table entries 2c and
+    // 2c + 1; per head, each tile's probability sum relative to the running
+    // maximum, and that maximum (the four lane quarters hold a tile's slots)
+    float bs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bs[j] = (sv[j][0] + sv[j][1]) + (sv[j][2] + sv[j][3]);
+      bs[j] += __shfl_xor(bs[j], 16, kWave);
+      bs[j] += __shfl_xor(bs[j], 32, kWave);
+    }
+    if (head && q4 == 0) {
+      s_lg[(2 * c) * HG + r16] = bs[0];
+      s_lg[(2 * c + 1) * HG + r16] = bs[1];
+      s_mc[c * HG + r16] = m_new;
+    }
+  } else if (OBS && head) {
     // the chunk's probabilities relative to its running maximum, and that
     // maximum: the probability pass rescales them once M and Z are known
 #pragma unroll
@@ -191,21 +208,31 @@ __device__ __forceinline__ void head_stats(const float (&wm)[NW][HG], const floa
   for (int x = 0; x < NW; ++x) Z += wm[x][h] == -INFINITY ? 0.f : wl[x][h] * __expf(wm[x][h] - M);
 }
 
-template <int NW, int HG, bool OBS>
-__global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
+// PG (block mode): the group's slots lie in the pages its block table
+// names, ptab[g][e] for table entry e = slot / 16, and the step's new token
+// takes slot count[g] (the last entry).  On an observation step the kernel
+// writes, instead of per-slot masses, the group mass of every table entry,
+// gmass[((b * L + l) * Hkv + kvh) * maxpages + e] = the sum of G[t] over
+// the entry's 16 slots.
+template <int NW, int HG, bool OBS, bool PG>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_seq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const int* __restrict__ count, const int* __restrict__ hole, float* __restrict__ out,
     float* __restrict__ gmass, int L, int G, int Hkv, int Hq, int64_t P, int maxpages, int64_t lstride,
-    int nstride, float scale, int nmax) {
+    int nstride, float scale, int nmax, const int* __restrict__ ptab) {
   static_assert(HG >= 1 && HG <= 8, "group size");
   constexpr int D = 128, NT = NW * kWave;
   extern __shared__ float dyn[];
-  // observation steps: [HG][nstride] probabilities and [nstride / 32][HG]
-  // chunk maxima; then [NW][HG][D] per-wave outputs
+  // observation steps: the probabilities (token mode [HG][nstride] per
+  // slot; block mode [nstride / 16][HG] per table entry) and
+  // [nstride / 32][HG] chunk maxima; then [NW][HG][D] per-wave outputs;
+  // then (block mode) the page of every table entry the loads can reach
+  const int nchm = (nmax + 31) / 32;  // chunks of the launch's slot bound (nstride / 32)
   float* s_lg = dyn;
-  float* s_mc = dyn + (OBS ? HG * nstride : 0);
+  float* s_mc = dyn + (OBS ? (PG ? HG * 2 * nchm : HG * nstride) : 0);
   float* o_m = s_mc + (OBS ? HG * (nstride / 32) : 0);
+  int* s_pt = reinterpret_cast<int*>(o_m + NW * HG * D);
   __shared__ float wm[NW][HG], wl[NW][HG], sf[NW][HG];
 
   const int g = blockIdx.x, l = blockIdx.y;
@@ -215,17 +242,36 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   const int Bsz = G / Hkv, b = g / Hkv, kvh = g % Hkv;
   const int64_t new_off = (static_cast<int64_t>(l * Bsz + b) * Hkv + kvh) * D;
   const bool head = r16 < HG;  // the lane's column is a real query head
-
-  // The chunk ranges come from the launch's slot bound nmax (>= every
-  // group's slot count), and a token-mode group's logical page i is the
-  // pool page g * maxpages + i, so the first page loads issue at once; slots
-  // past the group's count are masked.
-  const int nch = (nmax + 31) / 32;
-  const int cpw = (nch + NW - 1) / NW;
-  const int c0 = min(nch, wave * cpw), c1 = min(nch, c0 + cpw);
   const int page0 = g * maxpages;  // the group's first page
+
+  // Token mode: the chunk ranges come from the launch's slot bound nmax
+  // (>= every group's slot count), and a group's logical page i is the pool
+  // page g * maxpages + i, so the first page loads issue at once; slots past
+  // the group's count are masked.  Block mode: the table's pages (entries
+  // past the group's own, which only masked loads reach, and any value
+  // outside the pool become the group's first page) are staged in LDS
+  // beside the count, and the ranges split the group's own chunks evenly.
+  int c0, c1;
+  if constexpr (!PG) {
+    const int nch = nchm;
+    const int cpw = (nch + NW - 1) / NW;
+    c0 = min(nch, wave * cpw);
+    c1 = min(nch, c0 + cpw);
+  }
   const int n = count[g] + 1;  // slots including the new token
-  const int tnew = hole[g];
+  const int tnew = PG ? n - 1 : hole[g];
+  if constexpr (PG) {
+    const int* pt = ptab + static_cast<int64_t>(g) * maxpages;
+    const int npg = (n + 15) / 16;
+    for (int i = tid; i < 2 * nchm + 2; i += NT) {
+      const int v = (i < npg && i < maxpages) ? pt[i] : page0;
+      s_pt[i] = (v >= 0 && v < P) ? v : page0;
+    }
+    __syncthreads();
+    const int nch = min((n + 31) / 32, nchm);
+    c0 = wave * nch / NW;
+    c1 = (wave + 1) * nch / NW;
+  }
 
   // B operand of q.K^T: query head r16, channels 32s + 8q4 .. +8.  Lanes
   // past the group's heads repeat its last head: their logits are masked
@@ -265,25 +311,25 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   SeqChunk cur, nxt;
   int c = c0;
   __builtin_amdgcn_sched_barrier(0);
-  seq_load(cur, kpool, vpool, page0, maxpages, c0, l, r16, q4, P);
+  seq_load<PG>(cur, kpool, vpool, page0, s_pt, maxpages, c0, l, r16, q4, P);
 #pragma unroll 1
   for (; c + 2 < c1; c += 2) {
-    seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
-    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, s_mc, nstride, oacc, m_run, l_run);
-    seq_load(cur, kpool, vpool, page0, maxpages, c + 2, l, r16, q4, P);
-    seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_load<PG>(nxt, kpool, vpool, page0, s_pt, maxpages, c + 1, l, r16, q4, P);
+    seq_step<HG, OBS, PG>(cur, c, n, app, tnew, knew, vnew, page0, s_pt, kpool, vpool, l, r16, q4, P, head, qb,
+                          scale, s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_load<PG>(cur, kpool, vpool, page0, s_pt, maxpages, c + 2, l, r16, q4, P);
+    seq_step<HG, OBS, PG>(nxt, c + 1, n, app, tnew, knew, vnew, page0, s_pt, kpool, vpool, l, r16, q4, P, head, qb,
+                          scale, s_lg, s_mc, nstride, oacc, m_run, l_run);
   }
   if (c + 1 < c1) {
-    seq_load(nxt, kpool, vpool, page0, maxpages, c + 1, l, r16, q4, P);
-    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, s_mc, nstride, oacc, m_run, l_run);
-    seq_step<HG, OBS>(nxt, c + 1, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_load<PG>(nxt, kpool, vpool, page0, s_pt, maxpages, c + 1, l, r16, q4, P);
+    seq_step<HG, OBS, PG>(cur, c, n, app, tnew, knew, vnew, page0, s_pt, kpool, vpool, l, r16, q4, P, head, qb,
+                          scale, s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_step<HG, OBS, PG>(nxt, c + 1, n, app, tnew, knew, vnew, page0, s_pt, kpool, vpool, l, r16, q4, P, head, qb,
+                          scale, s_lg, s_mc, nstride, oacc, m_run, l_run);
   } else if (c < c1) {
-    seq_step<HG, OBS>(cur, c, n, app, tnew, knew, vnew, page0, kpool, vpool, l, r16, q4, P, head, qb, scale,
-                      s_lg, s_mc, nstride, oacc, m_run, l_run);
+    seq_step<HG, OBS, PG>(cur, c, n, app, tnew, knew, vnew, page0, s_pt, kpool, vpool, l, r16, q4, P, head, qb,
+                          scale, s_lg, s_mc, nstride, oacc, m_run, l_run);
   }
 
   // ---- merge the waves --------------------------------------------------------
@@ -327,7 +373,18 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
     for (int w = 0; w < NW; ++w) o += sf[w][h] * o_m[(w * HG + h) * D + cc];
     out[(static_cast<int64_t>(l * Bsz + b) * Hq + kvh * HG + h) * D + cc] = o;
   }
-  if constexpr (OBS) {
+  if constexpr (OBS && PG) {
+    // the group's mass of every table entry
+    float* gm = gmass + (static_cast<int64_t>(b * L + l) * Hkv + kvh) * maxpages;
+    const int ne = min((n + 15) / 16, 2 * nchm);
+    for (int e = tid; e < ne; e += NT) {
+      const float* f = s_mc + (e >> 1) * HG;
+      float m = 0.f;
+#pragma unroll
+      for (int h = 0; h < HG; ++h) m += s_lg[e * HG + h] * f[h];
+      gm[e] = m;
+    }
+  } else if constexpr (OBS) {
     // probability pass: the group's mass of every slot
     float* gm = gmass + (static_cast<int64_t>(g) * L + l) * lstride;
     for (int t = tid; t < n; t += NT) {
@@ -340,37 +397,57 @@ __global__ __launch_bounds__(NW * kWave) void attn_seq_kernel(
   }
 }
 
-// Grid (groups, layers), NW = 8 waves; dynamic LDS: the logits (observation
-// steps) and the per-wave outputs.
+// Grid (groups, layers); dynamic LDS: the probabilities (observation
+// steps), the per-wave outputs and (block mode) the staged page table.
+// Token modes: 8 waves, one workgroup per CU over about one round.  Block
+// mode: many rounds of workgroups, 4 waves each, so that two share a CU and
+// one's start and epilogue overlap the other's stream.
 constexpr int kSeqNW = 8;
+constexpr int kSeqBlkNW = 4;
 
-int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs) {
-  const int64_t nstride = (n_max + 31) / 32 * 32;
-  return ((obs ? hg * nstride + hg * (nstride / 32) : 0) + static_cast<int64_t>(kSeqNW) * hg * 128) * 4;
+int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs, bool paged) {
+  const int64_t nstride = (n_max + 31) / 32 * 32, nchm = nstride / 32;
+  const int64_t probs = obs ? (paged ? hg * 2 * nchm : hg * nstride) + hg * nchm : 0;
+  const int64_t nw = paged ? kSeqBlkNW : kSeqNW;
+  return (probs + nw * hg * 128 + (paged ? 2 * nchm + 2 : 0)) * 4;
 }
 
-hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
-                                float* out, int n_max, int obs) {
+static hipError_t launch_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new, float* out,
+                             int n_max, bool obs, bool paged) {
   const auto& cf = c->cfg;
   const int nstride = (n_max + 31) / 32 * 32;
-  const size_t shm = static_cast<size_t>(seq_attn_lds_bytes(c->HG, n_max, obs != 0));
+  const size_t shm = static_cast<size_t>(seq_attn_lds_bytes(c->HG, n_max, obs, paged));
   dim3 grid(c->G, cf.n_layers);
+  // block mode: the entry masses go to the per-block buffer
+  float* gm = paged ? c->d.bpart : c->d.logits;
   return with_group(c->HG, [&](auto hg) -> hipError_t {
     constexpr int HG = decltype(hg)::value;
     auto launch = [&](auto kern) -> hipError_t {
       if (hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(shm)))
         return e;
-      return timed_launch(c, "attn_whole", kern, grid, dim3(kSeqNW * kWave), shm, static_cast<const uint16_t*>(q),
-                          static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                          static_cast<uint16_t*>(c->d.kpool), static_cast<uint16_t*>(c->d.vpool),
-                          static_cast<const int*>(c->d.count), static_cast<const int*>(c->d.hole), out,
-                          c->d.logits, static_cast<int>(cf.n_layers), c->G, static_cast<int>(cf.n_kv_heads),
-                          static_cast<int>(cf.n_q_heads), c->P, c->maxpages, c->lstride, nstride,
-                          1.0f / sqrtf(128.0f), n_max);
+      const int nt = (paged ? kSeqBlkNW : kSeqNW) * kWave;
+      return timed_launch(c, "attn_whole", kern, grid, dim3(nt), shm,
+                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_new),
+                          static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(c->d.kpool),
+                          static_cast<uint16_t*>(c->d.vpool), static_cast<const int*>(c->d.count),
+                          static_cast<const int*>(c->d.hole), out, gm, static_cast<int>(cf.n_layers), c->G,
+                          static_cast<int>(cf.n_kv_heads), static_cast<int>(cf.n_q_heads), c->P, c->maxpages,
+                          c->lstride, nstride, 1.0f / sqrtf(128.0f), n_max, static_cast<const int*>(c->d.ptab));
     };
-    return obs ? launch(attn_seq_kernel<kSeqNW, HG, true>) : launch(attn_seq_kernel<kSeqNW, HG, false>);
+    if (paged) return launch(attn_seq_kernel<kSeqBlkNW, HG, true, true>);
+    return obs ? launch(attn_seq_kernel<kSeqNW, HG, true, false>) : launch(attn_seq_kernel<kSeqNW, HG, false, false>);
   });
+}
+
+hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                                float* out, int n_max, int obs) {
+  return launch_seq(c, q, k_new, v_new, out, n_max, obs != 0, false);
+}
+
+hipError_t launch_attention_seq_blocks(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                                       float* out, int n_max) {
+  return launch_seq(c, q, k_new, v_new, out, n_max, true, true);
 }
 
 }  // namespace kvev

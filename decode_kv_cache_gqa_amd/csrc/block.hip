@@ -264,6 +264,35 @@ __global__ __launch_bounds__(256) void blk_mass_part_kernel(BlockArgs A, const f
   if (lane == 0 && e < nres) A.bmass[static_cast<int64_t>(b) * A.maxpages + e] = acc;
 }
 
+// Mass after the whole-cache attention, which wrote the group mass of every
+// table entry per (layer, KV head) into gm [batch][L][Hkv][maxpages]: per
+// entry, their sum over every layer and KV head (each quarter of the
+// threads sums a quarter of the pairs in order, the quarters are added in
+// order).  Block (64 entries, sequence).
+__global__ __launch_bounds__(256) void blk_entry_mass_kernel(BlockArgs A, const float* __restrict__ gm) {
+  __shared__ float s_red[4][64];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  const int e = blockIdx.x * 64 + tid % 64, part = tid / 64;
+  const int nres = A.nres[b];
+  if (blockIdx.x * 64 >= nres) return;
+  const int np = A.L * A.Hkv;
+  const float* src = gm + static_cast<int64_t>(b) * np * A.maxpages + (e < nres ? e : 0);
+  float acc = 0.f;
+  for (int i0 = part; i0 < np; i0 += 4 * kMassLoads) {
+    float x[kMassLoads];
+#pragma unroll
+    for (int k = 0; k < kMassLoads; ++k) x[k] = src[static_cast<int64_t>(min(i0 + 4 * k, np - 1)) * A.maxpages];
+#pragma unroll
+    for (int k = 0; k < kMassLoads; ++k)
+      if (i0 + 4 * k < np) acc += x[k];
+  }
+  s_red[part][tid % 64] = acc;
+  __syncthreads();
+  if (tid < 64 && e < nres)
+    A.bmass[static_cast<int64_t>(b) * A.maxpages + e] =
+        ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+}
+
 // Exclusive prefix sum of one int per thread over the block (NT threads).
 template <int NT>
 __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
@@ -685,6 +714,12 @@ hipError_t launch_block_mass(kvev_ctx* c, int n_max) {
   dim3 grid((n_max + 63) / 64, c->cfg.batch);
   const size_t shm = (static_cast<size_t>(c->cfg.n_layers) * c->cfg.n_kv_heads * 8 + 256) * sizeof(float);
   return timed_launch(c, "mass", blk_mass_kernel, grid, dim3(kMassNT), shm, A);
+}
+
+hipError_t launch_block_entry_mass(kvev_ctx* c, int n_max) {
+  BlockArgs A = block_args(c, nullptr, n_max);
+  dim3 grid((n_max + 64 * kPageTokens - 1) / (64 * kPageTokens), c->cfg.batch);
+  return timed_launch(c, "mass", blk_entry_mass_kernel, grid, dim3(256), 0, A, static_cast<const float*>(c->d.bpart));
 }
 
 hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,

@@ -311,10 +311,15 @@ hipError_t launch_post(kvev_ctx* c, float* out, const void* k_new, const void* v
 // page g * maxpages + i)
 hipError_t launch_attention_seq(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
                                 float* out, int n_max, int obs);
+// the same kernel over the block mode's page tables: writes out and the
+// group mass of every table entry into d.bpart ([batch][L][Hkv][maxpages]);
+// launch_block_entry_mass then sums it per entry into bmass
+hipError_t launch_attention_seq_blocks(kvev_ctx* c, const void* q, const void* k_new, const void* v_new,
+                                       float* out, int n_max);
 // after it: fold of the masses, the new token's state and the selection
 // (policy.hip)
 hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64_t budget);
-int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs);
+int64_t seq_attn_lds_bytes(int hg, int64_t n_max, bool obs, bool paged);
 constexpr int kSeqMaxSlots = 8192;  // the whole-cache kernel's slot bound (64 pages per wave)
 hipError_t launch_select(kvev_ctx* c, int64_t budget);
 // plans the move of each over-budget group's last token into its inner free slot
@@ -332,6 +337,7 @@ kvev_status fmm_check(kvev_ctx* full, kvev_ctx* comp, const double* fmm);
 hipError_t launch_block_open(kvev_ctx* c, int n_max, int t);
 hipError_t launch_block_merge(kvev_ctx* c, float* out, int n_max);
 hipError_t launch_block_mass(kvev_ctx* c, int n_max);
+hipError_t launch_block_entry_mass(kvev_ctx* c, int n_max);
 hipError_t launch_block_policy(kvev_ctx* c, int t, int update, int do_select, int appended,
                                int budget_override);
 hipError_t launch_block_readmit(kvev_ctx* c, int b, int n, const int* ids_dev, int t);

@@ -158,7 +158,7 @@ class Workload:
     diag_topk: int = 0              # token modes: rank-trace diagnostics over the top-k (0: off)
     offload_blocks: int = 0         # block mode: host-offload pool slots (0: off)
     revival_gap: int = 0            # tiered mode: routing diagnostics, sustained-absence length (0: off)
-    attn_path: int = 0              # token modes: attention kernel (0 auto, 1 split, 2 whole-cache)
+    attn_path: int = 0              # token and block modes: attention kernel (0 auto, 1 split, 2 whole-cache)
     evict_interval: int = 1         # token modes: select only every evict_interval steps
     rope_theta: float = 0.0         # tiered mode: keys and queries arrive before the rotary embedding
     int2_key_groups: int = 0        # tiered mode: 1 = keys quantized per token and 32-channel group

@@ -201,16 +201,16 @@ typedef struct {
    * (the graded offload / drop rule of "MemDecay" section III-E; 0: every
    * evicted block is offloaded). */
   float offload_min_score;
-  /* Token policies, bf16 and head_dim 128: which attention kernel runs (a
-   * kvev_attn_path).  AUTO: the whole-cache kernel (one workgroup per (KV
-   * head group, layer) over every retained slot; it writes the outputs and
-   * each slot's group mass directly) when there are at least 224 (group,
-   * layer) pairs, the step's slot count fits its bound (8,192 slots and the
-   * logits in the workgroup's LDS) and neither a scorer variant nor
-   * per-sequence granularity is set; the split kernel otherwise.  SPLIT:
-   * always the split kernel.  WHOLE: the whole-cache kernel whenever it
-   * applies, whatever the pair count.  Results agree within the
-   * tolerances; each path is deterministic. */
+  /* Token policies and the block mode, bf16 and head_dim 128: which
+   * attention kernel runs (a kvev_attn_path).  AUTO: the whole-cache kernel
+   * (one workgroup per (KV head group, layer) over every retained slot; it
+   * writes the outputs and each slot's group mass, in the block mode each
+   * table entry's, directly) when there are at least 224 (group, layer)
+   * pairs, the step's slot count fits its bound (8,192 slots and its LDS)
+   * and neither a scorer variant nor per-sequence granularity is set; the
+   * split kernel otherwise.  SPLIT: always the split kernel.  WHOLE: the
+   * whole-cache kernel whenever it applies, whatever the pair count.
+   * Results agree within the tolerances; each path is deterministic. */
   int32_t attn_path;
   /* Token policies: kvev_step selects only after the steps t (counted from
    * 1) with (t - 1) % evict_interval == 0, and in between only appends, so

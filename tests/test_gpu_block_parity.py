@@ -1,5 +1,6 @@
-"""GPU parity of the block-granular LRFU path (block open, split attention,
-block mass over every layer and head, EMA score and access clock, region
+"""GPU parity of the block-granular LRFU path (block open, attention by the
+split kernel or the whole-cache kernel over the block tables, block mass
+over every layer and head, EMA score and access clock, region
 decay priority, pinned selection, stable table compaction, re-admission with
 persisted scores) against the CPU oracle, through the C ABI."""
 import numpy as np
@@ -17,6 +18,10 @@ def _gu():
     return gpu_util
 
 
+# attention kernels: split (1) and whole-cache (2)
+PATHS = pytest.mark.parametrize("path", [1, 2], ids=["split", "whole"])
+
+
 def _scaled(**kw):
     base = dict(n_layers=2, n_q_heads=8, n_kv_heads=2, prefill_lens=(300, 517, 704, 1000),
                 n_epochs=3, epoch_steps=16)
@@ -24,15 +29,17 @@ def _scaled(**kw):
     return synth.workload("lrfu64").scaled(**base)
 
 
-def test_block_lrfu_fused_step_with_readmission():
+@PATHS
+def test_block_lrfu_fused_step_with_readmission(path):
     """4 sequences (ragged, one a multiple of 16), 2 layers, bf16 d=128,
     48 steps over 3 heavy-key epochs with re-admission at each boundary."""
-    st = _gu().run_block_lockstep(_scaled(), 48)
+    st = _gu().run_block_lockstep(_scaled(attn_path=path), 48)
     assert st.steps == 48 and st.readmitted > 0 and st.kv_checks > 0
 
 
-def test_block_lrfu_separate_calls():
-    st = _gu().run_block_lockstep(_scaled(prefill_lens=(450, 333)), 40, fused=False)
+@PATHS
+def test_block_lrfu_separate_calls(path):
+    st = _gu().run_block_lockstep(_scaled(prefill_lens=(450, 333), attn_path=path), 40, fused=False)
     assert st.steps == 40
 
 
@@ -42,27 +49,30 @@ def test_block_lrfu_fp32_d64():
     assert st.max_out_err <= 1e-5 and st.max_score_err <= 1e-5
 
 
-def test_block_lrfu_strong_decay_and_tight_budget():
+@PATHS
+def test_block_lrfu_strong_decay_and_tight_budget(path):
     """beta 0.05 and short half-lives make the region decay dominate; the
     budget leaves room for few unpinned blocks."""
     w = _scaled(beta=0.05, region_half_lives=(40.0, 20.0, 10.0, 5.0, 3.0), budget_frac=0.15,
-                prefill_lens=(640, 900))
+                prefill_lens=(640, 900), attn_path=path)
     _gu().run_block_lockstep(w, 40)
 
 
-def test_block_lrfu_edge_cases():
+@PATHS
+def test_block_lrfu_edge_cases(path):
     """One-token prefill (its block is the tail), a prefill ending on a block
     boundary, and a budget that never binds."""
     w = _scaled(prefill_lens=(1, 16, 47), budget_frac=5.0, n_epochs=1, epoch_steps=0,
-                structured=False)
+                structured=False, attn_path=path)
     st = _gu().run_block_lockstep(w, 40, readmit=False)
     assert st.steps == 40
 
 
-def test_block_step_bitwise_equals_separate_calls():
+@PATHS
+def test_block_step_bitwise_equals_separate_calls(path):
     import torch
     from decode_kv_cache_gqa_amd import kvev
-    w = _scaled(n_layers=3, prefill_lens=(800, 1300))
+    w = _scaled(n_layers=3, prefill_lens=(800, 1300), attn_path=path)
     outs, states = [], []
     for fused in (True, False):
         ctx = kvev.context_for(w, max_steps=24)
