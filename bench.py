@@ -104,6 +104,7 @@ CSRC = os.path.join(ROOT, "decode_kv_cache_gqa_amd", "csrc")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_mfma_kernel_traffic_llama8b_32k.md")
 ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("attn.hip", "common.h")]
 SEQ_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_seq_kernel_traffic_llama8b_32k.md")
+BLK_SEQ_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_seq_kernel_traffic_lrfu64.md")
 TIER_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tier_attn_kernel_traffic_qevict131k.md")
 TIER_SOURCES = [os.path.join(CSRC, f) for f in ("tier.hip", "common.h")]
 SEQ_SOURCES = [os.path.join(CSRC, f) for f in ("attn_seq.hip", "common.h")]
@@ -353,7 +354,10 @@ def run_block(args, w):
         "roofline": {
             "bound": "hbm", "achieved": round(attn_gbps, 1) if attn_gbps else None, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4) if attn_gbps else None,
-            "traffic": None, "kernel": "attn_seq_kernel" if whole else "attn_mfma_kernel",
+            # counters taken on the 64-sequence workload's whole-cache launch
+            "traffic": (measured_traffic(BLK_SEQ_TRAFFIC_PROFILE, SEQ_SOURCES)
+                        if whole and args.workload == "lrfu64" else None),
+            "kernel": "attn_seq_kernel" if whole else "attn_mfma_kernel",
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
