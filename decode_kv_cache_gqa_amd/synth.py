@@ -14,7 +14,10 @@ GQA attention, 8k-131k contexts, 5-25% budgets):
 * K, V, Q entries ~ N(0, 1) (65536-level inverse-CDF quantiles).
 * Outlier channels: 4 of the 128 channels are scaled x8, drawn
   independently for K and for Q per (layer, sequence, KV head); the Q set is
-  shared by the KV head's query group.
+  shared by the KV head's query group.  ``outlier_shared_qk`` takes the
+  other reading of the 32k workload's wording: the same 4 channels in Q and
+  K (logits then grow about five times wider and one token takes nearly all
+  of a group's mass).
 * Mean query direction u: a unit vector with +-1/8 on 64 hashed channels.
   Queries add mu*u with mu = |c|/4, |c| = sqrt(124 + 4*64) the expected row
   norm.  Heavy keys: 64 positions per (layer, sequence, KV head, epoch) in
@@ -162,6 +165,7 @@ class Workload:
     evict_interval: int = 1         # token modes: select only every evict_interval steps
     rope_theta: float = 0.0         # tiered mode: keys and queries arrive before the rotary embedding
     int2_key_groups: int = 0        # tiered mode: 1 = keys quantized per token and 32-channel group
+    outlier_shared_qk: bool = False  # the same outlier channels in Q and K
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -184,7 +188,8 @@ class Workload:
     def _structure(self, layer, seq, kvh):
         d = self.head_dim
         kout = _rank_channels(stream_key(self.seed, _META_KOUT, layer, seq, kvh), d)[:4]
-        qout = _rank_channels(stream_key(self.seed, _META_QOUT, layer, seq, kvh), d)[:4]
+        qmeta = _META_KOUT if self.outlier_shared_qk else _META_QOUT
+        qout = _rank_channels(stream_key(self.seed, qmeta, layer, seq, kvh), d)[:4]
         ck = np.ones(d, np.float32)
         ck[kout] = 8.0
         cq = np.ones(d, np.float32)
@@ -207,7 +212,7 @@ class Workload:
         """(ck, cq) of _structure for broadcast index arrays: [..., d]."""
         d = self.head_dim
         out = []
-        for meta in (_META_KOUT, _META_QOUT):
+        for meta in (_META_KOUT, _META_KOUT if self.outlier_shared_qk else _META_QOUT):
             top = _rank_channels_many(stream_keys(self.seed, meta, layers, seqs, heads), d)[..., :4]
             c = np.ones(top.shape[:-1] + (d,), np.float32)
             np.put_along_axis(c, top, np.float32(8.0), axis=-1)

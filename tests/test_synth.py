@@ -41,3 +41,24 @@ def test_lengths_and_workload_table():
     assert synth.workload("tiny").dtype == "f32"
     for name in synth.WORKLOADS:
         synth.workload(name)
+
+
+def test_outlier_channels_shared_by_q_and_k():
+    """The literal reading of the 32k workload's outlier wording: the same 4
+    channels scaled in Q and K.  The logit spread then grows about five
+    times (the outlier products add up coherently), against independent
+    channel sets."""
+    base = synth.workload("llama8b_32k").scaled(n_layers=1, prefill_lens=(4096,))
+    shared = base.scaled(outlier_shared_qk=True)
+    for w, same in ((base, False), (shared, True)):
+        ck, cq = w._structure(0, 0, 0)
+        assert (set(np.flatnonzero(ck == 8)) == set(np.flatnonzero(cq == 8))) == same
+        ck2, cq2 = w._structure_many(np.array([0]), np.array([0]), np.array([0]))
+        assert np.array_equal(ck2[0], ck) and np.array_equal(cq2[0], cq)
+    std = []
+    for w in (base, shared):
+        K, _ = w.prefill_kv(0, heads=[0])
+        q, _, _ = w.step_inputs(1)
+        s = (q[0, 0, 0].float() @ K[0, 0].float().T) / np.sqrt(128.0)
+        std.append(float(s.std()))
+    assert 3.0 < std[1] / std[0] < 8.0
