@@ -562,7 +562,8 @@ class TokenModeOracle:
       the existing utilities ([InertiaKV] App. E); on a refresh step it
       starts at 0, like the prefill tokens (m_0 = 0, App. E), and is then
       folded with its own attention mass (reading: the page states only the
-      non-refresh rule).
+      non-refresh rule).  ``new_token_init`` = "mean" applies the stated
+      rule on refresh steps too: the mean, then the fold.
     * Eviction happens once per step after all layers, whenever the group
       holds more than ``budget`` tokens, including non-refresh steps with
       the stale utility ([InertiaKV] App. E "Eviction on non-refresh steps").
@@ -586,6 +587,7 @@ class TokenModeOracle:
     capacity: int = 0
     scorer: str = "attention"
     evict_interval: int = 1
+    new_token_init: str = "zero"
     groups: dict = field(default_factory=dict)
     prefill_len: dict = field(default_factory=dict)
     last_G: dict = field(default_factory=dict)
@@ -623,6 +625,11 @@ class TokenModeOracle:
             return t == 1
         return (t - 1) % self.refresh_interval == 0
 
+    def _starts_at_mean(self, refresh):
+        if self.new_token_init not in ("zero", "mean"):
+            raise ValueError(self.new_token_init)
+        return not refresh or self.new_token_init == "mean"
+
     def is_evict_step(self, t):
         """Whether step t selects (every step unless evict_interval > 1)."""
         return (t - 1) % max(self.evict_interval, 1) == 0
@@ -656,7 +663,7 @@ class TokenModeOracle:
         for bi, seq in enumerate(seqs):
             for h in self.held_heads(seq):
                 g = self.groups[(seq, h)]
-                init = 0.0 if refresh else float(g.m[:g.n].mean())
+                init = float(g.m[:g.n].mean()) if self._starts_at_mean(refresh) else 0.0
                 self._grow(g)
                 g.K[:, g.n] = k_new[:, bi, h]
                 g.V[:, g.n] = v_new[:, bi, h]
@@ -735,7 +742,7 @@ class PooledTokenOracle:
     retained set per sequence: every KV head at every layer holds the same
     positions, in the same slots, so selection and compaction act on all of
     them together.  Aggregation, refresh cadence, new-token rule, protection
-    and eviction are those of ``TokenModeOracle``.
+    and eviction are those of ``TokenModeOracle`` (``new_token_init`` too).
 
     Scorers ([InertiaKV] §5.1, App. E): "vnorm" weights each head's
     probabilities by the VNorm weights of its own KV head's values before the
@@ -755,6 +762,7 @@ class PooledTokenOracle:
     n_recent: int = 0
     capacity: int = 0
     scorer: str = "attention"
+    new_token_init: str = "zero"
     seqs: dict = field(default_factory=dict)
     prefill_len: dict = field(default_factory=dict)
     last_G: dict = field(default_factory=dict)
@@ -781,6 +789,8 @@ class PooledTokenOracle:
             return t == 1
         return (t - 1) % self.refresh_interval == 0
 
+    _starts_at_mean = TokenModeOracle._starts_at_mean
+
     def _grow(self, st):
         if st.n < st.K.shape[2]:
             return
@@ -802,7 +812,7 @@ class PooledTokenOracle:
         Hg, H = self.group_size, self.n_q_heads
         for bi, seq in enumerate(seqs):
             st = self.seqs[seq]
-            init = 0.0 if refresh else float(st.m[:st.n].mean())
+            init = float(st.m[:st.n].mean()) if self._starts_at_mean(refresh) else 0.0
             self._grow(st)
             st.K[:, :, st.n] = k_new[:, bi]
             st.V[:, :, st.n] = v_new[:, bi]

@@ -348,6 +348,44 @@ def test_new_token_mean_init_on_non_refresh_steps():
     assert not np.array_equal(o.scores(0, 0)[:-1], after)
 
 
+def _two_refresh_steps(**kw):
+    rng = np.random.default_rng(14)
+    L, Hq, Hkv, d, n0 = 3, 4, 1, 8, 20
+    K = rng.standard_normal((L, Hkv, n0, d)).astype(np.float32)
+    V = rng.standard_normal((L, Hkv, n0, d)).astype(np.float32)
+    steps = [tuple(rng.standard_normal((L, 1, Hx, d)).astype(np.float32) for Hx in (Hq, Hkv, Hkv))
+             for _ in range(2)]
+    o = orc.TokenModeOracle(L, Hq, Hkv, d, budget=100, **kw)
+    o.prefill(0, K, V)
+    o.decode_step(1, *steps[0], [0])
+    prior = o.scores(0, 0).copy()
+    out = o.decode_step(2, *steps[1], [0])
+    return prior, o.scores(0, 0), out
+
+
+@pytest.mark.parametrize("policy,alpha", [("ema", 0.05), ("ema", 0.3), ("cumulative", 0.05)])
+def test_new_token_mean_init_on_refresh_steps(policy, alpha):
+    """new_token_init = "mean" (the App. E rule applied on refresh steps
+    too): the new token starts at the mean of the group's utilities and is
+    then folded, so against the zero start its utility moves by the prior's
+    fold weight times that mean, (1 - a)^L for the EMA (Eq.4 unrolled over
+    the L layers) and 1 for the running sum (Eq.3); nothing else changes."""
+    p0, s0, o0 = _two_refresh_steps(policy=policy, alpha_new=alpha)
+    p1, s1, o1 = _two_refresh_steps(policy=policy, alpha_new=alpha, new_token_init="mean")
+    np.testing.assert_array_equal(p0, p1)
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(s0[:-1], s1[:-1])
+    w = 1.0 if policy == "cumulative" else (1.0 - alpha) ** 3
+    assert abs((s1[-1] - s0[-1]) - w * p0.mean()) <= 1e-15
+    assert p0.mean() > 0.0
+
+
+def test_new_token_init_has_no_effect_with_the_single_step_rule():
+    _, s0, _ = _two_refresh_steps(alpha_new=1.0)
+    _, s1, _ = _two_refresh_steps(alpha_new=1.0, new_token_init="mean")
+    np.testing.assert_array_equal(s0, s1)
+
+
 # --- tiered routing and byte accounting -------------------------------------
 
 def test_qevict_worked_example(golden_dir):
