@@ -178,6 +178,10 @@ kvev_status kvev_create(const kvev_config* cfg, void* hip_stream, kvev_ctx** out
   if (f.int2_key_groups != 0 && f.policy != KVEV_TIERED_INT2)
     return bad("int2_key_groups applies to the tiered mode only");
   if (f.int2_key_groups != 0 && f.int2_key_groups != 1) return bad("int2_key_groups must be 0 or 1");
+  if (f.new_token_init != KVEV_NEW_TOKEN_ZERO && f.new_token_init != KVEV_NEW_TOKEN_MEAN)
+    return bad("new_token_init must be 0 or 1");
+  if (f.new_token_init != KVEV_NEW_TOKEN_ZERO && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
+    return bad("new_token_init applies to the token policies only");
   if (f.evict_interval < 0) return bad("evict_interval must be >= 0");
   if (f.evict_interval > 1 && f.policy != KVEV_EMA && f.policy != KVEV_CUMULATIVE)
     return bad("evict_interval applies to the token policies only");

@@ -273,7 +273,9 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
       key = (static_cast<unsigned long long>(float_key(myscore)) << 32) | static_cast<uint32_t>(mypos);
       slot = t;
     }
-    float sum = mine ? myscore : 0.f;
+    // the sum of the utilities (with mean_init on an observation step: of
+    // the starting utilities, whose mean the new token starts at)
+    float sum = mine ? ((A.refresh && A.mean_init) ? prior : myscore) : 0.f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const unsigned long long y = __shfl_xor(key, o, kWave);
@@ -371,6 +373,14 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
   if (!A.refresh) {
     newscore = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
     if (tid == 0) st_coherent(gs + hn, newscore);
+  } else if (A.mean_init) {
+    // the fold is linear in the start: the new token's fold from 0 plus
+    // the start (the others' mean) times its fold weight
+    newscore = newscore_obs + A.wprior * (n > 1 ? total / static_cast<float>(n - 1) : 0.f);
+    if (tid == 0) {
+      st_coherent(gs + hn, newscore);
+      if (A.dg_util) A.dg_util[static_cast<int64_t>(g) * A.cap + hn] = newscore;
+    }
   }
   if (tid == 0) {
     st_coherent(gp + hn, newest);
@@ -462,6 +472,8 @@ struct FoldArgs {
   int64_t cap, lstride;
   float a;
   int cumulative, refresh, do_select, B, n_sink, n_recent;
+  int mean_init;  // as in PostArgs
+  float wprior;
 };
 
 template <int NL>
@@ -516,7 +528,8 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
     key = (static_cast<unsigned long long>(float_key(m)) << 32) | static_cast<uint32_t>(mypos);
     slot = t;
   }
-  float sum = mine ? m : 0.f;
+  // (with mean_init on an observation step: the sum of the starting utilities)
+  float sum = mine ? ((A.refresh && A.mean_init) ? prior : m) : 0.f;
   float mn = (A.refresh && in && t == hn) ? m : 0.f;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -599,9 +612,12 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
       bslot = s_slot[w];
     }
   }
-  const float newscore = A.refresh ? newscore_obs : (n > 1 ? total / static_cast<float>(n - 1) : 0.f);
+  const float mean = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
+  // mean_init: the new token's fold from 0 plus its start times the start's fold weight
+  const float newscore = A.refresh ? newscore_obs + (A.mean_init ? A.wprior * mean : 0.f) : mean;
   if (tid == 0) {
-    if (!A.refresh) st_coherent(gs + hn, newscore);
+    if (!A.refresh || A.mean_init) st_coherent(gs + hn, newscore);
+    if (A.refresh && A.mean_init && A.dg_util) A.dg_util[static_cast<int64_t>(g) * A.cap + hn] = newscore;
     st_coherent(gp + hn, newest);
     A.nextpos[g] = newest + 1;
     A.grpctr[g] = 0u;
@@ -677,6 +693,8 @@ hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64
   A.B = static_cast<int>(budget);
   A.n_sink = cf.n_sink;
   A.n_recent = cf.n_recent;
+  A.mean_init = cf.new_token_init == KVEV_NEW_TOKEN_MEAN;
+  A.wprior = prior_fold_weight(cf.alpha_new, cf.n_layers, A.cumulative != 0);
   dim3 grid(A.nblk, c->G);
   if (cf.n_layers <= 32) return timed_launch(c, "post", fold_kernel<32>, grid, dim3(kFoldNT), 0, A);
   return timed_launch(c, "post", fold_kernel<kFoldLayers>, grid, dim3(kFoldNT), 0, A);
@@ -921,6 +939,8 @@ static hipError_t post_impl(kvev_ctx* c, float* out, const void* k_new, const vo
   A.refresh = refresh;
   A.do_select = do_select;
   A.seq = 0;
+  A.mean_init = cf.new_token_init == KVEV_NEW_TOKEN_MEAN;
+  A.wprior = prior_fold_weight(cf.alpha_new, cf.n_layers, A.cumulative != 0);
   A.B = static_cast<int>(budget);
   A.n_sink = cf.n_sink;
   A.n_recent = cf.n_recent;

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
       key = (static_cast<unsigned long long>(float_key(myscore)) << 32) | static_cast<uint32_t>(mypos);
       slot = t;
     }
-    float sum = mine ? myscore : 0.f;
+    // (with mean_init on an observation step: the sum of the starting utilities)
+    float sum = mine ? ((A.refresh && A.mean_init) ? prior : myscore) : 0.f;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const unsigned long long y = __shfl_xor(key, o, kWave);
@@ -315,6 +316,11 @@ __global__ __launch_bounds__(kPoolNT) void pool_post_kernel(PostArgs A) {
   float newscore = newscore_obs;
   if (!A.refresh) {
     newscore = n > 1 ? total / static_cast<float>(n - 1) : 0.f;
+    if (tid == 0) st_coherent(gs + hn, newscore);
+  } else if (A.mean_init) {
+    // the new token's fold from 0 plus its start (the others' mean) times
+    // the start's fold weight
+    newscore = newscore_obs + A.wprior * (n > 1 ? total / static_cast<float>(n - 1) : 0.f);
     if (tid == 0) st_coherent(gs + hn, newscore);
   }
   if (tid == 0) {

@@ -272,7 +272,21 @@ struct PostArgs {
   float a;
   int cumulative, refresh, do_select, B, n_sink, n_recent, nblk;
   int seq;  // the whole-cache attention wrote the outputs and the per-slot group masses
+  // mean_init: on an observation step the new token starts at the mean of
+  // the others' utilities (else 0); wprior: the start's weight after the
+  // fold over the L layers ((1 - a)^L, or 1 for the running sum)
+  int mean_init;
+  float wprior;
 };
+
+// The fold weight of a utility's starting value after L layers, formed in
+// the fold's own fp32 order.
+inline float prior_fold_weight(float a, int L, bool cumulative) {
+  float w = 1.0f;
+  if (!cumulative)
+    for (int l = 0; l < L; ++l) w *= 1.0f - a;
+  return w;
+}
 
 // HG consecutive fp32 logits (one slot of one layer)
 template <int HG>

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libkvev.so")
 
 OK, EINVAL, ENOMEM, EHIP, ESTATE, ERANGE = 0, -1, -2, -3, -4, -5
 ATTN_AUTO, ATTN_SPLIT, ATTN_WHOLE = 0, 1, 2
+NEW_TOKEN_ZERO, NEW_TOKEN_MEAN = 0, 1
 F32, BF16 = 0, 1
 EMA, CUMULATIVE, LRFU_BLOCK, TIERED_INT2 = 0, 1, 2, 3
 SCORE_VNORM, SCORE_ENTROPY = 1, 2
@@ -60,6 +61,7 @@ class Config(ctypes.Structure):
         ("evict_interval", ctypes.c_int32),
         ("rope_theta", ctypes.c_float),
         ("int2_key_groups", ctypes.c_int32),
+        ("new_token_init", ctypes.c_int32),
     ]
 
 
@@ -550,5 +552,6 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
         n_sink=w.n_sink, n_recent=w.n_recent, budget=w.budget if budget is None else budget,
         scorer=_SCORER_BITS[w.scorer], granularity=_GRANULARITY[w.granularity],
         diag_topk=w.diag_topk if diag_topk is None else diag_topk,
-        attn_path=w.attn_path if attn_path is None else attn_path, evict_interval=w.evict_interval)
+        attn_path=w.attn_path if attn_path is None else attn_path, evict_interval=w.evict_interval,
+        new_token_init=w.new_token_init)
     return Context(cfg, stream=stream)

@@ -166,6 +166,7 @@ class Workload:
     rope_theta: float = 0.0         # tiered mode: keys and queries arrive before the rotary embedding
     int2_key_groups: int = 0        # tiered mode: 1 = keys quantized per token and 32-channel group
     outlier_shared_qk: bool = False  # the same outlier channels in Q and K
+    new_token_init: int = 0         # token modes: 1 = the new token starts at the mean on observation steps too
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property

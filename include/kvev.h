@@ -242,9 +242,18 @@ typedef struct {
    * its full-precision slot (as with rope_theta > 0), and kvev_tier_ledger
    * returns the key parameters as [W][4] (token, group). */
   int32_t int2_key_groups;
+  /* Token policies only (0 otherwise): the new token's starting utility on
+   * an observation step (a kvev_new_token_init).  ZERO: 0, as the prefill
+   * tokens start ("What Matters ...", appendix E), then folded with its
+   * own mass.  MEAN: the mean of the other utilities of its group (of its
+   * sequence, with per-sequence granularity), the rule appendix E states
+   * for the steps without an observation, then folded.  On those steps the
+   * new token takes the mean either way. */
+  int32_t new_token_init;
 } kvev_config;
 
 typedef enum { KVEV_ATTN_AUTO = 0, KVEV_ATTN_SPLIT = 1, KVEV_ATTN_WHOLE = 2 } kvev_attn_path;
+typedef enum { KVEV_NEW_TOKEN_ZERO = 0, KVEV_NEW_TOKEN_MEAN = 1 } kvev_new_token_init;
 
 /* Fill *cfg with defaults: page_tokens 16, EMA, alpha_new 0.05,
  * refresh_interval 1, no protection, window_tokens 32, rope_theta 0; shape

@@ -156,7 +156,8 @@ def run_token_lockstep(w, steps, *, sample_seqs=None, sample_heads=None, rtol=No
                                    policy=w.policy if w.policy == "cumulative" else "ema",
                                    refresh_interval=w.refresh_interval, score_free=w.score_free,
                                    n_sink=w.n_sink, n_recent=w.n_recent,
-                                   capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
+                                   capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer,
+                                   new_token_init="mean" if w.new_token_init == 1 else "zero")
 
     orcs = {k: new_oracle() for k in keys}
     for b in range(w.batch):
@@ -339,7 +340,8 @@ def run_diag_lockstep(w, steps, k, *, sample_seqs=None, sample_heads=None, rtol=
                                 alpha_new=w.alpha_new,
                                 policy=w.policy if w.policy == "cumulative" else "ema",
                                 n_sink=w.n_sink, n_recent=w.n_recent,
-                                capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
+                                capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer,
+                                new_token_init="mean" if w.new_token_init == 1 else "zero")
     for b in range(w.batch):
         K, V = w.prefill_kv(b, device=device)
         ctx.prefill(b, K.contiguous(), V.contiguous())
@@ -454,7 +456,8 @@ def run_pooled_lockstep(w, steps, *, sample_seqs=None, rtol=None, device="cuda",
                               policy=w.policy if w.policy == "cumulative" else "ema",
                               refresh_interval=w.refresh_interval, score_free=w.score_free,
                               n_sink=w.n_sink, n_recent=w.n_recent,
-                              capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer)
+                              capacity=max(w.prefill_lens) + steps + 1, scorer=w.scorer,
+                              new_token_init="mean" if w.new_token_init == 1 else "zero")
     for b in range(w.batch):
         K, V = w.prefill_kv(b, device=device)
         ctx.prefill(b, K.contiguous(), V.contiguous())

@@ -109,6 +109,9 @@ def _create(**kw):
     (dict(rope_theta=10000.0), "rope_theta applies to the tiered mode only"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, int2_key_groups=2), "int2_key_groups must be 0 or 1"),
     (dict(int2_key_groups=1), "int2_key_groups applies to the tiered mode only"),
+    (dict(new_token_init=2), "new_token_init must be 0 or 1"),
+    (dict(policy=kvev.LRFU_BLOCK, dtype=kvev.BF16, head_dim=128, new_token_init=1),
+     "new_token_init applies to the token policies only"),
     (dict(policy=kvev.TIERED_INT2, dtype=kvev.BF16, head_dim=128, refresh_interval=2), "refresh_interval"),
     (dict(diag_topk=-1), "diag_topk"),
     (dict(offload_blocks=-1), "offload_blocks"),
@@ -192,7 +195,7 @@ def test_config_defaults():
     assert abs(c.beta - 0.001) < 1e-9 and c.decode_region == 4 and c.access_tau_mult == 2.0
     assert c.pinned_region_mask == 0 and list(c.region_half_life) == [0.0] * 8
     assert c.window_tokens == 32 and c.fp_windows == 0 and c.int2_windows == 0 and c.rope_theta == 0.0
-    assert c.int2_key_groups == 0
+    assert c.int2_key_groups == 0 and c.new_token_init == 0
 
 
 def test_tier_entry_points_reject_null_context():

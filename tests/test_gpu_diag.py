@@ -120,3 +120,10 @@ def test_diag_state_changes_only_by_step():
     ctx.sync()
     ctx.close()
     plain.close()
+
+
+def test_diag_new_token_mean_init():
+    """The diagnostics record the new token's utility after its mean start."""
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(900,), budget=100, attn_path=2,
+                                             new_token_init=1)
+    _gu().run_diag_lockstep(w, 12, 40)

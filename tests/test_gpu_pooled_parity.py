@@ -98,3 +98,9 @@ def test_pooled_smaller_budget_after_single_token_evictions():
     compare("after the smaller budget")
     ctx.sync()
     ctx.close()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_pooled_new_token_mean_init(fused):
+    st = _gu().run_pooled_lockstep(_w(new_token_init=1), 16, fused=fused)
+    assert st.steps == 16

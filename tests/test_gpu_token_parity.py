@@ -332,3 +332,25 @@ def test_single_step_rule_alpha_one():
                                       gu.expected_after_evict(gs, gp, w.budget, w.n_sink, w.n_recent))
     ctx.sync()
     ctx.close()
+
+
+@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("fused", [False, True])
+def test_new_token_mean_init(path, fused):
+    """new_token_init = mean: on an observation step the new token starts at
+    the mean of its group's other utilities, then is folded ("What Matters
+    ...", appendix E's rule for the other steps, read for observation steps
+    too), with protection, on both attention kernels."""
+    w = synth.workload("llama8b_32k").scaled(n_layers=3, prefill_lens=(1100,), budget=120,
+                                             new_token_init=1, attn_path=path)
+    st = _gu().run_token_lockstep(w, 24, fused=fused)
+    assert st.steps == 24
+
+
+@pytest.mark.parametrize("policy,r", [("cumulative", 1), ("ema", 4)])
+def test_new_token_mean_init_cumulative_and_lazy(policy, r):
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(700, 900), budget=100,
+                                             policy=policy, refresh_interval=r, new_token_init=1,
+                                             attn_path=2)
+    _gu().run_token_lockstep(w, 16, fused=True)
+    _gu().run_token_lockstep(w.scaled(attn_path=1), 16)
