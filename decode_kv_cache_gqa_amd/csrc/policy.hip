@@ -548,6 +548,11 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
     red[wave] = sum;
     s_new[wave] = mn;
   }
+  // a selection of more than one token reads every slot's utility back in
+  // the group's last block: then each thread's utility store completes
+  // before the block arrives (with one token over budget only the summaries
+  // cross blocks, and thread 0 waits for those)
+  if (A.do_select && n > A.B + 1) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < NWV; ++w) {
