@@ -73,6 +73,15 @@ constexpr int kQW = 4;  // INT2 windows per wave of the fused INT2 path
 // scale and zero [4][8] (fp16)
 constexpr int kRec8K = 0, kRec8V = 256, kRec8SK = 512, kRec8ZK = 768, kRec8SV = 1024, kRec8ZV = 1088;
 
+// A store written through the L2 to memory (relaxed agent-scope atomic
+// store: global_store ... sc1).  The attention's chunk partials and window
+// masses use it: the merge and mass kernels read them next, and the launch
+// measured about 2.7 us shorter than with plain stores on the 131k
+// workload.
+__device__ __forceinline__ void st_through(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bf16x8_t as_b8(const uint4& r) {
   bf16x8_t v;
   __builtin_memcpy(&v, &r, sizeof(v));
@@ -759,10 +768,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
       o += f * o_lds[w][hh][c];
       Z += f * wstat[w][hh][1];
     }
-    A.part_o[pb * HG * D + idx] = o;
+    st_through(&A.part_o[pb * HG * D + idx], o);
     if (c == 0) {
-      A.part_ml[(pb * HG + hh) * 2 + 0] = M;
-      A.part_ml[(pb * HG + hh) * 2 + 1] = Z;
+      st_through(&A.part_ml[(pb * HG + hh) * 2 + 0], M);
+      st_through(&A.part_ml[(pb * HG + hh) * 2 + 1], Z);
     }
   }
   if (tid < 4 * wpw * HG) {
@@ -775,7 +784,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void t
       for (int w = 0; w < 4; ++w) M = fmaxf(M, wstat[w][hh][0]);
       const float f = wstat[wv][hh][0] == -INFINITY ? 0.f : __expf(wstat[wv][hh][0] - M);
       const int cidx = (isq ? n_fp : 0) + idx;
-      A.emass[(lh * A.NW + cidx) * HG + hh] = e_lds[wv][k][hh] * f;
+      st_through(&A.emass[(lh * A.NW + cidx) * HG + hh], e_lds[wv][k][hh] * f);
     }
   }
   (void)nch;
