@@ -968,7 +968,7 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
   __shared__ uint32_t freeF[kSlotWords], freeQ[kSlotWords], freshF[kSlotWords];
   __shared__ int preF[kSlotWords], preQ[kSlotWords], preN[kSlotWords];
   __shared__ int ncand, njobs, wsum[kRouteNT / kWave], tots[4];
-  __shared__ int hist[2][256], rsel[2];  // the two threshold searches
+  __shared__ int hist[2][256], rsel[2], nsel[2];  // the two threshold searches
   __shared__ unsigned long long psel[2];
   __shared__ int dsum[6][kRouteNT / kWave];
   const int l = l0 + blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
@@ -1005,8 +1005,11 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
       psel[0] = psel[1] = 0ull;
       rsel[0] = nsel0 - 1;
       rsel[1] = nsel1 - 1;
+      nsel[0] = act0 ? nc : 1;  // keys sharing the prefix found so far
+      nsel[1] = act1 ? nc : 1;
     }
-    for (int pass = 0; pass < 8; ++pass) {
+    int pass = 0;
+    for (; pass < 8; ++pass) {
       const int sh = 56 - 8 * pass;
       for (int i = tid; i < 512; i += kRouteNT) (&hist[0][0])[i] = 0;
       __syncthreads();
@@ -1038,11 +1041,26 @@ __global__ __launch_bounds__(kRouteNT) void tier_route_kernel(TierArgs A, int nw
             if (r < acc + c[u]) {
               psel[sx] |= static_cast<unsigned long long>(4 * lane + u) << sh;
               rsel[sx] = r - acc;
+              nsel[sx] = c[u];
               break;
             }
             acc += c[u];
           }
         }
+      }
+      __syncthreads();
+      // once each threshold's prefix is held by its key alone (distinct
+      // scores settle within the first bytes), that key is the threshold
+      if (nsel[0] == 1 && nsel[1] == 1) break;  // block-uniform (LDS after a barrier)
+    }
+    if (pass < 7) {
+      const unsigned long long hm = ~0ull << (56 - 8 * pass);
+      const unsigned long long p0 = psel[0], p1 = psel[1];
+      __syncthreads();  // every thread has read psel before it is replaced
+      for (int i = tid; i < nc; i += kRouteNT) {
+        const unsigned long long key = keys[i];
+        if (act0 && (key & hm) == p0) psel[0] = key;
+        if (act1 && (key & hm) == p1) psel[1] = key;
       }
       __syncthreads();
     }
