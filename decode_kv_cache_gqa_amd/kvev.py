@@ -529,7 +529,8 @@ def context_for(w, max_steps=None, budget=None, stream=None, diag_topk=None, off
             if budget is None else budget, beta=w.beta,
             pinned_region_mask=sum(1 << r for r in w.pinned_regions), decode_region=w.decode_region,
             access_tau_mult=2.0, offload_blocks=w.offload_blocks if offload_blocks is None else offload_blocks,
-            prefetch_blocks=prefetch_blocks, offload_min_score=offload_min_score)
+            prefetch_blocks=prefetch_blocks, offload_min_score=offload_min_score,
+            attn_path=w.attn_path if attn_path is None else attn_path)
         for r, hl in enumerate(w.region_half_lives):
             cfg.region_half_life[r] = hl
         return Context(cfg, stream=stream)

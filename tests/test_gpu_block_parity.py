@@ -131,3 +131,30 @@ def test_block_max_positions_sampled():
     w = synth.workload("lrfu64").scaled(n_layers=4, prefill_lens=(65520,))
     st = _gu().run_block_lockstep(w, 4, readmit=False, kv_every=4)
     assert st.steps == 4
+
+
+@pytest.mark.parametrize("path,expect", [(0, "attn"), (1, "attn"), (2, "attn_whole")])
+def test_attention_kernel_choice(path, expect):
+    """attn_path picks the kernel the steady steps run (the launches name
+    themselves when profiling): AUTO takes the split kernel below 224 (group,
+    layer) pairs, WHOLE the whole-cache kernel over the block tables."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    w = _scaled(prefill_lens=(300, 517), attn_path=path)
+    ctx = kvev.context_for(w, max_steps=6)
+    for b in range(w.batch):
+        K, V = w.prefill_kv(b, device="cuda")
+        ctx.prefill(b, K, V, w.region_labels(b))
+        ctx.set_budget(b, w.block_budget(b))
+    out = torch.empty((w.n_layers, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ctx.step(*w.step_inputs(1, device="cuda"), out)  # the prefill eviction
+    ctx.sync()
+    ctx.profile(True)
+    for t in range(2, 6):
+        ctx.step(*w.step_inputs(t, device="cuda"), out)
+    ctx.sync()
+    ran = {k: ctx.profile_read(k)[1] for k in ("attn", "attn_whole", "merge")}
+    ctx.close()
+    other = "attn_whole" if expect == "attn" else "attn"
+    assert ran[expect] == 4 and ran[other] == 0
+    assert ran["merge"] == (4 if expect == "attn" else 0)

@@ -26,10 +26,13 @@ def _scaled(**kw):
     return synth.workload("lrfu64").scaled(**base)
 
 
-def test_offload_pool_large_enough_for_every_eviction():
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "whole"])
+def test_offload_pool_large_enough_for_every_eviction(path):
     """Every block evicted by the first selection fits the pool: each epoch's
-    heavy blocks come back from host memory, bit-exact."""
-    st = _gu().run_offload_twins(_scaled(), 48, 512)
+    heavy blocks come back from host memory, bit-exact (also with the
+    whole-cache attention over the block tables, which the full-size
+    workload takes)."""
+    st = _gu().run_offload_twins(_scaled(attn_path=path), 48, 512)
     assert st["readmitted"] > 0 and st["dropped"] == 0 and st["refused"] == 0
 
 

@@ -354,3 +354,26 @@ def test_new_token_mean_init_cumulative_and_lazy(policy, r):
                                              attn_path=2)
     _gu().run_token_lockstep(w, 16, fused=True)
     _gu().run_token_lockstep(w.scaled(attn_path=1), 16)
+
+
+@pytest.mark.parametrize("path,expect", [(1, "attn"), (2, "attn_whole")])
+def test_attention_kernel_choice(path, expect):
+    """attn_path picks the kernel the steady steps run (the launches name
+    themselves when profiling)."""
+    import torch
+    from decode_kv_cache_gqa_amd import kvev
+    w = synth.workload("llama8b_32k").scaled(n_layers=2, prefill_lens=(700,), budget=100, attn_path=path)
+    ctx = kvev.context_for(w, max_steps=6)
+    K, V = w.prefill_kv(0, device="cuda")
+    ctx.prefill(0, K, V)
+    out = torch.empty((w.n_layers, 1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ctx.step(*w.step_inputs(1, device="cuda"), out)
+    ctx.sync()
+    ctx.profile(True)
+    for t in range(2, 6):
+        ctx.step(*w.step_inputs(t, device="cuda"), out)
+    ctx.sync()
+    ran = {k: ctx.profile_read(k)[1] for k in ("attn", "attn_whole")}
+    ctx.close()
+    other = "attn_whole" if expect == "attn" else "attn"
+    assert ran[expect] == 4 and ran[other] == 0
