@@ -431,9 +431,10 @@ __global__ __launch_bounds__(NT) void post_kernel(PostArgs A) {
 // ---------------------------------------------------------------------------
 // Fold + selection after the whole-cache attention (which wrote the
 // outputs and, on an observation step, every slot's group mass per layer
-// into gmass [G][L][lstride]).  Grid (slot blocks of 256, groups), one slot
-// per thread.  Each thread's loads do not wait for the group's count (slots
-// past it are masked afterwards): the slot's utility and position and, on
+// into gmass [G][L][lstride]).  Slot blocks of 256 per group in a 1-D grid,
+// group fastest; one slot per thread.  Each thread's loads do not wait for
+// the group's count (slots past it are masked afterwards): the slot's
+// utility and position and, on
 // an observation step, its masses of every layer, folded in ascending layer
 // order ("What Matters ...", section 3.1 Eq.3/Eq.4, appendix E "Layer
 // scoring"; the new token starts at 0).  Each block publishes the minimum
@@ -468,7 +469,7 @@ struct FoldArgs {
   int* dg_pos;
   float* dg_raw;
   float* dg_util;
-  int L, max_blk, nblk;
+  int L, max_blk, nblk, G;
   int64_t cap, lstride;
   float a;
   int cumulative, refresh, do_select, B, n_sink, n_recent;
@@ -483,7 +484,10 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
   __shared__ unsigned long long s_key[NWV];
   __shared__ int s_slot[NWV];
   __shared__ int s_last;
-  const int blk = blockIdx.x, g = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // a 1-D grid, group fastest: workgroups go to the eight XCDs round-robin,
+  // so group g's blocks share an XCD (and its L2) with the attention
+  // workgroups of group g, which wrote the masses (grid (groups, layers))
+  const int g = blockIdx.x % A.G, blk = blockIdx.x / A.G, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int t = blk * NT + tid;
   const bool valid = t < A.cap;
   int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
@@ -691,6 +695,7 @@ hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64
   A.L = cf.n_layers;
   A.max_blk = c->max_post_blocks;
   A.nblk = (n_max + kFoldNT - 1) / kFoldNT;
+  A.G = c->G;
   A.cap = c->cap;
   A.lstride = c->lstride;
   A.a = cf.alpha_new;
@@ -702,7 +707,7 @@ hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64
   A.n_recent = cf.n_recent;
   A.mean_init = cf.new_token_init == KVEV_NEW_TOKEN_MEAN;
   A.wprior = prior_fold_weight(cf.alpha_new, cf.n_layers, A.cumulative != 0);
-  dim3 grid(A.nblk, c->G);
+  dim3 grid(A.nblk * c->G);
   if (cf.n_layers <= 32) return timed_launch(c, "post", fold_kernel<32>, grid, dim3(kFoldNT), 0, A);
   return timed_launch(c, "post", fold_kernel<kFoldLayers>, grid, dim3(kFoldNT), 0, A);
 }
