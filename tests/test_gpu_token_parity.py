@@ -377,3 +377,14 @@ def test_attention_kernel_choice(path, expect):
     ctx.close()
     other = "attn_whole" if expect == "attn" else "attn"
     assert ran[expect] == 4 and ran[other] == 0
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_whole_cache_attention_four_wave_workgroups(fused):
+    """512 (group, layer) pairs or more (two rounds of the chip) take the
+    whole-cache kernel's 4-wave workgroups: 16 sequences x 8 KV heads x 4
+    layers, ragged prefills, lazy refresh."""
+    lens = tuple(500 + 37 * i for i in range(16))
+    w = synth.workload("lazy16x8k").scaled(n_layers=4, prefill_lens=lens, budget=150, attn_path=2)
+    st = _gu().run_token_lockstep(w, 12, sample_seqs=[0, 7, 15], fused=fused)
+    assert st.steps == 12
