@@ -718,12 +718,13 @@ static kvev_status check_pool_import(kvev_ctx* c) {
 }
 
 // The whole-cache attention kernel applies to the token policies with bf16,
-// head_dim 128, the attention scorer and per-KV-head granularity, when the
-// step's slots fit its bound and its LDS (the logits of an observation
-// step, the per-wave outputs and about 1 KiB of fixed arrays).
+// head_dim 128 and the attention scorer (per KV head or per sequence: the
+// fold kernel then pools a sequence's groups), when the step's slots fit
+// its bound and its LDS (the logits of an observation step, the per-wave
+// outputs and about 1 KiB of fixed arrays).
 static bool whole_cache_attention(const kvev_ctx* c, int64_t n_max) {
   const auto& f = c->cfg;
-  if (f.attn_path == KVEV_ATTN_SPLIT || c->block_mode || c->tier_mode || c->pooled) return false;
+  if (f.attn_path == KVEV_ATTN_SPLIT || c->block_mode || c->tier_mode) return false;
   if (f.dtype != KVEV_BF16 || f.head_dim != 128 || f.scorer != 0) return false;
   if (n_max > kSeqMaxSlots || seq_attn_lds_bytes(c->HG, n_max, true, false) + 1024 > c->max_lds) return false;
   return f.attn_path == KVEV_ATTN_WHOLE || static_cast<int64_t>(c->G) * f.n_layers >= 224;

@@ -475,9 +475,15 @@ struct FoldArgs {
   int cumulative, refresh, do_select, B, n_sink, n_recent;
   int mean_init;  // as in PostArgs
   float wprior;
+  // per-sequence granularity: G counts sequences, each of pool_hkv KV head
+  // groups whose state lives in its first group; a slot's layer
+  // observation is the sum of the groups' masses times inv_hq (the mean
+  // over every query head)
+  int pool_hkv;
+  float inv_hq;
 };
 
-template <int NL>
+template <int NL, bool POOL>
 __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
   constexpr int NT = kFoldNT, NWV = NT / kWave;
   __shared__ float red[NWV], s_new[NWV];
@@ -487,7 +493,9 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
   // a 1-D grid, group fastest: workgroups go to the eight XCDs round-robin,
   // so group g's blocks share an XCD (and its L2) with the attention
   // workgroups of group g, which wrote the masses (grid (groups, layers))
-  const int g = blockIdx.x % A.G, blk = blockIdx.x / A.G, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int gi = blockIdx.x % A.G, blk = blockIdx.x / A.G, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int nhg = POOL ? A.pool_hkv : 1;  // the KV head groups that share the state
+  const int g = gi * nhg;                 // the group holding the state
   const int t = blk * NT + tid;
   const bool valid = t < A.cap;
   int* gp = A.pos + static_cast<int64_t>(g) * A.cap;
@@ -500,6 +508,20 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
     const float* gm = A.gmass + static_cast<int64_t>(g) * A.L * A.lstride + (t < A.lstride ? t : 0);
 #pragma unroll
     for (int l = 0; l < NL; ++l) x[l] = l < A.L ? gm[static_cast<int64_t>(l) * A.lstride] : 0.f;
+    if constexpr (POOL) {
+      // the other groups' masses, added in group order, then the mean over
+      // every query head
+      for (int h = 1; h < nhg; ++h) {
+        const float* gh = gm + static_cast<int64_t>(h) * A.L * A.lstride;
+        float y[NL];
+#pragma unroll
+        for (int l = 0; l < NL; ++l) y[l] = l < A.L ? gh[static_cast<int64_t>(l) * A.lstride] : 0.f;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) x[l] += y[l];
+      }
+#pragma unroll
+      for (int l = 0; l < NL; ++l) x[l] *= A.inv_hq;
+    }
   }
   const int n = A.count[g] + 1, hn = A.hole[g], newest = A.nextpos[g];
   auto is_cand = [&](int p) { return !(p < A.n_sink || p > newest - A.n_recent); };
@@ -630,7 +652,7 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
     if (!A.refresh || A.mean_init) st_coherent(gs + hn, newscore);
     if (A.refresh && A.mean_init && A.dg_util) A.dg_util[static_cast<int64_t>(g) * A.cap + hn] = newscore;
     st_coherent(gp + hn, newest);
-    st_coherent(A.nextpos + g, newest + 1);
+    for (int h = 0; h < nhg; ++h) st_coherent(A.nextpos + g + h, newest + 1);
     st_coherent(A.grpctr + g, 0u);
   }
   const bool one_over = A.do_select && n == A.B + 1;
@@ -663,9 +685,11 @@ __global__ __launch_bounds__(kFoldNT) void fold_kernel(FoldArgs A) {
     final_n = A.B;
   }
   if (tid == 0) {
-    st_coherent(A.count + g, final_n);
-    st_coherent(A.hole + g, new_hole);
-    st_coherent(A.nmoves + g, nm);
+    for (int h = 0; h < nhg; ++h) {  // every KV head group follows the state's plan
+      st_coherent(A.count + g + h, final_n);
+      st_coherent(A.hole + g + h, new_hole);
+      st_coherent(A.nmoves + g + h, nm);
+    }
   }
 }
 
@@ -695,7 +719,9 @@ hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64
   A.L = cf.n_layers;
   A.max_blk = c->max_post_blocks;
   A.nblk = (n_max + kFoldNT - 1) / kFoldNT;
-  A.G = c->G;
+  A.G = c->pooled ? cf.batch : c->G;
+  A.pool_hkv = c->pooled ? cf.n_kv_heads : 1;
+  A.inv_hq = 1.0f / static_cast<float>(cf.n_q_heads);
   A.cap = c->cap;
   A.lstride = c->lstride;
   A.a = cf.alpha_new;
@@ -707,9 +733,12 @@ hipError_t launch_fold(kvev_ctx* c, int n_max, int refresh, int do_select, int64
   A.n_recent = cf.n_recent;
   A.mean_init = cf.new_token_init == KVEV_NEW_TOKEN_MEAN;
   A.wprior = prior_fold_weight(cf.alpha_new, cf.n_layers, A.cumulative != 0);
-  dim3 grid(A.nblk * c->G);
-  if (cf.n_layers <= 32) return timed_launch(c, "post", fold_kernel<32>, grid, dim3(kFoldNT), 0, A);
-  return timed_launch(c, "post", fold_kernel<kFoldLayers>, grid, dim3(kFoldNT), 0, A);
+  dim3 grid(A.nblk * A.G);
+  if (c->pooled)
+    return cf.n_layers <= 32 ? timed_launch(c, "post", fold_kernel<32, true>, grid, dim3(kFoldNT), 0, A)
+                             : timed_launch(c, "post", fold_kernel<kFoldLayers, true>, grid, dim3(kFoldNT), 0, A);
+  if (cf.n_layers <= 32) return timed_launch(c, "post", fold_kernel<32, false>, grid, dim3(kFoldNT), 0, A);
+  return timed_launch(c, "post", fold_kernel<kFoldLayers, false>, grid, dim3(kFoldNT), 0, A);
 }
 
 // Standalone selection (kvev_evict): one block per group, or, in the

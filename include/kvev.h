@@ -207,8 +207,9 @@ typedef struct {
    * writes the outputs and each slot's group mass, in the block mode each
    * table entry's, directly) when there are at least 224 (group, layer)
    * pairs, the step's slot count fits its bound (8,192 slots and its LDS)
-   * and neither a scorer variant nor per-sequence granularity is set; the
-   * split kernel otherwise.  SPLIT: always the split kernel.  WHOLE: the
+   * and no scorer variant is set (per-sequence granularity included: the
+   * fold then pools each sequence's KV head groups); the split kernel
+   * otherwise.  SPLIT: always the split kernel.  WHOLE: the
    * whole-cache kernel whenever it applies, whatever the pair count.
    * Results agree within the tolerances; each path is deterministic. */
   int32_t attn_path;

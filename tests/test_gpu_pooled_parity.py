@@ -1,7 +1,9 @@
 """GPU parity of the sequence-pooled token mode (one utility and one retained
 set per sequence, "What Matters ...", section 3.1 Eq.1) against the CPU
-oracle, through the C ABI: the pooled post kernel (fused step) and the
-per-sequence selection with the shared moves (separate evict call)."""
+oracle, through the C ABI: the pooled post kernel after the split attention,
+or the fold kernel pooling a sequence's KV head groups after the whole-cache
+attention (fused step), and the per-sequence selection with the shared
+moves (separate evict call)."""
 import pytest
 
 from conftest import gpu_available
@@ -22,15 +24,21 @@ def _w(**kw):
     return synth.workload("llama8b_32k_pooled").scaled(**base)
 
 
+# attention kernels: split (1) and whole-cache (2, its fold pools the sequence's groups)
+PATHS = pytest.mark.parametrize("path", [1, 2], ids=["split", "whole"])
+
+
+@PATHS
 @pytest.mark.parametrize("fused", [False, True])
-def test_pooled_llama_shape(fused):
-    st = _gu().run_pooled_lockstep(_w(), 24, fused=fused)
+def test_pooled_llama_shape(fused, path):
+    st = _gu().run_pooled_lockstep(_w(attn_path=path), 24, fused=fused)
     assert st.steps == 24
 
 
-def test_pooled_batch_lazy_refresh():
+@PATHS
+def test_pooled_batch_lazy_refresh(path):
     w = _w(n_layers=2, prefill_lens=(700, 513, 900), budget=120, refresh_interval=4,
-           n_sink=0, n_recent=8)
+           n_sink=0, n_recent=8, attn_path=path)
     _gu().run_pooled_lockstep(w, 18, fused=True, sample_seqs=[0, 1, 2])
 
 
@@ -47,13 +55,15 @@ def test_pooled_fp32_vector_path():
     assert st.max_out_err <= 1e-5 and st.max_score_err <= 1e-5
 
 
-def test_pooled_single_kv_head_and_cumulative():
+@PATHS
+def test_pooled_single_kv_head_and_cumulative(path):
     w = _w(n_layers=2, n_q_heads=8, n_kv_heads=1, prefill_lens=(600,), budget=90,
-           policy="cumulative")
+           policy="cumulative", attn_path=path)
     _gu().run_pooled_lockstep(w, 12)
 
 
-def test_pooled_smaller_budget_after_single_token_evictions():
+@PATHS
+def test_pooled_smaller_budget_after_single_token_evictions(path):
     """The per-sequence free slot (left by single-token evictions of the
     fused step) is filled from the last slot of every KV head before a
     kvev_evict with a smaller budget selects."""
@@ -62,7 +72,7 @@ def test_pooled_smaller_budget_after_single_token_evictions():
     import oracle as orc
     from decode_kv_cache_gqa_amd import kvev
     gu = _gu()
-    w = _w(n_layers=2, prefill_lens=(400,), budget=90, n_sink=2, n_recent=5)
+    w = _w(n_layers=2, prefill_lens=(400,), budget=90, n_sink=2, n_recent=5, attn_path=path)
     ctx = kvev.context_for(w, max_steps=16)
     o = orc.PooledTokenOracle(w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim, budget=90,
                               alpha_new=w.alpha_new, n_sink=2, n_recent=5, capacity=420)
@@ -100,7 +110,8 @@ def test_pooled_smaller_budget_after_single_token_evictions():
     ctx.close()
 
 
+@PATHS
 @pytest.mark.parametrize("fused", [False, True])
-def test_pooled_new_token_mean_init(fused):
-    st = _gu().run_pooled_lockstep(_w(new_token_init=1), 16, fused=fused)
+def test_pooled_new_token_mean_init(fused, path):
+    st = _gu().run_pooled_lockstep(_w(new_token_init=1, attn_path=path), 16, fused=fused)
     assert st.steps == 16
